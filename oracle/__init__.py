@@ -1,0 +1,189 @@
+"""CPU reference ("oracle") of batched CTC prefix beam search.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The decoder
+library (``ctc_prefix_beam_amd``) never imports, loads or calls it, and the two
+share no code.
+
+The arithmetic lives in ``ctc_oracle.c`` (plain C, float32, following the page
+"GPU CTC Prefix Beam Search Decoder", sections 3.1-3.7, 8 and 13); this module
+only builds it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ctc_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# One rounding per written operation: no contraction, no fast-math.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-fno-builtin-expf", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+NEG = -np.finfo(np.float32).max
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so next to its source (gcc, host only)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        f32, i32, i64, p = ctypes.c_float, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        L.oracle_exp.restype = f32
+        L.oracle_exp.argtypes = [f32]
+        L.oracle_log1p.restype = f32
+        L.oracle_log1p.argtypes = [f32]
+        L.oracle_lse.restype = f32
+        L.oracle_lse.argtypes = [f32, f32]
+        L.oracle_log_threshold.restype = f32
+        L.oracle_log_threshold.argtypes = [f32]
+        L.oracle_select_frames.restype = i32
+        L.oracle_select_frames.argtypes = [p, i64, i32, i32, f32, p]
+        L.oracle_decode.restype = i32
+        L.oracle_decode.argtypes = [p, i64, i64, i32, i32, p, i32, i32, i32, i32, f32, i32,
+                                    p, p, p]
+        L.oracle_stream_new.restype = p
+        L.oracle_stream_new.argtypes = [i32, i32, i32, i32]
+        L.oracle_stream_free.restype = None
+        L.oracle_stream_free.argtypes = [p]
+        L.oracle_stream_reset.restype = None
+        L.oracle_stream_reset.argtypes = [p]
+        L.oracle_stream_feed.restype = i32
+        L.oracle_stream_feed.argtypes = [p, p, i64, i32]
+        L.oracle_stream_step_count.restype = i32
+        L.oracle_stream_step_count.argtypes = [p]
+        L.oracle_stream_read.restype = None
+        L.oracle_stream_read.argtypes = [p, i32, i32, p, p, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def exp(x: float) -> float:
+    return lib().oracle_exp(float(x))
+
+
+def log1p(x: float) -> float:
+    return lib().oracle_log1p(float(x))
+
+
+def lse(a: float, b: float) -> float:
+    return lib().oracle_lse(float(a), float(b))
+
+
+def select_frames(lp_row: np.ndarray, length: int, blank: int, threshold: float) -> np.ndarray:
+    lp_row = np.ascontiguousarray(lp_row, dtype=np.float32)
+    T, V = lp_row.shape
+    sel = np.zeros(max(T, 1), np.int32)
+    n = lib().oracle_select_frames(_ptr(lp_row), V, int(length), int(blank),
+                                   float(threshold), _ptr(sel))
+    return sel[:n].copy()
+
+
+def decode(log_prob: np.ndarray, seq_lengths, beam: int, nbest: int | None = None,
+           blank: int = 0, threshold: float = 1.0, max_out_len: int | None = None):
+    """Offline decode.  Returns (tokens[B,N,max_out_len] -1 padded, lengths[B,N],
+    scores[B,N])."""
+    log_prob = np.ascontiguousarray(log_prob, dtype=np.float32)
+    B, T, V = log_prob.shape
+    nbest = beam if nbest is None else nbest
+    max_out_len = T if max_out_len is None else max_out_len
+    lens = np.ascontiguousarray(seq_lengths, dtype=np.int32)
+    assert lens.shape == (B,)
+    toks = np.full((B, nbest, max(max_out_len, 0)), -1, np.int32)
+    lengths = np.zeros((B, nbest), np.int32)
+    scores = np.zeros((B, nbest), np.float32)
+    rc = lib().oracle_decode(_ptr(log_prob), T * V, V, B, T, _ptr(lens), beam, nbest, V, blank,
+                             float(threshold), max_out_len, _ptr(toks), _ptr(lengths),
+                             _ptr(scores))
+    if rc != 0:
+        raise ValueError("oracle_decode: invalid argument")
+    return toks, lengths, scores
+
+
+class Stream:
+    """One streaming decode (frames fed in chunks; no frame skipping)."""
+
+    def __init__(self, beam: int, vocab: int, blank: int = 0, capacity: int = 4096):
+        self.beam, self.vocab = beam, vocab
+        self._h = lib().oracle_stream_new(beam, vocab, blank, capacity)
+        if not self._h:
+            raise ValueError("oracle_stream_new: invalid argument")
+
+    def feed(self, frames: np.ndarray) -> int:
+        frames = np.ascontiguousarray(frames, dtype=np.float32)
+        n, V = frames.shape
+        assert V == self.vocab
+        return lib().oracle_stream_feed(self._h, _ptr(frames), V, n)
+
+    @property
+    def step(self) -> int:
+        return lib().oracle_stream_step_count(self._h)
+
+    def reset(self):
+        lib().oracle_stream_reset(self._h)
+
+    def read(self, nbest: int | None = None, max_out_len: int = 4096):
+        nbest = self.beam if nbest is None else nbest
+        toks = np.full((nbest, max_out_len), -1, np.int32)
+        lengths = np.zeros(nbest, np.int32)
+        scores = np.zeros(nbest, np.float32)
+        lib().oracle_stream_read(self._h, nbest, max_out_len, _ptr(toks), _ptr(lengths),
+                                 _ptr(scores))
+        return toks, lengths, scores
+
+    def close(self):
+        if self._h:
+            lib().oracle_stream_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _decode_rows_worker(args):
+    (lp, lens, beam, nbest, blank, threshold, max_out_len) = args
+    return decode(lp, lens, beam, nbest, blank, threshold, max_out_len)
+
+
+def decode_parallel(log_prob, seq_lengths, beam, nbest=None, blank=0, threshold=1.0,
+                    max_out_len=None, processes: int = 1):
+    """Rows spread over a process pool (rows are independent).  Same results
+    as ``decode``; used for the CPU baseline timing."""
+    if processes <= 1:
+        return decode(log_prob, seq_lengths, beam, nbest, blank, threshold, max_out_len)
+    import multiprocessing as mp
+    B = log_prob.shape[0]
+    nbest = beam if nbest is None else nbest
+    max_out_len = log_prob.shape[1] if max_out_len is None else max_out_len
+    lens = np.asarray(seq_lengths, np.int32)
+    jobs = [(log_prob[b:b + 1], lens[b:b + 1], beam, nbest, blank, threshold, max_out_len)
+            for b in range(B)]
+    with mp.get_context("fork").Pool(processes) as pool:
+        parts = pool.map(_decode_rows_worker, jobs)
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            np.concatenate([p[2] for p in parts]))

@@ -1,0 +1,490 @@
+/*
+ * ctc_oracle.c -- plain CPU reference ("oracle") of batched CTC prefix beam
+ * search.  TEST INFRASTRUCTURE ONLY: it exists to check the HIP decoder.  Only
+ * the tests, the smoke check and the benchmark's cpu_baseline leg load it; the
+ * decoder library never links, loads or calls it, and the two share no source.
+ *
+ * Source of the method: the page "GPU CTC Prefix Beam Search Decoder" (OASR
+ * documentation, chiendb97.github.io/oasr/ctc_decoder_gpu).  Section numbers
+ * below are that page's.  Everything is done the slow, obvious way: for every
+ * step the full beam x vocab tables ptable / ptablen are built (sec. 3.4.1,
+ * 3.4.2), every ordered beam pair is tested for the merge by comparing tokens
+ * (sec. 3.4.3), and all live candidates are sorted to pick the survivors
+ * (sec. 3.4.4 / 3.4.5).  Scores are float32, as the page fixes them
+ * (log_prob is float32, pprev is a float2, score a float).
+ *
+ * Readings taken where the page is silent or ambiguous:
+ *   - NEG (the page's NEG_INF) is -FLT_MAX; the 0xcc memset pattern the page
+ *     mentions only pre-fills tables that are overwritten before use.
+ *   - logsumexp is the page's max + log(1 + exp(-|a-b|)) written as
+ *     m + log1p(exp(d)), d = min - max, with exp and log1p defined below
+ *     (fixed float32 operation sequences from named published methods) and
+ *     the correction dropped when d < -80 (every intermediate stays normal).
+ *   - Ties in the top-K are broken by ascending flat id k*V + c (the fused
+ *     path's order, sec. 3.4.6); ties in the step-0 vocabulary ranking by
+ *     ascending char id.
+ *   - need_add_blank at step s means "frames were skipped right before the
+ *     frame of step s" (t > t_prev + 1; step 0: first_t > 0), and it is
+ *     applied wherever the page names it: the collapse of pprev before the
+ *     tables (sec. 3.4), the blank-slot rule (sec. 3.4.2) and the pprev reset
+ *     of the winners (sec. 3.4.5), as well as the step-0 seeding (sec. 3.3).
+ *     PARITY UNPINNED for decodes that skip frames: no closed form exists for
+ *     this rule; it is checked against hand-worked cases only.
+ *   - Slots that no candidate fills are dead: score NEG, no tokens; they never
+ *     extend, never merge and are never reported.
+ *   - Offline, the token capacity is the row's frame count, so no hypothesis
+ *     is ever cut; max_out_len only truncates the copy into out_tokens while
+ *     out_lengths reports the full count (sec. 13).  Streaming, a stream
+ *     decodes at most `capacity` frames; later frames are ignored (sec. 13).
+ *   - Final hypotheses are reported in (score desc, slot asc) order; positions
+ *     past a hypothesis' length and dead hypotheses' tokens are -1.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ctc_oracle.h"
+
+#define NEG (-FLT_MAX)
+
+/* ---------------------------------------------------------------------- */
+/* Numerics.                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* exp(x) for x in [-80, 0].  Cody & Waite (1980) argument reduction
+ * x = n*ln2 + r with ln2 split into a 16-significant-bit high part and a
+ * low part, then the degree-7 Taylor polynomial of e^r in Horner form with
+ * fused multiply-adds, then the exact scaling by 2^n. */
+float oracle_exp(float x)
+{
+    const float log2e = 0x1.715476p+0f;
+    const float ln2_hi = 0x1.62e4p-1f;
+    const float ln2_lo = 0x1.7f7d1cp-20f;
+    float n = rintf(x * log2e);
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    float p = 0x1.a01a02p-13f;          /* 1/7! */
+    p = fmaf(p, r, 0x1.6c16c2p-10f);    /* 1/6! */
+    p = fmaf(p, r, 0x1.111112p-7f);     /* 1/5! */
+    p = fmaf(p, r, 0x1.555556p-5f);     /* 1/4! */
+    p = fmaf(p, r, 0x1.555556p-3f);     /* 1/3! */
+    p = fmaf(p, r, 0x1.0p-1f);          /* 1/2! */
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    return ldexpf(p, (int)n);
+}
+
+/* log(1 + x) for x in [0, 1]:  log1p(x) = 2 atanh(s), s = x / (2 + x), with
+ * the odd series 2 (s + s^3/3 + ... + s^15/15) summed as s + s z q(z),
+ * z = s^2, q in Horner form. */
+float oracle_log1p(float x)
+{
+    float s = x / (2.0f + x);
+    float z = s * s;
+    float q = 0x1.111112p-4f;           /* 1/15 */
+    q = fmaf(q, z, 0x1.3b13b2p-4f);     /* 1/13 */
+    q = fmaf(q, z, 0x1.745d18p-4f);     /* 1/11 */
+    q = fmaf(q, z, 0x1.c71c72p-4f);     /* 1/9  */
+    q = fmaf(q, z, 0x1.24924ap-3f);     /* 1/7  */
+    q = fmaf(q, z, 0x1.99999ap-3f);     /* 1/5  */
+    q = fmaf(q, z, 0x1.555556p-2f);     /* 1/3  */
+    float r = fmaf(s * z, q, s);
+    return r + r;
+}
+
+/* The page's logsumexp (sec. 3): max(a,b) + log(1 + exp(-|a-b|)). */
+float oracle_lse(float a, float b)
+{
+    float m = (a >= b) ? a : b;
+    float lo = (a >= b) ? b : a;
+    float d = lo - m;
+    if (!(d >= -80.0f))
+        return m;
+    return m + oracle_log1p(oracle_exp(d));
+}
+
+/* ---------------------------------------------------------------------- */
+/* Frame selection (sec. 3.5).                                              */
+/* ---------------------------------------------------------------------- */
+
+float oracle_log_threshold(float threshold)
+{
+    /* computed once on the host, in double, rounded to float */
+    return (float)log((double)threshold);
+}
+
+int oracle_select_frames(const float *lp_row, int64_t stride_t, int len, int blank,
+                         float threshold, int *sel)
+{
+    int n = 0;
+    if (threshold <= 0.0f)
+        return 0; /* log(0) = -inf: no frame passes (sec. 13) */
+    if (threshold >= 1.0f) {
+        for (int t = 0; t < len; t++)
+            sel[n++] = t; /* no skipping (sec. 13) */
+        return n;
+    }
+    float log_thr = oracle_log_threshold(threshold);
+    for (int t = 0; t < len; t++)
+        if (lp_row[(int64_t)t * stride_t + blank] < log_thr)
+            sel[n++] = t;
+    return n;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Beam state (sec. 3.1).                                                   */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    int live;
+    int len;
+    int *tok; /* capacity cap */
+    float pb, pnb, score;
+} Slot;
+
+struct OracleStream {
+    int beam, vocab, blank, capacity;
+    int step;    /* number of frames decoded so far */
+    int last_t;  /* frame index of the last decoded frame */
+    Slot *cur, *nxt;
+    float *ptable, *ptablen; /* [beam][vocab] */
+    int64_t *order;          /* candidate ids for the sort */
+    const float *sort_keys;  /* keys the comparator reads */
+};
+
+static int slot_clast(const Slot *s, int blank)
+{
+    return s->len > 0 ? s->tok[s->len - 1] : blank;
+}
+
+static const float *g_rank_lp; /* comparator context (single-threaded oracle) */
+
+static int cmp_vocab_rank(const void *a, const void *b)
+{
+    int ca = *(const int *)a, cb = *(const int *)b;
+    float la = g_rank_lp[ca], lb = g_rank_lp[cb];
+    if (la > lb) return -1;
+    if (la < lb) return 1;
+    return (ca < cb) ? -1 : (ca > cb);
+}
+
+static const float *g_keys;
+
+static int cmp_candidates(const void *a, const void *b)
+{
+    int64_t ia = *(const int64_t *)a, ib = *(const int64_t *)b;
+    float ka = g_keys[ia], kb = g_keys[ib];
+    if (ka > kb) return -1;
+    if (ka < kb) return 1;
+    return (ia < ib) ? -1 : (ia > ib);
+}
+
+static void reset_empty(OracleStream *st)
+{
+    /* sec. 13: a row that never runs step 0 holds the empty hypothesis in
+     * slot 0 at score 0 and dead slots elsewhere. */
+    for (int k = 0; k < st->beam; k++) {
+        Slot *s = &st->cur[k];
+        s->live = (k == 0);
+        s->len = 0;
+        s->pb = (k == 0) ? 0.0f : NEG;
+        s->pnb = NEG;
+        s->score = (k == 0) ? 0.0f : NEG;
+    }
+    st->step = 0;
+    st->last_t = -1;
+}
+
+OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
+{
+    if (beam < 1 || vocab < 2 || blank < 0 || blank >= vocab || capacity < 0)
+        return NULL;
+    OracleStream *st = (OracleStream *)calloc(1, sizeof(OracleStream));
+    st->beam = beam;
+    st->vocab = vocab;
+    st->blank = blank;
+    st->capacity = capacity;
+    st->cur = (Slot *)calloc((size_t)beam, sizeof(Slot));
+    st->nxt = (Slot *)calloc((size_t)beam, sizeof(Slot));
+    for (int k = 0; k < beam; k++) {
+        st->cur[k].tok = (int *)malloc(sizeof(int) * (size_t)(capacity + 1));
+        st->nxt[k].tok = (int *)malloc(sizeof(int) * (size_t)(capacity + 1));
+    }
+    st->ptable = (float *)malloc(sizeof(float) * (size_t)beam * (size_t)vocab);
+    st->ptablen = (float *)malloc(sizeof(float) * (size_t)beam * (size_t)vocab);
+    st->order = (int64_t *)malloc(sizeof(int64_t) * (size_t)beam * (size_t)vocab);
+    reset_empty(st);
+    return st;
+}
+
+void oracle_stream_free(OracleStream *st)
+{
+    if (!st) return;
+    for (int k = 0; k < st->beam; k++) {
+        free(st->cur[k].tok);
+        free(st->nxt[k].tok);
+    }
+    free(st->cur);
+    free(st->nxt);
+    free(st->ptable);
+    free(st->ptablen);
+    free(st->order);
+    free(st);
+}
+
+void oracle_stream_reset(OracleStream *st) { reset_empty(st); }
+
+int oracle_stream_step_count(const OracleStream *st) { return st->step; }
+
+/* Step 0 (sec. 3.3): seed the beams from the first decoded frame. */
+static void first_step(OracleStream *st, const float *lp, int t)
+{
+    const int W = st->beam, V = st->vocab, blank = st->blank;
+    int need_add_blank = (t > 0);
+    int nb = (W > 1) ? W - 1 : W;
+
+    int *chars = (int *)malloc(sizeof(int) * (size_t)V);
+    int nc = 0;
+    for (int c = 0; c < V; c++)
+        if (c != blank)
+            chars[nc++] = c;
+    g_rank_lp = lp;
+    qsort(chars, (size_t)nc, sizeof(int), cmp_vocab_rank);
+
+    for (int k = 0; k < W; k++) {
+        Slot *s = &st->cur[k];
+        s->live = 0;
+        s->len = 0;
+        s->pb = s->pnb = s->score = NEG;
+    }
+    int m = nb < nc ? nb : nc;
+    for (int k = 0; k < m; k++) {
+        Slot *s = &st->cur[k];
+        float key = lp[chars[k]];
+        s->live = 1;
+        s->len = 1;
+        s->tok[0] = chars[k];
+        if (need_add_blank) {
+            s->pb = key;
+            s->pnb = NEG;
+        } else {
+            s->pb = NEG;
+            s->pnb = key;
+        }
+        s->score = key;
+    }
+    if (W > 1) {
+        Slot *s = &st->cur[W - 1];
+        s->live = 1;
+        s->len = 0;
+        s->pb = lp[blank];
+        s->pnb = NEG;
+        s->score = lp[blank];
+    }
+    free(chars);
+}
+
+/* One step s >= 1 (sec. 3.4.1 - 3.4.5) on the frame row lp. */
+static void next_step(OracleStream *st, const float *lp, int need_add_blank)
+{
+    const int W = st->beam, V = st->vocab, blank = st->blank;
+    float *pt = st->ptable, *ptn = st->ptablen;
+
+    /* sec. 3.4.1 / 3.4.2: extension tables.  Dead beams get NEG everywhere. */
+    for (int k = 0; k < W; k++) {
+        const Slot *s = &st->cur[k];
+        float *rowb = pt + (size_t)k * V, *rown = ptn + (size_t)k * V;
+        if (!s->live) {
+            for (int c = 0; c < V; c++)
+                rowb[c] = rown[c] = NEG;
+            continue;
+        }
+        float prev_b, prev_nb;
+        if (need_add_blank) { /* collapsed-blank correction (sec. 3.4) */
+            prev_b = oracle_lse(s->pb, s->pnb);
+            prev_nb = NEG;
+        } else {
+            prev_b = s->pb;
+            prev_nb = s->pnb;
+        }
+        int last = slot_clast(s, blank);
+        for (int c = 0; c < V; c++) {
+            if (c == blank)
+                continue;
+            if (c == last) {
+                rown[c] = lp[c] + prev_b;        /* same label: blank path only */
+                rown[blank] = lp[c] + prev_nb;   /* "stay" folds into the blank slot */
+            } else {
+                rown[c] = lp[c] + oracle_lse(prev_b, prev_nb);
+            }
+            rowb[c] = NEG;
+        }
+        rowb[blank] = lp[blank] + oracle_lse(prev_b, prev_nb);
+        if (need_add_blank || last == blank)
+            rown[blank] = NEG;
+    }
+
+    /* sec. 3.4.3: prefix merge.  i = the shorter beam (source), j = the longer. */
+    for (int i = 0; i < W; i++) {
+        const Slot *si = &st->cur[i];
+        if (!si->live) continue;
+        for (int j = 0; j < W; j++) {
+            const Slot *sj = &st->cur[j];
+            if (j == i || !sj->live) continue;
+            if (sj->len - 1 != si->len) continue;
+            if (memcmp(sj->tok, si->tok, sizeof(int) * (size_t)si->len) != 0) continue;
+            size_t src = (size_t)i * V + (size_t)slot_clast(sj, blank);
+            size_t dst = (size_t)j * V + (size_t)blank;
+            pt[dst] = oracle_lse(pt[dst], pt[src]);
+            ptn[dst] = oracle_lse(ptn[dst], ptn[src]);
+            pt[src] = NEG;
+            ptn[src] = NEG;
+        }
+    }
+
+    /* sec. 3.4.4: key = logsumexp(ptable, ptablen); keep keys above NEG;
+     * order (key desc, flat id asc). */
+    const int64_t total = (int64_t)W * V;
+    float *keys = (float *)malloc(sizeof(float) * (size_t)total);
+    int64_t n = 0;
+    for (int64_t id = 0; id < total; id++) {
+        keys[id] = oracle_lse(pt[id], ptn[id]);
+        if (keys[id] > NEG)
+            st->order[n++] = id;
+    }
+    g_keys = keys;
+    qsort(st->order, (size_t)n, sizeof(int64_t), cmp_candidates);
+
+    /* sec. 3.4.5: state update from the snapshot of the source beams. */
+    int nw = (n < W) ? (int)n : W;
+    for (int r = 0; r < W; r++) {
+        Slot *d = &st->nxt[r];
+        if (r >= nw) {
+            d->live = 0;
+            d->len = 0;
+            d->pb = d->pnb = d->score = NEG;
+            continue;
+        }
+        int64_t id = st->order[r];
+        int k = (int)(id / V), c = (int)(id % V);
+        const Slot *s = &st->cur[k];
+        d->live = 1;
+        memcpy(d->tok, s->tok, sizeof(int) * (size_t)s->len);
+        d->len = s->len;
+        if (c != blank)
+            d->tok[d->len++] = c;
+        d->score = keys[id];
+        if (need_add_blank) {
+            d->pb = keys[id];
+            d->pnb = NEG;
+        } else {
+            d->pb = pt[id];
+            d->pnb = ptn[id];
+        }
+    }
+    free(keys);
+    Slot *tmp = st->cur;
+    st->cur = st->nxt;
+    st->nxt = tmp;
+}
+
+/* Decode one selected frame t (row lp) as the stream's next step. */
+static void decode_frame(OracleStream *st, const float *lp, int t)
+{
+    if (st->step == 0)
+        first_step(st, lp, t);
+    else
+        next_step(st, lp, t > st->last_t + 1);
+    st->last_t = t;
+    st->step++;
+}
+
+int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames)
+{
+    /* Streaming (sec. 8): every frame the caller gives is decoded, frame
+     * index = running count; frames past the capacity are ignored (sec. 13). */
+    for (int f = 0; f < n_frames; f++) {
+        if (st->step >= st->capacity)
+            break;
+        decode_frame(st, frames + (int64_t)f * stride_t, st->step == 0 ? 0 : st->last_t + 1);
+    }
+    return st->step;
+}
+
+static int cmp_slots_score(const void *a, const void *b, const Slot *slots)
+{
+    int ia = *(const int *)a, ib = *(const int *)b;
+    float sa = slots[ia].score, sb = slots[ib].score;
+    if (sa > sb) return -1;
+    if (sa < sb) return 1;
+    return (ia < ib) ? -1 : (ia > ib);
+}
+
+void oracle_stream_read(const OracleStream *st, int nbest, int max_out_len,
+                        int *out_tokens, int *out_lengths, float *out_scores)
+{
+    /* live slots in (score desc, slot asc) order, then the dead ones */
+    int W = st->beam;
+    int *idx = (int *)malloc(sizeof(int) * (size_t)W);
+    int nl = 0;
+    for (int k = 0; k < W; k++)
+        if (st->cur[k].live)
+            idx[nl++] = k;
+    /* insertion sort: W is small and this keeps the order rule explicit */
+    for (int a = 1; a < nl; a++) {
+        int v = idx[a], b = a - 1;
+        while (b >= 0 && cmp_slots_score(&idx[b], &v, st->cur) > 0) {
+            idx[b + 1] = idx[b];
+            b--;
+        }
+        idx[b + 1] = v;
+    }
+    for (int r = 0; r < nbest; r++) {
+        int *ot = out_tokens + (size_t)r * max_out_len;
+        for (int p = 0; p < max_out_len; p++)
+            ot[p] = -1;
+        if (r >= nl) {
+            out_lengths[r] = 0;
+            out_scores[r] = NEG;
+            continue;
+        }
+        const Slot *s = &st->cur[idx[r]];
+        out_lengths[r] = s->len;
+        out_scores[r] = s->score;
+        int n = s->len < max_out_len ? s->len : max_out_len;
+        for (int p = 0; p < n; p++)
+            ot[p] = s->tok[p];
+    }
+    free(idx);
+}
+
+/* Offline decode of a batch (sec. 3.7): select frames, decode every selected
+ * frame in order, report the N best per row. */
+int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                  int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
+                  int blank, float threshold, int max_out_len, int *out_tokens,
+                  int *out_lengths, float *out_scores)
+{
+    if (beam < 1 || nbest < 1 || nbest > beam || vocab < 2 || blank < 0 || blank >= vocab ||
+        max_out_len < 0 || batch < 0 || max_T < 0)
+        return 1;
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(max_T > 0 ? max_T : 1));
+    for (int b = 0; b < batch; b++) {
+        int len = seq_lengths[b];
+        if (len < 0) len = 0;
+        if (len > max_T) len = max_T;
+        const float *row = log_prob + (int64_t)b * stride_b;
+        int n = oracle_select_frames(row, stride_t, len, blank, threshold, sel);
+        OracleStream *st = oracle_stream_new(beam, vocab, blank, len);
+        for (int s = 0; s < n; s++)
+            decode_frame(st, row + (int64_t)sel[s] * stride_t, sel[s]);
+        oracle_stream_read(st, nbest, max_out_len,
+                           out_tokens + (size_t)b * nbest * max_out_len,
+                           out_lengths + (size_t)b * nbest, out_scores + (size_t)b * nbest);
+        oracle_stream_free(st);
+    }
+    free(sel);
+    return 0;
+}

@@ -1,0 +1,43 @@
+/* ctc_oracle.h -- interface of the CPU reference decoder (test infrastructure
+ * only; see ctc_oracle.c).  All buffers are host memory owned by the caller. */
+#ifndef CTC_ORACLE_H
+#define CTC_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+float oracle_exp(float x);     /* x in [-80, 0] */
+float oracle_log1p(float x);   /* x in [0, 1]   */
+float oracle_lse(float a, float b);
+float oracle_log_threshold(float threshold);
+
+/* Frame selection of one row: writes the selected frame indices (ascending)
+ * to sel and returns their count. */
+int oracle_select_frames(const float *lp_row, int64_t stride_t, int len, int blank,
+                         float threshold, int *sel);
+
+/* Offline decode.  log_prob[b, t, c] at b*stride_b + t*stride_t + c.
+ * Outputs: out_tokens[batch][nbest][max_out_len] (-1 padded),
+ * out_lengths[batch][nbest], out_scores[batch][nbest].  Returns 0, or 1 on
+ * an invalid argument. */
+int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                  int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
+                  int blank, float threshold, int max_out_len, int *out_tokens,
+                  int *out_lengths, float *out_scores);
+
+/* Streaming: one stream, frames fed in chunks, no frame skipping. */
+typedef struct OracleStream OracleStream;
+OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity);
+void oracle_stream_free(OracleStream *st);
+void oracle_stream_reset(OracleStream *st);
+int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames);
+int oracle_stream_step_count(const OracleStream *st);
+void oracle_stream_read(const OracleStream *st, int nbest, int max_out_len, int *out_tokens,
+                        int *out_lengths, float *out_scores);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

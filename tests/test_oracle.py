@@ -1,0 +1,291 @@
+"""Pins of the CPU oracle against facts outside the oracle itself.
+
+- brute force: with a beam wide enough to keep every prefix and no frame
+  skipping, prefix beam search is exact, so its scores must equal the log-sum
+  over all alignments that collapse to each prefix (enumerated here in fp64);
+- torch's CPU ``ctc_loss`` (the textbook CTC forward recursion, fp64): equal
+  to the exact posteriors above, and an upper bound of every pruned score;
+- closed forms at T = 1 (step-0 seeding, the empty slot, dead slots, ties);
+- the page's stated edge cases (empty rows, thresholds 0 and 1, truncation);
+- a hand-worked frame-skip case (tests/golden/gap_two_skips.json);
+- invariants on the five workloads' generators;
+- the numerics against libm in fp64.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NEG = -np.finfo(np.float32).max
+
+
+# ---------------------------------------------------------------- helpers --
+def collapse(path, blank=0):
+    out, prev = [], None
+    for c in path:
+        if c != prev and c != blank:
+            out.append(c)
+        prev = c
+    return tuple(out)
+
+
+def brute_force(lp, blank=0):
+    """{prefix: log P(prefix | x)} by enumerating every alignment (fp64)."""
+    T, V = lp.shape
+    lp64 = lp.astype(np.float64)
+    acc = {}
+    for path in itertools.product(range(V), repeat=T):
+        s = float(sum(lp64[t, c] for t, c in enumerate(path)))
+        key = collapse(path, blank)
+        acc[key] = np.logaddexp(acc[key], s) if key in acc else s
+    return acc
+
+
+def ctc_logp(lp, target, blank=0):
+    """log P(target | x) from torch's CTC forward (CPU, fp64)."""
+    T = lp.shape[0]
+    x = torch.from_numpy(lp.astype(np.float64)).unsqueeze(1)
+    tgt = torch.tensor(list(target), dtype=torch.long)
+    loss = torch.nn.functional.ctc_loss(x, tgt, torch.tensor([T]), torch.tensor([len(target)]),
+                                        blank=blank, reduction="sum", zero_infinity=False)
+    return -float(loss)
+
+
+def live_hyps(toks, lengths, scores):
+    out = []
+    for r in range(len(lengths)):
+        if scores[r] > NEG:
+            out.append((tuple(int(t) for t in toks[r, :lengths[r]]), float(scores[r])))
+    return out
+
+
+def f32log(p):
+    return np.log(np.asarray(p, np.float64)).astype(np.float32)
+
+
+# -------------------------------------------------------------- numerics --
+def test_exp_matches_libm(oracle_lib):
+    xs = np.concatenate([np.linspace(-80.0, 0.0, 20001), -np.logspace(-8, 1.9, 2001), [0.0]])
+    worst = 0.0
+    for x in xs.astype(np.float32):
+        got = oracle_lib.exp(float(x))
+        ref = math.exp(float(x))
+        worst = max(worst, abs(got - ref) / ref)
+    assert worst < 4e-7, worst  # a few ulp of float32
+
+
+def test_log1p_matches_libm(oracle_lib):
+    xs = np.concatenate([np.linspace(0.0, 1.0, 20001), np.logspace(-30, 0, 2001)])
+    worst = 0.0
+    for x in xs.astype(np.float32):
+        got = oracle_lib.log1p(float(x))
+        ref = math.log1p(float(x))
+        if ref > 0:
+            worst = max(worst, abs(got - ref) / ref)
+        else:
+            assert got == 0.0
+    assert worst < 4e-7, worst
+
+
+def test_lse_identities(oracle_lib):
+    lse = oracle_lib.lse
+    rng = np.random.default_rng(0)
+    for a in rng.uniform(-5000, 0, 200).astype(np.float32):
+        assert lse(float(a), NEG) == float(a)  # NEG is the identity
+        assert lse(NEG, float(a)) == float(a)
+        b = float(np.float32(a - rng.uniform(0, 90)))
+        assert lse(float(a), b) == lse(b, float(a))  # symmetric
+        ref = np.logaddexp(np.float64(a), np.float64(b))
+        assert abs(lse(float(a), b) - ref) <= 4 * np.spacing(np.float32(abs(ref))) + 1e-7
+    assert lse(NEG, NEG) == NEG
+    assert lse(0.0, 0.0) == pytest.approx(math.log(2.0), abs=1e-7)
+
+
+# ------------------------------------------------------ frame selection --
+def test_select_boundaries(oracle_lib):
+    lp, _ = synth.peaky(1, 40, 7, seed=3, p_blank=0.5, blank_bias=9.0)
+    row = lp[0]
+    assert list(oracle_lib.select_frames(row, 40, 0, 1.0)) == list(range(40))
+    assert list(oracle_lib.select_frames(row, 40, 0, 1.5)) == list(range(40))
+    assert len(oracle_lib.select_frames(row, 40, 0, 0.0)) == 0
+    assert len(oracle_lib.select_frames(row, 40, 0, -1.0)) == 0
+    assert list(oracle_lib.select_frames(row, 17, 0, 1.0)) == list(range(17))  # length bound
+    thr = 0.9
+    log_thr = np.float32(math.log(float(np.float32(thr))))  # threshold crosses as float32
+    expect = [t for t in range(40) if row[t, 0] < log_thr]
+    assert list(oracle_lib.select_frames(row, 40, 0, thr)) == expect
+    # strict comparison: a blank log-prob exactly at log(threshold) is kept out
+    row2 = row.copy()
+    row2[5, 0] = log_thr
+    assert 5 not in oracle_lib.select_frames(row2, 40, 0, thr)
+    row2[5, 0] = np.nextafter(log_thr, np.float32(-np.inf))
+    assert 5 in oracle_lib.select_frames(row2, 40, 0, thr)
+
+
+# ------------------------------------------------------------ brute force --
+@pytest.mark.parametrize("T,V,seed", [(1, 3, 0), (2, 3, 1), (3, 3, 2), (4, 3, 3), (5, 3, 4),
+                                      (6, 3, 5), (3, 4, 6), (4, 4, 7), (5, 4, 8), (4, 5, 9)])
+def test_unpruned_equals_brute_force(oracle_lib, T, V, seed):
+    lp, lens = synth.peaky(1, T, V, seed=seed, p_blank=0.5, blank_bias=1.0, token_bias=1.5,
+                           repeat_p=0.5)
+    exact = brute_force(lp[0])
+    W = len(exact) + V  # wide enough to keep every prefix
+    toks, L, S = oracle_lib.decode(lp, lens, W, W, 0, 1.0, T)
+    got = live_hyps(toks[0], L[0], S[0])
+    assert len(got) == len(exact)
+    assert {h for h, _ in got} == set(exact)
+    for h, s in got:
+        assert s == pytest.approx(exact[h], abs=2e-5), h
+    # scores are reported in non-increasing order
+    assert all(got[i][1] >= got[i + 1][1] for i in range(len(got) - 1))
+    # the posteriors of all prefixes sum to one
+    assert np.logaddexp.reduce([s for _, s in got]) == pytest.approx(0.0, abs=2e-5)
+
+
+def test_unpruned_equals_ctc_forward(oracle_lib):
+    lp, lens = synth.peaky(1, 6, 3, seed=11, p_blank=0.4, blank_bias=1.0, token_bias=1.0)
+    W = 200
+    toks, L, S = oracle_lib.decode(lp, lens, W, W, 0, 1.0, 6)
+    for h, s in live_hyps(toks[0], L[0], S[0]):
+        assert s == pytest.approx(ctc_logp(lp[0], h), abs=2e-5)
+
+
+@pytest.mark.parametrize("name,T,W", [("tiny", 50, 4), ("bpe256", 120, 8), ("stream512", 80, 10),
+                                      ("bpe1024", 60, 16)])
+def test_pruned_scores_bounded_by_ctc_forward(oracle_lib, name, T, W):
+    wl = synth.WORKLOADS[name]
+    gen = dict(wl.gen)
+    gen.pop("lengths", None)
+    gen.pop("nan_tail", None)
+    lp, lens = synth.peaky(2, T, wl.V, seed=5, **gen)
+    toks, L, S = oracle_lib.decode(lp, lens, W, W, 0, 1.0, T)
+    for b in range(2):
+        hyps = live_hyps(toks[b], L[b], S[b])
+        assert len(hyps) == W
+        for h, s in hyps:
+            exact = ctc_logp(lp[b], h)
+            # a beam-restricted alignment sum never exceeds the full sum
+            assert s <= exact + 1e-5 * abs(exact) + 1e-4, (h, s, exact)
+        # the 1-best of a peaky input keeps most of its exact posterior
+        assert hyps[0][1] >= ctc_logp(lp[b], hyps[0][0]) - 0.5
+
+
+# --------------------------------------------------------- closed forms --
+def test_single_frame_seeding(oracle_lib):
+    # T = 1: the top-(W-1) non-blank tokens by (lp desc, id asc) at their lp,
+    # plus the empty prefix at lp[blank]; reported by (score desc, slot asc).
+    lp = f32log([[0.30, 0.10, 0.25, 0.10, 0.05, 0.20]])[None]  # ties: ids 1 and 3
+    toks, L, S = oracle_lib.decode(lp, [1], 4, 4, 0, 1.0, 1)
+    got = live_hyps(toks[0], L[0], S[0])
+    assert [h for h, _ in got] == [(), (2,), (5,), (1,)]
+    assert [s for _, s in got] == [float(lp[0, 0, c]) for c in (0, 2, 5, 1)]
+
+
+def test_single_frame_beam_one(oracle_lib):
+    # beam 1 has no empty slot: the best non-blank token is kept (sec. 3.3)
+    lp = f32log([[0.90, 0.04, 0.06]])[None]
+    toks, L, S = oracle_lib.decode(lp, [1], 1, 1, 0, 1.0, 1)
+    assert live_hyps(toks[0], L[0], S[0]) == [((2,), float(lp[0, 0, 2]))]
+
+
+def test_dead_slots_when_vocab_is_narrow(oracle_lib):
+    # V - 1 < W - 1: slots without a token stay dead (score NEG, length 0)
+    lp = f32log([[0.7, 0.3], [0.6, 0.4]])[None]
+    toks, L, S = oracle_lib.decode(lp, [2], 4, 4, 0, 1.0, 2)
+    hyps = live_hyps(toks[0], L[0], S[0])
+    exact = brute_force(lp[0])
+    assert {h for h, _ in hyps} == set(exact)
+    assert list(S[0, len(hyps):]) == [NEG] * (4 - len(hyps))
+    assert list(L[0, len(hyps):]) == [0] * (4 - len(hyps))
+    assert (toks[0, len(hyps):] == -1).all()
+
+
+def test_empty_rows(oracle_lib):
+    # sec. 13: zero-length rows and rows with every frame skipped hold the
+    # empty hypothesis at 0.0, other slots at NEG with length 0
+    lp, _ = synth.peaky(2, 10, 5, seed=1)
+    for lens, thr in (([0, 0], 0.98), ([10, 10], 0.0), ([10, 10], -3.0)):
+        toks, L, S = oracle_lib.decode(lp, lens, 3, 3, 0, thr, 10)
+        assert (L == 0).all()
+        assert (S[:, 0] == 0.0).all() and (S[:, 1:] == NEG).all()
+        assert (toks == -1).all()
+
+
+def test_truncation_keeps_full_length(oracle_lib):
+    lp, lens = synth.peaky(1, 60, 12, seed=2, p_blank=0.3)
+    full = oracle_lib.decode(lp, lens, 5, 5, 0, 1.0, 60)
+    cut = oracle_lib.decode(lp, lens, 5, 5, 0, 1.0, 7)
+    assert (full[1] == cut[1]).all() and (full[2] == cut[2]).all()
+    assert (full[1][0] > 7).all()
+    assert (cut[0] == full[0][:, :, :7]).all()
+
+
+def test_gap_golden(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "gap_two_skips.json")))
+    lp = f32log(g["probs"])[None]
+    T = lp.shape[1]
+    sel = oracle_lib.select_frames(lp[0], T, g["blank"], g["threshold"])
+    assert list(sel) == [0, 2, 3]
+    toks, L, S = oracle_lib.decode(lp, [T], g["beam"], g["nbest"], g["blank"], g["threshold"], T)
+    hyps = live_hyps(toks[0], L[0], S[0])
+    assert [list(h) for h, _ in hyps] == g["expected_tokens"]
+    assert list(L[0]) == g["expected_lengths"]
+    for (_, s), p in zip(hyps, g["expected_scores_log"]):
+        assert s == pytest.approx(math.log(p), abs=1e-6)
+
+
+# -------------------------------------------------------------- invariants --
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_invariants_on_workload_generators(oracle_lib, name):
+    wl = synth.WORKLOADS[name]
+    T = min(wl.T, 120)
+    gen = dict(wl.gen)
+    if "lengths" in gen:
+        gen["lengths"] = (T // 2, T)
+    lp, lens = synth.peaky(2, T, wl.V, seed=7, **gen)
+    toks, L, S = oracle_lib.decode(lp, lens, wl.beam, wl.nbest, 0, wl.threshold, T)
+    for b in range(2):
+        nsel = len(oracle_lib.select_frames(lp[b], lens[b], 0, wl.threshold))
+        hyps = live_hyps(toks[b], L[b], S[b])
+        assert len(hyps) == wl.nbest
+        assert len({h for h, _ in hyps}) == len(hyps)                 # distinct
+        assert all(hyps[i][1] >= hyps[i + 1][1] for i in range(len(hyps) - 1))
+        for h, _ in hyps:
+            assert all(0 < c < wl.V for c in h)                       # blank-free, in range
+            assert len(h) <= nsel
+        assert np.logaddexp.reduce([s for _, s in hyps]) <= 1e-5      # total mass <= 1
+        for n in {len(h) for h, _ in hyps}:
+            assert np.logaddexp.reduce([s for h, s in hyps if len(h) == n]) <= 1e-5
+
+
+def test_streaming_equals_offline(oracle_lib):
+    lp, lens = synth.peaky(1, 70, 9, seed=4)
+    off = oracle_lib.decode(lp, lens, 6, 6, 0, 1.0, 70)
+    st = oracle_lib.Stream(6, 9, 0, capacity=4096)
+    for a in range(0, 70, 16):
+        st.feed(lp[0, a:a + 16])
+    t, l, s = st.read(6, 70)
+    assert (t == off[0][0]).all() and (l == off[1][0]).all() and (s == off[2][0]).all()
+
+
+def test_streaming_capacity_saturates(oracle_lib):
+    lp, lens = synth.peaky(1, 40, 9, seed=4)
+    st = oracle_lib.Stream(4, 9, 0, capacity=25)
+    assert st.feed(lp[0, :16]) == 16
+    assert st.feed(lp[0, 16:]) == 25  # frames past the capacity are ignored
+    off = oracle_lib.decode(lp, [25], 4, 4, 0, 1.0, 40)
+    t, l, s = st.read(4, 40)
+    assert (t == off[0][0]).all() and (s == off[2][0]).all()
+
+
+def test_fresh_stream_reads_empty(oracle_lib):
+    st = oracle_lib.Stream(3, 5, 0)
+    t, l, s = st.read(3, 4)
+    assert list(l) == [0, 0, 0] and s[0] == 0.0 and (s[1:] == NEG).all() and (t == -1).all()
