@@ -1,0 +1,213 @@
+"""Batched CTC prefix beam search on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libctcpb.so`` (C ABI in ``include/ctcpb.h``).  This
+module only marshals arguments: every step of the decode runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream.  If
+the library is missing the calls raise; there is no CPU fallback.
+
+The method and its options follow the page "GPU CTC Prefix Beam Search
+Decoder" (OASR documentation), sections 9-11: an offline batch decode and a
+streaming init / chunk / read-state lifecycle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libctcpb.so")
+
+FLAT, PAGED = 0, 1
+EXPORTS = ("ctcpb_workspace_size", "ctcpb_decode_offline", "ctcpb_state_size",
+           "ctcpb_stream_init", "ctcpb_stream_reset", "ctcpb_stream_chunk", "ctcpb_read_state",
+           "ctcpb_last_error", "ctcpb_version")
+
+
+class CtcpbConfig(ctypes.Structure):
+    _fields_ = [("beam", ctypes.c_int32), ("nbest", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("blank_id", ctypes.c_int32), ("blank_threshold", ctypes.c_float),
+                ("max_out_len", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("storage", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+@dataclass
+class DecoderConfig:
+    """Decoder options (the page's GpuDecoderConfig, sec. 10-11)."""
+    beam: int = 10
+    nbest: int | None = None
+    blank_id: int = 0
+    blank_threshold: float = 0.98
+    max_out_len: int | None = None
+    capacity: int = 0
+    paged: bool = False
+    page_size: int = 16
+    num_pages: int = 0
+
+    def c_struct(self, vocab: int, max_out_len: int) -> CtcpbConfig:
+        return CtcpbConfig(self.beam, self.nbest or self.beam, vocab, self.blank_id,
+                           float(self.blank_threshold), max_out_len, self.capacity,
+                           PAGED if self.paged else FLAT, self.page_size, self.num_pages)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with ctc_prefix_beam_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        cfgp = ctypes.POINTER(CtcpbConfig)
+        L.ctcpb_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
+        L.ctcpb_decode_offline.argtypes = [cfgp, p, i64, i64, i32, i32, p, p, sz, p, p, p, p]
+        L.ctcpb_state_size.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
+        L.ctcpb_stream_init.argtypes = [cfgp, p, sz, i32, p]
+        L.ctcpb_stream_reset.argtypes = [cfgp, p, sz, i32, p, i32, p]
+        L.ctcpb_stream_chunk.argtypes = [cfgp, p, sz, i32, p, i64, i64, i32, p, i32, p]
+        L.ctcpb_read_state.argtypes = [cfgp, p, sz, i32, p, i32, p, p, p, p]
+        for name in EXPORTS[:-2]:
+            getattr(L, name).restype = ctypes.c_int
+        L.ctcpb_last_error.restype = ctypes.c_char_p
+        L.ctcpb_last_error.argtypes = []
+        L.ctcpb_version.restype = ctypes.c_char_p
+        L.ctcpb_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        msg = lib().ctcpb_last_error().decode()
+        if rc == 1:
+            raise ValueError(msg)
+        raise RuntimeError(f"ctcpb error {rc}: {msg}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def workspace_size(cfg: DecoderConfig, vocab: int, batch: int, max_T: int,
+                   max_out_len: int | None = None) -> int:
+    out = ctypes.c_size_t()
+    c = cfg.c_struct(vocab, max_T if max_out_len is None else max_out_len)
+    _check(lib().ctcpb_workspace_size(ctypes.byref(c), batch, max_T, ctypes.byref(out)))
+    return out.value
+
+
+def state_size(cfg: DecoderConfig, vocab: int, num_streams: int) -> int:
+    out = ctypes.c_size_t()
+    c = cfg.c_struct(vocab, cfg.max_out_len or 0)
+    _check(lib().ctcpb_state_size(ctypes.byref(c), num_streams, ctypes.byref(out)))
+    return out.value
+
+
+class OfflineDecoder:
+    """Offline batch decode (sec. 3.7).  Holds a reusable device workspace."""
+
+    def __init__(self, cfg: DecoderConfig):
+        self.cfg = cfg
+        self.workspace = None
+
+    def decode(self, log_prob: torch.Tensor, seq_lengths: torch.Tensor, out=None, stream=None):
+        """log_prob: (B, T, V) float32 on the GPU, unit stride over V;
+        seq_lengths: (B,) int32 on the GPU.  Returns (tokens (B, N, max_out_len)
+        int32, lengths (B, N) int32, scores (B, N) float32) on the GPU."""
+        if log_prob.dtype != torch.float32 or log_prob.dim() != 3 or not log_prob.is_cuda:
+            raise ValueError("log_prob must be a 3-D float32 GPU tensor")
+        if log_prob.stride(2) != 1:
+            raise ValueError("log_prob must have unit stride over the vocabulary")
+        if seq_lengths.dtype != torch.int32 or seq_lengths.dim() != 1 or not seq_lengths.is_cuda:
+            raise ValueError("seq_lengths must be a 1-D int32 GPU tensor")
+        B, T, V = log_prob.shape
+        if seq_lengths.shape[0] != B:
+            raise ValueError("seq_lengths must have one entry per row")
+        cfg = self.cfg
+        N = cfg.nbest or cfg.beam
+        mol = T if cfg.max_out_len is None else cfg.max_out_len
+        c = cfg.c_struct(V, mol)
+        need = ctypes.c_size_t()
+        _check(lib().ctcpb_workspace_size(ctypes.byref(c), B, T, ctypes.byref(need)))
+        if self.workspace is None or self.workspace.numel() < need.value:
+            self.workspace = torch.empty(max(need.value, 1), dtype=torch.uint8,
+                                         device=log_prob.device)
+        if out is None:
+            out = (torch.empty((B, N, mol), dtype=torch.int32, device=log_prob.device),
+                   torch.empty((B, N), dtype=torch.int32, device=log_prob.device),
+                   torch.empty((B, N), dtype=torch.float32, device=log_prob.device))
+        toks, lens, scores = out
+        _check(lib().ctcpb_decode_offline(
+            ctypes.byref(c), _ptr(log_prob), log_prob.stride(0), log_prob.stride(1), B, T,
+            _ptr(seq_lengths), _ptr(self.workspace), self.workspace.numel(), _ptr(toks),
+            _ptr(lens), _ptr(scores), _stream(stream)))
+        return toks, lens, scores
+
+
+def decode_offline(log_prob, seq_lengths, **kw):
+    """One-shot offline decode; keyword arguments are DecoderConfig fields."""
+    return OfflineDecoder(DecoderConfig(**kw)).decode(log_prob, seq_lengths)
+
+
+class StreamPool:
+    """A device-resident state blob of `num_streams` independent streams
+    (sec. 8): init, chunk after chunk, read the N best at any time."""
+
+    def __init__(self, cfg: DecoderConfig, vocab: int, num_streams: int, device="cuda",
+                 stream=None):
+        self.cfg, self.vocab, self.num_streams = cfg, vocab, num_streams
+        self.max_out_len = cfg.max_out_len if cfg.max_out_len is not None else (
+            cfg.capacity or 4096)
+        self.c = cfg.c_struct(vocab, self.max_out_len)
+        need = ctypes.c_size_t()
+        _check(lib().ctcpb_state_size(ctypes.byref(self.c), num_streams, ctypes.byref(need)))
+        self.state = torch.empty(max(need.value, 1), dtype=torch.uint8, device=device)
+        self.nbytes = need.value
+        _check(lib().ctcpb_stream_init(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
+                                       num_streams, _stream(stream)))
+
+    def reset(self, rows: torch.Tensor | None = None, stream=None):
+        n = self.num_streams if rows is None else rows.numel()
+        _check(lib().ctcpb_stream_reset(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
+                                        self.num_streams, _ptr(rows), n, _stream(stream)))
+
+    def chunk(self, log_prob_chunk: torch.Tensor, rows: torch.Tensor | None = None, stream=None):
+        """log_prob_chunk: (n_rows, chunk_T, V) float32 on the GPU; row i
+        continues stream rows[i] (default: stream i)."""
+        if log_prob_chunk.dtype != torch.float32 or log_prob_chunk.dim() != 3:
+            raise ValueError("log_prob_chunk must be a 3-D float32 tensor")
+        if log_prob_chunk.stride(2) != 1:
+            raise ValueError("log_prob_chunk must have unit stride over the vocabulary")
+        n, T, V = log_prob_chunk.shape
+        if V != self.vocab:
+            raise ValueError("vocabulary size differs from the pool's")
+        if rows is not None and (rows.dtype != torch.int32 or rows.numel() != n):
+            raise ValueError("rows must be an int32 tensor with one entry per chunk row")
+        _check(lib().ctcpb_stream_chunk(
+            ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
+            _ptr(log_prob_chunk), log_prob_chunk.stride(0), log_prob_chunk.stride(1), T,
+            _ptr(rows), n, _stream(stream)))
+
+    def read(self, rows: torch.Tensor | None = None, stream=None):
+        n = self.num_streams if rows is None else rows.numel()
+        N = self.cfg.nbest or self.cfg.beam
+        dev = self.state.device
+        toks = torch.empty((n, N, self.max_out_len), dtype=torch.int32, device=dev)
+        lens = torch.empty((n, N), dtype=torch.int32, device=dev)
+        scores = torch.empty((n, N), dtype=torch.float32, device=dev)
+        _check(lib().ctcpb_read_state(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
+                                      self.num_streams, _ptr(rows), n, _ptr(toks), _ptr(lens),
+                                      _ptr(scores), _stream(stream)))
+        return toks, lens, scores

@@ -1,0 +1,1524 @@
+// ctcpb.hip -- batched CTC prefix beam search for gfx950 (MI355X), and the C
+// ABI declared in include/ctcpb.h.
+//
+// Method: the page "GPU CTC Prefix Beam Search Decoder" (OASR docs).  Every
+// step of its pipeline is computed here, but not with its kernels:
+//
+//   select_kernel   frame filter, sec. 3.5 (one block per row, ordered
+//                   ballot compaction instead of a block scan).
+//   decode_kernel   one wave per row (offline) or stream, the whole frame loop
+//                   in-kernel (the idea of sec. 3.4.8): per frame
+//     - stage the frame's log-probabilities in LDS (the next frame is loaded
+//       into registers while this one is decoded);
+//     - vocabulary top-K (sec. 3.3 step 0, sec. 3.4.7): the best 2W+3
+//       non-blank labels by (log-prob desc, label asc), wave64 bitonic sort;
+//     - step 0 seeding (sec. 3.3) from that list;
+//     - steps >= 1: the beam x vocab extension scores of sec. 3.4.1/3.4.2
+//       are never materialised.  An ordinary label c of beam k scores
+//       lp[c] + logsumexp(pb, pnb) (sec. 3.4.6), so only the ranked labels
+//       plus each beam's blank and repeated-label slots can reach the top W;
+//       the merge of sec. 3.4.3 folds a parent's (i, last label of j)
+//       extension into child j's blank slot and removes it from i's list;
+//       the top W by (score desc, k*V + c asc) is taken with a register
+//       bitonic sort of the few candidates above a provable lower bound, and
+//       an exactness test falls back to the full beam x vocab selection
+//       whenever a label outside the ranked list could still tie or win;
+//     - state update (sec. 3.4.5): new (pb, pnb), length, last label, and the
+//       token store: flat double-buffered lists (sec. 3.1, 7) or pages with
+//       reference-counted sharing (sec. 3.4.5 paged variant, 4.2).
+//   Prefix identity for the merge is tracked structurally: every beam knows
+//   which live beam is its prefix minus the last label ("parent"), derived
+//   from how the winners were formed; the one case the structure cannot
+//   decide (a parent prefix re-created from its own parent) is settled by a
+//   64-bit prefix hash filter and an exact token comparison.
+//
+// Numerics: float32, one rounding per operation, no contraction; exp / log1p
+// are fixed operation sequences (device_math.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+#include <mutex>
+#include <string>
+
+#include "../../include/ctcpb.h"
+#include "device_math.h"
+#include "layout.h"
+#include "wave_ops.h"
+
+namespace ctcpb {
+
+constexpr int kMaxVocab = 16384;
+constexpr int kMaxK = 2 * kMaxBeam + 3;   // ranked labels kept per frame
+constexpr int kBuf = 256;                 // candidate buffer (keys)
+constexpr int kPrefetch4 = 20;            // float4 per lane held for the next frame
+constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
+constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
+
+// LDS carve-up (byte offsets), computed on the host from the dimensions.
+struct LdsPlan {
+  int row0, row1, rank, Rc, Rl, buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh,
+      newlen, nchild, childc, scal, tab, ref, fstk, tail, total;
+};
+
+struct Params {
+  Layout L;
+  LdsPlan S;
+  int N, max_out_len;
+  int sel_mode;       // offline frame filter: 0 keep all, 1 keep none, 2 threshold
+  float log_thr;
+  const float* lp;
+  int64_t stride_b, stride_t;
+  int T;              // offline: max_T; streaming: chunk_T
+  int num_rows;       // streaming: streams in the blob
+  const int* seq_lengths;
+  const int* rows;
+  char* state;
+  int* out_tokens;
+  int* out_lengths;
+  float* out_scores;
+  int vec4;           // frame rows are 16-byte aligned and V % 4 == 0
+};
+
+// Per-row scalars kept in LDS while a row is decoded (mirrors of header fields).
+enum : int {
+  kScalFreeTop = 0, kScalNextFree, kScalStatus, kScalHigh, kScalLive0, kScalLive1, kScalCpl0,
+  kScalCpl1, kScalPcp0, kScalPcp1, kScalFallbacks, kScalVerifies, kScalCount
+};
+
+struct Beam {
+  int live;
+  float pb, pnb, score;
+  int len, last, parent, last2;
+  uint64_t h, hp;
+};
+
+struct Ctx {
+  const Params* P;
+  char* base;
+  int* hdr;
+  float* row[2];
+  int8_t* rank;
+  int* Rc;
+  float* Rl;
+  uint64_t* buf;
+  float* A;      // per beam: logsumexp(pb, pnb) after the gap collapse (NEG if dead)
+  float* kb;     // per beam: key of the blank slot (after the merge fold)
+  float* kc;     // per beam: key of the repeated-label slot (NEG if none / merged away)
+  int* lastk;    // per beam: last label
+  int* offs;
+  uint32_t* exm;
+  int* exclast;
+  int* bslot;
+  int* htab;
+  uint64_t* newh;
+  int* newlen;
+  int* nchild;
+  int* childc;
+  int* scal;
+  int* tab;       // paged: LDS copy of both block-table parities
+  int* ref;
+  int* fstk;
+  int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
+  int* clist;     // flat: global
+  int* pages;     // paged: global
+};
+
+// LDS-only ordering between the lanes of this wave (no wait on global memory).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, int slot, int pos) {
+  const Layout& L = C.P->L;
+  if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.cap + pos];
+  const int page = tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
+  if (page < 0) return -1;  // only after a row ran out of pages
+  return C.pages[(int64_t)page * L.ps + pos % L.ps];
+}
+
+// ----------------------------------------------------------------- frames --
+__device__ __forceinline__ void load_row_now(const float* g, float* s, int V, int vec4) {
+  const int lane = lane_id();
+  if (vec4) {
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    float4* s4 = reinterpret_cast<float4*>(s);
+    for (int i = lane; i < (V >> 2); i += kWave) s4[i] = g4[i];
+  } else {
+    for (int i = lane; i < V; i += kWave) s[i] = g[i];
+  }
+}
+
+struct RowPrefetch {
+  float4 v[kPrefetch4];
+  const float* g;
+  int active;
+};
+
+__device__ __forceinline__ void prefetch_issue(RowPrefetch& pf, const float* g, int V, int vec4) {
+  const int lane = lane_id();
+  pf.g = g;
+  pf.active = (g != nullptr) && vec4 && (V >> 2) <= kPrefetch4 * kWave;
+  if (pf.active) {
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    const int n4 = V >> 2;
+#pragma unroll
+    for (int j = 0; j < kPrefetch4; j++) {
+      const int i = lane + j * kWave;
+      if (i < n4) pf.v[j] = g4[i];
+    }
+  }
+}
+
+__device__ __forceinline__ void prefetch_commit(RowPrefetch& pf, float* s, int V, int vec4) {
+  if (pf.g == nullptr) return;
+  if (pf.active) {
+    const int lane = lane_id();
+    float4* s4 = reinterpret_cast<float4*>(s);
+    const int n4 = V >> 2;
+#pragma unroll
+    for (int j = 0; j < kPrefetch4; j++) {
+      const int i = lane + j * kWave;
+      if (i < n4) s4[i] = pf.v[j];
+    }
+  } else {
+    load_row_now(pf.g, s, V, vec4);
+  }
+}
+
+// ------------------------------------------------------ generic selection --
+// Keeps the best `K` (K <= 128) keys of a stream in C.buf.  Keys must be
+// distinct or 0 (= no candidate).  Items are produced 64 at a time by gen(i)
+// for i in [0, n); the buffer is sorted and cut back to K whenever it fills.
+template <typename Gen>
+__device__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
+  const int lane = lane_id();
+  uint64_t thr = comp_floor();
+  int cnt = 0;
+  for (int64_t base = 0; base < n; base += kWave) {
+    const int64_t i = base + lane;
+    const uint64_t x = i < n ? gen(i) : 0ull;
+    const bool pass = x > thr;
+    const uint64_t m = __ballot(pass);
+    if (pass) C.buf[cnt + lanes_below(m)] = x;
+    cnt += __popcll(m);
+    if (cnt > kBuf - kWave) {
+      lds_sync();
+      wave_sort_lds(C.buf, cnt);
+      lds_sync();
+      cnt = cnt < K ? cnt : K;
+      if (cnt == K) thr = C.buf[K - 1];
+    }
+  }
+  lds_sync();
+  wave_sort_lds(C.buf, cnt);
+  lds_sync();
+  return cnt < K ? cnt : K;
+}
+
+// ------------------------------------------------------- vocabulary top-K --
+// The best K non-blank labels of the frame by (lp desc, label asc), written to
+// Rc / Rl; rank[label] = position (or -1).  prevK = size of the previous list.
+__device__ void vocab_topk(const Ctx& C, const float* row, int K, int prevK) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int V = L.V, blank = L.blank;
+  const int n = V - 1;
+  for (int r = lane; r < prevK; r += kWave) C.rank[C.Rc[r]] = -1;
+  auto comp = [&](int i) -> uint64_t {
+    const int c = i + (i >= blank ? 1 : 0);
+    return compose(row[c], (uint32_t)c);
+  };
+  int got;
+  if (n <= kBuf) {
+    for (int i = lane; i < n; i += kWave) C.buf[i] = comp(i);
+    lds_sync();
+    wave_sort_lds(C.buf, n);
+    lds_sync();
+    got = n < K ? n : K;
+  } else {
+    // pass 1: the two best keys of every lane; the K-th best of those 128
+    // is a lower bound of the frame's K-th best key (K <= 128)
+    uint64_t a = 0, b = 0;
+    for (int i = lane; i < n; i += kWave) {
+      const uint64_t x = comp(i);
+      const uint64_t lo = x < a ? x : a;
+      a = x > a ? x : a;
+      b = lo > b ? lo : b;
+    }
+    uint64_t v[2] = {a, b};
+    wave_sort_desc<2>(v);
+    const int pos = K - 1;
+    const uint64_t vsel = (pos & 1) ? v[1] : v[0];
+    const uint64_t thr = shfl_u64(vsel, pos >> 1);
+    // pass 2: gather every key >= thr
+    int cnt = 0;
+    for (int base = 0; base < n; base += kWave) {
+      const int i = base + lane;
+      const uint64_t x = i < n ? comp(i) : 0ull;
+      const bool pass = x >= thr && x != 0ull;
+      const uint64_t m = __ballot(pass);
+      const int p = cnt + lanes_below(m);
+      if (pass && p < kBuf) C.buf[p] = x;
+      cnt += __popcll(m);
+    }
+    lds_sync();
+    if (cnt <= kBuf) {
+      wave_sort_lds(C.buf, cnt);
+      lds_sync();
+      got = K;
+    } else {
+      got = stream_topk(C, K, n, comp);
+    }
+  }
+  for (int r = lane; r < got; r += kWave) {
+    const int c = (int)comp_id(C.buf[r]);
+    C.Rc[r] = c;
+    C.Rl[r] = row[c];
+    C.rank[c] = (int8_t)r;
+  }
+  lds_sync();
+}
+
+// --------------------------------------------------------------- step 0 ----
+__device__ void first_step(const Ctx& C, Beam& b, const float* row, int g, int nR) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int W = L.W, blank = L.blank;
+  const int nb = W > 1 ? W - 1 : 1;
+  const int m = nb < nR ? nb : nR;
+  b.live = 0;
+  b.len = 0;
+  b.last = blank;
+  b.parent = -1;
+  b.last2 = -1;
+  b.pb = b.pnb = b.score = kNeg;
+  b.h = kHashEmpty;
+  b.hp = 0;
+  if (lane < m) {
+    const int c = C.Rc[lane];
+    const float key = C.Rl[lane];
+    b.live = 1;
+    b.len = 1;
+    b.last = c;
+    b.score = key;
+    if (g) {
+      b.pb = key;
+      b.pnb = kNeg;
+    } else {
+      b.pb = kNeg;
+      b.pnb = key;
+    }
+    b.h = hash_push(kHashEmpty, c);
+    b.hp = kHashEmpty;
+    b.parent = W > 1 ? W - 1 : -1;
+  }
+  if (W > 1 && lane == W - 1) {
+    b.live = 1;
+    b.pb = row[blank];
+    b.score = row[blank];
+  }
+  // token store, parity 0
+  if (!L.paged) {
+    if (lane < m) C.clist[(int64_t)lane * L.cap] = b.last;
+  } else {
+    // one fresh page per seeded label
+    const bool want = lane < m;
+    const uint64_t mk = __ballot(want);
+    const int idx = lanes_below(mk);
+    const int nw = __popcll(mk);
+    const int avail = C.scal[kScalFreeTop];
+    const int nf = C.scal[kScalNextFree];
+    int page = kInvalidPage;
+    if (want) {
+      if (idx < avail) page = C.fstk[avail - 1 - idx];
+      else if (nf + idx - avail < L.npages) page = nf + idx - avail;
+    }
+    lds_sync();
+    if (lane == 0) {
+      const int pops = nw < avail ? nw : avail;
+      C.scal[kScalFreeTop] = avail - pops;
+      int nn = nf + (nw - pops);
+      C.scal[kScalNextFree] = nn < L.npages ? nn : L.npages;
+    }
+    if (want) {
+      if (page == kInvalidPage) {
+        atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
+      } else {
+        C.ref[page] = 1;
+        C.tab[(0 * W + lane) * L.max_lp + 0] = page;
+        C.pages[(int64_t)page * L.ps] = b.last;
+        C.tail[(0 * W + lane) * L.ps] = b.last;
+      }
+    }
+  }
+}
+
+
+// ------------------------------------------------------------ steps >= 1 ---
+// Winner of output slot `lane` (valid lanes < W): source beam k, label c.
+struct Winner {
+  bool valid;
+  int k, c, len_k;
+};
+
+// The full beam x vocab selection (exact for any input): every candidate of
+// the step is regenerated from the per-beam values left in LDS and streamed
+// through stream_topk.  Used when the pruned candidate set cannot be proven
+// to contain the top W.
+__device__ int full_select(const Ctx& C, const float* row) {
+  const Layout& L = C.P->L;
+  const int W = L.W, V = L.V, blank = L.blank;
+  auto gen = [&](int64_t i) -> uint64_t {
+    const int k = (int)(i / V);
+    const int c = (int)(i - (int64_t)k * V);
+    const float A = C.A[k];
+    if (!(A > kNeg)) return 0ull;
+    float key;
+    if (c == blank) {
+      key = C.kb[k];
+    } else if (c == C.lastk[k]) {
+      key = C.kc[k];
+    } else {
+      const int nc = C.nchild[k];
+      for (int j = 0; j < nc; j++)
+        if (C.childc[k * kMaxBeam + j] == c) return 0ull;
+      key = row[c] + A;
+    }
+    return key > kNeg ? compose(key, (uint32_t)i) : 0ull;
+  };
+  return stream_topk(C, W, (int64_t)W * V, gen);
+}
+
+__device__ Winner beam_step(const Ctx& C, Beam& b, const float* row, int g, int step, int nR,
+                            int complete) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int W = L.W, V = L.V, blank = L.blank;
+  const bool lv = lane < W && b.live;
+
+  // collapsed-blank correction for skipped frames (sec. 3.4), then A_k
+  float pb1 = b.pb, pnb1 = b.pnb;
+  if (lv && g) {
+    pb1 = lse(b.pb, b.pnb);
+    pnb1 = kNeg;
+  }
+  const float A = lv ? lse(pb1, pnb1) : kNeg;
+  const int last = b.last;
+  const float lpc = (lv && last != blank) ? row[last] : kNeg;
+  const float lpb = row[blank];
+  // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
+  const float ptb = lv ? lpb + A : kNeg;
+  float ptnb = (lv && !g && last != blank) ? lpc + pnb1 : kNeg;
+  // merge (sec. 3.4.3): beam j = parent i + `last`; i's extension by `last`
+  // is folded into j's blank slot
+  const int par = lv ? b.parent : -1;
+  const int src = par >= 0 ? par : lane;
+  const float A_par = __shfl(A, src, 64);
+  const float pb1_par = __shfl(pb1, src, 64);
+  const int last_par = __shfl(last, src, 64);
+  if (par >= 0) {
+    const float from_parent = (last == last_par) ? lpc + pb1_par : lpc + A_par;
+    ptnb = lse(ptnb, from_parent);
+  }
+  const float keyb = lv ? lse(ptb, ptnb) : kNeg;
+
+  // labels removed from a beam's ordinary list: its own last label (that is
+  // the repeated-label slot) and the last label of each child (merged away)
+  if (lane < W) {
+    C.exm[lane * 3 + 0] = 0u;
+    C.exm[lane * 3 + 1] = 0u;
+    C.exm[lane * 3 + 2] = 0u;
+    C.exclast[lane] = 0;
+    C.nchild[lane] = 0;
+  }
+  lds_sync();
+  if (par >= 0) {
+    if (last == last_par) {
+      C.exclast[par] = 1;
+    } else {
+      const int rr = C.rank[last];
+      if (rr >= 0) atomicOr(&C.exm[par * 3 + (rr >> 5)], 1u << (rr & 31));
+    }
+    const int pos = atomicAdd(&C.nchild[par], 1);
+    C.childc[par * kMaxBeam + pos] = last;
+  }
+  if (lv && last != blank) {
+    const int rr = C.rank[last];
+    if (rr >= 0) atomicOr(&C.exm[lane * 3 + (rr >> 5)], 1u << (rr & 31));
+  }
+  lds_sync();
+  const bool rep_ok = lv && last != blank && C.exclast[lane] == 0;
+  const float keyc = rep_ok ? lpc + pb1 : kNeg;
+  if (lane < W) {
+    C.A[lane] = A;
+    C.kb[lane] = keyb;
+    C.kc[lane] = keyc;
+    C.lastk[lane] = last;
+  }
+
+  // a lower bound tau0 of the W-th best key: beam k's first W ordinary labels
+  // all score at least A_k + Rl[W - 1 + excluded_k]
+  const int nPool = complete ? nR : nR - 1;
+  int nEx = 0;
+  if (lv) {
+#pragma unroll
+    for (int w = 0; w < 3; w++) {
+      uint32_t m = C.exm[lane * 3 + w];
+      const int lo = w * 32;
+      if (lo >= nPool) m = 0u;
+      else if (nPool - lo < 32) m &= (1u << (nPool - lo)) - 1u;
+      nEx += __popc(m);
+    }
+  }
+  const int idx = W - 1 + nEx;
+  const float t0 = (lv && idx < nPool) ? C.Rl[idx] + A : kNeg;
+  const float tau0 = wave_max(t0);
+  // ranked labels of each beam scoring >= tau0 form a prefix of the list
+  int lo = 0, hi = lv ? nPool : 0;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (C.Rl[mid] + A >= tau0) lo = mid + 1;
+    else hi = mid;
+  }
+  const int nk = lo;
+  const int incl = wave_incl_scan(lane < W ? nk : 0);
+  const int M = __shfl(incl, 63, 64);
+  if (lane < W) C.offs[lane] = incl - nk;
+  const bool sb = keyb > kNeg && keyb >= tau0;
+  const bool sc = keyc > kNeg && keyc >= tau0;
+  lds_sync();
+
+  bool need_full = M + 2 * W > kBuf;
+  if (!need_full) {
+    for (int q = lane; q < M; q += kWave) {
+      int a = 0, z = W - 1;
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (C.offs[mid] <= q) a = mid;
+        else z = mid - 1;
+      }
+      const int rho = q - C.offs[a];
+      const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
+      const int c = C.Rc[rho];
+      C.buf[q] = ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + c));
+    }
+    if (lane < W) {
+      C.buf[M + 2 * lane] = sb ? compose(keyb, (uint32_t)(lane * V + blank)) : 0ull;
+      C.buf[M + 2 * lane + 1] = sc ? compose(keyc, (uint32_t)(lane * V + last)) : 0ull;
+    }
+    lds_sync();
+    wave_sort_lds(C.buf, M + 2 * W);
+    lds_sync();
+    if (!complete) {
+      // labels outside the ranked list score at most A_k + (last ranked lp);
+      // they must stay strictly below the W-th selected key
+      const uint64_t wl = C.buf[W - 1];
+      const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
+      const float bound = C.Rl[nR - 1];
+      const bool bad = lv && !((bound + A) < keyW);
+      need_full = __ballot(bad) != 0ull;
+    }
+  }
+  if (need_full) {
+    full_select(C, row);
+    if (lane == 0) C.scal[kScalFallbacks] += 1;
+  }
+
+  // winners in rank order (slot r = rank r), sec. 3.4.5
+  const uint64_t wc = lane < W ? C.buf[lane] : 0ull;
+  Winner w;
+  w.valid = lane < W && wc > comp_floor();
+  const uint32_t id = comp_id(wc);
+  w.k = w.valid ? (int)(id / (uint32_t)V) : lane;
+  w.c = w.valid ? (int)(id - (uint32_t)w.k * (uint32_t)V) : blank;
+  const float key = comp_key(wc);
+  const int k = w.k & 63;
+  const float ptb_k = __shfl(ptb, k, 64);
+  const float ptnb_k = __shfl(ptnb, k, 64);
+  const int len_k = __shfl(b.len, k, 64);
+  const int last_k = __shfl(last, k, 64);
+  const int par_k = __shfl(b.parent, k, 64);
+  const int last2_k = __shfl(b.last2, k, 64);
+  const uint64_t h_k = shfl_u64(b.h, k);
+  const uint64_t hp_k = shfl_u64(b.hp, k);
+  w.len_k = len_k;
+  const bool ext = w.valid && w.c != blank;
+  Beam nb;
+  nb.live = w.valid ? 1 : 0;
+  nb.len = w.valid ? len_k + (ext ? 1 : 0) : 0;
+  nb.last = ext ? w.c : (w.valid ? last_k : blank);
+  nb.last2 = ext ? (len_k >= 1 ? last_k : -1) : (w.valid ? last2_k : -1);
+  nb.h = ext ? hash_push(h_k, w.c) : (w.valid ? h_k : kHashEmpty);
+  nb.hp = ext ? h_k : (w.valid ? hp_k : 0ull);
+  nb.score = w.valid ? key : kNeg;
+  if (!w.valid) {
+    nb.pb = kNeg;
+    nb.pnb = kNeg;
+  } else if (g) {
+    nb.pb = key;
+    nb.pnb = kNeg;
+  } else if (w.c == blank) {
+    nb.pb = ptb_k;
+    nb.pnb = ptnb_k;
+  } else {
+    nb.pb = kNeg;
+    nb.pnb = key;
+  }
+
+  // parent slots of the new beams (the prefix one label shorter, if live)
+  if (lane < W) C.bslot[lane] = -1;
+  C.htab[lane] = -1;
+  lds_sync();
+  if (w.valid && w.c == blank) C.bslot[w.k] = lane;
+  if (lane < W) {
+    C.newh[lane] = nb.h;
+    C.newlen[lane] = nb.len;
+  }
+  lds_sync();
+  if (ext) {
+    int s = (int)((uint32_t)nb.h & 63u);
+    while (atomicCAS(&C.htab[s], -1, lane) != -1) s = (s + 1) & 63;
+  }
+  lds_sync();
+  int npar = -1, cand = -1;
+  if (ext) {
+    npar = C.bslot[w.k];
+  } else if (w.valid) {
+    if (par_k >= 0) {
+      npar = C.bslot[par_k];
+    } else if (len_k >= 2) {
+      // the parent prefix may have just been re-created from its own parent
+      int s = (int)((uint32_t)hp_k & 63u);
+      for (int probe = 0; probe < 64; probe++) {
+        const int e = C.htab[s];
+        if (e < 0) break;
+        if (C.newh[e] == hp_k && C.newlen[e] == len_k - 1) {
+          cand = e;
+          break;
+        }
+        s = (s + 1) & 63;
+      }
+    }
+  }
+  const int ce = cand >= 0 ? cand : lane;
+  const int k2 = __shfl(w.k, ce, 64);
+  const int c2 = __shfl(w.c, ce, 64);
+  if (cand >= 0 && c2 != last2_k) cand = -1;
+  uint64_t todo = __ballot(cand >= 0);
+  if (todo) {
+    wave_sync();  // the previous step's tokens are in memory
+    const int q = (step - 1) & 1;
+    const int from = C.scal[kScalCpl0 + q];
+    while (todo) {
+      const int v = __ffsll((long long)todo) - 1;
+      todo &= todo - 1;
+      const int ka = __shfl(w.k, v, 64);
+      const int kb2 = __shfl(k2, v, 64);
+      const int n = __shfl(len_k, v, 64) - 2;
+      bool eq = true;
+      for (int p = from + lane; p < n; p += kWave)
+        eq = eq && tok_at(C, C.tab, q, ka, p) == tok_at(C, C.tab, q, kb2, p);
+      const bool all = __ballot(!eq) == 0ull;
+      if (lane == v && all) npar = cand;
+      if (lane == 0) C.scal[kScalVerifies] += 1;
+    }
+  }
+  nb.parent = npar;
+  if (lane < W) b = nb;
+  return w;
+}
+
+// ------------------------------------------------------------ token stores --
+// Flat (sec. 3.1, 7): slot r of parity p receives its source's tokens from
+// parity p^1 plus the new label.  Positions below the common prefix that all
+// live beams of two steps ago shared are already in place and are skipped.
+__device__ void store_flat(const Ctx& C, int step, const Winner& w) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int W = L.W, blank = L.blank;
+  const int p = step & 1, q = p ^ 1;
+  const uint32_t live2 = (uint32_t)C.scal[kScalLive0 + p];
+  const int cplp = C.scal[kScalCpl0 + p];
+  const int start = w.valid ? (((live2 >> lane) & 1u) ? cplp : 0) : 0;
+  const int cnt = w.valid ? w.len_k - start : 0;
+  const int incl = wave_incl_scan(lane < W ? cnt : 0);
+  const int total = __shfl(incl, 63, 64);
+  int* offs = C.offs;            // [0, 33): offsets; [40, 72): starts; [80, 112): sources
+  if (lane < W) {
+    offs[lane] = incl - cnt;
+    offs[40 + lane] = start;
+    offs[80 + lane] = w.k;
+  }
+  lds_sync();
+  int* clist = C.clist;
+  const int64_t cap = L.cap;
+  for (int base = 0; base < total; base += 8 * kWave) {
+    int val[8];
+    int64_t dst[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int i = base + u * kWave + lane;
+      dst[u] = -1;
+      if (i < total) {
+        int a = 0, z = W - 1;
+        while (a < z) {
+          const int mid = (a + z + 1) >> 1;
+          if (offs[mid] <= i) a = mid;
+          else z = mid - 1;
+        }
+        const int pos = offs[40 + a] + (i - offs[a]);
+        val[u] = clist[((int64_t)(q * W + offs[80 + a])) * cap + pos];
+        dst[u] = ((int64_t)(p * W + a)) * cap + pos;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++)
+      if (dst[u] >= 0) clist[dst[u]] = val[u];
+  }
+  if (w.valid && w.c != blank) clist[((int64_t)(p * W + lane)) * cap + w.len_k] = w.c;
+  const uint64_t vm = __ballot(w.valid);
+  lds_sync();
+  if (lane == 0) {
+    C.scal[kScalLive0 + p] = (int)(uint32_t)vm;
+    C.scal[kScalCpl0 + p] = C.scal[kScalCpl0 + q];
+  }
+  lds_sync();
+}
+
+// Grow the common prefix of the live beams of parity p (flat store), reading
+// the next 64 positions of every live row.
+__device__ void advance_cpl_flat(const Ctx& C, int p, const Beam& b) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int W = L.W;
+  wave_sync();
+  const int cpl = C.scal[kScalCpl0 + p];
+  const uint64_t live = __ballot(lane < W && b.live);
+  if (live == 0ull) return;
+  int minlen = lane < W && b.live ? b.len : 0x7fffffff;
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) minlen = min(minlen, __shfl_xor(minlen, m, 64));
+  const int pos = cpl + lane;
+  const bool inside = pos < minlen;
+  int tk[kMaxBeam];
+#pragma unroll
+  for (int r = 0; r < kMaxBeam; r++)
+    tk[r] = (inside && ((live >> r) & 1ull)) ? C.clist[((int64_t)(p * W + r)) * L.cap + pos] : -3;
+  const int first = __ffsll((long long)live) - 1;
+  int ref = -3;
+#pragma unroll
+  for (int r = 0; r < kMaxBeam; r++)
+    if (r == first) ref = tk[r];
+  bool same = inside;
+#pragma unroll
+  for (int r = 0; r < kMaxBeam; r++)
+    if ((live >> r) & 1ull) same = same && tk[r] == ref;
+  const uint64_t ok = __ballot(same);
+  const int adv = ok == ~0ull ? 64 : __ffsll((long long)~ok) - 1;
+  if (lane == 0) C.scal[kScalCpl0 + p] = cpl + adv;
+  lds_sync();
+}
+
+// Paged (sec. 3.4.5 paged variant, 4.2): fork every slot's block-table row
+// from its source (pages acquired / released by reference count), then
+// append the new label on a fresh page or a copy of the shared partial page.
+__device__ void store_paged(const Ctx& C, int step, const Winner& w, const Beam& nb) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
+  const int p = step & 1, q = p ^ 1;
+  const uint32_t live2 = (uint32_t)C.scal[kScalLive0 + p];
+  const int pcpp = C.scal[kScalPcp0 + p];
+  // pass 1: fork
+  if (lane < W) {
+    int* drow = C.tab + (p * W + lane) * max_lp;
+    const int* srow = C.tab + (q * W + w.k) * max_lp;
+    const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
+    for (int qq = ((live2 >> lane) & 1u) ? pcpp : 0; qq < max_lp; qq++) {
+      const int old = drow[qq];
+      const int nw = qq < np_new ? srow[qq] : kInvalidPage;
+      if (old == kInvalidPage && nw == kInvalidPage) break;
+      if (old != nw) {
+        if (nw != kInvalidPage) atomicAdd(&C.ref[nw], 1);
+        if (old != kInvalidPage && atomicSub(&C.ref[old], 1) == 1) {
+          const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
+          if (at < L.npages) C.fstk[at] = old;
+        }
+        drow[qq] = nw;
+      }
+    }
+    if (w.valid) {
+      const int* st = C.tail + (q * W + w.k) * ps;
+      int* dt = C.tail + (p * W + lane) * ps;
+      const int off = w.len_k % ps;
+      for (int j = 0; j < off; j++) dt[j] = st[j];
+    }
+  }
+  lds_sync();
+  // pass 2: append
+  const bool ext = w.valid && w.c != blank;
+  const int off = w.len_k % ps;
+  const int qq = w.len_k / ps;
+  int phys = kInvalidPage;
+  bool inplace = false;
+  if (ext && off != 0) {
+    phys = C.tab[(p * W + lane) * max_lp + qq];
+    inplace = phys >= 0 && C.ref[phys] == 1;
+  }
+  const bool need = ext && !inplace;
+  const uint64_t mk = __ballot(need);
+  const int idx = lanes_below(mk);
+  const int nw = __popcll(mk);
+  const int avail = C.scal[kScalFreeTop];
+  const int nf = C.scal[kScalNextFree];
+  int page = kInvalidPage;
+  if (need) {
+    if (idx < avail) page = C.fstk[avail - 1 - idx];
+    else if (nf + idx - avail < L.npages) page = nf + idx - avail;
+  }
+  lds_sync();
+  if (lane == 0) {
+    const int pops = nw < avail ? nw : avail;
+    C.scal[kScalFreeTop] = avail - pops;
+    const int nn = nf + (nw - pops);
+    C.scal[kScalNextFree] = nn < L.npages ? nn : L.npages;
+  }
+  lds_sync();
+  bool push_old = false;
+  int* dt = C.tail + (p * W + lane) * ps;
+  if (need) {
+    if (page == kInvalidPage) {
+      atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
+    } else {
+      C.ref[page] = 1;
+      const int64_t g = (int64_t)page * ps;
+      for (int j = 0; j < off; j++) C.pages[g + j] = dt[j];
+      C.pages[g + off] = w.c;
+      C.tab[(p * W + lane) * max_lp + qq] = page;
+      if (off != 0 && phys >= 0) push_old = atomicSub(&C.ref[phys], 1) == 1;
+      dt[off] = w.c;
+    }
+  } else if (inplace) {
+    C.pages[(int64_t)phys * ps + off] = w.c;
+    dt[off] = w.c;
+  }
+  lds_sync();
+  if (push_old) {
+    const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
+    if (at < L.npages) C.fstk[at] = phys;
+  }
+  const uint64_t vm = __ballot(w.valid);
+  lds_sync();
+  if (lane == 0) {
+    C.scal[kScalLive0 + p] = (int)(uint32_t)vm;
+    const int used = C.scal[kScalNextFree] - C.scal[kScalFreeTop];
+    if (used > C.scal[kScalHigh]) C.scal[kScalHigh] = used;
+  }
+  // leading full pages shared by every live row of parity p
+  int pcp = C.scal[kScalPcp0 + q];
+  const bool lv = lane < W && nb.live;
+  const uint64_t lm = __ballot(lv);
+  const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
+  while (lm != 0ull && pcp < max_lp) {
+    const bool full = !lv || nb.len >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
+    const int e = (lv && full) ? C.tab[(p * W + lane) * max_lp + pcp] : kInvalidPage;
+    const int first = __shfl(e, first_live, 64);
+    const bool ok = full && (!lv || e == first);
+    if (__ballot(!ok) != 0ull) break;
+    pcp++;
+  }
+  lds_sync();
+  if (lane == 0) C.scal[kScalPcp0 + p] = pcp;
+  lds_sync();
+}
+
+// ------------------------------------------------------------------ output --
+// N best of the current beams, (score desc, slot asc), tokens of `parity`.
+__device__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int* tab,
+                              int out_row) {
+  const Layout& L = C.P->L;
+  const Params& P = *C.P;
+  const int lane = lane_id();
+  const int W = L.W, N = P.N, mol = P.max_out_len;
+  const bool lv = lane < W && b.live;
+  int rk = 0;
+  for (int j = 0; j < W; j++) {
+    const float sj = __shfl(b.score, j, 64);
+    const int lj = __shfl(lv ? 1 : 0, j, 64);
+    if (lj && (sj > b.score || (sj == b.score && j < lane))) rk++;
+  }
+  int* slot_of = C.offs;  // rank -> slot (or -1)
+  if (lane < N) slot_of[lane] = -1;
+  lds_sync();
+  if (lv && rk < N) slot_of[rk] = lane;
+  lds_sync();
+  const int s = lane < N ? slot_of[lane] : -1;
+  const int len = __shfl(b.len, s < 0 ? 0 : s, 64);
+  const float sc = __shfl(b.score, s < 0 ? 0 : s, 64);
+  if (lane < N) {
+    P.out_lengths[(int64_t)out_row * N + lane] = s < 0 ? 0 : len;
+    P.out_scores[(int64_t)out_row * N + lane] = s < 0 ? kNeg : sc;
+    slot_of[40 + lane] = s < 0 ? 0 : len;
+  }
+  lds_sync();
+  int* ot = P.out_tokens + (int64_t)out_row * N * mol;
+  const int total = N * mol;
+  for (int base = 0; base < total; base += 8 * kWave) {
+    int val[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int i = base + u * kWave + lane;
+      val[u] = -1;
+      if (i < total) {
+        const int n = i / mol, pos = i - n * mol;
+        const int s = slot_of[n];
+        if (s >= 0 && pos < slot_of[40 + n]) val[u] = tok_at(C, tab, parity, s, pos);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const int i = base + u * kWave + lane;
+      if (i < total) ot[i] = val[u];
+    }
+  }
+}
+
+// ---------------------------------------------------------- state helpers --
+__device__ void beam_load(const Ctx& C, Beam& b) {
+  const int lane = lane_id();
+  const char* a = C.base + C.P->L.o_beam;
+  if (lane < kMaxBeam) {
+    b.pb = reinterpret_cast<const float*>(a + BeamArrays::pb)[lane];
+    b.pnb = reinterpret_cast<const float*>(a + BeamArrays::pnb)[lane];
+    b.score = reinterpret_cast<const float*>(a + BeamArrays::score)[lane];
+    b.len = reinterpret_cast<const int*>(a + BeamArrays::len)[lane];
+    b.last = reinterpret_cast<const int*>(a + BeamArrays::last)[lane];
+    b.parent = reinterpret_cast<const int*>(a + BeamArrays::parent)[lane];
+    b.last2 = reinterpret_cast<const int*>(a + BeamArrays::last2)[lane];
+    b.live = reinterpret_cast<const int*>(a + BeamArrays::live)[lane];
+    b.h = reinterpret_cast<const uint64_t*>(a + BeamArrays::hash)[lane];
+    b.hp = reinterpret_cast<const uint64_t*>(a + BeamArrays::phash)[lane];
+  } else {
+    b.live = 0;
+    b.pb = b.pnb = b.score = kNeg;
+    b.len = 0;
+    b.last = C.P->L.blank;
+    b.parent = b.last2 = -1;
+    b.h = kHashEmpty;
+    b.hp = 0;
+  }
+}
+
+__device__ void beam_store(const Ctx& C, const Beam& b) {
+  const int lane = lane_id();
+  char* a = C.base + C.P->L.o_beam;
+  if (lane < kMaxBeam) {
+    reinterpret_cast<float*>(a + BeamArrays::pb)[lane] = b.pb;
+    reinterpret_cast<float*>(a + BeamArrays::pnb)[lane] = b.pnb;
+    reinterpret_cast<float*>(a + BeamArrays::score)[lane] = b.score;
+    reinterpret_cast<int*>(a + BeamArrays::len)[lane] = b.len;
+    reinterpret_cast<int*>(a + BeamArrays::last)[lane] = b.last;
+    reinterpret_cast<int*>(a + BeamArrays::parent)[lane] = b.parent;
+    reinterpret_cast<int*>(a + BeamArrays::last2)[lane] = b.last2;
+    reinterpret_cast<int*>(a + BeamArrays::live)[lane] = b.live;
+    reinterpret_cast<uint64_t*>(a + BeamArrays::hash)[lane] = b.h;
+    reinterpret_cast<uint64_t*>(a + BeamArrays::phash)[lane] = b.hp;
+  }
+}
+
+// The empty hypothesis in slot 0, every other slot dead (sec. 13).
+__device__ void beam_fresh(Beam& b, int blank) {
+  const int lane = lane_id();
+  b.live = lane == 0;
+  b.pb = lane == 0 ? 0.0f : kNeg;
+  b.pnb = kNeg;
+  b.score = lane == 0 ? 0.0f : kNeg;
+  b.len = 0;
+  b.last = blank;
+  b.parent = -1;
+  b.last2 = -1;
+  b.h = kHashEmpty;
+  b.hp = 0;
+}
+
+__device__ Ctx make_ctx(const Params& P, char* base, char* smem) {
+  Ctx C;
+  C.P = &P;
+  C.base = base;
+  C.hdr = reinterpret_cast<int*>(base);
+  const LdsPlan& S = P.S;
+  C.row[0] = reinterpret_cast<float*>(smem + S.row0);
+  C.row[1] = reinterpret_cast<float*>(smem + S.row1);
+  C.rank = reinterpret_cast<int8_t*>(smem + S.rank);
+  C.Rc = reinterpret_cast<int*>(smem + S.Rc);
+  C.Rl = reinterpret_cast<float*>(smem + S.Rl);
+  C.buf = reinterpret_cast<uint64_t*>(smem + S.buf);
+  C.A = reinterpret_cast<float*>(smem + S.A);
+  C.kb = reinterpret_cast<float*>(smem + S.kb);
+  C.kc = reinterpret_cast<float*>(smem + S.kc);
+  C.lastk = reinterpret_cast<int*>(smem + S.lastk);
+  C.offs = reinterpret_cast<int*>(smem + S.offs);
+  C.exm = reinterpret_cast<uint32_t*>(smem + S.exm);
+  C.exclast = reinterpret_cast<int*>(smem + S.exclast);
+  C.bslot = reinterpret_cast<int*>(smem + S.bslot);
+  C.htab = reinterpret_cast<int*>(smem + S.htab);
+  C.newh = reinterpret_cast<uint64_t*>(smem + S.newh);
+  C.newlen = reinterpret_cast<int*>(smem + S.newlen);
+  C.nchild = reinterpret_cast<int*>(smem + S.nchild);
+  C.childc = reinterpret_cast<int*>(smem + S.childc);
+  C.scal = reinterpret_cast<int*>(smem + S.scal);
+  C.tab = reinterpret_cast<int*>(smem + S.tab);
+  C.ref = reinterpret_cast<int*>(smem + S.ref);
+  C.fstk = reinterpret_cast<int*>(smem + S.fstk);
+  C.tail = reinterpret_cast<int*>(smem + S.tail);
+  C.clist = reinterpret_cast<int*>(base + P.L.o_clist);
+  C.pages = reinterpret_cast<int*>(base + P.L.o_pages);
+  return C;
+}
+
+// Paged metadata: global row region <-> LDS.
+__device__ void paged_meta_io(const Ctx& C, bool to_lds) {
+  const Layout& L = C.P->L;
+  const int lane = lane_id();
+  int* gt = reinterpret_cast<int*>(C.base + L.o_tab);
+  int* gr = reinterpret_cast<int*>(C.base + L.o_ref);
+  int* gf = reinterpret_cast<int*>(C.base + L.o_free);
+  int* gl = reinterpret_cast<int*>(C.base + L.o_tail);
+  const int nt = 2 * L.W * L.max_lp, nl = 2 * L.W * L.ps;
+  if (to_lds) {
+    for (int i = lane; i < nt; i += kWave) C.tab[i] = gt[i];
+    for (int i = lane; i < L.npages; i += kWave) {
+      C.ref[i] = gr[i];
+      C.fstk[i] = gf[i];
+    }
+    for (int i = lane; i < nl; i += kWave) C.tail[i] = gl[i];
+  } else {
+    for (int i = lane; i < nt; i += kWave) gt[i] = C.tab[i];
+    for (int i = lane; i < L.npages; i += kWave) {
+      gr[i] = C.ref[i];
+      gf[i] = C.fstk[i];
+    }
+    for (int i = lane; i < nl; i += kWave) gl[i] = C.tail[i];
+  }
+}
+
+// Header fields <-> LDS scalars.
+__device__ void scal_from_header(const Ctx& C) {
+  const int lane = lane_id();
+  if (lane == 0) {
+    const int* h = C.hdr;
+    C.scal[kScalFreeTop] = h[kFreeTop];
+    C.scal[kScalNextFree] = h[kNextFree];
+    C.scal[kScalStatus] = h[kStatus];
+    C.scal[kScalHigh] = h[kPagesHigh];
+    C.scal[kScalLive0] = h[kLive0];
+    C.scal[kScalLive1] = h[kLive1];
+    C.scal[kScalCpl0] = h[kCpl0];
+    C.scal[kScalCpl1] = h[kCpl1];
+    C.scal[kScalPcp0] = h[kPcp0];
+    C.scal[kScalPcp1] = h[kPcp1];
+    C.scal[kScalFallbacks] = h[kFallbacks];
+    C.scal[kScalVerifies] = h[kVerifies];
+  }
+}
+
+__device__ void scal_to_header(const Ctx& C, int step, int last_t) {
+  const int lane = lane_id();
+  if (lane == 0) {
+    int* h = C.hdr;
+    h[kStep] = step;
+    h[kLastT] = last_t;
+    h[kFreeTop] = C.scal[kScalFreeTop];
+    h[kNextFree] = C.scal[kScalNextFree];
+    h[kStatus] = C.scal[kScalStatus];
+    h[kPagesHigh] = C.scal[kScalHigh];
+    h[kLive0] = C.scal[kScalLive0];
+    h[kLive1] = C.scal[kScalLive1];
+    h[kCpl0] = C.scal[kScalCpl0];
+    h[kCpl1] = C.scal[kScalCpl1];
+    h[kPcp0] = C.scal[kScalPcp0];
+    h[kPcp1] = C.scal[kScalPcp1];
+    h[kFallbacks] = C.scal[kScalFallbacks];
+    h[kVerifies] = C.scal[kScalVerifies];
+  }
+}
+
+// ----------------------------------------------------------------- kernels --
+// Frame selection (sec. 3.5): sel = ascending t < len with lp[t, blank] <
+// log(threshold); one 256-thread block per row, ordered ballot compaction.
+__global__ __launch_bounds__(256) void select_kernel(Params P) {
+  __shared__ int wave_cnt[4];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  char* base = P.state + (int64_t)b * P.L.row_bytes;
+  int* hdr = reinterpret_cast<int*>(base);
+  int* sel = reinterpret_cast<int*>(base + P.L.o_sel);
+  int len = P.seq_lengths[b];
+  len = len < 0 ? 0 : (len > P.T ? P.T : len);
+  const float* row = P.lp + (int64_t)b * P.stride_b + P.L.blank;
+  int cnt = 0;
+  for (int t0 = 0; t0 < len; t0 += 256) {
+    const int t = t0 + tid;
+    bool keep = false;
+    if (t < len) {
+      if (P.sel_mode == 0) keep = true;
+      else if (P.sel_mode == 2) keep = row[(int64_t)t * P.stride_t] < P.log_thr;
+    }
+    const uint64_t m = __ballot(keep);
+    if (lane == 0) wave_cnt[wv] = __popcll(m);
+    __syncthreads();
+    int before = cnt;
+    for (int j = 0; j < wv; j++) before += wave_cnt[j];
+    if (keep) sel[before + lanes_below(m)] = t;
+    cnt += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+    __syncthreads();
+  }
+  if (tid == 0) hdr[kNSel] = cnt;
+}
+
+// Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).
+template <bool STREAM>
+__global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  const Layout& L = P.L;
+  const int lane = lane_id();
+  const int row_i = blockIdx.x;
+  int srow = row_i;
+  if (STREAM) {
+    srow = P.rows ? P.rows[row_i] : row_i;
+    if (srow < 0 || srow >= P.num_rows) return;
+  }
+  char* base = P.state + (int64_t)srow * L.row_bytes;
+  Ctx C = make_ctx(P, base, smem);
+  const int W = L.W, V = L.V;
+
+  for (int c = lane; c < V; c += kWave) C.rank[c] = -1;
+  Beam b;
+  int step, last_t, nframes;
+  const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
+  if (STREAM) {
+    step = C.hdr[kStep];
+    last_t = C.hdr[kLastT];
+    scal_from_header(C);
+    beam_load(C, b);
+    if (L.paged) paged_meta_io(C, true);
+    nframes = L.cap - step;
+    nframes = nframes < 0 ? 0 : (nframes > P.T ? P.T : nframes);
+  } else {
+    step = 0;
+    last_t = -1;
+    if (lane < kScalCount) C.scal[lane] = 0;
+    beam_fresh(b, L.blank);
+    if (L.paged) {
+      for (int i = lane; i < 2 * W * L.max_lp; i += kWave) C.tab[i] = kInvalidPage;
+      for (int i = lane; i < L.npages; i += kWave) C.ref[i] = 0;
+    }
+    wave_sync();
+    nframes = C.hdr[kNSel];
+  }
+  lds_sync();
+
+  const int K = min(V - 1, 2 * W + 3);  // ranked labels per frame
+  const int complete = K == V - 1;
+  auto frame_ptr = [&](int f) -> const float* {
+    if (STREAM) return P.lp + (int64_t)row_i * P.stride_b + (int64_t)f * P.stride_t;
+    return P.lp + (int64_t)srow * P.stride_b + (int64_t)sel[f] * P.stride_t;
+  };
+  auto frame_index = [&](int f) -> int { return STREAM ? step + f : sel[f]; };
+
+  int prevK = 0;
+  if (nframes > 0) load_row_now(frame_ptr(0), C.row[0], V, P.vec4);
+  RowPrefetch pf;
+  const int step0 = step;
+  for (int f = 0; f < nframes; f++) {
+    const float* row = C.row[f & 1];
+    const int t = STREAM ? step0 + f : frame_index(f);
+    prefetch_issue(pf, f + 1 < nframes ? frame_ptr(f + 1) : nullptr, V, P.vec4);
+    lds_sync();
+    vocab_topk(C, row, K, prevK);
+    prevK = K;
+    if (step == 0) {
+      first_step(C, b, row, t > 0 ? 1 : 0, K);
+      const uint64_t lm = __ballot(lane < W && b.live);
+      lds_sync();
+      if (lane == 0) C.scal[kScalLive0] = (int)(uint32_t)lm;
+    } else {
+      const int g = t > last_t + 1 ? 1 : 0;
+      const Winner w = beam_step(C, b, row, g, step, K, complete);
+      if (L.paged) {
+        store_paged(C, step, w, b);
+      } else {
+        store_flat(C, step, w);
+        if ((step & 15) == 15) advance_cpl_flat(C, step & 1, b);
+      }
+    }
+    last_t = t;
+    step++;
+    prefetch_commit(pf, C.row[(f + 1) & 1], V, P.vec4);
+  }
+  lds_sync();
+
+  if (STREAM) {
+    beam_store(C, b);
+    if (L.paged) paged_meta_io(C, false);
+    scal_to_header(C, step, last_t);
+  } else {
+    wave_sync();
+    const int parity = step > 0 ? (step - 1) & 1 : 0;
+    write_outputs(C, b, parity, C.tab, srow);
+    scal_to_header(C, step, last_t);
+  }
+}
+
+// Fresh streams (stream_init / stream_reset): one block per stream.
+__global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
+  const Layout& L = P.L;
+  const int lane = lane_id();
+  int srow = P.rows ? P.rows[blockIdx.x] : (int)blockIdx.x;
+  if (srow < 0 || srow >= P.num_rows) return;
+  char* base = P.state + (int64_t)srow * L.row_bytes;
+  int* hdr = reinterpret_cast<int*>(base);
+  if (lane < kHdrInts) hdr[lane] = 0;
+  if (lane == 0) hdr[kLastT] = -1;
+  Ctx C;
+  C.P = &P;
+  C.base = base;
+  Beam b;
+  beam_fresh(b, L.blank);
+  beam_store(C, b);
+  if (L.paged) {
+    int* gt = reinterpret_cast<int*>(base + L.o_tab);
+    int* gr = reinterpret_cast<int*>(base + L.o_ref);
+    for (int i = lane; i < 2 * L.W * L.max_lp; i += kWave) gt[i] = kInvalidPage;
+    for (int i = lane; i < L.npages; i += kWave) gr[i] = 0;
+  }
+}
+
+// read_state: report the N best of each listed stream without changing it.
+__global__ __launch_bounds__(64) void read_state_kernel(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  const Layout& L = P.L;
+  int srow = P.rows ? P.rows[blockIdx.x] : (int)blockIdx.x;
+  if (srow < 0 || srow >= P.num_rows) return;
+  char* base = P.state + (int64_t)srow * L.row_bytes;
+  Ctx C = make_ctx(P, base, smem);
+  Beam b;
+  beam_load(C, b);
+  const int step = C.hdr[kStep];
+  if (step == 0) beam_fresh(b, L.blank);
+  const int parity = step > 0 ? (step - 1) & 1 : 0;
+  const int* tab = reinterpret_cast<const int*>(base + L.o_tab);
+  write_outputs(C, b, parity, tab, (int)blockIdx.x);
+}
+
+}  // namespace ctcpb
+
+// ==================================================================== host ==
+namespace {
+
+using namespace ctcpb;
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return CTCPB_OK;
+}
+
+struct Resolved {
+  int W, N, V, blank, mol, paged, ps, npages_cfg, cap_stream;
+  float threshold;
+};
+
+int resolve(const ctcpb_config* cfg, Resolved& R) {
+  if (!cfg) return fail(CTCPB_ERR_INVALID, "config is NULL");
+  if (cfg->beam < 1 || cfg->beam > 128)
+    return fail(CTCPB_ERR_INVALID, "beam must be in [1, 128], got " + std::to_string(cfg->beam));
+  if (cfg->beam > kMaxBeam)
+    return fail(CTCPB_ERR_UNSUPPORTED, "beam > 32 is not supported by this build");
+  if (cfg->nbest < 1 || cfg->nbest > cfg->beam)
+    return fail(CTCPB_ERR_INVALID, "nbest must be in [1, beam]");
+  if (cfg->vocab < 2) return fail(CTCPB_ERR_INVALID, "vocab must be >= 2");
+  if (cfg->vocab > kMaxVocab)
+    return fail(CTCPB_ERR_UNSUPPORTED, "vocab > 16384 is not supported by this build");
+  if (cfg->blank_id < 0 || cfg->blank_id >= cfg->vocab)
+    return fail(CTCPB_ERR_INVALID, "blank_id must be in [0, vocab)");
+  if (cfg->max_out_len < 0) return fail(CTCPB_ERR_INVALID, "max_out_len must be >= 0");
+  if (cfg->storage != CTCPB_STORAGE_FLAT && cfg->storage != CTCPB_STORAGE_PAGED)
+    return fail(CTCPB_ERR_INVALID, "storage must be CTCPB_STORAGE_FLAT or CTCPB_STORAGE_PAGED");
+  if (std::isnan(cfg->blank_threshold)) return fail(CTCPB_ERR_INVALID, "blank_threshold is NaN");
+  const int ps = cfg->page_size == 0 ? 16 : cfg->page_size;
+  if (cfg->storage == CTCPB_STORAGE_PAGED && (ps < 4 || ps > 64))
+    return fail(CTCPB_ERR_INVALID, "page_size must be in [4, 64]");
+  if (cfg->num_pages < 0) return fail(CTCPB_ERR_INVALID, "num_pages must be >= 0");
+  if (cfg->capacity < 0) return fail(CTCPB_ERR_INVALID, "capacity must be >= 0");
+  R.W = cfg->beam;
+  R.N = cfg->nbest;
+  R.V = cfg->vocab;
+  R.blank = cfg->blank_id;
+  R.mol = cfg->max_out_len;
+  R.paged = cfg->storage == CTCPB_STORAGE_PAGED;
+  R.ps = ps;
+  R.npages_cfg = cfg->num_pages;
+  R.cap_stream = cfg->capacity == 0 ? kDefaultCapacity : cfg->capacity;
+  R.threshold = cfg->blank_threshold;
+  return CTCPB_OK;
+}
+
+int align16(int x) { return (x + 15) & ~15; }
+
+LdsPlan plan_lds(const Layout& L) {
+  LdsPlan S{};
+  int off = 0;
+  auto take = [&](int bytes) {
+    const int at = off;
+    off += align16(bytes);
+    return at;
+  };
+  S.row0 = take(L.V * 4);
+  S.row1 = take(L.V * 4);
+  S.rank = take(L.V);
+  S.Rc = take(kMaxK * 4);
+  S.Rl = take(kMaxK * 4);
+  S.buf = take(kBuf * 8);
+  S.A = take(kMaxBeam * 4);
+  S.kb = take(kMaxBeam * 4);
+  S.kc = take(kMaxBeam * 4);
+  S.lastk = take(kMaxBeam * 4);
+  S.offs = take(128 * 4);
+  S.exm = take(kMaxBeam * 3 * 4);
+  S.exclast = take(kMaxBeam * 4);
+  S.bslot = take(kMaxBeam * 4);
+  S.htab = take(64 * 4);
+  S.newh = take(kMaxBeam * 8);
+  S.newlen = take(kMaxBeam * 4);
+  S.nchild = take(kMaxBeam * 4);
+  S.childc = take(kMaxBeam * kMaxBeam * 4);
+  S.scal = take(kScalCount * 4);
+  S.tab = take(L.paged ? 2 * L.W * L.max_lp * 4 : 0);
+  S.ref = take(L.paged ? L.npages * 4 : 0);
+  S.fstk = take(L.paged ? L.npages * 4 : 0);
+  S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
+  S.total = off;
+  return S;
+}
+
+Layout layout_for(const Resolved& R, int cap, int cap_sel) {
+  return make_layout(R.W, R.V, R.blank, cap, R.paged, R.ps, R.npages_cfg, cap_sel);
+}
+
+int check_lds(const LdsPlan& S) {
+  if (S.total > kLdsLimit)
+    return fail(CTCPB_ERR_UNSUPPORTED,
+                "decoder state needs " + std::to_string(S.total) +
+                    " bytes of LDS per row, more than the 160 KiB of a CU (smaller vocab, "
+                    "beam, capacity or num_pages)");
+  return CTCPB_OK;
+}
+
+template <typename K>
+int launch(K kernel, int blocks, int threads, int lds, hipStream_t st, const Params& P,
+           const char* what) {
+  if (blocks <= 0) return CTCPB_OK;
+  if (lds > 64 * 1024) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+      return fail(CTCPB_ERR_DEVICE, std::string("hipFuncSetAttribute failed for ") + what);
+  }
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), lds, st, P);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(CTCPB_ERR_DEVICE, std::string(what) + " launch failed: " + hipGetErrorString(e));
+  return CTCPB_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ctcpb_last_error(void) { return g_err.c_str(); }
+
+const char* ctcpb_version(void) { return "ctcpb 0.1 gfx950"; }
+
+int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
+                         size_t* out_bytes) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
+  if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
+  const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
+  *out_bytes = (size_t)batch * (size_t)L.row_bytes;
+  return ok();
+}
+
+int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
+  if (num_streams < 0) return fail(CTCPB_ERR_INVALID, "num_streams must be >= 0");
+  const Layout L = layout_for(R, R.cap_stream, 0);
+  *out_bytes = (size_t)num_streams * (size_t)L.row_bytes;
+  return ok();
+}
+
+int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
+                         int64_t stride_t, int32_t batch, int32_t max_T,
+                         const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
+                         int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
+                         void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
+  if (batch == 0) return ok();
+  if (!log_prob || !seq_lengths || !workspace || !out_lengths || !out_scores ||
+      (!out_tokens && R.mol > 0))
+    return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
+  if (max_T > 0 && (stride_t < R.V || (batch > 1 && stride_b < (int64_t)max_T * 0)))
+    return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
+  if (!aligned16(workspace)) return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
+  const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
+  if (workspace_bytes < (size_t)batch * (size_t)L.row_bytes)
+    return fail(CTCPB_ERR_TOO_SMALL, "workspace smaller than ctcpb_workspace_size");
+  Params P{};
+  P.L = L;
+  P.S = plan_lds(L);
+  if (int rc = check_lds(P.S)) return rc;
+  P.N = R.N;
+  P.max_out_len = R.mol;
+  if (R.threshold >= 1.0f) {
+    P.sel_mode = 0;
+  } else if (R.threshold <= 0.0f) {
+    P.sel_mode = 1;
+  } else {
+    P.sel_mode = 2;
+    P.log_thr = (float)std::log((double)R.threshold);
+  }
+  P.lp = log_prob;
+  P.stride_b = stride_b;
+  P.stride_t = stride_t;
+  P.T = max_T;
+  P.num_rows = batch;
+  P.seq_lengths = seq_lengths;
+  P.rows = nullptr;
+  P.state = static_cast<char*>(workspace);
+  P.out_tokens = out_tokens;
+  P.out_lengths = out_lengths;
+  P.out_scores = out_scores;
+  P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
+  if (int rc = launch(decode_kernel<false>, batch, 64, P.S.total, st, P, "decode_kernel"))
+    return rc;
+  return ok();
+}
+
+int ctcpb_stream_init(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                      int32_t num_streams, void* stream) {
+  return ctcpb_stream_reset(cfg, state, state_bytes, num_streams, nullptr, num_streams, stream);
+}
+
+int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                       int32_t num_streams, const int32_t* rows, int32_t n_rows, void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
+    return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
+  if (n_rows == 0) return ok();
+  if (!state) return fail(CTCPB_ERR_INVALID, "state is NULL");
+  if (!aligned16(state)) return fail(CTCPB_ERR_INVALID, "state must be 16-byte aligned");
+  const Layout L = layout_for(R, R.cap_stream, 0);
+  if (state_bytes < (size_t)num_streams * (size_t)L.row_bytes)
+    return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");
+  Params P{};
+  P.L = L;
+  P.num_rows = num_streams;
+  P.rows = rows;
+  P.state = static_cast<char*>(state);
+  if (int rc = launch(stream_fresh_kernel, n_rows, 64, 0, static_cast<hipStream_t>(stream), P,
+                      "stream_fresh_kernel"))
+    return rc;
+  return ok();
+}
+
+int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                       int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
+                       int64_t stride_t, int32_t chunk_T, const int32_t* rows, int32_t n_rows,
+                       void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (num_streams < 0 || n_rows < 0 || n_rows > num_streams || chunk_T < 0)
+    return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams and chunk_T >= 0");
+  if (n_rows == 0 || chunk_T == 0) return ok();
+  if (!state || !log_prob_chunk) return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
+  if (stride_t < R.V) return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
+  if (!aligned16(state)) return fail(CTCPB_ERR_INVALID, "state must be 16-byte aligned");
+  const Layout L = layout_for(R, R.cap_stream, 0);
+  if (state_bytes < (size_t)num_streams * (size_t)L.row_bytes)
+    return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");
+  Params P{};
+  P.L = L;
+  P.S = plan_lds(L);
+  if (int rc = check_lds(P.S)) return rc;
+  P.N = R.N;
+  P.max_out_len = R.mol;
+  P.lp = log_prob_chunk;
+  P.stride_b = stride_row;
+  P.stride_t = stride_t;
+  P.T = chunk_T;
+  P.num_rows = num_streams;
+  P.rows = rows;
+  P.state = static_cast<char*>(state);
+  P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
+           (stride_t % 4 == 0);
+  if (int rc = launch(decode_kernel<true>, n_rows, 64, P.S.total,
+                      static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
+    return rc;
+  return ok();
+}
+
+int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_bytes,
+                     int32_t num_streams, const int32_t* rows, int32_t n_rows,
+                     int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
+                     void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
+    return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
+  if (n_rows == 0) return ok();
+  if (!state || !out_lengths || !out_scores || (!out_tokens && R.mol > 0))
+    return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
+  const Layout L = layout_for(R, R.cap_stream, 0);
+  if (state_bytes < (size_t)num_streams * (size_t)L.row_bytes)
+    return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");
+  Params P{};
+  P.L = L;
+  P.S = plan_lds(L);
+  P.N = R.N;
+  P.max_out_len = R.mol;
+  P.num_rows = num_streams;
+  P.rows = rows;
+  P.state = static_cast<char*>(const_cast<void*>(state));
+  P.out_tokens = out_tokens;
+  P.out_lengths = out_lengths;
+  P.out_scores = out_scores;
+  // only the small per-row scratch is needed: rows/ranks, no frame buffers
+  const int lds = P.S.scal + kScalCount * 4;
+  if (int rc = launch(read_state_kernel, n_rows, 64, lds, static_cast<hipStream_t>(stream), P,
+                      "read_state_kernel"))
+    return rc;
+  return ok();
+}
+
+}  // extern "C"

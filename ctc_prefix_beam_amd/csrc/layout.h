@@ -1,0 +1,105 @@
+// layout.h -- per-row (offline) / per-stream (streaming) state region.
+//
+// Offline workspaces and streaming state blobs are arrays of identical row
+// regions whose layout is a pure function of the configuration and the token
+// capacity, so the host rebuilds every pointer from the dimensions and never
+// reads device memory (the page's StreamingState idea, sec. 4.3 / 5).
+//
+//   header      64 x int32   step, last frame, counters, parity bookkeeping
+//   beam arrays kMaxBeam x {pb, pnb, score, len, last token, parent slot,
+//               second-to-last token, live, prefix hash, parent-prefix hash}
+//   sel         cap_sel x int32     offline: selected frame indices
+//   flat:       clist[2][beam][cap] int32 tokens, double-buffered by parity
+//   paged:      table[2][beam][max_lp] int32 page ids (-1 none),
+//               refcount[num_pages], free stack[num_pages],
+//               pages[num_pages][page_size] int32 tokens,
+//               tail[2][beam][page_size] int32: each beam's partial last page
+#pragma once
+#include <stdint.h>
+
+namespace ctcpb {
+
+constexpr int kMaxBeam = 32;     // widest beam of this build
+constexpr int kHdrInts = 64;
+constexpr int kInvalidPage = -1;
+
+enum HeaderField {
+  kStep = 0,      // frames decoded so far (steps)
+  kLastT,         // frame index of the last decoded frame, -1 before any
+  kNSel,          // offline: number of selected frames
+  kStatus,        // bit 0: a paged row ran out of pages
+  kCpl0,          // common token prefix of all live beams, parity 0 / 1
+  kCpl1,
+  kPcp0,          // leading full pages shared by all live beams, parity 0 / 1
+  kPcp1,
+  kNextFree,      // paged: bump pointer
+  kFreeTop,       // paged: free-stack depth
+  kLive0,         // live-slot bitmask written at parity 0 / 1
+  kLive1,
+  kPagesHigh,     // paged: high-water mark of pages in use
+  kFallbacks,     // steps that needed the full beam x vocab selection
+  kVerifies,      // exact token comparisons made for the merge test
+};
+
+enum Status { kStatusOutOfPages = 1 };
+
+struct Layout {
+  int W;          // beam
+  int V;          // vocabulary
+  int blank;
+  int cap;        // token (and frame) capacity of a row
+  int paged;      // 0 flat, 1 paged
+  int ps;         // page size
+  int max_lp;     // pages per block-table row
+  int npages;     // pages per row
+  int cap_sel;    // entries of sel (offline: max_T; streaming: 0)
+  int64_t row_bytes;
+  int64_t o_beam, o_sel, o_clist, o_tab, o_ref, o_free, o_pages, o_tail;
+};
+
+// Beam arrays inside a row region (offsets from o_beam).
+struct BeamArrays {
+  static constexpr int64_t pb = 0, pnb = 128, score = 256, len = 384, last = 512,
+                           parent = 640, last2 = 768, live = 896, hash = 1024, phash = 1280,
+                           bytes = 1536;
+};
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, int npages_cfg,
+                          int cap_sel) {
+  Layout L{};
+  L.W = W;
+  L.V = V;
+  L.blank = blank;
+  L.cap = cap;
+  L.paged = paged;
+  L.ps = paged ? ps : 0;
+  L.max_lp = paged ? (cap + ps - 1) / ps : 0;
+  L.npages = paged ? (npages_cfg > 0 ? npages_cfg : W * (L.max_lp + 1)) : 0;
+  L.cap_sel = cap_sel;
+  int64_t off = kHdrInts * 4;
+  L.o_beam = off;
+  off += BeamArrays::bytes;
+  L.o_sel = off;
+  off += align256((int64_t)cap_sel * 4);
+  if (!paged) {
+    L.o_clist = off;
+    off += align256((int64_t)2 * W * cap * 4);
+  } else {
+    L.o_tab = off;
+    off += align256((int64_t)2 * W * L.max_lp * 4);
+    L.o_ref = off;
+    off += align256((int64_t)L.npages * 4);
+    L.o_free = off;
+    off += align256((int64_t)L.npages * 4);
+    L.o_pages = off;
+    off += align256((int64_t)L.npages * ps * 4);
+    L.o_tail = off;
+    off += align256((int64_t)2 * W * ps * 4);
+  }
+  L.row_bytes = align256(off);
+  return L;
+}
+
+}  // namespace ctcpb

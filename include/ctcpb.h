@@ -1,0 +1,137 @@
+/*
+ * ctcpb.h -- C ABI of libctcpb.so, a batched CTC prefix beam search decoder
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of the page "GPU CTC Prefix Beam Search Decoder"
+ * (OASR documentation): from log_prob[B, T, V] it returns, per utterance, the
+ * N best collapsed label sequences with their CTC prefix scores, offline
+ * (sec. 3.7) or streaming chunk by chunk with the decoder state kept on the
+ * device (sec. 8).  The calls follow the page's public API (sec. 9, 12.5, 16):
+ * size queries, an offline decode, and a streaming init / chunk / read-state
+ * lifecycle.
+ *
+ * Conventions for every call:
+ *   - Pointers documented "device" are HIP device memory owned by the caller;
+ *     the library never allocates, frees or keeps device memory, and keeps no
+ *     host state between calls.  The configuration is passed on every call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns without synchronising; results are
+ *     ready when the stream reaches that point.
+ *   - Return value: CTCPB_OK (0) or an error code; ctcpb_last_error() then
+ *     describes the failure (thread-local, valid until the next call on the
+ *     same thread).  There is no partial success: on error nothing was
+ *     enqueued, except CTCPB_ERR_DEVICE, reported when a launch fails.
+ *   - Scores are float32 natural-log probabilities.  A reported slot with no
+ *     hypothesis has length 0, score -FLT_MAX and tokens -1.
+ */
+#ifndef CTCPB_H
+#define CTCPB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CTCPB_OK = 0,
+  CTCPB_ERR_INVALID = 1,     /* an argument is out of range or inconsistent */
+  CTCPB_ERR_TOO_SMALL = 2,   /* workspace / state buffer smaller than required */
+  CTCPB_ERR_UNSUPPORTED = 3, /* valid but outside this build (beam > 32, LDS budget) */
+  CTCPB_ERR_DEVICE = 4       /* a HIP launch failed */
+};
+
+enum { CTCPB_STORAGE_FLAT = 0, CTCPB_STORAGE_PAGED = 1 };
+
+/* Decoder configuration (sec. 10 GpuDecoderConfig, sec. 11 options). */
+typedef struct {
+  int32_t beam;            /* beam width W, 1..32 in this build (sec. 11 allows up to 128) */
+  int32_t nbest;           /* hypotheses reported per row, 1..beam */
+  int32_t vocab;           /* V >= 2, at most 16384 in this build */
+  int32_t blank_id;        /* 0 <= blank_id < vocab */
+  float blank_threshold;   /* offline frame skip (sec. 3.5): frame t is decoded iff
+                              log_prob[t, blank] < log(blank_threshold); >= 1 keeps
+                              every frame, <= 0 keeps none.  Streaming ignores it. */
+  int32_t max_out_len;     /* tokens copied per hypothesis; longer ones are truncated,
+                              lengths still report the full count (sec. 13) */
+  int32_t capacity;        /* streaming: frames (hence tokens) per stream, 0 = 4096;
+                              later frames are ignored (sec. 13).  Offline: unused,
+                              the capacity is max_T so nothing is ever cut. */
+  int32_t storage;         /* CTCPB_STORAGE_FLAT: double-buffered token lists
+                              (sec. 3.1, 7); CTCPB_STORAGE_PAGED: pages with
+                              reference-counted prefix sharing (sec. 3.4.5, 4.2) */
+  int32_t page_size;       /* paged: tokens per page, 4..64 (0 = 16) */
+  int32_t num_pages;       /* paged: pages per row/stream (0 = beam * (ceil(cap /
+                              page_size) + 1), the bound of sec. 4.2) */
+} ctcpb_config;
+
+/* Bytes of device workspace ctcpb_decode_offline needs for `batch` rows of up
+ * to `max_T` frames (sec. 5 calculate_[paged_]workspace_size). */
+int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
+                         size_t* out_bytes);
+
+/* Offline batch decode (sec. 3.7).
+ *   log_prob     device, float32; element (b, t, c) at
+ *                log_prob[b*stride_b + t*stride_t + c] (unit stride over the
+ *                vocabulary); only frames t < seq_lengths[b] are read, so
+ *                padding may hold anything (even NaN).  Values must be finite.
+ *   seq_lengths  device, int32 [batch]; clamped to [0, max_T] on the device.
+ *   workspace    device, >= ctcpb_workspace_size bytes, 256-byte aligned; its
+ *                contents on entry do not matter.
+ *   out_tokens   device, int32 [batch][nbest][max_out_len], -1 padded
+ *   out_lengths  device, int32 [batch][nbest], full hypothesis lengths
+ *   out_scores   device, float32 [batch][nbest]
+ * Hypotheses are reported in (score descending, slot ascending) order.  A row
+ * with no decodable frame reports the empty hypothesis at score 0 (sec. 13).
+ * No host synchronisation happens inside the call. */
+int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
+                         int64_t stride_t, int32_t batch, int32_t max_T,
+                         const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
+                         int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
+                         void* stream);
+
+/* Bytes of a streaming state blob holding `num_streams` independent streams
+ * (sec. 5 calculate_[paged_]state_buffer_size). */
+int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes);
+
+/* Put every stream of the blob in the fresh state (no frame decoded; reads
+ * back the empty hypothesis).  state: device, >= ctcpb_state_size bytes,
+ * 256-byte aligned. */
+int ctcpb_stream_init(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                      int32_t num_streams, void* stream);
+
+/* Reset the listed streams to the fresh state.  rows: device int32[n_rows]
+ * stream indices in [0, num_streams) (duplicates not allowed), or NULL for
+ * streams 0..n_rows-1. */
+int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                       int32_t num_streams, const int32_t* rows, int32_t n_rows, void* stream);
+
+/* Decode one chunk of frames for n_rows streams at once (sec. 3.4.8 / 3.4.9):
+ * row i of log_prob_chunk (element (i, t, c) at i*stride_row + t*stride_t + c,
+ * device float32, finite) continues stream rows[i] (NULL: stream i; distinct
+ * indices required).  Every frame is decoded (no skipping); frames past a
+ * stream's capacity are ignored.  The state stays on the device; nothing is
+ * read back. */
+int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                       int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
+                       int64_t stride_t, int32_t chunk_T, const int32_t* rows, int32_t n_rows,
+                       void* stream);
+
+/* Report the current N best of the listed streams (sec. 8 read_state) without
+ * changing them.  Outputs as in ctcpb_decode_offline with batch = n_rows. */
+int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_bytes,
+                     int32_t num_streams, const int32_t* rows, int32_t n_rows,
+                     int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
+                     void* stream);
+
+/* Human-readable description of the last error on this thread ("" if none). */
+const char* ctcpb_last_error(void);
+
+/* Library build identifier, e.g. "ctcpb 0.1 gfx950". */
+const char* ctcpb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CTCPB_H */

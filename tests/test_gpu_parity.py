@@ -1,0 +1,106 @@
+"""Parity of the HIP decoder (through the C ABI) with the CPU oracle on the
+same seeded inputs: tokens and lengths bit-exact, scores within 1e-4 (and in
+practice bit-identical), at sizes the oracle finishes in seconds."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import assert_parity, gpu_offline
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(lp, lens, beam, nbest, blank=0, threshold=1.0, max_out_len=None, paged=False,
+             page_size=16, what=""):
+    T = lp.shape[1]
+    mol = T if max_out_len is None else max_out_len
+    print(f"[case] {what} B={lp.shape[0]} T={T} V={lp.shape[2]} W={beam} paged={paged}",
+          flush=True)
+    got = gpu_offline(lp, lens, beam, nbest, blank, threshold, mol, paged, page_size)
+    ref = oracle.decode(lp, lens, beam, nbest, blank, threshold, mol)
+    assert_parity(got, ref, what=what)
+    return got, ref
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_tiny(paged):
+    lp, lens = synth.peaky(10, 50, 29, seed=0, p_blank=0.65)
+    run_both(lp, lens, 4, 4, paged=paged, what="tiny")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_bpe256_cut(paged):
+    wl = synth.WORKLOADS["bpe256"]
+    lp, lens = wl.make(1, B=4, T=200)
+    run_both(lp, lens, 8, 8, 0, 0.999, 200, paged, what="bpe256")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_bpe1024_ragged(paged):
+    lp, lens = synth.peaky(4, 300, 1024, seed=2, p_blank=0.7, token_bias=(3.0, 8.0),
+                           lengths=(100, 300), nan_tail=True)
+    run_both(lp, lens, 16, 16, 0, 0.999, 256, paged, what="bpe1024")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_vocab5000_cut(paged):
+    lp, lens = synth.peaky(2, 80, 5000, seed=3, p_blank=0.55, p_low=0.2)
+    run_both(lp, lens, 32, 32, 0, 0.999, 64, paged, what="vocab5000")
+
+
+def test_frame_skipping_active():
+    # strong blank frames so that a threshold of 0.9 really skips frames
+    lp, lens = synth.peaky(6, 120, 40, seed=5, p_blank=0.6, blank_bias=12.0)
+    nsel = [len(oracle.select_frames(lp[b], lens[b], 0, 0.9)) for b in range(6)]
+    assert min(nsel) < 100
+    for paged in (False, True):
+        run_both(lp, lens, 6, 6, 0, 0.9, 120, paged, what="skip")
+
+
+@pytest.mark.parametrize("W,V", [(1, 29), (2, 2), (4, 2), (16, 20), (32, 40), (3, 5)])
+def test_beam_vocab_corners(W, V):
+    lp, lens = synth.peaky(3, 40, V, seed=W * 100 + V, p_blank=0.5)
+    run_both(lp, lens, W, W, what=f"W{W}V{V}")
+
+
+def test_blank_not_zero_and_truncation():
+    lp, lens = synth.peaky(3, 70, 33, seed=8, p_blank=0.5, blank=32)
+    run_both(lp, lens, 5, 3, blank=32, max_out_len=6, what="blank32")
+    run_both(lp, lens, 5, 5, blank=32, max_out_len=0, what="mol0")
+
+
+def test_empty_rows_and_thresholds():
+    lp, _ = synth.peaky(4, 30, 12, seed=9)
+    lens = np.array([0, 30, 7, 1], np.int32)
+    for thr in (0.0, -1.0, 0.5, 1.0, 2.0):
+        run_both(lp, lens, 4, 4, 0, thr, 30, what=f"thr{thr}")
+
+
+def test_noncontiguous_rows():
+    lp, lens = synth.peaky(3, 40, 64, seed=10)
+    big = np.full((3, 50, 80), np.nan, np.float32)
+    big[:, :40, :64] = lp
+    x = torch.from_numpy(big)[:, :40, :64]          # stride_b = 4000, stride_t = 80
+    got = gpu_offline(x, lens, 6, 6, 0, 1.0, 40)
+    ref = oracle.decode(lp, lens, 6, 6, 0, 1.0, 40)
+    assert_parity(got, ref, what="strided")
+
+
+def test_flat_equals_paged_and_page_sizes():
+    lp, lens = synth.peaky(4, 150, 300, seed=11, p_blank=0.5)
+    base = gpu_offline(lp, lens, 12, 12, 0, 1.0, 150)
+    for ps in (4, 8, 16, 64):
+        other = gpu_offline(lp, lens, 12, 12, 0, 1.0, 150, paged=True, page_size=ps)
+        for a, b in zip(base, other):
+            assert np.array_equal(a, b), ps
+
+
+def test_repeat_runs_are_bitwise_identical():
+    lp, lens = synth.peaky(8, 200, 700, seed=12, p_blank=0.5, p_low=0.3)
+    first = gpu_offline(lp, lens, 24, 24, 0, 1.0, 200, paged=True)
+    for _ in range(3):
+        again = gpu_offline(lp, lens, 24, 24, 0, 1.0, 200, paged=True)
+        for a, b in zip(first, again):
+            assert np.array_equal(a, b)
