@@ -68,6 +68,56 @@ def peaky(B: int, T: int, V: int, seed: int, p_blank: float = 0.65,
     return out, lens
 
 
+def peaky_device(B: int, T: int, V: int, seed: int, device, p_blank: float = 0.65,
+                 blank_bias: float = 8.0, token_bias=6.0, p_low: float = 0.0,
+                 low_bias: float = 2.0, lengths=None, nan_tail: bool = False,
+                 blank: int = 0, repeat_p: float = 0.3, rows_per_chunk: int = 8):
+    """Same recipe as ``peaky`` for large tensors: the per-frame choices are
+    drawn with numpy, the logits with a seeded torch generator on `device`
+    (float64), so the tensor never exists on the host.  Returns (log_prob
+    torch float32 on device, lengths numpy int32).  Its bits differ from
+    ``peaky`` with the same seed (another generator), not its distribution."""
+    import torch
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lens = np.full(B, T, np.int32)
+    elif isinstance(lengths, tuple):
+        lens = rng.integers(lengths[0], lengths[1] + 1, size=B).astype(np.int32)
+    else:
+        lens = np.asarray(lengths, np.int32)
+    nonblank = np.array([c for c in range(V) if c != blank], np.int64)
+    low = rng.random((B, T)) < p_low
+    is_blank = rng.random((B, T)) < p_blank
+    u = rng.random((B, T))
+    rand_tok = nonblank[rng.integers(0, V - 1, size=(B, T))]
+    if isinstance(token_bias, tuple):
+        tb = rng.uniform(token_bias[0], token_bias[1], size=(B, T))
+    else:
+        tb = np.full((B, T), float(token_bias))
+    tok = np.empty((B, T), np.int64)
+    prev = np.full(B, -1, np.int64)
+    for t in range(T):
+        pick = np.where((prev >= 0) & (u[:, t] < repeat_p), prev, rand_tok[:, t])
+        tok[:, t] = np.where(is_blank[:, t], blank, pick)
+        prev = np.where(is_blank[:, t], prev, pick)
+    bias = np.where(low, low_bias, np.where(is_blank, blank_bias, tb))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = torch.empty((B, T, V), dtype=torch.float32, device=device)
+    for b0 in range(0, B, rows_per_chunk):
+        b1 = min(B, b0 + rows_per_chunk)
+        z = torch.randn((b1 - b0, T, V), generator=gen, device=device, dtype=torch.float64)
+        idx = torch.from_numpy(tok[b0:b1]).to(device).unsqueeze(-1)
+        z.scatter_add_(2, idx, torch.from_numpy(bias[b0:b1]).to(device).unsqueeze(-1))
+        out[b0:b1] = (z - torch.logsumexp(z, dim=2, keepdim=True)).to(torch.float32)
+        del z
+    if nan_tail:
+        for b in range(B):
+            if lens[b] < T:
+                out[b, lens[b]:] = float("nan")
+    return out, lens
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -86,6 +136,10 @@ class Workload:
     def make(self, seed: int, B: int | None = None, T: int | None = None):
         """Inputs of this workload (optionally with fewer rows or frames)."""
         return peaky(B or self.B, T or self.T, self.V, seed, **self.gen)
+
+    def make_device(self, seed: int, device, B: int | None = None, T: int | None = None):
+        """Full-size inputs drawn directly on `device` (see peaky_device)."""
+        return peaky_device(B or self.B, T or self.T, self.V, seed, device, **self.gen)
 
 
 # The five workloads: shapes, decode settings and generator parameters.

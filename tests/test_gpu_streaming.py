@@ -1,0 +1,106 @@
+"""Streaming decode on the GPU (stream_init / stream_chunk / read_state /
+stream_reset through the C ABI) against the oracle's streaming decode and
+against the GPU's own offline decode of the concatenated frames."""
+import numpy as np
+import pytest
+import torch
+
+import ctc_prefix_beam_amd as cpb
+import oracle
+import synth
+from gpu_util import assert_parity, gpu_offline
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_streams(lp, beam, capacity, chunk, nbest, mol):
+    S = lp.shape[0]
+    outs = []
+    for s in range(S):
+        st = oracle.Stream(beam, lp.shape[2], 0, capacity)
+        for a in range(0, lp.shape[1], chunk):
+            st.feed(lp[s, a:a + chunk])
+        outs.append(st.read(nbest, mol))
+    return tuple(np.stack([o[i] for o in outs]) for i in range(3))
+
+
+def read(pool, rows=None):
+    t, l, s = pool.read(rows)
+    torch.cuda.synchronize()
+    return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_chunks_equal_oracle_stream_and_offline(paged):
+    S, T, V, W, CH = 6, 96, 512, 10, 16
+    lp, _ = synth.peaky(S, T, V, seed=21, p_blank=0.65)
+    print(f"[case] stream S={S} T={T} V={V} W={W} paged={paged}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, capacity=4096, max_out_len=T, paged=paged)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    for a in range(0, T, CH):
+        pool.chunk(x[:, a:a + CH])
+    got = read(pool)
+    ref = oracle_streams(lp, W, 4096, CH, W, T)
+    assert_parity(got, ref, what="stream")
+    off = gpu_offline(lp, np.full(S, T, np.int32), W, W, 0, 1.0, T, paged=paged)
+    for a, b in zip(got, off):
+        assert np.array_equal(a, b)
+
+
+def test_read_is_non_mutating_and_midway_results():
+    S, T, V, W, CH = 3, 64, 100, 8, 16
+    lp, _ = synth.peaky(S, T, V, seed=22)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    fresh = read(pool)
+    assert (fresh[1] == 0).all() and (fresh[2][:, 0] == 0).all()
+    assert (fresh[2][:, 1:] == -np.finfo(np.float32).max).all()
+    for a in range(0, 32, CH):
+        pool.chunk(x[:, a:a + CH])
+    mid1, mid2 = read(pool), read(pool)
+    for a, b in zip(mid1, mid2):
+        assert np.array_equal(a, b)
+    assert_parity(mid1, oracle_streams(lp[:, :32], W, 4096, CH, W, T), what="mid")
+    for a in range(32, T, CH):
+        pool.chunk(x[:, a:a + CH])
+    assert_parity(read(pool), oracle_streams(lp, W, 4096, CH, W, T), what="end")
+
+
+def test_row_subsets_reset_and_capacity():
+    S, T, V, W = 5, 48, 64, 6
+    lp, _ = synth.peaky(S, T, V, seed=23)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, capacity=40)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    rows = torch.tensor([3, 0], dtype=torch.int32, device="cuda")
+    # only streams 3 and 0 advance; chunk row i feeds stream rows[i]
+    for a in range(0, T, 16):
+        pool.chunk(x[[3, 0], a:a + 16], rows=rows)
+    got = read(pool)
+    ref = oracle_streams(lp[[0, 3]], W, 40, 16, W, T)   # capacity 40 < 48 frames
+    assert_parity(tuple(g[[0, 3]] for g in got), ref, what="subset")
+    assert (got[1][[1, 2, 4]] == 0).all()               # untouched streams still fresh
+    # reset stream 3 and feed it stream 1's frames
+    pool.reset(torch.tensor([3], dtype=torch.int32, device="cuda"))
+    for a in range(0, T, 16):
+        pool.chunk(x[[1], a:a + 16], rows=torch.tensor([3], dtype=torch.int32, device="cuda"))
+    got = read(pool, torch.tensor([3, 0], dtype=torch.int32, device="cuda"))
+    ref = oracle_streams(lp[[1, 0]], W, 40, 16, W, T)
+    assert_parity(got, ref, what="reset")
+
+
+def test_uneven_chunks_equal_single_chunk():
+    S, T, V, W = 4, 75, 200, 12
+    lp, _ = synth.peaky(S, T, V, seed=24, p_low=0.2)
+    x = torch.from_numpy(lp).cuda()
+    outs = []
+    for cuts in ([0, 75], [0, 1, 2, 17, 40, 41, 75], list(range(0, 76, 5))):
+        pool = cpb.StreamPool(cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T), V, S)
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            pool.chunk(x[:, a:b])
+        outs.append(read(pool))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
