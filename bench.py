@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X CTC prefix beam search decoder.
+
+Headline: decoded frames per second (B*T per second) of the offline decode of
+the large-vocabulary workload (B=128 utterances x T=1500 frames, V=5000,
+beam 32, 32-best, blank threshold 0.999, 512-token outputs, paged token
+storage), one GPU, inputs resident in HBM before the timed region.  A step is
+one ctcpb_decode_offline call over the whole batch (frame filter + decode).
+Also reported on the same line: the roofline of the decode kernel, the CPU
+oracle's throughput on a bounded sample, per-chunk latency of 256 concurrent
+streams (V=512, beam 10, 16-frame chunks), and the other workloads' rates.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_vocab5000_pmc.json")
+KERNEL_SOURCES = ["ctc_prefix_beam_amd/csrc/ctcpb.hip", "ctc_prefix_beam_amd/csrc/device_math.h",
+                  "ctc_prefix_beam_amd/csrc/wave_ops.h", "ctc_prefix_beam_amd/csrc/layout.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes_per_frame(V, W):
+    # the frame's log-probabilities read once, plus the beam state of every
+    # slot read and written (pb, pnb, score, last label, length: 20 B) and one
+    # 4-byte token append
+    return 4 * V + 44 * W
+
+
+def time_offline(dec, x, lens_d, out, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        dec.decode(x, lens_d, out=out)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        dec.decode(x, lens_d, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in evs]
+    return wall, kernel_ms
+
+
+def cpu_baseline(x, lens, wl, seconds):
+    """The oracle as it stands on a bounded sample of the same workload: one
+    row per process, rows spread over the host's cores (at most 16)."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    procs = max(1, min(16, os.cpu_count() or 1))
+    # a quick probe on a few frames sizes the sample to about `seconds`
+    probe_T = min(60, wl.T)
+    lp1 = x[0:1, :probe_T].cpu().numpy()
+    t = time.perf_counter()
+    oracle.decode(lp1, np.array([probe_T], np.int32), wl.beam, wl.nbest, 0, wl.threshold,
+                  wl.max_out_len)
+    per_frame = (time.perf_counter() - t) / probe_T
+    T = int(min(wl.T, max(probe_T, seconds / max(per_frame, 1e-9))))
+    rows = list(range(procs))
+    lp = x[rows, :T].cpu().numpy()
+    ln = np.minimum(lens[rows], T).astype(np.int32)
+    t = time.perf_counter()
+    oracle.decode_parallel(lp, ln, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len,
+                           processes=procs)
+    wall = time.perf_counter() - t
+    return {"value": round(float(len(rows) * T / wall), 1), "unit": "decoded frames/s",
+            "cores": procs, "kind": "oracle",
+            "sample": f"{len(rows)} rows x first {T} frames of {wl.name}, one single-threaded "
+                      f"oracle process per row ({wall:.1f} s)"}
+
+
+def streaming_latency(reps=3, seed=0):
+    """256 streams, 64 chunks of 16 frames: per-chunk latency of one
+    ctcpb_stream_chunk call advancing every stream (device time by HIP events,
+    host time from enqueue to completion)."""
+    import numpy as np
+    import torch
+
+    import ctc_prefix_beam_amd as cpb
+    import synth
+    wl = synth.WORKLOADS["stream512"]
+    x, _ = wl.make_device(seed, "cuda")
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, max_out_len=wl.T),
+                          wl.V, wl.B)
+    dev_ms, host_ms = [], []
+    for rep in range(reps + 1):
+        pool.reset()
+        torch.cuda.synchronize()
+        for a in range(0, wl.T, wl.chunk):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t = time.perf_counter()
+            e0.record()
+            pool.chunk(x[:, a:a + wl.chunk])
+            e1.record()
+            torch.cuda.synchronize()
+            if rep > 0:  # the first pass is a warm-up
+                host_ms.append((time.perf_counter() - t) * 1e3)
+                dev_ms.append(e0.elapsed_time(e1))
+    d = np.array(dev_ms)
+    h = np.array(host_ms)
+    return {"workload": "stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks",
+            "p50_chunk_ms": round(float(np.percentile(d, 50)), 4),
+            "p90_chunk_ms": round(float(np.percentile(d, 90)), 4),
+            "p99_chunk_ms": round(float(np.percentile(d, 99)), 4),
+            "p50_host_chunk_ms": round(float(np.percentile(h, 50)), 4),
+            "frames_per_s": round(float(wl.B * wl.chunk / (d.mean() / 1e3)), 1),
+            "chunks_timed": int(d.size)}
+
+
+def other_workloads():
+    import numpy as np
+    import torch
+
+    import ctc_prefix_beam_amd as cpb
+    import synth
+    res = {}
+    for name, paged in (("bpe256", False), ("bpe1024", False), ("vocab5000", False)):
+        wl = synth.WORKLOADS[name]
+        x, lens = wl.make_device(0, "cuda")
+        lens_d = torch.from_numpy(lens).cuda()
+        dec = cpb.OfflineDecoder(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest,
+                                                   blank_threshold=wl.threshold,
+                                                   max_out_len=wl.max_out_len, paged=paged))
+        out = None
+        out = dec.decode(x, lens_d)
+        wall, kms = time_offline(dec, x, lens_d, out, 5, 1)
+        key = name + ("_paged" if paged else "_flat")
+        st = dec.row_stats().cpu().numpy()
+        res[key] = {"frames_per_s": round(wl.B * wl.T * 5 / wall, 1),
+                    "valid_frames_per_s": round(float(np.sum(lens)) * 5 / wall, 1),
+                    "ms_per_decode": round(float(np.mean(kms)), 4),
+                    "fallback_steps": int(st[:, 4].sum()), "steps": int(st[:, 0].sum())}
+        del x
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="vocab5000")
+    ap.add_argument("--storage", choices=["paged", "flat"], default="paged")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip streaming and other workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this decoder shards by utterance/stream with no "
+              f"exchange, and multi-GPU runs are not part of this build (got --gpus "
+              f"{args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ctc_prefix_beam_amd as cpb
+    import synth
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        a.fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": a.numel() * 4, "copies": 3}))
+        return
+
+    wl = synth.WORKLOADS[args.workload]
+    paged = args.storage == "paged"
+    log(f"[bench] generating {wl.name} inputs on the GPU: B={wl.B} T={wl.T} V={wl.V}")
+    x, lens = wl.make_device(0, "cuda")
+    lens_d = torch.from_numpy(lens).cuda()
+    cfg = cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, blank_threshold=wl.threshold,
+                            max_out_len=wl.max_out_len, paged=paged)
+    dec = cpb.OfflineDecoder(cfg)
+    out = dec.decode(x, lens_d)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} decodes after {args.warmup} warm-up")
+    wall, kernel_ms = time_offline(dec, x, lens_d, out, args.steps, args.warmup)
+    stats = dec.row_stats().cpu().numpy()
+    selected = int(stats[:, 1].sum())
+    frames = wl.B * wl.T
+    value = frames * args.steps / wall
+    launch_ms = float(np.mean(kernel_ms))
+    bytes_per_launch = selected * algorithmic_bytes_per_frame(wl.V, wl.beam)
+    achieved = bytes_per_launch / (launch_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        pmc = json.load(open(PMC_FILE))
+        if pmc.get("kernel_sha") == kernel_sha() and pmc.get("storage") == args.storage:
+            traffic = int(pmc["hbm_bytes_per_launch"])
+    ws_bytes = int(dec.workspace.numel())
+    pages_high = int(stats[:, 3].max()) if paged else None
+    result = {
+        "metric": "decoded frames/sec (B*T/s) offline + p50 streaming chunk latency; % HBM peak",
+        "value": round(value, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B} T={wl.T} V={wl.V} beam={wl.beam} "
+                               f"nbest={wl.nbest} threshold={wl.threshold} "
+                               f"max_out_len={wl.max_out_len} storage={args.storage}",
+                   "global_batch": wl.B, "seq_len": wl.T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_kernel (+ select_kernel, timed together per call)",
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "launch_ms": round(launch_ms, 4)},
+        "decode": {"selected_frames": selected, "fallback_steps": int(stats[:, 4].sum()),
+                   "merge_verifications": int(stats[:, 5].sum()),
+                   "workspace_bytes": ws_bytes, "paged_pages_high_per_row": pages_high,
+                   "kernel_sha": kernel_sha()},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(x, lens, wl, args.cpu_seconds)
+    del x
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("[bench] streaming latency, 256 streams")
+        result["streaming"] = streaming_latency()
+        log("[bench] other workloads")
+        result["other_workloads"] = other_workloads()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

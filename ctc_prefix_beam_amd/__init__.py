@@ -23,7 +23,9 @@ LIB_PATH = os.path.join(_HERE, "libctcpb.so")
 FLAT, PAGED = 0, 1
 EXPORTS = ("ctcpb_workspace_size", "ctcpb_decode_offline", "ctcpb_state_size",
            "ctcpb_stream_init", "ctcpb_stream_reset", "ctcpb_stream_chunk", "ctcpb_read_state",
-           "ctcpb_last_error", "ctcpb_version")
+           "ctcpb_row_stats", "ctcpb_last_error", "ctcpb_version")
+STAT_FIELDS = ("frames", "selected", "status", "pages_high", "fallbacks", "verifies", "common_prefix",
+               "shared_pages")
 
 
 class CtcpbConfig(ctypes.Structure):
@@ -72,7 +74,8 @@ def lib():
         L.ctcpb_stream_reset.argtypes = [cfgp, p, sz, i32, p, i32, p]
         L.ctcpb_stream_chunk.argtypes = [cfgp, p, sz, i32, p, i64, i64, i32, p, i32, p]
         L.ctcpb_read_state.argtypes = [cfgp, p, sz, i32, p, i32, p, p, p, p]
-        for name in EXPORTS[:-2]:
+        L.ctcpb_row_stats.argtypes = [cfgp, p, sz, i32, i32, p, p]
+        for name in EXPORTS[:-2]:  # all but the two string getters
             getattr(L, name).restype = ctypes.c_int
         L.ctcpb_last_error.restype = ctypes.c_char_p
         L.ctcpb_last_error.argtypes = []
@@ -153,7 +156,16 @@ class OfflineDecoder:
             ctypes.byref(c), _ptr(log_prob), log_prob.stride(0), log_prob.stride(1), B, T,
             _ptr(seq_lengths), _ptr(self.workspace), self.workspace.numel(), _ptr(toks),
             _ptr(lens), _ptr(scores), _stream(stream)))
+        self._last = (c, B, T)
         return toks, lens, scores
+
+    def row_stats(self, stream=None) -> torch.Tensor:
+        """Per-row counters of the last decode, int32 (B, 8): see STAT_FIELDS."""
+        c, B, T = self._last
+        out = torch.empty((B, 8), dtype=torch.int32, device=self.workspace.device)
+        _check(lib().ctcpb_row_stats(ctypes.byref(c), _ptr(self.workspace), self.workspace.numel(),
+                                     B, T, _ptr(out), _stream(stream)))
+        return out
 
 
 def decode_offline(log_prob, seq_lengths, **kw):
@@ -199,6 +211,13 @@ class StreamPool:
             ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
             _ptr(log_prob_chunk), log_prob_chunk.stride(0), log_prob_chunk.stride(1), T,
             _ptr(rows), n, _stream(stream)))
+
+    def row_stats(self, stream=None) -> torch.Tensor:
+        """Per-stream counters, int32 (num_streams, 8): see STAT_FIELDS."""
+        out = torch.empty((self.num_streams, 8), dtype=torch.int32, device=self.state.device)
+        _check(lib().ctcpb_row_stats(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
+                                     self.num_streams, 0, _ptr(out), _stream(stream)))
+        return out
 
     def read(self, rows: torch.Tensor | None = None, stream=None):
         n = self.num_streams if rows is None else rows.numel()

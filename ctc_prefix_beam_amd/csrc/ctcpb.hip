@@ -95,11 +95,19 @@ struct Beam {
   uint64_t h, hp;
 };
 
+constexpr int kProfBase = 32;   // header word of the first phase counter
+constexpr int kProfSlots = 8;
+
 struct Ctx {
-  const Params* P;
+  Layout L;       // copied from the kernel arguments (never address-taken)
+  int N, mol;
+  int* out_tokens;
+  int* out_lengths;
+  float* out_scores;
   char* base;
   int* hdr;
-  float* row[2];
+  float* row0;    // frame rows, double-buffered by frame parity
+  float* row1;
   int8_t* rank;
   int* Rc;
   float* Rl;
@@ -124,7 +132,27 @@ struct Ctx {
   int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
   int* clist;     // flat: global
   int* pages;     // paged: global
+#ifdef CTCPB_PHASE_PROF
+  uint64_t prof[kProfSlots];
+  uint64_t prof_t;
+#endif
 };
+
+// Optional per-phase cycle counters (build with -DCTCPB_PHASE_PROF): the
+// shader clock is read at phase boundaries and the deltas are summed into
+// header words kProfBase.. of the row (a diagnostics build, not the product).
+#ifdef CTCPB_PHASE_PROF
+#define PROF_MARK(slot)                                                       \
+  do {                                                                        \
+    const uint64_t now_ = clock64();                                          \
+    if (lane_id() == 0) C.prof[slot] += now_ - C.prof_t;                      \
+    C.prof_t = now_;                                                          \
+  } while (0)
+#else
+#define PROF_MARK(slot) \
+  do {                  \
+  } while (0)
+#endif
 
 // LDS-only ordering between the lanes of this wave (no wait on global memory).
 __device__ __forceinline__ void lds_sync() {
@@ -134,7 +162,7 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 __device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, int slot, int pos) {
-  const Layout& L = C.P->L;
+  const Layout& L = C.L;
   if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.cap + pos];
   const int page = tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
   if (page < 0) return -1;  // only after a row ran out of pages
@@ -142,52 +170,34 @@ __device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, 
 }
 
 // ----------------------------------------------------------------- frames --
-__device__ __forceinline__ void load_row_now(const float* g, float* s, int V, int vec4) {
+// Asynchronous copy of a frame row from global memory straight into LDS
+// (global_load_lds: lane l of each wave-wide load lands at base + 16 l, or
+// base + 4 l for the 4-byte variant, so coalesced reads stay contiguous).
+// The data is usable after row_fetch_wait().
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void row_fetch_async(const float* g, float* s, int V, int vec4) {
   const int lane = lane_id();
   if (vec4) {
-    const float4* g4 = reinterpret_cast<const float4*>(g);
-    float4* s4 = reinterpret_cast<float4*>(s);
-    for (int i = lane; i < (V >> 2); i += kWave) s4[i] = g4[i];
-  } else {
-    for (int i = lane; i < V; i += kWave) s[i] = g[i];
-  }
-}
-
-struct RowPrefetch {
-  float4 v[kPrefetch4];
-  const float* g;
-  int active;
-};
-
-__device__ __forceinline__ void prefetch_issue(RowPrefetch& pf, const float* g, int V, int vec4) {
-  const int lane = lane_id();
-  pf.g = g;
-  pf.active = (g != nullptr) && vec4 && (V >> 2) <= kPrefetch4 * kWave;
-  if (pf.active) {
-    const float4* g4 = reinterpret_cast<const float4*>(g);
     const int n4 = V >> 2;
-#pragma unroll
-    for (int j = 0; j < kPrefetch4; j++) {
-      const int i = lane + j * kWave;
-      if (i < n4) pf.v[j] = g4[i];
+    for (int i = 0; i * kWave < n4; i++) {
+      const int idx = i * kWave + lane;
+      if (idx < n4)
+        __builtin_amdgcn_global_load_lds(g + (int64_t)idx * 4, (lds_ptr_t)(s + i * 4 * kWave), 16,
+                                         0, 0);
+    }
+  } else {
+    for (int i = 0; i * kWave < V; i++) {
+      const int idx = i * kWave + lane;
+      if (idx < V) __builtin_amdgcn_global_load_lds(g + idx, (lds_ptr_t)(s + i * kWave), 4, 0, 0);
     }
   }
 }
 
-__device__ __forceinline__ void prefetch_commit(RowPrefetch& pf, float* s, int V, int vec4) {
-  if (pf.g == nullptr) return;
-  if (pf.active) {
-    const int lane = lane_id();
-    float4* s4 = reinterpret_cast<float4*>(s);
-    const int n4 = V >> 2;
-#pragma unroll
-    for (int j = 0; j < kPrefetch4; j++) {
-      const int i = lane + j * kWave;
-      if (i < n4) s4[i] = pf.v[j];
-    }
-  } else {
-    load_row_now(pf.g, s, V, vec4);
-  }
+__device__ __forceinline__ void row_fetch_wait() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
 }
 
 // ------------------------------------------------------ generic selection --
@@ -195,7 +205,7 @@ __device__ __forceinline__ void prefetch_commit(RowPrefetch& pf, float* s, int V
 // distinct or 0 (= no candidate).  Items are produced 64 at a time by gen(i)
 // for i in [0, n); the buffer is sorted and cut back to K whenever it fills.
 template <typename Gen>
-__device__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
+__device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
   const int lane = lane_id();
   uint64_t thr = comp_floor();
   int cnt = 0;
@@ -223,8 +233,8 @@ __device__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
 // ------------------------------------------------------- vocabulary top-K --
 // The best K non-blank labels of the frame by (lp desc, label asc), written to
 // Rc / Rl; rank[label] = position (or -1).  prevK = size of the previous list.
-__device__ void vocab_topk(const Ctx& C, const float* row, int K, int prevK) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void vocab_topk(const Ctx& C, const float* row, int K, int prevK) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int V = L.V, blank = L.blank;
   const int n = V - 1;
@@ -285,8 +295,8 @@ __device__ void vocab_topk(const Ctx& C, const float* row, int K, int prevK) {
 }
 
 // --------------------------------------------------------------- step 0 ----
-__device__ void first_step(const Ctx& C, Beam& b, const float* row, int g, int nR) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* row, int g, int nR) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, blank = L.blank;
   const int nb = W > 1 ? W - 1 : 1;
@@ -370,8 +380,8 @@ struct Winner {
 // the step is regenerated from the per-beam values left in LDS and streamed
 // through stream_topk.  Used when the pruned candidate set cannot be proven
 // to contain the top W.
-__device__ int full_select(const Ctx& C, const float* row) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ int full_select(const Ctx& C, const float* row) {
+  const Layout& L = C.L;
   const int W = L.W, V = L.V, blank = L.blank;
   auto gen = [&](int64_t i) -> uint64_t {
     const int k = (int)(i / V);
@@ -394,9 +404,9 @@ __device__ int full_select(const Ctx& C, const float* row) {
   return stream_topk(C, W, (int64_t)W * V, gen);
 }
 
-__device__ Winner beam_step(const Ctx& C, Beam& b, const float* row, int g, int step, int nR,
+__device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, int g, int step, int nR,
                             int complete) {
-  const Layout& L = C.P->L;
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, V = L.V, blank = L.blank;
   const bool lv = lane < W && b.live;
@@ -489,46 +499,54 @@ __device__ Winner beam_step(const Ctx& C, Beam& b, const float* row, int g, int 
   const int incl = wave_incl_scan(lane < W ? nk : 0);
   const int M = __shfl(incl, 63, 64);
   if (lane < W) C.offs[lane] = incl - nk;
-  const bool sb = keyb > kNeg && keyb >= tau0;
-  const bool sc = keyc > kNeg && keyc >= tau0;
   lds_sync();
 
-  bool need_full = M + 2 * W > kBuf;
-  if (!need_full) {
-    for (int q = lane; q < M; q += kWave) {
-      int a = 0, z = W - 1;
-      while (a < z) {
-        const int mid = (a + z + 1) >> 1;
-        if (C.offs[mid] <= q) a = mid;
-        else z = mid - 1;
-      }
-      const int rho = q - C.offs[a];
-      const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
-      const int c = C.Rc[rho];
-      C.buf[q] = ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + c));
+  PROF_MARK(2);
+  // the candidates: ranked labels above tau0 of every beam, then two
+  // special slots per beam (blank, repeated label)
+  const int ncand = M + 2 * W;
+  auto candidate = [&](int64_t q64) -> uint64_t {
+    const int q = (int)q64;
+    if (q >= M) {
+      const int j = q - M, kk = j >> 1;
+      const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
+      const int c = (j & 1) ? C.lastk[kk] : blank;
+      return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
     }
-    if (lane < W) {
-      C.buf[M + 2 * lane] = sb ? compose(keyb, (uint32_t)(lane * V + blank)) : 0ull;
-      C.buf[M + 2 * lane + 1] = sc ? compose(keyc, (uint32_t)(lane * V + last)) : 0ull;
+    int a = 0, z = W - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (C.offs[mid] <= q) a = mid;
+      else z = mid - 1;
     }
+    const int rho = q - C.offs[a];
+    const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
+    return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
+  };
+  if (ncand <= kBuf) {
+    for (int q = lane; q < ncand; q += kWave) C.buf[q] = candidate(q);
     lds_sync();
-    wave_sort_lds(C.buf, M + 2 * W);
+    wave_sort_lds(C.buf, ncand);
     lds_sync();
-    if (!complete) {
-      // labels outside the ranked list score at most A_k + (last ranked lp);
-      // they must stay strictly below the W-th selected key
-      const uint64_t wl = C.buf[W - 1];
-      const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
-      const float bound = C.Rl[nR - 1];
-      const bool bad = lv && !((bound + A) < keyW);
-      need_full = __ballot(bad) != 0ull;
-    }
+  } else {
+    stream_topk(C, W, ncand, candidate);
+  }
+  bool need_full = false;
+  if (!complete) {
+    // labels outside the ranked list score at most A_k + (last ranked lp);
+    // they must stay strictly below the W-th selected key
+    const uint64_t wl = C.buf[W - 1];
+    const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
+    const float bound = C.Rl[nR - 1];
+    const bool bad = lv && !((bound + A) < keyW);
+    need_full = __ballot(bad) != 0ull;
   }
   if (need_full) {
     full_select(C, row);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
   }
 
+  PROF_MARK(3);
   // winners in rank order (slot r = rank r), sec. 3.4.5
   const uint64_t wc = lane < W ? C.buf[lane] : 0ull;
   Winner w;
@@ -630,6 +648,7 @@ __device__ Winner beam_step(const Ctx& C, Beam& b, const float* row, int g, int 
   }
   nb.parent = npar;
   if (lane < W) b = nb;
+  PROF_MARK(4);
   return w;
 }
 
@@ -637,8 +656,8 @@ __device__ Winner beam_step(const Ctx& C, Beam& b, const float* row, int g, int 
 // Flat (sec. 3.1, 7): slot r of parity p receives its source's tokens from
 // parity p^1 plus the new label.  Positions below the common prefix that all
 // live beams of two steps ago shared are already in place and are skipped.
-__device__ void store_flat(const Ctx& C, int step, const Winner& w) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner& w) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, blank = L.blank;
   const int p = step & 1, q = p ^ 1;
@@ -692,8 +711,8 @@ __device__ void store_flat(const Ctx& C, int step, const Winner& w) {
 
 // Grow the common prefix of the live beams of parity p (flat store), reading
 // the next 64 positions of every live row.
-__device__ void advance_cpl_flat(const Ctx& C, int p, const Beam& b) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, const Beam& b) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W;
   wave_sync();
@@ -727,8 +746,8 @@ __device__ void advance_cpl_flat(const Ctx& C, int p, const Beam& b) {
 // Paged (sec. 3.4.5 paged variant, 4.2): fork every slot's block-table row
 // from its source (pages acquired / released by reference count), then
 // append the new label on a fresh page or a copy of the shared partial page.
-__device__ void store_paged(const Ctx& C, int step, const Winner& w, const Beam& nb) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w, const Beam& nb) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
   const int p = step & 1, q = p ^ 1;
@@ -839,12 +858,11 @@ __device__ void store_paged(const Ctx& C, int step, const Winner& w, const Beam&
 
 // ------------------------------------------------------------------ output --
 // N best of the current beams, (score desc, slot asc), tokens of `parity`.
-__device__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int* tab,
+__device__ __forceinline__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int* tab,
                               int out_row) {
-  const Layout& L = C.P->L;
-  const Params& P = *C.P;
+  const Layout& L = C.L;
   const int lane = lane_id();
-  const int W = L.W, N = P.N, mol = P.max_out_len;
+  const int W = L.W, N = C.N, mol = C.mol;
   const bool lv = lane < W && b.live;
   int rk = 0;
   for (int j = 0; j < W; j++) {
@@ -861,12 +879,12 @@ __device__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int
   const int len = __shfl(b.len, s < 0 ? 0 : s, 64);
   const float sc = __shfl(b.score, s < 0 ? 0 : s, 64);
   if (lane < N) {
-    P.out_lengths[(int64_t)out_row * N + lane] = s < 0 ? 0 : len;
-    P.out_scores[(int64_t)out_row * N + lane] = s < 0 ? kNeg : sc;
+    C.out_lengths[(int64_t)out_row * N + lane] = s < 0 ? 0 : len;
+    C.out_scores[(int64_t)out_row * N + lane] = s < 0 ? kNeg : sc;
     slot_of[40 + lane] = s < 0 ? 0 : len;
   }
   lds_sync();
-  int* ot = P.out_tokens + (int64_t)out_row * N * mol;
+  int* ot = C.out_tokens + (int64_t)out_row * N * mol;
   const int total = N * mol;
   for (int base = 0; base < total; base += 8 * kWave) {
     int val[8];
@@ -889,9 +907,9 @@ __device__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int
 }
 
 // ---------------------------------------------------------- state helpers --
-__device__ void beam_load(const Ctx& C, Beam& b) {
+__device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
   const int lane = lane_id();
-  const char* a = C.base + C.P->L.o_beam;
+  const char* a = C.base + C.L.o_beam;
   if (lane < kMaxBeam) {
     b.pb = reinterpret_cast<const float*>(a + BeamArrays::pb)[lane];
     b.pnb = reinterpret_cast<const float*>(a + BeamArrays::pnb)[lane];
@@ -907,16 +925,16 @@ __device__ void beam_load(const Ctx& C, Beam& b) {
     b.live = 0;
     b.pb = b.pnb = b.score = kNeg;
     b.len = 0;
-    b.last = C.P->L.blank;
+    b.last = C.L.blank;
     b.parent = b.last2 = -1;
     b.h = kHashEmpty;
     b.hp = 0;
   }
 }
 
-__device__ void beam_store(const Ctx& C, const Beam& b) {
+__device__ __forceinline__ void beam_store(const Ctx& C, const Beam& b) {
   const int lane = lane_id();
-  char* a = C.base + C.P->L.o_beam;
+  char* a = C.base + C.L.o_beam;
   if (lane < kMaxBeam) {
     reinterpret_cast<float*>(a + BeamArrays::pb)[lane] = b.pb;
     reinterpret_cast<float*>(a + BeamArrays::pnb)[lane] = b.pnb;
@@ -932,7 +950,7 @@ __device__ void beam_store(const Ctx& C, const Beam& b) {
 }
 
 // The empty hypothesis in slot 0, every other slot dead (sec. 13).
-__device__ void beam_fresh(Beam& b, int blank) {
+__device__ __forceinline__ void beam_fresh(Beam& b, int blank) {
   const int lane = lane_id();
   b.live = lane == 0;
   b.pb = lane == 0 ? 0.0f : kNeg;
@@ -946,14 +964,20 @@ __device__ void beam_fresh(Beam& b, int blank) {
   b.hp = 0;
 }
 
-__device__ Ctx make_ctx(const Params& P, char* base, char* smem) {
+__device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N, int mol,
+                                        int* out_tokens, int* out_lengths, float* out_scores,
+                                        char* base, char* smem) {
   Ctx C;
-  C.P = &P;
+  C.L = L;
+  C.N = N;
+  C.mol = mol;
+  C.out_tokens = out_tokens;
+  C.out_lengths = out_lengths;
+  C.out_scores = out_scores;
   C.base = base;
   C.hdr = reinterpret_cast<int*>(base);
-  const LdsPlan& S = P.S;
-  C.row[0] = reinterpret_cast<float*>(smem + S.row0);
-  C.row[1] = reinterpret_cast<float*>(smem + S.row1);
+  C.row0 = reinterpret_cast<float*>(smem + S.row0);
+  C.row1 = reinterpret_cast<float*>(smem + S.row1);
   C.rank = reinterpret_cast<int8_t*>(smem + S.rank);
   C.Rc = reinterpret_cast<int*>(smem + S.Rc);
   C.Rl = reinterpret_cast<float*>(smem + S.Rl);
@@ -976,14 +1000,14 @@ __device__ Ctx make_ctx(const Params& P, char* base, char* smem) {
   C.ref = reinterpret_cast<int*>(smem + S.ref);
   C.fstk = reinterpret_cast<int*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
-  C.clist = reinterpret_cast<int*>(base + P.L.o_clist);
-  C.pages = reinterpret_cast<int*>(base + P.L.o_pages);
+  C.clist = reinterpret_cast<int*>(base + L.o_clist);
+  C.pages = reinterpret_cast<int*>(base + L.o_pages);
   return C;
 }
 
 // Paged metadata: global row region <-> LDS.
-__device__ void paged_meta_io(const Ctx& C, bool to_lds) {
-  const Layout& L = C.P->L;
+__device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
+  const Layout& L = C.L;
   const int lane = lane_id();
   int* gt = reinterpret_cast<int*>(C.base + L.o_tab);
   int* gr = reinterpret_cast<int*>(C.base + L.o_ref);
@@ -1008,7 +1032,7 @@ __device__ void paged_meta_io(const Ctx& C, bool to_lds) {
 }
 
 // Header fields <-> LDS scalars.
-__device__ void scal_from_header(const Ctx& C) {
+__device__ __forceinline__ void scal_from_header(const Ctx& C) {
   const int lane = lane_id();
   if (lane == 0) {
     const int* h = C.hdr;
@@ -1027,7 +1051,7 @@ __device__ void scal_from_header(const Ctx& C) {
   }
 }
 
-__device__ void scal_to_header(const Ctx& C, int step, int last_t) {
+__device__ __forceinline__ void scal_to_header(const Ctx& C, int step, int last_t) {
   const int lane = lane_id();
   if (lane == 0) {
     int* h = C.hdr;
@@ -1085,7 +1109,7 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
 template <bool STREAM>
 __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
-  const Layout& L = P.L;
+  const Layout L = P.L;
   const int lane = lane_id();
   const int row_i = blockIdx.x;
   int srow = row_i;
@@ -1094,7 +1118,8 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
     if (srow < 0 || srow >= P.num_rows) return;
   }
   char* base = P.state + (int64_t)srow * L.row_bytes;
-  Ctx C = make_ctx(P, base, smem);
+  Ctx C = make_ctx(L, P.S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
+                   smem);
   const int W = L.W, V = L.V;
 
   for (int c = lane; c < V; c += kWave) C.rank[c] = -1;
@@ -1125,22 +1150,31 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
 
   const int K = min(V - 1, 2 * W + 3);  // ranked labels per frame
   const int complete = K == V - 1;
-  auto frame_ptr = [&](int f) -> const float* {
-    if (STREAM) return P.lp + (int64_t)row_i * P.stride_b + (int64_t)f * P.stride_t;
-    return P.lp + (int64_t)srow * P.stride_b + (int64_t)sel[f] * P.stride_t;
+  const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
+  const int64_t stride_t = P.stride_t;
+  const int vec4 = P.vec4;
+  auto frame_ptr = [=](int f) -> const float* {
+    return lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t;
   };
-  auto frame_index = [&](int f) -> int { return STREAM ? step + f : sel[f]; };
 
   int prevK = 0;
-  if (nframes > 0) load_row_now(frame_ptr(0), C.row[0], V, P.vec4);
-  RowPrefetch pf;
+  if (nframes > 0) row_fetch_async(frame_ptr(0), C.row0, V, vec4);
   const int step0 = step;
   for (int f = 0; f < nframes; f++) {
-    const float* row = C.row[f & 1];
-    const int t = STREAM ? step0 + f : frame_index(f);
-    prefetch_issue(pf, f + 1 < nframes ? frame_ptr(f + 1) : nullptr, V, P.vec4);
+    const float* row = (f & 1) ? C.row1 : C.row0;
+    const int t = STREAM ? step0 + f : sel[f];
+#ifdef CTCPB_PHASE_PROF
+    if (f == 0) {
+      for (int i = 0; i < kProfSlots; i++) C.prof[i] = 0;
+      C.prof_t = clock64();
+    }
+#endif
+    row_fetch_wait();  // this frame's row is in LDS
+    PROF_MARK(0);
+    if (f + 1 < nframes) row_fetch_async(frame_ptr(f + 1), (f & 1) ? C.row0 : C.row1, V, vec4);
     lds_sync();
     vocab_topk(C, row, K, prevK);
+    PROF_MARK(1);
     prevK = K;
     if (step == 0) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
@@ -1157,10 +1191,17 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
         if ((step & 15) == 15) advance_cpl_flat(C, step & 1, b);
       }
     }
+    PROF_MARK(5);
     last_t = t;
     step++;
-    prefetch_commit(pf, C.row[(f + 1) & 1], V, P.vec4);
   }
+  row_fetch_wait();
+#ifdef CTCPB_PHASE_PROF
+  if (lane == 0 && nframes > 0) {
+    uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
+    for (int i = 0; i < kProfSlots; i++) dst[i] = C.prof[i];
+  }
+#endif
   lds_sync();
 
   if (STREAM) {
@@ -1177,7 +1218,7 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
 
 // Fresh streams (stream_init / stream_reset): one block per stream.
 __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
-  const Layout& L = P.L;
+  const Layout L = P.L;
   const int lane = lane_id();
   int srow = P.rows ? P.rows[blockIdx.x] : (int)blockIdx.x;
   if (srow < 0 || srow >= P.num_rows) return;
@@ -1186,7 +1227,7 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
   if (lane < kHdrInts) hdr[lane] = 0;
   if (lane == 0) hdr[kLastT] = -1;
   Ctx C;
-  C.P = &P;
+  C.L = L;
   C.base = base;
   Beam b;
   beam_fresh(b, L.blank);
@@ -1202,11 +1243,12 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
 // read_state: report the N best of each listed stream without changing it.
 __global__ __launch_bounds__(64) void read_state_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
-  const Layout& L = P.L;
+  const Layout L = P.L;
   int srow = P.rows ? P.rows[blockIdx.x] : (int)blockIdx.x;
   if (srow < 0 || srow >= P.num_rows) return;
   char* base = P.state + (int64_t)srow * L.row_bytes;
-  Ctx C = make_ctx(P, base, smem);
+  Ctx C = make_ctx(L, P.S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
+                   smem);
   Beam b;
   beam_load(C, b);
   const int step = C.hdr[kStep];
@@ -1214,6 +1256,22 @@ __global__ __launch_bounds__(64) void read_state_kernel(Params P) {
   const int parity = step > 0 ? (step - 1) & 1 : 0;
   const int* tab = reinterpret_cast<const int*>(base + L.o_tab);
   write_outputs(C, b, parity, tab, (int)blockIdx.x);
+}
+
+// Diagnostics: copy per-row header counters out (one thread per row).
+__global__ __launch_bounds__(64) void row_stats_kernel(Params P) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= P.num_rows) return;
+  const int* h = reinterpret_cast<const int*>(P.state + (int64_t)i * P.L.row_bytes);
+  int* o = P.out_lengths + (int64_t)i * 8;
+  o[0] = h[kStep];
+  o[1] = h[kNSel];
+  o[2] = h[kStatus];
+  o[3] = h[kPagesHigh];
+  o[4] = h[kFallbacks];
+  o[5] = h[kVerifies];
+  o[6] = max(h[kCpl0], h[kCpl1]);
+  o[7] = max(h[kPcp0], h[kPcp1]);
 }
 
 }  // namespace ctcpb
@@ -1517,6 +1575,27 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
   const int lds = P.S.scal + kScalCount * 4;
   if (int rc = launch(read_state_kernel, n_rows, 64, lds, static_cast<hipStream_t>(stream), P,
                       "read_state_kernel"))
+    return rc;
+  return ok();
+}
+
+int ctcpb_row_stats(const ctcpb_config* cfg, const void* buf, size_t buf_bytes, int32_t num_rows,
+                    int32_t max_T, int32_t* out, void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  if (num_rows < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "num_rows and max_T must be >= 0");
+  if (num_rows == 0) return ok();
+  if (!buf || !out) return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
+  const Layout L = max_T > 0 ? layout_for(R, max_T, max_T) : layout_for(R, R.cap_stream, 0);
+  if (buf_bytes < (size_t)num_rows * (size_t)L.row_bytes)
+    return fail(CTCPB_ERR_TOO_SMALL, "buffer smaller than the rows it should hold");
+  Params P{};
+  P.L = L;
+  P.num_rows = num_rows;
+  P.state = static_cast<char*>(const_cast<void*>(buf));
+  P.out_lengths = out;
+  if (int rc = launch(row_stats_kernel, (num_rows + 63) / 64, 64, 0,
+                      static_cast<hipStream_t>(stream), P, "row_stats_kernel"))
     return rc;
   return ok();
 }

@@ -39,6 +39,7 @@ enum HeaderField {
   kPagesHigh,     // paged: high-water mark of pages in use
   kFallbacks,     // steps that needed the full beam x vocab selection
   kVerifies,      // exact token comparisons made for the merge test
+  // words 32..47: optional per-phase cycle counters of a diagnostics build
 };
 
 enum Status { kStatusOutOfPages = 1 };

@@ -125,6 +125,17 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
                      int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
                      void* stream);
 
+/* Per-row counters a decode left in an offline workspace (max_T = the max_T
+ * of that decode) or in a streaming state blob (max_T = 0), for diagnostics:
+ * out (device int32 [num_rows][8]) receives per row
+ *   [0] frames decoded  [1] frames selected (offline)  [2] status bits
+ *   (1 = a paged row ran out of pages)  [3] paged: most pages in use at once
+ *   [4] steps that needed the full beam x vocab selection  [5] exact token
+ *   comparisons made for the merge test  [6] common token prefix of the live
+ *   beams (flat)  [7] leading pages shared by every live beam (paged). */
+int ctcpb_row_stats(const ctcpb_config* cfg, const void* buf, size_t buf_bytes, int32_t num_rows,
+                    int32_t max_T, int32_t* out, void* stream);
+
 /* Human-readable description of the last error on this thread ("" if none). */
 const char* ctcpb_last_error(void);
 
