@@ -59,9 +59,13 @@ constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 1
 
 // LDS carve-up (byte offsets), computed on the host from the dimensions.
 struct LdsPlan {
-  int row0, row1, rank, Rc, Rl, buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh,
-      newlen, nchild, childc, scal, tab, ref, fstk, tail, total;
+  int slot0, slot_stride, slot_Rc, slot_Rl, slot_rank;  // ring of frame slots
+  int nslot, nprod;                                     // slots, producer waves
+  int scr, flags;                                       // producer scratch, hand-off flags
+  int buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh, newlen, nchild, childc, scal,
+      tab, ref, fstk, tail, tlen, total;
 };
+constexpr int kMaxSlots = 8;
 
 struct Params {
   Layout L;
@@ -85,7 +89,8 @@ struct Params {
 // Per-row scalars kept in LDS while a row is decoded (mirrors of header fields).
 enum : int {
   kScalFreeTop = 0, kScalNextFree, kScalStatus, kScalHigh, kScalLive0, kScalLive1, kScalCpl0,
-  kScalCpl1, kScalPcp0, kScalPcp1, kScalFallbacks, kScalVerifies, kScalCount
+  kScalCpl1, kScalPcp0, kScalPcp1, kScalFallbacks, kScalVerifies, kScalSurv, kScalWide,
+  kScalCount
 };
 
 struct Beam {
@@ -106,8 +111,6 @@ struct Ctx {
   float* out_scores;
   char* base;
   int* hdr;
-  float* row0;    // frame rows, double-buffered by frame parity
-  float* row1;
   int8_t* rank;
   int* Rc;
   float* Rl;
@@ -130,6 +133,7 @@ struct Ctx {
   int* ref;
   int* fstk;
   int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
+  int* tlen;      // paged: valid leading entries of each block-table row, both parities
   int* clist;     // flat: global
   int* pages;     // paged: global
 #ifdef CTCPB_PHASE_PROF
@@ -205,7 +209,7 @@ __device__ __forceinline__ void row_fetch_wait() {
 // distinct or 0 (= no candidate).  Items are produced 64 at a time by gen(i)
 // for i in [0, n); the buffer is sorted and cut back to K whenever it fills.
 template <typename Gen>
-__device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
+__device__ __forceinline__ int stream_topk_buf(uint64_t* buf, int K, int64_t n, Gen gen) {
   const int lane = lane_id();
   uint64_t thr = comp_floor();
   int cnt = 0;
@@ -214,82 +218,110 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
     const uint64_t x = i < n ? gen(i) : 0ull;
     const bool pass = x > thr;
     const uint64_t m = __ballot(pass);
-    if (pass) C.buf[cnt + lanes_below(m)] = x;
+    if (pass) buf[cnt + lanes_below(m)] = x;
     cnt += __popcll(m);
     if (cnt > kBuf - kWave) {
       lds_sync();
-      wave_sort_lds(C.buf, cnt);
+      wave_sort_lds(buf, cnt);
       lds_sync();
       cnt = cnt < K ? cnt : K;
-      if (cnt == K) thr = C.buf[K - 1];
+      if (cnt == K) thr = buf[K - 1];
     }
   }
   lds_sync();
-  wave_sort_lds(C.buf, cnt);
+  wave_sort_lds(buf, cnt);
   lds_sync();
   return cnt < K ? cnt : K;
 }
 
+template <typename Gen>
+__device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen gen) {
+  return stream_topk_buf(C.buf, K, n, gen);
+}
+
 // ------------------------------------------------------- vocabulary top-K --
-// The best K non-blank labels of the frame by (lp desc, label asc), written to
-// Rc / Rl; rank[label] = position (or -1).  prevK = size of the previous list.
-__device__ __forceinline__ void vocab_topk(const Ctx& C, const float* row, int K, int prevK) {
-  const Layout& L = C.L;
+// Ranks one frame (run by a producer wave): the best K non-blank labels by
+// (lp desc, label asc) into Rc / Rl, rank[label] = position (-1 elsewhere).
+// A threshold that at least K labels reach is found first (the K-th largest
+// of every lane's two best keys, by a radix search with ballots); the labels
+// at or above it are gathered and ranked by counting.  prevK = size of the
+// list this slot held before (its rank entries are cleared).
+__device__ __forceinline__ uint32_t sortable_bits(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ void rank_frame(const float* row, int V, int blank, int K, int prevK,
+                                           int* Rc, float* Rl, int8_t* rank, uint64_t* scr) {
   const int lane = lane_id();
-  const int V = L.V, blank = L.blank;
-  const int n = V - 1;
-  for (int r = lane; r < prevK; r += kWave) C.rank[C.Rc[r]] = -1;
-  auto comp = [&](int i) -> uint64_t {
-    const int c = i + (i >= blank ? 1 : 0);
-    return compose(row[c], (uint32_t)c);
-  };
-  int got;
-  if (n <= kBuf) {
-    for (int i = lane; i < n; i += kWave) C.buf[i] = comp(i);
-    lds_sync();
-    wave_sort_lds(C.buf, n);
-    lds_sync();
-    got = n < K ? n : K;
-  } else {
-    // pass 1: the two best keys of every lane; the K-th best of those 128
-    // is a lower bound of the frame's K-th best key (K <= 128)
-    uint64_t a = 0, b = 0;
-    for (int i = lane; i < n; i += kWave) {
-      const uint64_t x = comp(i);
-      const uint64_t lo = x < a ? x : a;
-      a = x > a ? x : a;
-      b = lo > b ? lo : b;
-    }
-    uint64_t v[2] = {a, b};
-    wave_sort_desc<2>(v);
-    const int pos = K - 1;
-    const uint64_t vsel = (pos & 1) ? v[1] : v[0];
-    const uint64_t thr = shfl_u64(vsel, pos >> 1);
-    // pass 2: gather every key >= thr
-    int cnt = 0;
-    for (int base = 0; base < n; base += kWave) {
-      const int i = base + lane;
-      const uint64_t x = i < n ? comp(i) : 0ull;
-      const bool pass = x >= thr && x != 0ull;
-      const uint64_t m = __ballot(pass);
-      const int p = cnt + lanes_below(m);
-      if (pass && p < kBuf) C.buf[p] = x;
-      cnt += __popcll(m);
-    }
-    lds_sync();
-    if (cnt <= kBuf) {
-      wave_sort_lds(C.buf, cnt);
-      lds_sync();
-      got = K;
-    } else {
-      got = stream_topk(C, K, n, comp);
-    }
+  for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
+  // pass 1: two best keys per lane
+  uint32_t a = 0u, b = 0u;
+  for (int c = lane; c < V; c += kWave) {
+    const uint32_t u = c == blank ? 0u : sortable_bits(row[c]);
+    const uint32_t lo = u < a ? u : a;
+    a = u > a ? u : a;
+    b = lo > b ? lo : b;
   }
-  for (int r = lane; r < got; r += kWave) {
-    const int c = (int)comp_id(C.buf[r]);
-    C.Rc[r] = c;
-    C.Rl[r] = row[c];
-    C.rank[c] = (int8_t)r;
+  uint32_t thr = 0u;
+  for (int bit = 31; bit >= 0; bit--) {
+    const uint32_t cand = thr | (1u << bit);
+    const int cnt = __popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand));
+    if (cnt >= K) thr = cand;
+  }
+  // pass 2: every label at or above the threshold
+  int cnt = 0;
+  for (int base = 0; base < V; base += kWave) {
+    const int c = base + lane;
+    const uint32_t u = (c < V && c != blank) ? sortable_bits(row[c]) : 0u;
+    const bool pass = u != 0u && u >= thr;
+    const uint64_t m = __ballot(pass);
+    const int pos = cnt + lanes_below(m);
+    if (pass && pos < kBuf) scr[pos] = ((uint64_t)u << 32) | (uint32_t)(~c);
+    cnt += __popcll(m);
+  }
+  lds_sync();
+  if (cnt <= 2 * kWave) {
+    const uint64_t x0 = lane < cnt ? scr[lane] : 0ull;
+    const uint64_t x1 = lane + kWave < cnt ? scr[lane + kWave] : 0ull;
+    int rk0 = 0, rk1 = 0;
+    const int n0 = cnt < kWave ? cnt : kWave;
+    for (int j = 0; j < n0; j++) {
+      const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x0 >> 32), j) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x0, j);
+      rk0 += y > x0 ? 1 : 0;
+      rk1 += y > x1 ? 1 : 0;
+    }
+    for (int j = 0; j + kWave < cnt; j++) {
+      const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x1 >> 32), j) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x1, j);
+      rk0 += y > x0 ? 1 : 0;
+      rk1 += y > x1 ? 1 : 0;
+    }
+    if (lane < cnt && rk0 < K) {
+      const int c = (int)(~(uint32_t)x0);
+      Rc[rk0] = c;
+      Rl[rk0] = row[c];
+      rank[c] = (int8_t)rk0;
+    }
+    if (lane + kWave < cnt && rk1 < K) {
+      const int c = (int)(~(uint32_t)x1);
+      Rc[rk1] = c;
+      Rl[rk1] = row[c];
+      rank[c] = (int8_t)rk1;
+    }
+  } else {
+    auto gen = [&](int64_t i) -> uint64_t {
+      const int c = (int)i;
+      return c == blank ? 0ull : (((uint64_t)sortable_bits(row[c]) << 32) | (uint32_t)(~c));
+    };
+    const int got = stream_topk_buf(scr, K, V, gen);
+    for (int r = lane; r < got; r += kWave) {
+      const int c = (int)(~(uint32_t)scr[r]);
+      Rc[r] = c;
+      Rl[r] = row[c];
+      rank[c] = (int8_t)r;
+    }
   }
   lds_sync();
 }
@@ -361,6 +393,7 @@ __device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* r
       } else {
         C.ref[page] = 1;
         C.tab[(0 * W + lane) * L.max_lp + 0] = page;
+        C.tlen[lane] = 1;
         C.pages[(int64_t)page * L.ps] = b.last;
         C.tail[(0 * W + lane) * L.ps] = b.last;
       }
@@ -471,65 +504,143 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     C.lastk[lane] = last;
   }
 
-  // a lower bound tau0 of the W-th best key: beam k's first W ordinary labels
-  // all score at least A_k + Rl[W - 1 + excluded_k]
+  // ---- a tight lower bound tau0 of the W-th best key: each beam offers its
+  // two best candidates (blank slot, repeated-label slot, first two
+  // non-excluded ranked labels); the W-th largest of those 2W values has at
+  // least W candidates at or above it
   const int nPool = complete ? nR : nR - 1;
-  int nEx = 0;
-  if (lv) {
+  uint32_t fr0, fr1, fr2;  // in-pool ranks still open to this beam
+  {
+    uint32_t m[3];
 #pragma unroll
     for (int w = 0; w < 3; w++) {
-      uint32_t m = C.exm[lane * 3 + w];
+      uint32_t x = lv ? ~C.exm[lane * 3 + w] : 0u;
       const int lo = w * 32;
-      if (lo >= nPool) m = 0u;
-      else if (nPool - lo < 32) m &= (1u << (nPool - lo)) - 1u;
-      nEx += __popc(m);
+      if (lo >= nPool) x = 0u;
+      else if (nPool - lo < 32) x &= (1u << (nPool - lo)) - 1u;
+      m[w] = x;
+    }
+    fr0 = m[0];
+    fr1 = m[1];
+    fr2 = m[2];
+  }
+  auto first_bit = [](uint32_t a, uint32_t b, uint32_t c) -> int {
+    return a ? __builtin_ctz(a) : (b ? 32 + __builtin_ctz(b) : (c ? 64 + __builtin_ctz(c) : -1));
+  };
+  const int r0 = first_bit(fr0, fr1, fr2);
+  uint32_t g0 = fr0, g1 = fr1, g2 = fr2;
+  if (r0 >= 0) {
+    if (r0 < 32) g0 &= g0 - 1u;
+    else if (r0 < 64) g1 &= g1 - 1u;
+    else g2 &= g2 - 1u;
+  }
+  const int r1 = first_bit(g0, g1, g2);
+  const float o1 = r0 >= 0 ? C.Rl[r0] + A : kNeg;
+  const float o2 = r1 >= 0 ? C.Rl[r1] + A : kNeg;
+  const float shi = fmaxf(keyb, keyc), slo = fminf(keyb, keyc);
+  const float v1 = fmaxf(shi, o1);
+  const float v2 = fmaxf(fminf(shi, o1), fmaxf(slo, o2));
+  const uint32_t s1 = (lv && v1 > kNeg) ? sortable(v1) : 0u;
+  const uint32_t s2 = (lv && v2 > kNeg) ? sortable(v2) : 0u;
+  float tau0 = kNeg;
+  if (__popcll(__ballot(s1 != 0u)) + __popcll(__ballot(s2 != 0u)) >= W) {
+    uint32_t prefix = 0u;
+    for (int bit = 30; bit >= 0; bit--) {  // keys are negative: bit 31 is 0
+      const uint32_t cand = prefix | (1u << bit);
+      const int cnt = __popcll(__ballot(s1 >= cand)) + __popcll(__ballot(s2 >= cand));
+      if (cnt >= W) prefix = cand;
+    }
+    tau0 = unsortable(prefix);
+  }
+
+  // ---- every candidate at or above tau0 (ranked labels are sorted, so each
+  // beam's qualifying labels form a prefix of its list)
+  if (lane == 0) C.scal[kScalSurv] = 0;
+  lds_sync();
+  if (lv) {
+    if (keyb > kNeg && keyb >= tau0) {
+      const int p = atomicAdd(&C.scal[kScalSurv], 1);
+      if (p < kBuf) C.buf[p] = compose(keyb, (uint32_t)(lane * V + blank));
+    }
+    if (keyc > kNeg && keyc >= tau0) {
+      const int p = atomicAdd(&C.scal[kScalSurv], 1);
+      if (p < kBuf) C.buf[p] = compose(keyc, (uint32_t)(lane * V + last));
+    }
+    for (int r = 0; r < nPool; r += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(C.Rl + r);
+      const float lpv[4] = {q.x, q.y, q.z, q.w};
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int rr = r + j;
+        const float key = lpv[j] + A;
+        if (rr < nPool && key >= tau0) {
+          any = true;
+          const uint32_t open = rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
+          if (open & 1u) {
+            const int p = atomicAdd(&C.scal[kScalSurv], 1);
+            if (p < kBuf) C.buf[p] = compose(key, (uint32_t)(lane * V + C.Rc[rr]));
+          }
+        }
+      }
+      if (!any) break;
     }
   }
-  const int idx = W - 1 + nEx;
-  const float t0 = (lv && idx < nPool) ? C.Rl[idx] + A : kNeg;
-  const float tau0 = wave_max(t0);
-  // ranked labels of each beam scoring >= tau0 form a prefix of the list
-  int lo = 0, hi = lv ? nPool : 0;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (C.Rl[mid] + A >= tau0) lo = mid + 1;
-    else hi = mid;
-  }
-  const int nk = lo;
-  const int incl = wave_incl_scan(lane < W ? nk : 0);
-  const int M = __shfl(incl, 63, 64);
-  if (lane < W) C.offs[lane] = incl - nk;
   lds_sync();
+  const int nsurv = C.scal[kScalSurv];
 
   PROF_MARK(2);
-  // the candidates: ranked labels above tau0 of every beam, then two
-  // special slots per beam (blank, repeated label)
-  const int ncand = M + 2 * W;
-  auto candidate = [&](int64_t q64) -> uint64_t {
-    const int q = (int)q64;
-    if (q >= M) {
-      const int j = q - M, kk = j >> 1;
-      const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
-      const int c = (j & 1) ? C.lastk[kk] : blank;
-      return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
+  if (nsurv <= kWave) {
+    // rank by counting: rank = number of survivors with a larger key
+    const uint64_t x = lane < nsurv ? C.buf[lane] : 0ull;
+    const uint32_t xh = (uint32_t)(x >> 32), xl = (uint32_t)x;
+    int rk = 0;
+    for (int j = 0; j < nsurv; j++) {
+      const uint32_t yh = (uint32_t)__builtin_amdgcn_readlane((int)xh, j);
+      const uint32_t yl = (uint32_t)__builtin_amdgcn_readlane((int)xl, j);
+      const uint64_t y = ((uint64_t)yh << 32) | yl;
+      rk += y > x ? 1 : 0;
     }
-    int a = 0, z = W - 1;
-    while (a < z) {
-      const int mid = (a + z + 1) >> 1;
-      if (C.offs[mid] <= q) a = mid;
-      else z = mid - 1;
-    }
-    const int rho = q - C.offs[a];
-    const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
-    return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
-  };
-  if (ncand <= kBuf) {
-    for (int q = lane; q < ncand; q += kWave) C.buf[q] = candidate(q);
     lds_sync();
-    wave_sort_lds(C.buf, ncand);
+    const int nw = nsurv < W ? nsurv : W;
+    if (lane < nsurv && rk < W) C.buf[rk] = x;
+    if (lane >= nw && lane < W) C.buf[lane] = 0ull;
     lds_sync();
   } else {
+    // many survivors: exact streaming top-W over them (regenerated per beam
+    // from the ranked list, since the buffer kept only the first kBuf)
+    int lo = 0, hi = lv ? nPool : 0;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (C.Rl[mid] + A >= tau0) lo = mid + 1;
+      else hi = mid;
+    }
+    const int nk = lo;
+    const int incl = wave_incl_scan(lane < W ? nk : 0);
+    const int M = __shfl(incl, 63, 64);
+    if (lane < W) C.offs[lane] = incl - nk;
+    lds_sync();
+    const int ncand = M + 2 * W;
+    auto candidate = [&](int64_t q64) -> uint64_t {
+      const int q = (int)q64;
+      if (q >= M) {
+        const int j = q - M, kk = j >> 1;
+        const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
+        const int c = (j & 1) ? C.lastk[kk] : blank;
+        return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
+      }
+      int a = 0, z = W - 1;
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (C.offs[mid] <= q) a = mid;
+        else z = mid - 1;
+      }
+      const int rho = q - C.offs[a];
+      const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
+      return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
+    };
     stream_topk(C, W, ncand, candidate);
+    if (lane == 0) C.scal[kScalWide] += 1;
   }
   bool need_full = false;
   if (!complete) {
@@ -745,8 +856,12 @@ __device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, const Beam
 
 // Paged (sec. 3.4.5 paged variant, 4.2): fork every slot's block-table row
 // from its source (pages acquired / released by reference count), then
-// append the new label on a fresh page or a copy of the shared partial page.
-__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w, const Beam& nb) {
+// append the new label on a fresh page or on a copy of the shared partial
+// page rebuilt from the LDS mirror of that page (no global read).  Leading
+// full pages shared by every live row of two steps ago are identical in the
+// old and the new row and are skipped.
+__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w,
+                                            const Beam& nb) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
@@ -758,10 +873,13 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
     int* drow = C.tab + (p * W + lane) * max_lp;
     const int* srow = C.tab + (q * W + w.k) * max_lp;
     const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
-    for (int qq = ((live2 >> lane) & 1u) ? pcpp : 0; qq < max_lp; qq++) {
-      const int old = drow[qq];
+    const int old_t = C.tlen[p * kMaxBeam + lane];
+    const int start = ((live2 >> lane) & 1u) ? (pcpp < old_t ? pcpp : old_t) : 0;
+    const int end = old_t > np_new ? old_t : np_new;
+#pragma unroll 4
+    for (int qq = start; qq < end; qq++) {
+      const int old = qq < old_t ? drow[qq] : kInvalidPage;
       const int nw = qq < np_new ? srow[qq] : kInvalidPage;
-      if (old == kInvalidPage && nw == kInvalidPage) break;
       if (old != nw) {
         if (nw != kInvalidPage) atomicAdd(&C.ref[nw], 1);
         if (old != kInvalidPage && atomicSub(&C.ref[old], 1) == 1) {
@@ -771,11 +889,12 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
         drow[qq] = nw;
       }
     }
+    C.tlen[p * kMaxBeam + lane] = np_new > 0 ? np_new : start;
     if (w.valid) {
-      const int* st = C.tail + (q * W + w.k) * ps;
-      int* dt = C.tail + (p * W + lane) * ps;
+      const int4* st = reinterpret_cast<const int4*>(C.tail + (q * W + w.k) * ps);
+      int4* dt = reinterpret_cast<int4*>(C.tail + (p * W + lane) * ps);
       const int off = w.len_k % ps;
-      for (int j = 0; j < off; j++) dt[j] = st[j];
+      for (int j = 0; j * 4 < off; j++) dt[j] = st[j];
     }
   }
   lds_sync();
@@ -810,21 +929,21 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   lds_sync();
   bool push_old = false;
   int* dt = C.tail + (p * W + lane) * ps;
+  if (ext) dt[off] = w.c;
   if (need) {
     if (page == kInvalidPage) {
       atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
     } else {
       C.ref[page] = 1;
-      const int64_t g = (int64_t)page * ps;
-      for (int j = 0; j < off; j++) C.pages[g + j] = dt[j];
-      C.pages[g + off] = w.c;
+      int4* g4 = reinterpret_cast<int4*>(C.pages + (int64_t)page * ps);
+      const int4* t4 = reinterpret_cast<const int4*>(dt);
+      for (int j = 0; j * 4 <= off; j++) g4[j] = t4[j];
       C.tab[(p * W + lane) * max_lp + qq] = page;
+      if (off == 0) C.tlen[p * kMaxBeam + lane] = qq + 1;
       if (off != 0 && phys >= 0) push_old = atomicSub(&C.ref[phys], 1) == 1;
-      dt[off] = w.c;
     }
   } else if (inplace) {
     C.pages[(int64_t)phys * ps + off] = w.c;
-    dt[off] = w.c;
   }
   lds_sync();
   if (push_old) {
@@ -976,11 +1095,9 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.out_scores = out_scores;
   C.base = base;
   C.hdr = reinterpret_cast<int*>(base);
-  C.row0 = reinterpret_cast<float*>(smem + S.row0);
-  C.row1 = reinterpret_cast<float*>(smem + S.row1);
-  C.rank = reinterpret_cast<int8_t*>(smem + S.rank);
-  C.Rc = reinterpret_cast<int*>(smem + S.Rc);
-  C.Rl = reinterpret_cast<float*>(smem + S.Rl);
+  C.rank = nullptr;  // per frame slot, set by the frame loop
+  C.Rc = nullptr;
+  C.Rl = nullptr;
   C.buf = reinterpret_cast<uint64_t*>(smem + S.buf);
   C.A = reinterpret_cast<float*>(smem + S.A);
   C.kb = reinterpret_cast<float*>(smem + S.kb);
@@ -1000,6 +1117,7 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.ref = reinterpret_cast<int*>(smem + S.ref);
   C.fstk = reinterpret_cast<int*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
+  C.tlen = reinterpret_cast<int*>(smem + S.tlen);
   C.clist = reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
   return C;
@@ -1013,6 +1131,7 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
   int* gr = reinterpret_cast<int*>(C.base + L.o_ref);
   int* gf = reinterpret_cast<int*>(C.base + L.o_free);
   int* gl = reinterpret_cast<int*>(C.base + L.o_tail);
+  int* gn = reinterpret_cast<int*>(C.base + L.o_tlen);
   const int nt = 2 * L.W * L.max_lp, nl = 2 * L.W * L.ps;
   if (to_lds) {
     for (int i = lane; i < nt; i += kWave) C.tab[i] = gt[i];
@@ -1021,6 +1140,7 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
       C.fstk[i] = gf[i];
     }
     for (int i = lane; i < nl; i += kWave) C.tail[i] = gl[i];
+    for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = gn[i];
   } else {
     for (int i = lane; i < nt; i += kWave) gt[i] = C.tab[i];
     for (int i = lane; i < L.npages; i += kWave) {
@@ -1028,6 +1148,7 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
       gf[i] = C.fstk[i];
     }
     for (int i = lane; i < nl; i += kWave) gl[i] = C.tail[i];
+    for (int i = lane; i < 2 * kMaxBeam; i += kWave) gn[i] = C.tlen[i];
   }
 }
 
@@ -1105,12 +1226,43 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
   if (tid == 0) hdr[kNSel] = cnt;
 }
 
-// Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).
+// Producer / consumer hand-off inside a workgroup: LDS flags written with
+// release and read with acquire semantics at workgroup scope.  A wait gives up
+// after kSpinLimit polls and raises the workgroup's abort flag, which every
+// wave checks, so no wave can wait forever.
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ int flag_load(int* f) {
+  return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_store(int* f, int v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Waits until *flag == target (eq) or *flag >= target (!eq); false on abort.
+__device__ __forceinline__ bool spin_wait(int* flag, int target, bool eq, int* abortf) {
+  for (int it = 0; it < kSpinLimit; it++) {
+    const int v = flag_load(flag);
+    if (eq ? v == target : v >= target) return true;
+    if (flag_load(abortf)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  flag_store(abortf, 1);
+  return false;
+}
+
+// Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).  One
+// workgroup per row: wave 0 decodes the frames in order (the serial beam
+// recursion); waves 1..P each take every P-th frame, copy its row into a free
+// LDS slot and rank its labels, so the vocabulary pass runs ahead of, and in
+// parallel with, the beam recursion.  Every row of log_prob is read once.
 template <bool STREAM>
-__global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
+__global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
   const Layout L = P.L;
+  const LdsPlan S = P.S;
   const int lane = lane_id();
+  const int wave = (int)(threadIdx.x >> 6);
   const int row_i = blockIdx.x;
   int srow = row_i;
   if (STREAM) {
@@ -1118,22 +1270,69 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
     if (srow < 0 || srow >= P.num_rows) return;
   }
   char* base = P.state + (int64_t)srow * L.row_bytes;
-  Ctx C = make_ctx(L, P.S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
-                   smem);
   const int W = L.W, V = L.V;
-
-  for (int c = lane; c < V; c += kWave) C.rank[c] = -1;
-  Beam b;
-  int step, last_t, nframes;
+  int* hdr = reinterpret_cast<int*>(base);
   const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
+  int* flags = reinterpret_cast<int*>(smem + S.flags);
+  int* ready = flags;                    // [kMaxSlots]: frame held by each slot
+  int* consumed = flags + kMaxSlots;     // last frame the beam wave finished
+  int* abortf = consumed + 1;
+  const int nslot = S.nslot, nprod = S.nprod;
+  auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride); };
+  auto slot_Rc = [&](int sl) { return reinterpret_cast<int*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rc); };
+  auto slot_Rl = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rl); };
+  auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + S.slot0 + sl * S.slot_stride + S.slot_rank); };
+
+  // set-up shared by all waves: empty label ranks, flags
+  for (int sl = 0; sl < nslot; sl++)
+    for (int c = (int)threadIdx.x; c < V; c += (int)blockDim.x) slot_rank(sl)[c] = -1;
+  if (threadIdx.x < kMaxSlots) ready[threadIdx.x] = -1;
+  if (threadIdx.x == 0) {
+    *consumed = -1;
+    *abortf = 0;
+  }
+  const int step_in = STREAM ? hdr[kStep] : 0;
+  int nframes;
   if (STREAM) {
-    step = C.hdr[kStep];
-    last_t = C.hdr[kLastT];
+    nframes = L.cap - step_in;
+    nframes = nframes < 0 ? 0 : (nframes > P.T ? P.T : nframes);
+  } else {
+    nframes = hdr[kNSel];
+  }
+  const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
+  const int64_t stride_t = P.stride_t;
+  const int vec4 = P.vec4;
+  const int K = min(V - 1, 2 * W + 3);  // ranked labels per frame
+  const int complete = K == V - 1;
+  __syncthreads();
+
+  if (wave > 0) {
+    // ------------------------------------------------------------ producer
+    uint64_t* scr = reinterpret_cast<uint64_t*>(smem + S.scr + (wave - 1) * kBuf * 8);
+    for (int f = wave - 1; f < nframes; f += nprod) {
+      const int sl = f % nslot;
+      if (!spin_wait(consumed, f - nslot, false, abortf)) break;
+      float* row = slot_row(sl);
+      row_fetch_async(lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t, row, V, vec4);
+      row_fetch_wait();
+      rank_frame(row, V, L.blank, K, f >= nslot ? K : 0, slot_Rc(sl), slot_Rl(sl), slot_rank(sl),
+                 scr);
+      flag_store(&ready[sl], f);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- beam wave
+  Ctx C = make_ctx(L, S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
+                   smem);
+  Beam b;
+  int step, last_t;
+  if (STREAM) {
+    step = step_in;
+    last_t = hdr[kLastT];
     scal_from_header(C);
     beam_load(C, b);
     if (L.paged) paged_meta_io(C, true);
-    nframes = L.cap - step;
-    nframes = nframes < 0 ? 0 : (nframes > P.T ? P.T : nframes);
   } else {
     step = 0;
     last_t = -1;
@@ -1142,40 +1341,32 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
     if (L.paged) {
       for (int i = lane; i < 2 * W * L.max_lp; i += kWave) C.tab[i] = kInvalidPage;
       for (int i = lane; i < L.npages; i += kWave) C.ref[i] = 0;
+      for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
-    wave_sync();
-    nframes = C.hdr[kNSel];
   }
   lds_sync();
 
-  const int K = min(V - 1, 2 * W + 3);  // ranked labels per frame
-  const int complete = K == V - 1;
-  const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
-  const int64_t stride_t = P.stride_t;
-  const int vec4 = P.vec4;
-  auto frame_ptr = [=](int f) -> const float* {
-    return lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t;
-  };
-
-  int prevK = 0;
-  if (nframes > 0) row_fetch_async(frame_ptr(0), C.row0, V, vec4);
   const int step0 = step;
+  bool aborted = false;
   for (int f = 0; f < nframes; f++) {
-    const float* row = (f & 1) ? C.row1 : C.row0;
-    const int t = STREAM ? step0 + f : sel[f];
+    const int sl = f % nslot;
 #ifdef CTCPB_PHASE_PROF
     if (f == 0) {
       for (int i = 0; i < kProfSlots; i++) C.prof[i] = 0;
       C.prof_t = clock64();
     }
 #endif
-    row_fetch_wait();  // this frame's row is in LDS
+    if (!spin_wait(&ready[sl], f, true, abortf)) {
+      aborted = true;
+      break;
+    }
     PROF_MARK(0);
-    if (f + 1 < nframes) row_fetch_async(frame_ptr(f + 1), (f & 1) ? C.row0 : C.row1, V, vec4);
-    lds_sync();
-    vocab_topk(C, row, K, prevK);
+    const float* row = slot_row(sl);
+    C.Rc = slot_Rc(sl);
+    C.Rl = slot_Rl(sl);
+    C.rank = slot_rank(sl);
+    const int t = STREAM ? step0 + f : sel[f];
     PROF_MARK(1);
-    prevK = K;
     if (step == 0) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
       const uint64_t lm = __ballot(lane < W && b.live);
@@ -1194,8 +1385,10 @@ __global__ __launch_bounds__(64, 1) void decode_kernel(Params P) {
     PROF_MARK(5);
     last_t = t;
     step++;
+    lds_sync();
+    flag_store(consumed, f);
   }
-  row_fetch_wait();
+  if (aborted && lane == 0) C.scal[kScalStatus] |= kStatusAborted;
 #ifdef CTCPB_PHASE_PROF
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
@@ -1237,6 +1430,8 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
     int* gr = reinterpret_cast<int*>(base + L.o_ref);
     for (int i = lane; i < 2 * L.W * L.max_lp; i += kWave) gt[i] = kInvalidPage;
     for (int i = lane; i < L.npages; i += kWave) gr[i] = 0;
+    int* gn = reinterpret_cast<int*>(base + L.o_tlen);
+    for (int i = lane; i < 2 * kMaxBeam; i += kWave) gn[i] = 0;
   }
 }
 
@@ -1316,8 +1511,8 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
     return fail(CTCPB_ERR_INVALID, "storage must be CTCPB_STORAGE_FLAT or CTCPB_STORAGE_PAGED");
   if (std::isnan(cfg->blank_threshold)) return fail(CTCPB_ERR_INVALID, "blank_threshold is NaN");
   const int ps = cfg->page_size == 0 ? 16 : cfg->page_size;
-  if (cfg->storage == CTCPB_STORAGE_PAGED && (ps < 4 || ps > 64))
-    return fail(CTCPB_ERR_INVALID, "page_size must be in [4, 64]");
+  if (cfg->storage == CTCPB_STORAGE_PAGED && (ps < 4 || ps > 64 || ps % 4 != 0))
+    return fail(CTCPB_ERR_INVALID, "page_size must be a multiple of 4 in [4, 64]");
   if (cfg->num_pages < 0) return fail(CTCPB_ERR_INVALID, "num_pages must be >= 0");
   if (cfg->capacity < 0) return fail(CTCPB_ERR_INVALID, "capacity must be >= 0");
   R.W = cfg->beam;
@@ -1335,7 +1530,7 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
 
 int align16(int x) { return (x + 15) & ~15; }
 
-LdsPlan plan_lds(const Layout& L) {
+LdsPlan plan_lds_with(const Layout& L, int nprod) {
   LdsPlan S{};
   int off = 0;
   auto take = [&](int bytes) {
@@ -1343,11 +1538,7 @@ LdsPlan plan_lds(const Layout& L) {
     off += align16(bytes);
     return at;
   };
-  S.row0 = take(L.V * 4);
-  S.row1 = take(L.V * 4);
-  S.rank = take(L.V);
-  S.Rc = take(kMaxK * 4);
-  S.Rl = take(kMaxK * 4);
+  // beam wave
   S.buf = take(kBuf * 8);
   S.A = take(kMaxBeam * 4);
   S.kb = take(kMaxBeam * 4);
@@ -1367,7 +1558,28 @@ LdsPlan plan_lds(const Layout& L) {
   S.ref = take(L.paged ? L.npages * 4 : 0);
   S.fstk = take(L.paged ? L.npages * 4 : 0);
   S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
+  S.tlen = take(L.paged ? 2 * kMaxBeam * 4 : 0);
+  // hand-off
+  S.flags = take((kMaxSlots + 2) * 4);
+  S.nprod = nprod;
+  S.nslot = nprod + 1;
+  S.scr = take(nprod * kBuf * 8);
+  // ring of frame slots: row, ranked labels, label -> rank map
+  S.slot_Rc = align16(L.V * 4);
+  S.slot_Rl = S.slot_Rc + align16(kMaxK * 4);
+  S.slot_rank = S.slot_Rl + align16(kMaxK * 4);
+  S.slot_stride = S.slot_rank + align16(L.V);
+  S.slot0 = take(S.nslot * S.slot_stride);
   S.total = off;
+  return S;
+}
+
+// More producer waves for wider vocabularies (the ranking pass grows with
+// V while the beam recursion does not), as many as the LDS budget allows.
+LdsPlan plan_lds(const Layout& L) {
+  int nprod = L.V >= 3000 ? 3 : (L.V >= 1000 ? 2 : 1);
+  LdsPlan S = plan_lds_with(L, nprod);
+  while (S.total > kLdsLimit && nprod > 1) S = plan_lds_with(L, --nprod);
   return S;
 }
 
@@ -1477,7 +1689,8 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
-  if (int rc = launch(decode_kernel<false>, batch, 64, P.S.total, st, P, "decode_kernel"))
+  if (int rc = launch(decode_kernel<false>, batch, 64 * (1 + P.S.nprod), P.S.total, st, P,
+                      "decode_kernel"))
     return rc;
   return ok();
 }
@@ -1540,7 +1753,7 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
-  if (int rc = launch(decode_kernel<true>, n_rows, 64, P.S.total,
+  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (1 + P.S.nprod), P.S.total,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
   return ok();

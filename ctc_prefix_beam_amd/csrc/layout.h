@@ -13,7 +13,8 @@
 //   paged:      table[2][beam][max_lp] int32 page ids (-1 none),
 //               refcount[num_pages], free stack[num_pages],
 //               pages[num_pages][page_size] int32 tokens,
-//               tail[2][beam][page_size] int32: each beam's partial last page
+//               tail[2][beam][page_size] int32: each beam's partial last page,
+//               tlen[2][32] int32: valid leading entries of each table row
 #pragma once
 #include <stdint.h>
 
@@ -42,7 +43,7 @@ enum HeaderField {
   // words 32..47: optional per-phase cycle counters of a diagnostics build
 };
 
-enum Status { kStatusOutOfPages = 1 };
+enum Status { kStatusOutOfPages = 1, kStatusAborted = 2 };
 
 struct Layout {
   int W;          // beam
@@ -55,7 +56,7 @@ struct Layout {
   int npages;     // pages per row
   int cap_sel;    // entries of sel (offline: max_T; streaming: 0)
   int64_t row_bytes;
-  int64_t o_beam, o_sel, o_clist, o_tab, o_ref, o_free, o_pages, o_tail;
+  int64_t o_beam, o_sel, o_clist, o_tab, o_ref, o_free, o_pages, o_tail, o_tlen;
 };
 
 // Beam arrays inside a row region (offsets from o_beam).
@@ -98,6 +99,8 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
     off += align256((int64_t)L.npages * ps * 4);
     L.o_tail = off;
     off += align256((int64_t)2 * W * ps * 4);
+    L.o_tlen = off;
+    off += align256((int64_t)2 * kMaxBeam * 4);
   }
   L.row_bytes = align256(off);
   return L;

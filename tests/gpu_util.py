@@ -17,7 +17,9 @@ def gpu_offline(lp, lens, beam, nbest, blank, threshold, max_out_len, paged=Fals
                                                page_size=page_size, num_pages=num_pages))
     x = lp if isinstance(lp, torch.Tensor) else torch.from_numpy(lp)
     t, l, s = dec.decode(x.to(device), torch.as_tensor(lens, dtype=torch.int32).to(device))
+    stats = dec.row_stats().cpu().numpy()
     torch.cuda.synchronize()
+    assert (stats[:, 2] == 0).all(), f"row status bits set: {np.unique(stats[:, 2])}"
     return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
 
 

@@ -26,7 +26,9 @@ def oracle_streams(lp, beam, capacity, chunk, nbest, mol):
 
 def read(pool, rows=None):
     t, l, s = pool.read(rows)
+    st = pool.row_stats().cpu().numpy()
     torch.cuda.synchronize()
+    assert (st[:, 2] == 0).all(), f"stream status bits set: {np.unique(st[:, 2])}"
     return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
 
 
