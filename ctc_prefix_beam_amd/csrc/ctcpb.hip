@@ -53,7 +53,6 @@ namespace ctcpb {
 constexpr int kMaxVocab = 16384;
 constexpr int kMaxK = 2 * kMaxBeam + 3;   // ranked labels kept per frame
 constexpr int kBuf = 256;                 // candidate buffer (keys)
-constexpr int kPrefetch4 = 20;            // float4 per lane held for the next frame
 constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
 constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
 
@@ -62,6 +61,8 @@ struct LdsPlan {
   int slot0, slot_stride, slot_Rc, slot_Rl, slot_rank;  // ring of frame slots
   int nslot, nprod;                                     // slots, producer waves
   int scr, flags;                                       // producer scratch, hand-off flags
+  int clist, clist_lds;                                 // flat token lists held in LDS
+  int fsrc, flen;                                       // flat copy lineage
   int buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh, newlen, nchild, childc, scal,
       tab, ref, fstk, tail, tlen, total;
 };
@@ -134,7 +135,9 @@ struct Ctx {
   int* fstk;
   int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
   int* tlen;      // paged: valid leading entries of each block-table row, both parities
-  int* clist;     // flat: global
+  int* fsrc;      // flat: [2][32] source slot of the row written at each parity (-1 unknown)
+  int* flen;      // flat: [2][32] length of that row
+  int* clist;     // flat: global or LDS
   int* pages;     // paged: global
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
@@ -167,7 +170,7 @@ __device__ __forceinline__ void lds_sync() {
 
 __device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, int slot, int pos) {
   const Layout& L = C.L;
-  if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.cap + pos];
+  if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.ldc + pos];
   const int page = tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
   if (page < 0) return -1;  // only after a row ran out of pages
   return C.pages[(int64_t)page * L.ps + pos % L.ps];
@@ -255,13 +258,29 @@ __device__ __forceinline__ void rank_frame(const float* row, int V, int blank, i
                                            int* Rc, float* Rl, int8_t* rank, uint64_t* scr) {
   const int lane = lane_id();
   for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
-  // pass 1: two best keys per lane
+  // pass 1: two best keys per lane (4 labels per 16-byte LDS read when the
+  // row is a whole number of float4)
   uint32_t a = 0u, b = 0u;
-  for (int c = lane; c < V; c += kWave) {
-    const uint32_t u = c == blank ? 0u : sortable_bits(row[c]);
+  auto push2 = [&](uint32_t u) {
     const uint32_t lo = u < a ? u : a;
     a = u > a ? u : a;
     b = lo > b ? lo : b;
+  };
+  const bool v4 = (V & 3) == 0;
+  if (v4) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = V >> 2;
+
+    for (int i = lane; i < n4; i += kWave) {
+      const float4 q = r4[i];
+      const int c = 4 * i;
+      push2(c == blank ? 0u : sortable_bits(q.x));
+      push2(c + 1 == blank ? 0u : sortable_bits(q.y));
+      push2(c + 2 == blank ? 0u : sortable_bits(q.z));
+      push2(c + 3 == blank ? 0u : sortable_bits(q.w));
+    }
+  } else {
+    for (int c = lane; c < V; c += kWave) push2(c == blank ? 0u : sortable_bits(row[c]));
   }
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; bit--) {
@@ -269,16 +288,36 @@ __device__ __forceinline__ void rank_frame(const float* row, int V, int blank, i
     const int cnt = __popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand));
     if (cnt >= K) thr = cand;
   }
-  // pass 2: every label at or above the threshold
+  // pass 2: every label at or above the threshold (gathered in any order:
+  // they are ranked below)
   int cnt = 0;
-  for (int base = 0; base < V; base += kWave) {
-    const int c = base + lane;
-    const uint32_t u = (c < V && c != blank) ? sortable_bits(row[c]) : 0u;
+  auto gather = [&](uint32_t u, int c) {
     const bool pass = u != 0u && u >= thr;
     const uint64_t m = __ballot(pass);
     const int pos = cnt + lanes_below(m);
     if (pass && pos < kBuf) scr[pos] = ((uint64_t)u << 32) | (uint32_t)(~c);
     cnt += __popcll(m);
+  };
+  if (v4) {
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    const int n4 = V >> 2;
+
+    for (int i0 = 0; i0 < n4; i0 += kWave) {
+      const int i = i0 + lane;
+      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < n4) q = r4[i];
+      const int c = 4 * i;
+      const bool in = i < n4;
+      gather((in && c != blank) ? sortable_bits(q.x) : 0u, c);
+      gather((in && c + 1 != blank) ? sortable_bits(q.y) : 0u, c + 1);
+      gather((in && c + 2 != blank) ? sortable_bits(q.z) : 0u, c + 2);
+      gather((in && c + 3 != blank) ? sortable_bits(q.w) : 0u, c + 3);
+    }
+  } else {
+    for (int base = 0; base < V; base += kWave) {
+      const int c = base + lane;
+      gather((c < V && c != blank) ? sortable_bits(row[c]) : 0u, c);
+    }
   }
   lds_sync();
   if (cnt <= 2 * kWave) {
@@ -364,9 +403,13 @@ __device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* r
     b.pb = row[blank];
     b.score = row[blank];
   }
-  // token store, parity 0
+  // token store, parity 0 (seeded, not copied from any slot)
+  if (lane < kMaxBeam) {
+    C.fsrc[lane] = -1;
+    C.flen[lane] = lane < m ? 1 : 0;
+  }
   if (!L.paged) {
-    if (lane < m) C.clist[(int64_t)lane * L.cap] = b.last;
+    if (lane < m) C.clist[(int64_t)lane * L.ldc] = b.last;
   } else {
     // one fresh page per seeded label
     const bool want = lane < m;
@@ -470,6 +513,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
   const float keyb = lv ? lse(ptb, ptnb) : kNeg;
 
+  PROF_MARK(1);
   // labels removed from a beam's ordinary list: its own last label (that is
   // the repeated-label slot) and the last label of each child (merged away)
   if (lane < W) {
@@ -504,6 +548,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     C.lastk[lane] = last;
   }
 
+  PROF_MARK(2);
   // ---- a tight lower bound tau0 of the W-th best key: each beam offers its
   // two best candidates (blank slot, repeated-label slot, first two
   // non-excluded ranked labels); the W-th largest of those 2W values has at
@@ -540,66 +585,75 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float shi = fmaxf(keyb, keyc), slo = fminf(keyb, keyc);
   const float v1 = fmaxf(shi, o1);
   const float v2 = fmaxf(fminf(shi, o1), fmaxf(slo, o2));
-  const uint32_t s1 = (lv && v1 > kNeg) ? sortable(v1) : 0u;
-  const uint32_t s2 = (lv && v2 > kNeg) ? sortable(v2) : 0u;
-  float tau0 = kNeg;
-  if (__popcll(__ballot(s1 != 0u)) + __popcll(__ballot(s2 != 0u)) >= W) {
-    uint32_t prefix = 0u;
-    for (int bit = 30; bit >= 0; bit--) {  // keys are negative: bit 31 is 0
-      const uint32_t cand = prefix | (1u << bit);
-      const int cnt = __popcll(__ballot(s1 >= cand)) + __popcll(__ballot(s2 >= cand));
-      if (cnt >= W) prefix = cand;
-    }
-    tau0 = unsortable(prefix);
+  // the W-th largest of the 2W values, by counting with broadcast LDS reads
+  // (lane j < 32 holds beam j's best, lane 32 + j its second best)
+  float* tv = reinterpret_cast<float*>(C.buf);
+  if (lane < kMaxBeam) {
+    tv[lane] = lv ? v1 : kNeg;
+    tv[kMaxBeam + lane] = lv ? v2 : kNeg;
   }
-
+  lds_sync();
+  const float mine = tv[lane];
+  int ge = 0;
+#pragma unroll
+  for (int j = 0; j < kWave; j += 4) {
+    const float4 y = *reinterpret_cast<const float4*>(tv + j);
+    ge += (y.x >= mine ? 1 : 0) + (y.y >= mine ? 1 : 0) + (y.z >= mine ? 1 : 0) +
+          (y.w >= mine ? 1 : 0);
+  }
+  const float tau0 = wave_max((mine > kNeg && ge >= W) ? mine : kNeg);
+  lds_sync();
+  PROF_MARK(3);
   // ---- every candidate at or above tau0 (ranked labels are sorted, so each
   // beam's qualifying labels form a prefix of its list)
-  if (lane == 0) C.scal[kScalSurv] = 0;
-  lds_sync();
-  if (lv) {
-    if (keyb > kNeg && keyb >= tau0) {
-      const int p = atomicAdd(&C.scal[kScalSurv], 1);
-      if (p < kBuf) C.buf[p] = compose(keyb, (uint32_t)(lane * V + blank));
-    }
-    if (keyc > kNeg && keyc >= tau0) {
-      const int p = atomicAdd(&C.scal[kScalSurv], 1);
-      if (p < kBuf) C.buf[p] = compose(keyc, (uint32_t)(lane * V + last));
-    }
+  // gathered with a wave-uniform running count (ballot + lane prefix), the
+  // ranked labels in chunks of four until no beam has one at or above tau0
+  int nsurv = 0;
+  {
+    auto put = [&](bool pass, uint64_t key) {
+      const uint64_t m = __ballot(pass);
+      const int pos = nsurv + lanes_below(m);
+      if (pass && pos < kBuf) C.buf[pos] = key;
+      nsurv += __popcll(m);
+    };
+    put(lv && keyb > kNeg && keyb >= tau0, compose(keyb, (uint32_t)(lane * V + blank)));
+    put(lv && keyc > kNeg && keyc >= tau0, compose(keyc, (uint32_t)(lane * V + last)));
+    bool more = lv;
     for (int r = 0; r < nPool; r += 4) {
+      if (!__ballot(more)) break;
       const float4 q = *reinterpret_cast<const float4*>(C.Rl + r);
+      const int4 cq = *reinterpret_cast<const int4*>(C.Rc + r);
       const float lpv[4] = {q.x, q.y, q.z, q.w};
+      const int cv[4] = {cq.x, cq.y, cq.z, cq.w};
       bool any = false;
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const int rr = r + j;
         const float key = lpv[j] + A;
-        if (rr < nPool && key >= tau0) {
-          any = true;
-          const uint32_t open = rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
-          if (open & 1u) {
-            const int p = atomicAdd(&C.scal[kScalSurv], 1);
-            if (p < kBuf) C.buf[p] = compose(key, (uint32_t)(lane * V + C.Rc[rr]));
-          }
-        }
+        const bool above = more && rr < nPool && key >= tau0;
+        any = any || above;
+        const uint32_t open =
+            rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
+        put(above && (open & 1u), compose(key, (uint32_t)(lane * V + cv[j])));
       }
-      if (!any) break;
+      more = more && any;
     }
   }
   lds_sync();
-  const int nsurv = C.scal[kScalSurv];
-
-  PROF_MARK(2);
+  PROF_MARK(4);
   if (nsurv <= kWave) {
-    // rank by counting: rank = number of survivors with a larger key
+    // rank by counting: rank = number of survivors with a larger key, read
+    // two at a time with broadcast LDS loads
+    const int n8 = (nsurv + 7) & ~7;
+    if (nsurv + lane < n8) C.buf[nsurv + lane] = 0ull;
+    lds_sync();
     const uint64_t x = lane < nsurv ? C.buf[lane] : 0ull;
-    const uint32_t xh = (uint32_t)(x >> 32), xl = (uint32_t)x;
     int rk = 0;
-    for (int j = 0; j < nsurv; j++) {
-      const uint32_t yh = (uint32_t)__builtin_amdgcn_readlane((int)xh, j);
-      const uint32_t yl = (uint32_t)__builtin_amdgcn_readlane((int)xl, j);
-      const uint64_t y = ((uint64_t)yh << 32) | yl;
-      rk += y > x ? 1 : 0;
+    for (int j = 0; j < n8; j += 8) {
+      const ulonglong2* y2 = reinterpret_cast<const ulonglong2*>(C.buf + j);
+      const ulonglong2 a0 = y2[0], a1 = y2[1], a2 = y2[2], a3 = y2[3];
+      rk += (a0.x > x ? 1 : 0) + (a0.y > x ? 1 : 0) + (a1.x > x ? 1 : 0) + (a1.y > x ? 1 : 0) +
+            (a2.x > x ? 1 : 0) + (a2.y > x ? 1 : 0) + (a3.x > x ? 1 : 0) + (a3.y > x ? 1 : 0);
     }
     lds_sync();
     const int nw = nsurv < W ? nsurv : W;
@@ -657,7 +711,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     if (lane == 0) C.scal[kScalFallbacks] += 1;
   }
 
-  PROF_MARK(3);
+  PROF_MARK(5);
   // winners in rank order (slot r = rank r), sec. 3.4.5
   const uint64_t wc = lane < W ? C.buf[lane] : 0ull;
   Winner w;
@@ -759,14 +813,17 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
   nb.parent = npar;
   if (lane < W) b = nb;
-  PROF_MARK(4);
+  PROF_MARK(6);
   return w;
 }
 
 // ------------------------------------------------------------ token stores --
 // Flat (sec. 3.1, 7): slot r of parity p receives its source's tokens from
-// parity p^1 plus the new label.  Positions below the common prefix that all
-// live beams of two steps ago shared are already in place and are skipped.
+// parity p^1 plus the new label.  Only positions that can differ from what
+// the row already holds are copied: if the source beam was itself copied
+// from slot r one step earlier, the row's old content is a prefix of the new
+// one; otherwise positions below the common prefix that every live beam of
+// two steps ago shared are already in place.  Copies move 4 tokens at once.
 __device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner& w) {
   const Layout& L = C.L;
   const int lane = lane_id();
@@ -774,43 +831,43 @@ __device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner&
   const int p = step & 1, q = p ^ 1;
   const uint32_t live2 = (uint32_t)C.scal[kScalLive0 + p];
   const int cplp = C.scal[kScalCpl0 + p];
-  const int start = w.valid ? (((live2 >> lane) & 1u) ? cplp : 0) : 0;
-  const int cnt = w.valid ? w.len_k - start : 0;
+  int start = 0;
+  if (w.valid) {
+    const int old_len = C.flen[p * kMaxBeam + lane];
+    if (C.fsrc[q * kMaxBeam + w.k] == lane && old_len >= 0) start = old_len;
+    else if ((live2 >> lane) & 1u) start = cplp;
+    if (start > w.len_k) start = w.len_k;
+  }
+  const int s4 = start >> 2;
+  const int e4 = w.valid ? (w.len_k + 3) >> 2 : 0;
+  const int cnt = w.valid ? e4 - s4 : 0;
   const int incl = wave_incl_scan(lane < W ? cnt : 0);
   const int total = __shfl(incl, 63, 64);
-  int* offs = C.offs;            // [0, 33): offsets; [40, 72): starts; [80, 112): sources
+  int* offs = C.offs;  // [0, 33): offsets; [40, 72): first int4; [80, 112): sources
   if (lane < W) {
     offs[lane] = incl - cnt;
-    offs[40 + lane] = start;
+    offs[40 + lane] = s4;
     offs[80 + lane] = w.k;
   }
   lds_sync();
-  int* clist = C.clist;
-  const int64_t cap = L.cap;
-  for (int base = 0; base < total; base += 8 * kWave) {
-    int val[8];
-    int64_t dst[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int i = base + u * kWave + lane;
-      dst[u] = -1;
-      if (i < total) {
-        int a = 0, z = W - 1;
-        while (a < z) {
-          const int mid = (a + z + 1) >> 1;
-          if (offs[mid] <= i) a = mid;
-          else z = mid - 1;
-        }
-        const int pos = offs[40 + a] + (i - offs[a]);
-        val[u] = clist[((int64_t)(q * W + offs[80 + a])) * cap + pos];
-        dst[u] = ((int64_t)(p * W + a)) * cap + pos;
-      }
+  int4* c4 = reinterpret_cast<int4*>(C.clist);
+  const int64_t ld4 = L.ldc >> 2;
+  for (int i = lane; i < total; i += kWave) {
+    int a = 0, z = W - 1;
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (offs[mid] <= i) a = mid;
+      else z = mid - 1;
     }
-#pragma unroll
-    for (int u = 0; u < 8; u++)
-      if (dst[u] >= 0) clist[dst[u]] = val[u];
+    const int64_t pos4 = offs[40 + a] + (i - offs[a]);
+    c4[(int64_t)(p * W + a) * ld4 + pos4] = c4[(int64_t)(q * W + offs[80 + a]) * ld4 + pos4];
   }
-  if (w.valid && w.c != blank) clist[((int64_t)(p * W + lane)) * cap + w.len_k] = w.c;
+  wave_sync();  // the copies land before the appended label
+  if (w.valid && w.c != blank) C.clist[((int64_t)(p * W + lane)) * L.ldc + w.len_k] = w.c;
+  if (lane < W) {
+    C.fsrc[p * kMaxBeam + lane] = w.valid ? w.k : -1;
+    C.flen[p * kMaxBeam + lane] = w.valid ? w.len_k + (w.c != blank ? 1 : 0) : -1;
+  }
   const uint64_t vm = __ballot(w.valid);
   lds_sync();
   if (lane == 0) {
@@ -838,7 +895,7 @@ __device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, const Beam
   int tk[kMaxBeam];
 #pragma unroll
   for (int r = 0; r < kMaxBeam; r++)
-    tk[r] = (inside && ((live >> r) & 1ull)) ? C.clist[((int64_t)(p * W + r)) * L.cap + pos] : -3;
+    tk[r] = (inside && ((live >> r) & 1ull)) ? C.clist[((int64_t)(p * W + r)) * L.ldc + pos] : -3;
   const int first = __ffsll((long long)live) - 1;
   int ref = -3;
 #pragma unroll
@@ -874,7 +931,11 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
     const int* srow = C.tab + (q * W + w.k) * max_lp;
     const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
     const int old_t = C.tlen[p * kMaxBeam + lane];
-    const int start = ((live2 >> lane) & 1u) ? (pcpp < old_t ? pcpp : old_t) : 0;
+    int start = ((live2 >> lane) & 1u) ? (pcpp < old_t ? pcpp : old_t) : 0;
+    // if the source was forked from this very slot one step earlier, the two
+    // rows differ at most from the old row's last page on
+    if (w.valid && C.fsrc[q * kMaxBeam + w.k] == lane && old_t > 0 && start < old_t - 1)
+      start = old_t - 1;
     const int end = old_t > np_new ? old_t : np_new;
 #pragma unroll 4
     for (int qq = start; qq < end; qq++) {
@@ -890,6 +951,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
       }
     }
     C.tlen[p * kMaxBeam + lane] = np_new > 0 ? np_new : start;
+    C.fsrc[p * kMaxBeam + lane] = w.valid ? w.k : -1;
     if (w.valid) {
       const int4* st = reinterpret_cast<const int4*>(C.tail + (q * W + w.k) * ps);
       int4* dt = reinterpret_cast<int4*>(C.tail + (p * W + lane) * ps);
@@ -1118,7 +1180,10 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.fstk = reinterpret_cast<int*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
   C.tlen = reinterpret_cast<int*>(smem + S.tlen);
-  C.clist = reinterpret_cast<int*>(base + L.o_clist);
+  C.fsrc = reinterpret_cast<int*>(smem + S.fsrc);
+  C.flen = reinterpret_cast<int*>(smem + S.flen);
+  C.clist = S.clist_lds ? reinterpret_cast<int*>(smem + S.clist)
+                        : reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
   return C;
 }
@@ -1149,6 +1214,24 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
     }
     for (int i = lane; i < nl; i += kWave) gl[i] = C.tail[i];
     for (int i = lane; i < 2 * kMaxBeam; i += kWave) gn[i] = C.tlen[i];
+  }
+}
+
+// Flat token lists kept in LDS: the live rows of the current parity are
+// restored from / saved to the row region around a streaming chunk.
+__device__ __forceinline__ void clist_io(const Ctx& C, const Beam& b, int parity, bool to_lds) {
+  const Layout& L = C.L;
+  const int lane = lane_id();
+  int* g = reinterpret_cast<int*>(C.base + L.o_clist);
+  const uint64_t live = __ballot(lane < L.W && b.live);
+  for (int r = 0; r < L.W; r++) {
+    if (!((live >> r) & 1ull)) continue;
+    const int len = __shfl(b.len, r, 64);
+    const int64_t at = ((int64_t)(parity * L.W + r)) * L.ldc;
+    for (int i = lane; i < len; i += kWave) {
+      if (to_lds) C.clist[at + i] = g[at + i];
+      else g[at + i] = C.clist[at + i];
+    }
   }
 }
 
@@ -1333,6 +1416,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     scal_from_header(C);
     beam_load(C, b);
     if (L.paged) paged_meta_io(C, true);
+    if (S.clist_lds && step > 0) {
+      clist_io(C, b, (step - 1) & 1, true);
+      // the other parity was not kept: its rows must be rewritten in full
+      if (lane == 0) C.scal[kScalLive0 + (step & 1)] = 0;
+    }
   } else {
     step = 0;
     last_t = -1;
@@ -1343,6 +1431,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       for (int i = lane; i < L.npages; i += kWave) C.ref[i] = 0;
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
+  }
+  for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
+    C.fsrc[i] = -1;
+    C.flen[i] = -1;
   }
   lds_sync();
 
@@ -1366,7 +1458,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.Rl = slot_Rl(sl);
     C.rank = slot_rank(sl);
     const int t = STREAM ? step0 + f : sel[f];
-    PROF_MARK(1);
     if (step == 0) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
       const uint64_t lm = __ballot(lane < W && b.live);
@@ -1382,7 +1473,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
         if ((step & 15) == 15) advance_cpl_flat(C, step & 1, b);
       }
     }
-    PROF_MARK(5);
+    PROF_MARK(7);
     last_t = t;
     step++;
     lds_sync();
@@ -1400,6 +1491,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (STREAM) {
     beam_store(C, b);
     if (L.paged) paged_meta_io(C, false);
+    if (S.clist_lds && step > 0) {
+      wave_sync();
+      clist_io(C, b, (step - 1) & 1, false);
+    }
     scal_to_header(C, step, last_t);
   } else {
     wave_sync();
@@ -1444,6 +1539,7 @@ __global__ __launch_bounds__(64) void read_state_kernel(Params P) {
   char* base = P.state + (int64_t)srow * L.row_bytes;
   Ctx C = make_ctx(L, P.S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
                    smem);
+  C.clist = reinterpret_cast<int*>(base + L.o_clist);  // the persisted copy
   Beam b;
   beam_load(C, b);
   const int step = C.hdr[kStep];
@@ -1530,7 +1626,7 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
 
 int align16(int x) { return (x + 15) & ~15; }
 
-LdsPlan plan_lds_with(const Layout& L, int nprod) {
+LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   LdsPlan S{};
   int off = 0;
   auto take = [&](int bytes) {
@@ -1559,6 +1655,10 @@ LdsPlan plan_lds_with(const Layout& L, int nprod) {
   S.fstk = take(L.paged ? L.npages * 4 : 0);
   S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
   S.tlen = take(L.paged ? 2 * kMaxBeam * 4 : 0);
+  S.fsrc = take(2 * kMaxBeam * 4);
+  S.flen = take(2 * kMaxBeam * 4);
+  S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
+  S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
   // hand-off
   S.flags = take((kMaxSlots + 2) * 4);
   S.nprod = nprod;
@@ -1577,10 +1677,16 @@ LdsPlan plan_lds_with(const Layout& L, int nprod) {
 // More producer waves for wider vocabularies (the ranking pass grows with
 // V while the beam recursion does not), as many as the LDS budget allows.
 LdsPlan plan_lds(const Layout& L) {
-  int nprod = L.V >= 3000 ? 3 : (L.V >= 1000 ? 2 : 1);
-  LdsPlan S = plan_lds_with(L, nprod);
-  while (S.total > kLdsLimit && nprod > 1) S = plan_lds_with(L, --nprod);
-  return S;
+  const int pref = L.V >= 3000 ? 3 : (L.V >= 1000 ? 2 : 1);
+  // flat token lists in LDS if they fit next to at least one producer
+  for (int lds_clist = 1; lds_clist >= 0; lds_clist--) {
+    if (lds_clist && L.paged) continue;
+    for (int nprod = pref; nprod >= 1; nprod--) {
+      const LdsPlan S = plan_lds_with(L, nprod, lds_clist != 0);
+      if (S.total <= kLdsLimit) return S;
+    }
+  }
+  return plan_lds_with(L, 1, false);  // too large: check_lds reports it
 }
 
 Layout layout_for(const Resolved& R, int cap, int cap_sel) {

@@ -9,7 +9,8 @@
 //   beam arrays kMaxBeam x {pb, pnb, score, len, last token, parent slot,
 //               second-to-last token, live, prefix hash, parent-prefix hash}
 //   sel         cap_sel x int32     offline: selected frame indices
-//   flat:       clist[2][beam][cap] int32 tokens, double-buffered by parity
+//   flat:       clist[2][beam][ldc] int32 tokens, double-buffered by parity
+//               (ldc = cap rounded up to a multiple of 4)
 //   paged:      table[2][beam][max_lp] int32 page ids (-1 none),
 //               refcount[num_pages], free stack[num_pages],
 //               pages[num_pages][page_size] int32 tokens,
@@ -50,6 +51,7 @@ struct Layout {
   int V;          // vocabulary
   int blank;
   int cap;        // token (and frame) capacity of a row
+  int ldc;        // flat: row stride of clist (cap rounded up to 4)
   int paged;      // 0 flat, 1 paged
   int ps;         // page size
   int max_lp;     // pages per block-table row
@@ -75,6 +77,7 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   L.V = V;
   L.blank = blank;
   L.cap = cap;
+  L.ldc = (cap + 3) & ~3;
   L.paged = paged;
   L.ps = paged ? ps : 0;
   L.max_lp = paged ? (cap + ps - 1) / ps : 0;
@@ -87,7 +90,7 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   off += align256((int64_t)cap_sel * 4);
   if (!paged) {
     L.o_clist = off;
-    off += align256((int64_t)2 * W * cap * 4);
+    off += align256((int64_t)2 * W * L.ldc * 4);
   } else {
     L.o_tab = off;
     off += align256((int64_t)2 * W * L.max_lp * 4);

@@ -36,26 +36,52 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// DPP lane moves (VALU, no LDS round trip).  Controls follow the GCN/CDNA
+// DPP encoding: quad_perm, row_half_mirror, row_mirror, row_shr:n,
+// row_bcast:15 and row_bcast:31.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_mov(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kDppXor1 = 0xb1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4e;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // reverse within 8 lanes
+constexpr int kDppMirror = 0x140;       // reverse within 16 lanes
+constexpr int kDppBcast15 = 0x142;      // lane 15 of each row -> next row
+constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
+__device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+
+// Maximum over the wave, returned to every lane.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppXor1>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppXor2>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppHalfMirror>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppMirror>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppBcast15, 0xa>(x, x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp_mov<kDppBcast31, 0xc>(x, x))));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_mov<kDppXor1>(0, v);
+  v += dpp_mov<kDppXor2>(0, v);
+  v += dpp_mov<kDppHalfMirror>(0, v);
+  v += dpp_mov<kDppMirror>(0, v);
+  v += dpp_mov<kDppBcast15, 0xa>(0, v);
+  v += dpp_mov<kDppBcast31, 0xc>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Inclusive prefix sum over the wave.
+// Inclusive prefix sum over the wave (row_shr within rows of 16, then row
+// broadcasts carry the row totals forward).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  v += dpp_mov<dpp_row_shr(1)>(0, v);
+  v += dpp_mov<dpp_row_shr(2)>(0, v);
+  v += dpp_mov<dpp_row_shr(4)>(0, v);
+  v += dpp_mov<dpp_row_shr(8)>(0, v);
+  v += dpp_mov<kDppBcast15, 0xa>(0, v);
+  v += dpp_mov<kDppBcast31, 0xc>(0, v);
   return v;
 }
 
