@@ -24,8 +24,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_vocab5000_pmc.json")
-KERNEL_SOURCES = ["ctc_prefix_beam_amd/csrc/ctcpb.hip", "ctc_prefix_beam_amd/csrc/device_math.h",
-                  "ctc_prefix_beam_amd/csrc/wave_ops.h", "ctc_prefix_beam_amd/csrc/layout.h"]
 
 
 def log(*a):
@@ -33,10 +31,11 @@ def log(*a):
 
 
 def kernel_sha():
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return h.hexdigest()[:16]
+    """Identity of the built decoder (hash of libctcpb.so): the stored HBM
+    counter figures are used only while the library they were taken on is the
+    one being timed."""
+    import ctc_prefix_beam_amd as cpb
+    return hashlib.sha256(open(cpb.LIB_PATH, "rb").read()).hexdigest()[:16]
 
 
 def algorithmic_bytes_per_frame(V, W):
@@ -104,8 +103,10 @@ def streaming_latency(reps=3, seed=0):
     import synth
     wl = synth.WORKLOADS["stream512"]
     x, _ = wl.make_device(seed, "cuda")
-    pool = cpb.StreamPool(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, max_out_len=wl.T),
-                          wl.V, wl.B)
+    # capacity sized to the session (1024 frames), as the decoder's state is
+    # allocated for the longest stream it must hold
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, max_out_len=wl.T,
+                                            capacity=wl.T), wl.V, wl.B)
     dev_ms, host_ms = [], []
     for rep in range(reps + 1):
         pool.reset()
@@ -122,7 +123,8 @@ def streaming_latency(reps=3, seed=0):
                 dev_ms.append(e0.elapsed_time(e1))
     d = np.array(dev_ms)
     h = np.array(host_ms)
-    return {"workload": "stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks",
+    return {"workload": "stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks, "
+                        "capacity 1024",
             "p50_chunk_ms": round(float(np.percentile(d, 50)), 4),
             "p90_chunk_ms": round(float(np.percentile(d, 90)), 4),
             "p99_chunk_ms": round(float(np.percentile(d, 99)), 4),
@@ -132,13 +134,16 @@ def streaming_latency(reps=3, seed=0):
 
 
 def other_workloads():
+    """Every offline workload once more (flat storage, and vocab5000 paged),
+    for the comparison table; not part of the default run."""
     import numpy as np
     import torch
 
     import ctc_prefix_beam_amd as cpb
     import synth
     res = {}
-    for name, paged in (("bpe256", False), ("bpe1024", False), ("vocab5000", False)):
+    for name, paged in (("bpe256", False), ("bpe1024", False), ("vocab5000", False),
+                        ("vocab5000", True)):
         wl = synth.WORKLOADS[name]
         x, lens = wl.make_device(0, "cuda")
         lens_d = torch.from_numpy(lens).cuda()
@@ -153,7 +158,9 @@ def other_workloads():
         res[key] = {"frames_per_s": round(wl.B * wl.T * 5 / wall, 1),
                     "valid_frames_per_s": round(float(np.sum(lens)) * 5 / wall, 1),
                     "ms_per_decode": round(float(np.mean(kms)), 4),
-                    "fallback_steps": int(st[:, 4].sum()), "steps": int(st[:, 0].sum())}
+                    "fallback_steps": int(st[:, 4].sum()), "steps": int(st[:, 0].sum()),
+                    "workspace_bytes": int(dec.workspace.numel()),
+                    "pages_high_per_row": int(st[:, 3].max()) if paged else None}
         del x
     return res
 
@@ -167,9 +174,13 @@ def main():
     ap.add_argument("--storage", choices=["paged", "flat"], default="paged")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip streaming and other workloads")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the streaming latency run")
+    ap.add_argument("--compare", action="store_true",
+                    help="also time every offline workload (flat and paged) for comparison")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="after the timed decodes, run a plain streaming kernel of known size "
+                         "twice (1 GiB read, 1 GiB written, 16-byte accesses per lane) to "
+                         "calibrate the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -185,16 +196,6 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
-        a.fill_(1.0)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_each_way": a.numel() * 4, "copies": 3}))
-        return
 
     wl = synth.WORKLOADS[args.workload]
     paged = args.storage == "paged"
@@ -250,6 +251,16 @@ def main():
                    "workspace_bytes": ws_bytes, "paged_pages_high_per_row": pages_high,
                    "kernel_sha": kernel_sha()},
     }
+    if args.with_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        a.fill_(1.0)
+        c = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.add(a, 1.0, out=c)   # vectorised elementwise kernel: 16 B per lane
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_each_way": a.numel() * 4, "copies": 2}
+        del a, c
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(x, lens, wl, args.cpu_seconds)
@@ -258,6 +269,7 @@ def main():
     if not args.no_extras:
         log("[bench] streaming latency, 256 streams")
         result["streaming"] = streaming_latency()
+    if args.compare:
         log("[bench] other workloads")
         result["other_workloads"] = other_workloads()
     print(json.dumps(result))

@@ -6,13 +6,16 @@
 //
 //   select_kernel   frame filter, sec. 3.5 (one block per row, ordered
 //                   ballot compaction instead of a block scan).
-//   decode_kernel   one wave per row (offline) or stream, the whole frame loop
-//                   in-kernel (the idea of sec. 3.4.8): per frame
-//     - stage the frame's log-probabilities in LDS (the next frame is loaded
-//       into registers while this one is decoded);
+//   decode_kernel   one workgroup per row (offline) or stream, the whole
+//                   frame loop in-kernel (the idea of sec. 3.4.8).  Waves
+//                   1..P ("producers") take the selected frames in turn:
+//     - stream the frame's log-probabilities HBM -> LDS (16-byte
+//       global-to-LDS loads) into a ring of P+1 frame slots;
 //     - vocabulary top-K (sec. 3.3 step 0, sec. 3.4.7): the best 2W+3
-//       non-blank labels by (log-prob desc, label asc), wave64 bitonic sort;
-//     - step 0 seeding (sec. 3.3) from that list;
+//       non-blank labels by (log-prob desc, label asc), radix threshold,
+//       ballot gather and count ranking; publish the slot by an LDS flag.
+//   Wave 0 runs the serial beam recursion over the published slots:
+//     - step 0 seeding (sec. 3.3) from the ranked list;
 //     - steps >= 1: the beam x vocab extension scores of sec. 3.4.1/3.4.2
 //       are never materialised.  An ordinary label c of beam k scores
 //       lp[c] + logsumexp(pb, pnb) (sec. 3.4.6), so only the ranked labels
