@@ -64,12 +64,14 @@ struct LdsPlan {
   int slot0, slot_stride, slot_Rc, slot_Rl, slot_rank;  // ring of frame slots
   int nslot, nprod;                                     // slots, producer waves
   int scr, flags;                                       // producer scratch, hand-off flags
+  int ring, soffs;                                      // winners ring, store-wave scratch
   int clist, clist_lds;                                 // flat token lists held in LDS
   int fsrc, flen;                                       // flat copy lineage
   int buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh, newlen, nchild, childc, scal,
       tab, ref, fstk, tail, tlen, total;
 };
 constexpr int kMaxSlots = 8;
+constexpr int kRing = 8;   // steps of winners the store wave may lag behind
 
 struct Params {
   Layout L;
@@ -104,8 +106,9 @@ struct Beam {
   uint64_t h, hp;
 };
 
-constexpr int kProfBase = 32;   // header word of the first phase counter
+constexpr int kProfBase = 32;   // header word of the first phase counter (beam wave)
 constexpr int kProfSlots = 8;
+constexpr int kProfExtra = 48;  // header word of the producer / store-wave counters
 
 struct Ctx {
   Layout L;       // copied from the kernel arguments (never address-taken)
@@ -142,6 +145,8 @@ struct Ctx {
   int* flen;      // flat: [2][32] length of that row
   int* clist;     // flat: global or LDS
   int* pages;     // paged: global
+  int* wdone;     // last step whose tokens the store wave has written
+  int* abortf;
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
   uint64_t prof_t;
@@ -169,6 +174,32 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_wave_barrier();
+}
+
+// Producer / consumer hand-off inside a workgroup: LDS flags written with
+// release and read with acquire semantics at workgroup scope.  A wait gives up
+// after kSpinLimit polls and raises the workgroup's abort flag, which every
+// wave checks, so no wave can wait forever.
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ int flag_load(int* f) {
+  return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void flag_store(int* f, int v) {
+  __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Waits until *flag == target (eq) or *flag >= target (!eq); false on abort
+// (abortf == nullptr: not cancelled by the abort flag, still bounded).
+__device__ __forceinline__ bool spin_wait(int* flag, int target, bool eq, int* abortf) {
+  for (int it = 0; it < kSpinLimit; it++) {
+    const int v = flag_load(flag);
+    if (eq ? v == target : v >= target) return true;
+    if (abortf && flag_load(abortf)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (abortf) flag_store(abortf, 1);
+  return false;
 }
 
 __device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, int slot, int pos) {
@@ -248,123 +279,171 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 // ------------------------------------------------------- vocabulary top-K --
 // Ranks one frame (run by a producer wave): the best K non-blank labels by
 // (lp desc, label asc) into Rc / Rl, rank[label] = position (-1 elsewhere).
-// A threshold that at least K labels reach is found first (the K-th largest
-// of every lane's two best keys, by a radix search with ballots); the labels
-// at or above it are gathered and ranked by counting.  prevK = size of the
-// list this slot held before (its rank entries are cleared).
+// prevK = size of the list this slot held before (its rank entries are
+// cleared).  The row is read as groups of four labels (the LDS row is 16-byte
+// aligned whatever V is; the blank and the padding past V are set to -inf
+// while the frame is ranked and the blank is restored before returning):
+//   1. every lane keeps the two largest group maxima it sees;
+//   2. thr = the K-th largest of those 128 values (radix search with
+//      ballots): at least K groups, hence K labels, reach it;
+//   3. the groups whose maximum reaches thr are listed;
+//   4. their labels at or above thr are gathered as composite keys;
+//   5. the gathered keys are ranked by counting (broadcast LDS reads).
+// Lists that do not fit the scratch fall back to a streaming top-K over the
+// whole row.
 __device__ __forceinline__ uint32_t sortable_bits(float f) {
   const uint32_t u = __float_as_uint(f + 0.0f);
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
-__device__ __forceinline__ void rank_frame(const float* row, int V, int blank, int K, int prevK,
+constexpr int kMaxGroups = 256;   // listed groups (step 3), ints after the keys
+constexpr int kMaxGather = 128;   // gathered keys (step 4)
+
+__device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, int prevK,
                                            int* Rc, float* Rl, int8_t* rank, uint64_t* scr) {
   const int lane = lane_id();
+  const float ninf = -__builtin_inff();
   for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
-  // pass 1: two best keys per lane (4 labels per 16-byte LDS read when the
-  // row is a whole number of float4)
-  uint32_t a = 0u, b = 0u;
-  auto push2 = [&](uint32_t u) {
-    const uint32_t lo = u < a ? u : a;
-    a = u > a ? u : a;
-    b = lo > b ? lo : b;
-  };
-  const bool v4 = (V & 3) == 0;
-  if (v4) {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    const int n4 = V >> 2;
+  const int n4 = (V + 3) >> 2;
+  const float lpb = row[blank];
+  lds_sync();
+  if (lane == 0) row[blank] = ninf;
+  if (lane < 4 * n4 - V) row[V + lane] = ninf;
+  lds_sync();
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
+  constexpr int U = 8;  // groups per lane loaded before use
 
-    for (int i = lane; i < n4; i += kWave) {
-      const float4 q = r4[i];
-      const int c = 4 * i;
-      push2(c == blank ? 0u : sortable_bits(q.x));
-      push2(c + 1 == blank ? 0u : sortable_bits(q.y));
-      push2(c + 2 == blank ? 0u : sortable_bits(q.z));
-      push2(c + 3 == blank ? 0u : sortable_bits(q.w));
+  // 1. two largest group maxima per lane
+  float hi = ninf, lo = ninf;
+  for (int base = 0; base < n4; base += U * kWave) {
+    float4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = base + u * kWave + lane;
+      q[u] = g < n4 ? r4[g] : ninf4;
     }
-  } else {
-    for (int c = lane; c < V; c += kWave) push2(c == blank ? 0u : sortable_bits(row[c]));
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      lo = __builtin_amdgcn_fmed3f(m, hi, lo);
+      hi = fmaxf(hi, m);
+    }
   }
+  // 2. threshold (never below -inf)
+  const uint32_t a = sortable_bits(hi), b = sortable_bits(lo);
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; bit--) {
     const uint32_t cand = thr | (1u << bit);
     const int cnt = __popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand));
     if (cnt >= K) thr = cand;
   }
-  // pass 2: every label at or above the threshold (gathered in any order:
-  // they are ranked below)
-  int cnt = 0;
-  auto gather = [&](uint32_t u, int c) {
-    const bool pass = u != 0u && u >= thr;
-    const uint64_t m = __ballot(pass);
-    const int pos = cnt + lanes_below(m);
-    if (pass && pos < kBuf) scr[pos] = ((uint64_t)u << 32) | (uint32_t)(~c);
-    cnt += __popcll(m);
-  };
-  if (v4) {
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    const int n4 = V >> 2;
+  const uint32_t thr_min = sortable_bits(ninf);
+  thr = thr > thr_min ? thr : thr_min;
+  const float tf = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
 
-    for (int i0 = 0; i0 < n4; i0 += kWave) {
-      const int i = i0 + lane;
-      float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < n4) q = r4[i];
-      const int c = 4 * i;
-      const bool in = i < n4;
-      gather((in && c != blank) ? sortable_bits(q.x) : 0u, c);
-      gather((in && c + 1 != blank) ? sortable_bits(q.y) : 0u, c + 1);
-      gather((in && c + 2 != blank) ? sortable_bits(q.z) : 0u, c + 2);
-      gather((in && c + 3 != blank) ? sortable_bits(q.w) : 0u, c + 3);
+  // 3. groups reaching the threshold
+  int* gid = reinterpret_cast<int*>(scr + kMaxGather);
+  int ng = 0;
+  for (int base = 0; base < n4; base += U * kWave) {
+    float4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = base + u * kWave + lane;
+      q[u] = g < n4 ? r4[g] : ninf4;
     }
-  } else {
-    for (int base = 0; base < V; base += kWave) {
-      const int c = base + lane;
-      gather((c < V && c != blank) ? sortable_bits(row[c]) : 0u, c);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = base + u * kWave + lane;
+      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      const bool pass = g < n4 && m >= tf;
+      const uint64_t mk = __ballot(pass);
+      const int pos = ng + lanes_below(mk);
+      if (pass && pos < kMaxGroups) gid[pos] = g;
+      ng += __popcll(mk);
     }
   }
   lds_sync();
-  if (cnt <= 2 * kWave) {
-    const uint64_t x0 = lane < cnt ? scr[lane] : 0ull;
-    const uint64_t x1 = lane + kWave < cnt ? scr[lane + kWave] : 0ull;
+
+  // 4. their labels at or above the threshold
+  int n = 0;
+  if (ng <= kMaxGroups) {
+    for (int j0 = 0; j0 < ng; j0 += kWave) {
+      const int j = j0 + lane;
+      const bool in = j < ng;
+      const int g = in ? gid[j] : 0;
+      const float4 q = in ? r4[g] : ninf4;
+      const float xv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int c = 4 * g + e;
+        const bool pass = in && c != blank && c < V && xv[e] >= tf;
+        const uint64_t mk = __ballot(pass);
+        const int pos = n + lanes_below(mk);
+        if (pass && pos < kMaxGather)
+          scr[pos] = ((uint64_t)sortable_bits(xv[e]) << 32) | (uint32_t)(~c);
+        n += __popcll(mk);
+      }
+    }
+  }
+  lds_sync();
+
+  if (ng <= kMaxGroups && n >= K && n <= kMaxGather) {
+    // 5. rank by counting, two keys per lane
+    const int n8 = (n + 7) & ~7;
+    if (n + lane < n8) scr[n + lane] = 0ull;
+    lds_sync();
+    const uint64_t x0 = lane < n ? scr[lane] : 0ull;
+    const uint64_t x1 = lane + kWave < n ? scr[lane + kWave] : 0ull;
     int rk0 = 0, rk1 = 0;
-    const int n0 = cnt < kWave ? cnt : kWave;
-    for (int j = 0; j < n0; j++) {
-      const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x0 >> 32), j) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x0, j);
-      rk0 += y > x0 ? 1 : 0;
-      rk1 += y > x1 ? 1 : 0;
+    const ulonglong2* y2 = reinterpret_cast<const ulonglong2*>(scr);
+    if (n <= kWave) {
+      for (int j = 0; j < n8; j += 8) {
+        const ulonglong2 p0 = y2[j / 2], p1 = y2[j / 2 + 1], p2 = y2[j / 2 + 2], p3 = y2[j / 2 + 3];
+        rk0 += (p0.x > x0 ? 1 : 0) + (p0.y > x0 ? 1 : 0) + (p1.x > x0 ? 1 : 0) +
+               (p1.y > x0 ? 1 : 0) + (p2.x > x0 ? 1 : 0) + (p2.y > x0 ? 1 : 0) +
+               (p3.x > x0 ? 1 : 0) + (p3.y > x0 ? 1 : 0);
+      }
+    } else {
+      for (int j = 0; j < n8; j += 8) {
+        const ulonglong2 p0 = y2[j / 2], p1 = y2[j / 2 + 1], p2 = y2[j / 2 + 2], p3 = y2[j / 2 + 3];
+        rk0 += (p0.x > x0 ? 1 : 0) + (p0.y > x0 ? 1 : 0) + (p1.x > x0 ? 1 : 0) +
+               (p1.y > x0 ? 1 : 0) + (p2.x > x0 ? 1 : 0) + (p2.y > x0 ? 1 : 0) +
+               (p3.x > x0 ? 1 : 0) + (p3.y > x0 ? 1 : 0);
+        rk1 += (p0.x > x1 ? 1 : 0) + (p0.y > x1 ? 1 : 0) + (p1.x > x1 ? 1 : 0) +
+               (p1.y > x1 ? 1 : 0) + (p2.x > x1 ? 1 : 0) + (p2.y > x1 ? 1 : 0) +
+               (p3.x > x1 ? 1 : 0) + (p3.y > x1 ? 1 : 0);
+      }
     }
-    for (int j = 0; j + kWave < cnt; j++) {
-      const uint64_t y = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x1 >> 32), j) << 32) |
-                         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x1, j);
-      rk0 += y > x0 ? 1 : 0;
-      rk1 += y > x1 ? 1 : 0;
-    }
-    if (lane < cnt && rk0 < K) {
+    if (lane < n && rk0 < K) {
       const int c = (int)(~(uint32_t)x0);
       Rc[rk0] = c;
       Rl[rk0] = row[c];
       rank[c] = (int8_t)rk0;
     }
-    if (lane + kWave < cnt && rk1 < K) {
+    if (lane + kWave < n && rk1 < K) {
       const int c = (int)(~(uint32_t)x1);
       Rc[rk1] = c;
       Rl[rk1] = row[c];
       rank[c] = (int8_t)rk1;
     }
   } else {
+    // fallback: streaming top-K over the whole row (exact for any input)
     auto gen = [&](int64_t i) -> uint64_t {
       const int c = (int)i;
       return c == blank ? 0ull : (((uint64_t)sortable_bits(row[c]) << 32) | (uint32_t)(~c));
     };
     const int got = stream_topk_buf(scr, K, V, gen);
-    for (int r = lane; r < got; r += kWave) {
-      const int c = (int)(~(uint32_t)scr[r]);
+    for (int r = lane; r < K; r += kWave) {
+      // fewer than K orderable labels only with NaN input: pad with the blank
+      const int c = r < got ? (int)(~(uint32_t)scr[r]) : blank;
       Rc[r] = c;
-      Rl[r] = row[c];
-      rank[c] = (int8_t)r;
+      Rl[r] = r < got ? row[c] : ninf;
+      if (r < got) rank[c] = (int8_t)r;
     }
   }
+  lds_sync();
+  if (lane == 0) row[blank] = lpb;
   lds_sync();
 }
 
@@ -406,16 +485,31 @@ __device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* r
     b.pb = row[blank];
     b.score = row[blank];
   }
-  // token store, parity 0 (seeded, not copied from any slot)
+}
+
+// ------------------------------------------------------------ token stores --
+// Winner of output slot `lane` (valid lanes < W): source beam k, label c, the
+// source's length.  k == kSeed marks a step-0 slot (tokens = [c]).
+struct Winner {
+  bool valid;
+  int k, c, len_k;
+};
+constexpr int kSeed = 0x7f;
+
+// Step 0 (sec. 3.3): each seeded slot holds its one label, written fresh.
+__device__ __forceinline__ void store_seed(const Ctx& C, const Winner& w) {
+  const Layout& L = C.L;
+  const int lane = lane_id();
+  const int W = L.W;
+  const bool want = w.valid && w.c != L.blank;
   if (lane < kMaxBeam) {
     C.fsrc[lane] = -1;
-    C.flen[lane] = lane < m ? 1 : 0;
+    C.flen[lane] = want ? 1 : 0;
   }
   if (!L.paged) {
-    if (lane < m) C.clist[(int64_t)lane * L.ldc] = b.last;
+    if (want) C.clist[(int64_t)lane * L.ldc] = w.c;
   } else {
     // one fresh page per seeded label
-    const bool want = lane < m;
     const uint64_t mk = __ballot(want);
     const int idx = lanes_below(mk);
     const int nw = __popcll(mk);
@@ -440,21 +534,18 @@ __device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* r
         C.ref[page] = 1;
         C.tab[(0 * W + lane) * L.max_lp + 0] = page;
         C.tlen[lane] = 1;
-        C.pages[(int64_t)page * L.ps] = b.last;
-        C.tail[(0 * W + lane) * L.ps] = b.last;
+        C.pages[(int64_t)page * L.ps] = w.c;
+        C.tail[(0 * W + lane) * L.ps] = w.c;
       }
     }
   }
+  const uint64_t lm = __ballot(lane < W && w.valid);
+  lds_sync();
+  if (lane == 0) C.scal[kScalLive0] = (int)(uint32_t)lm;
+  lds_sync();
 }
 
-
 // ------------------------------------------------------------ steps >= 1 ---
-// Winner of output slot `lane` (valid lanes < W): source beam k, label c.
-struct Winner {
-  bool valid;
-  int k, c, len_k;
-};
-
 // The full beam x vocab selection (exact for any input): every candidate of
 // the step is regenerated from the per-beam values left in LDS and streamed
 // through stream_topk.  Used when the pruned candidate set cannot be proven
@@ -796,8 +887,9 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int c2 = __shfl(w.c, ce, 64);
   if (cand >= 0 && c2 != last2_k) cand = -1;
   uint64_t todo = __ballot(cand >= 0);
+  // the previous step's tokens must have been written by the store wave
+  if (todo && !spin_wait(C.wdone, step - 1, false, C.abortf)) todo = 0ull;
   if (todo) {
-    wave_sync();  // the previous step's tokens are in memory
     const int q = (step - 1) & 1;
     const int from = C.scal[kScalCpl0 + q];
     while (todo) {
@@ -882,15 +974,15 @@ __device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner&
 
 // Grow the common prefix of the live beams of parity p (flat store), reading
 // the next 64 positions of every live row.
-__device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, const Beam& b) {
+__device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, bool nlive, int nlen) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W;
   wave_sync();
   const int cpl = C.scal[kScalCpl0 + p];
-  const uint64_t live = __ballot(lane < W && b.live);
+  const uint64_t live = __ballot(lane < W && nlive);
   if (live == 0ull) return;
-  int minlen = lane < W && b.live ? b.len : 0x7fffffff;
+  int minlen = lane < W && nlive ? nlen : 0x7fffffff;
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) minlen = min(minlen, __shfl_xor(minlen, m, 64));
   const int pos = cpl + lane;
@@ -920,8 +1012,8 @@ __device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, const Beam
 // page rebuilt from the LDS mirror of that page (no global read).  Leading
 // full pages shared by every live row of two steps ago are identical in the
 // old and the new row and are skipped.
-__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w,
-                                            const Beam& nb) {
+__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w, bool nlive,
+                                            int nlen) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
@@ -1024,11 +1116,11 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   }
   // leading full pages shared by every live row of parity p
   int pcp = C.scal[kScalPcp0 + q];
-  const bool lv = lane < W && nb.live;
+  const bool lv = lane < W && nlive;
   const uint64_t lm = __ballot(lv);
   const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
   while (lm != 0ull && pcp < max_lp) {
-    const bool full = !lv || nb.len >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
+    const bool full = !lv || nlen >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
     const int e = (lv && full) ? C.tab[(p * W + lane) * max_lp + pcp] : kInvalidPage;
     const int first = __shfl(e, first_live, 64);
     const bool ok = full && (!lv || e == first);
@@ -1188,6 +1280,8 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.clist = S.clist_lds ? reinterpret_cast<int*>(smem + S.clist)
                         : reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
+  C.wdone = nullptr;
+  C.abortf = nullptr;
   return C;
 }
 
@@ -1312,36 +1406,17 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
   if (tid == 0) hdr[kNSel] = cnt;
 }
 
-// Producer / consumer hand-off inside a workgroup: LDS flags written with
-// release and read with acquire semantics at workgroup scope.  A wait gives up
-// after kSpinLimit polls and raises the workgroup's abort flag, which every
-// wave checks, so no wave can wait forever.
-constexpr int kSpinLimit = 1 << 22;
-
-__device__ __forceinline__ int flag_load(int* f) {
-  return __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void flag_store(int* f, int v) {
-  __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Waits until *flag == target (eq) or *flag >= target (!eq); false on abort.
-__device__ __forceinline__ bool spin_wait(int* flag, int target, bool eq, int* abortf) {
-  for (int it = 0; it < kSpinLimit; it++) {
-    const int v = flag_load(flag);
-    if (eq ? v == target : v >= target) return true;
-    if (flag_load(abortf)) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
-  flag_store(abortf, 1);
-  return false;
-}
-
 // Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).  One
-// workgroup per row: wave 0 decodes the frames in order (the serial beam
-// recursion); waves 1..P each take every P-th frame, copy its row into a free
-// LDS slot and rank its labels, so the vocabulary pass runs ahead of, and in
-// parallel with, the beam recursion.  Every row of log_prob is read once.
+// workgroup per row, three roles:
+//   wave 0       the serial beam recursion, frame by frame; it publishes each
+//                step's winners (source slot, label, source length) into a
+//                ring of kRing entries;
+//   wave 1       the token store, following the beam wave through that ring
+//                (up to kRing steps behind): flat copies or paged forks and
+//                appends, so token traffic is off the recursion's path;
+//   waves 2..    producers: each takes every P-th frame, copies its row into
+//                a free LDS slot and ranks its labels, ahead of the recursion.
+// Every row of log_prob is read once.
 template <bool STREAM>
 __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
@@ -1363,12 +1438,16 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* ready = flags;                    // [kMaxSlots]: frame held by each slot
   int* consumed = flags + kMaxSlots;     // last frame the beam wave finished
   int* abortf = consumed + 1;
+  int* wpub = consumed + 2;              // last step whose winners are in the ring
+  int* wdone = consumed + 3;             // last step the store wave has written
+  int2* ring = reinterpret_cast<int2*>(smem + S.ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride); };
   auto slot_Rc = [&](int sl) { return reinterpret_cast<int*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rc); };
   auto slot_Rl = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rl); };
   auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + S.slot0 + sl * S.slot_stride + S.slot_rank); };
 
+  const int step_in = STREAM ? hdr[kStep] : 0;
   // set-up shared by all waves: empty label ranks, flags
   for (int sl = 0; sl < nslot; sl++)
     for (int c = (int)threadIdx.x; c < V; c += (int)blockDim.x) slot_rank(sl)[c] = -1;
@@ -1376,8 +1455,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (threadIdx.x == 0) {
     *consumed = -1;
     *abortf = 0;
+    *wpub = step_in - 1;
+    *wdone = step_in - 1;
   }
-  const int step_in = STREAM ? hdr[kStep] : 0;
   int nframes;
   if (STREAM) {
     nframes = L.cap - step_in;
@@ -1392,25 +1472,105 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int complete = K == V - 1;
   __syncthreads();
 
-  if (wave > 0) {
+  if (wave >= 2) {
     // ------------------------------------------------------------ producer
-    uint64_t* scr = reinterpret_cast<uint64_t*>(smem + S.scr + (wave - 1) * kBuf * 8);
-    for (int f = wave - 1; f < nframes; f += nprod) {
+    const int pid = wave - 2;
+    uint64_t* scr = reinterpret_cast<uint64_t*>(smem + S.scr + pid * kBuf * 8);
+#ifdef CTCPB_PHASE_PROF
+    uint64_t pw = 0, pf = 0, pr = 0, t0 = clock64();
+#endif
+    for (int f = pid; f < nframes; f += nprod) {
       const int sl = f % nslot;
       if (!spin_wait(consumed, f - nslot, false, abortf)) break;
+#ifdef CTCPB_PHASE_PROF
+      uint64_t t1 = clock64();
+      pw += t1 - t0;
+#endif
       float* row = slot_row(sl);
       row_fetch_async(lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t, row, V, vec4);
       row_fetch_wait();
+#ifdef CTCPB_PHASE_PROF
+      t0 = clock64();
+      pf += t0 - t1;
+#endif
       rank_frame(row, V, L.blank, K, f >= nslot ? K : 0, slot_Rc(sl), slot_Rl(sl), slot_rank(sl),
                  scr);
       flag_store(&ready[sl], f);
+#ifdef CTCPB_PHASE_PROF
+      t1 = clock64();
+      pr += t1 - t0;
+      t0 = t1;
+#endif
     }
+#ifdef CTCPB_PHASE_PROF
+    if (lane == 0) {
+      unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
+      atomicAdd(dst + 0, (unsigned long long)pw);
+      atomicAdd(dst + 1, (unsigned long long)pf);
+      atomicAdd(dst + 2, (unsigned long long)pr);
+    }
+#endif
+    return;
+  }
+
+  Ctx C = make_ctx(L, S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
+                   smem);
+  C.wdone = wdone;
+  C.abortf = abortf;
+
+  if (wave == 1) {
+    // ---------------------------------------------------------- store wave
+    C.offs = reinterpret_cast<int*>(smem + S.soffs);
+    for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
+      C.fsrc[i] = -1;
+      C.flen[i] = -1;
+    }
+    lds_sync();
+#ifdef CTCPB_PHASE_PROF
+    uint64_t sw = 0, sk = 0, t0 = clock64();
+#endif
+    for (int f = 0; f < nframes; f++) {
+      const int step = step_in + f;
+      if (!spin_wait(wpub, step, false, abortf)) break;
+#ifdef CTCPB_PHASE_PROF
+      uint64_t t1 = clock64();
+      sw += t1 - t0;
+#endif
+      const int2 rec = lane < W ? ring[(f % kRing) * kMaxBeam + lane] : make_int2(-1, 0);
+      Winner w;
+      w.valid = rec.x >= 0;
+      w.k = w.valid ? (rec.x >> 16) : lane;
+      w.c = w.valid ? (rec.x & 0xffff) : L.blank;
+      w.len_k = w.valid ? rec.y : 0;
+      const bool nlive = w.valid;
+      const int nlen = w.valid ? w.len_k + (w.c != L.blank ? 1 : 0) : 0;
+      if (step == 0) {
+        store_seed(C, w);
+      } else if (L.paged) {
+        store_paged(C, step, w, nlive, nlen);
+      } else {
+        store_flat(C, step, w);
+        if ((step & 15) == 15) advance_cpl_flat(C, step & 1, nlive, nlen);
+      }
+      lds_sync();
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): global token writes done
+      flag_store(wdone, step);
+#ifdef CTCPB_PHASE_PROF
+      t0 = clock64();
+      sk += t0 - t1;
+#endif
+    }
+#ifdef CTCPB_PHASE_PROF
+    if (lane == 0) {
+      unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
+      atomicAdd(dst + 3, (unsigned long long)sw);
+      atomicAdd(dst + 4, (unsigned long long)sk);
+    }
+#endif
     return;
   }
 
   // -------------------------------------------------------------- beam wave
-  Ctx C = make_ctx(L, S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
-                   smem);
   Beam b;
   int step, last_t;
   if (STREAM) {
@@ -1435,13 +1595,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
   }
-  for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
-    C.fsrc[i] = -1;
-    C.flen[i] = -1;
-  }
   lds_sync();
 
-  const int step0 = step;
   bool aborted = false;
   for (int f = 0; f < nframes; f++) {
     const int sl = f % nslot;
@@ -1460,29 +1615,38 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.Rc = slot_Rc(sl);
     C.Rl = slot_Rl(sl);
     C.rank = slot_rank(sl);
-    const int t = STREAM ? step0 + f : sel[f];
+    const int t = STREAM ? step_in + f : sel[f];
+    Winner w;
     if (step == 0) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
-      const uint64_t lm = __ballot(lane < W && b.live);
-      lds_sync();
-      if (lane == 0) C.scal[kScalLive0] = (int)(uint32_t)lm;
+      const int nb0 = W > 1 ? W - 1 : 1;
+      w.valid = lane < W && b.live;
+      w.k = kSeed;
+      w.c = lane < (nb0 < K ? nb0 : K) ? C.Rc[lane] : L.blank;
+      w.len_k = 0;
     } else {
       const int g = t > last_t + 1 ? 1 : 0;
-      const Winner w = beam_step(C, b, row, g, step, K, complete);
-      if (L.paged) {
-        store_paged(C, step, w, b);
-      } else {
-        store_flat(C, step, w);
-        if ((step & 15) == 15) advance_cpl_flat(C, step & 1, b);
-      }
+      w = beam_step(C, b, row, g, step, K, complete);
     }
+    // hand the winners to the store wave (its ring entry must be free)
+    if (!spin_wait(wdone, step - kRing, false, abortf)) {
+      aborted = true;
+      break;
+    }
+    if (lane < W)
+      ring[(f % kRing) * kMaxBeam + lane] =
+          make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
     last_t = t;
-    step++;
     lds_sync();
     flag_store(consumed, f);
+    flag_store(wpub, step);
+    step++;
   }
-  if (aborted && lane == 0) C.scal[kScalStatus] |= kStatusAborted;
+  // every published step stored (bounded wait that the abort flag does not cut
+  // short: the store wave drains what was published before it stops)
+  if (!spin_wait(wdone, step - 1, false, nullptr)) aborted = true;
+  if (aborted) atomicOr(&C.scal[kScalStatus], kStatusAborted);
 #ifdef CTCPB_PHASE_PROF
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
@@ -1663,7 +1827,9 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
   // hand-off
-  S.flags = take((kMaxSlots + 2) * 4);
+  S.flags = take((kMaxSlots + 4) * 4);
+  S.ring = take(kRing * kMaxBeam * 8);
+  S.soffs = take(128 * 4);
   S.nprod = nprod;
   S.nslot = nprod + 1;
   S.scr = take(nprod * kBuf * 8);
@@ -1798,7 +1964,7 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
-  if (int rc = launch(decode_kernel<false>, batch, 64 * (1 + P.S.nprod), P.S.total, st, P,
+  if (int rc = launch(decode_kernel<false>, batch, 64 * (2 + P.S.nprod), P.S.total, st, P,
                       "decode_kernel"))
     return rc;
   return ok();
@@ -1862,7 +2028,7 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
-  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (1 + P.S.nprod), P.S.total,
+  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (2 + P.S.nprod), P.S.total,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
   return ok();
