@@ -150,6 +150,8 @@ struct Ctx {
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
   uint64_t prof_t;
+  uint64_t stat_surv, stat_iters, stat_wide;   // survivors, gather rounds, wide steps
+  uint64_t stat_multi;                          // steps where a beam has 3+ survivors
 #endif
 };
 
@@ -643,10 +645,11 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
 
   PROF_MARK(2);
-  // ---- a tight lower bound tau0 of the W-th best key: each beam offers its
-  // two best candidates (blank slot, repeated-label slot, first two
-  // non-excluded ranked labels); the W-th largest of those 2W values has at
-  // least W candidates at or above it
+  // ---- each beam's two best candidates, as composite keys (0 = none): the
+  // blank slot, the repeated-label slot and its first non-excluded ranked
+  // labels.  Sorting those 2W keys gives the top W exactly whenever no beam
+  // has a third candidate above the W-th of them (checked below); otherwise
+  // the W-th key is a tight threshold for the general gather.
   const int nPool = complete ? nR : nR - 1;
   uint32_t fr0, fr1, fr2;  // in-pool ranks still open to this beam
   {
@@ -666,135 +669,140 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   auto first_bit = [](uint32_t a, uint32_t b, uint32_t c) -> int {
     return a ? __builtin_ctz(a) : (b ? 32 + __builtin_ctz(b) : (c ? 64 + __builtin_ctz(c) : -1));
   };
-  const int r0 = first_bit(fr0, fr1, fr2);
+  auto drop_bit = [](int r, uint32_t& a, uint32_t& b, uint32_t& c) {
+    if (r < 0) return;
+    if (r < 32) a &= a - 1u;
+    else if (r < 64) b &= b - 1u;
+    else c &= c - 1u;
+  };
   uint32_t g0 = fr0, g1 = fr1, g2 = fr2;
-  if (r0 >= 0) {
-    if (r0 < 32) g0 &= g0 - 1u;
-    else if (r0 < 64) g1 &= g1 - 1u;
-    else g2 &= g2 - 1u;
-  }
+  const int r0 = first_bit(g0, g1, g2);
+  drop_bit(r0, g0, g1, g2);
   const int r1 = first_bit(g0, g1, g2);
-  const float o1 = r0 >= 0 ? C.Rl[r0] + A : kNeg;
-  const float o2 = r1 >= 0 ? C.Rl[r1] + A : kNeg;
-  const float shi = fmaxf(keyb, keyc), slo = fminf(keyb, keyc);
-  const float v1 = fmaxf(shi, o1);
-  const float v2 = fmaxf(fminf(shi, o1), fmaxf(slo, o2));
-  // the W-th largest of the 2W values, by counting with broadcast LDS reads
-  // (lane j < 32 holds beam j's best, lane 32 + j its second best)
-  float* tv = reinterpret_cast<float*>(C.buf);
-  if (lane < kMaxBeam) {
-    tv[lane] = lv ? v1 : kNeg;
-    tv[kMaxBeam + lane] = lv ? v2 : kNeg;
-  }
-  lds_sync();
-  const float mine = tv[lane];
-  int ge = 0;
-#pragma unroll
-  for (int j = 0; j < kWave; j += 4) {
-    const float4 y = *reinterpret_cast<const float4*>(tv + j);
-    ge += (y.x >= mine ? 1 : 0) + (y.y >= mine ? 1 : 0) + (y.z >= mine ? 1 : 0) +
-          (y.w >= mine ? 1 : 0);
-  }
-  const float tau0 = wave_max((mine > kNeg && ge >= W) ? mine : kNeg);
-  lds_sync();
+  drop_bit(r1, g0, g1, g2);
+  const int r2 = first_bit(g0, g1, g2);
+  const uint32_t idb = (uint32_t)(lane * V);
+  auto ordinary = [&](int r) -> uint64_t {
+    if (!lv || r < 0) return 0ull;
+    const float key = C.Rl[r] + A;
+    return key > kNeg ? compose(key, idb + (uint32_t)C.Rc[r]) : 0ull;
+  };
+  const uint64_t o1 = ordinary(r0), o2 = ordinary(r1), o3 = ordinary(r2);
+  const uint64_t cb = (lv && keyb > kNeg) ? compose(keyb, idb + (uint32_t)blank) : 0ull;
+  const uint64_t cc = (lv && keyc > kNeg) ? compose(keyc, idb + (uint32_t)last) : 0ull;
+  const uint64_t shi = cb > cc ? cb : cc, slo = cb > cc ? cc : cb;
+  const uint64_t t1 = shi > o1 ? shi : o1;
+  const uint64_t mid = shi > o1 ? o1 : shi, lo2 = slo > o2 ? slo : o2;
+  const uint64_t t2 = mid > lo2 ? mid : lo2;
+  // the beam's third candidate (its lists are sorted, so all later ones are
+  // below it); ranked labels past the list are bounded separately below
+  const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
+  // lane j < 32 holds beam j's best, lane 32 + j its second best
+  const uint64_t t2x = xor_lane_u64<32>(t2);
+  const uint64_t top = wave_sort64_desc<uint64_t>(lane < kMaxBeam ? t1 : t2x);
+  const uint64_t cW =
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(top >> 32), W - 1) << 32) |
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, W - 1);
+  const bool exact = __ballot(n3 > cW) == 0ull;
   PROF_MARK(3);
-  // ---- every candidate at or above tau0 (ranked labels are sorted, so each
-  // beam's qualifying labels form a prefix of its list)
-  // gathered with a wave-uniform running count (ballot + lane prefix), the
-  // ranked labels in chunks of four until no beam has one at or above tau0
-  int nsurv = 0;
-  {
-    auto put = [&](bool pass, uint64_t key) {
-      const uint64_t m = __ballot(pass);
-      const int pos = nsurv + lanes_below(m);
-      if (pass && pos < kBuf) C.buf[pos] = key;
-      nsurv += __popcll(m);
-    };
-    put(lv && keyb > kNeg && keyb >= tau0, compose(keyb, (uint32_t)(lane * V + blank)));
-    put(lv && keyc > kNeg && keyc >= tau0, compose(keyc, (uint32_t)(lane * V + last)));
-    bool more = lv;
-    for (int r = 0; r < nPool; r += 4) {
-      if (!__ballot(more)) break;
-      const float4 q = *reinterpret_cast<const float4*>(C.Rl + r);
-      const int4 cq = *reinterpret_cast<const int4*>(C.Rc + r);
-      const float lpv[4] = {q.x, q.y, q.z, q.w};
-      const int cv[4] = {cq.x, cq.y, cq.z, cq.w};
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int rr = r + j;
-        const float key = lpv[j] + A;
-        const bool above = more && rr < nPool && key >= tau0;
-        any = any || above;
-        const uint32_t open =
-            rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
-        put(above && (open & 1u), compose(key, (uint32_t)(lane * V + cv[j])));
-      }
-      more = more && any;
-    }
-  }
-  lds_sync();
-  PROF_MARK(4);
-  if (nsurv <= kWave) {
-    // rank by counting: rank = number of survivors with a larger key, read
-    // two at a time with broadcast LDS loads
-    const int n8 = (nsurv + 7) & ~7;
-    if (nsurv + lane < n8) C.buf[nsurv + lane] = 0ull;
-    lds_sync();
-    const uint64_t x = lane < nsurv ? C.buf[lane] : 0ull;
-    int rk = 0;
-    for (int j = 0; j < n8; j += 8) {
-      const ulonglong2* y2 = reinterpret_cast<const ulonglong2*>(C.buf + j);
-      const ulonglong2 a0 = y2[0], a1 = y2[1], a2 = y2[2], a3 = y2[3];
-      rk += (a0.x > x ? 1 : 0) + (a0.y > x ? 1 : 0) + (a1.x > x ? 1 : 0) + (a1.y > x ? 1 : 0) +
-            (a2.x > x ? 1 : 0) + (a2.y > x ? 1 : 0) + (a3.x > x ? 1 : 0) + (a3.y > x ? 1 : 0);
-    }
-    lds_sync();
-    const int nw = nsurv < W ? nsurv : W;
-    if (lane < nsurv && rk < W) C.buf[rk] = x;
-    if (lane >= nw && lane < W) C.buf[lane] = 0ull;
-    lds_sync();
+  uint64_t wc;  // winner of slot `lane` (composite key, 0 = none)
+  if (exact) {
+    wc = lane < W ? top : 0ull;
+    PROF_MARK(4);
   } else {
-    // many survivors: exact streaming top-W over them (regenerated per beam
-    // from the ranked list, since the buffer kept only the first kBuf)
-    int lo = 0, hi = lv ? nPool : 0;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (C.Rl[mid] + A >= tau0) lo = mid + 1;
-      else hi = mid;
+    const float tau0 = cW > comp_floor() ? comp_key(cW) : kNeg;
+    // ---- every candidate at or above tau0 (ranked labels are sorted, so each
+    // beam's qualifying labels form a prefix of its list)
+    // gathered with a wave-uniform running count (ballot + lane prefix), the
+    // ranked labels in chunks of four until no beam has one at or above tau0
+    int nsurv = 0;
+    {
+      auto put = [&](bool pass, uint64_t key) {
+        const uint64_t m = __ballot(pass);
+        const int pos = nsurv + lanes_below(m);
+        if (pass && pos < kBuf) C.buf[pos] = key;
+        nsurv += __popcll(m);
+      };
+      put(lv && keyb > kNeg && keyb >= tau0, compose(keyb, (uint32_t)(lane * V + blank)));
+      put(lv && keyc > kNeg && keyc >= tau0, compose(keyc, (uint32_t)(lane * V + last)));
+      bool more = lv;
+      for (int r = 0; r < nPool; r += 4) {
+        if (!__ballot(more)) break;
+#ifdef CTCPB_PHASE_PROF
+        C.stat_iters++;
+#endif
+        const float4 q = *reinterpret_cast<const float4*>(C.Rl + r);
+        const int4 cq = *reinterpret_cast<const int4*>(C.Rc + r);
+        const float lpv[4] = {q.x, q.y, q.z, q.w};
+        const int cv[4] = {cq.x, cq.y, cq.z, cq.w};
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int rr = r + j;
+          const float key = lpv[j] + A;
+          const bool above = more && rr < nPool && key >= tau0;
+          any = any || above;
+          const uint32_t open =
+              rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
+          put(above && (open & 1u), compose(key, (uint32_t)(lane * V + cv[j])));
+        }
+        more = more && any;
+      }
     }
-    const int nk = lo;
-    const int incl = wave_incl_scan(lane < W ? nk : 0);
-    const int M = __shfl(incl, 63, 64);
-    if (lane < W) C.offs[lane] = incl - nk;
     lds_sync();
-    const int ncand = M + 2 * W;
-    auto candidate = [&](int64_t q64) -> uint64_t {
-      const int q = (int)q64;
-      if (q >= M) {
-        const int j = q - M, kk = j >> 1;
-        const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
-        const int c = (j & 1) ? C.lastk[kk] : blank;
-        return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
+    PROF_MARK(4);
+#ifdef CTCPB_PHASE_PROF
+    C.stat_surv += nsurv;
+    C.stat_multi += 1;
+    C.stat_wide += nsurv > kWave ? 1 : 0;
+#endif
+    if (nsurv <= kWave) {
+      // one survivor per lane, sorted in registers
+      wc = wave_sort64_desc<uint64_t>(lane < nsurv ? C.buf[lane] : 0ull);
+      if (lane >= W) wc = 0ull;
+    } else {
+      // many survivors: exact streaming top-W over them (regenerated per beam
+      // from the ranked list, since the buffer kept only the first kBuf)
+      int lo = 0, hi = lv ? nPool : 0;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (C.Rl[mid] + A >= tau0) lo = mid + 1;
+        else hi = mid;
       }
-      int a = 0, z = W - 1;
-      while (a < z) {
-        const int mid = (a + z + 1) >> 1;
-        if (C.offs[mid] <= q) a = mid;
-        else z = mid - 1;
-      }
-      const int rho = q - C.offs[a];
-      const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
-      return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
-    };
-    stream_topk(C, W, ncand, candidate);
-    if (lane == 0) C.scal[kScalWide] += 1;
+      const int nk = lo;
+      const int incl = wave_incl_scan(lane < W ? nk : 0);
+      const int M = __shfl(incl, 63, 64);
+      if (lane < W) C.offs[lane] = incl - nk;
+      lds_sync();
+      const int ncand = M + 2 * W;
+      auto candidate = [&](int64_t q64) -> uint64_t {
+        const int q = (int)q64;
+        if (q >= M) {
+          const int j = q - M, kk = j >> 1;
+          const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
+          const int c = (j & 1) ? C.lastk[kk] : blank;
+          return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
+        }
+        int a = 0, z = W - 1;
+        while (a < z) {
+          const int mid = (a + z + 1) >> 1;
+          if (C.offs[mid] <= q) a = mid;
+          else z = mid - 1;
+        }
+        const int rho = q - C.offs[a];
+        const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
+        return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
+      };
+      stream_topk(C, W, ncand, candidate);
+      if (lane == 0) C.scal[kScalWide] += 1;
+      wc = lane < W ? C.buf[lane] : 0ull;
+    }
   }
   bool need_full = false;
   if (!complete) {
     // labels outside the ranked list score at most A_k + (last ranked lp);
     // they must stay strictly below the W-th selected key
-    const uint64_t wl = C.buf[W - 1];
+    const uint64_t wl = shfl_u64(wc, W - 1);
     const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
     const float bound = C.Rl[nR - 1];
     const bool bad = lv && !((bound + A) < keyW);
@@ -803,11 +811,11 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   if (need_full) {
     full_select(C, row);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
+    wc = lane < W ? C.buf[lane] : 0ull;
   }
 
   PROF_MARK(5);
   // winners in rank order (slot r = rank r), sec. 3.4.5
-  const uint64_t wc = lane < W ? C.buf[lane] : 0ull;
   Winner w;
   w.valid = lane < W && wc > comp_floor();
   const uint32_t id = comp_id(wc);
@@ -1603,6 +1611,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
 #ifdef CTCPB_PHASE_PROF
     if (f == 0) {
       for (int i = 0; i < kProfSlots; i++) C.prof[i] = 0;
+      C.stat_surv = C.stat_iters = C.stat_wide = C.stat_multi = 0;
       C.prof_t = clock64();
     }
 #endif
@@ -1651,6 +1660,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
     for (int i = 0; i < kProfSlots; i++) dst[i] = C.prof[i];
+    uint64_t* st = reinterpret_cast<uint64_t*>(C.hdr + kProfExtra) + 5;
+    st[0] = C.stat_surv;
+    st[1] = C.stat_iters;
+    st[2] = C.stat_wide;
+    C.hdr[kLastT + 20] = (int)C.stat_multi;   // header word 21 (unused field), diagnostics only
   }
 #endif
   lds_sync();

@@ -50,6 +50,78 @@ constexpr int kDppMirror = 0x140;       // reverse within 16 lanes
 constexpr int kDppBcast15 = 0x142;      // lane 15 of each row -> next row
 constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
 __device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
+__device__ __forceinline__ constexpr int dpp_row_shl(int n) { return 0x100 + n; }
+
+// Value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}, without an LDS
+// round trip: quad permutes for 1 and 2, a row shift each way for 4 and 8,
+// and the gfx950 lane-swap instructions across rows (16) and halves (32).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int x = (int)v;
+  if constexpr (J == 1) {
+    return (uint32_t)dpp_mov<kDppXor1>(x, x);
+  } else if constexpr (J == 2) {
+    return (uint32_t)dpp_mov<kDppXor2>(x, x);
+  } else if constexpr (J == 4 || J == 8) {
+    const int dn = dpp_mov<dpp_row_shr(J)>(x, x);  // lane i <- lane i - J
+    const int up = dpp_mov<dpp_row_shl(J)>(x, x);  // lane i <- lane i + J
+    return (uint32_t)((lane_id() & J) ? dn : up);
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane_id() & 32) ? r[0] : r[1];
+  }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
+  const uint32_t lo = xor_lane<J>((uint32_t)v);
+  const uint32_t hi = xor_lane<J>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage of a 64-lane bitonic sort (descending overall):
+// lane i keeps the larger of (own, lane i ^ J) when bit J of i equals bit K of
+// i, else the smaller.
+template <int K, int J, typename T>
+__device__ __forceinline__ T bitonic_stage(T v) {
+  T p;
+  if constexpr (sizeof(T) == 8) p = xor_lane_u64<J>(v);
+  else p = xor_lane<J>(v);
+  const int lane = lane_id();
+  const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
+  return (keep_max == (v > p)) ? v : p;
+}
+
+// Sorts one 32- or 64-bit unsigned key per lane into descending lane order.
+template <typename T>
+__device__ __forceinline__ T wave_sort64_desc(T v) {
+  v = bitonic_stage<2, 1>(v);
+  v = bitonic_stage<4, 2>(v);
+  v = bitonic_stage<4, 1>(v);
+  v = bitonic_stage<8, 4>(v);
+  v = bitonic_stage<8, 2>(v);
+  v = bitonic_stage<8, 1>(v);
+  v = bitonic_stage<16, 8>(v);
+  v = bitonic_stage<16, 4>(v);
+  v = bitonic_stage<16, 2>(v);
+  v = bitonic_stage<16, 1>(v);
+  v = bitonic_stage<32, 16>(v);
+  v = bitonic_stage<32, 8>(v);
+  v = bitonic_stage<32, 4>(v);
+  v = bitonic_stage<32, 2>(v);
+  v = bitonic_stage<32, 1>(v);
+  v = bitonic_stage<64, 32>(v);
+  v = bitonic_stage<64, 16>(v);
+  v = bitonic_stage<64, 8>(v);
+  v = bitonic_stage<64, 4>(v);
+  v = bitonic_stage<64, 2>(v);
+  v = bitonic_stage<64, 1>(v);
+  return v;
+}
 
 // Maximum over the wave, returned to every lane.
 __device__ __forceinline__ float wave_max(float v) {
