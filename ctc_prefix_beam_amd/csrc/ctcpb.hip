@@ -7,10 +7,10 @@
 //   select_kernel   frame filter, sec. 3.5 (one block per row, ordered
 //                   ballot compaction instead of a block scan).
 //   decode_kernel   one workgroup per row (offline) or stream, the whole
-//                   frame loop in-kernel (the idea of sec. 3.4.8).  Waves
-//                   1..P ("producers") take the selected frames in turn:
-//     - stream the frame's log-probabilities HBM -> LDS (16-byte
-//       global-to-LDS loads) into a ring of P+1 frame slots;
+//                   frame loop in-kernel (the idea of sec. 3.4.8).  A loader
+//                   wave streams each frame's log-probabilities HBM -> LDS
+//                   (16-byte global-to-LDS loads) into a ring of P+1 frame
+//                   slots; P producer waves take the frames in turn:
 //     - vocabulary top-K (sec. 3.3 step 0, sec. 3.4.7): the best 2W+3
 //       non-blank labels by (log-prob desc, label asc), radix threshold,
 //       ballot gather and count ranking; publish the slot by an LDS flag.
@@ -190,6 +190,14 @@ __device__ __forceinline__ int flag_load(int* f) {
 __device__ __forceinline__ void flag_store(int* f, int v) {
   __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
+// Publishes data that lives only in LDS and is complete in it (the release
+// above would also wait for this wave's outstanding global loads, e.g. a row
+// being prefetched into another slot).  LDS operations of a wave complete in
+// order, so waiting for them and then storing the flag orders the two.
+__device__ __forceinline__ void flag_publish_lds(int* f, int v) {
+  lds_sync();
+  __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
 // Waits until *flag == target (eq) or *flag >= target (!eq); false on abort
 // (abortf == nullptr: not cancelled by the abort flag, still bounded).
@@ -286,8 +294,8 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 // aligned whatever V is; the blank and the padding past V are set to -inf
 // while the frame is ranked and the blank is restored before returning):
 //   1. every lane keeps the two largest group maxima it sees;
-//   2. thr = the K-th largest of those 128 values (radix search with
-//      ballots): at least K groups, hence K labels, reach it;
+//   2. thr = a lower bound (exact to 24 bits of the key) of the K-th largest
+//      of those 128 values: at least K groups, hence K labels, reach it;
 //   3. the groups whose maximum reaches thr are listed;
 //   4. their labels at or above thr are gathered as composite keys;
 //   5. the gathered keys are ranked by counting (broadcast LDS reads).
@@ -301,8 +309,28 @@ __device__ __forceinline__ uint32_t sortable_bits(float f) {
 constexpr int kMaxGroups = 256;   // listed groups (step 3), ints after the keys
 constexpr int kMaxGather = 128;   // gathered keys (step 4)
 
+#ifdef CTCPB_PHASE_PROF
+#define RF_MARK(i)                        \
+  do {                                    \
+    const uint64_t now_ = clock64();      \
+    rprof[i] += now_ - rprof_t;           \
+    rprof_t = now_;                       \
+  } while (0)
+#else
+#define RF_MARK(i) \
+  do {             \
+  } while (0)
+#endif
+
 __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, int prevK,
-                                           int* Rc, float* Rl, int8_t* rank, uint64_t* scr) {
+                                           int* Rc, float* Rl, int8_t* rank, uint64_t* scr
+#ifdef CTCPB_PHASE_PROF
+                                           , uint64_t (&rprof)[8]
+#endif
+) {
+#ifdef CTCPB_PHASE_PROF
+  uint64_t rprof_t = clock64();
+#endif
   const int lane = lane_id();
   const float ninf = -__builtin_inff();
   for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
@@ -313,8 +341,8 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   if (lane < 4 * n4 - V) row[V + lane] = ninf;
   lds_sync();
   const float4* r4 = reinterpret_cast<const float4*>(row);
-  const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
   constexpr int U = 8;  // groups per lane loaded before use
+  RF_MARK(0);
 
   // 1. two largest group maxima per lane
   float hi = ninf, lo = ninf;
@@ -323,73 +351,100 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int g = base + u * kWave + lane;
-      q[u] = g < n4 ? r4[g] : ninf4;
+      q[u] = r4[g < n4 ? g : n4 - 1];   // in bounds; groups past the row are masked below
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      const int g = base + u * kWave + lane;
+      float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      m = g < n4 ? m : ninf;
       lo = __builtin_amdgcn_fmed3f(m, hi, lo);
       hi = fmaxf(hi, m);
     }
   }
-  // 2. threshold (never below -inf)
+  RF_MARK(1);
+  // 2. threshold: the largest value (to 24 bits of its key, two bits per
+  // round) that at least K of the 128 values reach; never below -inf
   const uint32_t a = sortable_bits(hi), b = sortable_bits(lo);
   uint32_t thr = 0u;
-  for (int bit = 31; bit >= 0; bit--) {
-    const uint32_t cand = thr | (1u << bit);
-    const int cnt = __popcll(__ballot(a >= cand)) + __popcll(__ballot(b >= cand));
-    if (cnt >= K) thr = cand;
+  for (int bit = 30; bit >= 8; bit -= 2) {
+    const uint32_t c1 = thr | (1u << bit), c2 = thr | (2u << bit), c3 = thr | (3u << bit);
+    const int n1 = __popcll(__ballot(a >= c1)) + __popcll(__ballot(b >= c1));
+    const int n2 = __popcll(__ballot(a >= c2)) + __popcll(__ballot(b >= c2));
+    const int n3 = __popcll(__ballot(a >= c3)) + __popcll(__ballot(b >= c3));
+    thr = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : thr));
   }
   const uint32_t thr_min = sortable_bits(ninf);
   thr = thr > thr_min ? thr : thr_min;
   const float tf = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
 
-  // 3. groups reaching the threshold
+  RF_MARK(2);
+  // 3. groups reaching the threshold: a bit per group of this lane, then one
+  // wave scan places every lane's list
   int* gid = reinterpret_cast<int*>(scr + kMaxGather);
-  int ng = 0;
-  for (int base = 0; base < n4; base += U * kWave) {
+  uint64_t pm = 0ull;
+  for (int base = 0, u0 = 0; base < n4; base += U * kWave, u0 += U) {
     float4 q[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int g = base + u * kWave + lane;
-      q[u] = g < n4 ? r4[g] : ninf4;
+      q[u] = r4[g < n4 ? g : n4 - 1];
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int g = base + u * kWave + lane;
       const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      const bool pass = g < n4 && m >= tf;
-      const uint64_t mk = __ballot(pass);
-      const int pos = ng + lanes_below(mk);
-      if (pass && pos < kMaxGroups) gid[pos] = g;
-      ng += __popcll(mk);
+      if (g < n4 && m >= tf) pm |= 1ull << (u0 + u);
+    }
+  }
+  int ng;
+  {
+    const int cnt = __popcll(pm);
+    const int incl = wave_incl_scan(cnt);
+    ng = __builtin_amdgcn_readlane(incl, 63);
+    int pos = incl - cnt;
+    while (pm) {
+      const int u = __builtin_ctzll(pm);
+      pm &= pm - 1ull;
+      if (pos < kMaxGroups) gid[pos] = u * kWave + lane;
+      pos++;
     }
   }
   lds_sync();
 
-  // 4. their labels at or above the threshold
+  RF_MARK(3);
+  // 4. their labels at or above the threshold, placed the same way
   int n = 0;
   if (ng <= kMaxGroups) {
     for (int j0 = 0; j0 < ng; j0 += kWave) {
       const int j = j0 + lane;
       const bool in = j < ng;
       const int g = in ? gid[j] : 0;
-      const float4 q = in ? r4[g] : ninf4;
+      const float4 q = r4[g];
       const float xv[4] = {q.x, q.y, q.z, q.w};
+      uint32_t em = 0u;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int c = 4 * g + e;
-        const bool pass = in && c != blank && c < V && xv[e] >= tf;
-        const uint64_t mk = __ballot(pass);
-        const int pos = n + lanes_below(mk);
-        if (pass && pos < kMaxGather)
-          scr[pos] = ((uint64_t)sortable_bits(xv[e]) << 32) | (uint32_t)(~c);
-        n += __popcll(mk);
+        if (in && c != blank && c < V && xv[e] >= tf) em |= 1u << e;
       }
+      const int cnt = __popcll(em);
+      const int incl = wave_incl_scan(cnt);
+      int pos = n + incl - cnt;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if ((em >> e) & 1u) {
+          if (pos < kMaxGather)
+            scr[pos] = ((uint64_t)sortable_bits(xv[e]) << 32) | (uint32_t)(~(4 * g + e));
+          pos++;
+        }
+      }
+      n += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   lds_sync();
 
+  RF_MARK(4);
   if (ng <= kMaxGroups && n >= K && n <= kMaxGather) {
     // 5. rank by counting, two keys per lane
     const int n8 = (n + 7) & ~7;
@@ -444,9 +499,11 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
       if (r < got) rank[c] = (int8_t)r;
     }
   }
+  RF_MARK(5);
   lds_sync();
   if (lane == 0) row[blank] = lpb;
   lds_sync();
+  RF_MARK(6);
 }
 
 // --------------------------------------------------------------- step 0 ----
@@ -1422,8 +1479,9 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
 //   wave 1       the token store, following the beam wave through that ring
 //                (up to kRing steps behind): flat copies or paged forks and
 //                appends, so token traffic is off the recursion's path;
-//   waves 2..    producers: each takes every P-th frame, copies its row into
-//                a free LDS slot and ranks its labels, ahead of the recursion.
+//   wave 2       the loader: copies each frame's row into a free LDS slot;
+//   waves 3..    producers: each takes every P-th frame once its row has
+//                landed and ranks its labels, ahead of the recursion.
 // Every row of log_prob is read once.
 template <bool STREAM>
 __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
@@ -1448,6 +1506,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* abortf = consumed + 1;
   int* wpub = consumed + 2;              // last step whose winners are in the ring
   int* wdone = consumed + 3;             // last step the store wave has written
+  int* loaded = consumed + 4;            // [kMaxSlots]: frame whose row each slot holds
   int2* ring = reinterpret_cast<int2*>(smem + S.ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride); };
@@ -1459,7 +1518,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   // set-up shared by all waves: empty label ranks, flags
   for (int sl = 0; sl < nslot; sl++)
     for (int c = (int)threadIdx.x; c < V; c += (int)blockDim.x) slot_rank(sl)[c] = -1;
-  if (threadIdx.x < kMaxSlots) ready[threadIdx.x] = -1;
+  if (threadIdx.x < kMaxSlots) {
+    ready[threadIdx.x] = -1;
+    loaded[threadIdx.x] = -1;
+  }
   if (threadIdx.x == 0) {
     *consumed = -1;
     *abortf = 0;
@@ -1480,42 +1542,55 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int complete = K == V - 1;
   __syncthreads();
 
-  if (wave >= 2) {
+  if (wave == 2) {
+    // ------------------------------------------------------------ loader
+    // Copies each frame's row into its slot as soon as the slot is free and
+    // flags it once the copy has landed.  It is the only wave that copies
+    // global memory into LDS, so no other wave's LDS reads wait on a copy.
+    for (int f = 0; f < nframes; f++) {
+      const int sl = f % nslot;
+      if (!spin_wait(consumed, f - nslot, false, abortf)) break;
+      row_fetch_async(lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t, slot_row(sl), V, vec4);
+      row_fetch_wait();
+      flag_publish_lds(&loaded[sl], f);
+    }
+    return;
+  }
+
+  if (wave >= 3) {
     // ------------------------------------------------------------ producer
-    const int pid = wave - 2;
+    const int pid = wave - 3;
     uint64_t* scr = reinterpret_cast<uint64_t*>(smem + S.scr + pid * kBuf * 8);
 #ifdef CTCPB_PHASE_PROF
-    uint64_t pw = 0, pf = 0, pr = 0, t0 = clock64();
+    uint64_t pw = 0, pr = 0, t0 = clock64(), t1;
+    uint64_t rprof[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #endif
     for (int f = pid; f < nframes; f += nprod) {
       const int sl = f % nslot;
-      if (!spin_wait(consumed, f - nslot, false, abortf)) break;
-#ifdef CTCPB_PHASE_PROF
-      uint64_t t1 = clock64();
-      pw += t1 - t0;
-#endif
-      float* row = slot_row(sl);
-      row_fetch_async(lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t, row, V, vec4);
-      row_fetch_wait();
-#ifdef CTCPB_PHASE_PROF
-      t0 = clock64();
-      pf += t0 - t1;
-#endif
-      rank_frame(row, V, L.blank, K, f >= nslot ? K : 0, slot_Rc(sl), slot_Rl(sl), slot_rank(sl),
-                 scr);
-      flag_store(&ready[sl], f);
+      if (!spin_wait(&loaded[sl], f, true, abortf)) break;
 #ifdef CTCPB_PHASE_PROF
       t1 = clock64();
-      pr += t1 - t0;
-      t0 = t1;
+      pw += t1 - t0;
+#endif
+      rank_frame(slot_row(sl), V, L.blank, K, f >= nslot ? K : 0, slot_Rc(sl), slot_Rl(sl),
+                 slot_rank(sl), scr
+#ifdef CTCPB_PHASE_PROF
+                 , rprof
+#endif
+      );
+      flag_publish_lds(&ready[sl], f);
+#ifdef CTCPB_PHASE_PROF
+      t0 = clock64();
+      pr += t0 - t1;
 #endif
     }
 #ifdef CTCPB_PHASE_PROF
     if (lane == 0) {
       unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
       atomicAdd(dst + 0, (unsigned long long)pw);
-      atomicAdd(dst + 1, (unsigned long long)pf);
       atomicAdd(dst + 2, (unsigned long long)pr);
+      unsigned long long* rd = reinterpret_cast<unsigned long long*>(hdr + 16);
+      for (int i = 0; i < 8; i++) atomicAdd(rd + i, (unsigned long long)rprof[i]);
     }
 #endif
     return;
@@ -1664,7 +1739,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     st[0] = C.stat_surv;
     st[1] = C.stat_iters;
     st[2] = C.stat_wide;
-    C.hdr[kLastT + 20] = (int)C.stat_multi;   // header word 21 (unused field), diagnostics only
+    C.hdr[15] = (int)C.stat_multi;   // unused header word, diagnostics only
   }
 #endif
   lds_sync();
@@ -1841,7 +1916,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
   // hand-off
-  S.flags = take((kMaxSlots + 4) * 4);
+  S.flags = take((2 * kMaxSlots + 4) * 4);
   S.ring = take(kRing * kMaxBeam * 8);
   S.soffs = take(128 * 4);
   S.nprod = nprod;
@@ -1978,7 +2053,7 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
-  if (int rc = launch(decode_kernel<false>, batch, 64 * (2 + P.S.nprod), P.S.total, st, P,
+  if (int rc = launch(decode_kernel<false>, batch, 64 * (3 + P.S.nprod), P.S.total, st, P,
                       "decode_kernel"))
     return rc;
   return ok();
@@ -2042,7 +2117,7 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
-  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (2 + P.S.nprod), P.S.total,
+  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (3 + P.S.nprod), P.S.total,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
   return ok();
