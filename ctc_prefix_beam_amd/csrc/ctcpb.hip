@@ -107,8 +107,8 @@ struct Beam {
 };
 
 constexpr int kProfBase = 32;   // header word of the first phase counter (beam wave)
-constexpr int kProfSlots = 8;
-constexpr int kProfExtra = 48;  // header word of the producer / store-wave counters
+constexpr int kProfSlots = 12;
+constexpr int kProfExtra = 56;  // header word of the producer / store-wave counters
 
 struct Ctx {
   Layout L;       // copied from the kernel arguments (never address-taken)
@@ -150,8 +150,7 @@ struct Ctx {
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
   uint64_t prof_t;
-  uint64_t stat_surv, stat_iters, stat_wide;   // survivors, gather rounds, wide steps
-  uint64_t stat_multi;                          // steps where a beam has 3+ survivors
+  uint64_t stat_multi;   // steps that needed the general gather
 #endif
 };
 
@@ -555,6 +554,15 @@ struct Winner {
 };
 constexpr int kSeed = 0x7f;
 
+// Candidate id (k, c) as (k << 14) | c: ordered exactly like k * V + c since
+// c < V <= 2^14, and decoded without a division.
+constexpr int kIdShift = 14;
+static_assert(kMaxVocab <= (1 << kIdShift), "labels must fit the id field");
+constexpr int kHtab = 256;   // open-addressing table of new prefixes (>= 8 x beam)
+__device__ __forceinline__ uint32_t cand_id(int k, int c) {
+  return ((uint32_t)k << kIdShift) | (uint32_t)c;
+}
+
 // Step 0 (sec. 3.3): each seeded slot holds its one label, written fresh.
 __device__ __forceinline__ void store_seed(const Ctx& C, const Winner& w) {
   const Layout& L = C.L;
@@ -609,9 +617,18 @@ __device__ __forceinline__ void store_seed(const Ctx& C, const Winner& w) {
 // the step is regenerated from the per-beam values left in LDS and streamed
 // through stream_topk.  Used when the pruned candidate set cannot be proven
 // to contain the top W.
-__device__ __forceinline__ int full_select(const Ctx& C, const float* row) {
+__device__ __forceinline__ int full_select(const Ctx& C, const float* row, int par, int last) {
   const Layout& L = C.L;
   const int W = L.W, V = L.V, blank = L.blank;
+  const int lane = lane_id();
+  // labels merged away from each beam: the last label of each of its children
+  if (lane < W) C.nchild[lane] = 0;
+  lds_sync();
+  if (par >= 0) {
+    const int pos = atomicAdd(&C.nchild[par], 1);
+    C.childc[par * kMaxBeam + pos] = last;
+  }
+  lds_sync();
   auto gen = [&](int64_t i) -> uint64_t {
     const int k = (int)(i / V);
     const int c = (int)(i - (int64_t)k * V);
@@ -628,7 +645,7 @@ __device__ __forceinline__ int full_select(const Ctx& C, const float* row) {
         if (C.childc[k * kMaxBeam + j] == c) return 0ull;
       key = row[c] + A;
     }
-    return key > kNeg ? compose(key, (uint32_t)i) : 0ull;
+    return key > kNeg ? compose(key, cand_id(k, c)) : 0ull;
   };
   return stream_topk(C, W, (int64_t)W * V, gen);
 }
@@ -640,26 +657,44 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int W = L.W, V = L.V, blank = L.blank;
   const bool lv = lane < W && b.live;
 
-  // collapsed-blank correction for skipped frames (sec. 3.4), then A_k
-  float pb1 = b.pb, pnb1 = b.pnb;
-  if (lv && g) {
-    pb1 = lse(b.pb, b.pnb);
-    pnb1 = kNeg;
-  }
-  const float A = lv ? lse(pb1, pnb1) : kNeg;
   const int last = b.last;
+  // merge (sec. 3.4.3): beam j = parent i + `last`; i's extension by `last`
+  // is folded into j's blank slot.  The parent's state is exchanged first so
+  // that the exchange overlaps the arithmetic below.
+  const int par = lv ? b.parent : -1;
+  const int src = par >= 0 ? par : lane;
+  const float pb_par = __shfl(b.pb, src, 64);
+  const float pnb_par = __shfl(b.pnb, src, 64);
+  const int last_par = __shfl(last, src, 64);
   const float lpc = (lv && last != blank) ? row[last] : kNeg;
   const float lpb = row[blank];
+  // labels removed from a beam's ordinary list: its own last label (that is
+  // the repeated-label slot) and the last label of each child (merged away).
+  // The masks were cleared at the end of the previous step.
+  const int rr_own = (lv && last != blank) ? (int)C.rank[last] : -1;
+  if (par >= 0 && last == last_par) C.exclast[par] = 1;
+  if (par >= 0 && last != last_par && rr_own >= 0)
+    atomicOr(&C.exm[par * 3 + (rr_own >> 5)], 1u << (rr_own & 31));
+  if (rr_own >= 0) atomicOr(&C.exm[lane * 3 + (rr_own >> 5)], 1u << (rr_own & 31));
+
+  // collapsed-blank correction for skipped frames (sec. 3.4), then A_k; the
+  // parent's A is recomputed here from its state (same operations, same bits)
+  float pb1 = b.pb, pnb1 = b.pnb, pb1_par = pb_par, pnb1_par = pnb_par;
+  if (g) {
+    if (lv) {
+      pb1 = lse(b.pb, b.pnb);
+      pnb1 = kNeg;
+    }
+    if (par >= 0) {
+      pb1_par = lse(pb_par, pnb_par);
+      pnb1_par = kNeg;
+    }
+  }
+  const float A = lv ? lse(pb1, pnb1) : kNeg;
+  const float A_par = par >= 0 ? lse(pb1_par, pnb1_par) : kNeg;
   // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
   const float ptb = lv ? lpb + A : kNeg;
   float ptnb = (lv && !g && last != blank) ? lpc + pnb1 : kNeg;
-  // merge (sec. 3.4.3): beam j = parent i + `last`; i's extension by `last`
-  // is folded into j's blank slot
-  const int par = lv ? b.parent : -1;
-  const int src = par >= 0 ? par : lane;
-  const float A_par = __shfl(A, src, 64);
-  const float pb1_par = __shfl(pb1, src, 64);
-  const int last_par = __shfl(last, src, 64);
   if (par >= 0) {
     const float from_parent = (last == last_par) ? lpc + pb1_par : lpc + A_par;
     ptnb = lse(ptnb, from_parent);
@@ -667,30 +702,6 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float keyb = lv ? lse(ptb, ptnb) : kNeg;
 
   PROF_MARK(1);
-  // labels removed from a beam's ordinary list: its own last label (that is
-  // the repeated-label slot) and the last label of each child (merged away)
-  if (lane < W) {
-    C.exm[lane * 3 + 0] = 0u;
-    C.exm[lane * 3 + 1] = 0u;
-    C.exm[lane * 3 + 2] = 0u;
-    C.exclast[lane] = 0;
-    C.nchild[lane] = 0;
-  }
-  lds_sync();
-  if (par >= 0) {
-    if (last == last_par) {
-      C.exclast[par] = 1;
-    } else {
-      const int rr = C.rank[last];
-      if (rr >= 0) atomicOr(&C.exm[par * 3 + (rr >> 5)], 1u << (rr & 31));
-    }
-    const int pos = atomicAdd(&C.nchild[par], 1);
-    C.childc[par * kMaxBeam + pos] = last;
-  }
-  if (lv && last != blank) {
-    const int rr = C.rank[last];
-    if (rr >= 0) atomicOr(&C.exm[lane * 3 + (rr >> 5)], 1u << (rr & 31));
-  }
   lds_sync();
   const bool rep_ok = lv && last != blank && C.exclast[lane] == 0;
   const float keyc = rep_ok ? lpc + pb1 : kNeg;
@@ -732,13 +743,14 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     else if (r < 64) b &= b - 1u;
     else c &= c - 1u;
   };
+  PROF_MARK(8);
   uint32_t g0 = fr0, g1 = fr1, g2 = fr2;
   const int r0 = first_bit(g0, g1, g2);
   drop_bit(r0, g0, g1, g2);
   const int r1 = first_bit(g0, g1, g2);
   drop_bit(r1, g0, g1, g2);
   const int r2 = first_bit(g0, g1, g2);
-  const uint32_t idb = (uint32_t)(lane * V);
+  const uint32_t idb = cand_id(lane, 0);
   auto ordinary = [&](int r) -> uint64_t {
     if (!lv || r < 0) return 0ull;
     const float key = C.Rl[r] + A;
@@ -754,6 +766,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // the beam's third candidate (its lists are sorted, so all later ones are
   // below it); ranked labels past the list are bounded separately below
   const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
+  PROF_MARK(9);
+  PROF_MARK(10);
   // lane j < 32 holds beam j's best, lane 32 + j its second best
   const uint64_t t2x = xor_lane_u64<32>(t2);
   const uint64_t top = wave_sort64_desc<uint64_t>(lane < kMaxBeam ? t1 : t2x);
@@ -780,13 +794,12 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
         if (pass && pos < kBuf) C.buf[pos] = key;
         nsurv += __popcll(m);
       };
-      put(lv && keyb > kNeg && keyb >= tau0, compose(keyb, (uint32_t)(lane * V + blank)));
-      put(lv && keyc > kNeg && keyc >= tau0, compose(keyc, (uint32_t)(lane * V + last)));
+      put(lv && keyb > kNeg && keyb >= tau0, compose(keyb, cand_id(lane, blank)));
+      put(lv && keyc > kNeg && keyc >= tau0, compose(keyc, cand_id(lane, last)));
       bool more = lv;
       for (int r = 0; r < nPool; r += 4) {
         if (!__ballot(more)) break;
 #ifdef CTCPB_PHASE_PROF
-        C.stat_iters++;
 #endif
         const float4 q = *reinterpret_cast<const float4*>(C.Rl + r);
         const int4 cq = *reinterpret_cast<const int4*>(C.Rc + r);
@@ -801,7 +814,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
           any = any || above;
           const uint32_t open =
               rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
-          put(above && (open & 1u), compose(key, (uint32_t)(lane * V + cv[j])));
+          put(above && (open & 1u), compose(key, cand_id(lane, cv[j])));
         }
         more = more && any;
       }
@@ -809,9 +822,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     lds_sync();
     PROF_MARK(4);
 #ifdef CTCPB_PHASE_PROF
-    C.stat_surv += nsurv;
     C.stat_multi += 1;
-    C.stat_wide += nsurv > kWave ? 1 : 0;
 #endif
     if (nsurv <= kWave) {
       // one survivor per lane, sorted in registers
@@ -838,7 +849,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
           const int j = q - M, kk = j >> 1;
           const float key = (j & 1) ? C.kc[kk] : C.kb[kk];
           const int c = (j & 1) ? C.lastk[kk] : blank;
-          return (key > kNeg && key >= tau0) ? compose(key, (uint32_t)(kk * V + c)) : 0ull;
+          return (key > kNeg && key >= tau0) ? compose(key, cand_id(kk, c)) : 0ull;
         }
         int a = 0, z = W - 1;
         while (a < z) {
@@ -848,7 +859,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
         }
         const int rho = q - C.offs[a];
         const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
-        return ex ? 0ull : compose(C.Rl[rho] + C.A[a], (uint32_t)(a * V + C.Rc[rho]));
+        return ex ? 0ull : compose(C.Rl[rho] + C.A[a], cand_id(a, C.Rc[rho]));
       };
       stream_topk(C, W, ncand, candidate);
       if (lane == 0) C.scal[kScalWide] += 1;
@@ -866,7 +877,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     need_full = __ballot(bad) != 0ull;
   }
   if (need_full) {
-    full_select(C, row);
+    full_select(C, row, par, last);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
     wc = lane < W ? C.buf[lane] : 0ull;
   }
@@ -876,8 +887,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   Winner w;
   w.valid = lane < W && wc > comp_floor();
   const uint32_t id = comp_id(wc);
-  w.k = w.valid ? (int)(id / (uint32_t)V) : lane;
-  w.c = w.valid ? (int)(id - (uint32_t)w.k * (uint32_t)V) : blank;
+  w.k = w.valid ? (int)(id >> kIdShift) : lane;
+  w.c = w.valid ? (int)(id & ((1u << kIdShift) - 1u)) : blank;
   const float key = comp_key(wc);
   const int k = w.k & 63;
   const float ptb_k = __shfl(ptb, k, 64);
@@ -912,39 +923,41 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     nb.pnb = key;
   }
 
-  // parent slots of the new beams (the prefix one label shorter, if live)
-  if (lane < W) C.bslot[lane] = -1;
-  C.htab[lane] = -1;
-  lds_sync();
+  // parent slots of the new beams (the prefix one label shorter, if live).
+  // bslot and htab were cleared at the end of the previous step.  The hash
+  // table is only needed when some stay winner's parent prefix was not live
+  // (it may just have been re-created by extending its own parent).
+  const bool need_look = w.valid && !ext && par_k < 0 && len_k >= 2;
+  const bool any_look = __ballot(need_look) != 0ull;
   if (w.valid && w.c == blank) C.bslot[w.k] = lane;
-  if (lane < W) {
-    C.newh[lane] = nb.h;
-    C.newlen[lane] = nb.len;
-  }
-  lds_sync();
-  if (ext) {
-    int s = (int)((uint32_t)nb.h & 63u);
-    while (atomicCAS(&C.htab[s], -1, lane) != -1) s = (s + 1) & 63;
+  int hslot = -1;
+  if (any_look) {
+    if (lane < W) {
+      C.newh[lane] = nb.h;
+      C.newlen[lane] = nb.len;
+    }
+    if (ext) {
+      int s = (int)((uint32_t)nb.h & (kHtab - 1));
+      while (atomicCAS(&C.htab[s], -1, lane) != -1) s = (s + 1) & (kHtab - 1);
+      hslot = s;
+    }
   }
   lds_sync();
   int npar = -1, cand = -1;
   if (ext) {
     npar = C.bslot[w.k];
-  } else if (w.valid) {
-    if (par_k >= 0) {
-      npar = C.bslot[par_k];
-    } else if (len_k >= 2) {
-      // the parent prefix may have just been re-created from its own parent
-      int s = (int)((uint32_t)hp_k & 63u);
-      for (int probe = 0; probe < 64; probe++) {
-        const int e = C.htab[s];
-        if (e < 0) break;
-        if (C.newh[e] == hp_k && C.newlen[e] == len_k - 1) {
-          cand = e;
-          break;
-        }
-        s = (s + 1) & 63;
+  } else if (w.valid && par_k >= 0) {
+    npar = C.bslot[par_k];
+  } else if (need_look) {
+    int s = (int)((uint32_t)hp_k & (kHtab - 1));
+    for (int probe = 0; probe < kHtab; probe++) {
+      const int e = C.htab[s];
+      if (e < 0) break;
+      if (C.newh[e] == hp_k && C.newlen[e] == len_k - 1) {
+        cand = e;
+        break;
       }
+      s = (s + 1) & (kHtab - 1);
     }
   }
   const int ce = cand >= 0 ? cand : lane;
@@ -973,6 +986,17 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
   nb.parent = npar;
   if (lane < W) b = nb;
+  // clear the exclusion masks, parent slots and hash entries for the next
+  // step (LDS operations of this wave complete in order, after every read of
+  // them above)
+  if (lane < kMaxBeam) {
+    C.exm[lane * 3 + 0] = 0u;
+    C.exm[lane * 3 + 1] = 0u;
+    C.exm[lane * 3 + 2] = 0u;
+    C.exclast[lane] = 0;
+    C.bslot[lane] = -1;
+  }
+  if (hslot >= 0) C.htab[hslot] = -1;
   PROF_MARK(6);
   return w;
 }
@@ -1472,16 +1496,16 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
 }
 
 // Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).  One
-// workgroup per row, three roles:
+// workgroup per row, four roles:
 //   wave 0       the serial beam recursion, frame by frame; it publishes each
 //                step's winners (source slot, label, source length) into a
 //                ring of kRing entries;
-//   wave 1       the token store, following the beam wave through that ring
+//   store wave   the token store, following the beam wave through that ring
 //                (up to kRing steps behind): flat copies or paged forks and
 //                appends, so token traffic is off the recursion's path;
-//   wave 2       the loader: copies each frame's row into a free LDS slot;
-//   waves 3..    producers: each takes every P-th frame once its row has
-//                landed and ranks its labels, ahead of the recursion.
+//   loader       copies each frame's row into a free LDS slot;
+//   producers    each takes every P-th frame once its row has landed and
+//                ranks its labels, ahead of the recursion.
 // Every row of log_prob is read once.
 template <bool STREAM>
 __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
@@ -1507,6 +1531,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* wpub = consumed + 2;              // last step whose winners are in the ring
   int* wdone = consumed + 3;             // last step the store wave has written
   int* loaded = consumed + 4;            // [kMaxSlots]: frame whose row each slot holds
+  int* frame_t = loaded + kMaxSlots;     // [kMaxSlots]: time index of that frame
   int2* ring = reinterpret_cast<int2*>(smem + S.ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride); };
@@ -1542,7 +1567,14 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int complete = K == V - 1;
   __syncthreads();
 
-  if (wave == 2) {
+  // wave roles: 0 beam; with 5 or more waves the light loader shares SIMD 0
+  // with the beam wave (waves are spread over the 4 SIMDs in order)
+  const int nwaves = 3 + nprod;
+  const int store_wave = nwaves >= 5 ? 3 : 2;
+  const int loader_wave = nwaves >= 5 ? 4 : 3;
+  const int pid = wave == 1 ? 0 : (wave == 2 && nwaves >= 5 ? 1 : wave - 3);
+
+  if (wave == loader_wave) {
     // ------------------------------------------------------------ loader
     // Copies each frame's row into its slot as soon as the slot is free and
     // flags it once the copy has landed.  It is the only wave that copies
@@ -1550,16 +1582,17 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     for (int f = 0; f < nframes; f++) {
       const int sl = f % nslot;
       if (!spin_wait(consumed, f - nslot, false, abortf)) break;
-      row_fetch_async(lp_row + (int64_t)(STREAM ? f : sel[f]) * stride_t, slot_row(sl), V, vec4);
+      const int t = STREAM ? step_in + f : sel[f];
+      row_fetch_async(lp_row + (int64_t)(STREAM ? f : t) * stride_t, slot_row(sl), V, vec4);
+      if (lane == 0) frame_t[sl] = t;
       row_fetch_wait();
       flag_publish_lds(&loaded[sl], f);
     }
     return;
   }
 
-  if (wave >= 3) {
+  if (wave != 0 && wave != store_wave) {
     // ------------------------------------------------------------ producer
-    const int pid = wave - 3;
     uint64_t* scr = reinterpret_cast<uint64_t*>(smem + S.scr + pid * kBuf * 8);
 #ifdef CTCPB_PHASE_PROF
     uint64_t pw = 0, pr = 0, t0 = clock64(), t1;
@@ -1588,7 +1621,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     if (lane == 0) {
       unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
       atomicAdd(dst + 0, (unsigned long long)pw);
-      atomicAdd(dst + 2, (unsigned long long)pr);
+      atomicAdd(dst + 1, (unsigned long long)pr);
       unsigned long long* rd = reinterpret_cast<unsigned long long*>(hdr + 16);
       for (int i = 0; i < 8; i++) atomicAdd(rd + i, (unsigned long long)rprof[i]);
     }
@@ -1601,7 +1634,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   C.wdone = wdone;
   C.abortf = abortf;
 
-  if (wave == 1) {
+  if (wave == store_wave) {
     // ---------------------------------------------------------- store wave
     C.offs = reinterpret_cast<int*>(smem + S.soffs);
     for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
@@ -1646,8 +1679,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
 #ifdef CTCPB_PHASE_PROF
     if (lane == 0) {
       unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
-      atomicAdd(dst + 3, (unsigned long long)sw);
-      atomicAdd(dst + 4, (unsigned long long)sk);
+      atomicAdd(dst + 2, (unsigned long long)sw);
+      atomicAdd(dst + 3, (unsigned long long)sk);
     }
 #endif
     return;
@@ -1678,28 +1711,39 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
   }
+  if (lane < kMaxBeam) {
+    C.exm[lane * 3 + 0] = 0u;
+    C.exm[lane * 3 + 1] = 0u;
+    C.exm[lane * 3 + 2] = 0u;
+    C.exclast[lane] = 0;
+    C.bslot[lane] = -1;
+  }
+  for (int i = lane; i < kHtab; i += kWave) C.htab[i] = -1;
   lds_sync();
 
   bool aborted = false;
+  int next_ready = -2;          // value of the next slot's flag, read one step early
+  int wdone_seen = step - 1;    // store-wave progress last observed
   for (int f = 0; f < nframes; f++) {
     const int sl = f % nslot;
 #ifdef CTCPB_PHASE_PROF
     if (f == 0) {
       for (int i = 0; i < kProfSlots; i++) C.prof[i] = 0;
-      C.stat_surv = C.stat_iters = C.stat_wide = C.stat_multi = 0;
+      C.stat_multi = 0;
       C.prof_t = clock64();
     }
 #endif
-    if (!spin_wait(&ready[sl], f, true, abortf)) {
+    if (next_ready != f && !spin_wait(&ready[sl], f, true, abortf)) {
       aborted = true;
       break;
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     PROF_MARK(0);
     const float* row = slot_row(sl);
     C.Rc = slot_Rc(sl);
     C.Rl = slot_Rl(sl);
     C.rank = slot_rank(sl);
-    const int t = STREAM ? step_in + f : sel[f];
+    const int t = frame_t[sl];
     Winner w;
     if (step == 0) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
@@ -1713,18 +1757,28 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       w = beam_step(C, b, row, g, step, K, complete);
     }
     // hand the winners to the store wave (its ring entry must be free)
-    if (!spin_wait(wdone, step - kRing, false, abortf)) {
-      aborted = true;
-      break;
+    if (wdone_seen < step - kRing) {
+      if (!spin_wait(wdone, step - kRing, false, abortf)) {
+        aborted = true;
+        break;
+      }
+      wdone_seen = flag_load(wdone);
     }
+    // peek at the next frame's flag now: the read completes with the LDS
+    // wait below instead of on its own at the top of the next step (LDS
+    // operations of a wave complete in order, so a flag seen set here was
+    // written after the slot's data)
+    next_ready = __hip_atomic_load(&ready[(f + 1) % nslot], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
     if (lane < W)
       ring[(f % kRing) * kMaxBeam + lane] =
           make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
     last_t = t;
-    lds_sync();
-    flag_store(consumed, f);
-    flag_store(wpub, step);
+    // the ring entry and this step's reads of the slot are LDS operations:
+    // complete them, then release the slot and publish the winners
+    flag_publish_lds(consumed, f);
+    __hip_atomic_store(wpub, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     step++;
   }
   // every published step stored (bounded wait that the abort flag does not cut
@@ -1735,10 +1789,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
     for (int i = 0; i < kProfSlots; i++) dst[i] = C.prof[i];
-    uint64_t* st = reinterpret_cast<uint64_t*>(C.hdr + kProfExtra) + 5;
-    st[0] = C.stat_surv;
-    st[1] = C.stat_iters;
-    st[2] = C.stat_wide;
     C.hdr[15] = (int)C.stat_multi;   // unused header word, diagnostics only
   }
 #endif
@@ -1900,7 +1950,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.exm = take(kMaxBeam * 3 * 4);
   S.exclast = take(kMaxBeam * 4);
   S.bslot = take(kMaxBeam * 4);
-  S.htab = take(64 * 4);
+  S.htab = take(kHtab * 4);
   S.newh = take(kMaxBeam * 8);
   S.newlen = take(kMaxBeam * 4);
   S.nchild = take(kMaxBeam * 4);
@@ -1916,7 +1966,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
   // hand-off
-  S.flags = take((2 * kMaxSlots + 4) * 4);
+  S.flags = take((3 * kMaxSlots + 4) * 4);
   S.ring = take(kRing * kMaxBeam * 8);
   S.soffs = take(128 * 4);
   S.nprod = nprod;

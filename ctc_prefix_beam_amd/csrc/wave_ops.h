@@ -59,12 +59,14 @@ template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   const int x = (int)v;
   if constexpr (J == 1) {
-    return (uint32_t)dpp_mov<kDppXor1>(x, x);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, kDppXor1, 0xf, 0xf, true);
   } else if constexpr (J == 2) {
-    return (uint32_t)dpp_mov<kDppXor2>(x, x);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, kDppXor2, 0xf, 0xf, true);
   } else if constexpr (J == 4 || J == 8) {
-    const int dn = dpp_mov<dpp_row_shr(J)>(x, x);  // lane i <- lane i - J
-    const int up = dpp_mov<dpp_row_shl(J)>(x, x);  // lane i <- lane i + J
+    // lanes a shift leaves without a source read 0; the select below never
+    // uses them
+    const int dn = __builtin_amdgcn_mov_dpp(x, dpp_row_shr(J), 0xf, 0xf, true);  // i <- i - J
+    const int up = __builtin_amdgcn_mov_dpp(x, dpp_row_shl(J), 0xf, 0xf, true);  // i <- i + J
     return (uint32_t)((lane_id() & J) ? dn : up);
   } else if constexpr (J == 16) {
     const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
