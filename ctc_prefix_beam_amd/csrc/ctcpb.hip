@@ -674,8 +674,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int rr_own = (lv && last != blank) ? (int)C.rank[last] : -1;
   if (par >= 0 && last == last_par) C.exclast[par] = 1;
   if (par >= 0 && last != last_par && rr_own >= 0)
-    atomicOr(&C.exm[par * 3 + (rr_own >> 5)], 1u << (rr_own & 31));
-  if (rr_own >= 0) atomicOr(&C.exm[lane * 3 + (rr_own >> 5)], 1u << (rr_own & 31));
+    atomicOr(&C.exm[par * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
+  if (rr_own >= 0) atomicOr(&C.exm[lane * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
 
   // collapsed-blank correction for skipped frames (sec. 3.4), then A_k; the
   // parent's A is recomputed here from its state (same operations, same bits)
@@ -721,42 +721,50 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int nPool = complete ? nR : nR - 1;
   uint32_t fr0, fr1, fr2;  // in-pool ranks still open to this beam
   {
-    uint32_t m[3];
+    const uint4 ex = reinterpret_cast<const uint4*>(C.exm)[lane & (kMaxBeam - 1)];
+    const uint32_t m[3] = {ex.x, ex.y, ex.z};
+    uint32_t o[3];
 #pragma unroll
     for (int w = 0; w < 3; w++) {
-      uint32_t x = lv ? ~C.exm[lane * 3 + w] : 0u;
       const int lo = w * 32;
-      if (lo >= nPool) x = 0u;
-      else if (nPool - lo < 32) x &= (1u << (nPool - lo)) - 1u;
-      m[w] = x;
+      const uint32_t in_pool =
+          lo >= nPool ? 0u : (nPool - lo >= 32 ? 0xffffffffu : (1u << (nPool - lo)) - 1u);
+      o[w] = lv ? (~m[w] & in_pool) : 0u;
     }
-    fr0 = m[0];
-    fr1 = m[1];
-    fr2 = m[2];
+    fr0 = o[0];
+    fr1 = o[1];
+    fr2 = o[2];
   }
-  auto first_bit = [](uint32_t a, uint32_t b, uint32_t c) -> int {
-    return a ? __builtin_ctz(a) : (b ? 32 + __builtin_ctz(b) : (c ? 64 + __builtin_ctz(c) : -1));
-  };
-  auto drop_bit = [](int r, uint32_t& a, uint32_t& b, uint32_t& c) {
-    if (r < 0) return;
-    if (r < 32) a &= a - 1u;
-    else if (r < 64) b &= b - 1u;
-    else c &= c - 1u;
-  };
   PROF_MARK(8);
-  uint32_t g0 = fr0, g1 = fr1, g2 = fr2;
-  const int r0 = first_bit(g0, g1, g2);
-  drop_bit(r0, g0, g1, g2);
-  const int r1 = first_bit(g0, g1, g2);
-  drop_bit(r1, g0, g1, g2);
-  const int r2 = first_bit(g0, g1, g2);
+  // the first three open ranks, without branches (-1: none)
+  uint64_t g01 = (uint64_t)fr0 | ((uint64_t)fr1 << 32);
+  uint32_t g2 = fr2;
+  int rr[3];
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    const int a = __ffsll((long long)g01) - 1;
+    const int c = __ffs((int)g2) - 1;
+    rr[i] = a >= 0 ? a : (c >= 0 ? 64 + c : -1);
+    g2 = a >= 0 ? g2 : (g2 & (g2 - 1u));
+    g01 &= g01 - 1ull;
+  }
+  // their lists entries, all loads issued together (index 0 stands in for none)
   const uint32_t idb = cand_id(lane, 0);
-  auto ordinary = [&](int r) -> uint64_t {
-    if (!lv || r < 0) return 0ull;
-    const float key = C.Rl[r] + A;
-    return key > kNeg ? compose(key, idb + (uint32_t)C.Rc[r]) : 0ull;
-  };
-  const uint64_t o1 = ordinary(r0), o2 = ordinary(r1), o3 = ordinary(r2);
+  float rl[3];
+  int rc[3];
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    const int r = rr[i] >= 0 ? rr[i] : 0;
+    rl[i] = C.Rl[r];
+    rc[i] = C.Rc[r];
+  }
+  uint64_t oc[3];
+#pragma unroll
+  for (int i = 0; i < 3; i++) {
+    const float key = rl[i] + A;
+    oc[i] = (lv && rr[i] >= 0 && key > kNeg) ? compose(key, idb + (uint32_t)rc[i]) : 0ull;
+  }
+  const uint64_t o1 = oc[0], o2 = oc[1], o3 = oc[2];
   const uint64_t cb = (lv && keyb > kNeg) ? compose(keyb, idb + (uint32_t)blank) : 0ull;
   const uint64_t cc = (lv && keyc > kNeg) ? compose(keyc, idb + (uint32_t)last) : 0ull;
   const uint64_t shi = cb > cc ? cb : cc, slo = cb > cc ? cc : cb;
@@ -858,7 +866,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
           else z = mid - 1;
         }
         const int rho = q - C.offs[a];
-        const uint32_t ex = (C.exm[a * 3 + (rho >> 5)] >> (rho & 31)) & 1u;
+        const uint32_t ex = (C.exm[a * 4 + (rho >> 5)] >> (rho & 31)) & 1u;
         return ex ? 0ull : compose(C.Rl[rho] + C.A[a], cand_id(a, C.Rc[rho]));
       };
       stream_topk(C, W, ncand, candidate);
@@ -990,9 +998,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // step (LDS operations of this wave complete in order, after every read of
   // them above)
   if (lane < kMaxBeam) {
-    C.exm[lane * 3 + 0] = 0u;
-    C.exm[lane * 3 + 1] = 0u;
-    C.exm[lane * 3 + 2] = 0u;
+    reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
     C.exclast[lane] = 0;
     C.bslot[lane] = -1;
   }
@@ -1712,9 +1718,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     }
   }
   if (lane < kMaxBeam) {
-    C.exm[lane * 3 + 0] = 0u;
-    C.exm[lane * 3 + 1] = 0u;
-    C.exm[lane * 3 + 2] = 0u;
+    reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
     C.exclast[lane] = 0;
     C.bslot[lane] = -1;
   }
@@ -1947,7 +1951,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.kc = take(kMaxBeam * 4);
   S.lastk = take(kMaxBeam * 4);
   S.offs = take(128 * 4);
-  S.exm = take(kMaxBeam * 3 * 4);
+  S.exm = take(kMaxBeam * 4 * 4);   // 4 words per beam: ranks 0..95 (+ padding)
   S.exclast = take(kMaxBeam * 4);
   S.bslot = take(kMaxBeam * 4);
   S.htab = take(kHtab * 4);
