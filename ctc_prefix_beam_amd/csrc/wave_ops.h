@@ -95,7 +95,12 @@ __device__ __forceinline__ T bitonic_stage(T v) {
   else p = xor_lane<J>(v);
   const int lane = lane_id();
   const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
-  return (keep_max == (v > p)) ? v : p;
+  // lanes that keep the smaller key compare complemented keys (complement
+  // reverses the order), so every lane takes a maximum: the compare result
+  // feeds the selects directly, with no lane-mask combination in between
+  const T flip = keep_max ? (T)0 : ~(T)0;
+  const T a = v ^ flip, b = p ^ flip;
+  return (a > b ? a : b) ^ flip;
 }
 
 // Sorts one 32- or 64-bit unsigned key per lane into descending lane order.
