@@ -102,6 +102,7 @@ enum : int {
 struct Beam {
   int live;
   float pb, pnb, score;
+  float A;        // logsumexp(pb, pnb) (NEG if dead), kept with the state
   int len, last, parent, last2;
   uint64_t h, hp;
 };
@@ -543,6 +544,7 @@ __device__ __forceinline__ void first_step(const Ctx& C, Beam& b, const float* r
     b.pb = row[blank];
     b.score = row[blank];
   }
+  b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
 }
 
 // ------------------------------------------------------------ token stores --
@@ -664,7 +666,6 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int par = lv ? b.parent : -1;
   const int src = par >= 0 ? par : lane;
   const float pb_par = __shfl(b.pb, src, 64);
-  const float pnb_par = __shfl(b.pnb, src, 64);
   const int last_par = __shfl(last, src, 64);
   const float lpc = (lv && last != blank) ? row[last] : kNeg;
   const float lpb = row[blank];
@@ -677,21 +678,13 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     atomicOr(&C.exm[par * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
   if (rr_own >= 0) atomicOr(&C.exm[lane * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
 
-  // collapsed-blank correction for skipped frames (sec. 3.4), then A_k; the
-  // parent's A is recomputed here from its state (same operations, same bits)
-  float pb1 = b.pb, pnb1 = b.pnb, pb1_par = pb_par, pnb1_par = pnb_par;
-  if (g) {
-    if (lv) {
-      pb1 = lse(b.pb, b.pnb);
-      pnb1 = kNeg;
-    }
-    if (par >= 0) {
-      pb1_par = lse(pb_par, pnb_par);
-      pnb1_par = kNeg;
-    }
-  }
-  const float A = lv ? lse(pb1, pnb1) : kNeg;
-  const float A_par = par >= 0 ? lse(pb1_par, pnb1_par) : kNeg;
+  // A_k = logsumexp(pb, pnb) was computed with the state.  The collapse for
+  // skipped frames (sec. 3.4) turns (pb, pnb) into (A_k, NEG), and since
+  // logsumexp(x, NEG) == x exactly, A_k is the same either way.
+  const float A = lv ? b.A : kNeg;
+  const float A_par = __shfl(b.A, src, 64);
+  const float pb1 = g ? A : b.pb, pnb1 = g ? kNeg : b.pnb;
+  const float pb1_par = g ? A_par : pb_par;
   // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
   const float ptb = lv ? lpb + A : kNeg;
   float ptnb = (lv && !g && last != blank) ? lpc + pnb1 : kNeg;
@@ -765,6 +758,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     oc[i] = (lv && rr[i] >= 0 && key > kNeg) ? compose(key, idb + (uint32_t)rc[i]) : 0ull;
   }
   const uint64_t o1 = oc[0], o2 = oc[1], o3 = oc[2];
+  const float bound = C.Rl[nR - 1];   // no label outside the ranked list scores above A + bound
   const uint64_t cb = (lv && keyb > kNeg) ? compose(keyb, idb + (uint32_t)blank) : 0ull;
   const uint64_t cc = (lv && keyc > kNeg) ? compose(keyc, idb + (uint32_t)last) : 0ull;
   const uint64_t shi = cb > cc ? cb : cc, slo = cb > cc ? cc : cb;
@@ -878,9 +872,10 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   if (!complete) {
     // labels outside the ranked list score at most A_k + (last ranked lp);
     // they must stay strictly below the W-th selected key
-    const uint64_t wl = shfl_u64(wc, W - 1);
+    const uint64_t wl =
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(wc >> 32), W - 1) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wc, W - 1);
     const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
-    const float bound = C.Rl[nR - 1];
     const bool bad = lv && !((bound + A) < keyW);
     need_full = __ballot(bad) != 0ull;
   }
@@ -950,6 +945,9 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
       hslot = s;
     }
   }
+  // the next step's A of every new beam, computed while the table writes
+  // above are in flight
+  nb.A = w.valid ? lse(nb.pb, nb.pnb) : kNeg;
   lds_sync();
   int npar = -1, cand = -1;
   if (ext) {
@@ -1292,6 +1290,7 @@ __device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
     b.live = reinterpret_cast<const int*>(a + BeamArrays::live)[lane];
     b.h = reinterpret_cast<const uint64_t*>(a + BeamArrays::hash)[lane];
     b.hp = reinterpret_cast<const uint64_t*>(a + BeamArrays::phash)[lane];
+    b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
   } else {
     b.live = 0;
     b.pb = b.pnb = b.score = kNeg;
@@ -1300,6 +1299,7 @@ __device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
     b.parent = b.last2 = -1;
     b.h = kHashEmpty;
     b.hp = 0;
+    b.A = kNeg;
   }
 }
 
@@ -1327,6 +1327,7 @@ __device__ __forceinline__ void beam_fresh(Beam& b, int blank) {
   b.pb = lane == 0 ? 0.0f : kNeg;
   b.pnb = kNeg;
   b.score = lane == 0 ? 0.0f : kNeg;
+  b.A = lane == 0 ? 0.0f : kNeg;   // logsumexp(0, NEG)
   b.len = 0;
   b.last = blank;
   b.parent = -1;
