@@ -770,9 +770,22 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
   PROF_MARK(9);
   PROF_MARK(10);
-  // lane j < 32 holds beam j's best, lane 32 + j its second best
-  const uint64_t t2x = xor_lane_u64<32>(t2);
-  const uint64_t top = wave_sort64_desc<uint64_t>(lane < kMaxBeam ? t1 : t2x);
+  // beam j's best goes to lane j, its second best to lane j + 2^ceil(log2 W)
+  // (one lane swap); the sorting network covers those first 16, 32 or 64
+  // lanes only
+  // (lane exchanges run on every lane, outside any lane-dependent branch:
+  // a lane that is switched off supplies no value to the exchange)
+  uint64_t top;
+  if (W <= 8) {
+    const uint64_t t2x = xor_lane_u64<8>(t2);
+    top = wave_sort_blocks_desc<16>(lane < 8 ? t1 : t2x);
+  } else if (W <= 16) {
+    const uint64_t t2x = xor_lane_u64<16>(t2);
+    top = wave_sort_blocks_desc<32>(lane < 16 ? t1 : t2x);
+  } else {
+    const uint64_t t2x = xor_lane_u64<32>(t2);
+    top = wave_sort_blocks_desc<64>(lane < 32 ? t1 : t2x);
+  }
   const uint64_t cW =
       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(top >> 32), W - 1) << 32) |
       (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, W - 1);

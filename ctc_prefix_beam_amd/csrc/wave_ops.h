@@ -87,7 +87,8 @@ __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
 
 // One compare-exchange stage of a 64-lane bitonic sort (descending overall):
 // lane i keeps the larger of (own, lane i ^ J) when bit J of i equals bit K of
-// i, else the smaller.
+// i, else the smaller.  For 64-bit keys the compare result is combined with
+// that lane constant in one scalar operation and selects both halves.
 template <int K, int J, typename T>
 __device__ __forceinline__ T bitonic_stage(T v) {
   T p;
@@ -101,6 +102,38 @@ __device__ __forceinline__ T bitonic_stage(T v) {
   const T flip = keep_max ? (T)0 : ~(T)0;
   const T a = v ^ flip, b = p ^ flip;
   return (a > b ? a : b) ^ flip;
+}
+
+// The stages of a bitonic sort over blocks of N lanes (N = 16, 32 or 64),
+// each block into descending order.
+template <int N, typename T>
+__device__ __forceinline__ T wave_sort_blocks_desc(T v) {
+  v = bitonic_stage<2, 1>(v);
+  v = bitonic_stage<4, 2>(v);
+  v = bitonic_stage<4, 1>(v);
+  v = bitonic_stage<8, 4>(v);
+  v = bitonic_stage<8, 2>(v);
+  v = bitonic_stage<8, 1>(v);
+  v = bitonic_stage<16, 8>(v);
+  v = bitonic_stage<16, 4>(v);
+  v = bitonic_stage<16, 2>(v);
+  v = bitonic_stage<16, 1>(v);
+  if constexpr (N >= 32) {
+    v = bitonic_stage<32, 16>(v);
+    v = bitonic_stage<32, 8>(v);
+    v = bitonic_stage<32, 4>(v);
+    v = bitonic_stage<32, 2>(v);
+    v = bitonic_stage<32, 1>(v);
+  }
+  if constexpr (N >= 64) {
+    v = bitonic_stage<64, 32>(v);
+    v = bitonic_stage<64, 16>(v);
+    v = bitonic_stage<64, 8>(v);
+    v = bitonic_stage<64, 4>(v);
+    v = bitonic_stage<64, 2>(v);
+    v = bitonic_stage<64, 1>(v);
+  }
+  return v;
 }
 
 // Sorts one 32- or 64-bit unsigned key per lane into descending lane order.
