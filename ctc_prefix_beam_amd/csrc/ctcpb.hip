@@ -667,16 +667,23 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int src = par >= 0 ? par : lane;
   const float pb_par = __shfl(b.pb, src, 64);
   const int last_par = __shfl(last, src, 64);
-  const float lpc = (lv && last != blank) ? row[last] : kNeg;
+  // (reads and writes below run on every lane: `last` is always a label, and
+  // lanes without an effect write to their own spare entry or OR in zero)
+  const bool has_last = lv && last != blank;
+  const float lpc_raw = row[last];
+  const float lpc = has_last ? lpc_raw : kNeg;
   const float lpb = row[blank];
   // labels removed from a beam's ordinary list: its own last label (that is
   // the repeated-label slot) and the last label of each child (merged away).
   // The masks were cleared at the end of the previous step.
-  const int rr_own = (lv && last != blank) ? (int)C.rank[last] : -1;
-  if (par >= 0 && last == last_par) C.exclast[par] = 1;
-  if (par >= 0 && last != last_par && rr_own >= 0)
-    atomicOr(&C.exm[par * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
-  if (rr_own >= 0) atomicOr(&C.exm[lane * 4 + (rr_own >> 5)], 1u << (rr_own & 31));
+  const int rr_raw = (int)C.rank[last];
+  const int rr_own = has_last ? rr_raw : -1;
+  const int rw = rr_own >= 0 ? rr_own : 0;
+  const uint32_t rbit = rr_own >= 0 ? 1u << (rw & 31) : 0u;
+  C.exclast[(par >= 0 && last == last_par) ? par : kWave - 1 - lane % (kWave - kMaxBeam)] = 1;
+  atomicOr(&C.exm[(par >= 0 ? par : lane) * 4 + (rw >> 5)],
+           (par >= 0 && last != last_par) ? rbit : 0u);
+  atomicOr(&C.exm[lane * 4 + (rw >> 5)], rbit);
 
   // A_k = logsumexp(pb, pnb) was computed with the state.  The collapse for
   // skipped frames (sec. 3.4) turns (pb, pnb) into (A_k, NEG), and since
@@ -688,8 +695,9 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
   const float ptb = lv ? lpb + A : kNeg;
   float ptnb = (lv && !g && last != blank) ? lpc + pnb1 : kNeg;
-  if (par >= 0) {
-    const float from_parent = (last == last_par) ? lpc + pb1_par : lpc + A_par;
+  {
+    // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
+    const float from_parent = par < 0 ? kNeg : ((last == last_par) ? lpc + pb1_par : lpc + A_par);
     ptnb = lse(ptnb, from_parent);
   }
   const float keyb = lv ? lse(ptb, ptnb) : kNeg;
@@ -698,12 +706,16 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   lds_sync();
   const bool rep_ok = lv && last != blank && C.exclast[lane] == 0;
   const float keyc = rep_ok ? lpc + pb1 : kNeg;
-  if (lane < W) {
-    C.A[lane] = A;
-    C.kb[lane] = keyb;
-    C.kc[lane] = keyc;
-    C.lastk[lane] = last;
-  }
+  // per-beam values that only the rare selection fallbacks read from LDS
+  auto share_beam_values = [&]() {
+    if (lane < W) {
+      C.A[lane] = A;
+      C.kb[lane] = keyb;
+      C.kc[lane] = keyc;
+      C.lastk[lane] = last;
+    }
+    lds_sync();
+  };
 
   PROF_MARK(2);
   // ---- each beam's two best candidates, as composite keys (0 = none): the
@@ -846,6 +858,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     } else {
       // many survivors: exact streaming top-W over them (regenerated per beam
       // from the ranked list, since the buffer kept only the first kBuf)
+      share_beam_values();
       int lo = 0, hi = lv ? nPool : 0;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -893,6 +906,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     need_full = __ballot(bad) != 0ull;
   }
   if (need_full) {
+    share_beam_values();
     full_select(C, row, par, last);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
     wc = lane < W ? C.buf[lane] : 0ull;
@@ -922,22 +936,15 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   nb.len = w.valid ? len_k + (ext ? 1 : 0) : 0;
   nb.last = ext ? w.c : (w.valid ? last_k : blank);
   nb.last2 = ext ? (len_k >= 1 ? last_k : -1) : (w.valid ? last2_k : -1);
-  nb.h = ext ? hash_push(h_k, w.c) : (w.valid ? h_k : kHashEmpty);
+  const uint64_t h_ext = hash_push(h_k, w.c);   // computed on every lane, then selected
+  nb.h = ext ? h_ext : (w.valid ? h_k : kHashEmpty);
   nb.hp = ext ? h_k : (w.valid ? hp_k : 0ull);
   nb.score = w.valid ? key : kNeg;
-  if (!w.valid) {
-    nb.pb = kNeg;
-    nb.pnb = kNeg;
-  } else if (g) {
-    nb.pb = key;
-    nb.pnb = kNeg;
-  } else if (w.c == blank) {
-    nb.pb = ptb_k;
-    nb.pnb = ptnb_k;
-  } else {
-    nb.pb = kNeg;
-    nb.pnb = key;
-  }
+  // (pb, pnb): dead (NEG, NEG); after skipped frames (key, NEG); blank slot
+  // (its two parts); a new label (NEG, key)
+  const bool stay = w.c == blank;
+  nb.pb = !w.valid ? kNeg : (g ? key : (stay ? ptb_k : kNeg));
+  nb.pnb = !w.valid ? kNeg : (g ? kNeg : (stay ? ptnb_k : key));
 
   // parent slots of the new beams (the prefix one label shorter, if live).
   // bslot and htab were cleared at the end of the previous step.  The hash
@@ -945,7 +952,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // (it may just have been re-created by extending its own parent).
   const bool need_look = w.valid && !ext && par_k < 0 && len_k >= 2;
   const bool any_look = __ballot(need_look) != 0ull;
-  if (w.valid && w.c == blank) C.bslot[w.k] = lane;
+  C.bslot[(w.valid && w.c == blank) ? w.k : kWave - 1 - lane % (kWave - kMaxBeam)] = lane;
   int hslot = -1;
   if (any_look) {
     if (lane < W) {
@@ -962,12 +969,11 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // above are in flight
   nb.A = w.valid ? lse(nb.pb, nb.pnb) : kNeg;
   lds_sync();
-  int npar = -1, cand = -1;
-  if (ext) {
-    npar = C.bslot[w.k];
-  } else if (w.valid && par_k >= 0) {
-    npar = C.bslot[par_k];
-  } else if (need_look) {
+  int cand = -1;
+  const bool from_slot = ext || (w.valid && par_k >= 0);
+  const int npar_raw = C.bslot[ext ? w.k : (par_k >= 0 ? par_k : 0)];
+  int npar = from_slot ? npar_raw : -1;
+  if (need_look) {
     int s = (int)((uint32_t)hp_k & (kHtab - 1));
     for (int probe = 0; probe < kHtab; probe++) {
       const int e = C.htab[s];
@@ -1004,15 +1010,13 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     }
   }
   nb.parent = npar;
-  if (lane < W) b = nb;
+  b = nb;   // lanes past the beam hold the dead state either way
   // clear the exclusion masks, parent slots and hash entries for the next
   // step (LDS operations of this wave complete in order, after every read of
   // them above)
-  if (lane < kMaxBeam) {
-    reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    C.exclast[lane] = 0;
-    C.bslot[lane] = -1;
-  }
+  reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  C.exclast[lane] = 0;
+  C.bslot[lane] = -1;
   if (hslot >= 0) C.htab[hslot] = -1;
   PROF_MARK(6);
   return w;
@@ -1672,7 +1676,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       uint64_t t1 = clock64();
       sw += t1 - t0;
 #endif
-      const int2 rec = lane < W ? ring[(f % kRing) * kMaxBeam + lane] : make_int2(-1, 0);
+      const int2 rec = lane < W ? ring[(f % kRing) * kWave + lane] : make_int2(-1, 0);
       Winner w;
       w.valid = rec.x >= 0;
       w.k = w.valid ? (rec.x >> 16) : lane;
@@ -1731,11 +1735,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
   }
-  if (lane < kMaxBeam) {
-    reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
-    C.exclast[lane] = 0;
-    C.bslot[lane] = -1;
-  }
+  reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  C.exclast[lane] = 0;
+  C.bslot[lane] = -1;
   for (int i = lane; i < kHtab; i += kWave) C.htab[i] = -1;
   lds_sync();
 
@@ -1788,9 +1790,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     // written after the slot's data)
     next_ready = __hip_atomic_load(&ready[(f + 1) % nslot], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (lane < W)
-      ring[(f % kRing) * kMaxBeam + lane] =
-          make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
+    ring[(f % kRing) * kWave + lane] =
+        make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
     last_t = t;
     // the ring entry and this step's reads of the slot are LDS operations:
@@ -1965,9 +1966,11 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.kc = take(kMaxBeam * 4);
   S.lastk = take(kMaxBeam * 4);
   S.offs = take(128 * 4);
-  S.exm = take(kMaxBeam * 4 * 4);   // 4 words per beam: ranks 0..95 (+ padding)
-  S.exclast = take(kMaxBeam * 4);
-  S.bslot = take(kMaxBeam * 4);
+  // one entry per lane (not per beam) where lanes write without a guard: the
+  // entries past the beam absorb writes that have no effect
+  S.exm = take(kWave * 4 * 4);   // 4 words per beam: ranks 0..95 (+ padding)
+  S.exclast = take(kWave * 4);
+  S.bslot = take(kWave * 4);
   S.htab = take(kHtab * 4);
   S.newh = take(kMaxBeam * 8);
   S.newlen = take(kMaxBeam * 4);
@@ -1985,7 +1988,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
   // hand-off
   S.flags = take((3 * kMaxSlots + 4) * 4);
-  S.ring = take(kRing * kMaxBeam * 8);
+  S.ring = take(kRing * kWave * 8);
   S.soffs = take(128 * 4);
   S.nprod = nprod;
   S.nslot = nprod + 1;
