@@ -11,8 +11,8 @@
 //                   wave streams each frame's log-probabilities HBM -> LDS
 //                   (16-byte global-to-LDS loads) into a ring of P+1 frame
 //                   slots; P producer waves take the frames in turn:
-//     - vocabulary top-K (sec. 3.3 step 0, sec. 3.4.7): the best 2W+3
-//       non-blank labels by (log-prob desc, label asc), radix threshold,
+//     - vocabulary top-K (sec. 3.3 step 0, sec. 3.4.7): the best
+//       min(2W+3, 40) non-blank labels by (log-prob desc, label asc), radix threshold,
 //       ballot gather and count ranking; publish the slot by an LDS flag.
 //   Wave 0 runs the serial beam recursion over the published slots:
 //     - step 0 seeding (sec. 3.3) from the ranked list;
@@ -54,7 +54,8 @@
 namespace ctcpb {
 
 constexpr int kMaxVocab = 16384;
-constexpr int kMaxK = 2 * kMaxBeam + 3;   // ranked labels kept per frame
+constexpr int kMaxK = 2 * kMaxBeam + 3;   // ranked labels kept per frame (capacity)
+constexpr int kMaxRanked = 40;            // ranked labels used per frame
 constexpr int kBuf = 256;                 // candidate buffer (keys)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
 constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
@@ -1587,7 +1588,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
   const int64_t stride_t = P.stride_t;
   const int vec4 = P.vec4;
-  const int K = min(V - 1, 2 * W + 3);  // ranked labels per frame
+  // ranked labels per frame: 2W + 3, at most 40, so that the labels gathered
+  // to rank them mostly fit one per lane.  Any step where a label outside the
+  // list could still compete is detected and decoded by the full beam x vocab
+  // selection instead.
+  const int K = min(V - 1, min(2 * W + 3, kMaxRanked));
   const int complete = K == V - 1;
   __syncthreads();
 
