@@ -33,7 +33,7 @@
 //   which live beam is its prefix minus the last label ("parent"), derived
 //   from how the winners were formed; the one case the structure cannot
 //   decide (a parent prefix re-created from its own parent) is settled by a
-//   64-bit prefix hash filter and an exact token comparison.
+//   32-bit prefix hash filter and an exact token comparison.
 //
 // Numerics: float32, one rounding per operation, no contraction; exp / log1p
 // are fixed operation sequences (device_math.h).
@@ -105,7 +105,7 @@ struct Beam {
   float pb, pnb, score;
   float A;        // logsumexp(pb, pnb) (NEG if dead), kept with the state
   int len, last, parent, last2;
-  uint64_t h, hp;
+  uint32_t h, hp;
 };
 
 constexpr int kProfBase = 32;   // header word of the first phase counter (beam wave)
@@ -133,7 +133,7 @@ struct Ctx {
   int* exclast;
   int* bslot;
   int* htab;
-  uint64_t* newh;
+  uint32_t* newh;
   int* newlen;
   int* nchild;
   int* childc;
@@ -175,6 +175,15 @@ struct Ctx {
 // LDS-only ordering between the lanes of this wave (no wait on global memory).
 __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Orders this wave's LDS accesses for the compiler only.  The LDS performs
+// one wave's operations in issue order, so a read issued after a write or
+// atomic of this wave (by any of its lanes) sees it without a wait for the
+// write's completion.
+__device__ __forceinline__ void lds_order() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_wave_barrier();
 }
@@ -302,11 +311,6 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 //   5. the gathered keys are ranked by counting (broadcast LDS reads).
 // Lists that do not fit the scratch fall back to a streaming top-K over the
 // whole row.
-__device__ __forceinline__ uint32_t sortable_bits(float f) {
-  const uint32_t u = __float_as_uint(f + 0.0f);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
 constexpr int kMaxGroups = 256;   // listed groups (step 3), ints after the keys
 constexpr int kMaxGather = 128;   // gathered keys (step 4)
 
@@ -366,7 +370,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   RF_MARK(1);
   // 2. threshold: the largest value (to 24 bits of its key, two bits per
   // round) that at least K of the 128 values reach; never below -inf
-  const uint32_t a = sortable_bits(hi), b = sortable_bits(lo);
+  const uint32_t a = sortable(hi), b = sortable(lo);
   uint32_t thr = 0u;
   for (int bit = 30; bit >= 8; bit -= 2) {
     const uint32_t c1 = thr | (1u << bit), c2 = thr | (2u << bit), c3 = thr | (3u << bit);
@@ -375,7 +379,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
     const int n3 = __popcll(__ballot(a >= c3)) + __popcll(__ballot(b >= c3));
     thr = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : thr));
   }
-  const uint32_t thr_min = sortable_bits(ninf);
+  const uint32_t thr_min = sortable(ninf);
   thr = thr > thr_min ? thr : thr_min;
   const float tf = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
 
@@ -436,7 +440,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
       for (int e = 0; e < 4; e++) {
         if ((em >> e) & 1u) {
           if (pos < kMaxGather)
-            scr[pos] = ((uint64_t)sortable_bits(xv[e]) << 32) | (uint32_t)(~(4 * g + e));
+            scr[pos] = ((uint64_t)sortable(xv[e]) << 32) | (uint32_t)(~(4 * g + e));
           pos++;
         }
       }
@@ -489,7 +493,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
     // fallback: streaming top-K over the whole row (exact for any input)
     auto gen = [&](int64_t i) -> uint64_t {
       const int c = (int)i;
-      return c == blank ? 0ull : (((uint64_t)sortable_bits(row[c]) << 32) | (uint32_t)(~c));
+      return c == blank ? 0ull : (((uint64_t)sortable(row[c]) << 32) | (uint32_t)(~c));
     };
     const int got = stream_topk_buf(scr, K, V, gen);
     for (int r = lane; r < K; r += kWave) {
@@ -653,6 +657,7 @@ __device__ __forceinline__ int full_select(const Ctx& C, const float* row, int p
   return stream_topk(C, W, (int64_t)W * V, gen);
 }
 
+template <int NB>
 __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, int g, int step, int nR,
                             int complete) {
   const Layout& L = C.L;
@@ -704,7 +709,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float keyb = lv ? lse(ptb, ptnb) : kNeg;
 
   PROF_MARK(1);
-  lds_sync();
+  lds_order();
   const bool rep_ok = lv && last != blank && C.exclast[lane] == 0;
   const float keyc = rep_ok ? lpc + pb1 : kNeg;
   // per-beam values that only the rare selection fallbacks read from LDS
@@ -783,21 +788,16 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
   PROF_MARK(9);
   PROF_MARK(10);
-  // beam j's best goes to lane j, its second best to lane j + 2^ceil(log2 W)
-  // (one lane swap); the sorting network covers those first 16, 32 or 64
-  // lanes only
-  // (lane exchanges run on every lane, outside any lane-dependent branch:
-  // a lane that is switched off supplies no value to the exchange)
+  // beam j's best goes to lane j, its second best to lane j + NB / 2 (one
+  // lane swap; W <= NB / 2); the sorting network covers those first NB lanes
+  // only (lane exchanges run on every lane, outside any lane-dependent
+  // branch: a lane that is switched off supplies no value to the exchange)
   uint64_t top;
-  if (W <= 8) {
-    const uint64_t t2x = xor_lane_u64<8>(t2);
-    top = wave_sort_blocks_desc<16>(lane < 8 ? t1 : t2x);
-  } else if (W <= 16) {
-    const uint64_t t2x = xor_lane_u64<16>(t2);
-    top = wave_sort_blocks_desc<32>(lane < 16 ? t1 : t2x);
-  } else {
-    const uint64_t t2x = xor_lane_u64<32>(t2);
-    top = wave_sort_blocks_desc<64>(lane < 32 ? t1 : t2x);
+  {
+    constexpr int H = NB / 2;
+    const uint64_t t2x = xor_lane_u64<H>(t2);
+    top = wave_sort_blocks_desc<NB>(
+        __builtin_amdgcn_inverse_ballot_w64(lanes_below_n(H)) ? t1 : t2x);
   }
   const uint64_t cW =
       ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(top >> 32), W - 1) << 32) |
@@ -805,8 +805,10 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const bool exact = __ballot(n3 > cW) == 0ull;
   PROF_MARK(3);
   uint64_t wc;  // winner of slot `lane` (composite key, 0 = none)
-  if (exact) {
+  uint64_t wW;  // the W-th winner (wave-uniform)
+  if (__builtin_expect(exact, 1)) {
     wc = lane < W ? top : 0ull;
+    wW = cW;
     PROF_MARK(4);
   } else {
     const float tau0 = cW > comp_floor() ? comp_key(cW) : kNeg;
@@ -894,19 +896,18 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
       if (lane == 0) C.scal[kScalWide] += 1;
       wc = lane < W ? C.buf[lane] : 0ull;
     }
+    wW = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(wc >> 32), W - 1) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wc, W - 1);
   }
   bool need_full = false;
   if (!complete) {
     // labels outside the ranked list score at most A_k + (last ranked lp);
     // they must stay strictly below the W-th selected key
-    const uint64_t wl =
-        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(wc >> 32), W - 1) << 32) |
-        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wc, W - 1);
-    const float keyW = wl > comp_floor() ? comp_key(wl) : kNeg;
+    const float keyW = wW > comp_floor() ? comp_key(wW) : kNeg;
     const bool bad = lv && !((bound + A) < keyW);
     need_full = __ballot(bad) != 0ull;
   }
-  if (need_full) {
+  if (__builtin_expect(need_full, 0)) {
     share_beam_values();
     full_select(C, row, par, last);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
@@ -928,8 +929,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const int last_k = __shfl(last, k, 64);
   const int par_k = __shfl(b.parent, k, 64);
   const int last2_k = __shfl(b.last2, k, 64);
-  const uint64_t h_k = shfl_u64(b.h, k);
-  const uint64_t hp_k = shfl_u64(b.hp, k);
+  const uint32_t h_k = (uint32_t)__shfl((int)b.h, k, 64);
+  const uint32_t hp_k = (uint32_t)__shfl((int)b.hp, k, 64);
   w.len_k = len_k;
   const bool ext = w.valid && w.c != blank;
   Beam nb;
@@ -937,9 +938,9 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   nb.len = w.valid ? len_k + (ext ? 1 : 0) : 0;
   nb.last = ext ? w.c : (w.valid ? last_k : blank);
   nb.last2 = ext ? (len_k >= 1 ? last_k : -1) : (w.valid ? last2_k : -1);
-  const uint64_t h_ext = hash_push(h_k, w.c);   // computed on every lane, then selected
+  const uint32_t h_ext = hash_push(h_k, w.c);   // computed on every lane, then selected
   nb.h = ext ? h_ext : (w.valid ? h_k : kHashEmpty);
-  nb.hp = ext ? h_k : (w.valid ? hp_k : 0ull);
+  nb.hp = ext ? h_k : (w.valid ? hp_k : 0u);
   nb.score = w.valid ? key : kNeg;
   // (pb, pnb): dead (NEG, NEG); after skipped frames (key, NEG); blank slot
   // (its two parts); a new label (NEG, key)
@@ -955,59 +956,63 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const bool any_look = __ballot(need_look) != 0ull;
   C.bslot[(w.valid && w.c == blank) ? w.k : kWave - 1 - lane % (kWave - kMaxBeam)] = lane;
   int hslot = -1;
-  if (any_look) {
+  if (__builtin_expect(any_look, 0)) {
     if (lane < W) {
       C.newh[lane] = nb.h;
       C.newlen[lane] = nb.len;
     }
     if (ext) {
-      int s = (int)((uint32_t)nb.h & (kHtab - 1));
+      int s = (int)(nb.h & (kHtab - 1));
       while (atomicCAS(&C.htab[s], -1, lane) != -1) s = (s + 1) & (kHtab - 1);
       hslot = s;
     }
   }
-  // the next step's A of every new beam, computed while the table writes
-  // above are in flight
-  nb.A = w.valid ? lse(nb.pb, nb.pnb) : kNeg;
-  lds_sync();
-  int cand = -1;
+  // the next step's A = logsumexp(pb, pnb) of every new beam is its selection
+  // key: a stay winner's key is logsumexp of the two parts it keeps, computed
+  // from the same operands in the same order, and every other winner has one
+  // part at NEG, where logsumexp(x, NEG) == x
+  nb.A = w.valid ? key : kNeg;
+  lds_order();
   const bool from_slot = ext || (w.valid && par_k >= 0);
   const int npar_raw = C.bslot[ext ? w.k : (par_k >= 0 ? par_k : 0)];
   int npar = from_slot ? npar_raw : -1;
-  if (need_look) {
-    int s = (int)((uint32_t)hp_k & (kHtab - 1));
-    for (int probe = 0; probe < kHtab; probe++) {
-      const int e = C.htab[s];
-      if (e < 0) break;
-      if (C.newh[e] == hp_k && C.newlen[e] == len_k - 1) {
-        cand = e;
-        break;
+  if (__builtin_expect(any_look, 0)) {
+    int cand = -1;
+    if (need_look) {
+      int s = (int)(hp_k & (kHtab - 1));
+      for (int probe = 0; probe < kHtab; probe++) {
+        const int e = C.htab[s];
+        if (e < 0) break;
+        if (C.newh[e] == hp_k && C.newlen[e] == len_k - 1) {
+          cand = e;
+          break;
+        }
+        s = (s + 1) & (kHtab - 1);
       }
-      s = (s + 1) & (kHtab - 1);
     }
-  }
-  const int ce = cand >= 0 ? cand : lane;
-  const int k2 = __shfl(w.k, ce, 64);
-  const int c2 = __shfl(w.c, ce, 64);
-  if (cand >= 0 && c2 != last2_k) cand = -1;
-  uint64_t todo = __ballot(cand >= 0);
-  // the previous step's tokens must have been written by the store wave
-  if (todo && !spin_wait(C.wdone, step - 1, false, C.abortf)) todo = 0ull;
-  if (todo) {
-    const int q = (step - 1) & 1;
-    const int from = C.scal[kScalCpl0 + q];
-    while (todo) {
-      const int v = __ffsll((long long)todo) - 1;
-      todo &= todo - 1;
-      const int ka = __shfl(w.k, v, 64);
-      const int kb2 = __shfl(k2, v, 64);
-      const int n = __shfl(len_k, v, 64) - 2;
-      bool eq = true;
-      for (int p = from + lane; p < n; p += kWave)
-        eq = eq && tok_at(C, C.tab, q, ka, p) == tok_at(C, C.tab, q, kb2, p);
-      const bool all = __ballot(!eq) == 0ull;
-      if (lane == v && all) npar = cand;
-      if (lane == 0) C.scal[kScalVerifies] += 1;
+    const int ce = cand >= 0 ? cand : lane;
+    const int k2 = __shfl(w.k, ce, 64);
+    const int c2 = __shfl(w.c, ce, 64);
+    if (cand >= 0 && c2 != last2_k) cand = -1;
+    uint64_t todo = __ballot(cand >= 0);
+    // the previous step's tokens must have been written by the store wave
+    if (todo && !spin_wait(C.wdone, step - 1, false, C.abortf)) todo = 0ull;
+    if (todo) {
+      const int q = (step - 1) & 1;
+      const int from = C.scal[kScalCpl0 + q];
+      while (todo) {
+        const int v = __ffsll((long long)todo) - 1;
+        todo &= todo - 1;
+        const int ka = __shfl(w.k, v, 64);
+        const int kb2 = __shfl(k2, v, 64);
+        const int n = __shfl(len_k, v, 64) - 2;
+        bool eq = true;
+        for (int p = from + lane; p < n; p += kWave)
+          eq = eq && tok_at(C, C.tab, q, ka, p) == tok_at(C, C.tab, q, kb2, p);
+        const bool all = __ballot(!eq) == 0ull;
+        if (lane == v && all) npar = cand;
+        if (lane == 0) C.scal[kScalVerifies] += 1;
+      }
     }
   }
   nb.parent = npar;
@@ -1306,8 +1311,8 @@ __device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
     b.parent = reinterpret_cast<const int*>(a + BeamArrays::parent)[lane];
     b.last2 = reinterpret_cast<const int*>(a + BeamArrays::last2)[lane];
     b.live = reinterpret_cast<const int*>(a + BeamArrays::live)[lane];
-    b.h = reinterpret_cast<const uint64_t*>(a + BeamArrays::hash)[lane];
-    b.hp = reinterpret_cast<const uint64_t*>(a + BeamArrays::phash)[lane];
+    b.h = reinterpret_cast<const uint32_t*>(a + BeamArrays::hash)[lane];
+    b.hp = reinterpret_cast<const uint32_t*>(a + BeamArrays::phash)[lane];
     b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
   } else {
     b.live = 0;
@@ -1333,8 +1338,8 @@ __device__ __forceinline__ void beam_store(const Ctx& C, const Beam& b) {
     reinterpret_cast<int*>(a + BeamArrays::parent)[lane] = b.parent;
     reinterpret_cast<int*>(a + BeamArrays::last2)[lane] = b.last2;
     reinterpret_cast<int*>(a + BeamArrays::live)[lane] = b.live;
-    reinterpret_cast<uint64_t*>(a + BeamArrays::hash)[lane] = b.h;
-    reinterpret_cast<uint64_t*>(a + BeamArrays::phash)[lane] = b.hp;
+    reinterpret_cast<uint32_t*>(a + BeamArrays::hash)[lane] = b.h;
+    reinterpret_cast<uint32_t*>(a + BeamArrays::phash)[lane] = b.hp;
   }
 }
 
@@ -1379,7 +1384,7 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.exclast = reinterpret_cast<int*>(smem + S.exclast);
   C.bslot = reinterpret_cast<int*>(smem + S.bslot);
   C.htab = reinterpret_cast<int*>(smem + S.htab);
-  C.newh = reinterpret_cast<uint64_t*>(smem + S.newh);
+  C.newh = reinterpret_cast<uint32_t*>(smem + S.newh);
   C.newlen = reinterpret_cast<int*>(smem + S.newlen);
   C.nchild = reinterpret_cast<int*>(smem + S.nchild);
   C.childc = reinterpret_cast<int*>(smem + S.childc);
@@ -1532,7 +1537,7 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
 //   producers    each takes every P-th frame once its row has landed and
 //                ranks its labels, ahead of the recursion.
 // Every row of log_prob is read once.
-template <bool STREAM>
+template <bool STREAM, int NB>
 __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
   const Layout L = P.L;
@@ -1608,8 +1613,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     // Copies each frame's row into its slot as soon as the slot is free and
     // flags it once the copy has landed.  It is the only wave that copies
     // global memory into LDS, so no other wave's LDS reads wait on a copy.
-    for (int f = 0; f < nframes; f++) {
-      const int sl = f % nslot;
+    for (int f = 0, sl = 0; f < nframes; f++, sl = sl + 1 == nslot ? 0 : sl + 1) {
       if (!spin_wait(consumed, f - nslot, false, abortf)) break;
       const int t = STREAM ? step_in + f : sel[f];
       row_fetch_async(lp_row + (int64_t)(STREAM ? f : t) * stride_t, slot_row(sl), V, vec4);
@@ -1627,8 +1631,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     uint64_t pw = 0, pr = 0, t0 = clock64(), t1;
     uint64_t rprof[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #endif
-    for (int f = pid; f < nframes; f += nprod) {
-      const int sl = f % nslot;
+    // frame f sits in slot f mod nslot (kept incrementally: nprod <= nslot)
+    for (int f = pid, sl = pid % nslot; f < nframes;
+         f += nprod, sl = sl + nprod >= nslot ? sl + nprod - nslot : sl + nprod) {
       if (!spin_wait(&loaded[sl], f, true, abortf)) break;
 #ifdef CTCPB_PHASE_PROF
       t1 = clock64();
@@ -1749,8 +1754,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   bool aborted = false;
   int next_ready = -2;          // value of the next slot's flag, read one step early
   int wdone_seen = step - 1;    // store-wave progress last observed
-  for (int f = 0; f < nframes; f++) {
-    const int sl = f % nslot;
+  for (int f = 0, sl = 0; f < nframes; f++) {
+    const int sl_next = sl + 1 == nslot ? 0 : sl + 1;   // slot of frame f + 1
 #ifdef CTCPB_PHASE_PROF
     if (f == 0) {
       for (int i = 0; i < kProfSlots; i++) C.prof[i] = 0;
@@ -1758,7 +1763,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       C.prof_t = clock64();
     }
 #endif
-    if (next_ready != f && !spin_wait(&ready[sl], f, true, abortf)) {
+    if (__builtin_expect(next_ready != f, 0) && !spin_wait(&ready[sl], f, true, abortf)) {
       aborted = true;
       break;
     }
@@ -1770,7 +1775,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.rank = slot_rank(sl);
     const int t = frame_t[sl];
     Winner w;
-    if (step == 0) {
+    if (__builtin_expect(step == 0, 0)) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
       const int nb0 = W > 1 ? W - 1 : 1;
       w.valid = lane < W && b.live;
@@ -1779,31 +1784,35 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       w.len_k = 0;
     } else {
       const int g = t > last_t + 1 ? 1 : 0;
-      w = beam_step(C, b, row, g, step, K, complete);
+      w = beam_step<NB>(C, b, row, g, step, K, complete);
     }
     // hand the winners to the store wave (its ring entry must be free)
-    if (wdone_seen < step - kRing) {
+    if (__builtin_expect(wdone_seen < step - kRing, 0)) {
       if (!spin_wait(wdone, step - kRing, false, abortf)) {
         aborted = true;
         break;
       }
       wdone_seen = flag_load(wdone);
     }
-    // peek at the next frame's flag now: the read completes with the LDS
-    // wait below instead of on its own at the top of the next step (LDS
-    // operations of a wave complete in order, so a flag seen set here was
-    // written after the slot's data)
-    next_ready = __hip_atomic_load(&ready[(f + 1) % nslot], __ATOMIC_RELAXED,
+    // peek at the next frame's flag now: its latency overlaps the end of
+    // this step instead of stalling the top of the next one (LDS operations
+    // complete in order, so a flag seen set here was written after the
+    // slot's data)
+    next_ready = __hip_atomic_load(&ready[sl_next], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
     ring[(f % kRing) * kWave + lane] =
         make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
     last_t = t;
-    // the ring entry and this step's reads of the slot are LDS operations:
-    // complete them, then release the slot and publish the winners
-    flag_publish_lds(consumed, f);
+    // the ring entry and this step's reads of the slot are LDS operations of
+    // this wave, which the LDS performs in issue order: the flags written
+    // after them (release the slot, publish the winners) are seen only after
+    // them, with no wait for their completion
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __hip_atomic_store(consumed, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __hip_atomic_store(wpub, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     step++;
+    sl = sl_next;
   }
   // every published step stored (bounded wait that the abort flag does not cut
   // short: the store wave drains what was published before it stops)
@@ -1977,7 +1986,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   S.exclast = take(kWave * 4);
   S.bslot = take(kWave * 4);
   S.htab = take(kHtab * 4);
-  S.newh = take(kMaxBeam * 8);
+  S.newh = take(kMaxBeam * 4);
   S.newlen = take(kMaxBeam * 4);
   S.nchild = take(kMaxBeam * 4);
   S.childc = take(kMaxBeam * kMaxBeam * 4);
@@ -2034,6 +2043,15 @@ int check_lds(const LdsPlan& S) {
                     " bytes of LDS per row, more than the 160 KiB of a CU (smaller vocab, "
                     "beam, capacity or num_pages)");
   return CTCPB_OK;
+}
+
+// The decode kernel whose sorting network fits the beam: 16, 32 or 64 lanes
+// for beams up to 8, 16 or 32.
+template <bool STREAM>
+void (*decode_kernel_for(int W))(Params) {
+  if (W <= 8) return decode_kernel<STREAM, 16>;
+  if (W <= 16) return decode_kernel<STREAM, 32>;
+  return decode_kernel<STREAM, 64>;
 }
 
 template <typename K>
@@ -2129,8 +2147,8 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
-  if (int rc = launch(decode_kernel<false>, batch, 64 * (3 + P.S.nprod), P.S.total, st, P,
-                      "decode_kernel"))
+  if (int rc = launch(decode_kernel_for<false>(R.W), batch, 64 * (3 + P.S.nprod), P.S.total,
+                      st, P, "decode_kernel"))
     return rc;
   return ok();
 }
@@ -2193,7 +2211,7 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
-  if (int rc = launch(decode_kernel<true>, n_rows, 64 * (3 + P.S.nprod), P.S.total,
+  if (int rc = launch(decode_kernel_for<true>(R.W), n_rows, 64 * (3 + P.S.nprod), P.S.total,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
   return ok();

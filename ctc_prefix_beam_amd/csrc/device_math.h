@@ -80,7 +80,8 @@ __device__ __forceinline__ float lse(float a, float b) {
 // into +0.0 so that the two zeros, equal as floats, map to one key.
 __device__ __forceinline__ uint32_t sortable(float f) {
   const uint32_t u = __float_as_uint(f + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negatives: all bits flipped; non-negatives: the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float unsortable(uint32_t s) {
@@ -101,14 +102,14 @@ __device__ __forceinline__ uint64_t comp_floor() {
   return ((uint64_t)0x00800000u << 32) | 0xffffffffu;  // sortable(-FLT_MAX), id 0
 }
 
-// 64-bit mix of a token into a prefix hash (splitmix64 finaliser).  Used
-// only as a filter before an exact token comparison.
-__device__ __forceinline__ uint64_t hash_push(uint64_t h, int tok) {
-  uint64_t x = h + 0x9e3779b97f4a7c15ull * (uint64_t)(uint32_t)(tok + 1);
-  x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ull;
-  x = (x ^ (x >> 27)) * 0x94d049bb133111ebull;
-  return x ^ (x >> 31);
+// Mix of a token into a 32-bit prefix hash: xor, multiply by an odd
+// constant, xor-shift (each a bijection of the 32-bit state, so prefixes of
+// one length that differ in one label never collide).  Used only as a filter
+// before an exact token comparison.
+__device__ __forceinline__ uint32_t hash_push(uint32_t h, int tok) {
+  uint32_t x = (h ^ (uint32_t)(tok + 1)) * 0x9e3779b1u;
+  return x ^ (x >> 16);
 }
-constexpr uint64_t kHashEmpty = 0x2545f4914f6cdd1dull;
+constexpr uint32_t kHashEmpty = 0x4f6cdd1du;
 
 }  // namespace ctcpb

@@ -64,8 +64,8 @@ struct Layout {
 // Beam arrays inside a row region (offsets from o_beam).
 struct BeamArrays {
   static constexpr int64_t pb = 0, pnb = 128, score = 256, len = 384, last = 512,
-                           parent = 640, last2 = 768, live = 896, hash = 1024, phash = 1280,
-                           bytes = 1536;
+                           parent = 640, last2 = 768, live = 896, hash = 1024, phash = 1152,
+                           bytes = 1280;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }

@@ -36,6 +36,19 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Lanes i with (i & J) == 0, as a wave mask (all lanes for J = 64).
+__host__ __device__ constexpr uint64_t lanes_bit_clear(int j) {
+  uint64_t m = 0;
+  for (int i = 0; i < 64; i++)
+    if ((i & j) == 0) m |= 1ull << i;
+  return m;
+}
+
+// Lanes i < n, as a wave mask.
+__host__ __device__ constexpr uint64_t lanes_below_n(int n) {
+  return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
 // DPP lane moves (VALU, no LDS round trip).  Controls follow the GCN/CDNA
 // DPP encoding: quad_perm, row_half_mirror, row_mirror, row_shr:n,
 // row_bcast:15 and row_bcast:31.
@@ -51,10 +64,13 @@ constexpr int kDppBcast15 = 0x142;      // lane 15 of each row -> next row
 constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
 __device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
 __device__ __forceinline__ constexpr int dpp_row_shl(int n) { return 0x100 + n; }
+__device__ __forceinline__ constexpr int dpp_row_ror(int n) { return 0x120 + n; }
 
 // Value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}, without an LDS
-// round trip: quad permutes for 1 and 2, a row shift each way for 4 and 8,
-// and the gfx950 lane-swap instructions across rows (16) and halves (32).
+// round trip: quad permutes for 1 and 2; for 4, a row shift each way, each
+// written only to the banks (groups of 4 lanes) it serves; a rotation by 8
+// within the row for 8; the gfx950 lane-swap instructions across rows (16)
+// and halves (32).
 template <int J>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   const int x = (int)v;
@@ -62,19 +78,19 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp(x, kDppXor1, 0xf, 0xf, true);
   } else if constexpr (J == 2) {
     return (uint32_t)__builtin_amdgcn_mov_dpp(x, kDppXor2, 0xf, 0xf, true);
-  } else if constexpr (J == 4 || J == 8) {
-    // lanes a shift leaves without a source read 0; the select below never
-    // uses them
-    const int dn = __builtin_amdgcn_mov_dpp(x, dpp_row_shr(J), 0xf, 0xf, true);  // i <- i - J
-    const int up = __builtin_amdgcn_mov_dpp(x, dpp_row_shl(J), 0xf, 0xf, true);  // i <- i + J
-    return (uint32_t)((lane_id() & J) ? dn : up);
+  } else if constexpr (J == 4) {
+    // banks 0 and 2 read lane i + 4, banks 1 and 3 lane i - 4
+    const int up = __builtin_amdgcn_update_dpp(0, x, dpp_row_shl(4), 0xf, 0x5, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(up, x, dpp_row_shr(4), 0xf, 0xa, false);
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp(x, dpp_row_ror(8), 0xf, 0xf, true);
   } else if constexpr (J == 16) {
     const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (lane_id() & 16) ? r[0] : r[1];
+    return __builtin_amdgcn_inverse_ballot_w64(~lanes_bit_clear(16)) ? r[0] : r[1];
   } else {
     static_assert(J == 32, "lane distance");
     const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (lane_id() & 32) ? r[0] : r[1];
+    return __builtin_amdgcn_inverse_ballot_w64(~lanes_bit_clear(32)) ? r[0] : r[1];
   }
 }
 
@@ -87,21 +103,52 @@ __device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v) {
 
 // One compare-exchange stage of a 64-lane bitonic sort (descending overall):
 // lane i keeps the larger of (own, lane i ^ J) when bit J of i equals bit K of
-// i, else the smaller.  For 64-bit keys the compare result is combined with
-// that lane constant in one scalar operation and selects both halves.
+// i, else the smaller.  The pair is (a, b) = (own, partner) for J <= 8; for
+// J = 16 and 32 the lane-swap instruction leaves the lower block's key in a
+// and the upper block's in b on both sides of the pair, which serves as well
+// since the kept key depends only on the pair and the lane's side.  One
+// compare gives the wave mask of a > b; a scalar XOR with the stage's lane
+// constant turns it into "take a", which selects both halves of the key.
 template <int K, int J, typename T>
 __device__ __forceinline__ T bitonic_stage(T v) {
-  T p;
-  if constexpr (sizeof(T) == 8) p = xor_lane_u64<J>(v);
-  else p = xor_lane<J>(v);
-  const int lane = lane_id();
-  const bool keep_max = ((lane & J) == 0) == ((lane & K) == 0);
-  // lanes that keep the smaller key compare complemented keys (complement
-  // reverses the order), so every lane takes a maximum: the compare result
-  // feeds the selects directly, with no lane-mask combination in between
-  const T flip = keep_max ? (T)0 : ~(T)0;
-  const T a = v ^ flip, b = p ^ flip;
-  return (a > b ? a : b) ^ flip;
+  // lanes that keep the smaller key of their pair
+  constexpr uint64_t kFlip = lanes_bit_clear(J) ^ lanes_bit_clear(K);
+  T a, b;
+  if constexpr (J <= 8) {
+    a = v;
+    if constexpr (sizeof(T) == 8) {
+      b = ((uint64_t)xor_lane<J>((uint32_t)(v >> 32)) << 32) | xor_lane<J>((uint32_t)v);
+    } else {
+      b = xor_lane<J>(v);
+    }
+  } else if constexpr (sizeof(T) == 8) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    if constexpr (J == 16) {
+      const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+      const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+      a = ((uint64_t)h[0] << 32) | l[0];
+      b = ((uint64_t)h[1] << 32) | l[1];
+    } else {
+      static_assert(J == 32, "lane distance");
+      const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      a = ((uint64_t)h[0] << 32) | l[0];
+      b = ((uint64_t)h[1] << 32) | l[1];
+    }
+  } else {
+    if constexpr (J == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      a = r[0];
+      b = r[1];
+    } else {
+      static_assert(J == 32, "lane distance");
+      const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      a = r[0];
+      b = r[1];
+    }
+  }
+  const uint64_t gt = __builtin_amdgcn_ballot_w64(a > b);
+  return __builtin_amdgcn_inverse_ballot_w64(gt ^ kFlip) ? a : b;
 }
 
 // The stages of a bitonic sort over blocks of N lanes (N = 16, 32 or 64),
