@@ -54,22 +54,21 @@
 namespace ctcpb {
 
 constexpr int kMaxVocab = 16384;
-constexpr int kMaxK = 2 * kMaxBeam + 3;   // ranked labels kept per frame (capacity)
 constexpr int kMaxRanked = 40;            // ranked labels used per frame
 constexpr int kBuf = 256;                 // candidate buffer (keys)
+constexpr int kHtab = 256;   // open-addressing table of new prefixes (>= 8 x beam)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
 constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
 
 // LDS carve-up (byte offsets), computed on the host from the dimensions.
+// LDS offsets computed on the host: the frame slots and everything whose size
+// depends on the configuration (the fixed part is the lds namespace below).
 struct LdsPlan {
-  int slot0, slot_stride, slot_Rc, slot_Rl, slot_rank;  // ring of frame slots
-  int nslot, nprod;                                     // slots, producer waves
-  int scr, flags;                                       // producer scratch, hand-off flags
-  int ring, soffs;                                      // winners ring, store-wave scratch
-  int clist, clist_lds;                                 // flat token lists held in LDS
-  int fsrc, flen;                                       // flat copy lineage
-  int buf, A, kb, kc, lastk, offs, exm, exclast, bslot, htab, newh, newlen, nchild, childc, scal,
-      tab, ref, fstk, tail, tlen, total;
+  int slot_stride, slot_rank;   // frame slot: row of V floats, then the label -> rank map
+  int nslot, nprod;             // slots, producer waves
+  int scr;                      // producer scratch
+  int clist, clist_lds;         // flat token lists held in LDS
+  int tab, ref, fstk, tail, tlen, total;
 };
 constexpr int kMaxSlots = 8;
 constexpr int kRing = 8;   // steps of winners the store wave may lag behind
@@ -99,6 +98,39 @@ enum : int {
   kScalCpl1, kScalPcp0, kScalPcp1, kScalFallbacks, kScalVerifies, kScalSurv, kScalWide,
   kScalCount
 };
+
+// The fixed part of the workgroup's LDS: structures whose sizes do not depend
+// on the configuration, at compile-time offsets (immediate LDS addresses in
+// the kernels).  The frame slots follow at lds::end.
+namespace lds {
+constexpr int a16(int x) { return (x + 15) & ~15; }
+constexpr int buf = 0;                                  // candidate keys
+constexpr int A = buf + a16(kBuf * 8);                  // per-beam values of the fallbacks
+constexpr int kb = A + a16(kMaxBeam * 4);
+constexpr int kc = kb + a16(kMaxBeam * 4);
+constexpr int lastk = kc + a16(kMaxBeam * 4);
+constexpr int offs = lastk + a16(kMaxBeam * 4);
+// one entry per lane (not per beam) where lanes write without a guard: the
+// entries past the beam absorb writes that have no effect
+constexpr int exm = offs + a16(128 * 4);                // 2 words per beam: ranks 0..63
+constexpr int exclast = exm + a16(kWave * 2 * 4);
+constexpr int bslot = exclast + a16(kWave * 4);
+constexpr int htab = bslot + a16(kWave * 4);
+constexpr int newh = htab + a16(kHtab * 4);
+constexpr int newlen = newh + a16(kMaxBeam * 4);
+constexpr int nchild = newlen + a16(kMaxBeam * 4);
+constexpr int childc = nchild + a16(kMaxBeam * 4);
+constexpr int scal = childc + a16(kMaxBeam * kMaxBeam * 4);
+constexpr int fsrc = scal + a16(kScalCount * 4);        // flat copy lineage
+constexpr int flen = fsrc + a16(2 * kMaxBeam * 4);
+constexpr int flags = flen + a16(2 * kMaxBeam * 4);     // hand-off flags
+constexpr int ring = flags + a16((3 * kMaxSlots + 4) * 4);  // winners ring
+constexpr int soffs = ring + a16(kRing * kWave * 8);    // store-wave scratch
+constexpr int slot_k = a16(kMaxRanked * 4);             // per-slot stride of the ranked lists
+constexpr int Rc = soffs + a16(128 * 4);                // [kMaxSlots] ranked labels
+constexpr int Rl = Rc + kMaxSlots * slot_k;             // [kMaxSlots] their log-probabilities
+constexpr int end = Rl + kMaxSlots * slot_k;
+}  // namespace lds
 
 struct Beam {
   int live;
@@ -563,9 +595,16 @@ constexpr int kSeed = 0x7f;
 
 // Candidate id (k, c) as (k << 14) | c: ordered exactly like k * V + c since
 // c < V <= 2^14, and decoded without a division.
+static_assert(kMaxRanked <= 64, "ranks of a frame fit one 64-bit mask");
+
+// c ? a : b over values already computed (a select, not a branch).
+template <typename T>
+__device__ __forceinline__ T sel(bool c, T a, T b) {
+  return c ? a : b;
+}
+
 constexpr int kIdShift = 14;
 static_assert(kMaxVocab <= (1 << kIdShift), "labels must fit the id field");
-constexpr int kHtab = 256;   // open-addressing table of new prefixes (>= 8 x beam)
 __device__ __forceinline__ uint32_t cand_id(int k, int c) {
   return ((uint32_t)k << kIdShift) | (uint32_t)c;
 }
@@ -663,55 +702,57 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, V = L.V, blank = L.blank;
-  const bool lv = lane < W && b.live;
+  // (values are computed on every lane and then selected: conditional
+  // operators over computed values, no control flow on the common path)
+  const bool lv = (lane < W) & (b.live != 0);
 
   const int last = b.last;
   // merge (sec. 3.4.3): beam j = parent i + `last`; i's extension by `last`
   // is folded into j's blank slot.  The parent's state is exchanged first so
   // that the exchange overlaps the arithmetic below.
-  const int par = lv ? b.parent : -1;
-  const int src = par >= 0 ? par : lane;
+  const int par = sel(lv, b.parent, -1);
+  const int src = sel(par >= 0, par, lane);
   const float pb_par = __shfl(b.pb, src, 64);
   const int last_par = __shfl(last, src, 64);
+  const float A_par = __shfl(b.A, src, 64);
   // (reads and writes below run on every lane: `last` is always a label, and
   // lanes without an effect write to their own spare entry or OR in zero)
-  const bool has_last = lv && last != blank;
+  const bool has_last = lv & (last != blank);
   const float lpc_raw = row[last];
-  const float lpc = has_last ? lpc_raw : kNeg;
   const float lpb = row[blank];
+  const int rr_raw = (int)C.rank[last];
+  const float lpc = sel(has_last, lpc_raw, kNeg);
   // labels removed from a beam's ordinary list: its own last label (that is
   // the repeated-label slot) and the last label of each child (merged away).
-  // The masks were cleared at the end of the previous step.
-  const int rr_raw = (int)C.rank[last];
-  const int rr_own = has_last ? rr_raw : -1;
-  const int rw = rr_own >= 0 ? rr_own : 0;
-  const uint32_t rbit = rr_own >= 0 ? 1u << (rw & 31) : 0u;
-  C.exclast[(par >= 0 && last == last_par) ? par : kWave - 1 - lane % (kWave - kMaxBeam)] = 1;
-  atomicOr(&C.exm[(par >= 0 ? par : lane) * 4 + (rw >> 5)],
-           (par >= 0 && last != last_par) ? rbit : 0u);
-  atomicOr(&C.exm[lane * 4 + (rw >> 5)], rbit);
+  // The masks (two words per lane: ranks 0..63) were cleared at the end of
+  // the previous step.
+  const bool same = (par >= 0) & (last == last_par);
+  const bool child_other = (par >= 0) & (last != last_par);
+  const bool rr_in = has_last & (rr_raw >= 0);
+  const int rw = sel(rr_in, rr_raw, 0);
+  const uint32_t rbit = sel(rr_in, 1u << (rw & 31), 0u);
+  C.exclast[sel(same, par, kWave - 1 - lane % (kWave - kMaxBeam))] = 1;
+  atomicOr(&C.exm[sel(par >= 0, par, lane) * 2 + (rw >> 5)], sel(child_other, rbit, 0u));
+  atomicOr(&C.exm[lane * 2 + (rw >> 5)], rbit);
 
   // A_k = logsumexp(pb, pnb) was computed with the state.  The collapse for
   // skipped frames (sec. 3.4) turns (pb, pnb) into (A_k, NEG), and since
   // logsumexp(x, NEG) == x exactly, A_k is the same either way.
-  const float A = lv ? b.A : kNeg;
-  const float A_par = __shfl(b.A, src, 64);
+  const float A = sel(lv, b.A, kNeg);
   const float pb1 = g ? A : b.pb, pnb1 = g ? kNeg : b.pnb;
   const float pb1_par = g ? A_par : pb_par;
   // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
-  const float ptb = lv ? lpb + A : kNeg;
-  float ptnb = (lv && !g && last != blank) ? lpc + pnb1 : kNeg;
-  {
-    // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
-    const float from_parent = par < 0 ? kNeg : ((last == last_par) ? lpc + pb1_par : lpc + A_par);
-    ptnb = lse(ptnb, from_parent);
-  }
-  const float keyb = lv ? lse(ptb, ptnb) : kNeg;
+  const float ptb = sel(lv, lpb + A, kNeg);
+  // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
+  const float from_parent = sel(par < 0, kNeg, sel(same, lpc + pb1_par, lpc + A_par));
+  const float ptnb = lse(sel(lv & !g & (last != blank), lpc + pnb1, kNeg), from_parent);
+  const float keyb = sel(lv, lse(ptb, ptnb), kNeg);
 
   PROF_MARK(1);
   lds_order();
-  const bool rep_ok = lv && last != blank && C.exclast[lane] == 0;
-  const float keyc = rep_ok ? lpc + pb1 : kNeg;
+  const int excl_own = C.exclast[lane];
+  const bool rep_ok = has_last & (excl_own == 0);
+  const float keyc = sel(rep_ok, lpc + pb1, kNeg);
   // per-beam values that only the rare selection fallbacks read from LDS
   auto share_beam_values = [&]() {
     if (lane < W) {
@@ -730,34 +771,20 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // has a third candidate above the W-th of them (checked below); otherwise
   // the W-th key is a tight threshold for the general gather.
   const int nPool = complete ? nR : nR - 1;
-  uint32_t fr0, fr1, fr2;  // in-pool ranks still open to this beam
-  {
-    const uint4 ex = reinterpret_cast<const uint4*>(C.exm)[lane & (kMaxBeam - 1)];
-    const uint32_t m[3] = {ex.x, ex.y, ex.z};
-    uint32_t o[3];
-#pragma unroll
-    for (int w = 0; w < 3; w++) {
-      const int lo = w * 32;
-      const uint32_t in_pool =
-          lo >= nPool ? 0u : (nPool - lo >= 32 ? 0xffffffffu : (1u << (nPool - lo)) - 1u);
-      o[w] = lv ? (~m[w] & in_pool) : 0u;
-    }
-    fr0 = o[0];
-    fr1 = o[1];
-    fr2 = o[2];
-  }
+  // in-pool ranks still open to this beam (nPool <= kMaxRanked <= 64)
+  const uint64_t in_pool = nPool >= 64 ? ~0ull : ((1ull << nPool) - 1ull);
+  const uint64_t exw = reinterpret_cast<const uint64_t*>(C.exm)[lane & (kMaxBeam - 1)];
+  const uint64_t fr = sel(lv, ~exw & in_pool, (uint64_t)0);
   PROF_MARK(8);
   // the first three open ranks, without branches (-1: none)
-  uint64_t g01 = (uint64_t)fr0 | ((uint64_t)fr1 << 32);
-  uint32_t g2 = fr2;
   int rr[3];
+  {
+    uint64_t g01 = fr;
 #pragma unroll
-  for (int i = 0; i < 3; i++) {
-    const int a = __ffsll((long long)g01) - 1;
-    const int c = __ffs((int)g2) - 1;
-    rr[i] = a >= 0 ? a : (c >= 0 ? 64 + c : -1);
-    g2 = a >= 0 ? g2 : (g2 & (g2 - 1u));
-    g01 &= g01 - 1ull;
+    for (int i = 0; i < 3; i++) {
+      rr[i] = __ffsll((long long)g01) - 1;
+      g01 &= g01 - 1ull;
+    }
   }
   // their lists entries, all loads issued together (index 0 stands in for none)
   const uint32_t idb = cand_id(lane, 0);
@@ -765,7 +792,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   int rc[3];
 #pragma unroll
   for (int i = 0; i < 3; i++) {
-    const int r = rr[i] >= 0 ? rr[i] : 0;
+    const int r = sel(rr[i] >= 0, rr[i], 0);
     rl[i] = C.Rl[r];
     rc[i] = C.Rc[r];
   }
@@ -773,12 +800,12 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
 #pragma unroll
   for (int i = 0; i < 3; i++) {
     const float key = rl[i] + A;
-    oc[i] = (lv && rr[i] >= 0 && key > kNeg) ? compose(key, idb + (uint32_t)rc[i]) : 0ull;
+    oc[i] = sel(lv & (rr[i] >= 0) & (key > kNeg), compose(key, idb + (uint32_t)rc[i]), (uint64_t)0);
   }
   const uint64_t o1 = oc[0], o2 = oc[1], o3 = oc[2];
   const float bound = C.Rl[nR - 1];   // no label outside the ranked list scores above A + bound
-  const uint64_t cb = (lv && keyb > kNeg) ? compose(keyb, idb + (uint32_t)blank) : 0ull;
-  const uint64_t cc = (lv && keyc > kNeg) ? compose(keyc, idb + (uint32_t)last) : 0ull;
+  const uint64_t cb = sel(lv & (keyb > kNeg), compose(keyb, idb + (uint32_t)blank), (uint64_t)0);
+  const uint64_t cc = sel(lv & (keyc > kNeg), compose(keyc, idb + (uint32_t)last), (uint64_t)0);
   const uint64_t shi = cb > cc ? cb : cc, slo = cb > cc ? cc : cb;
   const uint64_t t1 = shi > o1 ? shi : o1;
   const uint64_t mid = shi > o1 ? o1 : shi, lo2 = slo > o2 ? slo : o2;
@@ -842,8 +869,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
           const float key = lpv[j] + A;
           const bool above = more && rr < nPool && key >= tau0;
           any = any || above;
-          const uint32_t open =
-              rr < 32 ? (fr0 >> rr) : (rr < 64 ? (fr1 >> (rr - 32)) : (fr2 >> (rr - 64)));
+          const uint64_t open = fr >> (rr & 63);
           put(above && (open & 1u), compose(key, cand_id(lane, cv[j])));
         }
         more = more && any;
@@ -889,7 +915,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
           else z = mid - 1;
         }
         const int rho = q - C.offs[a];
-        const uint32_t ex = (C.exm[a * 4 + (rho >> 5)] >> (rho & 31)) & 1u;
+        const uint32_t ex = (C.exm[a * 2 + (rho >> 5)] >> (rho & 31)) & 1u;
         return ex ? 0ull : compose(C.Rl[rho] + C.A[a], cand_id(a, C.Rc[rho]));
       };
       stream_topk(C, W, ncand, candidate);
@@ -1020,7 +1046,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // clear the exclusion masks, parent slots and hash entries for the next
   // step (LDS operations of this wave complete in order, after every read of
   // them above)
-  reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint64_t*>(C.exm)[lane] = 0ull;
   C.exclast[lane] = 0;
   C.bslot[lane] = -1;
   if (hslot >= 0) C.htab[hslot] = -1;
@@ -1374,28 +1400,28 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.rank = nullptr;  // per frame slot, set by the frame loop
   C.Rc = nullptr;
   C.Rl = nullptr;
-  C.buf = reinterpret_cast<uint64_t*>(smem + S.buf);
-  C.A = reinterpret_cast<float*>(smem + S.A);
-  C.kb = reinterpret_cast<float*>(smem + S.kb);
-  C.kc = reinterpret_cast<float*>(smem + S.kc);
-  C.lastk = reinterpret_cast<int*>(smem + S.lastk);
-  C.offs = reinterpret_cast<int*>(smem + S.offs);
-  C.exm = reinterpret_cast<uint32_t*>(smem + S.exm);
-  C.exclast = reinterpret_cast<int*>(smem + S.exclast);
-  C.bslot = reinterpret_cast<int*>(smem + S.bslot);
-  C.htab = reinterpret_cast<int*>(smem + S.htab);
-  C.newh = reinterpret_cast<uint32_t*>(smem + S.newh);
-  C.newlen = reinterpret_cast<int*>(smem + S.newlen);
-  C.nchild = reinterpret_cast<int*>(smem + S.nchild);
-  C.childc = reinterpret_cast<int*>(smem + S.childc);
-  C.scal = reinterpret_cast<int*>(smem + S.scal);
+  C.buf = reinterpret_cast<uint64_t*>(smem + lds::buf);
+  C.A = reinterpret_cast<float*>(smem + lds::A);
+  C.kb = reinterpret_cast<float*>(smem + lds::kb);
+  C.kc = reinterpret_cast<float*>(smem + lds::kc);
+  C.lastk = reinterpret_cast<int*>(smem + lds::lastk);
+  C.offs = reinterpret_cast<int*>(smem + lds::offs);
+  C.exm = reinterpret_cast<uint32_t*>(smem + lds::exm);
+  C.exclast = reinterpret_cast<int*>(smem + lds::exclast);
+  C.bslot = reinterpret_cast<int*>(smem + lds::bslot);
+  C.htab = reinterpret_cast<int*>(smem + lds::htab);
+  C.newh = reinterpret_cast<uint32_t*>(smem + lds::newh);
+  C.newlen = reinterpret_cast<int*>(smem + lds::newlen);
+  C.nchild = reinterpret_cast<int*>(smem + lds::nchild);
+  C.childc = reinterpret_cast<int*>(smem + lds::childc);
+  C.scal = reinterpret_cast<int*>(smem + lds::scal);
   C.tab = reinterpret_cast<int*>(smem + S.tab);
   C.ref = reinterpret_cast<int*>(smem + S.ref);
   C.fstk = reinterpret_cast<int*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
   C.tlen = reinterpret_cast<int*>(smem + S.tlen);
-  C.fsrc = reinterpret_cast<int*>(smem + S.fsrc);
-  C.flen = reinterpret_cast<int*>(smem + S.flen);
+  C.fsrc = reinterpret_cast<int*>(smem + lds::fsrc);
+  C.flen = reinterpret_cast<int*>(smem + lds::flen);
   C.clist = S.clist_lds ? reinterpret_cast<int*>(smem + S.clist)
                         : reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
@@ -1554,7 +1580,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int W = L.W, V = L.V;
   int* hdr = reinterpret_cast<int*>(base);
   const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
-  int* flags = reinterpret_cast<int*>(smem + S.flags);
+  int* flags = reinterpret_cast<int*>(smem + lds::flags);
   int* ready = flags;                    // [kMaxSlots]: frame held by each slot
   int* consumed = flags + kMaxSlots;     // last frame the beam wave finished
   int* abortf = consumed + 1;
@@ -1562,12 +1588,12 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* wdone = consumed + 3;             // last step the store wave has written
   int* loaded = consumed + 4;            // [kMaxSlots]: frame whose row each slot holds
   int* frame_t = loaded + kMaxSlots;     // [kMaxSlots]: time index of that frame
-  int2* ring = reinterpret_cast<int2*>(smem + S.ring);
+  int2* ring = reinterpret_cast<int2*>(smem + lds::ring);
   const int nslot = S.nslot, nprod = S.nprod;
-  auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride); };
-  auto slot_Rc = [&](int sl) { return reinterpret_cast<int*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rc); };
-  auto slot_Rl = [&](int sl) { return reinterpret_cast<float*>(smem + S.slot0 + sl * S.slot_stride + S.slot_Rl); };
-  auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + S.slot0 + sl * S.slot_stride + S.slot_rank); };
+  auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + lds::end + sl * S.slot_stride); };
+  auto slot_Rc = [&](int sl) { return reinterpret_cast<int*>(smem + lds::Rc + sl * lds::slot_k); };
+  auto slot_Rl = [&](int sl) { return reinterpret_cast<float*>(smem + lds::Rl + sl * lds::slot_k); };
+  auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + lds::end + sl * S.slot_stride + S.slot_rank); };
 
   const int step_in = STREAM ? hdr[kStep] : 0;
   // set-up shared by all waves: empty label ranks, flags
@@ -1670,7 +1696,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
 
   if (wave == store_wave) {
     // ---------------------------------------------------------- store wave
-    C.offs = reinterpret_cast<int*>(smem + S.soffs);
+    C.offs = reinterpret_cast<int*>(smem + lds::soffs);
     for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
       C.fsrc[i] = -1;
       C.flen[i] = -1;
@@ -1745,7 +1771,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
   }
-  reinterpret_cast<uint4*>(C.exm)[lane] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint64_t*>(C.exm)[lane] = 0ull;
   C.exclast[lane] = 0;
   C.bslot[lane] = -1;
   for (int i = lane; i < kHtab; i += kWave) C.htab[i] = -1;
@@ -1967,52 +1993,27 @@ int align16(int x) { return (x + 15) & ~15; }
 
 LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   LdsPlan S{};
-  int off = 0;
+  int off = lds::end;
   auto take = [&](int bytes) {
     const int at = off;
     off += align16(bytes);
     return at;
   };
-  // beam wave
-  S.buf = take(kBuf * 8);
-  S.A = take(kMaxBeam * 4);
-  S.kb = take(kMaxBeam * 4);
-  S.kc = take(kMaxBeam * 4);
-  S.lastk = take(kMaxBeam * 4);
-  S.offs = take(128 * 4);
-  // one entry per lane (not per beam) where lanes write without a guard: the
-  // entries past the beam absorb writes that have no effect
-  S.exm = take(kWave * 4 * 4);   // 4 words per beam: ranks 0..95 (+ padding)
-  S.exclast = take(kWave * 4);
-  S.bslot = take(kWave * 4);
-  S.htab = take(kHtab * 4);
-  S.newh = take(kMaxBeam * 4);
-  S.newlen = take(kMaxBeam * 4);
-  S.nchild = take(kMaxBeam * 4);
-  S.childc = take(kMaxBeam * kMaxBeam * 4);
-  S.scal = take(kScalCount * 4);
+  // ring of frame slots from lds::end: row, then the label -> rank map
+  S.nprod = nprod;
+  S.nslot = nprod + 1;
+  S.slot_rank = align16(L.V * 4);
+  S.slot_stride = S.slot_rank + align16(L.V);
+  take(S.nslot * S.slot_stride);
+  S.scr = take(nprod * kBuf * 8);
+  // paged token metadata, or the flat token lists when they fit
   S.tab = take(L.paged ? 2 * L.W * L.max_lp * 4 : 0);
   S.ref = take(L.paged ? L.npages * 4 : 0);
   S.fstk = take(L.paged ? L.npages * 4 : 0);
   S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
   S.tlen = take(L.paged ? 2 * kMaxBeam * 4 : 0);
-  S.fsrc = take(2 * kMaxBeam * 4);
-  S.flen = take(2 * kMaxBeam * 4);
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
-  // hand-off
-  S.flags = take((3 * kMaxSlots + 4) * 4);
-  S.ring = take(kRing * kWave * 8);
-  S.soffs = take(128 * 4);
-  S.nprod = nprod;
-  S.nslot = nprod + 1;
-  S.scr = take(nprod * kBuf * 8);
-  // ring of frame slots: row, ranked labels, label -> rank map
-  S.slot_Rc = align16(L.V * 4);
-  S.slot_Rl = S.slot_Rc + align16(kMaxK * 4);
-  S.slot_rank = S.slot_Rl + align16(kMaxK * 4);
-  S.slot_stride = S.slot_rank + align16(L.V);
-  S.slot0 = take(S.nslot * S.slot_stride);
   S.total = off;
   return S;
 }
@@ -2243,7 +2244,7 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
   P.out_lengths = out_lengths;
   P.out_scores = out_scores;
   // only the small per-row scratch is needed: rows/ranks, no frame buffers
-  const int lds = P.S.scal + kScalCount * 4;
+  const int lds = lds::scal + kScalCount * 4;
   if (int rc = launch(read_state_kernel, n_rows, 64, lds, static_cast<hipStream_t>(stream), P,
                       "read_state_kernel"))
     return rc;
