@@ -819,17 +819,30 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // lane swap; W <= NB / 2); the sorting network covers those first NB lanes
   // only (lane exchanges run on every lane, outside any lane-dependent
   // branch: a lane that is switched off supplies no value to the exchange)
-  uint64_t top;
-  {
+  //
+  // Usually the sort is not needed: when each beam's best candidate ranks in
+  // beam order (beam j's above beam j + 1's) and no beam's second candidate
+  // beats the last beam's best, the top W are exactly the beams' best
+  // candidates, already in rank order (nonzero keys are distinct, and beams
+  // without a candidate hold 0, so t1[j] >= t1[j + 1] means "in order").
+  const uint64_t t1_next = wave_shl1_u64(t1);   // lane j: t1 of lane j + 1 (0 past the end)
+  const uint64_t c1W = readlane_u64(t1, W - 1);
+  const bool in_order = __ballot(t1 < t1_next) == 0ull;
+  const bool no_second = __ballot((t2 != 0ull) & (t2 > c1W)) == 0ull;
+  uint64_t top, cW;
+  bool exact;
+  if (__builtin_expect(in_order & no_second, 1)) {
+    top = t1;
+    cW = c1W;
+    exact = true;   // every third candidate is below its beam's second
+  } else {
     constexpr int H = NB / 2;
     const uint64_t t2x = xor_lane_u64<H>(t2);
     top = wave_sort_blocks_desc<NB>(
         __builtin_amdgcn_inverse_ballot_w64(lanes_below_n(H)) ? t1 : t2x);
+    cW = readlane_u64(top, W - 1);
+    exact = __ballot(n3 > cW) == 0ull;
   }
-  const uint64_t cW =
-      ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(top >> 32), W - 1) << 32) |
-      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)top, W - 1);
-  const bool exact = __ballot(n3 > cW) == 0ull;
   PROF_MARK(3);
   uint64_t wc;  // winner of slot `lane` (composite key, 0 = none)
   uint64_t wW;  // the W-th winner (wave-uniform)

@@ -62,9 +62,24 @@ constexpr int kDppHalfMirror = 0x141;   // reverse within 8 lanes
 constexpr int kDppMirror = 0x140;       // reverse within 16 lanes
 constexpr int kDppBcast15 = 0x142;      // lane 15 of each row -> next row
 constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
+constexpr int kDppWaveShl1 = 0x130;     // lane i <- lane i + 1 across the wave
 __device__ __forceinline__ constexpr int dpp_row_shr(int n) { return 0x110 + n; }
 __device__ __forceinline__ constexpr int dpp_row_shl(int n) { return 0x100 + n; }
 __device__ __forceinline__ constexpr int dpp_row_ror(int n) { return 0x120 + n; }
+
+// Value of lane i + 1 (0 on the last lane), both halves by one DPP move each.
+__device__ __forceinline__ uint64_t wave_shl1_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, kDppWaveShl1, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), kDppWaveShl1, 0xf, 0xf, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Value of lane `src` (wave-uniform), in scalar registers.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int src) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), src) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+}
+
 
 // Value held by lane (lane ^ J), J in {1, 2, 4, 8, 16, 32}, without an LDS
 // round trip: quad permutes for 1 and 2; for 4, a row shift each way, each
