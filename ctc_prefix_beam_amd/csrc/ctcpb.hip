@@ -336,11 +336,12 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 // aligned whatever V is; the blank and the padding past V are set to -inf
 // while the frame is ranked and the blank is restored before returning):
 //   1. every lane keeps the two largest group maxima it sees;
-//   2. thr = a lower bound (exact to 24 bits of the key) of the K-th largest
+//   2. thr = a lower bound (exact to 16 bits of the key) of the K-th largest
 //      of those 128 values: at least K groups, hence K labels, reach it;
 //   3. the groups whose maximum reaches thr are listed;
 //   4. their labels at or above thr are gathered as composite keys;
-//   5. the gathered keys are ranked by counting (broadcast LDS reads).
+//   5. the gathered keys are ranked: sorted one per lane, or by counting
+//      (broadcast LDS reads) when there are more than 64.
 // Lists that do not fit the scratch fall back to a streaming top-K over the
 // whole row.
 constexpr int kMaxGroups = 256;   // listed groups (step 3), ints after the keys
@@ -400,11 +401,12 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
     }
   }
   RF_MARK(1);
-  // 2. threshold: the largest value (to 24 bits of its key, two bits per
-  // round) that at least K of the 128 values reach; never below -inf
+  // 2. threshold: the largest value (to 16 bits of its key: sign, exponent
+  // and 7 mantissa bits, two bits per round) that at least K of the 128
+  // values reach; never below -inf
   const uint32_t a = sortable(hi), b = sortable(lo);
   uint32_t thr = 0u;
-  for (int bit = 30; bit >= 8; bit -= 2) {
+  for (int bit = 30; bit >= 16; bit -= 2) {
     const uint32_t c1 = thr | (1u << bit), c2 = thr | (2u << bit), c3 = thr | (3u << bit);
     const int n1 = __popcll(__ballot(a >= c1)) + __popcll(__ballot(b >= c1));
     const int n2 = __popcll(__ballot(a >= c2)) + __popcll(__ballot(b >= c2));
@@ -482,8 +484,17 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   lds_sync();
 
   RF_MARK(4);
-  if (ng <= kMaxGroups && n >= K && n <= kMaxGather) {
-    // 5. rank by counting, two keys per lane
+  if (ng <= kMaxGroups && n >= K && n <= kWave) {
+    // 5. up to one key per lane: sort, lane r holds rank r
+    const uint64_t x = wave_sort64_desc<uint64_t>(lane < n ? scr[lane] : 0ull);
+    if (lane < K) {
+      const int c = (int)(~(uint32_t)x);
+      Rc[lane] = c;
+      Rl[lane] = row[c];
+      rank[c] = (int8_t)lane;
+    }
+  } else if (ng <= kMaxGroups && n >= K && n <= kMaxGather) {
+    // 5'. more keys: rank by counting, two keys per lane
     const int n8 = (n + 7) & ~7;
     if (n + lane < n8) scr[n + lane] = 0ull;
     lds_sync();

@@ -65,6 +65,15 @@ def test_beam_vocab_corners(W, V):
     run_both(lp, lens, W, W, what=f"W{W}V{V}")
 
 
+@pytest.mark.parametrize("W,paged", [(8, False), (16, True), (32, False)])
+def test_flat_posteriors(W, paged):
+    # no blank or token peaks (plain Gaussian logits): in about a third of the
+    # steps the beams' best candidates leave beam order or second candidates
+    # compete, and the step takes the sorting network and the selection fallbacks
+    lp, lens = synth.peaky(3, 60, 300, seed=40 + W, p_blank=0.1, blank_bias=0.0, token_bias=0.0)
+    run_both(lp, lens, W, W, paged=paged, what=f"flat W{W}")
+
+
 def test_blank_not_zero_and_truncation():
     lp, lens = synth.peaky(3, 70, 33, seed=8, p_blank=0.5, blank=32)
     run_both(lp, lens, 5, 3, blank=32, max_out_len=6, what="blank32")
