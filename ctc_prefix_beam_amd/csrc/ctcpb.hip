@@ -58,6 +58,7 @@ constexpr int kMaxRanked = 40;            // ranked labels used per frame
 constexpr int kBuf = 256;                 // candidate buffer (keys)
 constexpr int kHtab = 256;   // open-addressing table of new prefixes (>= 8 x beam)
 constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
+constexpr int kMaxPages = 32767;          // pages per row: ids are kept as 16-bit in LDS
 constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
 
 // LDS carve-up (byte offsets), computed on the host from the dimensions.
@@ -170,9 +171,9 @@ struct Ctx {
   int* nchild;
   int* childc;
   int* scal;
-  int* tab;       // paged: LDS copy of both block-table parities
+  int16_t* tab;   // paged: LDS copy of both block-table parities (page ids fit 15 bits)
   int* ref;
-  int* fstk;
+  int16_t* fstk;  // paged: free-page stack
   int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
   int* tlen;      // paged: valid leading entries of each block-table row, both parities
   int* fsrc;      // flat: [2][32] source slot of the row written at each parity (-1 unknown)
@@ -254,10 +255,11 @@ __device__ __forceinline__ bool spin_wait(int* flag, int target, bool eq, int* a
   return false;
 }
 
-__device__ __forceinline__ int tok_at(const Ctx& C, const int* tab, int parity, int slot, int pos) {
+template <typename TabT>
+__device__ __forceinline__ int tok_at(const Ctx& C, const TabT* tab, int parity, int slot, int pos) {
   const Layout& L = C.L;
   if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.ldc + pos];
-  const int page = tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
+  const int page = (int)tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
   if (page < 0) return -1;  // only after a row ran out of pages
   return C.pages[(int64_t)page * L.ps + pos % L.ps];
 }
@@ -656,7 +658,7 @@ __device__ __forceinline__ void store_seed(const Ctx& C, const Winner& w) {
         atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
       } else {
         C.ref[page] = 1;
-        C.tab[(0 * W + lane) * L.max_lp + 0] = page;
+        C.tab[(0 * W + lane) * L.max_lp + 0] = (int16_t)page;
         C.tlen[lane] = 1;
         C.pages[(int64_t)page * L.ps] = w.c;
         C.tail[(0 * W + lane) * L.ps] = w.c;
@@ -1188,8 +1190,8 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   const int pcpp = C.scal[kScalPcp0 + p];
   // pass 1: fork
   if (lane < W) {
-    int* drow = C.tab + (p * W + lane) * max_lp;
-    const int* srow = C.tab + (q * W + w.k) * max_lp;
+    int16_t* drow = C.tab + (p * W + lane) * max_lp;
+    const int16_t* srow = C.tab + (q * W + w.k) * max_lp;
     const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
     const int old_t = C.tlen[p * kMaxBeam + lane];
     int start = ((live2 >> lane) & 1u) ? (pcpp < old_t ? pcpp : old_t) : 0;
@@ -1206,9 +1208,9 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
         if (nw != kInvalidPage) atomicAdd(&C.ref[nw], 1);
         if (old != kInvalidPage && atomicSub(&C.ref[old], 1) == 1) {
           const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
-          if (at < L.npages) C.fstk[at] = old;
+          if (at < L.npages) C.fstk[at] = (int16_t)old;
         }
-        drow[qq] = nw;
+        drow[qq] = (int16_t)nw;
       }
     }
     C.tlen[p * kMaxBeam + lane] = np_new > 0 ? np_new : start;
@@ -1261,7 +1263,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
       int4* g4 = reinterpret_cast<int4*>(C.pages + (int64_t)page * ps);
       const int4* t4 = reinterpret_cast<const int4*>(dt);
       for (int j = 0; j * 4 <= off; j++) g4[j] = t4[j];
-      C.tab[(p * W + lane) * max_lp + qq] = page;
+      C.tab[(p * W + lane) * max_lp + qq] = (int16_t)page;
       if (off == 0) C.tlen[p * kMaxBeam + lane] = qq + 1;
       if (off != 0 && phys >= 0) push_old = atomicSub(&C.ref[phys], 1) == 1;
     }
@@ -1271,7 +1273,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   lds_sync();
   if (push_old) {
     const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
-    if (at < L.npages) C.fstk[at] = phys;
+    if (at < L.npages) C.fstk[at] = (int16_t)phys;
   }
   const uint64_t vm = __ballot(w.valid);
   lds_sync();
@@ -1300,7 +1302,8 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
 
 // ------------------------------------------------------------------ output --
 // N best of the current beams, (score desc, slot asc), tokens of `parity`.
-__device__ __forceinline__ void write_outputs(const Ctx& C, const Beam& b, int parity, const int* tab,
+template <typename TabT>
+__device__ __forceinline__ void write_outputs(const Ctx& C, const Beam& b, int parity, const TabT* tab,
                               int out_row) {
   const Layout& L = C.L;
   const int lane = lane_id();
@@ -1439,9 +1442,9 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.nchild = reinterpret_cast<int*>(smem + lds::nchild);
   C.childc = reinterpret_cast<int*>(smem + lds::childc);
   C.scal = reinterpret_cast<int*>(smem + lds::scal);
-  C.tab = reinterpret_cast<int*>(smem + S.tab);
+  C.tab = reinterpret_cast<int16_t*>(smem + S.tab);
   C.ref = reinterpret_cast<int*>(smem + S.ref);
-  C.fstk = reinterpret_cast<int*>(smem + S.fstk);
+  C.fstk = reinterpret_cast<int16_t*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
   C.tlen = reinterpret_cast<int*>(smem + S.tlen);
   C.fsrc = reinterpret_cast<int*>(smem + lds::fsrc);
@@ -1465,10 +1468,10 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
   int* gn = reinterpret_cast<int*>(C.base + L.o_tlen);
   const int nt = 2 * L.W * L.max_lp, nl = 2 * L.W * L.ps;
   if (to_lds) {
-    for (int i = lane; i < nt; i += kWave) C.tab[i] = gt[i];
+    for (int i = lane; i < nt; i += kWave) C.tab[i] = (int16_t)gt[i];
     for (int i = lane; i < L.npages; i += kWave) {
       C.ref[i] = gr[i];
-      C.fstk[i] = gf[i];
+      C.fstk[i] = (int16_t)gf[i];
     }
     for (int i = lane; i < nl; i += kWave) C.tail[i] = gl[i];
     for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = gn[i];
@@ -1790,7 +1793,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     if (lane < kScalCount) C.scal[lane] = 0;
     beam_fresh(b, L.blank);
     if (L.paged) {
-      for (int i = lane; i < 2 * W * L.max_lp; i += kWave) C.tab[i] = kInvalidPage;
+      for (int i = lane; i < 2 * W * L.max_lp; i += kWave) C.tab[i] = (int16_t)kInvalidPage;
       for (int i = lane; i < L.npages; i += kWave) C.ref[i] = 0;
       for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = 0;
     }
@@ -2031,9 +2034,9 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   take(S.nslot * S.slot_stride);
   S.scr = take(nprod * kBuf * 8);
   // paged token metadata, or the flat token lists when they fit
-  S.tab = take(L.paged ? 2 * L.W * L.max_lp * 4 : 0);
-  S.ref = take(L.paged ? L.npages * 4 : 0);
-  S.fstk = take(L.paged ? L.npages * 4 : 0);
+  S.tab = take(L.paged ? 2 * L.W * L.max_lp * 2 : 0);   // 16-bit page ids
+  S.ref = take(L.paged ? L.npages * 4 : 0);             // 32-bit: updated atomically
+  S.fstk = take(L.paged ? L.npages * 2 : 0);
   S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
   S.tlen = take(L.paged ? 2 * kMaxBeam * 4 : 0);
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
@@ -2045,7 +2048,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
 // More producer waves for wider vocabularies (the ranking pass grows with
 // V while the beam recursion does not), as many as the LDS budget allows.
 LdsPlan plan_lds(const Layout& L) {
-  const int pref = L.V >= 3000 ? 3 : (L.V >= 1000 ? 2 : 1);
+  const int pref = L.V >= 3000 ? 4 : (L.V >= 1000 ? 3 : 2);
   // flat token lists in LDS if they fit next to at least one producer
   for (int lds_clist = 1; lds_clist >= 0; lds_clist--) {
     if (lds_clist && L.paged) continue;
@@ -2061,7 +2064,10 @@ Layout layout_for(const Resolved& R, int cap, int cap_sel) {
   return make_layout(R.W, R.V, R.blank, cap, R.paged, R.ps, R.npages_cfg, cap_sel);
 }
 
-int check_lds(const LdsPlan& S) {
+int check_lds(const Layout& L, const LdsPlan& S) {
+  if (L.paged && L.npages > kMaxPages)
+    return fail(CTCPB_ERR_UNSUPPORTED,
+                "num_pages " + std::to_string(L.npages) + " exceeds " + std::to_string(kMaxPages));
   if (S.total > kLdsLimit)
     return fail(CTCPB_ERR_UNSUPPORTED,
                 "decoder state needs " + std::to_string(S.total) +
@@ -2147,7 +2153,7 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   Params P{};
   P.L = L;
   P.S = plan_lds(L);
-  if (int rc = check_lds(P.S)) return rc;
+  if (int rc = check_lds(P.L, P.S)) return rc;
   P.N = R.N;
   P.max_out_len = R.mol;
   if (R.threshold >= 1.0f) {
@@ -2224,7 +2230,7 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   Params P{};
   P.L = L;
   P.S = plan_lds(L);
-  if (int rc = check_lds(P.S)) return rc;
+  if (int rc = check_lds(P.L, P.S)) return rc;
   P.N = R.N;
   P.max_out_len = R.mol;
   P.lp = log_prob_chunk;
