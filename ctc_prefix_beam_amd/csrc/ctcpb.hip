@@ -2018,7 +2018,7 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
 
 int align16(int x) { return (x + 15) & ~15; }
 
-LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
+LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
   LdsPlan S{};
   int off = lds::end;
   auto take = [&](int bytes) {
@@ -2028,7 +2028,7 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
   };
   // ring of frame slots from lds::end: row, then the label -> rank map
   S.nprod = nprod;
-  S.nslot = nprod + 1;
+  S.nslot = nprod + spare;
   S.slot_rank = align16(L.V * 4);
   S.slot_stride = S.slot_rank + align16(L.V);
   take(S.nslot * S.slot_stride);
@@ -2046,18 +2046,23 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, bool clist_lds) {
 }
 
 // More producer waves for wider vocabularies (the ranking pass grows with
-// V while the beam recursion does not), as many as the LDS budget allows.
+// V while the beam recursion does not), as many as the LDS budget allows, and
+// up to three frame slots beyond one per producer so that the loader can run
+// ahead (a slot is held from its load until the beam wave has used it).
 LdsPlan plan_lds(const Layout& L) {
   const int pref = L.V >= 3000 ? 4 : (L.V >= 1000 ? 3 : 2);
   // flat token lists in LDS if they fit next to at least one producer
   for (int lds_clist = 1; lds_clist >= 0; lds_clist--) {
     if (lds_clist && L.paged) continue;
     for (int nprod = pref; nprod >= 1; nprod--) {
-      const LdsPlan S = plan_lds_with(L, nprod, lds_clist != 0);
-      if (S.total <= kLdsLimit) return S;
+      for (int spare = 3; spare >= 1; spare--) {
+        if (nprod + spare > kMaxSlots) continue;
+        const LdsPlan S = plan_lds_with(L, nprod, spare, lds_clist != 0);
+        if (S.total <= kLdsLimit) return S;
+      }
     }
   }
-  return plan_lds_with(L, 1, false);  // too large: check_lds reports it
+  return plan_lds_with(L, 1, 1, false);  // too large: check_lds reports it
 }
 
 Layout layout_for(const Resolved& R, int cap, int cap_sel) {
