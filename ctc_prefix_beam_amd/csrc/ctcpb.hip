@@ -331,6 +331,8 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 }
 
 // ------------------------------------------------------- vocabulary top-K --
+// (All LDS hand-offs inside the ranking are between lanes of the one wave,
+// whose LDS operations are performed in issue order: no waits.)
 // Ranks one frame (run by a producer wave): the best K non-blank labels by
 // (lp desc, label asc) into Rc / Rl, rank[label] = position (-1 elsewhere).
 // prevK = size of the list this slot held before (its rank entries are
@@ -376,10 +378,10 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
   const int n4 = (V + 3) >> 2;
   const float lpb = row[blank];
-  lds_sync();
+  lds_order();
   if (lane == 0) row[blank] = ninf;
   if (lane < 4 * n4 - V) row[V + lane] = ninf;
-  lds_sync();
+  lds_order();
   const float4* r4 = reinterpret_cast<const float4*>(row);
   constexpr int U = 8;  // groups per lane loaded before use
   RF_MARK(0);
@@ -431,12 +433,14 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
       const int g = base + u * kWave + lane;
       q[u] = r4[g < n4 ? g : n4 - 1];
     }
+    uint32_t m8 = 0u;   // this round's U bits (constant positions), then placed at u0
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int g = base + u * kWave + lane;
       const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      if (g < n4 && m >= tf) pm |= 1ull << (u0 + u);
+      m8 |= ((g < n4) & (m >= tf)) ? (1u << u) : 0u;
     }
+    pm |= (uint64_t)m8 << u0;
   }
   int ng;
   {
@@ -451,7 +455,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
       pos++;
     }
   }
-  lds_sync();
+  lds_order();
 
   RF_MARK(3);
   // 4. their labels at or above the threshold, placed the same way
@@ -483,7 +487,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
       n += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  lds_sync();
+  lds_order();
 
   RF_MARK(4);
   if (ng <= kMaxGroups && n >= K && n <= kWave) {
@@ -499,7 +503,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
     // 5'. more keys: rank by counting, two keys per lane
     const int n8 = (n + 7) & ~7;
     if (n + lane < n8) scr[n + lane] = 0ull;
-    lds_sync();
+    lds_order();
     const uint64_t x0 = lane < n ? scr[lane] : 0ull;
     const uint64_t x1 = lane + kWave < n ? scr[lane + kWave] : 0ull;
     int rk0 = 0, rk1 = 0;
@@ -550,9 +554,9 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
     }
   }
   RF_MARK(5);
-  lds_sync();
+  lds_order();
   if (lane == 0) row[blank] = lpb;
-  lds_sync();
+  lds_order();
   RF_MARK(6);
 }
 
@@ -1180,6 +1184,8 @@ __device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, bool nlive
 // page rebuilt from the LDS mirror of that page (no global read).  Leading
 // full pages shared by every live row of two steps ago are identical in the
 // old and the new row and are skipped.
+// (The paged metadata is touched only by this wave here, in issue order: its
+// LDS hand-offs between lanes need no waits.)
 __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w, bool nlive,
                                             int nlen) {
   const Layout& L = C.L;
@@ -1222,7 +1228,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
       for (int j = 0; j * 4 < off; j++) dt[j] = st[j];
     }
   }
-  lds_sync();
+  lds_order();
   // pass 2: append
   const bool ext = w.valid && w.c != blank;
   const int off = w.len_k % ps;
@@ -1244,14 +1250,14 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
     if (idx < avail) page = C.fstk[avail - 1 - idx];
     else if (nf + idx - avail < L.npages) page = nf + idx - avail;
   }
-  lds_sync();
+  lds_order();
   if (lane == 0) {
     const int pops = nw < avail ? nw : avail;
     C.scal[kScalFreeTop] = avail - pops;
     const int nn = nf + (nw - pops);
     C.scal[kScalNextFree] = nn < L.npages ? nn : L.npages;
   }
-  lds_sync();
+  lds_order();
   bool push_old = false;
   int* dt = C.tail + (p * W + lane) * ps;
   if (ext) dt[off] = w.c;
@@ -1270,13 +1276,13 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   } else if (inplace) {
     C.pages[(int64_t)phys * ps + off] = w.c;
   }
-  lds_sync();
+  lds_order();
   if (push_old) {
     const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
     if (at < L.npages) C.fstk[at] = (int16_t)phys;
   }
   const uint64_t vm = __ballot(w.valid);
-  lds_sync();
+  lds_order();
   if (lane == 0) {
     C.scal[kScalLive0 + p] = (int)(uint32_t)vm;
     const int used = C.scal[kScalNextFree] - C.scal[kScalFreeTop];
@@ -1295,9 +1301,9 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
     if (__ballot(!ok) != 0ull) break;
     pcp++;
   }
-  lds_sync();
+  lds_order();
   if (lane == 0) C.scal[kScalPcp0 + p] = pcp;
-  lds_sync();
+  lds_order();
 }
 
 // ------------------------------------------------------------------ output --
