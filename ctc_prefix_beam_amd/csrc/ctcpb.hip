@@ -386,9 +386,24 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   constexpr int U = 8;  // groups per lane loaded before use
   RF_MARK(0);
 
-  // 1. two largest group maxima per lane
+  // 1. two largest group maxima per lane (complete rounds of U groups per
+  // lane read at constant offsets, then the last partial round with bounds)
   float hi = ninf, lo = ninf;
-  for (int base = 0; base < n4; base += U * kWave) {
+  int base = 0;
+  for (; base + U * kWave <= n4; base += U * kWave) {
+    const float4* p4 = r4 + base + lane;
+    float4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      lo = __builtin_amdgcn_fmed3f(m, hi, lo);
+      hi = fmaxf(hi, m);
+    }
+  }
+  const int base_tail = base;
+  if (base < n4) {
     float4 q[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -426,17 +441,31 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   // wave scan places every lane's list
   int* gid = reinterpret_cast<int*>(scr + kMaxGather);
   uint64_t pm = 0ull;
-  for (int base = 0, u0 = 0; base < n4; base += U * kWave, u0 += U) {
+  int u0 = 0;   // bit of round base / (U * kWave), group u: u0 + u
+  for (base = 0; base < base_tail; base += U * kWave, u0 += U) {
+    const float4* p4 = r4 + base + lane;
     float4 q[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int g = base + u * kWave + lane;
-      q[u] = r4[g < n4 ? g : n4 - 1];
-    }
+    for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
     uint32_t m8 = 0u;   // this round's U bits (constant positions), then placed at u0
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int g = base + u * kWave + lane;
+      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+      m8 |= (m >= tf) ? (1u << u) : 0u;
+    }
+    pm |= (uint64_t)m8 << u0;
+  }
+  if (base_tail < n4) {
+    float4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = base_tail + u * kWave + lane;
+      q[u] = r4[g < n4 ? g : n4 - 1];
+    }
+    uint32_t m8 = 0u;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int g = base_tail + u * kWave + lane;
       const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
       m8 |= ((g < n4) & (m >= tf)) ? (1u << u) : 0u;
     }
