@@ -1265,8 +1265,12 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
   int phys = kInvalidPage;
   bool inplace = false;
   if (ext && off != 0) {
+    // the partial last page is the source's (the fork copied its entry), so
+    // the source's row of the previous step holds one reference and this row
+    // one: with no other reference the label can be written in place, since
+    // the source's row ends before it (and is not read again)
     phys = C.tab[(p * W + lane) * max_lp + qq];
-    inplace = phys >= 0 && C.ref[phys] == 1;
+    inplace = phys >= 0 && C.ref[phys] <= 2;
   }
   const bool need = ext && !inplace;
   const uint64_t mk = __ballot(need);
@@ -1317,10 +1321,12 @@ __device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner
     const int used = C.scal[kScalNextFree] - C.scal[kScalFreeTop];
     if (used > C.scal[kScalHigh]) C.scal[kScalHigh] = used;
   }
-  // leading full pages shared by every live row of parity p
+  // leading full pages shared by every live row of parity p.  Rows only grow
+  // at their last page and new rows extend rows of the previous step, so the
+  // previous count stays a valid bound; it is advanced every 16 steps.
   int pcp = C.scal[kScalPcp0 + q];
   const bool lv = lane < W && nlive;
-  const uint64_t lm = __ballot(lv);
+  const uint64_t lm = (step & 15) == 15 ? __ballot(lv) : 0ull;
   const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
   while (lm != 0ull && pcp < max_lp) {
     const bool full = !lv || nlen >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
