@@ -61,12 +61,12 @@ constexpr int kLdsLimit = 160 * 1024;     // LDS per CU on gfx950
 constexpr int kMaxPages = 32767;          // pages per row: ids are kept as 16-bit in LDS
 constexpr int kDefaultCapacity = 4096;    // streaming tokens per stream (sec. 11)
 
-// LDS carve-up (byte offsets), computed on the host from the dimensions.
 // LDS offsets computed on the host: the frame slots and everything whose size
 // depends on the configuration (the fixed part is the lds namespace below).
 struct LdsPlan {
   int slot_stride, slot_rank;   // frame slot: row of V floats, then the label -> rank map
   int nslot, nprod;             // slots, producer waves
+  int rk, nrk;                  // ring of ranked lists (labels, then log-probs), entries
   int scr;                      // producer scratch
   int clist, clist_lds;         // flat token lists held in LDS
   int tab, ref, fstk, tail, tlen, total;
@@ -127,10 +127,8 @@ constexpr int flen = fsrc + a16(2 * kMaxBeam * 4);
 constexpr int flags = flen + a16(2 * kMaxBeam * 4);     // hand-off flags
 constexpr int ring = flags + a16((3 * kMaxSlots + 4) * 4);  // winners ring
 constexpr int soffs = ring + a16(kRing * kWave * 8);    // store-wave scratch
-constexpr int slot_k = a16(kMaxRanked * 4);             // per-slot stride of the ranked lists
-constexpr int Rc = soffs + a16(128 * 4);                // [kMaxSlots] ranked labels
-constexpr int Rl = Rc + kMaxSlots * slot_k;             // [kMaxSlots] their log-probabilities
-constexpr int end = Rl + kMaxSlots * slot_k;
+constexpr int slot_k = a16(kMaxRanked * 4);             // ranked labels (or log-probs) of a frame
+constexpr int end = soffs + a16(128 * 4);
 }  // namespace lds
 
 struct Beam {
@@ -181,6 +179,9 @@ struct Ctx {
   int* clist;     // flat: global or LDS
   int* pages;     // paged: global
   int* wdone;     // last step whose tokens the store wave has written
+  int* release;   // last frame whose slot the beam wave has handed back
+  int frame;      // frame of the current step
+  const float* grow;  // its log-prob row in global memory (the exact fallback)
   int* abortf;
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
@@ -335,8 +336,8 @@ __device__ __forceinline__ int stream_topk(const Ctx& C, int K, int64_t n, Gen g
 // whose LDS operations are performed in issue order: no waits.)
 // Ranks one frame (run by a producer wave): the best K non-blank labels by
 // (lp desc, label asc) into Rc / Rl, rank[label] = position (-1 elsewhere).
-// prevK = size of the list this slot held before (its rank entries are
-// cleared).  The row is read as groups of four labels (the LDS row is 16-byte
+// prevK = size of the list Rc_old of the frame this slot held before (its
+// rank entries are cleared).  The row is read as groups of four labels (the LDS row is 16-byte
 // aligned whatever V is; the blank and the padding past V are set to -inf
 // while the frame is ranked and the blank is restored before returning):
 //   1. every lane keeps the two largest group maxima it sees;
@@ -365,7 +366,8 @@ constexpr int kMaxGather = 128;   // gathered keys (step 4)
 #endif
 
 __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, int prevK,
-                                           int* Rc, float* Rl, int8_t* rank, uint64_t* scr
+                                           const int* Rc_old, int* Rc, float* Rl, int8_t* rank,
+                                           uint64_t* scr
 #ifdef CTCPB_PHASE_PROF
                                            , uint64_t (&rprof)[8]
 #endif
@@ -375,7 +377,7 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
 #endif
   const int lane = lane_id();
   const float ninf = -__builtin_inff();
-  for (int r = lane; r < prevK; r += kWave) rank[Rc[r]] = -1;
+  for (int r = lane; r < prevK; r += kWave) rank[Rc_old[r]] = -1;
   const int n4 = (V + 3) >> 2;
   const float lpb = row[blank];
   lds_order();
@@ -767,6 +769,13 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float lpc_raw = row[last];
   const float lpb = row[blank];
   const int rr_raw = (int)C.rank[last];
+  // nothing else of the slot (row, label map) is read in this step: the exact
+  // fallback reads the row from global memory.  The slot goes back to the
+  // loader now (the reads above are LDS operations of this wave, performed
+  // before the flag store that follows them).
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_store(C.release, C.frame, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const float lpc = sel(has_last, lpc_raw, kNeg);
   // labels removed from a beam's ordinary list: its own last label (that is
   // the repeated-label slot) and the last label of each child (merged away).
@@ -994,7 +1003,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
   if (__builtin_expect(need_full, 0)) {
     share_beam_values();
-    full_select(C, row, par, last);
+    full_select(C, C.grow, par, last);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
     wc = lane < W ? C.buf[lane] : 0ull;
   }
@@ -1650,7 +1659,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
   int* flags = reinterpret_cast<int*>(smem + lds::flags);
   int* ready = flags;                    // [kMaxSlots]: frame held by each slot
-  int* consumed = flags + kMaxSlots;     // last frame the beam wave finished
+  int* consumed = flags + kMaxSlots;     // last frame whose slot the beam wave handed back
   int* abortf = consumed + 1;
   int* wpub = consumed + 2;              // last step whose winners are in the ring
   int* wdone = consumed + 3;             // last step the store wave has written
@@ -1659,8 +1668,13 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int2* ring = reinterpret_cast<int2*>(smem + lds::ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + lds::end + sl * S.slot_stride); };
-  auto slot_Rc = [&](int sl) { return reinterpret_cast<int*>(smem + lds::Rc + sl * lds::slot_k); };
-  auto slot_Rl = [&](int sl) { return reinterpret_cast<float*>(smem + lds::Rl + sl * lds::slot_k); };
+  // ranked list of frame f: entry f mod nrk of its own ring (nrk = nslot + nprod), so that a
+  // slot can be released as soon as the beam wave has read the few row entries it needs
+  const int nrk = S.nrk;
+  auto rk_Rc = [&](int e) { return reinterpret_cast<int*>(smem + S.rk + e * 2 * lds::slot_k); };
+  auto rk_Rl = [&](int e) {
+    return reinterpret_cast<float*>(smem + S.rk + e * 2 * lds::slot_k + lds::slot_k);
+  };
   auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + lds::end + sl * S.slot_stride + S.slot_rank); };
 
   const int step_in = STREAM ? hdr[kStep] : 0;
@@ -1733,8 +1747,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       t1 = clock64();
       pw += t1 - t0;
 #endif
-      rank_frame(slot_row(sl), V, L.blank, K, f >= nslot ? K : 0, slot_Rc(sl), slot_Rl(sl),
-                 slot_rank(sl), scr
+      // the list of frame f - nslot (this slot's previous frame) is entry
+      // (f - nslot) mod nrk = (f + nprod) mod nrk, which only frame f + nprod,
+      // ranked next by this wave, overwrites
+      rank_frame(slot_row(sl), V, L.blank, K, f >= nslot ? K : 0, rk_Rc((f + nprod) % nrk),
+                 rk_Rc(f % nrk), rk_Rl(f % nrk), slot_rank(sl), scr
 #ifdef CTCPB_PHASE_PROF
                  , rprof
 #endif
@@ -1848,7 +1865,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   bool aborted = false;
   int next_ready = -2;          // value of the next slot's flag, read one step early
   int wdone_seen = step - 1;    // store-wave progress last observed
-  for (int f = 0, sl = 0; f < nframes; f++) {
+  C.release = consumed;
+  for (int f = 0, sl = 0, ek = 0; f < nframes; f++) {
     const int sl_next = sl + 1 == nslot ? 0 : sl + 1;   // slot of frame f + 1
 #ifdef CTCPB_PHASE_PROF
     if (f == 0) {
@@ -1864,13 +1882,17 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     PROF_MARK(0);
     const float* row = slot_row(sl);
-    C.Rc = slot_Rc(sl);
-    C.Rl = slot_Rl(sl);
+    C.Rc = rk_Rc(ek);
+    C.Rl = rk_Rl(ek);
     C.rank = slot_rank(sl);
     const int t = frame_t[sl];
+    C.frame = f;
+    C.grow = lp_row + (int64_t)(STREAM ? f : t) * stride_t;
     Winner w;
     if (__builtin_expect(step == 0, 0)) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __hip_atomic_store(consumed, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       const int nb0 = W > 1 ? W - 1 : 1;
       w.valid = lane < W && b.live;
       w.k = kSeed;
@@ -1898,15 +1920,14 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
         make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
     last_t = t;
-    // the ring entry and this step's reads of the slot are LDS operations of
-    // this wave, which the LDS performs in issue order: the flags written
-    // after them (release the slot, publish the winners) are seen only after
+    // the ring entry is written by LDS operations of this wave, which the LDS
+    // performs in issue order: the flag written after them is seen only after
     // them, with no wait for their completion
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __hip_atomic_store(consumed, f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     __hip_atomic_store(wpub, step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     step++;
     sl = sl_next;
+    ek = ek + 1 == nrk ? 0 : ek + 1;
   }
   // every published step stored (bounded wait that the abort flag does not cut
   // short: the store wave drains what was published before it stops)
@@ -2073,6 +2094,8 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
   S.slot_rank = align16(L.V * 4);
   S.slot_stride = S.slot_rank + align16(L.V);
   take(S.nslot * S.slot_stride);
+  S.nrk = S.nslot + nprod;
+  S.rk = take(S.nrk * 2 * lds::slot_k);
   S.scr = take(nprod * kBuf * 8);
   // paged token metadata, or the flat token lists when they fit
   S.tab = take(L.paged ? 2 * L.W * L.max_lp * 2 : 0);   // 16-bit page ids

@@ -20,6 +20,7 @@ def gpu_offline(lp, lens, beam, nbest, blank, threshold, max_out_len, paged=Fals
     stats = dec.row_stats().cpu().numpy()
     torch.cuda.synchronize()
     assert (stats[:, 2] == 0).all(), f"row status bits set: {np.unique(stats[:, 2])}"
+    gpu_offline.last_stats = stats   # per-row counters of the call (cpb.STAT_FIELDS)
     return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
 
 

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import ctc_prefix_beam_amd as cpb
 import oracle
 import synth
 from gpu_util import assert_parity, gpu_offline
@@ -72,6 +73,30 @@ def test_flat_posteriors(W, paged):
     # compete, and the step takes the sorting network and the selection fallbacks
     lp, lens = synth.peaky(3, 60, 300, seed=40 + W, p_blank=0.1, blank_bias=0.0, token_bias=0.0)
     run_both(lp, lens, W, W, paged=paged, what=f"flat W{W}")
+
+
+def uniform_frames(B, T, V, seed, frac):
+    """Peaky frames, a fraction `frac` of them replaced by frames in which every
+    non-blank label has the same log-probability."""
+    lp, lens = synth.peaky(B, T, V, seed=seed, p_blank=0.5)
+    rng = np.random.default_rng(seed + 1)
+    pick = rng.random((B, T)) < frac
+    flat = np.full(V, np.log(0.999 / (V - 1)), np.float32)   # blank below every label
+    flat[0] = np.float32(np.log(0.001))
+    lp[pick] = flat
+    return lp, lens
+
+
+@pytest.mark.parametrize("W,paged", [(8, False), (32, True)])
+def test_exact_selection_on_uniform_frames(W, paged):
+    # labels past the ranked list tie with ranked ones, so the pruned candidate
+    # set cannot be shown to hold the top W: the full beam x vocabulary
+    # selection decides those steps (its log-probs come from the frame in
+    # global memory, the slot having been handed back at the top of the step)
+    lp, lens = uniform_frames(3, 50, 120, seed=60 + W, frac=0.3)
+    run_both(lp, lens, W, W, paged=paged, what=f"uniform W{W}")
+    fb = int(gpu_offline.last_stats[:, cpb.STAT_FIELDS.index("fallbacks")].sum())
+    assert fb > 0, "no step took the full selection"
 
 
 def test_blank_not_zero_and_truncation():

@@ -50,6 +50,28 @@ def test_chunks_equal_oracle_stream_and_offline(paged):
         assert np.array_equal(a, b)
 
 
+def test_uniform_frames_take_the_exact_selection():
+    # frames whose non-blank labels all share one log-probability force the
+    # full beam x vocabulary selection, which reads the chunk's frame from
+    # global memory
+    S, T, V, W, CH = 4, 64, 96, 12, 16
+    lp, _ = synth.peaky(S, T, V, seed=23, p_blank=0.5)
+    pick = np.random.default_rng(24).random((S, T)) < 0.3
+    flat = np.full(V, np.log(0.999 / (V - 1)), np.float32)   # blank below every label
+    flat[0] = np.float32(np.log(0.001))
+    lp[pick] = flat
+    print(f"[case] stream uniform S={S} T={T} V={V} W={W}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    for a in range(0, T, CH):
+        pool.chunk(x[:, a:a + CH])
+    got = read(pool)
+    st = pool.row_stats().cpu().numpy()
+    assert st[:, cpb.STAT_FIELDS.index("fallbacks")].sum() > 0, "no step took the full selection"
+    assert_parity(got, oracle_streams(lp, W, 4096, CH, W, T), what="stream uniform")
+
+
 def test_read_is_non_mutating_and_midway_results():
     S, T, V, W, CH = 3, 64, 100, 8, 16
     lp, _ = synth.peaky(S, T, V, seed=22)
