@@ -122,9 +122,7 @@ constexpr int newlen = newh + a16(kMaxBeam * 4);
 constexpr int nchild = newlen + a16(kMaxBeam * 4);
 constexpr int childc = nchild + a16(kMaxBeam * 4);
 constexpr int scal = childc + a16(kMaxBeam * kMaxBeam * 4);
-constexpr int fsrc = scal + a16(kScalCount * 4);        // flat copy lineage
-constexpr int flen = fsrc + a16(2 * kMaxBeam * 4);
-constexpr int flags = flen + a16(2 * kMaxBeam * 4);     // hand-off flags
+constexpr int flags = scal + a16(kScalCount * 4);      // hand-off flags
 constexpr int ring = flags + a16((3 * kMaxSlots + 4) * 4);  // winners ring
 constexpr int soffs = ring + a16(kRing * kWave * 8);    // store-wave scratch
 constexpr int slot_k = a16(kMaxRanked * 4);             // ranked labels (or log-probs) of a frame
@@ -174,8 +172,6 @@ struct Ctx {
   int16_t* fstk;  // paged: free-page stack
   int* tail;      // paged: LDS mirror of each beam's partial last page, both parities
   int* tlen;      // paged: valid leading entries of each block-table row, both parities
-  int* fsrc;      // flat: [2][32] source slot of the row written at each parity (-1 unknown)
-  int* flen;      // flat: [2][32] length of that row
   int* clist;     // flat: global or LDS
   int* pages;     // paged: global
   int* wdone;     // last step whose tokens the store wave has written
@@ -657,53 +653,101 @@ __device__ __forceinline__ uint32_t cand_id(int k, int c) {
   return ((uint32_t)k << kIdShift) | (uint32_t)c;
 }
 
+// Store-wave bookkeeping kept in registers from step to step: wave-uniform
+// masks, prefixes and free-page counters, and per lane its slot's lineage.
+// Read from LDS when the wave starts and written back after its last step
+// (the launch's epilogue and the stream state take them from there).
+struct StoreState {
+  uint32_t live0, live1;   // live slots of parity 0 / 1
+  int pre0, pre1;          // leading part shared by every live row of parity 0 / 1
+                           // (flat: tokens, paged: pages)
+  int freetop, nextfree, high;   // paged: free-stack top, next never-used page, high water
+  int len0, len1;          // this lane's slot (flat: row length, -1 unknown; paged: pages)
+  int src0, src1;          // this lane's slot: source slot of its last fork (-1 none)
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ StoreState store_state_load(const Ctx& C) {
+  const Layout& L = C.L;
+  const int lane = lane_id();
+  StoreState ss;
+  ss.live0 = (uint32_t)uni(C.scal[kScalLive0]);
+  ss.live1 = (uint32_t)uni(C.scal[kScalLive1]);
+  const int pk = L.paged ? kScalPcp0 : kScalCpl0;
+  ss.pre0 = uni(C.scal[pk]);
+  ss.pre1 = uni(C.scal[pk + 1]);
+  ss.freetop = uni(C.scal[kScalFreeTop]);
+  ss.nextfree = uni(C.scal[kScalNextFree]);
+  ss.high = uni(C.scal[kScalHigh]);
+  const bool in = lane < kMaxBeam;
+  ss.len0 = L.paged ? (in ? C.tlen[lane] : 0) : -1;
+  ss.len1 = L.paged ? (in ? C.tlen[kMaxBeam + lane] : 0) : -1;
+  ss.src0 = -1;
+  ss.src1 = -1;
+  return ss;
+}
+
+__device__ __forceinline__ void store_state_save(const Ctx& C, const StoreState& ss) {
+  const Layout& L = C.L;
+  const int lane = lane_id();
+  lds_order();
+  if (lane == 0) {
+    C.scal[kScalLive0] = (int)ss.live0;
+    C.scal[kScalLive1] = (int)ss.live1;
+    const int pk = L.paged ? kScalPcp0 : kScalCpl0;
+    C.scal[pk] = ss.pre0;
+    C.scal[pk + 1] = ss.pre1;
+    C.scal[kScalFreeTop] = ss.freetop;
+    C.scal[kScalNextFree] = ss.nextfree;
+    C.scal[kScalHigh] = ss.high;
+  }
+  if (L.paged && lane < kMaxBeam) {
+    C.tlen[lane] = ss.len0;
+    C.tlen[kMaxBeam + lane] = ss.len1;
+  }
+  lds_order();
+}
+
 // Step 0 (sec. 3.3): each seeded slot holds its one label, written fresh.
-__device__ __forceinline__ void store_seed(const Ctx& C, const Winner& w) {
+__device__ __forceinline__ void store_seed(const Ctx& C, StoreState& ss, const Winner& w) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W;
   const bool want = w.valid && w.c != L.blank;
-  if (lane < kMaxBeam) {
-    C.fsrc[lane] = -1;
-    C.flen[lane] = want ? 1 : 0;
-  }
+  ss.src0 = -1;
   if (!L.paged) {
+    ss.len0 = want ? 1 : 0;
     if (want) C.clist[(int64_t)lane * L.ldc] = w.c;
   } else {
     // one fresh page per seeded label
     const uint64_t mk = __ballot(want);
     const int idx = lanes_below(mk);
     const int nw = __popcll(mk);
-    const int avail = C.scal[kScalFreeTop];
-    const int nf = C.scal[kScalNextFree];
+    const int avail = ss.freetop, nf = ss.nextfree;
     int page = kInvalidPage;
     if (want) {
       if (idx < avail) page = C.fstk[avail - 1 - idx];
       else if (nf + idx - avail < L.npages) page = nf + idx - avail;
     }
-    lds_sync();
-    if (lane == 0) {
-      const int pops = nw < avail ? nw : avail;
-      C.scal[kScalFreeTop] = avail - pops;
-      int nn = nf + (nw - pops);
-      C.scal[kScalNextFree] = nn < L.npages ? nn : L.npages;
-    }
+    const int pops = nw < avail ? nw : avail;
+    ss.freetop = avail - pops;
+    const int nn = nf + (nw - pops);
+    ss.nextfree = nn < L.npages ? nn : L.npages;
     if (want) {
       if (page == kInvalidPage) {
         atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
       } else {
         C.ref[page] = 1;
         C.tab[(0 * W + lane) * L.max_lp + 0] = (int16_t)page;
-        C.tlen[lane] = 1;
+        ss.len0 = 1;
         C.pages[(int64_t)page * L.ps] = w.c;
         C.tail[(0 * W + lane) * L.ps] = w.c;
       }
     }
   }
-  const uint64_t lm = __ballot(lane < W && w.valid);
-  lds_sync();
-  if (lane == 0) C.scal[kScalLive0] = (int)(uint32_t)lm;
-  lds_sync();
+  ss.live0 = (uint32_t)__ballot(lane < W && w.valid);
+  lds_order();
 }
 
 // ------------------------------------------------------------ steps >= 1 ---
@@ -1129,17 +1173,18 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
 // from slot r one step earlier, the row's old content is a prefix of the new
 // one; otherwise positions below the common prefix that every live beam of
 // two steps ago shared are already in place.  Copies move 4 tokens at once.
-__device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner& w) {
+__device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int step, const Winner& w) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, blank = L.blank;
   const int p = step & 1, q = p ^ 1;
-  const uint32_t live2 = (uint32_t)C.scal[kScalLive0 + p];
-  const int cplp = C.scal[kScalCpl0 + p];
+  const uint32_t live2 = p ? ss.live1 : ss.live0;
+  const int cplp = p ? ss.pre1 : ss.pre0;
+  const int old_len = p ? ss.len1 : ss.len0;
+  const int ksrc = __shfl(p ? ss.src0 : ss.src1, w.k, 64);   // source of w.k one step earlier
   int start = 0;
   if (w.valid) {
-    const int old_len = C.flen[p * kMaxBeam + lane];
-    if (C.fsrc[q * kMaxBeam + w.k] == lane && old_len >= 0) start = old_len;
+    if (ksrc == lane && old_len >= 0) start = old_len;
     else if ((live2 >> lane) & 1u) start = cplp;
     if (start > w.len_k) start = w.len_k;
   }
@@ -1169,38 +1214,41 @@ __device__ __forceinline__ void store_flat(const Ctx& C, int step, const Winner&
   }
   wave_sync();  // the copies land before the appended label
   if (w.valid && w.c != blank) C.clist[((int64_t)(p * W + lane)) * L.ldc + w.len_k] = w.c;
-  if (lane < W) {
-    C.fsrc[p * kMaxBeam + lane] = w.valid ? w.k : -1;
-    C.flen[p * kMaxBeam + lane] = w.valid ? w.len_k + (w.c != blank ? 1 : 0) : -1;
+  const int nlen = w.valid ? w.len_k + (w.c != blank ? 1 : 0) : -1;
+  const int nsrc = w.valid ? w.k : -1;
+  const uint32_t vm = (uint32_t)__ballot(w.valid);
+  const int cplq = q ? ss.pre1 : ss.pre0;
+  if (p) {
+    ss.len1 = nlen;
+    ss.src1 = nsrc;
+    ss.live1 = vm;
+    ss.pre1 = cplq;
+  } else {
+    ss.len0 = nlen;
+    ss.src0 = nsrc;
+    ss.live0 = vm;
+    ss.pre0 = cplq;
   }
-  const uint64_t vm = __ballot(w.valid);
-  lds_sync();
-  if (lane == 0) {
-    C.scal[kScalLive0 + p] = (int)(uint32_t)vm;
-    C.scal[kScalCpl0 + p] = C.scal[kScalCpl0 + q];
-  }
-  lds_sync();
 }
 
 // Grow the common prefix of the live beams of parity p (flat store), reading
-// the next 64 positions of every live row.
-__device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, bool nlive, int nlen) {
-  const Layout& L = C.L;
+// the next 64 positions of every live row.  Not inlined: its 32 row
+// addresses would otherwise be computed (and held) on every store step.
+__device__ __attribute__((noinline)) int common_prefix_flat(const int* clist, int W, int ldc,
+                                                            int p, int cpl, bool nlive, int nlen) {
   const int lane = lane_id();
-  const int W = L.W;
-  wave_sync();
-  const int cpl = C.scal[kScalCpl0 + p];
   const uint64_t live = __ballot(lane < W && nlive);
-  if (live == 0ull) return;
+  if (live == 0ull) return cpl;
   int minlen = lane < W && nlive ? nlen : 0x7fffffff;
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) minlen = min(minlen, __shfl_xor(minlen, m, 64));
   const int pos = cpl + lane;
   const bool inside = pos < minlen;
+  const int* base = clist + (int64_t)(p * W) * ldc + pos;
   int tk[kMaxBeam];
 #pragma unroll
   for (int r = 0; r < kMaxBeam; r++)
-    tk[r] = (inside && ((live >> r) & 1ull)) ? C.clist[((int64_t)(p * W + r)) * L.ldc + pos] : -3;
+    tk[r] = (inside && ((live >> r) & 1ull)) ? base[(int64_t)r * ldc] : -3;
   const int first = __ffsll((long long)live) - 1;
   int ref = -3;
 #pragma unroll
@@ -1211,142 +1259,184 @@ __device__ __forceinline__ void advance_cpl_flat(const Ctx& C, int p, bool nlive
   for (int r = 0; r < kMaxBeam; r++)
     if ((live >> r) & 1ull) same = same && tk[r] == ref;
   const uint64_t ok = __ballot(same);
-  const int adv = ok == ~0ull ? 64 : __ffsll((long long)~ok) - 1;
-  if (lane == 0) C.scal[kScalCpl0 + p] = cpl + adv;
-  lds_sync();
+  return cpl + (ok == ~0ull ? 64 : __ffsll((long long)~ok) - 1);
+}
+
+// The LDS copy that the exact prefix comparison reads is refreshed too (any
+// older value is a lower bound: the common prefix never shrinks).
+__device__ __forceinline__ void advance_cpl_flat(const Ctx& C, StoreState& ss, int p, bool nlive,
+                                                 int nlen) {
+  wave_sync();
+  const int ncpl = common_prefix_flat(C.clist, C.L.W, C.L.ldc, p, p ? ss.pre1 : ss.pre0, nlive,
+                                      nlen);
+  if (p) ss.pre1 = ncpl;
+  else ss.pre0 = ncpl;
+  if (lane_id() == 0) C.scal[kScalCpl0 + p] = ncpl;
+}
+
+// Copies min(n, 4) int4 (n >= 1) from LDS: the loads are issued together,
+// then the stores.
+__device__ __forceinline__ void copy4_lds(int4* d, const int4* s, int n) {
+  const int4 v0 = s[0];
+  int4 v1, v2, v3;
+  if (n > 1) v1 = s[1];
+  if (n > 2) v2 = s[2];
+  if (n > 3) v3 = s[3];
+  d[0] = v0;
+  if (n > 1) d[1] = v1;
+  if (n > 2) d[2] = v2;
+  if (n > 3) d[3] = v3;
 }
 
 // Paged (sec. 3.4.5 paged variant, 4.2): fork every slot's block-table row
 // from its source (pages acquired / released by reference count), then
-// append the new label on a fresh page or on a copy of the shared partial
-// page rebuilt from the LDS mirror of that page (no global read).  Leading
-// full pages shared by every live row of two steps ago are identical in the
-// old and the new row and are skipped.
+// append the new label on a fresh page, in place, or on a copy of the shared
+// partial page rebuilt from the LDS mirror of that page (no global read).
+// Leading full pages shared by every live row of two steps ago are identical
+// in the old and the new row and are skipped.
 // (The paged metadata is touched only by this wave here, in issue order: its
 // LDS hand-offs between lanes need no waits.)
-__device__ __forceinline__ void store_paged(const Ctx& C, int step, const Winner& w, bool nlive,
-                                            int nlen) {
+__device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int step, const Winner& w,
+                                            bool nlive, int nlen) {
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
   const int p = step & 1, q = p ^ 1;
-  const uint32_t live2 = (uint32_t)C.scal[kScalLive0 + p];
-  const int pcpp = C.scal[kScalPcp0 + p];
-  // pass 1: fork
-  if (lane < W) {
-    int16_t* drow = C.tab + (p * W + lane) * max_lp;
-    const int16_t* srow = C.tab + (q * W + w.k) * max_lp;
-    const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
-    const int old_t = C.tlen[p * kMaxBeam + lane];
-    int start = ((live2 >> lane) & 1u) ? (pcpp < old_t ? pcpp : old_t) : 0;
-    // if the source was forked from this very slot one step earlier, the two
-    // rows differ at most from the old row's last page on
-    if (w.valid && C.fsrc[q * kMaxBeam + w.k] == lane && old_t > 0 && start < old_t - 1)
-      start = old_t - 1;
-    const int end = old_t > np_new ? old_t : np_new;
-#pragma unroll 4
-    for (int qq = start; qq < end; qq++) {
-      const int old = qq < old_t ? drow[qq] : kInvalidPage;
-      const int nw = qq < np_new ? srow[qq] : kInvalidPage;
-      if (old != nw) {
-        if (nw != kInvalidPage) atomicAdd(&C.ref[nw], 1);
-        if (old != kInvalidPage && atomicSub(&C.ref[old], 1) == 1) {
-          const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
-          if (at < L.npages) C.fstk[at] = (int16_t)old;
-        }
-        drow[qq] = (int16_t)nw;
-      }
-    }
-    C.tlen[p * kMaxBeam + lane] = np_new > 0 ? np_new : start;
-    C.fsrc[p * kMaxBeam + lane] = w.valid ? w.k : -1;
-    if (w.valid) {
-      const int4* st = reinterpret_cast<const int4*>(C.tail + (q * W + w.k) * ps);
-      int4* dt = reinterpret_cast<int4*>(C.tail + (p * W + lane) * ps);
-      const int off = w.len_k % ps;
-      for (int j = 0; j * 4 < off; j++) dt[j] = st[j];
-    }
-  }
-  lds_order();
-  // pass 2: append
+  const bool in = lane < W;
+  const uint32_t live2 = p ? ss.live1 : ss.live0;
+  const int pcpp = p ? ss.pre1 : ss.pre0;
+  const int old_t = in ? (p ? ss.len1 : ss.len0) : 0;
+  const int ksrc = __shfl(p ? ss.src0 : ss.src1, w.k, 64);   // source of w.k one step earlier
+  const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
   const bool ext = w.valid && w.c != blank;
-  const int off = w.len_k % ps;
-  const int qq = w.len_k / ps;
-  int phys = kInvalidPage;
-  bool inplace = false;
-  if (ext && off != 0) {
-    // the partial last page is the source's (the fork copied its entry), so
-    // the source's row of the previous step holds one reference and this row
-    // one: with no other reference the label can be written in place, since
-    // the source's row ends before it (and is not read again)
-    phys = C.tab[(p * W + lane) * max_lp + qq];
-    inplace = phys >= 0 && C.ref[phys] <= 2;
+  const int off = w.len_k % ps;   // position of the new label in its page
+  const int qq2 = w.len_k / ps;   // and that page's entry
+  int16_t* drow = C.tab + (p * W + (in ? lane : 0)) * max_lp;
+  const int16_t* srow = C.tab + (q * W + (in ? w.k : 0)) * max_lp;
+  // the page the label joins when it does not start one: the source's (the
+  // fork copies that entry), read before any row of parity p changes
+  const int phys = (ext && off != 0) ? (int)srow[qq2] : kInvalidPage;
+
+  // tail mirror: the source's partial last page (its loads issued together)
+  int* dt = C.tail + (p * W + (in ? lane : 0)) * ps;
+  {
+    const int4* st4 = reinterpret_cast<const int4*>(C.tail + (q * W + (in ? w.k : 0)) * ps);
+    int4* dt4 = reinterpret_cast<int4*>(dt);
+    const int n4 = w.valid ? (off + 3) >> 2 : 0;
+    for (int j0 = 0; j0 < n4; j0 += 4) copy4_lds(dt4 + j0, st4 + j0, n4 - j0);
   }
+
+  // pass 1: fork, two entries per round (the round count is the wave's
+  // largest, so the free-stack top stays wave-uniform)
+  int start = (in && ((live2 >> lane) & 1u)) ? (pcpp < old_t ? pcpp : old_t) : 0;
+  // if the source was forked from this very slot one step earlier, the two
+  // rows differ at most from the old row's last page on
+  if (w.valid && ksrc == lane && old_t > 0 && start < old_t - 1) start = old_t - 1;
+  const int end = in ? (old_t > np_new ? old_t : np_new) : 0;
+  int ft = ss.freetop;
+  for (int qq = start; __ballot(qq < end) != 0ull; qq += 2) {
+    const bool a0 = qq < end, a1 = qq + 1 < end;
+    const int o0 = (a0 && qq < old_t) ? (int)drow[qq] : kInvalidPage;
+    const int n0 = (a0 && qq < np_new) ? (int)srow[qq] : kInvalidPage;
+    const int o1 = (a1 && qq + 1 < old_t) ? (int)drow[qq + 1] : kInvalidPage;
+    const int n1 = (a1 && qq + 1 < np_new) ? (int)srow[qq + 1] : kInvalidPage;
+    const bool c0 = o0 != n0, c1 = o1 != n1;
+    // a page released here is held by no row of parity p^1, so no fork of
+    // this step acquires it: the order of the updates does not matter
+    if (c0 && n0 != kInvalidPage) atomicAdd(&C.ref[n0], 1);
+    if (c1 && n1 != kInvalidPage) atomicAdd(&C.ref[n1], 1);
+    const bool f0 = c0 && o0 != kInvalidPage && atomicSub(&C.ref[o0], 1) == 1;
+    const bool f1 = c1 && o1 != kInvalidPage && atomicSub(&C.ref[o1], 1) == 1;
+    if (c0) drow[qq] = (int16_t)n0;
+    if (c1) drow[qq + 1] = (int16_t)n1;
+    const uint64_t m0 = __ballot(f0);
+    const int at0 = ft + lanes_below(m0);
+    if (f0 && at0 < L.npages) C.fstk[at0] = (int16_t)o0;
+    ft += __popcll(m0);
+    const uint64_t m1 = __ballot(f1);
+    const int at1 = ft + lanes_below(m1);
+    if (f1 && at1 < L.npages) C.fstk[at1] = (int16_t)o1;
+    ft += __popcll(m1);
+  }
+  int new_t = in ? (np_new > 0 ? np_new : start) : old_t;
+  lds_order();
+
+  // pass 2: append.  With only the source's row of the previous step and this
+  // row referencing the partial page, the label is written in place: the
+  // source's row ends before it (and is not read again).
+  const bool inplace = phys >= 0 && C.ref[phys] <= 2;
   const bool need = ext && !inplace;
   const uint64_t mk = __ballot(need);
   const int idx = lanes_below(mk);
   const int nw = __popcll(mk);
-  const int avail = C.scal[kScalFreeTop];
-  const int nf = C.scal[kScalNextFree];
+  const int avail = ft, nf = ss.nextfree;
   int page = kInvalidPage;
   if (need) {
     if (idx < avail) page = C.fstk[avail - 1 - idx];
     else if (nf + idx - avail < L.npages) page = nf + idx - avail;
   }
-  lds_order();
-  if (lane == 0) {
-    const int pops = nw < avail ? nw : avail;
-    C.scal[kScalFreeTop] = avail - pops;
-    const int nn = nf + (nw - pops);
-    C.scal[kScalNextFree] = nn < L.npages ? nn : L.npages;
-  }
-  lds_order();
-  bool push_old = false;
-  int* dt = C.tail + (p * W + lane) * ps;
+  const int pops = nw < avail ? nw : avail;
+  ft = avail - pops;
+  const int nn = nf + (nw - pops);
+  ss.nextfree = nn < L.npages ? nn : L.npages;
+  lds_order();   // the pops above read the stack before the pushes below
   if (ext) dt[off] = w.c;
+  bool push_old = false;
   if (need) {
     if (page == kInvalidPage) {
       atomicOr(&C.scal[kScalStatus], kStatusOutOfPages);
     } else {
       C.ref[page] = 1;
+      // the page's tokens up to the new label, from the tail mirror
       int4* g4 = reinterpret_cast<int4*>(C.pages + (int64_t)page * ps);
       const int4* t4 = reinterpret_cast<const int4*>(dt);
-      for (int j = 0; j * 4 <= off; j++) g4[j] = t4[j];
-      C.tab[(p * W + lane) * max_lp + qq] = (int16_t)page;
-      if (off == 0) C.tlen[p * kMaxBeam + lane] = qq + 1;
+      const int n4 = (off >> 2) + 1;
+      for (int j0 = 0; j0 < n4; j0 += 4) copy4_lds(g4 + j0, t4 + j0, n4 - j0);
+      C.tab[(p * W + lane) * max_lp + qq2] = (int16_t)page;
+      if (off == 0) new_t = qq2 + 1;
       if (off != 0 && phys >= 0) push_old = atomicSub(&C.ref[phys], 1) == 1;
     }
   } else if (inplace) {
     C.pages[(int64_t)phys * ps + off] = w.c;
   }
-  lds_order();
-  if (push_old) {
-    const int at = atomicAdd(&C.scal[kScalFreeTop], 1);
-    if (at < L.npages) C.fstk[at] = (int16_t)phys;
-  }
-  const uint64_t vm = __ballot(w.valid);
-  lds_order();
-  if (lane == 0) {
-    C.scal[kScalLive0 + p] = (int)(uint32_t)vm;
-    const int used = C.scal[kScalNextFree] - C.scal[kScalFreeTop];
-    if (used > C.scal[kScalHigh]) C.scal[kScalHigh] = used;
-  }
+  const uint64_t mp = __ballot(push_old);
+  const int atp = ft + lanes_below(mp);
+  if (push_old && atp < L.npages) C.fstk[atp] = (int16_t)phys;
+  ft += __popcll(mp);
+  ss.freetop = ft;
+  const int used = ss.nextfree - ft;
+  ss.high = used > ss.high ? used : ss.high;
+  const uint32_t vm = (uint32_t)__ballot(w.valid);
+  const int nsrc = w.valid ? w.k : -1;
   // leading full pages shared by every live row of parity p.  Rows only grow
   // at their last page and new rows extend rows of the previous step, so the
   // previous count stays a valid bound; it is advanced every 16 steps.
-  int pcp = C.scal[kScalPcp0 + q];
-  const bool lv = lane < W && nlive;
-  const uint64_t lm = (step & 15) == 15 ? __ballot(lv) : 0ull;
-  const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
-  while (lm != 0ull && pcp < max_lp) {
-    const bool full = !lv || nlen >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
-    const int e = (lv && full) ? C.tab[(p * W + lane) * max_lp + pcp] : kInvalidPage;
-    const int first = __shfl(e, first_live, 64);
-    const bool ok = full && (!lv || e == first);
-    if (__ballot(!ok) != 0ull) break;
-    pcp++;
+  int pcp = q ? ss.pre1 : ss.pre0;
+  if ((step & 15) == 15) {
+    lds_order();
+    const bool lv = in && nlive;
+    const uint64_t lm = __ballot(lv);
+    const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
+    while (lm != 0ull && pcp < max_lp) {
+      const bool full = !lv || nlen >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
+      const int e = (lv && full) ? (int)drow[pcp] : kInvalidPage;
+      const int first = __shfl(e, first_live, 64);
+      const bool ok = full && (!lv || e == first);
+      if (__ballot(!ok) != 0ull) break;
+      pcp++;
+    }
   }
-  lds_order();
-  if (lane == 0) C.scal[kScalPcp0 + p] = pcp;
+  if (p) {
+    ss.len1 = new_t;
+    ss.src1 = nsrc;
+    ss.live1 = vm;
+    ss.pre1 = pcp;
+  } else {
+    ss.len0 = new_t;
+    ss.src0 = nsrc;
+    ss.live0 = vm;
+    ss.pre0 = pcp;
+  }
   lds_order();
 }
 
@@ -1497,8 +1587,6 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.fstk = reinterpret_cast<int16_t*>(smem + S.fstk);
   C.tail = reinterpret_cast<int*>(smem + S.tail);
   C.tlen = reinterpret_cast<int*>(smem + S.tlen);
-  C.fsrc = reinterpret_cast<int*>(smem + lds::fsrc);
-  C.flen = reinterpret_cast<int*>(smem + lds::flen);
   C.clist = S.clist_lds ? reinterpret_cast<int*>(smem + S.clist)
                         : reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
@@ -1782,11 +1870,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (wave == store_wave) {
     // ---------------------------------------------------------- store wave
     C.offs = reinterpret_cast<int*>(smem + lds::soffs);
-    for (int i = lane; i < 2 * kMaxBeam; i += kWave) {
-      C.fsrc[i] = -1;
-      C.flen[i] = -1;
-    }
-    lds_sync();
+    StoreState ss{};
 #ifdef CTCPB_PHASE_PROF
     uint64_t sw = 0, sk = 0, t0 = clock64();
 #endif
@@ -1805,14 +1889,18 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       w.len_k = w.valid ? rec.y : 0;
       const bool nlive = w.valid;
       const int nlen = w.valid ? w.len_k + (w.c != L.blank ? 1 : 0) : 0;
+      // (the beam wave's set-up of the LDS state is visible once its first
+      // step is published)
+      if (f == 0) ss = store_state_load(C);
       if (step == 0) {
-        store_seed(C, w);
+        store_seed(C, ss, w);
       } else if (L.paged) {
-        store_paged(C, step, w, nlive, nlen);
+        store_paged(C, ss, step, w, nlive, nlen);
       } else {
-        store_flat(C, step, w);
-        if ((step & 15) == 15) advance_cpl_flat(C, step & 1, nlive, nlen);
+        store_flat(C, ss, step, w);
+        if ((step & 15) == 15) advance_cpl_flat(C, ss, step & 1, nlive, nlen);
       }
+      if (f == nframes - 1) store_state_save(C, ss);
       lds_sync();
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): global token writes done
       flag_store(wdone, step);
