@@ -68,6 +68,10 @@ def lib():
         L.oracle_stream_reset.argtypes = [p]
         L.oracle_stream_feed.restype = i32
         L.oracle_stream_feed.argtypes = [p, p, i64, i32]
+        L.oracle_stream_feed_ex.restype = i32
+        L.oracle_stream_feed_ex.argtypes = [p, p, i64, i32, p, i32]
+        L.oracle_stream_frame_count.restype = i32
+        L.oracle_stream_frame_count.argtypes = [p]
         L.oracle_stream_step_count.restype = i32
         L.oracle_stream_step_count.argtypes = [p]
         L.oracle_stream_read.restype = None
@@ -123,7 +127,9 @@ def decode(log_prob: np.ndarray, seq_lengths, beam: int, nbest: int | None = Non
 
 
 class Stream:
-    """One streaming decode (frames fed in chunks; no frame skipping)."""
+    """One streaming decode: frames fed in chunks, optionally gated by a
+    speech mask (0 = skip the frame) and numbered from a caller-given frame
+    index."""
 
     def __init__(self, beam: int, vocab: int, blank: int = 0, capacity: int = 4096):
         self.beam, self.vocab = beam, vocab
@@ -131,11 +137,31 @@ class Stream:
         if not self._h:
             raise ValueError("oracle_stream_new: invalid argument")
 
-    def feed(self, frames: np.ndarray) -> int:
+    def feed(self, frames: np.ndarray, is_speech=None, start_frame: int | None = None) -> int:
+        """Chunk frame f is frame number start + f (start = start_frame, or the
+        frames given so far); it is decoded unless is_speech[f] == 0."""
         frames = np.ascontiguousarray(frames, dtype=np.float32)
         n, V = frames.shape
         assert V == self.vocab
-        return lib().oracle_stream_feed(self._h, _ptr(frames), V, n)
+        if is_speech is None and start_frame is None:
+            return lib().oracle_stream_feed(self._h, _ptr(frames), V, n)
+        mask = None
+        if is_speech is not None:
+            mask = np.ascontiguousarray(is_speech, dtype=np.uint8)
+            assert mask.shape == (n,)
+        start = -1 if start_frame is None else int(start_frame)
+        assert start_frame is None or start >= 0
+        return lib().oracle_stream_feed_ex(self._h, _ptr(frames), V, n,
+                                           None if mask is None else _ptr(mask), start)
+
+    def step_at(self, frame: np.ndarray, frame_index: int) -> int:
+        """One frame decoded as frame number frame_index (the page's per-frame
+        step with the caller's actual frame index)."""
+        return self.feed(np.asarray(frame, np.float32).reshape(1, -1), None, frame_index)
+
+    @property
+    def frames(self) -> int:
+        return lib().oracle_stream_frame_count(self._h)
 
     @property
     def step(self) -> int:

@@ -36,6 +36,12 @@
  *     is ever cut; max_out_len only truncates the copy into out_tokens while
  *     out_lengths reports the full count (sec. 13).  Streaming, a stream
  *     decodes at most `capacity` frames; later frames are ignored (sec. 13).
+ *   - Streaming frame indices: chunk frame f is frame start + f, where start
+ *     is the caller's start frame when given (sec. 9, ctc_beam_search_chunk's
+ *     start_frame_idx, or the per-frame step's actual_frame_index) and the
+ *     count of frames given so far otherwise.  A frame that the speech mask
+ *     marks 0 is not decoded but is counted, so the next decoded frame takes
+ *     the gap rule above, exactly as after an offline skip.
  *   - Final hypotheses are reported in (score desc, slot asc) order; positions
  *     past a hypothesis' length and dead hypotheses' tokens are -1.
  */
@@ -148,6 +154,7 @@ struct OracleStream {
     int beam, vocab, blank, capacity;
     int step;    /* number of frames decoded so far */
     int last_t;  /* frame index of the last decoded frame */
+    int frames;  /* frames given so far, decoded or not: the next frame's index */
     Slot *cur, *nxt;
     float *ptable, *ptablen; /* [beam][vocab] */
     int64_t *order;          /* candidate ids for the sort */
@@ -195,6 +202,7 @@ static void reset_empty(OracleStream *st)
     }
     st->step = 0;
     st->last_t = -1;
+    st->frames = 0;
 }
 
 OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
@@ -401,17 +409,35 @@ static void decode_frame(OracleStream *st, const float *lp, int t)
     st->step++;
 }
 
-int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames)
+int oracle_stream_feed_ex(OracleStream *st, const float *frames, int64_t stride_t, int n_frames,
+                          const unsigned char *is_speech, int start_frame)
 {
-    /* Streaming (sec. 8): every frame the caller gives is decoded, frame
-     * index = running count; frames past the capacity are ignored (sec. 13). */
+    /* Streaming (sec. 8): chunk frame f is frame number start + f of the
+     * stream, start being the caller's start_frame (sec. 9
+     * ctc_beam_search_chunk) or, when that is negative, the count of frames
+     * given so far.  It is decoded unless is_speech marks it 0 (the page's
+     * is_speech_mask, sec. 12: a skipped frame bypasses the decoder) or the
+     * stream has reached its capacity (sec. 13).  A frame decoded after
+     * skipped ones takes the gap rule through its frame index. */
+    if (start_frame >= 0)
+        st->frames = start_frame;
     for (int f = 0; f < n_frames; f++) {
+        if (is_speech && !is_speech[f])
+            continue;
         if (st->step >= st->capacity)
             break;
-        decode_frame(st, frames + (int64_t)f * stride_t, st->step == 0 ? 0 : st->last_t + 1);
+        decode_frame(st, frames + (int64_t)f * stride_t, st->frames + f);
     }
+    st->frames += n_frames;
     return st->step;
 }
+
+int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames)
+{
+    return oracle_stream_feed_ex(st, frames, stride_t, n_frames, NULL, -1);
+}
+
+int oracle_stream_frame_count(const OracleStream *st) { return st->frames; }
 
 static int cmp_slots_score(const void *a, const void *b, const Slot *slots)
 {

@@ -27,12 +27,16 @@ int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int
                   int blank, float threshold, int max_out_len, int *out_tokens,
                   int *out_lengths, float *out_scores);
 
-/* Streaming: one stream, frames fed in chunks, no frame skipping. */
+/* Streaming: one stream, frames fed in chunks (optionally gated by a speech
+ * mask, and from a caller-given frame index). */
 typedef struct OracleStream OracleStream;
 OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity);
 void oracle_stream_free(OracleStream *st);
 void oracle_stream_reset(OracleStream *st);
 int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames);
+int oracle_stream_feed_ex(OracleStream *st, const float *frames, int64_t stride_t, int n_frames,
+                          const unsigned char *is_speech, int start_frame);
+int oracle_stream_frame_count(const OracleStream *st);
 int oracle_stream_step_count(const OracleStream *st);
 void oracle_stream_read(const OracleStream *st, int nbest, int max_out_len, int *out_tokens,
                         int *out_lengths, float *out_scores);

@@ -289,3 +289,103 @@ def test_fresh_stream_reads_empty(oracle_lib):
     st = oracle_lib.Stream(3, 5, 0)
     t, l, s = st.read(3, 4)
     assert list(l) == [0, 0, 0] and s[0] == 0.0 and (s[1:] == NEG).all() and (t == -1).all()
+
+
+# ------------------------------------------- streaming with a speech mask --
+# The page's is_speech_mask (sec. 9, 12): a frame marked 0 bypasses the
+# decoder; the next decoded frame carries the gap through its frame index.
+def test_masked_stream_gap_golden(oracle_lib):
+    # the hand-worked frame-skip case, its skipped frame given as a 0 flag
+    g = json.load(open(os.path.join(GOLDEN, "gap_two_skips.json")))
+    lp = f32log(g["probs"])
+    st = oracle_lib.Stream(g["beam"], g["vocab"], g["blank"])
+    st.feed(lp[:2], is_speech=[1, 0])
+    st.feed(lp[2:], is_speech=[1, 1])
+    assert st.step == 3 and st.frames == 4
+    toks, L, S = st.read(g["nbest"], 4)
+    hyps = live_hyps(toks, L, S)
+    assert [list(h) for h, _ in hyps] == g["expected_tokens"]
+    for (_, s), p in zip(hyps, g["expected_scores_log"]):
+        assert s == pytest.approx(math.log(p), abs=1e-6)
+
+
+def test_masked_stream_gap_golden_by_frame_index(oracle_lib):
+    # the same case through the per-frame step with the caller's frame index
+    g = json.load(open(os.path.join(GOLDEN, "gap_two_skips.json")))
+    lp = f32log(g["probs"])
+    st = oracle_lib.Stream(g["beam"], g["vocab"], g["blank"])
+    for t in (0, 2, 3):
+        st.step_at(lp[t], t)
+    toks, L, S = st.read(g["nbest"], 4)
+    assert [list(h) for h, _ in live_hyps(toks, L, S)] == g["expected_tokens"]
+
+
+@pytest.mark.parametrize("theta,chunk", [(0.9, 7), (0.99, 16), (0.5, 5)])
+def test_masked_stream_equals_offline_selection(oracle_lib, theta, chunk):
+    # a mask computed as the offline filter (blank lp below log(theta), sec.
+    # 3.5) must give the offline decode of that selection, bit for bit
+    lp, lens = synth.peaky(3, 90, 13, seed=31, p_blank=0.6)
+    off = oracle_lib.decode(lp, lens, 5, 5, 0, theta, 90)
+    for b in range(3):
+        sel = oracle_lib.select_frames(lp[b], 90, 0, theta)
+        mask = np.zeros(90, np.uint8)
+        mask[sel] = 1
+        assert 0 < mask.sum() < 90
+        st = oracle_lib.Stream(5, 13, 0)
+        for a in range(0, 90, chunk):
+            st.feed(lp[b, a:a + chunk], is_speech=mask[a:a + chunk])
+        assert st.step == len(sel) and st.frames == 90
+        t, l, s = st.read(5, 90)
+        assert (t == off[0][b]).all() and (l == off[1][b]).all() and (s == off[2][b]).all()
+
+
+def test_mask_of_ones_and_frame_indices_match_plain_feed(oracle_lib):
+    lp, _ = synth.peaky(1, 48, 11, seed=32)
+    plain = oracle_lib.Stream(4, 11, 0)
+    ones = oracle_lib.Stream(4, 11, 0)
+    steps = oracle_lib.Stream(4, 11, 0)
+    for a in range(0, 48, 16):
+        plain.feed(lp[0, a:a + 16])
+        ones.feed(lp[0, a:a + 16], is_speech=np.ones(16, np.uint8))
+    for t in range(48):
+        steps.step_at(lp[0, t], t)
+    ref = plain.read(4, 48)
+    for other in (ones, steps):
+        got = other.read(4, 48)
+        assert all((x == y).all() for x, y in zip(got, ref))
+        assert other.frames == 48
+
+
+def test_start_frame_equals_masked_gap(oracle_lib):
+    # a chunk fed from frame 20 after frames 0..15 is the same stream as one
+    # whose frames 16..19 were marked 0
+    lp, _ = synth.peaky(1, 36, 9, seed=33)
+    a = oracle_lib.Stream(4, 9, 0)
+    a.feed(lp[0, :16])
+    a.feed(lp[0, 16:], start_frame=20)
+    assert a.frames == 40 and a.step == 36
+    b = oracle_lib.Stream(4, 9, 0)
+    b.feed(lp[0, :16])
+    b.feed(np.concatenate([np.zeros((4, 9), np.float32), lp[0, 16:]]),
+           is_speech=np.r_[np.zeros(4), np.ones(20)].astype(np.uint8))
+    assert b.frames == 40 and b.step == 36
+    assert all((x == y).all() for x, y in zip(a.read(4, 36), b.read(4, 36)))
+    # and it differs from the gap-free stream (the gap rule took effect)
+    c = oracle_lib.Stream(4, 9, 0)
+    c.feed(lp[0])
+    assert not all((x == y).all() for x, y in zip(a.read(4, 36), c.read(4, 36)))
+
+
+def test_all_zero_mask_decodes_nothing(oracle_lib):
+    lp, _ = synth.peaky(1, 20, 7, seed=34)
+    st = oracle_lib.Stream(3, 7, 0)
+    st.feed(lp[0, :10], is_speech=np.zeros(10, np.uint8))
+    assert st.step == 0 and st.frames == 10
+    fresh = oracle_lib.Stream(3, 7, 0).read(3, 5)
+    assert all((x == y).all() for x, y in zip(st.read(3, 5), fresh))
+    # the first decoded frame then has index 10 > 0: seeded under the gap rule
+    st.feed(lp[0, 10:])
+    ref = oracle_lib.Stream(3, 7, 0)
+    for t in range(10, 20):
+        ref.step_at(lp[0, t], t)
+    assert all((x == y).all() for x, y in zip(st.read(3, 10), ref.read(3, 10)))
