@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libctcpb.so")
 
 FLAT, PAGED = 0, 1
 EXPORTS = ("ctcpb_workspace_size", "ctcpb_decode_offline", "ctcpb_state_size",
-           "ctcpb_stream_init", "ctcpb_stream_reset", "ctcpb_stream_chunk", "ctcpb_read_state",
+           "ctcpb_stream_init", "ctcpb_stream_reset", "ctcpb_stream_chunk",
+           "ctcpb_stream_chunk_ex", "ctcpb_stream_step", "ctcpb_read_state",
            "ctcpb_row_stats", "ctcpb_last_error", "ctcpb_version")
 STAT_FIELDS = ("frames", "selected", "status", "pages_high", "fallbacks", "verifies", "common_prefix",
                "shared_pages")
@@ -73,6 +74,8 @@ def lib():
         L.ctcpb_stream_init.argtypes = [cfgp, p, sz, i32, p]
         L.ctcpb_stream_reset.argtypes = [cfgp, p, sz, i32, p, i32, p]
         L.ctcpb_stream_chunk.argtypes = [cfgp, p, sz, i32, p, i64, i64, i32, p, i32, p]
+        L.ctcpb_stream_chunk_ex.argtypes = [cfgp, p, sz, i32, p, i64, i64, i32, p, p, p, i32, p]
+        L.ctcpb_stream_step.argtypes = [cfgp, p, sz, i32, p, i64, p, p, i32, p]
         L.ctcpb_read_state.argtypes = [cfgp, p, sz, i32, p, i32, p, p, p, p]
         L.ctcpb_row_stats.argtypes = [cfgp, p, sz, i32, i32, p, p]
         for name in EXPORTS[:-2]:  # all but the two string getters
@@ -195,9 +198,13 @@ class StreamPool:
         _check(lib().ctcpb_stream_reset(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
                                         self.num_streams, _ptr(rows), n, _stream(stream)))
 
-    def chunk(self, log_prob_chunk: torch.Tensor, rows: torch.Tensor | None = None, stream=None):
+    def chunk(self, log_prob_chunk: torch.Tensor, rows: torch.Tensor | None = None, stream=None,
+              is_speech: torch.Tensor | None = None, start_frame: torch.Tensor | None = None):
         """log_prob_chunk: (n_rows, chunk_T, V) float32 on the GPU; row i
-        continues stream rows[i] (default: stream i)."""
+        continues stream rows[i] (default: stream i).  is_speech: optional
+        (n_rows, chunk_T) uint8 on the GPU, 0 = skip the frame; start_frame:
+        optional (n_rows,) int32 on the GPU, the number of each row's first
+        frame (default: the stream's own frame count)."""
         if log_prob_chunk.dtype != torch.float32 or log_prob_chunk.dim() != 3:
             raise ValueError("log_prob_chunk must be a 3-D float32 tensor")
         if log_prob_chunk.stride(2) != 1:
@@ -207,10 +214,45 @@ class StreamPool:
             raise ValueError("vocabulary size differs from the pool's")
         if rows is not None and (rows.dtype != torch.int32 or rows.numel() != n):
             raise ValueError("rows must be an int32 tensor with one entry per chunk row")
-        _check(lib().ctcpb_stream_chunk(
+        if is_speech is not None and (is_speech.dtype != torch.uint8 or
+                                      tuple(is_speech.shape) != (n, T) or
+                                      not is_speech.is_contiguous()):
+            raise ValueError("is_speech must be a contiguous (n_rows, chunk_T) uint8 tensor")
+        if start_frame is not None and (start_frame.dtype != torch.int32 or
+                                        start_frame.numel() != n):
+            raise ValueError("start_frame must be an int32 tensor with one entry per chunk row")
+        if is_speech is None and start_frame is None:
+            _check(lib().ctcpb_stream_chunk(
+                ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
+                _ptr(log_prob_chunk), log_prob_chunk.stride(0), log_prob_chunk.stride(1), T,
+                _ptr(rows), n, _stream(stream)))
+        else:
+            _check(lib().ctcpb_stream_chunk_ex(
+                ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
+                _ptr(log_prob_chunk), log_prob_chunk.stride(0), log_prob_chunk.stride(1), T,
+                _ptr(is_speech), _ptr(start_frame), _ptr(rows), n, _stream(stream)))
+
+    def step(self, log_prob_frame: torch.Tensor, frame_index: torch.Tensor | None = None,
+             rows: torch.Tensor | None = None, stream=None):
+        """One frame per row: log_prob_frame (n_rows, V) float32 on the GPU,
+        decoded as frame number frame_index[i] (int32 on the GPU; default: the
+        stream's own frame count) of stream rows[i]."""
+        if log_prob_frame.dtype != torch.float32 or log_prob_frame.dim() != 2:
+            raise ValueError("log_prob_frame must be a 2-D float32 tensor")
+        if log_prob_frame.stride(1) != 1:
+            raise ValueError("log_prob_frame must have unit stride over the vocabulary")
+        n, V = log_prob_frame.shape
+        if V != self.vocab:
+            raise ValueError("vocabulary size differs from the pool's")
+        if rows is not None and (rows.dtype != torch.int32 or rows.numel() != n):
+            raise ValueError("rows must be an int32 tensor with one entry per row")
+        if frame_index is not None and (frame_index.dtype != torch.int32 or
+                                        frame_index.numel() != n):
+            raise ValueError("frame_index must be an int32 tensor with one entry per row")
+        _check(lib().ctcpb_stream_step(
             ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
-            _ptr(log_prob_chunk), log_prob_chunk.stride(0), log_prob_chunk.stride(1), T,
-            _ptr(rows), n, _stream(stream)))
+            _ptr(log_prob_frame), log_prob_frame.stride(0), _ptr(frame_index), _ptr(rows), n,
+            _stream(stream)))
 
     def row_stats(self, stream=None) -> torch.Tensor:
         """Per-stream counters, int32 (num_streams, 8): see STAT_FIELDS."""

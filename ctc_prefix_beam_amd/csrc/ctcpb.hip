@@ -86,6 +86,9 @@ struct Params {
   int num_rows;       // streaming: streams in the blob
   const int* seq_lengths;
   const int* rows;
+  const uint8_t* speech;    // streaming: [rows of the call][T] frame flags (0 = skip), or null
+  const int* start_frame;   // streaming: [rows of the call] index of the chunk's first frame,
+                            // or null (the stream's own count)
   char* state;
   int* out_tokens;
   int* out_lengths;
@@ -123,7 +126,7 @@ constexpr int nchild = newlen + a16(kMaxBeam * 4);
 constexpr int childc = nchild + a16(kMaxBeam * 4);
 constexpr int scal = childc + a16(kMaxBeam * kMaxBeam * 4);
 constexpr int flags = scal + a16(kScalCount * 4);      // hand-off flags
-constexpr int ring = flags + a16((3 * kMaxSlots + 4) * 4);  // winners ring
+constexpr int ring = flags + a16((3 * kMaxSlots + 5) * 4);  // winners ring
 constexpr int soffs = ring + a16(kRing * kWave * 8);    // store-wave scratch
 constexpr int slot_k = a16(kMaxRanked * 4);             // ranked labels (or log-probs) of a frame
 constexpr int end = soffs + a16(128 * 4);
@@ -1662,12 +1665,13 @@ __device__ __forceinline__ void scal_from_header(const Ctx& C) {
   }
 }
 
-__device__ __forceinline__ void scal_to_header(const Ctx& C, int step, int last_t) {
+__device__ __forceinline__ void scal_to_header(const Ctx& C, int step, int last_t, int frames) {
   const int lane = lane_id();
   if (lane == 0) {
     int* h = C.hdr;
     h[kStep] = step;
     h[kLastT] = last_t;
+    if (frames >= 0) h[kFrames] = frames;
     h[kFreeTop] = C.scal[kScalFreeTop];
     h[kNextFree] = C.scal[kScalNextFree];
     h[kStatus] = C.scal[kScalStatus];
@@ -1753,6 +1757,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* wdone = consumed + 3;             // last step the store wave has written
   int* loaded = consumed + 4;            // [kMaxSlots]: frame whose row each slot holds
   int* frame_t = loaded + kMaxSlots;     // [kMaxSlots]: time index of that frame
+  int* nspeech = frame_t + kMaxSlots;    // streaming: frames of the chunk to decode
   int2* ring = reinterpret_cast<int2*>(smem + lds::ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + lds::end + sl * S.slot_stride); };
@@ -1779,10 +1784,24 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     *wpub = step_in - 1;
     *wdone = step_in - 1;
   }
+  // streaming: chunk frame f is frame number frame0 + f; with a speech mask
+  // only the frames it flags are decoded (sec. 9 is_speech_mask, start_frame_idx)
+  const int frame0 = STREAM ? (P.start_frame ? P.start_frame[row_i] : hdr[kFrames]) : 0;
+  const uint8_t* speech = STREAM && P.speech ? P.speech + (int64_t)row_i * P.T : nullptr;
   int nframes;
   if (STREAM) {
+    int avail = P.T;
+    if (speech) {
+      if (threadIdx.x == 0) *nspeech = 0;
+      __syncthreads();
+      int cnt = 0;
+      for (int f = (int)threadIdx.x; f < P.T; f += (int)blockDim.x) cnt += speech[f] != 0;
+      if (cnt) atomicAdd(nspeech, cnt);
+      __syncthreads();
+      avail = *nspeech;
+    }
     nframes = L.cap - step_in;
-    nframes = nframes < 0 ? 0 : (nframes > P.T ? P.T : nframes);
+    nframes = nframes < 0 ? 0 : (nframes > avail ? avail : nframes);
   } else {
     nframes = hdr[kNSel];
   }
@@ -1809,10 +1828,37 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     // Copies each frame's row into its slot as soon as the slot is free and
     // flags it once the copy has landed.  It is the only wave that copies
     // global memory into LDS, so no other wave's LDS reads wait on a copy.
+    int cur = 0;            // streaming with a mask: next chunk frame to look at
+    int blk_base = -64;     // the 64 flags read last, as a bit mask
+    uint64_t blk = 0ull;
     for (int f = 0, sl = 0; f < nframes; f++, sl = sl + 1 == nslot ? 0 : sl + 1) {
       if (!spin_wait(consumed, f - nslot, false, abortf)) break;
-      const int t = STREAM ? step_in + f : sel[f];
-      row_fetch_async(lp_row + (int64_t)(STREAM ? f : t) * stride_t, slot_row(sl), V, vec4);
+      int c = f;   // chunk frame decoded as step f
+      if (STREAM && speech) {
+        // the next flagged frame (nframes counts flagged frames only, so one
+        // exists; the scan still stops at the end of the chunk)
+        c = -1;
+        while (cur < P.T) {
+          const int base = cur & ~63;
+          if (base != blk_base) {
+            blk = __ballot(base + lane < P.T && speech[base + lane] != 0);
+            blk_base = base;
+          }
+          const uint64_t m = blk & (~0ull << (cur & 63));
+          if (m) {
+            c = base + __ffsll((long long)m) - 1;
+            break;
+          }
+          cur = base + 64;
+        }
+        if (c < 0) {
+          flag_store(abortf, 1);
+          break;
+        }
+        cur = c + 1;
+      }
+      const int t = STREAM ? frame0 + c : sel[f];
+      row_fetch_async(lp_row + (int64_t)(STREAM ? c : t) * stride_t, slot_row(sl), V, vec4);
       if (lane == 0) frame_t[sl] = t;
       row_fetch_wait();
       flag_publish_lds(&loaded[sl], f);
@@ -2025,7 +2071,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
     for (int i = 0; i < kProfSlots; i++) dst[i] = C.prof[i];
-    C.hdr[15] = (int)C.stat_multi;   // unused header word, diagnostics only
+    if (!STREAM) C.hdr[kFrames] = (int)C.stat_multi;   // diagnostics only (offline)
   }
 #endif
   lds_sync();
@@ -2037,12 +2083,12 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       wave_sync();
       clist_io(C, b, (step - 1) & 1, false);
     }
-    scal_to_header(C, step, last_t);
+    scal_to_header(C, step, last_t, STREAM ? frame0 + P.T : -1);
   } else {
     wave_sync();
     const int parity = step > 0 ? (step - 1) & 1 : 0;
     write_outputs(C, b, parity, C.tab, srow);
-    scal_to_header(C, step, last_t);
+    scal_to_header(C, step, last_t, STREAM ? frame0 + P.T : -1);
   }
 }
 
@@ -2098,7 +2144,7 @@ __global__ __launch_bounds__(64) void row_stats_kernel(Params P) {
   const int* h = reinterpret_cast<const int*>(P.state + (int64_t)i * P.L.row_bytes);
   int* o = P.out_lengths + (int64_t)i * 8;
   o[0] = h[kStep];
-  o[1] = h[kNSel];
+  o[1] = P.L.cap_sel > 0 ? h[kNSel] : h[kFrames];
   o[2] = h[kStatus];
   o[3] = h[kPagesHigh];
   o[4] = h[kFallbacks];
@@ -2369,10 +2415,11 @@ int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
   return ok();
 }
 
-int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
-                       int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
-                       int64_t stride_t, int32_t chunk_T, const int32_t* rows, int32_t n_rows,
-                       void* stream) {
+int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                          int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
+                          int64_t stride_t, int32_t chunk_T, const uint8_t* is_speech,
+                          const int32_t* start_frame, const int32_t* rows, int32_t n_rows,
+                          void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams || chunk_T < 0)
@@ -2396,6 +2443,8 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
   P.T = chunk_T;
   P.num_rows = num_streams;
   P.rows = rows;
+  P.speech = is_speech;
+  P.start_frame = start_frame;
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
@@ -2403,6 +2452,24 @@ int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
   return ok();
+}
+
+int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                       int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
+                       int64_t stride_t, int32_t chunk_T, const int32_t* rows, int32_t n_rows,
+                       void* stream) {
+  return ctcpb_stream_chunk_ex(cfg, state, state_bytes, num_streams, log_prob_chunk, stride_row,
+                               stride_t, chunk_T, nullptr, nullptr, rows, n_rows, stream);
+}
+
+int ctcpb_stream_step(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                      int32_t num_streams, const float* log_prob_frame, int64_t stride_row,
+                      const int32_t* frame_index, const int32_t* rows, int32_t n_rows,
+                      void* stream) {
+  Resolved R;
+  if (int rc = resolve(cfg, R)) return rc;
+  return ctcpb_stream_chunk_ex(cfg, state, state_bytes, num_streams, log_prob_frame, stride_row,
+                               R.V, 1, nullptr, frame_index, rows, n_rows, stream);
 }
 
 int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_bytes,

@@ -41,6 +41,7 @@ enum HeaderField {
   kPagesHigh,     // paged: high-water mark of pages in use
   kFallbacks,     // steps that needed the full beam x vocab selection
   kVerifies,      // exact token comparisons made for the merge test
+  kFrames,        // streaming: frames given so far, decoded or not (the next frame's index)
   // words 32..47: optional per-phase cycle counters of a diagnostics build
 };
 

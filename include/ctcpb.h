@@ -112,11 +112,42 @@ int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
  * device float32, finite) continues stream rows[i] (NULL: stream i; distinct
  * indices required).  Every frame is decoded (no skipping); frames past a
  * stream's capacity are ignored.  The state stays on the device; nothing is
- * read back. */
+ * read back.  Same as ctcpb_stream_chunk_ex with no mask and no start frame. */
 int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
                        int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
                        int64_t stride_t, int32_t chunk_T, const int32_t* rows, int32_t n_rows,
                        void* stream);
+
+/* ctcpb_stream_chunk gated by a speech mask and/or numbered from caller-given
+ * frame indices (sec. 9 ctc_beam_search_chunk with is_speech_mask and
+ * start_frame_idx; sec. 12: skipped frames bypass the decoder).
+ *   is_speech    device uint8 [n_rows][chunk_T] (row i for stream rows[i]), or
+ *                NULL: frame t of row i is decoded iff is_speech[i*chunk_T + t]
+ *                is nonzero; other frames are skipped but counted.
+ *   start_frame  device int32 [n_rows] (>= 0), or NULL: frame t of row i is
+ *                frame number start_frame[i] + t of its stream; NULL uses the
+ *                stream's own count of frames given so far.
+ * A decoded frame whose number exceeds the previous decoded one by more than
+ * one takes the gap rule of an offline skip (sec. 3.3 / 3.4 need_add_blank).
+ * Afterwards a stream's frame count is its chunk's first frame number plus
+ * chunk_T.  Frames past a stream's capacity (in decoded frames) are ignored.
+ * Other arguments and errors as ctcpb_stream_chunk. */
+int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                          int32_t num_streams, const float* log_prob_chunk, int64_t stride_row,
+                          int64_t stride_t, int32_t chunk_T, const uint8_t* is_speech,
+                          const int32_t* start_frame, const int32_t* rows, int32_t n_rows,
+                          void* stream);
+
+/* One frame for n_rows streams (sec. 9 ctc_beam_search_step with
+ * actual_frame_index): row i of log_prob_frame (device float32, element
+ * (i, c) at i*stride_row + c) is decoded as frame number frame_index[i] of
+ * stream rows[i] (device int32 [n_rows], >= 0; NULL: the stream's own frame
+ * count).  Equivalent to ctcpb_stream_chunk_ex with chunk_T = 1,
+ * is_speech = NULL and start_frame = frame_index. */
+int ctcpb_stream_step(const ctcpb_config* cfg, void* state, size_t state_bytes,
+                      int32_t num_streams, const float* log_prob_frame, int64_t stride_row,
+                      const int32_t* frame_index, const int32_t* rows, int32_t n_rows,
+                      void* stream);
 
 /* Report the current N best of the listed streams (sec. 8 read_state) without
  * changing them.  Outputs as in ctcpb_decode_offline with batch = n_rows. */
@@ -128,7 +159,8 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
 /* Per-row counters a decode left in an offline workspace (max_T = the max_T
  * of that decode) or in a streaming state blob (max_T = 0), for diagnostics:
  * out (device int32 [num_rows][8]) receives per row
- *   [0] frames decoded  [1] frames selected (offline)  [2] status bits
+ *   [0] frames decoded  [1] offline: frames selected; streaming: frames
+ *   given so far (the next frame's number)  [2] status bits
  *   (1 = a paged row ran out of pages)  [3] paged: most pages in use at once
  *   [4] steps that needed the full beam x vocab selection  [5] exact token
  *   comparisons made for the merge test  [6] common token prefix of the live

@@ -117,6 +117,18 @@ def test_stream_argument_errors_need_no_device(L):
     assert L.ctcpb_stream_chunk(ctypes.byref(c), p, need, 4, p, 16 * 512, 100, 16, n, 4, n) == 1
     assert L.ctcpb_stream_chunk(ctypes.byref(c), p, need, 4, p, 16 * 512, 512, -1, n, 4, n) == 1
     assert L.ctcpb_stream_chunk(ctypes.byref(c), p, need, 4, p, 16 * 512, 512, 0, n, 4, n) == 0
+    # the gated / indexed variants validate the same way
+    assert L.ctcpb_stream_chunk_ex(ctypes.byref(c), p, need, 4, p, 16 * 512, 512, 16, p, p, n, 5,
+                                   n) == 1
+    assert L.ctcpb_stream_chunk_ex(ctypes.byref(c), p, need - 1, 4, p, 16 * 512, 512, 16, p, n,
+                                   n, 4, n) == 2
+    assert L.ctcpb_stream_chunk_ex(ctypes.byref(c), p, need, 4, n, 16 * 512, 512, 16, p, n, n, 4,
+                                   n) == 1
+    assert L.ctcpb_stream_chunk_ex(ctypes.byref(c), p, need, 4, p, 16 * 512, 512, 0, p, p, n, 4,
+                                   n) == 0
+    assert L.ctcpb_stream_step(ctypes.byref(c), p, need, 4, p, 512, p, n, 5, n) == 1
+    assert L.ctcpb_stream_step(ctypes.byref(c), p, need - 1, 4, p, 512, p, n, 4, n) == 2
+    assert L.ctcpb_stream_step(ctypes.byref(c), n, need, 4, p, 512, p, n, 4, n) == 1
     assert L.ctcpb_read_state(ctypes.byref(c), p, need - 1, 4, n, 4, p, p, p, n) == 2
     assert L.ctcpb_read_state(ctypes.byref(c), n, need, 4, n, 4, p, p, p, n) == 1
 

@@ -128,3 +128,113 @@ def test_uneven_chunks_equal_single_chunk():
     for o in outs[1:]:
         for a, b in zip(outs[0], o):
             assert np.array_equal(a, b)
+
+
+# ------------------------------------ speech mask and caller frame indices --
+def oracle_masked(lp, mask, W, capacity, chunk, nbest, mol, start=None):
+    outs, frames = [], []
+    for s in range(lp.shape[0]):
+        st = oracle.Stream(W, lp.shape[2], 0, capacity)
+        for a in range(0, lp.shape[1], chunk):
+            sf = None if (start is None or a > 0) else int(start[s])
+            st.feed(lp[s, a:a + chunk], None if mask is None else mask[s, a:a + chunk], sf)
+        outs.append(st.read(nbest, mol))
+        frames.append(st.frames)
+    return tuple(np.stack([o[i] for o in outs]) for i in range(3)), frames
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_speech_mask_equals_oracle(paged):
+    S, T, V, W, CH = 6, 64, 96, 8, 16
+    lp, _ = synth.peaky(S, T, V, seed=41, p_blank=0.6)
+    rng = np.random.default_rng(42)
+    mask = (rng.random((S, T)) < 0.7).astype(np.uint8)
+    mask[1] = 0                       # a stream that decodes nothing
+    mask[2, :20] = 0                  # first decoded frame > 0: seeded under the gap rule
+    print(f"[case] stream mask S={S} T={T} V={V} W={W} paged={paged}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, paged=paged)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    m = torch.from_numpy(mask).cuda()
+    for a in range(0, T, CH):
+        pool.chunk(x[:, a:a + CH], is_speech=m[:, a:a + CH].contiguous())
+    got = read(pool)
+    ref, frames = oracle_masked(lp, mask, W, 4096, CH, W, T)
+    assert_parity(got, ref, what="stream mask")
+    st = pool.row_stats().cpu().numpy()
+    assert list(st[:, 0]) == list(mask.sum(1))          # steps decoded
+    assert list(st[:, 1]) == frames == [T] * S          # frames given
+
+
+def test_mask_from_threshold_equals_offline():
+    # the page's recipe: a mask computed from the blank log-prob against the
+    # threshold turns the stream into the offline decode of that selection
+    S, T, V, W, theta = 4, 80, 64, 6, 0.9
+    lp, _ = synth.peaky(S, T, V, seed=43, p_blank=0.6)
+    mask = np.zeros((S, T), np.uint8)
+    for s in range(S):
+        mask[s, oracle.select_frames(lp[s], T, 0, theta)] = 1
+    assert 0 < mask.sum() < S * T
+    print(f"[case] stream threshold mask S={S} T={T} V={V} W={W}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    m = torch.from_numpy(mask).cuda()
+    for a in range(0, T, 16):
+        pool.chunk(x[:, a:a + 16], is_speech=m[:, a:a + 16].contiguous())
+    got = read(pool)
+    off = gpu_offline(lp, np.full(S, T, np.int32), W, W, 0, theta, T)
+    for a, b in zip(got, off):
+        assert np.array_equal(a, b)
+    assert_parity(got, oracle.decode(lp, np.full(S, T), W, W, 0, theta, T), what="thr mask")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_per_frame_step_with_frame_index(paged):
+    S, T, V, W = 3, 40, 50, 5
+    lp, _ = synth.peaky(S, T, V, seed=44)
+    rng = np.random.default_rng(45)
+    # per stream, increasing frame numbers with gaps of 1..3
+    idx = np.cumsum(rng.integers(1, 4, size=(S, T)), axis=1).astype(np.int32) - 1
+    print(f"[case] stream step S={S} T={T} V={V} W={W} paged={paged}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, paged=paged)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    fi = torch.from_numpy(idx).cuda()
+    for t in range(T):
+        pool.step(x[:, t], frame_index=fi[:, t].contiguous())
+    got = read(pool)
+    outs = []
+    for s in range(S):
+        st = oracle.Stream(W, V, 0)
+        for t in range(T):
+            st.step_at(lp[s, t], int(idx[s, t]))
+        outs.append(st.read(W, T))
+    ref = tuple(np.stack([o[i] for o in outs]) for i in range(3))
+    assert_parity(got, ref, what="step")
+    st = pool.row_stats().cpu().numpy()
+    assert list(st[:, 1]) == list(idx[:, -1] + 1)
+
+
+def test_start_frame_capacity_and_row_subsets():
+    S, T, V, W, CH, CAP = 4, 48, 40, 4, 16, 30
+    lp, _ = synth.peaky(S, T, V, seed=46)
+    mask = (np.random.default_rng(47).random((S, T)) < 0.8).astype(np.uint8)
+    start = np.array([0, 5, 100, 7], np.int32)
+    print(f"[case] stream start frames S={S} T={T} V={V} W={W} cap={CAP}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, capacity=CAP)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    m = torch.from_numpy(mask).cuda()
+    rows = torch.tensor([2, 0, 3, 1], dtype=torch.int32, device="cuda")
+    perm = [2, 0, 3, 1]   # chunk row i continues stream perm[i]
+    for a in range(0, T, CH):
+        sf = torch.from_numpy(start[perm]).cuda() if a == 0 else None
+        pool.chunk(x[perm, a:a + CH], rows=rows, is_speech=m[perm, a:a + CH].contiguous(),
+                   start_frame=sf)
+    got = read(pool)
+    ref, frames = oracle_masked(lp, mask, W, CAP, CH, W, T, start=start)
+    assert_parity(got, ref, what="start frames")
+    st = pool.row_stats().cpu().numpy()
+    assert list(st[:, 0]) == [min(CAP, int(mask[s].sum())) for s in range(S)]
+    assert list(st[:, 1]) == frames == list(start + T)
