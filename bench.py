@@ -92,10 +92,12 @@ def cpu_baseline(x, lens, wl, seconds):
                       f"oracle process per row ({wall:.1f} s)"}
 
 
-def streaming_latency(reps=3, seed=0):
+def streaming_latency(reps=3, seed=0, mask_theta=None):
     """256 streams, 64 chunks of 16 frames: per-chunk latency of one
     ctcpb_stream_chunk call advancing every stream (device time by HIP events,
-    host time from enqueue to completion)."""
+    host time from enqueue to completion).  With mask_theta, each chunk is
+    gated by a speech mask computed once on the GPU as blank log-prob <
+    log(mask_theta) (frames flagged 0 are skipped)."""
     import numpy as np
     import torch
 
@@ -107,15 +109,19 @@ def streaming_latency(reps=3, seed=0):
     # allocated for the longest stream it must hold
     pool = cpb.StreamPool(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, max_out_len=wl.T,
                                             capacity=wl.T), wl.V, wl.B)
+    mask = None
+    if mask_theta is not None:
+        mask = (x[:, :, 0] < float(np.float32(np.log(mask_theta)))).to(torch.uint8)
+        masks = [mask[:, a:a + wl.chunk].contiguous() for a in range(0, wl.T, wl.chunk)]
     dev_ms, host_ms = [], []
     for rep in range(reps + 1):
         pool.reset()
         torch.cuda.synchronize()
-        for a in range(0, wl.T, wl.chunk):
+        for ci, a in enumerate(range(0, wl.T, wl.chunk)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             t = time.perf_counter()
             e0.record()
-            pool.chunk(x[:, a:a + wl.chunk])
+            pool.chunk(x[:, a:a + wl.chunk], is_speech=None if mask is None else masks[ci])
             e1.record()
             torch.cuda.synchronize()
             if rep > 0:  # the first pass is a warm-up
@@ -123,6 +129,14 @@ def streaming_latency(reps=3, seed=0):
                 dev_ms.append(e0.elapsed_time(e1))
     d = np.array(dev_ms)
     h = np.array(host_ms)
+    if mask is not None:
+        frac = float(mask.float().mean())
+        return {"mask": f"blank log-prob < log({mask_theta}), computed once on the GPU",
+                "speech_fraction": round(frac, 4),
+                "p50_chunk_ms": round(float(np.percentile(d, 50)), 4),
+                "p90_chunk_ms": round(float(np.percentile(d, 90)), 4),
+                "decoded_frames_per_s": round(float(wl.B * wl.chunk * frac / (d.mean() / 1e3)), 1),
+                "chunks_timed": int(d.size)}
     return {"workload": "stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks, "
                         "capacity 1024",
             "p50_chunk_ms": round(float(np.percentile(d, 50)), 4),
@@ -269,6 +283,8 @@ def main():
     if not args.no_extras:
         log("[bench] streaming latency, 256 streams")
         result["streaming"] = streaming_latency()
+        log("[bench] streaming latency with a speech mask")
+        result["streaming"]["speech_masked"] = streaming_latency(mask_theta=0.7)
     if args.compare:
         log("[bench] other workloads")
         result["other_workloads"] = other_workloads()
