@@ -1720,6 +1720,10 @@ __global__ __launch_bounds__(256) void select_kernel(Params P) {
   if (tid == 0) hdr[kNSel] = cnt;
 }
 
+}  // namespace ctcpb
+#include "wide.h"
+namespace ctcpb {
+
 // Offline rows (STREAM = false) or streaming chunk rows (STREAM = true).  One
 // workgroup per row, four roles:
 //   wave 0       the serial beam recursion, frame by frame; it publishes each
@@ -2181,8 +2185,6 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
   if (!cfg) return fail(CTCPB_ERR_INVALID, "config is NULL");
   if (cfg->beam < 1 || cfg->beam > 128)
     return fail(CTCPB_ERR_INVALID, "beam must be in [1, 128], got " + std::to_string(cfg->beam));
-  if (cfg->beam > kMaxBeam)
-    return fail(CTCPB_ERR_UNSUPPORTED, "beam > 32 is not supported by this build");
   if (cfg->nbest < 1 || cfg->nbest > cfg->beam)
     return fail(CTCPB_ERR_INVALID, "nbest must be in [1, beam]");
   if (cfg->vocab < 2) return fail(CTCPB_ERR_INVALID, "vocab must be >= 2");
@@ -2213,6 +2215,19 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
 }
 
 int align16(int x) { return (x + 15) & ~15; }
+
+// Beams above 32 run on the wide offline kernel, which keeps flat token lists:
+// paged storage and streaming need the narrow decoder.
+int check_wide(const Resolved& R, bool streaming) {
+  if (R.W <= kMaxBeam) return CTCPB_OK;
+  if (streaming)
+    return fail(CTCPB_ERR_UNSUPPORTED, "streaming supports beam <= 32 (this beam: " +
+                                           std::to_string(R.W) + ")");
+  if (R.paged)
+    return fail(CTCPB_ERR_UNSUPPORTED, "paged storage supports beam <= 32 (this beam: " +
+                                           std::to_string(R.W) + "); use flat storage");
+  return CTCPB_OK;
+}
 
 LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
   LdsPlan S{};
@@ -2318,6 +2333,7 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
                          size_t* out_bytes) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, false)) return rc;
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
@@ -2328,6 +2344,7 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
 int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, true)) return rc;
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (num_streams < 0) return fail(CTCPB_ERR_INVALID, "num_streams must be >= 0");
   const Layout L = layout_for(R, R.cap_stream, 0);
@@ -2350,13 +2367,19 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   if (max_T > 0 && (stride_t < R.V || (batch > 1 && stride_b < (int64_t)max_T * 0)))
     return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
   if (!aligned16(workspace)) return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (int rc = check_wide(R, false)) return rc;
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
   if (workspace_bytes < (size_t)batch * (size_t)L.row_bytes)
     return fail(CTCPB_ERR_TOO_SMALL, "workspace smaller than ctcpb_workspace_size");
+  const bool wide_path = R.W > kMaxBeam;
   Params P{};
   P.L = L;
-  P.S = plan_lds(L);
-  if (int rc = check_lds(P.L, P.S)) return rc;
+  if (!wide_path) {
+    P.S = plan_lds(L);
+    if (int rc = check_lds(P.L, P.S)) return rc;
+  } else if (wide::lds_bytes(R.V) > kLdsLimit) {
+    return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
+  }
   P.N = R.N;
   P.max_out_len = R.mol;
   if (R.threshold >= 1.0f) {
@@ -2381,6 +2404,12 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   P.vec4 = aligned16(log_prob) && (R.V % 4 == 0) && (stride_b % 4 == 0) && (stride_t % 4 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
+  if (wide_path) {
+    if (int rc = launch(wide::decode_wide_kernel, batch, wide::kNT, wide::lds_bytes(R.V), st, P,
+                        "decode_wide_kernel"))
+      return rc;
+    return ok();
+  }
   if (int rc = launch(decode_kernel_for<false>(R.W), batch, 64 * (3 + P.S.nprod), P.S.total,
                       st, P, "decode_kernel"))
     return rc;
@@ -2396,6 +2425,7 @@ int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
                        int32_t num_streams, const int32_t* rows, int32_t n_rows, void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
   if (n_rows == 0) return ok();
@@ -2422,6 +2452,7 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
                           void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams || chunk_T < 0)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams and chunk_T >= 0");
   if (n_rows == 0 || chunk_T == 0) return ok();
@@ -2478,6 +2509,7 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
                      void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
   if (n_rows == 0) return ok();
@@ -2509,6 +2541,7 @@ int ctcpb_row_stats(const ctcpb_config* cfg, const void* buf, size_t buf_bytes, 
                     int32_t max_T, int32_t* out, void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
+  if (int rc = check_wide(R, max_T == 0)) return rc;
   if (num_rows < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "num_rows and max_T must be >= 0");
   if (num_rows == 0) return ok();
   if (!buf || !out) return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
