@@ -147,6 +147,38 @@ def streaming_latency(reps=3, seed=0, mask_theta=None):
             "chunks_timed": int(d.size)}
 
 
+def wide_beams():
+    """Beams above 32 (the wide offline decoder, flat tokens) on the bpe1024
+    inputs (B=64, T=875, V=1024, ragged lengths), beam 64 and 128."""
+    import numpy as np
+    import torch
+
+    import ctc_prefix_beam_amd as cpb
+    import synth
+    wl = synth.WORKLOADS["bpe1024"]
+    x, lens = wl.make_device(0, "cuda")
+    lens_d = torch.from_numpy(lens).cuda()
+    res = {"workload": "bpe1024 inputs: B=64 T=875 V=1024 ragged 300..875, threshold 0.999, "
+                       "flat tokens"}
+    for W in (64, 128):
+        dec = cpb.OfflineDecoder(cpb.DecoderConfig(beam=W, nbest=W,
+                                                   blank_threshold=wl.threshold,
+                                                   max_out_len=wl.max_out_len))
+        out = dec.decode(x, lens_d)
+        wall, kms = time_offline(dec, x, lens_d, out, 3, 1)
+        st = dec.row_stats().cpu().numpy()
+        steps = int(st[:, 0].sum())
+        ms = float(np.mean(kms))
+        alg = steps * algorithmic_bytes_per_frame(wl.V, W)
+        res[f"beam{W}"] = {"ms_per_decode": round(ms, 3),
+                           "frames_per_s": round(wl.B * wl.T / (ms / 1e3), 1),
+                           "decoded_frames_per_s": round(steps / (ms / 1e3), 1),
+                           "us_per_step": round(ms * 1e3 / max(1, int(st[:, 0].max())), 2),
+                           "hbm_frac": round(alg / (ms / 1e3) / 8.0e12, 5)}
+    del x
+    return res
+
+
 def other_workloads():
     """Every offline workload once more (flat storage, and vocab5000 paged),
     for the comparison table; not part of the default run."""
@@ -285,6 +317,8 @@ def main():
         result["streaming"] = streaming_latency()
         log("[bench] streaming latency with a speech mask")
         result["streaming"]["speech_masked"] = streaming_latency(mask_theta=0.7)
+        log("[bench] wide beams (64, 128)")
+        result["wide_beams"] = wide_beams()
     if args.compare:
         log("[bench] other workloads")
         result["other_workloads"] = other_workloads()

@@ -2377,8 +2377,11 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   if (!wide_path) {
     P.S = plan_lds(L);
     if (int rc = check_lds(P.L, P.S)) return rc;
-  } else if (wide::lds_bytes(R.V) > kLdsLimit) {
-    return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
+  } else {
+    // two frame rows in LDS when they fit (the next frame is fetched ahead)
+    P.S.nslot = wide::lds_bytes(R.V, 2) <= kLdsLimit ? 2 : 1;
+    if (wide::lds_bytes(R.V, P.S.nslot) > kLdsLimit)
+      return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
   }
   P.N = R.N;
   P.max_out_len = R.mol;
@@ -2405,8 +2408,8 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
   if (wide_path) {
-    if (int rc = launch(wide::decode_wide_kernel, batch, wide::kNT, wide::lds_bytes(R.V), st, P,
-                        "decode_wide_kernel"))
+    if (int rc = launch(wide::decode_wide_kernel, batch, wide::kNT,
+                        wide::lds_bytes(R.V, P.S.nslot), st, P, "decode_wide_kernel"))
       return rc;
     return ok();
   }

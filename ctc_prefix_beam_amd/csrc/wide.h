@@ -27,14 +27,15 @@ constexpr int kMaxW = 128;
 constexpr int kMaxK = 2 * kMaxW + 2;      // ranked labels per frame
 constexpr int kExw = (kMaxK + 31) / 32;   // exclusion words per beam
 constexpr int kItems = 36;                // candidates per thread (>= (W(W+1)/2 + 4W) / kNT)
+constexpr int kCBuf = 1024;               // candidates at or above the sample bound
 
 // LDS: fixed part at compile-time offsets, then the row and the label map.
 namespace off {
 constexpr int a16(int x) { return (x + 15) & ~15; }
 constexpr int Rc = 0;                                   // int [kMaxK]
 constexpr int Rl = Rc + a16(kMaxK * 4);                 // float [kMaxK]
-constexpr int kb64 = Rl + a16(kMaxK * 4);               // u64 [kMaxK]: gathered keys
-constexpr int win = kb64 + a16(kMaxK * 8);              // u64 [kMaxW]: winners in rank order
+constexpr int kb64 = Rl + a16(kMaxK * 4);               // u64 [kMaxK + 8]: gathered keys
+constexpr int win = kb64 + a16((kMaxK + 8) * 8);        // u64 [kMaxW]: winners in rank order
 constexpr int f_pb = win + a16(kMaxW * 8);              // per beam, float
 constexpr int f_pnb = f_pb + kMaxW * 4;
 constexpr int f_sc = f_pnb + kMaxW * 4;
@@ -58,14 +59,19 @@ constexpr int i_src = i_bslot + kMaxW * 4;              // [2][kMaxW] copy sourc
 constexpr int i_flen = i_src + 2 * kMaxW * 4;           // [2][kMaxW] row length per parity
 constexpr int i_offs = i_flen + 2 * kMaxW * 4;          // [kMaxW + 1] prefix sums
 constexpr int u64_head = i_offs + a16((kMaxW + 1) * 4); // u64 [kMaxW]: each beam's best
-constexpr int exm = u64_head + kMaxW * 8;               // u32 [kMaxW][kExw]
-constexpr int hist = exm + a16(kMaxW * kExw * 4);       // int [256]
+constexpr int tag = u64_head + kMaxW * 8;               // u64 [kMaxW]: (length, hash) of live slots
+constexpr int exm = tag + kMaxW * 8;                    // u32 [kMaxW][kExw]
+constexpr int cbuf = exm + a16(kMaxW * kExw * 4);       // u64 [kCBuf]: candidates
+constexpr int hist = cbuf + kCBuf * 8;                  // int [256]
 constexpr int sh = hist + 256 * 4;                      // int [16] block scalars
 constexpr int end = sh + 16 * 4;
 }  // namespace off
 
-// Bytes of LDS for vocabulary V (row of floats, then a 16-bit label -> rank map).
-inline int lds_bytes(int V) { return off::end + off::a16(V * 4) + off::a16(V * 2); }
+// Bytes of LDS for vocabulary V: nbuf rows of floats (2: the next frame is
+// fetched while this one is decoded), then a 16-bit label -> rank map.
+inline int lds_bytes(int V, int nbuf) {
+  return off::end + nbuf * off::a16(V * 4) + off::a16(V * 2);
+}
 
 // Block-wide: the kth largest (1-based) nonzero 64-bit key of the items, by
 // radix select over 8-bit digits; 0 when fewer than kth keys are nonzero.
@@ -92,32 +98,42 @@ __device__ uint64_t kth_largest(int n, int kth, Gen gen, int* hist, int* sh) {
       const int incl = wave_incl_scan(s);
       const int ex = incl - s;
       const int total = __shfl(incl, 63, 64);
-      int d = -1, above = 0;
       if (ex < need && incl >= need) {
-        if (ex + c0 >= need) { d = d0; above = ex; }
-        else if (ex + c0 + c1 >= need) { d = d0 - 1; above = ex + c0; }
-        else if (ex + c0 + c1 + c2 >= need) { d = d0 - 2; above = ex + c0 + c1; }
-        else { d = d0 - 3; above = ex + c0 + c1 + c2; }
+        int d, above, in;
+        if (ex + c0 >= need) { d = d0; above = ex; in = c0; }
+        else if (ex + c0 + c1 >= need) { d = d0 - 1; above = ex + c0; in = c1; }
+        else if (ex + c0 + c1 + c2 >= need) { d = d0 - 2; above = ex + c0 + c1; in = c2; }
+        else { d = d0 - 3; above = ex + c0 + c1 + c2; in = c3; }
         sh[0] = d;
         sh[1] = above;
+        sh[2] = in;
       }
       if (lane == 0 && total < need) sh[0] = -1;
     }
     __syncthreads();
-    const int d = sh[0], above = sh[1];
+    const int d = sh[0], above = sh[1], in = sh[2];
     __syncthreads();
     if (d < 0) return 0ull;
     prefix |= (uint64_t)d << shift;
     need -= above;
+    // once the score half is fixed, a group of keys sharing it that is needed
+    // whole ends the search: every key at or above prefix is taken
+    if (shift == 32 && in == need) return prefix;
   }
   return prefix;
 }
 
-// Rank of buf[i] among the n distinct keys of buf (0 = largest), by counting.
-__device__ __forceinline__ int rank_of(const uint64_t* buf, int n, int i) {
-  const uint64_t x = buf[i];
+// Number of keys of buf[0, n) above x.  buf is 16-byte aligned and zero from
+// n up to the next multiple of 8 (zeros are below every key counted); eight
+// keys are read per round, four 16-byte loads in flight.
+__device__ __forceinline__ int count_above(const uint64_t* buf, int n, uint64_t x) {
+  const ulonglong2* b2 = reinterpret_cast<const ulonglong2*>(buf);
   int r = 0;
-  for (int j = 0; j < n; j++) r += buf[j] > x ? 1 : 0;
+  for (int j = 0; j < n; j += 8) {
+    const ulonglong2 a = b2[j / 2], b = b2[j / 2 + 1], c = b2[j / 2 + 2], d = b2[j / 2 + 3];
+    r += (a.x > x) + (a.y > x) + (b.x > x) + (b.y > x) + (c.x > x) + (c.y > x) + (d.x > x) +
+         (d.y > x);
+  }
   return r;
 }
 
@@ -160,11 +176,16 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   int* s_flen = reinterpret_cast<int*>(smem + off::i_flen);
   int* s_offs = reinterpret_cast<int*>(smem + off::i_offs);
   uint64_t* s_head = reinterpret_cast<uint64_t*>(smem + off::u64_head);
+  uint64_t* s_tag = reinterpret_cast<uint64_t*>(smem + off::tag);
   uint32_t* s_exm = reinterpret_cast<uint32_t*>(smem + off::exm);
+  uint64_t* cbuf = reinterpret_cast<uint64_t*>(smem + off::cbuf);
   int* hist = reinterpret_cast<int*>(smem + off::hist);
   int* sh = reinterpret_cast<int*>(smem + off::sh);
-  float* row = reinterpret_cast<float*>(smem + off::end);
-  int16_t* rmap = reinterpret_cast<int16_t*>(smem + off::end + off::a16(V * 4));
+  const int nbuf = P.S.nslot;   // frame rows in LDS: 1 or 2
+  float* rows = reinterpret_cast<float*>(smem + off::end);
+  const int rstride = off::a16(V * 4) / 4;
+  int16_t* rmap = reinterpret_cast<int16_t*>(smem + off::end + nbuf * off::a16(V * 4));
+  const int wave = tid >> 6;
 
   const int nframes = hdr[kNSel];
   const int K = min(V - 1, 2 * W + 2);
@@ -185,8 +206,12 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     s_src[tid] = s_src[kMaxW + tid] = -1;
     s_flen[tid] = s_flen[kMaxW + tid] = -1;
   }
+  // with two row buffers, wave 3 fetches frame f + 1 while frame f is decoded
+  if (nbuf == 2 && wave == 3 && nframes > 0)
+    row_fetch_async(lp_row + (int64_t)sel[0] * P.stride_t, rows, V, P.vec4);
   int last_t = -1, step = 0, prevK = 0, nver = 0;
   if (tid == 0) {
+    sh[6] = sh[7] = 0;   // common token prefix of the live rows of parity 0 / 1
     sh[9] = 0;    // exact token comparisons
     sh[10] = 0;   // status bits
   }
@@ -197,15 +222,24 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     const bool g = t > last_t + 1;    // frames skipped before t (step 0: t > 0)
     const int p = step & 1, q = p ^ 1;
     // ---- stage the row; clear the previous list's label map entries
-    const float* gr = lp_row + (int64_t)t * P.stride_t;
-    if (P.vec4) {
-      for (int i = tid; i < (V >> 2); i += kNT)
-        reinterpret_cast<float4*>(row)[i] = reinterpret_cast<const float4*>(gr)[i];
+    float* row = rows + (nbuf == 2 ? (f & 1) * rstride : 0);
+    if (nbuf == 2) {
+      if (wave == 3) row_fetch_wait();
     } else {
-      for (int i = tid; i < V; i += kNT) row[i] = gr[i];
+      const float* gr = lp_row + (int64_t)t * P.stride_t;
+      if (P.vec4) {
+        for (int i = tid; i < (V >> 2); i += kNT)
+          reinterpret_cast<float4*>(row)[i] = reinterpret_cast<const float4*>(gr)[i];
+      } else {
+        for (int i = tid; i < V; i += kNT) row[i] = gr[i];
+      }
     }
     for (int r = tid; r < prevK; r += kNT) rmap[Rc[r]] = -1;
     __syncthreads();
+    // the other buffer was last read in the previous step: fetch the next frame
+    if (nbuf == 2 && wave == 3 && f + 1 < nframes)
+      row_fetch_async(lp_row + (int64_t)sel[f + 1] * P.stride_t, rows + ((f + 1) & 1) * rstride,
+                      V, P.vec4);
 
     // ---- the frame's best K non-blank labels, (lp desc, label asc)
     auto lkey = [&](int c) -> uint64_t {
@@ -219,8 +253,10 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       if (x != 0ull && x >= xk) kb64[atomicAdd(&sh[2], 1)] = x;
     }
     __syncthreads();
+    if (tid < 8) kb64[K + tid] = 0ull;
+    __syncthreads();
     for (int i = tid; i < K; i += kNT) {
-      const int r = rank_of(kb64, K, i);
+      const int r = count_above(kb64, K, kb64[i]);
       const int c = (int)comp_id(kb64[i]);
       Rc[r] = c;
       Rl[r] = row[c];
@@ -322,153 +358,259 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_lpc[k] = lpc;
     }
     __syncthreads();
-    // each beam's best candidate
+    // each beam's best candidate, its first two open ranks, and the sample
+    // (both slots and those two ranks of every beam) whose W-th largest key
+    // bounds the W-th largest candidate from below
     if (tid < W) {
       const int k = tid;
       const bool lv = s_live[k] != 0;
       if (s_exc[k]) s_kc[k] = kNeg;
       const float kb = s_kb[k], kc = s_exc[k] ? kNeg : s_kc[k];
-      uint64_t best = 0ull;
+      uint64_t cb = 0ull, cc = 0ull, o0 = 0ull, o1 = 0ull;
       if (lv) {
-        const uint64_t cb = kb > kNeg ? compose(kb, (uint32_t)((k << kIdShift) | blank)) : 0ull;
-        const uint64_t cc =
-            kc > kNeg ? compose(kc, (uint32_t)((k << kIdShift) | s_last[k])) : 0ull;
-        best = cb > cc ? cb : cc;
-        int r0 = -1;
-        for (int w = 0; w < kExw && r0 < 0; w++) {
-          const uint32_t open = ~s_exm[k * kExw + w];
-          if (open) r0 = w * 32 + __ffs((int)open) - 1;
+        cb = kb > kNeg ? compose(kb, (uint32_t)((k << kIdShift) | blank)) : 0ull;
+        cc = kc > kNeg ? compose(kc, (uint32_t)((k << kIdShift) | s_last[k])) : 0ull;
+        int r0 = -1, r1 = -1;
+        for (int w = 0; w < kExw && r1 < 0; w++) {
+          uint32_t open = ~s_exm[k * kExw + w];
+          while (open && r1 < 0) {
+            const int r = w * 32 + __ffs((int)open) - 1;
+            open &= open - 1u;
+            if (r >= K) break;
+            if (r0 < 0) r0 = r;
+            else r1 = r;
+          }
         }
-        if (r0 >= 0 && r0 < K) {
+        if (r0 >= 0) {
           const float key = s_A[k] + Rl[r0];
-          const uint64_t co = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | Rc[r0])) : 0ull;
-          best = best > co ? best : co;
+          o0 = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | Rc[r0])) : 0ull;
+        }
+        if (r1 >= 0) {
+          const float key = s_A[k] + Rl[r1];
+          o1 = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | Rc[r1])) : 0ull;
         }
       }
-      s_head[k] = best;
+      const uint64_t b1 = cb > cc ? cb : cc;
+      s_head[k] = b1 > o0 ? b1 : o0;
+      if (k + W < kMaxW) s_head[k + W] = 0ull;   // (zero past the beam for count_above)
+      cbuf[4 * k + 0] = cb;
+      cbuf[4 * k + 1] = cc;
+      cbuf[4 * k + 2] = o0;
+      cbuf[4 * k + 3] = o1;
     }
     __syncthreads();
-    // candidates considered: at most W - h + 1 open ranks of a beam whose best
-    // is the h-th best of the beams, plus its two slots
+    uint64_t tau = kth_largest(4 * W, W, [&](int i) { return cbuf[i]; }, hist, sh);
+    if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
+    const float tau_key = comp_key(tau);
+    // per beam: open ranks considered (at most W - h + 1 open ones when its
+    // best is the h-th best of the beams), and the leading ones whose key
+    // reaches the bound
     if (tid < W) {
       const int k = tid;
       const uint64_t mine = s_head[k];
-      int lim = 0;
+      int lim = 0, reach = 0;
       if (mine != 0ull) {
-        int h = 1;
-        for (int j = 0; j < W; j++) h += s_head[j] > mine ? 1 : 0;
+        const int h = 1 + count_above(s_head, W, mine);
         int want = W - h + 1;
-        int r = 0;
-        while (r < K && want > 0) {
-          if (!((s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u)) want--;
-          r++;
+        for (int w = 0; w < kExw && want > 0; w++) {
+          const int base = w * 32;
+          const int nb = min(32, K - base);
+          if (nb <= 0) break;
+          uint32_t open = ~s_exm[k * kExw + w] & (nb >= 32 ? ~0u : ((1u << nb) - 1u));
+          const int cnt = __popc(open);
+          if (cnt < want) {
+            want -= cnt;
+            lim = base + nb;
+          } else {
+            for (int x = 1; x < want; x++) open &= open - 1u;
+            lim = base + __ffs((int)open);
+            want = 0;
+          }
         }
-        lim = r;
+        // keys A + Rl[r] do not increase with r: binary search of the first
+        // rank below the bound
+        const float A = s_A[k];
+        int lo = 0, hi = lim;
+        if (tau > 1ull) {
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (A + Rl[mid] >= tau_key) lo = mid + 1;
+            else hi = mid;
+          }
+          reach = lo;
+        } else {
+          reach = lim;
+        }
       }
       s_lim[k] = lim;
+      s_bslot[k] = mine != 0ull ? 2 + reach : 0;   // (reused: survivor items of the beam)
     }
     __syncthreads();
     if (tid < 64) {
-      // prefix sums of the per-beam item counts (2 slots + lim ranks)
       const int k0 = 2 * tid, k1 = 2 * tid + 1;
-      const int n0 = k0 < W ? (s_head[k0] != 0ull ? 2 + s_lim[k0] : 0) : 0;
-      const int n1 = k1 < W ? (s_head[k1] != 0ull ? 2 + s_lim[k1] : 0) : 0;
+      const int n0 = k0 < W ? s_bslot[k0] : 0;
+      const int n1 = k1 < W ? s_bslot[k1] : 0;
       const int incl = wave_incl_scan(n0 + n1);
       const int ex = incl - n0 - n1;
       if (k0 < W) s_offs[k0] = ex;
       if (k1 < W) s_offs[k1] = ex + n0;
       if (tid == 63) {
         sh[3] = incl;
-        s_offs[W] = incl;   // end sentinel of the walk below
+        s_offs[W] = incl;   // end sentinel
       }
     }
     __syncthreads();
-    const int ntot = sh[3];
-    if (tid == 0 && ntot > kItems * kNT) sh[10] |= kStatusAborted;   // cannot happen (bound above)
-    // this thread's candidates, kept in registers
-    uint64_t ck[kItems];
-    {
-      int k = 0;
-#pragma unroll
-      for (int u = 0; u < kItems; u++) {
-        const int qi = tid + u * kNT;
-        uint64_t x = 0ull;
-        if (qi < ntot) {
-          while (s_offs[k + 1] <= qi) k++;
-          const int j = qi - s_offs[k];
-          float key;
-          int c;
-          if (j == 0) {
-            key = s_kb[k];
-            c = blank;
-          } else if (j == 1) {
-            key = s_kc[k];
-            c = s_last[k];
-          } else {
-            const int r = j - 2;
-            const bool ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
-            key = ex ? kNeg : s_A[k] + Rl[r];
-            c = Rc[r];
-          }
-          x = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
+    const int nsurv = sh[3];
+    int nw;
+    if (nsurv <= kCBuf) {
+      // ---- top W (sec. 3.4.4 / 3.4.5) among the candidates at or above the
+      // bound, each beam writing its own
+      for (int i = tid; i < nsurv; i += kNT) {
+        // the beam of item i: the last k with s_offs[k] <= i
+        int lo = 0, hi = W - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_offs[mid] <= i) lo = mid;
+          else hi = mid - 1;
         }
-        ck[u] = x;
+        const int k = lo, j = i - s_offs[k];
+        float key;
+        int c;
+        bool ex = false;
+        if (j == 0) {
+          key = s_kb[k];
+          c = blank;
+        } else if (j == 1) {
+          key = s_kc[k];
+          c = s_last[k];
+        } else {
+          const int r = j - 2;
+          ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
+          key = s_A[k] + Rl[r];
+          c = Rc[r];
+        }
+        const uint64_t x =
+            (!ex && key > kNeg) ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
+        cbuf[i] = x >= tau ? x : 0ull;
       }
-    }
-    // ---- top W (sec. 3.4.4 / 3.4.5): radix select over the register keys
-    uint64_t prefix = 0ull;
-    int need = W;
-    bool few = false;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
       __syncthreads();
-      const uint64_t hmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-#pragma unroll
+      uint64_t xw = kth_largest(nsurv, W, [&](int i) { return cbuf[i]; }, hist, sh);
+      if (xw == 0ull) xw = 1ull;   // fewer than W candidates: all of them win
+      if (tid == 0) sh[4] = 0;
+      __syncthreads();
+      for (int i = tid; i < nsurv; i += kNT) {
+        const uint64_t x = cbuf[i];
+        if (x != 0ull && x >= xw) kb64[atomicAdd(&sh[4], 1)] = x;
+      }
+      __syncthreads();
+      nw = sh[4];
+    } else {
+      // many candidates at the bound (exact ties): every considered candidate,
+      // held in registers, through a radix select
+      if (tid < 64) {
+        const int k0 = 2 * tid, k1 = 2 * tid + 1;
+        const int n0 = k0 < W ? (s_head[k0] != 0ull ? 2 + s_lim[k0] : 0) : 0;
+        const int n1 = k1 < W ? (s_head[k1] != 0ull ? 2 + s_lim[k1] : 0) : 0;
+        const int incl = wave_incl_scan(n0 + n1);
+        const int ex = incl - n0 - n1;
+        if (k0 < W) s_offs[k0] = ex;
+        if (k1 < W) s_offs[k1] = ex + n0;
+        if (tid == 63) {
+          sh[3] = incl;
+          s_offs[W] = incl;   // end sentinel of the walk below
+        }
+      }
+      __syncthreads();
+      const int ntot = sh[3];
+      if (tid == 0 && ntot > kItems * kNT) sh[10] |= kStatusAborted;   // cannot happen (bound above)
+      // this thread's candidates, kept in registers
+      uint64_t ck[kItems];
+      {
+        int k = 0;
+  #pragma unroll
+        for (int u = 0; u < kItems; u++) {
+          const int qi = tid + u * kNT;
+          uint64_t x = 0ull;
+          if (qi < ntot) {
+            while (s_offs[k + 1] <= qi) k++;
+            const int j = qi - s_offs[k];
+            float key;
+            int c;
+            if (j == 0) {
+              key = s_kb[k];
+              c = blank;
+            } else if (j == 1) {
+              key = s_kc[k];
+              c = s_last[k];
+            } else {
+              const int r = j - 2;
+              const bool ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
+              key = ex ? kNeg : s_A[k] + Rl[r];
+              c = Rc[r];
+            }
+            x = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
+          }
+          ck[u] = x;
+        }
+      }
+      // ---- top W (sec. 3.4.4 / 3.4.5): radix select over the register keys
+      uint64_t prefix = 0ull;
+      int need = W;
+      bool few = false;
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[tid] = 0;
+        __syncthreads();
+        const uint64_t hmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+  #pragma unroll
+        for (int u = 0; u < kItems; u++) {
+          const uint64_t x = ck[u];
+          if (x != 0ull && (x & hmask) == prefix) atomicAdd(&hist[(int)((x >> shift) & 255u)], 1);
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const int lane = tid;
+          const int d0 = 255 - 4 * lane;
+          const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
+          const int s = c0 + c1 + c2 + c3;
+          const int incl = wave_incl_scan(s);
+          const int ex = incl - s;
+          const int total = __shfl(incl, 63, 64);
+          if (ex < need && incl >= need) {
+            int d, above;
+            if (ex + c0 >= need) { d = d0; above = ex; }
+            else if (ex + c0 + c1 >= need) { d = d0 - 1; above = ex + c0; }
+            else if (ex + c0 + c1 + c2 >= need) { d = d0 - 2; above = ex + c0 + c1; }
+            else { d = d0 - 3; above = ex + c0 + c1 + c2; }
+            sh[0] = d;
+            sh[1] = above;
+          }
+          if (lane == 0 && total < need) sh[0] = -1;
+        }
+        __syncthreads();
+        const int d = sh[0], above = sh[1];
+        __syncthreads();
+        if (d < 0) {
+          few = true;   // fewer than W candidates: all of them win
+          break;
+        }
+        prefix |= (uint64_t)d << shift;
+        need -= above;
+      }
+      const uint64_t xw = few ? 1ull : prefix;
+      if (tid == 0) sh[4] = 0;
+      __syncthreads();
+  #pragma unroll
       for (int u = 0; u < kItems; u++) {
         const uint64_t x = ck[u];
-        if (x != 0ull && (x & hmask) == prefix) atomicAdd(&hist[(int)((x >> shift) & 255u)], 1);
+        if (x != 0ull && x >= xw) kb64[atomicAdd(&sh[4], 1)] = x;
       }
       __syncthreads();
-      if (tid < 64) {
-        const int lane = tid;
-        const int d0 = 255 - 4 * lane;
-        const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
-        const int s = c0 + c1 + c2 + c3;
-        const int incl = wave_incl_scan(s);
-        const int ex = incl - s;
-        const int total = __shfl(incl, 63, 64);
-        if (ex < need && incl >= need) {
-          int d, above;
-          if (ex + c0 >= need) { d = d0; above = ex; }
-          else if (ex + c0 + c1 >= need) { d = d0 - 1; above = ex + c0; }
-          else if (ex + c0 + c1 + c2 >= need) { d = d0 - 2; above = ex + c0 + c1; }
-          else { d = d0 - 3; above = ex + c0 + c1 + c2; }
-          sh[0] = d;
-          sh[1] = above;
-        }
-        if (lane == 0 && total < need) sh[0] = -1;
-      }
-      __syncthreads();
-      const int d = sh[0], above = sh[1];
-      __syncthreads();
-      if (d < 0) {
-        few = true;   // fewer than W candidates: all of them win
-        break;
-      }
-      prefix |= (uint64_t)d << shift;
-      need -= above;
+      nw = sh[4];
     }
-    const uint64_t xw = few ? 1ull : prefix;
-    if (tid == 0) sh[4] = 0;
+    if (tid < 8) kb64[nw + tid] = 0ull;
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kItems; u++) {
-      const uint64_t x = ck[u];
-      if (x != 0ull && x >= xw) kb64[atomicAdd(&sh[4], 1)] = x;
-    }
-    __syncthreads();
-    const int nw = sh[4];   // <= W
-    for (int i = tid; i < nw; i += kNT) win[rank_of(kb64, nw, i)] = kb64[i];
+    for (int i = tid; i < nw; i += kNT) win[count_above(kb64, nw, kb64[i])] = kb64[i];
+    if (tid < kMaxW) s_bslot[tid] = -1;
     __syncthreads();
 
     // ---- new state of slot r <- winner (k, c) (sec. 3.4.5)
@@ -507,10 +649,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     // ---- tokens: row tid of parity p <- row k of parity q (+ c).  If row k
     // was itself copied from slot tid one step earlier, slot tid's row of
     // parity p already holds its first s_flen[p][tid] tokens.
+    // Otherwise, if slot tid was live two steps ago, its row already holds the
+    // tokens that every live row then shared.
     int start = 0;
     const int klen = k >= 0 ? s_len[k] : 0;
-    if (k >= 0 && s_src[q * kMaxW + k] == tid && s_flen[p * kMaxW + tid] >= 0)
-      start = min(s_flen[p * kMaxW + tid], klen);
+    if (k >= 0) {
+      const int oldlen = s_flen[p * kMaxW + tid];
+      if (oldlen >= 0) start = min(s_src[q * kMaxW + k] == tid ? oldlen : sh[6 + p], klen);
+    }
     const int s4 = start >> 2;
     const int e4 = (klen + 3) >> 2;
     const int cnt = k >= 0 ? e4 - s4 : 0;
@@ -535,11 +681,47 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       const int ntok4 = sh[5];
       int4* c4 = reinterpret_cast<int4*>(clist);
       const int64_t ld4 = ldc >> 2;
+      // destination of this thread's first item by binary search, later ones
+      // by walking forward
       int a = 0;
-      for (int i = tid; i < ntok4; i += kNT) {
+      if (tid < ntok4) {
+        int lo = 0, hi = W - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_offs[mid] <= tid) lo = mid;
+          else hi = mid - 1;
+        }
+        a = lo;
+      }
+      auto where = [&](int i, int64_t& dst, int64_t& src) {
         while (a + 1 < W && s_offs[a + 1] <= i) a++;
         const int64_t pos4 = s_lim[a] + (i - s_offs[a]);
-        c4[(int64_t)(p * W + a) * ld4 + pos4] = c4[(int64_t)(q * W + hist[128 + a]) * ld4 + pos4];
+        dst = (int64_t)(p * W + a) * ld4 + pos4;
+        src = (int64_t)(q * W + hist[128 + a]) * ld4 + pos4;
+      };
+      // four copies per round: the loads are issued before the stores
+      for (int i = tid; i < ntok4; i += 4 * kNT) {
+        int64_t d0, s0, d1 = 0, s1 = 0, d2 = 0, s2 = 0, d3 = 0, s3 = 0;
+        int4 v1, v2, v3;
+        where(i, d0, s0);
+        const int4 v0 = c4[s0];
+        const bool b1 = i + kNT < ntok4, b2 = i + 2 * kNT < ntok4, b3 = i + 3 * kNT < ntok4;
+        if (b1) {
+          where(i + kNT, d1, s1);
+          v1 = c4[s1];
+        }
+        if (b2) {
+          where(i + 2 * kNT, d2, s2);
+          v2 = c4[s2];
+        }
+        if (b3) {
+          where(i + 3 * kNT, d3, s3);
+          v3 = c4[s3];
+        }
+        c4[d0] = v0;
+        if (b1) c4[d1] = v1;
+        if (b2) c4[d2] = v2;
+        if (b3) c4[d3] = v3;
       }
     }
     __syncthreads();
@@ -559,24 +741,50 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     // publish the new hashes and lengths before the lookup (old values are no
     // longer read)
     __syncthreads();
+    auto tag_pos = [](uint64_t tg) {
+      return (int)((((uint32_t)tg ^ (uint32_t)(tg >> 32)) * 0x9e3779b1u) >> 24);
+    };
+    const uint64_t mytag = nlive ? (((uint64_t)(uint32_t)nlen << 32) | nh) : ~0ull;
     if (tid < W) {
       s_h[tid] = nh;
       s_hp[tid] = nhp;
       s_len[tid] = nlen;
       s_live[tid] = nlive;
+      s_tag[tid] = mytag;
+    }
+    hist[tid] = -1;   // open-addressing table (length, hash) -> slot
+    __syncthreads();
+    if (tid < W && nlive) {
+      int pos = tag_pos(mytag);
+      while (atomicCAS(&hist[pos], -1, tid) != -1) pos = (pos + 1) & 255;
     }
     __syncthreads();
     if (tid < W && k >= 0 && c == blank && npar < 0 && nlen >= 1) {
-      for (int i = 0; i < W; i++) {
-        if (i == tid || !s_live[i] || s_len[i] != nlen - 1 || s_h[i] != nhp) continue;
-        const int* ra = clist + (int64_t)(p * W + tid) * ldc;
-        const int* rb = clist + (int64_t)(p * W + i) * ldc;
-        bool eq = true;
-        for (int x = 0; x < nlen - 1 && eq; x++) eq = ra[x] == rb[x];
-        nver++;
-        if (eq) {
-          npar = i;
-          break;
+      const uint64_t want = ((uint64_t)(uint32_t)(nlen - 1) << 32) | nhp;
+      // at most W of the 256 entries are used, so every probe ends at an empty one
+      for (int pos = tag_pos(want); hist[pos] >= 0 && npar < 0; pos = (pos + 1) & 255) {
+        {
+          const int i = hist[pos];
+          if (s_tag[i] != want || i == tid) continue;
+          // the first nlen - 1 tokens of both rows, 16 per round (rows are
+          // 16-byte aligned: ldc is a multiple of 4)
+          const int4* ra = reinterpret_cast<const int4*>(clist + (int64_t)(p * W + tid) * ldc);
+          const int4* rb = reinterpret_cast<const int4*>(clist + (int64_t)(p * W + i) * ldc);
+          const int n = nlen - 1;
+          bool eq = true;
+          for (int x4 = 0; x4 * 4 < n && eq; x4 += 4) {
+#pragma unroll
+            for (int u2 = 0; u2 < 4; u2++) {
+              const int b = (x4 + u2) * 4;
+              if (b < n) {
+                const int4 va = ra[x4 + u2], vb = rb[x4 + u2];
+                eq = eq && (va.x == vb.x) && (b + 1 >= n || va.y == vb.y) &&
+                     (b + 2 >= n || va.z == vb.z) && (b + 3 >= n || va.w == vb.w);
+              }
+            }
+          }
+          nver++;
+          if (eq) npar = i;
         }
       }
     }
@@ -589,6 +797,48 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_par[tid] = npar;
       s_src[p * kMaxW + tid] = k;
       s_flen[p * kMaxW + tid] = nlive ? nlen : -1;
+    }
+    if ((step & 15) == 15) {
+      // grow the common prefix of the live rows of parity p by up to 64
+      // positions (it never shrinks: every row extends a row of the step before)
+      if (tid < 64) {
+        const int r0 = 2 * tid, r1 = 2 * tid + 1;
+        const bool l0 = r0 < W && s_live[r0], l1 = r1 < W && s_live[r1];
+        int mn = min(l0 ? s_len[r0] : 0x7fffffff, l1 ? s_len[r1] : 0x7fffffff);
+#pragma unroll
+        for (int m = 32; m > 0; m >>= 1) mn = min(mn, __shfl_xor(mn, m, 64));
+        const uint64_t lm = __ballot(l0 || l1);
+        if (tid == 0) {
+          sh[8] = mn;
+          int first = -1;
+          if (lm) {
+            const int ln = __ffsll((long long)lm) - 1;
+            first = s_live[2 * ln] ? 2 * ln : 2 * ln + 1;
+          }
+          sh[11] = first;
+          reinterpret_cast<unsigned long long*>(sh + 12)[0] = ~0ull;
+        }
+      }
+      __syncthreads();
+      const int first = sh[11];
+      if (first >= 0) {
+        const int c0 = max(sh[6], sh[7]);
+        const int pos = c0 + (tid & 63);
+        bool ok = pos < sh[8];
+        if (ok) {
+          const int ref = clist[(int64_t)(p * W + first) * ldc + pos];
+          for (int r = tid >> 6; r < W; r += 4)
+            if (s_live[r]) ok = ok && clist[(int64_t)(p * W + r) * ldc + pos] == ref;
+        }
+        const uint64_t okm = __ballot(ok);
+        if ((tid & 63) == 0)
+          atomicAnd(reinterpret_cast<unsigned long long*>(sh + 12), (unsigned long long)okm);
+        __syncthreads();
+        if (tid == 0) {
+          const uint64_t all = reinterpret_cast<unsigned long long*>(sh + 12)[0];
+          sh[6 + p] = c0 + (all == ~0ull ? 64 : __ffsll((long long)~all) - 1);
+        }
+      }
     }
     __syncthreads();
     last_t = t;

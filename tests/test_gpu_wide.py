@@ -64,3 +64,17 @@ def test_wide_beams_larger_vocabulary():
     run_both(lp, lens, 64, 64, what="V1024")
     st = gpu_offline.last_stats
     assert (st[:, 0] == 120).all() and (st[:, 2] == 0).all()
+
+
+def test_wide_beam_bpe1024_full_size_sampled():
+    # the bpe1024 inputs at full size (B=64, T=875, ragged) with beam 64, in the
+    # launch the benchmark times; rows sampled against the oracle
+    wl = synth.WORKLOADS["bpe1024"]
+    x, lens = wl.make_device(0, "cuda")
+    W = 64
+    print(f"[case] wide bpe1024 full B={wl.B} T={wl.T} W={W}", flush=True)
+    got = gpu_offline(x, lens, W, W, 0, wl.threshold, wl.max_out_len)
+    rows = [5, 40]
+    lp = x[rows].cpu().numpy()
+    ref = oracle.decode(lp, lens[rows], W, W, 0, wl.threshold, wl.max_out_len)
+    assert_parity(tuple(g[rows] for g in got), ref, what="wide bpe1024")
