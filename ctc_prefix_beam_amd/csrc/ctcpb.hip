@@ -1598,10 +1598,25 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   return C;
 }
 
+// dst[i] = src[i] for i < n by one wave, four loads per lane in flight before
+// their stores.
+template <typename D, typename S>
+__device__ __forceinline__ void wave_copy(D* dst, const S* src, int n) {
+  const int lane = lane_id();
+  for (int i = lane; i < n; i += 4 * kWave) {
+    const int j1 = i + kWave, j2 = i + 2 * kWave, j3 = i + 3 * kWave;
+    const S v0 = src[i], v1 = src[min(j1, n - 1)], v2 = src[min(j2, n - 1)],
+            v3 = src[min(j3, n - 1)];
+    dst[i] = (D)v0;
+    if (j1 < n) dst[j1] = (D)v1;
+    if (j2 < n) dst[j2] = (D)v2;
+    if (j3 < n) dst[j3] = (D)v3;
+  }
+}
+
 // Paged metadata: global row region <-> LDS.
 __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
   const Layout& L = C.L;
-  const int lane = lane_id();
   int* gt = reinterpret_cast<int*>(C.base + L.o_tab);
   int* gr = reinterpret_cast<int*>(C.base + L.o_ref);
   int* gf = reinterpret_cast<int*>(C.base + L.o_free);
@@ -1609,40 +1624,54 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
   int* gn = reinterpret_cast<int*>(C.base + L.o_tlen);
   const int nt = 2 * L.W * L.max_lp, nl = 2 * L.W * L.ps;
   if (to_lds) {
-    for (int i = lane; i < nt; i += kWave) C.tab[i] = (int16_t)gt[i];
-    for (int i = lane; i < L.npages; i += kWave) {
-      C.ref[i] = gr[i];
-      C.fstk[i] = (int16_t)gf[i];
-    }
-    for (int i = lane; i < nl; i += kWave) C.tail[i] = gl[i];
-    for (int i = lane; i < 2 * kMaxBeam; i += kWave) C.tlen[i] = gn[i];
+    wave_copy(C.tab, gt, nt);
+    wave_copy(C.ref, gr, L.npages);
+    wave_copy(C.fstk, gf, L.npages);
+    wave_copy(C.tail, gl, nl);
+    wave_copy(C.tlen, gn, 2 * kMaxBeam);
   } else {
-    for (int i = lane; i < nt; i += kWave) gt[i] = C.tab[i];
-    for (int i = lane; i < L.npages; i += kWave) {
-      gr[i] = C.ref[i];
-      gf[i] = C.fstk[i];
-    }
-    for (int i = lane; i < nl; i += kWave) gl[i] = C.tail[i];
-    for (int i = lane; i < 2 * kMaxBeam; i += kWave) gn[i] = C.tlen[i];
+    wave_copy(gt, C.tab, nt);
+    wave_copy(gr, C.ref, L.npages);
+    wave_copy(gf, C.fstk, L.npages);
+    wave_copy(gl, C.tail, nl);
+    wave_copy(gn, C.tlen, 2 * kMaxBeam);
   }
 }
 
-// Flat token lists kept in LDS: the live rows of the current parity are
-// restored from / saved to the row region around a streaming chunk.
 __device__ __forceinline__ void clist_io(const Ctx& C, const Beam& b, int parity, bool to_lds) {
+  // The live rows' tokens as one flat list of 16-byte pieces (rows start
+  // 16-byte aligned: ldc is a multiple of 4), eight pieces per lane in flight
+  // before any is stored.
   const Layout& L = C.L;
   const int lane = lane_id();
-  int* g = reinterpret_cast<int*>(C.base + L.o_clist);
-  const uint64_t live = __ballot(lane < L.W && b.live);
-  for (int r = 0; r < L.W; r++) {
-    if (!((live >> r) & 1ull)) continue;
-    const int len = __shfl(b.len, r, 64);
-    const int64_t at = ((int64_t)(parity * L.W + r)) * L.ldc;
-    for (int i = lane; i < len; i += kWave) {
-      if (to_lds) C.clist[at + i] = g[at + i];
-      else g[at + i] = C.clist[at + i];
-    }
+  int4* g4 = reinterpret_cast<int4*>(C.base + L.o_clist);
+  int4* s4 = reinterpret_cast<int4*>(C.clist);
+  const int64_t ld4 = L.ldc >> 2;
+  const bool lv = lane < L.W && b.live;
+  const int n4 = lv ? (b.len + 3) >> 2 : 0;
+  const int incl = wave_incl_scan(n4);
+  const int total = __shfl(incl, 63, 64);
+  int* offs = C.offs;   // first piece of each row
+  offs[lane] = incl - n4;
+  lds_sync();
+  int r = 0;   // row of this lane's current piece (pieces only move forward)
+  auto where = [&](int i) -> int64_t {
+    i = min(i, total - 1);
+    while (r + 1 < L.W && offs[r + 1] <= i) r++;
+    return (int64_t)(parity * L.W + r) * ld4 + (i - offs[r]);
+  };
+  for (int i0 = lane; i0 < total; i0 += 4 * kWave) {
+    const int64_t a0 = where(i0), a1 = where(i0 + kWave), a2 = where(i0 + 2 * kWave),
+                  a3 = where(i0 + 3 * kWave);
+    const int4* src = to_lds ? g4 : s4;
+    int4* dst = to_lds ? s4 : g4;
+    const int4 v0 = src[a0], v1 = src[a1], v2 = src[a2], v3 = src[a3];
+    dst[a0] = v0;
+    if (i0 + kWave < total) dst[a1] = v1;
+    if (i0 + 2 * kWave < total) dst[a2] = v2;
+    if (i0 + 3 * kWave < total) dst[a3] = v3;
   }
+  lds_sync();
 }
 
 // Header fields <-> LDS scalars.
