@@ -2337,9 +2337,22 @@ int launch(K kernel, int blocks, int threads, int lds, hipStream_t st, const Par
            const char* what) {
   if (blocks <= 0) return CTCPB_OK;
   if (lds > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-      return fail(CTCPB_ERR_DEVICE, std::string("hipFuncSetAttribute failed for ") + what);
+    // raised once per kernel to the CU's whole LDS (not a stream operation, but
+    // kept out of repeated calls so that launches under stream capture are
+    // plain kernel nodes)
+    static std::mutex mu;
+    static const void* raised[32];
+    static int nraised = 0;
+    const void* k = reinterpret_cast<const void*>(kernel);
+    std::lock_guard<std::mutex> lock(mu);
+    bool done = false;
+    for (int i = 0; i < nraised; i++) done = done || raised[i] == k;
+    if (!done) {
+      if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit) !=
+          hipSuccess)
+        return fail(CTCPB_ERR_DEVICE, std::string("hipFuncSetAttribute failed for ") + what);
+      if (nraised < 32) raised[nraised++] = k;
+    }
   }
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), lds, st, P);
   const hipError_t e = hipGetLastError();

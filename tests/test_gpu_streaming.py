@@ -238,3 +238,41 @@ def test_start_frame_capacity_and_row_subsets():
     st = pool.row_stats().cpu().numpy()
     assert list(st[:, 0]) == [min(CAP, int(mask[s].sum())) for s in range(S)]
     assert list(st[:, 1]) == frames == list(start + T)
+
+
+def test_chunks_replayed_from_a_captured_graph():
+    # reset + four chunk calls captured once into a HIP graph (no host sync and
+    # no allocation inside the calls), replayed several times with eager work
+    # and synchronisations in between: every replay equals the eager decode
+    S, T, V, W, CH = 8, 64, 512, 10, 16
+    lp, _ = synth.peaky(S, T, V, seed=26, p_blank=0.65)
+    print(f"[case] stream graph S={S} T={T} V={V} W={W}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, capacity=T)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    chunks = [x[:, a:a + CH].contiguous() for a in range(0, T, CH)]
+    for c in chunks:
+        pool.chunk(c)
+    eager = read(pool)
+    assert_parity(eager, oracle_streams(lp, W, T, CH, W, T), what="graph eager")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pool.reset()
+            for c in chunks:
+                pool.chunk(c)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        pool.reset()                       # eager work between replays
+        junk = torch.ones(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = read(pool)
+        for a, b in zip(got, eager):
+            assert np.array_equal(a, b), rep
+        assert float(junk) == float(1 << 20)
