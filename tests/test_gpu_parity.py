@@ -138,3 +138,34 @@ def test_repeat_runs_are_bitwise_identical():
         again = gpu_offline(lp, lens, 24, 24, 0, 1.0, 200, paged=True)
         for a, b in zip(first, again):
             assert np.array_equal(a, b)
+
+
+def test_offline_decode_replayed_from_a_captured_graph():
+    # frame selection + decode captured once (workspace and outputs allocated
+    # beforehand), replayed with eager work in between: every replay equals
+    # the eager decode and the oracle
+    lp, lens = synth.peaky(4, 120, 300, seed=97, p_blank=0.6)
+    print("[case] offline graph B=4 T=120 V=300 W=8", flush=True)
+    dec = cpb.OfflineDecoder(cpb.DecoderConfig(beam=8, nbest=8, blank_threshold=0.9,
+                                               max_out_len=120))
+    x = torch.from_numpy(lp).cuda()
+    ld = torch.from_numpy(lens).cuda()
+    out = dec.decode(x, ld)
+    eager = tuple(t.cpu().numpy().copy() for t in out)
+    assert_parity(eager, oracle.decode(lp, lens, 8, 8, 0, 0.9, 120), what="graph eager")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dec.decode(x, ld, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert np.array_equal(a.cpu().numpy(), b), rep
