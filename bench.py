@@ -297,6 +297,17 @@ def main():
                    "workspace_bytes": ws_bytes, "paged_pages_high_per_row": pages_high,
                    "kernel_sha": kernel_sha()},
     }
+    if paged:
+        # token storage per row (f32-sized tokens): the two flat lists of every
+        # slot at full capacity, the default page pool (the bound that cannot
+        # run out) and the pool this decode's busiest row actually needed
+        ps = cfg.page_size or 16
+        flat_b = 2 * wl.beam * wl.T * 4
+        pool_b = wl.beam * (-(-wl.T // ps) + 1) * ps * 4
+        high_b = pages_high * ps * 4
+        result["decode"]["token_store_bytes_per_row"] = {
+            "flat_lists": flat_b, "paged_default_pool": pool_b, "paged_high_water": high_b,
+            "flat_over_high_water": round(flat_b / max(high_b, 1), 2)}
     if args.with_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
         a.fill_(1.0)

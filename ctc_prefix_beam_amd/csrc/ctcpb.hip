@@ -1330,7 +1330,10 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
   }
 
   // pass 1: fork, two entries per round (the round count is the wave's
-  // largest, so the free-stack top stays wave-uniform)
+  // largest, so the free-stack top stays wave-uniform).  The top is capped at
+  // the pool size: after a row has run out of pages its tables can name pages
+  // twice, and the cap keeps every stack read and page index inside the pool.
+  // (Only the row's own pool is affected; its outputs are then unspecified.)
   int start = (in && ((live2 >> lane) & 1u)) ? (pcpp < old_t ? pcpp : old_t) : 0;
   // if the source was forked from this very slot one step earlier, the two
   // rows differ at most from the old row's last page on
@@ -1355,11 +1358,11 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
     const uint64_t m0 = __ballot(f0);
     const int at0 = ft + lanes_below(m0);
     if (f0 && at0 < L.npages) C.fstk[at0] = (int16_t)o0;
-    ft += __popcll(m0);
+    ft = min(ft + __popcll(m0), L.npages);
     const uint64_t m1 = __ballot(f1);
     const int at1 = ft + lanes_below(m1);
     if (f1 && at1 < L.npages) C.fstk[at1] = (int16_t)o1;
-    ft += __popcll(m1);
+    ft = min(ft + __popcll(m1), L.npages);
   }
   int new_t = in ? (np_new > 0 ? np_new : start) : old_t;
   lds_order();
@@ -1405,7 +1408,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
   const uint64_t mp = __ballot(push_old);
   const int atp = ft + lanes_below(mp);
   if (push_old && atp < L.npages) C.fstk[atp] = (int16_t)phys;
-  ft += __popcll(mp);
+  ft = min(ft + __popcll(mp), L.npages);
   ss.freetop = ft;
   const int used = ss.nextfree - ft;
   ss.high = used > ss.high ? used : ss.high;

@@ -65,7 +65,13 @@ typedef struct {
                               reference-counted prefix sharing (sec. 3.4.5, 4.2) */
   int32_t page_size;       /* paged: tokens per page, a multiple of 4 in 4..64 (0 = 16) */
   int32_t num_pages;       /* paged: pages per row/stream (0 = beam * (ceil(cap /
-                              page_size) + 1), the bound of sec. 4.2) */
+                              page_size) + 1), the bound of sec. 4.2), at most 32767.
+                              A smaller pool is allowed: a row that needs more pages
+                              than it holds sets status bit 0 (ctcpb_row_stats [2]),
+                              its outputs are then unspecified (all accesses stay in
+                              its own pool) and the other rows are unaffected.  The
+                              high-water mark (ctcpb_row_stats [3]) of a decode is
+                              the pool that decodes that row exactly. */
 } ctcpb_config;
 
 /* Bytes of device workspace ctcpb_decode_offline needs for `batch` rows of up

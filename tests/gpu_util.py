@@ -10,7 +10,7 @@ TOL = 1e-4  # absolute, log domain
 
 
 def gpu_offline(lp, lens, beam, nbest, blank, threshold, max_out_len, paged=False, page_size=16,
-                num_pages=0, device="cuda"):
+                num_pages=0, device="cuda", check_status=True):
     dec = cpb.OfflineDecoder(cpb.DecoderConfig(beam=beam, nbest=nbest, blank_id=blank,
                                                blank_threshold=threshold,
                                                max_out_len=max_out_len, paged=paged,
@@ -19,7 +19,7 @@ def gpu_offline(lp, lens, beam, nbest, blank, threshold, max_out_len, paged=Fals
     t, l, s = dec.decode(x.to(device), torch.as_tensor(lens, dtype=torch.int32).to(device))
     stats = dec.row_stats().cpu().numpy()
     torch.cuda.synchronize()
-    assert (stats[:, 2] == 0).all(), f"row status bits set: {np.unique(stats[:, 2])}"
+    assert not check_status or (stats[:, 2] == 0).all(), f"row status bits set: {np.unique(stats[:, 2])}"
     gpu_offline.last_stats = stats   # per-row counters of the call (cpb.STAT_FIELDS)
     return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
 

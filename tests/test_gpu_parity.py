@@ -169,3 +169,36 @@ def test_offline_decode_replayed_from_a_captured_graph():
         torch.cuda.synchronize()
         for a, b in zip(out, eager):
             assert np.array_equal(a.cpu().numpy(), b), rep
+
+
+def test_bounded_page_pool():
+    # pages come from a pool of num_pages per row.  The high-water mark a
+    # decode reports per row is exactly what that row needs: a row whose mark
+    # fits the pool decodes as with the default pool, a row whose mark does
+    # not runs out, which sets its status bit 0 (its outputs are then
+    # unspecified) and leaves the other rows untouched
+    lp, lens = synth.peaky(6, 240, 300, seed=98, p_blank=0.4)
+    lens[:] = [240, 200, 160, 120, 80, 40]
+    print("[case] bounded pool B=6 T=240 V=300 W=16 ps=8", flush=True)
+    full = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8)
+    high = gpu_offline.last_stats[:, 3].copy()
+    assert (gpu_offline.last_stats[:, 2] == 0).all()
+    assert_parity(full, oracle.decode(lp, lens, 16, 16, 0, 1.0, 240), what="bounded pool")
+    assert high.min() < high.max()
+    npages = int(np.median(high))
+    fits = high <= npages
+    assert fits.any() and (~fits).any()
+    got = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8, num_pages=npages,
+                      check_status=False)
+    st = gpu_offline.last_stats
+    assert np.array_equal(st[:, 2] & 1, (~fits).astype(st.dtype))
+    for b in np.nonzero(fits)[0]:
+        for a, e in zip(got, full):
+            assert np.array_equal(a[b], e[b])
+    # a pool of exactly the largest mark is enough for every row
+    got = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8,
+                      num_pages=int(high.max()))
+    assert (gpu_offline.last_stats[:, 2] == 0).all()
+    assert np.array_equal(gpu_offline.last_stats[:, 3], high)
+    for a, e in zip(got, full):
+        assert np.array_equal(a, e)
