@@ -137,6 +137,38 @@ __device__ __forceinline__ int count_above(const uint64_t* buf, int n, uint64_t 
   return r;
 }
 
+// Ranks the n keys of keys[0, n) (nonzero, pairwise distinct, n <= 64 *
+// kRankChunks) in descending order and calls out(rank, key) once per key.
+// Each wave sorts chunks of 64 keys in registers into tmp[0, 64 * chunks);
+// a key's rank is its place in its own chunk plus, for every other chunk, the
+// number of that chunk's keys above it (a binary search of the sorted chunk).
+constexpr int kRankChunks = 5;
+template <typename Out>
+__device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t* tmp, Out out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (n + 63) >> 6;
+  for (int c = wave; c < nch; c += kNT / 64) {   // wave-uniform: every lane sorts
+    const int i = c * 64 + lane;
+    tmp[i] = wave_sort64_desc<uint64_t>(i < n ? keys[i] : 0ull);
+  }
+  __syncthreads();
+  for (int i = tid; i < nch * 64; i += kNT) {
+    const uint64_t x = tmp[i];
+    const int own = i >> 6;
+    int r = i & 63;
+#pragma unroll
+    for (int c = 0; c < kRankChunks; c++) {
+      const uint64_t* a = tmp + (c < nch ? c : 0) * 64;
+      int lo = 0;   // keys of chunk c above x: a leading run (descending, zero-padded)
+#pragma unroll
+      for (int st = 32; st >= 1; st >>= 1) lo += a[lo + st - 1] > x ? st : 0;
+      lo += a[lo] > x ? 1 : 0;   // lo <= 63 before this
+      r += (c < nch && c != own) ? lo : 0;
+    }
+    if (x != 0ull) out(r, x);
+  }
+}
+
 __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
   const Layout L = P.L;
@@ -253,15 +285,12 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       if (x != 0ull && x >= xk) kb64[atomicAdd(&sh[2], 1)] = x;
     }
     __syncthreads();
-    if (tid < 8) kb64[K + tid] = 0ull;
-    __syncthreads();
-    for (int i = tid; i < K; i += kNT) {
-      const int r = count_above(kb64, K, kb64[i]);
-      const int c = (int)comp_id(kb64[i]);
+    rank_keys(kb64, K, cbuf, [&](int r, uint64_t x) {
+      const int c = (int)comp_id(x);
       Rc[r] = c;
       Rl[r] = row[c];
       rmap[c] = (int16_t)r;
-    }
+    });
     prevK = K;
     if (tid < kMaxW) {
       for (int w = 0; w < kExw; w++) s_exm[tid * kExw + w] = 0u;
@@ -607,9 +636,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       __syncthreads();
       nw = sh[4];
     }
-    if (tid < 8) kb64[nw + tid] = 0ull;
-    __syncthreads();
-    for (int i = tid; i < nw; i += kNT) win[count_above(kb64, nw, kb64[i])] = kb64[i];
+    rank_keys(kb64, nw, cbuf, [&](int r, uint64_t x) { win[r] = x; });
     if (tid < kMaxW) s_bslot[tid] = -1;
     __syncthreads();
 
