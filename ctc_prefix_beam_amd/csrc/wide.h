@@ -64,7 +64,9 @@ constexpr int exm = tag + kMaxW * 8;                    // u32 [kMaxW][kExw]
 constexpr int cbuf = exm + a16(kMaxW * kExw * 4);       // u64 [kCBuf]: candidates
 constexpr int hist = cbuf + kCBuf * 8;                  // int [256]
 constexpr int sh = hist + 256 * 4;                      // int [16] block scalars
-constexpr int end = sh + 16 * 4;
+constexpr int khist = sh + 16 * 4;                      // int [2][256]: kth_largest, kept zero
+constexpr int ksh = khist + 2 * 256 * 4;                // int [8]: kth_largest's scalars
+constexpr int end = ksh + 8 * 4;
 }  // namespace off
 
 // Bytes of LDS for vocabulary V: nbuf rows of floats (2: the next frame is
@@ -75,17 +77,31 @@ inline int lds_bytes(int V, int nbuf) {
 
 // Block-wide: the kth largest (1-based) nonzero 64-bit key of the items, by
 // radix select over 8-bit digits; 0 when fewer than kth keys are nonzero.
-// gen(i) gives item i's key for i in [0, n) (called once per item and pass).
-template <typename Gen>
-__device__ uint64_t kth_largest(int n, int kth, Gen gen, int* hist, int* sh) {
+// gen(i) gives item i's key for i in [0, n): the keys of items tid + j kNT,
+// j < R, are generated once and kept in registers, any further ones are
+// generated again in every pass.  khist holds two 256-bin histograms used by alternate passes; both are zero
+// on entry and again on return (wave 0 clears the bins it has read), so a
+// pass needs two barriers: after the counts, and after the digit is chosen
+// (ksh holds one set of the chosen digit's scalars per histogram, and a set
+// is written again only two passes later, after everyone has read it).
+template <int R, typename Gen>
+__device__ uint64_t kth_largest(int n, int kth, Gen gen, int* khist, int* ksh) {
   const int tid = threadIdx.x, lane = tid & 63;
+  uint64_t kr[R];
+#pragma unroll
+  for (int j = 0; j < R; j++) kr[j] = tid + j * kNT < n ? gen(tid + j * kNT) : 0ull;
   uint64_t prefix = 0ull;
   int need = kth;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
+  for (int pass = 0, shift = 56; shift >= 0; pass++, shift -= 8) {
+    int* hist = khist + (pass & 1) * 256;
+    int* sv = ksh + (pass & 1) * 4;
     const uint64_t hmask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-    for (int i = tid; i < n; i += kNT) {
+#pragma unroll
+    for (int j = 0; j < R; j++) {
+      const uint64_t x = kr[j];
+      if (x != 0ull && (x & hmask) == prefix) atomicAdd(&hist[(int)((x >> shift) & 255u)], 1);
+    }
+    for (int i = tid + R * kNT; i < n; i += kNT) {
       const uint64_t x = gen(i);
       if (x != 0ull && (x & hmask) == prefix) atomicAdd(&hist[(int)((x >> shift) & 255u)], 1);
     }
@@ -94,25 +110,28 @@ __device__ uint64_t kth_largest(int n, int kth, Gen gen, int* hist, int* sh) {
       // lane l holds digits 255 - 4l .. 252 - 4l (descending)
       const int d0 = 255 - 4 * lane;
       const int c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
+      hist[d0] = 0;
+      hist[d0 - 1] = 0;
+      hist[d0 - 2] = 0;
+      hist[d0 - 3] = 0;
       const int s = c0 + c1 + c2 + c3;
       const int incl = wave_incl_scan(s);
       const int ex = incl - s;
-      const int total = __shfl(incl, 63, 64);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
       if (ex < need && incl >= need) {
         int d, above, in;
         if (ex + c0 >= need) { d = d0; above = ex; in = c0; }
         else if (ex + c0 + c1 >= need) { d = d0 - 1; above = ex + c0; in = c1; }
         else if (ex + c0 + c1 + c2 >= need) { d = d0 - 2; above = ex + c0 + c1; in = c2; }
         else { d = d0 - 3; above = ex + c0 + c1 + c2; in = c3; }
-        sh[0] = d;
-        sh[1] = above;
-        sh[2] = in;
+        sv[0] = d;
+        sv[1] = above;
+        sv[2] = in;
       }
-      if (lane == 0 && total < need) sh[0] = -1;
+      if (lane == 0 && total < need) sv[0] = -1;
     }
     __syncthreads();
-    const int d = sh[0], above = sh[1], in = sh[2];
-    __syncthreads();
+    const int d = sv[0], above = sv[1], in = sv[2];
     if (d < 0) return 0ull;
     prefix |= (uint64_t)d << shift;
     need -= above;
@@ -213,6 +232,8 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   uint64_t* cbuf = reinterpret_cast<uint64_t*>(smem + off::cbuf);
   int* hist = reinterpret_cast<int*>(smem + off::hist);
   int* sh = reinterpret_cast<int*>(smem + off::sh);
+  int* khist = reinterpret_cast<int*>(smem + off::khist);
+  int* ksh = reinterpret_cast<int*>(smem + off::ksh);
   const int nbuf = P.S.nslot;   // frame rows in LDS: 1 or 2
   float* rows = reinterpret_cast<float*>(smem + off::end);
   const int rstride = off::a16(V * 4) / 4;
@@ -242,6 +263,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   if (nbuf == 2 && wave == 3 && nframes > 0)
     row_fetch_async(lp_row + (int64_t)sel[0] * P.stride_t, rows, V, P.vec4);
   int last_t = -1, step = 0, prevK = 0, nver = 0;
+  for (int i = tid; i < 2 * 256; i += kNT) khist[i] = 0;
   if (tid == 0) {
     sh[6] = sh[7] = 0;   // common token prefix of the live rows of parity 0 / 1
     sh[9] = 0;    // exact token comparisons
@@ -277,7 +299,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     auto lkey = [&](int c) -> uint64_t {
       return c == blank ? 0ull : compose(row[c], (uint32_t)c);
     };
-    const uint64_t xk = kth_largest(V, K, lkey, hist, sh);
+    const uint64_t xk = kth_largest<8>(V, K, lkey, khist, ksh);
     if (tid == 0) sh[2] = 0;
     __syncthreads();
     for (int c = tid; c < V; c += kNT) {
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       cbuf[4 * k + 3] = o1;
     }
     __syncthreads();
-    uint64_t tau = kth_largest(4 * W, W, [&](int i) { return cbuf[i]; }, hist, sh);
+    uint64_t tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
     if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
     const float tau_key = comp_key(tau);
     // per beam: open ranks considered (at most W - h + 1 open ones when its
@@ -523,7 +545,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         cbuf[i] = x >= tau ? x : 0ull;
       }
       __syncthreads();
-      uint64_t xw = kth_largest(nsurv, W, [&](int i) { return cbuf[i]; }, hist, sh);
+      uint64_t xw = kth_largest<4>(nsurv, W, [&](int i) { return cbuf[i]; }, khist, ksh);
       if (xw == 0ull) xw = 1ull;   // fewer than W candidates: all of them win
       if (tid == 0) sh[4] = 0;
       __syncthreads();
