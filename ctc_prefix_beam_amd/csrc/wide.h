@@ -156,8 +156,10 @@ __device__ __forceinline__ int count_above(const uint64_t* buf, int n, uint64_t 
   return r;
 }
 
-// Ranks the n keys of keys[0, n) (nonzero, pairwise distinct, n <= 64 *
-// kRankChunks) in descending order and calls out(rank, key) once per key.
+// Ranks the n keys of keys[0, n) (n <= 64 * kRankChunks; the nonzero ones
+// pairwise distinct) in descending order and calls out(rank, key) once per
+// nonzero key; zero keys rank below all others and are skipped.  keys may be
+// tmp itself.
 // Each wave sorts chunks of 64 keys in registers into tmp[0, 64 * chunks);
 // a key's rank is its place in its own chunk plus, for every other chunk, the
 // number of that chunk's keys above it (a binary search of the sorted chunk).
@@ -513,6 +515,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     __syncthreads();
     const int nsurv = sh[3];
     int nw;
+    bool ranked = false;   // win[0, nw) already holds the winners in rank order
     if (nsurv <= kCBuf) {
       // ---- top W (sec. 3.4.4 / 3.4.5) among the candidates at or above the
       // bound, each beam writing its own
@@ -544,17 +547,31 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
             (!ex && key > kNeg) ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
         cbuf[i] = x >= tau ? x : 0ull;
       }
-      __syncthreads();
-      uint64_t xw = kth_largest<4>(nsurv, W, [&](int i) { return cbuf[i]; }, khist, ksh);
-      if (xw == 0ull) xw = 1ull;   // fewer than W candidates: all of them win
       if (tid == 0) sh[4] = 0;
       __syncthreads();
-      for (int i = tid; i < nsurv; i += kNT) {
-        const uint64_t x = cbuf[i];
-        if (x != 0ull && x >= xw) kb64[atomicAdd(&sh[4], 1)] = x;
+      if (nsurv <= 64 * kRankChunks) {
+        // few survivors (the usual case): rank them all, in place, and keep
+        // the first W (zeros, the candidates below the bound, rank last and
+        // are skipped)
+        rank_keys(cbuf, nsurv, cbuf, [&](int r, uint64_t x) {
+          if (r < W) {
+            win[r] = x;
+            atomicMax(&sh[4], r + 1);
+          }
+        });
+        __syncthreads();
+        nw = sh[4];
+        ranked = true;
+      } else {
+        uint64_t xw = kth_largest<4>(nsurv, W, [&](int i) { return cbuf[i]; }, khist, ksh);
+        if (xw == 0ull) xw = 1ull;   // fewer than W candidates: all of them win
+        for (int i = tid; i < nsurv; i += kNT) {
+          const uint64_t x = cbuf[i];
+          if (x != 0ull && x >= xw) kb64[atomicAdd(&sh[4], 1)] = x;
+        }
+        __syncthreads();
+        nw = sh[4];
       }
-      __syncthreads();
-      nw = sh[4];
     } else {
       // many candidates at the bound (exact ties): every considered candidate,
       // held in registers, through a radix select
@@ -658,7 +675,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       __syncthreads();
       nw = sh[4];
     }
-    rank_keys(kb64, nw, cbuf, [&](int r, uint64_t x) { win[r] = x; });
+    if (!ranked) rank_keys(kb64, nw, cbuf, [&](int r, uint64_t x) { win[r] = x; });
     if (tid < kMaxW) s_bslot[tid] = -1;
     __syncthreads();
 
