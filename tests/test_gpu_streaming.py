@@ -276,3 +276,47 @@ def test_chunks_replayed_from_a_captured_graph():
         for a, b in zip(got, eager):
             assert np.array_equal(a, b), rep
         assert float(junk) == float(1 << 20)
+
+
+def test_bounded_page_pool_streams():
+    # streams with a page pool below the default: a stream whose high-water
+    # mark (row_stats [3], reported by the unbounded run) fits decodes exactly
+    # as before, a stream that needs more sets status bit 0; a reset clears it
+    S, T, V, W, CH = 6, 160, 300, 12, 16
+    lp, _ = synth.peaky(S, T, V, seed=33, p_blank=0.4)
+    print(f"[case] stream bounded pool S={S} T={T} V={V} W={W} ps=8", flush=True)
+    x = torch.from_numpy(lp).cuda()
+
+    def run(num_pages):
+        cfg = cpb.DecoderConfig(beam=W, nbest=W, capacity=T, max_out_len=T, paged=True,
+                                page_size=8, num_pages=num_pages)
+        pool = cpb.StreamPool(cfg, V, S)
+        for a in range(0, T, CH):
+            pool.chunk(x[:, a:a + CH])
+        t, l, s = pool.read()
+        st = pool.row_stats().cpu().numpy()
+        return pool, (t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()), st
+
+    _, full, st = run(0)
+    assert (st[:, 2] == 0).all()
+    assert_parity(full, oracle_streams(lp, W, T, CH, W, T), what="stream pool")
+    high = st[:, 3].copy()
+    npages = int(np.median(high))
+    fits = high <= npages
+    assert fits.any() and (~fits).any(), high
+    pool, got, st = run(npages)
+    assert np.array_equal(st[:, 2] & 1, (~fits).astype(st.dtype))
+    for b in np.nonzero(fits)[0]:
+        for a, e in zip(got, full):
+            assert np.array_equal(a[b], e[b])
+    # the flagged streams start again, on their own, and their first chunk
+    # decodes as in an unbounded pool
+    idx = [int(i) for i in np.nonzero(~fits)[0]]
+    bad = torch.tensor(idx, dtype=torch.int32, device="cuda")
+    pool.reset(bad)
+    pool.chunk(x[idx, :CH], rows=bad)
+    st = pool.row_stats().cpu().numpy()
+    assert (st[:, 2] == 0).all()
+    t, l, s = pool.read(bad)
+    ref = oracle_streams(lp[np.nonzero(~fits)[0], :CH], W, T, CH, W, T)
+    assert_parity((t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()), ref, what="after reset")
