@@ -142,20 +142,6 @@ __device__ uint64_t kth_largest(int n, int kth, Gen gen, int* khist, int* ksh) {
   return prefix;
 }
 
-// Number of keys of buf[0, n) above x.  buf is 16-byte aligned and zero from
-// n up to the next multiple of 8 (zeros are below every key counted); eight
-// keys are read per round, four 16-byte loads in flight.
-__device__ __forceinline__ int count_above(const uint64_t* buf, int n, uint64_t x) {
-  const ulonglong2* b2 = reinterpret_cast<const ulonglong2*>(buf);
-  int r = 0;
-  for (int j = 0; j < n; j += 8) {
-    const ulonglong2 a = b2[j / 2], b = b2[j / 2 + 1], c = b2[j / 2 + 2], d = b2[j / 2 + 3];
-    r += (a.x > x) + (a.y > x) + (b.x > x) + (b.y > x) + (c.x > x) + (c.y > x) + (d.x > x) +
-         (d.y > x);
-  }
-  return r;
-}
-
 // Ranks the n keys of keys[0, n) (n <= 64 * kRankChunks; the nonzero ones
 // pairwise distinct) in descending order and calls out(rank, key) once per
 // nonzero key; zero keys rank below all others and are skipped.  keys may be
@@ -177,6 +163,7 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
     const uint64_t x = tmp[i];
     const int own = i >> 6;
     int r = i & 63;
+    if (nch > 1) {
 #pragma unroll
     for (int c = 0; c < kRankChunks; c++) {
       const uint64_t* a = tmp + (c < nch ? c : 0) * 64;
@@ -185,6 +172,7 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
       for (int st = 32; st >= 1; st >>= 1) lo += a[lo + st - 1] > x ? st : 0;
       lo += a[lo] > x ? 1 : 0;   // lo <= 63 before this
       r += (c < nch && c != own) ? lo : 0;
+    }
     }
     if (x != 0ull) out(r, x);
   }
@@ -445,7 +433,6 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       }
       const uint64_t b1 = cb > cc ? cb : cc;
       s_head[k] = b1 > o0 ? b1 : o0;
-      if (k + W < kMaxW) s_head[k + W] = 0ull;   // (zero past the beam for count_above)
       cbuf[4 * k + 0] = cb;
       cbuf[4 * k + 1] = cc;
       cbuf[4 * k + 2] = o0;
@@ -455,6 +442,10 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     uint64_t tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
     if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
     const float tau_key = comp_key(tau);
+    // each live beam's place h - 1 among the beams' bests (in s_lim until the
+    // beam overwrites it below)
+    rank_keys(s_head, W, kb64, [&](int r, uint64_t x) { s_lim[comp_id(x) >> kIdShift] = r; });
+    __syncthreads();
     // per beam: open ranks considered (at most W - h + 1 open ones when its
     // best is the h-th best of the beams), and the leading ones whose key
     // reaches the bound
@@ -463,22 +454,43 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       const uint64_t mine = s_head[k];
       int lim = 0, reach = 0;
       if (mine != 0ull) {
-        const int h = 1 + count_above(s_head, W, mine);
-        int want = W - h + 1;
-        for (int w = 0; w < kExw && want > 0; w++) {
-          const int base = w * 32;
-          const int nb = min(32, K - base);
-          if (nb <= 0) break;
-          uint32_t open = ~s_exm[k * kExw + w] & (nb >= 32 ? ~0u : ((1u << nb) - 1u));
-          const int cnt = __popc(open);
-          if (cnt < want) {
-            want -= cnt;
-            lim = base + nb;
-          } else {
-            for (int x = 1; x < want; x++) open &= open - 1u;
-            lim = base + __ffs((int)open);
-            want = 0;
+        const int h = 1 + s_lim[k];
+        // the (W - h + 1)-th open rank: every exclusion word loaded at once,
+        // the word holding it found by running popcounts, the bit inside it by
+        // halving (all ranks below K when fewer are open)
+        const int want = W - h + 1;
+        uint32_t wd[kExw];
+#pragma unroll
+        for (int w = 0; w < kExw; w++) {
+          const int nb = K - w * 32;
+          const uint32_t valid = nb >= 32 ? ~0u : (nb <= 0 ? 0u : ((1u << nb) - 1u));
+          wd[w] = ~s_exm[k * kExw + w] & valid;
+        }
+        lim = K;
+        int acc = 0, fr = 0, fbase = -1;
+        uint32_t fv = 0u;
+#pragma unroll
+        for (int w = 0; w < kExw; w++) {
+          const int c = __popc(wd[w]);
+          if (fbase < 0 && acc + c >= want) {
+            fbase = w * 32;
+            fv = wd[w];
+            fr = want - acc;   // 1-based among the word's set bits
           }
+          acc += c;
+        }
+        if (fbase >= 0) {
+          int pos = 0;
+#pragma unroll
+          for (int sh2 = 16; sh2 >= 1; sh2 >>= 1) {
+            const int c = __popc(fv & ((1u << sh2) - 1u));
+            if (c < fr) {
+              fr -= c;
+              pos += sh2;
+              fv >>= sh2;
+            }
+          }
+          lim = fbase + pos + 1;
         }
         // keys A + Rl[r] do not increase with r: binary search of the first
         // rank below the bound
