@@ -230,8 +230,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this decoder shards by utterance/stream with no "
-              f"exchange, and multi-GPU runs are not part of this build (got --gpus "
+        print(f"bench.py runs on one GPU only: the decoder shards by utterance/stream with no "
+              f"exchange between GPUs, and this benchmark measures one GPU's share (got --gpus "
               f"{args.gpus}).", file=sys.stderr)
         sys.exit(2)
 

@@ -2221,7 +2221,7 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
     return fail(CTCPB_ERR_INVALID, "nbest must be in [1, beam]");
   if (cfg->vocab < 2) return fail(CTCPB_ERR_INVALID, "vocab must be >= 2");
   if (cfg->vocab > kMaxVocab)
-    return fail(CTCPB_ERR_UNSUPPORTED, "vocab > 16384 is not supported by this build");
+    return fail(CTCPB_ERR_UNSUPPORTED, "vocab > 16384 is not supported");
   if (cfg->blank_id < 0 || cfg->blank_id >= cfg->vocab)
     return fail(CTCPB_ERR_INVALID, "blank_id must be in [0, vocab)");
   if (cfg->max_out_len < 0) return fail(CTCPB_ERR_INVALID, "max_out_len must be >= 0");

@@ -21,7 +21,7 @@
 
 namespace ctcpb {
 
-constexpr int kMaxBeam = 32;     // widest beam of this build
+constexpr int kMaxBeam = 32;     // widest beam of the fused decoder
 constexpr int kHdrInts = 64;
 constexpr int kInvalidPage = -1;
 

@@ -38,7 +38,7 @@ enum {
   CTCPB_OK = 0,
   CTCPB_ERR_INVALID = 1,     /* an argument is out of range or inconsistent */
   CTCPB_ERR_TOO_SMALL = 2,   /* workspace / state buffer smaller than required */
-  CTCPB_ERR_UNSUPPORTED = 3, /* valid but outside this build (beam > 32 with paged storage
+  CTCPB_ERR_UNSUPPORTED = 3, /* valid but not supported by this library (beam > 32 with paged storage
                                 or streaming, LDS budget) */
   CTCPB_ERR_DEVICE = 4       /* a HIP launch failed */
 };
@@ -50,7 +50,7 @@ typedef struct {
   int32_t beam;            /* beam width W, 1..128 (sec. 10); beams above 32 (the page's
                               multi-kernel path) are decoded offline with flat storage only */
   int32_t nbest;           /* hypotheses reported per row, 1..beam */
-  int32_t vocab;           /* V >= 2, at most 16384 in this build */
+  int32_t vocab;           /* V >= 2, at most 16384 */
   int32_t blank_id;        /* 0 <= blank_id < vocab */
   float blank_threshold;   /* offline frame skip (sec. 3.5): frame t is decoded iff
                               log_prob[t, blank] < log(blank_threshold); >= 1 keeps
