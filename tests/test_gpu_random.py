@@ -1,7 +1,11 @@
 """Seeded random configurations against the oracle: beam, vocabulary, blank id,
 threshold, storage, page size, frame lengths and streaming chunkings drawn
 from one generator, so that combinations no hand-written case covers are
-exercised.  Every case prints its parameters before it runs."""
+exercised.  Every case prints its parameters before it runs.  The number of
+cases can be raised with CTCPB_RANDOM_CASES (offline; a tenth of it for
+streaming) for a longer sweep."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -31,7 +35,11 @@ def draw(seed):
                 p_blank=p_blank, seed=seed)
 
 
-@pytest.mark.parametrize("seed", range(48))
+N_OFFLINE = int(os.environ.get("CTCPB_RANDOM_CASES", "48"))
+N_STREAMING = max(16, N_OFFLINE // 10)
+
+
+@pytest.mark.parametrize("seed", range(N_OFFLINE))
 def test_random_offline(seed):
     c = draw(seed)
     print(f"[case] random offline {c}", flush=True)
@@ -44,7 +52,7 @@ def test_random_offline(seed):
     assert_parity(got, ref, what=f"random {seed}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(N_STREAMING))
 def test_random_streaming(seed):
     c = draw(100 + seed)
     W = min(c["W"], 32)
