@@ -106,6 +106,22 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _check_dev(t, device, name, dtype=None, shape=None, contiguous=False):
+    """Raise ValueError unless `t` is a GPU tensor on `device` (and of the given
+    dtype, shape and layout): the library hands raw device pointers to its
+    kernels, so a host tensor or one on another GPU must never reach it."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def workspace_size(cfg: DecoderConfig, vocab: int, batch: int, max_T: int,
                    max_out_len: int | None = None) -> int:
     out = ctypes.c_size_t()
@@ -132,15 +148,17 @@ class OfflineDecoder:
         """log_prob: (B, T, V) float32 on the GPU, unit stride over V;
         seq_lengths: (B,) int32 on the GPU.  Returns (tokens (B, N, max_out_len)
         int32, lengths (B, N) int32, scores (B, N) float32) on the GPU."""
-        if log_prob.dtype != torch.float32 or log_prob.dim() != 3 or not log_prob.is_cuda:
+        if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda:
+            raise ValueError("log_prob must be a GPU tensor")
+        dev = log_prob.device
+        if log_prob.dtype != torch.float32 or log_prob.dim() != 3:
             raise ValueError("log_prob must be a 3-D float32 GPU tensor")
         if log_prob.stride(2) != 1:
             raise ValueError("log_prob must have unit stride over the vocabulary")
-        if seq_lengths.dtype != torch.int32 or seq_lengths.dim() != 1 or not seq_lengths.is_cuda:
-            raise ValueError("seq_lengths must be a 1-D int32 GPU tensor")
         B, T, V = log_prob.shape
-        if seq_lengths.shape[0] != B:
-            raise ValueError("seq_lengths must have one entry per row")
+        _check_dev(seq_lengths, dev, "seq_lengths", torch.int32, (B,), contiguous=True)
+        if self.workspace is not None and self.workspace.device != dev:
+            self.workspace = None   # a decoder reused on another GPU gets a new workspace
         cfg = self.cfg
         N = cfg.nbest or cfg.beam
         mol = T if cfg.max_out_len is None else cfg.max_out_len
@@ -155,6 +173,9 @@ class OfflineDecoder:
                    torch.empty((B, N), dtype=torch.int32, device=log_prob.device),
                    torch.empty((B, N), dtype=torch.float32, device=log_prob.device))
         toks, lens, scores = out
+        _check_dev(toks, dev, "out tokens", torch.int32, (B, N, mol), contiguous=True)
+        _check_dev(lens, dev, "out lengths", torch.int32, (B, N), contiguous=True)
+        _check_dev(scores, dev, "out scores", torch.float32, (B, N), contiguous=True)
         _check(lib().ctcpb_decode_offline(
             ctypes.byref(c), _ptr(log_prob), log_prob.stride(0), log_prob.stride(1), B, T,
             _ptr(seq_lengths), _ptr(self.workspace), self.workspace.numel(), _ptr(toks),
@@ -193,7 +214,15 @@ class StreamPool:
         _check(lib().ctcpb_stream_init(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
                                        num_streams, _stream(stream)))
 
+    def _rows(self, rows, n=None):
+        if rows is not None:
+            _check_dev(rows, self.state.device, "rows", torch.int32, contiguous=True)
+            if rows.dim() != 1 or (n is not None and rows.numel() != n):
+                raise ValueError("rows must be a 1-D int32 tensor with one entry per row")
+        return rows
+
     def reset(self, rows: torch.Tensor | None = None, stream=None):
+        self._rows(rows)
         n = self.num_streams if rows is None else rows.numel()
         _check(lib().ctcpb_stream_reset(ctypes.byref(self.c), _ptr(self.state), self.nbytes,
                                         self.num_streams, _ptr(rows), n, _stream(stream)))
@@ -205,22 +234,21 @@ class StreamPool:
         (n_rows, chunk_T) uint8 on the GPU, 0 = skip the frame; start_frame:
         optional (n_rows,) int32 on the GPU, the number of each row's first
         frame (default: the stream's own frame count)."""
-        if log_prob_chunk.dtype != torch.float32 or log_prob_chunk.dim() != 3:
+        _check_dev(log_prob_chunk, self.state.device, "log_prob_chunk", torch.float32)
+        if log_prob_chunk.dim() != 3:
             raise ValueError("log_prob_chunk must be a 3-D float32 tensor")
         if log_prob_chunk.stride(2) != 1:
             raise ValueError("log_prob_chunk must have unit stride over the vocabulary")
         n, T, V = log_prob_chunk.shape
         if V != self.vocab:
             raise ValueError("vocabulary size differs from the pool's")
-        if rows is not None and (rows.dtype != torch.int32 or rows.numel() != n):
-            raise ValueError("rows must be an int32 tensor with one entry per chunk row")
-        if is_speech is not None and (is_speech.dtype != torch.uint8 or
-                                      tuple(is_speech.shape) != (n, T) or
-                                      not is_speech.is_contiguous()):
-            raise ValueError("is_speech must be a contiguous (n_rows, chunk_T) uint8 tensor")
-        if start_frame is not None and (start_frame.dtype != torch.int32 or
-                                        start_frame.numel() != n):
-            raise ValueError("start_frame must be an int32 tensor with one entry per chunk row")
+        self._rows(rows, n)
+        if is_speech is not None:
+            _check_dev(is_speech, self.state.device, "is_speech", torch.uint8, (n, T),
+                       contiguous=True)
+        if start_frame is not None:
+            _check_dev(start_frame, self.state.device, "start_frame", torch.int32, (n,),
+                       contiguous=True)
         if is_speech is None and start_frame is None:
             _check(lib().ctcpb_stream_chunk(
                 ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
@@ -237,18 +265,18 @@ class StreamPool:
         """One frame per row: log_prob_frame (n_rows, V) float32 on the GPU,
         decoded as frame number frame_index[i] (int32 on the GPU; default: the
         stream's own frame count) of stream rows[i]."""
-        if log_prob_frame.dtype != torch.float32 or log_prob_frame.dim() != 2:
+        _check_dev(log_prob_frame, self.state.device, "log_prob_frame", torch.float32)
+        if log_prob_frame.dim() != 2:
             raise ValueError("log_prob_frame must be a 2-D float32 tensor")
         if log_prob_frame.stride(1) != 1:
             raise ValueError("log_prob_frame must have unit stride over the vocabulary")
         n, V = log_prob_frame.shape
         if V != self.vocab:
             raise ValueError("vocabulary size differs from the pool's")
-        if rows is not None and (rows.dtype != torch.int32 or rows.numel() != n):
-            raise ValueError("rows must be an int32 tensor with one entry per row")
-        if frame_index is not None and (frame_index.dtype != torch.int32 or
-                                        frame_index.numel() != n):
-            raise ValueError("frame_index must be an int32 tensor with one entry per row")
+        self._rows(rows, n)
+        if frame_index is not None:
+            _check_dev(frame_index, self.state.device, "frame_index", torch.int32, (n,),
+                       contiguous=True)
         _check(lib().ctcpb_stream_step(
             ctypes.byref(self.c), _ptr(self.state), self.nbytes, self.num_streams,
             _ptr(log_prob_frame), log_prob_frame.stride(0), _ptr(frame_index), _ptr(rows), n,
@@ -262,6 +290,7 @@ class StreamPool:
         return out
 
     def read(self, rows: torch.Tensor | None = None, stream=None):
+        self._rows(rows)
         n = self.num_streams if rows is None else rows.numel()
         N = self.cfg.nbest or self.cfg.beam
         dev = self.state.device

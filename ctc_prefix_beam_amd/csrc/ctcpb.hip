@@ -2057,7 +2057,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.rank = slot_rank(sl);
     const int t = frame_t[sl];
     C.frame = f;
-    C.grow = lp_row + (int64_t)(STREAM ? f : t) * stride_t;
+    // its row in global memory: offline, frame t of the row; streaming, chunk
+    // row t - frame0 (not f: with a speech mask, step f of the chunk decodes
+    // the f-th flagged frame, which can sit further into the chunk)
+    C.grow = lp_row + (int64_t)(STREAM ? t - frame0 : t) * stride_t;
     Winner w;
     if (__builtin_expect(step == 0, 0)) {
       first_step(C, b, row, t > 0 ? 1 : 0, K);
@@ -2409,8 +2412,9 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   if (!log_prob || !seq_lengths || !workspace || !out_lengths || !out_scores ||
       (!out_tokens && R.mol > 0))
     return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
-  if (max_T > 0 && (stride_t < R.V || (batch > 1 && stride_b < (int64_t)max_T * 0)))
-    return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
+  if (max_T > 0 && stride_t < R.V) return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
+  if (stride_b < 0)
+    return fail(CTCPB_ERR_INVALID, "stride_b must be >= 0 (0: every row reads the same frames)");
   if (!aligned16(workspace)) return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
   if (int rc = check_wide(R, false)) return rc;
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
@@ -2506,6 +2510,8 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
   if (n_rows == 0 || chunk_T == 0) return ok();
   if (!state || !log_prob_chunk) return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
   if (stride_t < R.V) return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
+  if (stride_row < 0)
+    return fail(CTCPB_ERR_INVALID, "stride_row must be >= 0 (0: every row reads the same frames)");
   if (!aligned16(state)) return fail(CTCPB_ERR_INVALID, "state must be 16-byte aligned");
   const Layout L = layout_for(R, R.cap_stream, 0);
   if (state_bytes < (size_t)num_streams * (size_t)L.row_bytes)
@@ -2563,6 +2569,7 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
   if (n_rows == 0) return ok();
   if (!state || !out_lengths || !out_scores || (!out_tokens && R.mol > 0))
     return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned16(state)) return fail(CTCPB_ERR_INVALID, "state must be 16-byte aligned");
   const Layout L = layout_for(R, R.cap_stream, 0);
   if (state_bytes < (size_t)num_streams * (size_t)L.row_bytes)
     return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");

@@ -82,17 +82,29 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
 /* Offline batch decode (sec. 3.7).
  *   log_prob     device, float32; element (b, t, c) at
  *                log_prob[b*stride_b + t*stride_t + c] (unit stride over the
- *                vocabulary); only frames t < seq_lengths[b] are read, so
- *                padding may hold anything (even NaN).  Values must be finite.
+ *                vocabulary, stride_t >= vocab, stride_b >= 0; 0 makes every
+ *                row read the same frames); only frames t < seq_lengths[b] are
+ *                read, so padding may hold anything (even NaN).  Values must
+ *                be finite.  Rows are read with 16-byte loads when log_prob,
+ *                stride_b and stride_t are multiples of 4 floats and vocab %
+ *                4 == 0, else 4 bytes at a time.
  *   seq_lengths  device, int32 [batch]; clamped to [0, max_T] on the device.
- *   workspace    device, >= ctcpb_workspace_size bytes, 256-byte aligned; its
- *                contents on entry do not matter.
+ *   workspace    device, >= ctcpb_workspace_size bytes, 16-byte aligned; its
+ *                contents on entry do not matter.  It holds the decode's
+ *                state until the call completes (and its counters afterwards,
+ *                see ctcpb_row_stats): calls that share a workspace must not
+ *                overlap.
  *   out_tokens   device, int32 [batch][nbest][max_out_len], -1 padded
  *   out_lengths  device, int32 [batch][nbest], full hypothesis lengths
  *   out_scores   device, float32 [batch][nbest]
  * Hypotheses are reported in (score descending, slot ascending) order.  A row
  * with no decodable frame reports the empty hypothesis at score 0 (sec. 13).
- * No host synchronisation happens inside the call. */
+ * No host synchronisation happens inside the call.  Per-row status bits
+ * (ctcpb_row_stats [2]) flag rows whose outputs are not a complete decode:
+ * value 1, a paged row ran out of pages; value 2, the row's decode was abandoned
+ * (a bounded internal wait between the kernel's wave roles gave up, which a
+ * correct launch never reaches) and its outputs hold the hypotheses of the
+ * last completed step or are unspecified. */
 int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
                          int64_t stride_t, int32_t batch, int32_t max_T,
                          const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
@@ -105,7 +117,7 @@ int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_b
 
 /* Put every stream of the blob in the fresh state (no frame decoded; reads
  * back the empty hypothesis).  state: device, >= ctcpb_state_size bytes,
- * 256-byte aligned. */
+ * 16-byte aligned (every call that takes the blob checks this). */
 int ctcpb_stream_init(const ctcpb_config* cfg, void* state, size_t state_bytes,
                       int32_t num_streams, void* stream);
 
@@ -117,8 +129,8 @@ int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
 
 /* Decode one chunk of frames for n_rows streams at once (sec. 3.4.8 / 3.4.9):
  * row i of log_prob_chunk (element (i, t, c) at i*stride_row + t*stride_t + c,
- * device float32, finite) continues stream rows[i] (NULL: stream i; distinct
- * indices required).  Every frame is decoded (no skipping); frames past a
+ * device float32, finite; stride_t >= vocab, stride_row >= 0) continues stream
+ * rows[i] (NULL: stream i; distinct indices required).  Every frame is decoded (no skipping); frames past a
  * stream's capacity are ignored.  The state stays on the device; nothing is
  * read back.  Same as ctcpb_stream_chunk_ex with no mask and no start frame. */
 int ctcpb_stream_chunk(const ctcpb_config* cfg, void* state, size_t state_bytes,
@@ -168,8 +180,10 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
  * of that decode) or in a streaming state blob (max_T = 0), for diagnostics:
  * out (device int32 [num_rows][8]) receives per row
  *   [0] frames decoded  [1] offline: frames selected; streaming: frames
- *   given so far (the next frame's number)  [2] status bits
- *   (1 = a paged row ran out of pages)  [3] paged: most pages in use at once
+ *   given so far (the next frame's number)  [2] status bits (value 1: a
+ *   paged row ran out of pages; value 2: the row's decode was abandoned
+ *   when a bounded wait inside the kernel gave up, so its outputs are not a
+ *   complete decode; stream_reset clears both)  [3] paged: most pages in use at once
  *   [4] steps that needed the full beam x vocab selection  [5] exact token
  *   comparisons made for the merge test  [6] common token prefix of the live
  *   beams (flat)  [7] leading pages shared by every live beam (paged). */

@@ -53,6 +53,8 @@ def lib():
         L.oracle_log1p.argtypes = [f32]
         L.oracle_lse.restype = f32
         L.oracle_lse.argtypes = [f32, f32]
+        L.oracle_math_sweep.restype = None
+        L.oracle_math_sweep.argtypes = [i32, ctypes.c_uint32, i64, p, p, p]
         L.oracle_log_threshold.restype = f32
         L.oracle_log_threshold.argtypes = [f32]
         L.oracle_select_frames.restype = i32
@@ -94,6 +96,32 @@ def log1p(x: float) -> float:
 
 def lse(a: float, b: float) -> float:
     return lib().oracle_lse(float(a), float(b))
+
+
+def math_sweep(op: int, first_bits: int, n: int, a=None, b=None, threads: int = 1) -> np.ndarray:
+    """The oracle's exp (op 0), log1p (op 1) or x / (2 + x) (op 2) of the n
+    floats whose bit patterns start at first_bits, or lse(a, b) (op 3), as a
+    float32 array.  Runs on `threads` threads (ctypes releases the GIL)."""
+    out = np.empty(n, np.float32)
+    if op == 3:
+        a = np.ascontiguousarray(a, np.float32)
+        b = np.ascontiguousarray(b, np.float32)
+        assert a.shape == b.shape == (n,)
+
+    def part(lo, hi):
+        pa = None if op != 3 else a[lo:hi].ctypes.data_as(ctypes.c_void_p)
+        pb = None if op != 3 else b[lo:hi].ctypes.data_as(ctypes.c_void_p)
+        lib().oracle_math_sweep(op, (first_bits + lo) & 0xffffffff, hi - lo, pa, pb,
+                                out[lo:hi].ctypes.data_as(ctypes.c_void_p))
+
+    if threads <= 1 or n < 1 << 16:
+        part(0, n)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        step = -(-n // threads)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda lo: part(lo, min(n, lo + step)), range(0, n, step)))
+    return out
 
 
 def select_frames(lp_row: np.ndarray, length: int, blank: int, threshold: float) -> np.ndarray:
@@ -191,25 +219,24 @@ class Stream:
             pass
 
 
-def _decode_rows_worker(args):
-    (lp, lens, beam, nbest, blank, threshold, max_out_len) = args
-    return decode(lp, lens, beam, nbest, blank, threshold, max_out_len)
-
-
 def decode_parallel(log_prob, seq_lengths, beam, nbest=None, blank=0, threshold=1.0,
                     max_out_len=None, processes: int = 1):
-    """Rows spread over a process pool (rows are independent).  Same results
-    as ``decode``; used for the CPU baseline timing."""
+    """Rows spread over `processes` threads of this process (rows are
+    independent, each decode is single-threaded C and ctypes releases the
+    GIL).  Same results as ``decode``."""
     if processes <= 1:
         return decode(log_prob, seq_lengths, beam, nbest, blank, threshold, max_out_len)
-    import multiprocessing as mp
+    from concurrent.futures import ThreadPoolExecutor
     B = log_prob.shape[0]
     nbest = beam if nbest is None else nbest
     max_out_len = log_prob.shape[1] if max_out_len is None else max_out_len
     lens = np.asarray(seq_lengths, np.int32)
-    jobs = [(log_prob[b:b + 1], lens[b:b + 1], beam, nbest, blank, threshold, max_out_len)
-            for b in range(B)]
-    with mp.get_context("fork").Pool(processes) as pool:
-        parts = pool.map(_decode_rows_worker, jobs)
+
+    def one(b):
+        return decode(log_prob[b:b + 1], lens[b:b + 1], beam, nbest, blank, threshold,
+                      max_out_len)
+
+    with ThreadPoolExecutor(processes) as ex:
+        parts = list(ex.map(one, range(B)))
     return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
             np.concatenate([p[2] for p in parts]))

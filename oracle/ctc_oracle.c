@@ -111,6 +111,26 @@ float oracle_lse(float a, float b)
     return m + oracle_log1p(oracle_exp(d));
 }
 
+/* The functions above over a range of inputs, for exhaustive comparisons:
+ * element i uses the float whose bit pattern is first_bits + i (op 0 exp,
+ * 1 log1p, 2 the IEEE quotient x / (2 + x) that log1p starts from), or the
+ * pair (a[i], b[i]) (op 3 lse). */
+void oracle_math_sweep(int op, uint32_t first_bits, int64_t n, const float *a, const float *b,
+                       float *out)
+{
+    for (int64_t i = 0; i < n; i++) {
+        float x;
+        uint32_t u = first_bits + (uint32_t)i;
+        memcpy(&x, &u, sizeof x);
+        switch (op) {
+        case 0: out[i] = oracle_exp(x); break;
+        case 1: out[i] = oracle_log1p(x); break;
+        case 2: out[i] = x / (2.0f + x); break;
+        default: out[i] = oracle_lse(a[i], b[i]); break;
+        }
+    }
+}
+
 /* ---------------------------------------------------------------------- */
 /* Frame selection (sec. 3.5).                                              */
 /* ---------------------------------------------------------------------- */
@@ -166,7 +186,9 @@ static int slot_clast(const Slot *s, int blank)
     return s->len > 0 ? s->tok[s->len - 1] : blank;
 }
 
-static const float *g_rank_lp; /* comparator context (single-threaded oracle) */
+/* comparator context of qsort: per thread, so that independent decodes may run
+ * on threads of one process (each decode itself is single-threaded) */
+static _Thread_local const float *g_rank_lp;
 
 static int cmp_vocab_rank(const void *a, const void *b)
 {
@@ -177,7 +199,7 @@ static int cmp_vocab_rank(const void *a, const void *b)
     return (ca < cb) ? -1 : (ca > cb);
 }
 
-static const float *g_keys;
+static _Thread_local const float *g_keys;
 
 static int cmp_candidates(const void *a, const void *b)
 {

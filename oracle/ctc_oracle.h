@@ -13,6 +13,12 @@ float oracle_log1p(float x);   /* x in [0, 1]   */
 float oracle_lse(float a, float b);
 float oracle_log_threshold(float threshold);
 
+/* exp (op 0), log1p (op 1) or the quotient x / (2 + x) (op 2) of the floats
+ * with bit patterns first_bits .. first_bits + n - 1, or lse(a[i], b[i])
+ * (op 3), into out[0 .. n). */
+void oracle_math_sweep(int op, uint32_t first_bits, int64_t n, const float *a, const float *b,
+                       float *out);
+
 /* Frame selection of one row: writes the selected frame indices (ascending)
  * to sel and returns their count. */
 int oracle_select_frames(const float *lp_row, int64_t stride_t, int len, int blank,

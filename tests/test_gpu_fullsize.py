@@ -1,7 +1,11 @@
 """The five workloads at full size, in the launch configuration the benchmark
-times (one call for the whole batch / all streams): sampled rows against the
-oracle, every row against the cross-path identities (flat = paged, streaming
-= offline)."""
+times (one call for the whole batch / all streams), against the oracle: every
+row of bpe256 and bpe1024, 16 rows of vocab5000 for each of three seeds, 64 of
+the 256 streams of stream512; and every row against the cross-path identities
+(flat = paged, streaming = offline).  The oracle runs one row per thread over
+the host's cores (at most 16)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -13,10 +17,13 @@ from gpu_util import assert_parity, gpu_offline
 
 pytestmark = pytest.mark.gpu
 
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
 
 def sampled_oracle(lp_dev, lens, rows, wl, mol):
     lp = lp_dev[rows].cpu().numpy()
-    return oracle.decode(lp, lens[rows], wl.beam, wl.nbest, 0, wl.threshold, mol)
+    return oracle.decode_parallel(lp, lens[rows], wl.beam, wl.nbest, 0, wl.threshold, mol,
+                                  processes=THREADS)
 
 
 def subset(got, rows):
@@ -28,36 +35,56 @@ def test_bpe256_full_all_rows():
     lp, lens = wl.make(0)
     print(f"[case] bpe256 full B={wl.B}", flush=True)
     got = gpu_offline(lp, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
-    ref = oracle.decode(lp, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
+    ref = oracle.decode_parallel(lp, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len,
+                                 processes=THREADS)
     assert_parity(got, ref, what="bpe256")
 
 
-def test_bpe1024_full_sampled():
+def test_bpe1024_full_all_rows():
     wl = synth.WORKLOADS["bpe1024"]
     x, lens = wl.make_device(0, "cuda")
     print(f"[case] bpe1024 full B={wl.B} T={wl.T}", flush=True)
     got = gpu_offline(x, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
-    rows = [0, 17, 42, 63]
+    rows = list(range(wl.B))
     ref = sampled_oracle(x, lens, rows, wl, wl.max_out_len)
-    assert_parity(subset(got, rows), ref, what="bpe1024")
+    assert_parity(got, ref, what="bpe1024")
     paged = gpu_offline(x, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len, paged=True)
     for a, b in zip(got, paged):
         assert np.array_equal(a, b)
 
 
-def test_vocab5000_full_sampled_flat_and_paged():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_vocab5000_full_sampled(seed):
     wl = synth.WORKLOADS["vocab5000"]
-    x, lens = wl.make_device(0, "cuda")
-    print(f"[case] vocab5000 full B={wl.B} T={wl.T} V={wl.V}", flush=True)
+    x, lens = wl.make_device(seed, "cuda")
+    print(f"[case] vocab5000 full B={wl.B} T={wl.T} V={wl.V} seed={seed}", flush=True)
     paged = gpu_offline(x, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len, paged=True)
-    flat = gpu_offline(x, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
-    for a, b in zip(flat, paged):
-        assert np.array_equal(a, b)
-    rows = [77]
+    if seed == 0:
+        flat = gpu_offline(x, lens, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
+        for a, b in zip(flat, paged):
+            assert np.array_equal(a, b)
+    # 16 rows spread over the batch, a different set per seed
+    rows = sorted({int(r) for r in (np.arange(16) * 8 + 3 * seed) % wl.B})
     ref = sampled_oracle(x, lens, rows, wl, wl.max_out_len)
-    assert_parity(subset(paged, rows), ref, what="vocab5000")
+    assert_parity(subset(paged, rows), ref, what=f"vocab5000 seed {seed}")
     # best paths are longer than the 512-token output: lengths report the full count
     assert (paged[1][:, 0] > wl.max_out_len).all()
+    del x
+    torch.cuda.empty_cache()
+
+
+def oracle_streams_parallel(lp, W, capacity, chunk, nbest, mol):
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(s):
+        st = oracle.Stream(W, lp.shape[2], 0, capacity)
+        for a in range(0, lp.shape[1], chunk):
+            st.feed(lp[s, a:a + chunk])
+        return st.read(nbest, mol)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        outs = list(ex.map(one, range(lp.shape[0])))
+    return tuple(np.stack([o[i] for o in outs]) for i in range(3))
 
 
 def test_stream512_full_sampled():
@@ -71,15 +98,8 @@ def test_stream512_full_sampled():
     t, l, s = pool.read()
     torch.cuda.synchronize()
     got = (t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy())
-    rows = [0, 255]
-    lp = x[rows].cpu().numpy()
-    outs = []
-    for i in range(len(rows)):
-        st = oracle.Stream(wl.beam, wl.V, 0, 4096)
-        for a in range(0, wl.T, wl.chunk):
-            st.feed(lp[i, a:a + wl.chunk])
-        outs.append(st.read(wl.nbest, wl.T))
-    ref = tuple(np.stack([o[i] for o in outs]) for i in range(3))
+    rows = list(range(0, wl.B, 4))                       # 64 streams
+    ref = oracle_streams_parallel(x[rows].cpu().numpy(), wl.beam, 4096, wl.chunk, wl.nbest, wl.T)
     assert_parity(subset(got, rows), ref, what="stream512")
     off = gpu_offline(x, np.full(wl.B, wl.T, np.int32), wl.beam, wl.nbest, 0, 1.0, wl.T)
     for a, b in zip(got, off):

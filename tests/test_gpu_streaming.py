@@ -320,3 +320,36 @@ def test_bounded_page_pool_streams():
     t, l, s = pool.read(bad)
     ref = oracle_streams(lp[np.nonzero(~fits)[0], :CH], W, T, CH, W, T)
     assert_parity((t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()), ref, what="after reset")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_masked_chunks_take_the_exact_selection_from_the_flagged_frame(paged):
+    # frames whose non-blank labels all share one log-probability force the
+    # full beam x vocabulary selection, which reads the decoded frame's row
+    # from global memory.  With a speech mask, the step that decodes the f-th
+    # flagged frame of a chunk must read that frame's row, not chunk row f:
+    # masked frames sit before uniform ones in every chunk
+    S, T, V, W, CH = 4, 64, 96, 12, 16
+    lp, _ = synth.peaky(S, T, V, seed=27, p_blank=0.5)
+    rng = np.random.default_rng(28)
+    flat = np.full(V, np.log(0.999 / (V - 1)), np.float32)   # blank below every label
+    flat[0] = np.float32(np.log(0.001))
+    mask = np.ones((S, T), np.uint8)
+    for a in range(0, T, CH):
+        mask[:, a:a + 3] = 0                                  # three masked frames first
+        pick = rng.random((S, CH - 3)) < 0.4
+        for s in range(S):
+            for j in np.nonzero(pick[s])[0]:
+                lp[s, a + 3 + j] = flat
+    print(f"[case] stream masked uniform S={S} T={T} V={V} W={W} paged={paged}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, paged=paged)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    m = torch.from_numpy(mask).cuda()
+    for a in range(0, T, CH):
+        pool.chunk(x[:, a:a + CH], is_speech=m[:, a:a + CH].contiguous())
+    got = read(pool)
+    st = pool.row_stats().cpu().numpy()
+    assert st[:, cpb.STAT_FIELDS.index("fallbacks")].sum() > 0, "no step took the full selection"
+    ref, _ = oracle_masked(lp, mask, W, 4096, CH, W, T)
+    assert_parity(got, ref, what="stream masked uniform")

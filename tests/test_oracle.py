@@ -241,6 +241,97 @@ def test_gap_golden(oracle_lib):
         assert s == pytest.approx(math.log(p), abs=1e-6)
 
 
+def test_gap_leading_skip_golden(oracle_lib):
+    # step 0 after skipped leading frames seeds the labels' mass into the
+    # blank-ending part (sec. 3.3 need_add_blank); the next frame repeats the
+    # first label, which only the blank-ending part can extend
+    g = json.load(open(os.path.join(GOLDEN, "gap_leading_skip.json")))
+    lp = f32log(g["probs"])
+    T = lp.shape[0]
+    assert list(oracle_lib.select_frames(lp, T, g["blank"], g["threshold"])) == [1, 2]
+    toks, L, S = oracle_lib.decode(lp[None], [T], g["beam"], g["nbest"], g["blank"],
+                                   g["threshold"], T)
+    hyps = live_hyps(toks[0], L[0], S[0])
+    assert [list(h) for h, _ in hyps] == g["expected_tokens"]
+    assert list(L[0]) == g["expected_lengths"]
+    for (_, s), p in zip(hyps, g["expected_scores_log"]):
+        assert s == pytest.approx(math.log(p), abs=1e-6)
+    # the same selection as a masked stream and as frames numbered 1, 2
+    st = oracle_lib.Stream(g["beam"], g["vocab"], g["blank"])
+    st.feed(lp, is_speech=[0, 1, 1])
+    assert [list(h) for h, _ in live_hyps(*st.read(g["nbest"], T))] == g["expected_tokens"]
+    st = oracle_lib.Stream(g["beam"], g["vocab"], g["blank"])
+    st.step_at(lp[1], 1)
+    st.step_at(lp[2], 2)
+    t2, l2, s2 = st.read(g["nbest"], T)
+    assert (t2 == toks[0]).all() and (l2 == L[0]).all() and (s2 == S[0]).all()
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_final_tie_golden(oracle_lib, case):
+    # exactly tied final scores: the order is (score desc, slot asc), the
+    # slots of a step being in (key desc, flat id asc) order
+    g = json.load(open(os.path.join(GOLDEN, "final_tie.json")))["cases"][case]
+    lp = f32log(g["probs"])
+    T = lp.shape[0]
+    toks, L, S = oracle_lib.decode(lp[None], [T], g["beam"], g["nbest"], g["blank"],
+                                   g["threshold"], T)
+    hyps = live_hyps(toks[0], L[0], S[0])
+    assert [list(h) for h, _ in hyps] == g["expected_tokens"]
+    assert list(L[0]) == g["expected_lengths"]
+    for (_, s), p in zip(hyps, g["expected_scores_log"]):
+        assert s == pytest.approx(math.log(p), abs=1e-6)
+    assert S[0, 0] == S[0, 1]          # the tie is exact in float32
+
+
+def brute_force_masked(lp, allowed, blank=0):
+    """{prefix: log P} over the alignments whose frame t emits a label of
+    allowed[t] (fp64, -inf log-probs excluded by construction)."""
+    lp64 = lp.astype(np.float64)
+    acc = {}
+    for path in itertools.product(*allowed):
+        s = float(sum(lp64[t, c] for t, c in enumerate(path)))
+        key = collapse(path, blank)
+        acc[key] = np.logaddexp(acc[key], s) if key in acc else s
+    return acc
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gap_rule_equals_certain_blank_frames(oracle_lib, seed):
+    # The gap rule (sec. 3.3 step 0, sec. 3.4 collapse before the tables and
+    # blank-slot rule, sec. 3.4.5 winners' reset) is what a frame that is
+    # blank with probability one does to every beam: (pb, pnb) becomes
+    # (logsumexp(pb, pnb), NEG) and nothing else survives.  So a decode that
+    # skips frames equals, when nothing is pruned, the exact posteriors of the
+    # selected frames with a certain-blank frame before (after step 0) and
+    # after each frame that follows a gap.  Pinned by enumeration.
+    V, T, theta = 3, 8, 0.9
+    lp, _ = synth.peaky(1, T, V, seed=200 + seed, p_blank=0.6, blank_bias=3.5,
+                        token_bias=1.5, repeat_p=0.5)
+    sel = list(oracle_lib.select_frames(lp[0], T, 0, theta))
+    assert 0 < len(sel) < T
+    frames, allowed = [], []
+    blank_only, every = [0], list(range(V))
+    for s, t in enumerate(sel):
+        gap = t > 0 if s == 0 else t > sel[s - 1] + 1
+        if gap and s > 0:
+            frames.append(np.zeros(V, np.float32))
+            allowed.append(blank_only)
+        frames.append(lp[0, t])
+        allowed.append(every)
+        if gap:
+            frames.append(np.zeros(V, np.float32))
+            allowed.append(blank_only)
+    exact = brute_force_masked(np.stack(frames), allowed)
+    W = len(exact) + V
+    toks, L, S = oracle_lib.decode(lp, [T], W, W, 0, theta, T)
+    got = live_hyps(toks[0], L[0], S[0])
+    assert {h for h, _ in got} == set(exact)
+    for h, sc in got:
+        assert sc == pytest.approx(exact[h], abs=2e-5), h
+    assert np.logaddexp.reduce([sc for _, sc in got]) == pytest.approx(0.0, abs=2e-5)
+
+
 # -------------------------------------------------------------- invariants --
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_invariants_on_workload_generators(oracle_lib, name):
