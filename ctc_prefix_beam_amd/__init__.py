@@ -24,7 +24,9 @@ FLAT, PAGED = 0, 1
 EXPORTS = ("ctcpb_workspace_size", "ctcpb_decode_offline", "ctcpb_state_size",
            "ctcpb_stream_init", "ctcpb_stream_reset", "ctcpb_stream_chunk",
            "ctcpb_stream_chunk_ex", "ctcpb_stream_step", "ctcpb_read_state",
-           "ctcpb_row_stats", "ctcpb_last_error", "ctcpb_version")
+           "ctcpb_row_stats", "ctcpb_decode_offline_noalloc", "ctcpb_last_error",
+           "ctcpb_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # CTCPB_NOALLOC_SCRATCH_BYTES
 STAT_FIELDS = ("frames", "selected", "status", "pages_high", "fallbacks", "verifies", "common_prefix",
                "shared_pages")
 
@@ -78,6 +80,7 @@ def lib():
         L.ctcpb_stream_step.argtypes = [cfgp, p, sz, i32, p, i64, p, p, i32, p]
         L.ctcpb_read_state.argtypes = [cfgp, p, sz, i32, p, i32, p, p, p, p]
         L.ctcpb_row_stats.argtypes = [cfgp, p, sz, i32, i32, p, p]
+        L.ctcpb_decode_offline_noalloc.argtypes = [cfgp, p, i64, i64, i32, i32, p, p, p, p, p]
         for name in EXPORTS[:-2]:  # all but the two string getters
             getattr(L, name).restype = ctypes.c_int
         L.ctcpb_last_error.restype = ctypes.c_char_p
@@ -190,6 +193,33 @@ class OfflineDecoder:
         _check(lib().ctcpb_row_stats(ctypes.byref(c), _ptr(self.workspace), self.workspace.numel(),
                                      B, T, _ptr(out), _stream(stream)))
         return out
+
+
+def decode_offline_noalloc(cfg: DecoderConfig, log_prob: torch.Tensor,
+                           seq_lengths: torch.Tensor, out, stream=None):
+    """ctcpb_decode_offline_noalloc: the offline decode with the library's
+    fixed device scratch as its workspace (no allocation by the library or
+    here).  `out` = (tokens (B, N, max_out_len) int32, lengths (B, N) int32,
+    scores (B, N) float32), preallocated on log_prob's GPU.  Calls that may
+    overlap on one GPU must be ordered by the caller (they share the scratch)."""
+    if not isinstance(log_prob, torch.Tensor) or not log_prob.is_cuda:
+        raise ValueError("log_prob must be a GPU tensor")
+    dev = log_prob.device
+    if log_prob.dtype != torch.float32 or log_prob.dim() != 3 or log_prob.stride(2) != 1:
+        raise ValueError("log_prob must be a 3-D float32 tensor with unit stride over V")
+    B, T, V = log_prob.shape
+    _check_dev(seq_lengths, dev, "seq_lengths", torch.int32, (B,), contiguous=True)
+    N = cfg.nbest or cfg.beam
+    toks, lens, scores = out
+    mol = toks.shape[2] if toks.dim() == 3 else -1
+    _check_dev(toks, dev, "out tokens", torch.int32, (B, N, mol), contiguous=True)
+    _check_dev(lens, dev, "out lengths", torch.int32, (B, N), contiguous=True)
+    _check_dev(scores, dev, "out scores", torch.float32, (B, N), contiguous=True)
+    c = cfg.c_struct(V, mol)
+    _check(lib().ctcpb_decode_offline_noalloc(
+        ctypes.byref(c), _ptr(log_prob), log_prob.stride(0), log_prob.stride(1), B, T,
+        _ptr(seq_lengths), _ptr(toks), _ptr(lens), _ptr(scores), _stream(stream)))
+    return toks, lens, scores
 
 
 def decode_offline(log_prob, seq_lengths, **kw):

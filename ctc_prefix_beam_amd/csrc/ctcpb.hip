@@ -2400,26 +2400,43 @@ int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_b
   return ok();
 }
 
-int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
-                         int64_t stride_t, int32_t batch, int32_t max_T,
-                         const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
-                         int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The offline decode with a workspace of `workspace_bytes` bytes.  With
+// `scratch_ws`, the workspace is the library's fixed device scratch array and
+// is resolved only after every host-side check has passed (its address is
+// taken from `get_ws`, which may fail).
+template <typename GetWs>
+int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
+                        int64_t stride_t, int32_t batch, int32_t max_T,
+                        const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
+                        bool scratch_ws, GetWs get_ws, int32_t* out_tokens, int32_t* out_lengths,
+                        float* out_scores, void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
   if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
   if (batch == 0) return ok();
-  if (!log_prob || !seq_lengths || !workspace || !out_lengths || !out_scores ||
+  if (!log_prob || !seq_lengths || (!workspace && !scratch_ws) || !out_lengths || !out_scores ||
       (!out_tokens && R.mol > 0))
     return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");
   if (max_T > 0 && stride_t < R.V) return fail(CTCPB_ERR_INVALID, "stride_t must be >= vocab");
   if (stride_b < 0)
     return fail(CTCPB_ERR_INVALID, "stride_b must be >= 0 (0: every row reads the same frames)");
-  if (!aligned16(workspace)) return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
+  if (!scratch_ws && !aligned16(workspace))
+    return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
   if (int rc = check_wide(R, false)) return rc;
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
-  if (workspace_bytes < (size_t)batch * (size_t)L.row_bytes)
+  const size_t need = (size_t)batch * (size_t)L.row_bytes;
+  if (workspace_bytes < need) {
+    if (scratch_ws)
+      return fail(CTCPB_ERR_TOO_SMALL,
+                  "this decode needs " + std::to_string(need) +
+                      " bytes of workspace, more than the fixed scratch of " +
+                      std::to_string(workspace_bytes) + " bytes (fewer rows per call)");
     return fail(CTCPB_ERR_TOO_SMALL, "workspace smaller than ctcpb_workspace_size");
+  }
   const bool wide_path = R.W > kMaxBeam;
   Params P{};
   P.L = L;
@@ -2441,6 +2458,9 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
   } else {
     P.sel_mode = 2;
     P.log_thr = (float)std::log((double)R.threshold);
+  }
+  if (scratch_ws) {
+    if (int rc = get_ws(&workspace)) return rc;
   }
   P.lp = log_prob;
   P.stride_b = stride_b;
@@ -2466,6 +2486,78 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
                       st, P, "decode_kernel"))
     return rc;
   return ok();
+}
+
+}  // namespace
+
+// ------------------------------------------------------- allocation-free --
+// The workspace of ctcpb_decode_offline_noalloc: one fixed device array.  Each
+// GPU that runs the call holds its own copy for the life of the process.  In
+// host code `scratch` names a host-side stand-in, not the device memory: its
+// device address is taken once per device with hipGetSymbolAddress and only
+// that address is used.
+namespace ctcpb {
+__device__ __align__(256) char scratch[CTCPB_NOALLOC_SCRATCH_BYTES];
+}  // namespace ctcpb
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (resolved on the device's
+// first call, with that device current).
+int scratch_for_current_device(void** out, void* stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(CTCPB_ERR_DEVICE, "no current HIP device");
+  if (dev >= kMaxDevices)
+    return fail(CTCPB_ERR_UNSUPPORTED, "device index " + std::to_string(dev) + " >= 64");
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return fail(CTCPB_ERR_INVALID, "stream is not a valid HIP stream");
+    if (sdev != dev)
+      return fail(CTCPB_ERR_INVALID, "stream belongs to device " + std::to_string(sdev) +
+                                         ", not the current device " + std::to_string(dev));
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CTCPB_ERR_DEVICE,
+                  std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CTCPB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t stride_b,
+                         int64_t stride_t, int32_t batch, int32_t max_T,
+                         const int32_t* seq_lengths, void* workspace, size_t workspace_bytes,
+                         int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
+                         void* stream) {
+  return decode_offline_impl(cfg, log_prob, stride_b, stride_t, batch, max_T, seq_lengths,
+                             workspace, workspace_bytes, false, [](void**) { return 0; },
+                             out_tokens, out_lengths, out_scores, stream);
+}
+
+int ctcpb_decode_offline_noalloc(const ctcpb_config* cfg, const float* log_prob,
+                                 int64_t stride_b, int64_t stride_t, int32_t batch,
+                                 int32_t max_T, const int32_t* seq_lengths, int32_t* out_tokens,
+                                 int32_t* out_lengths, float* out_scores, void* stream) {
+  return decode_offline_impl(
+      cfg, log_prob, stride_b, stride_t, batch, max_T, seq_lengths, nullptr,
+      (size_t)CTCPB_NOALLOC_SCRATCH_BYTES, true,
+      [stream](void** ws) { return scratch_for_current_device(ws, stream); }, out_tokens,
+      out_lengths, out_scores, stream);
 }
 
 int ctcpb_stream_init(const ctcpb_config* cfg, void* state, size_t state_bytes,

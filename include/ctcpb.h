@@ -111,6 +111,28 @@ int ctcpb_decode_offline(const ctcpb_config* cfg, const float* log_prob, int64_t
                          int32_t* out_tokens, int32_t* out_lengths, float* out_scores,
                          void* stream);
 
+/* Size of the fixed device scratch of ctcpb_decode_offline_noalloc. */
+#define CTCPB_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* ctcpb_decode_offline without a caller workspace and without any device
+ * memory allocation, for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a fixed array of CTCPB_NOALLOC_SCRATCH_BYTES bytes of device
+ * memory inside the library, one per GPU, held until the process ends.
+ *   - Runs on the calling thread's current device; `stream` (NULL = the
+ *     default stream) must belong to that device (CTCPB_ERR_INVALID otherwise).
+ *   - A decode whose ctcpb_workspace_size exceeds the scratch is refused with
+ *     CTCPB_ERR_TOO_SMALL before anything is enqueued (decode fewer rows per
+ *     call).
+ *   - Every call on one GPU uses that GPU's one array: calls that may overlap
+ *     in time on one GPU (other streams, other threads) race and must be
+ *     ordered by the caller.  ctcpb_row_stats cannot read this scratch.
+ * Arguments, outputs and errors otherwise as ctcpb_decode_offline. */
+int ctcpb_decode_offline_noalloc(const ctcpb_config* cfg, const float* log_prob,
+                                 int64_t stride_b, int64_t stride_t, int32_t batch,
+                                 int32_t max_T, const int32_t* seq_lengths, int32_t* out_tokens,
+                                 int32_t* out_lengths, float* out_scores, void* stream);
+
 /* Bytes of a streaming state blob holding `num_streams` independent streams
  * (sec. 5 calculate_[paged_]state_buffer_size). */
 int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes);
