@@ -126,7 +126,7 @@ constexpr int nchild = newlen + a16(kMaxBeam * 4);
 constexpr int childc = nchild + a16(kMaxBeam * 4);
 constexpr int scal = childc + a16(kMaxBeam * kMaxBeam * 4);
 constexpr int flags = scal + a16(kScalCount * 4);      // hand-off flags
-constexpr int ring = flags + a16((3 * kMaxSlots + 5) * 4);  // winners ring
+constexpr int ring = flags + a16((3 * kMaxSlots + 6) * 4);  // winners ring
 constexpr int soffs = ring + a16(kRing * kWave * 8);    // store-wave scratch
 constexpr int slot_k = a16(kMaxRanked * 4);             // ranked labels (or log-probs) of a frame
 constexpr int end = soffs + a16(128 * 4);
@@ -177,7 +177,8 @@ struct Ctx {
   int* tlen;      // paged: valid leading entries of each block-table row, both parities
   int* clist;     // flat: global or LDS
   int* pages;     // paged: global
-  int* wdone;     // last step whose tokens the store wave has written
+  int* tdone;     // last step whose tokens the store wave has written, durably
+                  // (global page / list writes complete)
   int* release;   // last frame whose slot the beam wave has handed back
   int frame;      // frame of the current step
   const float* grow;  // its log-prob row in global memory (the exact fallback)
@@ -185,6 +186,8 @@ struct Ctx {
 #ifdef CTCPB_PHASE_PROF
   uint64_t prof[kProfSlots];
   uint64_t prof_t;
+  uint64_t sprof[4];
+  uint64_t sprof_t;
   uint64_t stat_multi;   // steps that needed the general gather
 #endif
 };
@@ -259,9 +262,9 @@ template <typename TabT>
 __device__ __forceinline__ int tok_at(const Ctx& C, const TabT* tab, int parity, int slot, int pos) {
   const Layout& L = C.L;
   if (!L.paged) return C.clist[((int64_t)(parity * L.W + slot)) * L.ldc + pos];
-  const int page = (int)tab[(parity * L.W + slot) * L.max_lp + pos / L.ps];
+  const int page = (int)tab[(parity * L.W + slot) * L.max_lp + (pos >> L.ps_log2)];
   if (page < 0) return -1;  // only after a row ran out of pages
-  return C.pages[(int64_t)page * L.ps + pos % L.ps];
+  return C.pages[(int64_t)page * L.ps + (pos & (L.ps - 1))];
 }
 
 // ----------------------------------------------------------------- frames --
@@ -352,6 +355,13 @@ constexpr int kMaxGroups = 256;   // listed groups (step 3), ints after the keys
 constexpr int kMaxGather = 128;   // gathered keys (step 4)
 
 #ifdef CTCPB_PHASE_PROF
+// store-wave sub-phases: cycles since the previous mark into C.sprof[i]
+#define SP_MARK(i)                                              \
+  do {                                                          \
+    const uint64_t now_ = clock64();                            \
+    C.sprof[i] += now_ - C.sprof_t;                             \
+    C.sprof_t = now_;                                           \
+  } while (0)
 #define RF_MARK(i)                        \
   do {                                    \
     const uint64_t now_ = clock64();      \
@@ -359,6 +369,9 @@ constexpr int kMaxGather = 128;   // gathered keys (step 4)
     rprof_t = now_;                       \
   } while (0)
 #else
+#define SP_MARK(i) \
+  do {             \
+  } while (0)
 #define RF_MARK(i) \
   do {             \
   } while (0)
@@ -387,39 +400,72 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   constexpr int U = 8;  // groups per lane loaded before use
   RF_MARK(0);
 
-  // 1. two largest group maxima per lane (complete rounds of U groups per
-  // lane read at constant offsets, then the last partial round with bounds)
+  // 1. two largest group maxima per lane.  Rows of up to kRegRounds rounds
+  // of U groups per lane (V <= 8192) keep every group maximum in registers
+  // for step 3; longer rows read complete rounds at constant offsets, then
+  // the last partial round with bounds, and are read again in step 3.
+  constexpr int kRegRounds = 4;
+  const bool in_regs = n4 <= kRegRounds * U * kWave;   // wave-uniform
+  float gm[kRegRounds][U];
   float hi = ninf, lo = ninf;
   int base = 0;
-  for (; base + U * kWave <= n4; base += U * kWave) {
-    const float4* p4 = r4 + base + lane;
-    float4 q[U];
+  if (in_regs) {
 #pragma unroll
-    for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
+    for (int r = 0; r < kRegRounds; r++) {
+      const int rb = r * U * kWave;
+      if (rb < n4) {
+        const bool full = rb + U * kWave <= n4;
+        float4 q[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      lo = __builtin_amdgcn_fmed3f(m, hi, lo);
-      hi = fmaxf(hi, m);
+        for (int u = 0; u < U; u++) {
+          const int g = rb + u * kWave + lane;
+          q[u] = r4[full ? g : (g < n4 ? g : n4 - 1)];   // in bounds; masked below
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const int g = rb + u * kWave + lane;
+          float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+          m = (full || g < n4) ? m : ninf;
+          gm[r][u] = m;
+          lo = __builtin_amdgcn_fmed3f(m, hi, lo);
+          hi = fmaxf(hi, m);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; u++) gm[r][u] = ninf;
+      }
+    }
+  } else {
+    for (; base + U * kWave <= n4; base += U * kWave) {
+      const float4* p4 = r4 + base + lane;
+      float4 q[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+        lo = __builtin_amdgcn_fmed3f(m, hi, lo);
+        hi = fmaxf(hi, m);
+      }
+    }
+    if (base < n4) {
+      float4 q[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int g = base + u * kWave + lane;
+        q[u] = r4[g < n4 ? g : n4 - 1];   // in bounds; groups past the row are masked below
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int g = base + u * kWave + lane;
+        float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+        m = g < n4 ? m : ninf;
+        lo = __builtin_amdgcn_fmed3f(m, hi, lo);
+        hi = fmaxf(hi, m);
+      }
     }
   }
   const int base_tail = base;
-  if (base < n4) {
-    float4 q[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int g = base + u * kWave + lane;
-      q[u] = r4[g < n4 ? g : n4 - 1];   // in bounds; groups past the row are masked below
-    }
-#pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int g = base + u * kWave + lane;
-      float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      m = g < n4 ? m : ninf;
-      lo = __builtin_amdgcn_fmed3f(m, hi, lo);
-      hi = fmaxf(hi, m);
-    }
-  }
   RF_MARK(1);
   // 2. threshold: the largest value (to 16 bits of its key: sign, exponent
   // and 7 mantissa bits, two bits per round) that at least K of the 128
@@ -438,39 +484,47 @@ __device__ __forceinline__ void rank_frame(float* row, int V, int blank, int K, 
   const float tf = __uint_as_float((thr & 0x80000000u) ? (thr & 0x7fffffffu) : ~thr);
 
   RF_MARK(2);
-  // 3. groups reaching the threshold: a bit per group of this lane, then one
-  // wave scan places every lane's list
+  // 3. groups reaching the threshold: a bit per group of this lane (group
+  // (u0 + u) * 64 + lane at bit u0 + u), then one wave scan places every
+  // lane's list
   int* gid = reinterpret_cast<int*>(scr + kMaxGather);
   uint64_t pm = 0ull;
-  int u0 = 0;   // bit of round base / (U * kWave), group u: u0 + u
-  for (base = 0; base < base_tail; base += U * kWave, u0 += U) {
-    const float4* p4 = r4 + base + lane;
-    float4 q[U];
+  if (in_regs) {
 #pragma unroll
-    for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
-    uint32_t m8 = 0u;   // this round's U bits (constant positions), then placed at u0
+    for (int r = 0; r < kRegRounds; r++)
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      m8 |= (m >= tf) ? (1u << u) : 0u;
+      for (int u = 0; u < U; u++) pm |= (gm[r][u] >= tf) ? (1ull << (r * U + u)) : 0ull;
+  } else {
+    int u0 = 0;   // bit of round base / (U * kWave), group u: u0 + u
+    for (base = 0; base < base_tail; base += U * kWave, u0 += U) {
+      const float4* p4 = r4 + base + lane;
+      float4 q[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) q[u] = p4[u * kWave];
+      uint32_t m8 = 0u;   // this round's U bits (constant positions), then placed at u0
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+        m8 |= (m >= tf) ? (1u << u) : 0u;
+      }
+      pm |= (uint64_t)m8 << u0;
     }
-    pm |= (uint64_t)m8 << u0;
-  }
-  if (base_tail < n4) {
-    float4 q[U];
+    if (base_tail < n4) {
+      float4 q[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int g = base_tail + u * kWave + lane;
-      q[u] = r4[g < n4 ? g : n4 - 1];
-    }
-    uint32_t m8 = 0u;
+      for (int u = 0; u < U; u++) {
+        const int g = base_tail + u * kWave + lane;
+        q[u] = r4[g < n4 ? g : n4 - 1];
+      }
+      uint32_t m8 = 0u;
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int g = base_tail + u * kWave + lane;
-      const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
-      m8 |= ((g < n4) & (m >= tf)) ? (1u << u) : 0u;
+      for (int u = 0; u < U; u++) {
+        const int g = base_tail + u * kWave + lane;
+        const float m = fmaxf(fmaxf(q[u].x, q[u].y), fmaxf(q[u].z, q[u].w));
+        m8 |= ((g < n4) & (m >= tf)) ? (1u << u) : 0u;
+      }
+      pm |= (uint64_t)m8 << u0;
     }
-    pm |= (uint64_t)m8 << u0;
   }
   int ng;
   {
@@ -836,37 +890,14 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   C.exclast[sel(same, par, kWave - 1 - lane % (kWave - kMaxBeam))] = 1;
   atomicOr(&C.exm[sel(par >= 0, par, lane) * 2 + (rw >> 5)], sel(child_other, rbit, 0u));
   atomicOr(&C.exm[lane * 2 + (rw >> 5)], rbit);
-
-  // A_k = logsumexp(pb, pnb) was computed with the state.  The collapse for
-  // skipped frames (sec. 3.4) turns (pb, pnb) into (A_k, NEG), and since
-  // logsumexp(x, NEG) == x exactly, A_k is the same either way.
-  const float A = sel(lv, b.A, kNeg);
-  const float pb1 = g ? A : b.pb, pnb1 = g ? kNeg : b.pnb;
-  const float pb1_par = g ? A_par : pb_par;
-  // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
-  const float ptb = sel(lv, lpb + A, kNeg);
-  // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
-  const float from_parent = sel(par < 0, kNeg, sel(same, lpc + pb1_par, lpc + A_par));
-  const float ptnb = lse(sel(lv & !g & (last != blank), lpc + pnb1, kNeg), from_parent);
-  const float keyb = sel(lv, lse(ptb, ptnb), kNeg);
-
-  PROF_MARK(1);
+  // The reads of the exclusion masks below follow this wave's writes above
+  // (one wave's LDS operations are performed in issue order); the fence only
+  // keeps the compiler from moving them up.  The reads are issued before the
+  // blank slot's two dependent logsumexp chains, whose arithmetic then
+  // overlaps their latency.
   lds_order();
+  PROF_MARK(1);
   const int excl_own = C.exclast[lane];
-  const bool rep_ok = has_last & (excl_own == 0);
-  const float keyc = sel(rep_ok, lpc + pb1, kNeg);
-  // per-beam values that only the rare selection fallbacks read from LDS
-  auto share_beam_values = [&]() {
-    if (lane < W) {
-      C.A[lane] = A;
-      C.kb[lane] = keyb;
-      C.kc[lane] = keyc;
-      C.lastk[lane] = last;
-    }
-    lds_sync();
-  };
-
-  PROF_MARK(2);
   // ---- each beam's two best candidates, as composite keys (0 = none): the
   // blank slot, the repeated-label slot and its first non-excluded ranked
   // labels.  Sorting those 2W keys gives the top W exactly whenever no beam
@@ -876,8 +907,18 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // in-pool ranks still open to this beam (nPool <= kMaxRanked <= 64)
   const uint64_t in_pool = nPool >= 64 ? ~0ull : ((1ull << nPool) - 1ull);
   const uint64_t exw = reinterpret_cast<const uint64_t*>(C.exm)[lane & (kMaxBeam - 1)];
+  const float bound = C.Rl[nR - 1];   // no label outside the ranked list scores above A + bound
+
+  // A_k = logsumexp(pb, pnb) was computed with the state.  The collapse for
+  // skipped frames (sec. 3.4) turns (pb, pnb) into (A_k, NEG), and since
+  // logsumexp(x, NEG) == x exactly, A_k is the same either way.
+  const float A = sel(lv, b.A, kNeg);
+  const float pb1 = g ? A : b.pb, pnb1 = g ? kNeg : b.pnb;
+  const float pb1_par = g ? A_par : pb_par;
+  const bool rep_ok = has_last & (excl_own == 0);
+  const float keyc = sel(rep_ok, lpc + pb1, kNeg);
+
   const uint64_t fr = sel(lv, ~exw & in_pool, (uint64_t)0);
-  PROF_MARK(8);
   // the first three open ranks, without branches (-1: none)
   int rr[3];
   {
@@ -898,6 +939,24 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     rl[i] = C.Rl[r];
     rc[i] = C.Rc[r];
   }
+
+  // blank slot (sec. 3.4.2) holding the same-label "stay" term (sec. 3.4.1)
+  const float ptb = sel(lv, lpb + A, kNeg);
+  // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
+  const float from_parent = sel(par < 0, kNeg, sel(same, lpc + pb1_par, lpc + A_par));
+  const float ptnb = lse(sel(lv & !g & (last != blank), lpc + pnb1, kNeg), from_parent);
+  const float keyb = sel(lv, lse(ptb, ptnb), kNeg);
+  // per-beam values that only the rare selection fallbacks read from LDS
+  auto share_beam_values = [&]() {
+    if (lane < W) {
+      C.A[lane] = A;
+      C.kb[lane] = keyb;
+      C.kc[lane] = keyc;
+      C.lastk[lane] = last;
+    }
+    lds_sync();
+  };
+
   uint64_t oc[3];
 #pragma unroll
   for (int i = 0; i < 3; i++) {
@@ -905,7 +964,6 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     oc[i] = sel(lv & (rr[i] >= 0) & (key > kNeg), compose(key, idb + (uint32_t)rc[i]), (uint64_t)0);
   }
   const uint64_t o1 = oc[0], o2 = oc[1], o3 = oc[2];
-  const float bound = C.Rl[nR - 1];   // no label outside the ranked list scores above A + bound
   const uint64_t cb = sel(lv & (keyb > kNeg), compose(keyb, idb + (uint32_t)blank), (uint64_t)0);
   const uint64_t cc = sel(lv & (keyc > kNeg), compose(keyc, idb + (uint32_t)last), (uint64_t)0);
   const uint64_t shi = cb > cc ? cb : cc, slo = cb > cc ? cc : cb;
@@ -916,7 +974,6 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // below it); ranked labels past the list are bounded separately below
   const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
   PROF_MARK(9);
-  PROF_MARK(10);
   // beam j's best goes to lane j, its second best to lane j + NB / 2 (one
   // lane swap; W <= NB / 2); the sorting network covers those first NB lanes
   // only (lane exchanges run on every lane, outside any lane-dependent
@@ -1064,6 +1121,11 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   w.c = w.valid ? (int)(id & ((1u << kIdShift) - 1u)) : blank;
   const float key = comp_key(wc);
   const int k = w.k & 63;
+  // parent slots of the new beams (the prefix one label shorter, if live):
+  // the slot that beam k's blank winner went to.  Written first, so that its
+  // LDS round trip overlaps the state exchange below; bslot was cleared at the
+  // end of the previous step.
+  C.bslot[(w.valid && w.c == blank) ? w.k : kWave - 1 - lane % (kWave - kMaxBeam)] = lane;
   const float ptb_k = __shfl(ptb, k, 64);
   const float ptnb_k = __shfl(ptnb, k, 64);
   const int len_k = __shfl(b.len, k, 64);
@@ -1089,13 +1151,11 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   nb.pb = !w.valid ? kNeg : (g ? key : (stay ? ptb_k : kNeg));
   nb.pnb = !w.valid ? kNeg : (g ? kNeg : (stay ? ptnb_k : key));
 
-  // parent slots of the new beams (the prefix one label shorter, if live).
-  // bslot and htab were cleared at the end of the previous step.  The hash
-  // table is only needed when some stay winner's parent prefix was not live
-  // (it may just have been re-created by extending its own parent).
+  // The hash table (cleared at the end of the previous step) is only needed
+  // when some stay winner's parent prefix was not live (it may just have been
+  // re-created by extending its own parent).
   const bool need_look = w.valid && !ext && par_k < 0 && len_k >= 2;
   const bool any_look = __ballot(need_look) != 0ull;
-  C.bslot[(w.valid && w.c == blank) ? w.k : kWave - 1 - lane % (kWave - kMaxBeam)] = lane;
   int hslot = -1;
   if (__builtin_expect(any_look, 0)) {
     if (lane < W) {
@@ -1137,7 +1197,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
     if (cand >= 0 && c2 != last2_k) cand = -1;
     uint64_t todo = __ballot(cand >= 0);
     // the previous step's tokens must have been written by the store wave
-    if (todo && !spin_wait(C.wdone, step - 1, false, C.abortf)) todo = 0ull;
+    if (todo && !spin_wait(C.tdone, step - 1, false, C.abortf)) todo = 0ull;
     if (todo) {
       const int q = (step - 1) & 1;
       const int from = C.scal[kScalCpl0 + q];
@@ -1299,8 +1359,11 @@ __device__ __forceinline__ void copy4_lds(int4* d, const int4* s, int n) {
 // in the old and the new row and are skipped.
 // (The paged metadata is touched only by this wave here, in issue order: its
 // LDS hand-offs between lanes need no waits.)
-__device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int step, const Winner& w,
+__device__ __forceinline__ void store_paged(Ctx& C, StoreState& ss, int step, const Winner& w,
                                             bool nlive, int nlen) {
+#ifdef CTCPB_PHASE_PROF
+  C.sprof_t = clock64();
+#endif
   const Layout& L = C.L;
   const int lane = lane_id();
   const int W = L.W, ps = L.ps, blank = L.blank, max_lp = L.max_lp;
@@ -1310,10 +1373,11 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
   const int pcpp = p ? ss.pre1 : ss.pre0;
   const int old_t = in ? (p ? ss.len1 : ss.len0) : 0;
   const int ksrc = __shfl(p ? ss.src0 : ss.src1, w.k, 64);   // source of w.k one step earlier
-  const int np_new = w.valid ? (w.len_k + ps - 1) / ps : 0;
+  const int sh = L.ps_log2;   // page size = 1 << sh
+  const int np_new = w.valid ? (w.len_k + ps - 1) >> sh : 0;
   const bool ext = w.valid && w.c != blank;
-  const int off = w.len_k % ps;   // position of the new label in its page
-  const int qq2 = w.len_k / ps;   // and that page's entry
+  const int off = w.len_k & (ps - 1);   // position of the new label in its page
+  const int qq2 = w.len_k >> sh;        // and that page's entry
   int16_t* drow = C.tab + (p * W + (in ? lane : 0)) * max_lp;
   const int16_t* srow = C.tab + (q * W + (in ? w.k : 0)) * max_lp;
   // the page the label joins when it does not start one: the source's (the
@@ -1328,6 +1392,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
     const int n4 = w.valid ? (off + 3) >> 2 : 0;
     for (int j0 = 0; j0 < n4; j0 += 4) copy4_lds(dt4 + j0, st4 + j0, n4 - j0);
   }
+  SP_MARK(0);
 
   // pass 1: fork, two entries per round (the round count is the wave's
   // largest, so the free-stack top stays wave-uniform).  The top is capped at
@@ -1347,6 +1412,8 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
     const int o1 = (a1 && qq + 1 < old_t) ? (int)drow[qq + 1] : kInvalidPage;
     const int n1 = (a1 && qq + 1 < np_new) ? (int)srow[qq + 1] : kInvalidPage;
     const bool c0 = o0 != n0, c1 = o1 != n1;
+    // (usually no entry of the round changes: the rows are already equal)
+    if (__builtin_expect(__ballot(c0 | c1) == 0ull, 1)) continue;
     // a page released here is held by no row of parity p^1, so no fork of
     // this step acquires it: the order of the updates does not matter
     if (c0 && n0 != kInvalidPage) atomicAdd(&C.ref[n0], 1);
@@ -1366,6 +1433,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
   }
   int new_t = in ? (np_new > 0 ? np_new : start) : old_t;
   lds_order();
+  SP_MARK(1);
 
   // pass 2: append.  With only the source's row of the previous step and this
   // row referencing the partial page, the label is written in place: the
@@ -1412,6 +1480,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
   ss.freetop = ft;
   const int used = ss.nextfree - ft;
   ss.high = used > ss.high ? used : ss.high;
+  SP_MARK(2);
   const uint32_t vm = (uint32_t)__ballot(w.valid);
   const int nsrc = w.valid ? w.k : -1;
   // leading full pages shared by every live row of parity p.  Rows only grow
@@ -1424,9 +1493,9 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
     const uint64_t lm = __ballot(lv);
     const int first_live = lm ? __ffsll((long long)lm) - 1 : 0;
     while (lm != 0ull && pcp < max_lp) {
-      const bool full = !lv || nlen >= (pcp + 1) * ps;  // len <= cap keeps pcp < max_lp
+      const bool full = !lv || nlen >= ((pcp + 1) << sh);  // len <= cap keeps pcp < max_lp
       const int e = (lv && full) ? (int)drow[pcp] : kInvalidPage;
-      const int first = __shfl(e, first_live, 64);
+      const int first = __builtin_amdgcn_readlane(e, first_live);
       const bool ok = full && (!lv || e == first);
       if (__ballot(!ok) != 0ull) break;
       pcp++;
@@ -1444,6 +1513,7 @@ __device__ __forceinline__ void store_paged(const Ctx& C, StoreState& ss, int st
     ss.pre0 = pcp;
   }
   lds_order();
+  SP_MARK(3);
 }
 
 // ------------------------------------------------------------------ output --
@@ -1596,7 +1666,7 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   C.clist = S.clist_lds ? reinterpret_cast<int*>(smem + S.clist)
                         : reinterpret_cast<int*>(base + L.o_clist);
   C.pages = reinterpret_cast<int*>(base + L.o_pages);
-  C.wdone = nullptr;
+  C.tdone = nullptr;
   C.abortf = nullptr;
   return C;
 }
@@ -1790,10 +1860,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int* consumed = flags + kMaxSlots;     // last frame whose slot the beam wave handed back
   int* abortf = consumed + 1;
   int* wpub = consumed + 2;              // last step whose winners are in the ring
-  int* wdone = consumed + 3;             // last step the store wave has written
+  int* wdone = consumed + 3;             // last step the store wave has taken from the ring
   int* loaded = consumed + 4;            // [kMaxSlots]: frame whose row each slot holds
   int* frame_t = loaded + kMaxSlots;     // [kMaxSlots]: time index of that frame
   int* nspeech = frame_t + kMaxSlots;    // streaming: frames of the chunk to decode
+  int* tdone = nspeech + 1;              // last step whose token writes are complete
   int2* ring = reinterpret_cast<int2*>(smem + lds::ring);
   const int nslot = S.nslot, nprod = S.nprod;
   auto slot_row = [&](int sl) { return reinterpret_cast<float*>(smem + lds::end + sl * S.slot_stride); };
@@ -1819,6 +1890,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     *abortf = 0;
     *wpub = step_in - 1;
     *wdone = step_in - 1;
+    *tdone = step_in - 1;
   }
   // streaming: chunk frame f is frame number frame0 + f; with a speech mask
   // only the frames it flags are decoded (sec. 9 is_speech_mask, start_frame_idx)
@@ -1946,7 +2018,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
 
   Ctx C = make_ctx(L, S, P.N, P.max_out_len, P.out_tokens, P.out_lengths, P.out_scores, base,
                    smem);
-  C.wdone = wdone;
+  C.tdone = tdone;
   C.abortf = abortf;
 
   if (wave == store_wave) {
@@ -1954,11 +2026,26 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.offs = reinterpret_cast<int*>(smem + lds::soffs);
     StoreState ss{};
 #ifdef CTCPB_PHASE_PROF
+    for (int i = 0; i < 4; i++) C.sprof[i] = 0;
+#endif
+#ifdef CTCPB_PHASE_PROF
     uint64_t sw = 0, sk = 0, t0 = clock64();
 #endif
+    int durable = step_in - 1;   // last step announced in tdone
     for (int f = 0; f < nframes; f++) {
       const int step = step_in + f;
-      if (!spin_wait(wpub, step, false, abortf)) break;
+      if (flag_load(wpub) < step) {
+        // caught up with the beam wave: before waiting for its next step,
+        // make the token writes so far durable and announce them (the beam
+        // wave reads tokens only after tdone: in the rare exact prefix
+        // comparison, and for the outputs)
+        if (durable < step - 1) {
+          __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): global token writes done
+          flag_store(tdone, step - 1);
+          durable = step - 1;
+        }
+        if (!spin_wait(wpub, step, false, abortf)) break;
+      }
 #ifdef CTCPB_PHASE_PROF
       uint64_t t1 = clock64();
       sw += t1 - t0;
@@ -1983,9 +2070,13 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
         if ((step & 15) == 15) advance_cpl_flat(C, ss, step & 1, nlive, nlen);
       }
       if (f == nframes - 1) store_state_save(C, ss);
-      lds_sync();
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): global token writes done
-      flag_store(wdone, step);
+      // the ring entry is free again (its LDS state is written); the token
+      // writes may still be in flight
+      flag_publish_lds(wdone, step);
+      if (f == nframes - 1) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): global token writes done
+        flag_store(tdone, step);
+      }
 #ifdef CTCPB_PHASE_PROF
       t0 = clock64();
       sk += t0 - t1;
@@ -1996,6 +2087,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       unsigned long long* dst = reinterpret_cast<unsigned long long*>(hdr + kProfExtra);
       atomicAdd(dst + 2, (unsigned long long)sw);
       atomicAdd(dst + 3, (unsigned long long)sk);
+      unsigned long long* sd = reinterpret_cast<unsigned long long*>(hdr + kProfBase);
+      sd[2] = C.sprof[0];
+      sd[8] = C.sprof[1];
+      sd[10] = C.sprof[2];
+      sd[11] = C.sprof[3];
     }
 #endif
     return;
@@ -2104,12 +2200,13 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   }
   // every published step stored (bounded wait that the abort flag does not cut
   // short: the store wave drains what was published before it stops)
-  if (!spin_wait(wdone, step - 1, false, nullptr)) aborted = true;
+  if (!spin_wait(tdone, step - 1, false, nullptr)) aborted = true;
   if (aborted) atomicOr(&C.scal[kScalStatus], kStatusAborted);
 #ifdef CTCPB_PHASE_PROF
   if (lane == 0 && nframes > 0) {
     uint64_t* dst = reinterpret_cast<uint64_t*>(C.hdr + kProfBase);
-    for (int i = 0; i < kProfSlots; i++) dst[i] = C.prof[i];
+    for (int i = 0; i < 10; i++)   // 2, 8, 10, 11: store-wave counters
+      if (i != 2 && i != 8) dst[i] = C.prof[i];
     if (!STREAM) C.hdr[kFrames] = (int)C.stat_multi;   // diagnostics only (offline)
   }
 #endif
@@ -2232,8 +2329,8 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
     return fail(CTCPB_ERR_INVALID, "storage must be CTCPB_STORAGE_FLAT or CTCPB_STORAGE_PAGED");
   if (std::isnan(cfg->blank_threshold)) return fail(CTCPB_ERR_INVALID, "blank_threshold is NaN");
   const int ps = cfg->page_size == 0 ? 16 : cfg->page_size;
-  if (cfg->storage == CTCPB_STORAGE_PAGED && (ps < 4 || ps > 64 || ps % 4 != 0))
-    return fail(CTCPB_ERR_INVALID, "page_size must be a multiple of 4 in [4, 64]");
+  if (cfg->storage == CTCPB_STORAGE_PAGED && (ps < 4 || ps > 64 || (ps & (ps - 1)) != 0))
+    return fail(CTCPB_ERR_INVALID, "page_size must be a power of two in [4, 64]");
   if (cfg->num_pages < 0) return fail(CTCPB_ERR_INVALID, "num_pages must be >= 0");
   if (cfg->capacity < 0) return fail(CTCPB_ERR_INVALID, "capacity must be >= 0");
   R.W = cfg->beam;

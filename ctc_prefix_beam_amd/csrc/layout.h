@@ -54,7 +54,8 @@ struct Layout {
   int cap;        // token (and frame) capacity of a row
   int ldc;        // flat: row stride of clist (cap rounded up to 4)
   int paged;      // 0 flat, 1 paged
-  int ps;         // page size
+  int ps;         // page size (a power of two)
+  int ps_log2;    // log2(page size)
   int max_lp;     // pages per block-table row
   int npages;     // pages per row
   int cap_sel;    // entries of sel (offline: max_T; streaming: 0)
@@ -81,6 +82,8 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   L.ldc = (cap + 3) & ~3;
   L.paged = paged;
   L.ps = paged ? ps : 0;
+  L.ps_log2 = 0;
+  while (paged && (1 << L.ps_log2) < ps) L.ps_log2++;
   L.max_lp = paged ? (cap + ps - 1) / ps : 0;
   L.npages = paged ? (npages_cfg > 0 ? npages_cfg : W * (L.max_lp + 1)) : 0;
   L.cap_sel = cap_sel;

@@ -63,7 +63,7 @@ typedef struct {
   int32_t storage;         /* CTCPB_STORAGE_FLAT: double-buffered token lists
                               (sec. 3.1, 7); CTCPB_STORAGE_PAGED: pages with
                               reference-counted prefix sharing (sec. 3.4.5, 4.2) */
-  int32_t page_size;       /* paged: tokens per page, a multiple of 4 in 4..64 (0 = 16) */
+  int32_t page_size;       /* paged: tokens per page, a power of two in 4..64 (0 = 16) */
   int32_t num_pages;       /* paged: pages per row/stream (0 = beam * (ceil(cap /
                               page_size) + 1), the bound of sec. 4.2), at most 32767.
                               A smaller pool is allowed: a row that needs more pages

@@ -72,7 +72,7 @@ def test_size_queries(L):
     (dict(nbest=0), 1), (dict(nbest=9), 1), (dict(vocab=1), 1), (dict(vocab=20000), 3),
     (dict(blank_id=-1), 1), (dict(blank_id=256), 1), (dict(max_out_len=-1), 1),
     (dict(storage=2), 1), (dict(storage=1, page_size=3), 1), (dict(storage=1, page_size=65), 1),
-    (dict(storage=1, page_size=6), 1),
+    (dict(storage=1, page_size=6), 1), (dict(storage=1, page_size=12), 1),
     (dict(num_pages=-1), 1), (dict(capacity=-5), 1), (dict(blank_threshold=float("nan")), 1),
 ])
 def test_config_validation(L, kw, code):
