@@ -7,8 +7,11 @@ beam 32, 32-best, blank threshold 0.999, 512-token outputs, paged token
 storage), one GPU, inputs resident in HBM before the timed region.  A step is
 one ctcpb_decode_offline call over the whole batch (frame filter + decode).
 Also reported on the same line: the roofline of the decode kernel, the CPU
-oracle's throughput on a bounded sample, per-chunk latency of 256 concurrent
-streams (V=512, beam 10, 16-frame chunks), and the other workloads' rates.
+oracle's throughput on a bounded sample (one thread and the host's cores),
+the other offline workloads (tiny, bpe256, bpe1024, vocab5000 with flat
+storage) with their roofline fractions, per-chunk latency of 256 concurrent
+streams (V=512, beam 10, 16-frame chunks) at capacity 1024 and 4096, and
+beams of 64 and 128.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -63,15 +66,27 @@ def time_offline(dec, x, lens_d, out, steps, warmup):
     return wall, kernel_ms
 
 
+def host_threads():
+    """Threads the oracle may use: the cores this process may run on, at most
+    16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(x, lens, wl, seconds):
-    """The oracle as it stands on a bounded sample of the same workload: one
-    row per process, rows spread over the host's cores (at most 16)."""
+    """The oracle as it stands on a bounded sample of the same workload: first
+    on one thread (the first frames of one row), then one row per thread on
+    the host's cores (the first frames of `threads` rows), each sized to about
+    `seconds` of work."""
     import numpy as np
 
     import oracle
     oracle.build(force=False)
-    procs = max(1, min(16, os.cpu_count() or 1))
-    # a quick probe on a few frames sizes the sample to about `seconds`
+    threads = host_threads()
+    # a quick probe on a few frames sizes the samples
     probe_T = min(60, wl.T)
     lp1 = x[0:1, :probe_T].cpu().numpy()
     t = time.perf_counter()
@@ -79,25 +94,38 @@ def cpu_baseline(x, lens, wl, seconds):
                   wl.max_out_len)
     per_frame = (time.perf_counter() - t) / probe_T
     T = int(min(wl.T, max(probe_T, seconds / max(per_frame, 1e-9))))
-    rows = list(range(procs))
+
+    # one thread, one row
+    lp = x[0:1, :T].cpu().numpy()
+    ln = np.minimum(lens[0:1], T).astype(np.int32)
+    t = time.perf_counter()
+    oracle.decode(lp, ln, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len)
+    wall1 = time.perf_counter() - t
+    one = {"value": round(float(T / wall1), 1), "unit": "decoded frames/s", "cores": 1,
+           "sample": f"row 0 x first {T} frames of {wl.name} ({wall1:.1f} s)"}
+
+    rows = list(range(threads))
     lp = x[rows, :T].cpu().numpy()
     ln = np.minimum(lens[rows], T).astype(np.int32)
     t = time.perf_counter()
     oracle.decode_parallel(lp, ln, wl.beam, wl.nbest, 0, wl.threshold, wl.max_out_len,
-                           processes=procs)
+                           processes=threads)
     wall = time.perf_counter() - t
     return {"value": round(float(len(rows) * T / wall), 1), "unit": "decoded frames/s",
-            "cores": procs, "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} rows x first {T} frames of {wl.name}, one single-threaded "
-                      f"oracle process per row ({wall:.1f} s)"}
+                      f"oracle decode per row on {threads} threads ({wall:.1f} s)",
+            "host_cpu_count": os.cpu_count(), "one_core": one}
 
 
-def streaming_latency(reps=3, seed=0, mask_theta=None):
+def streaming_latency(reps=3, seed=0, mask_theta=None, capacity=None):
     """256 streams, 64 chunks of 16 frames: per-chunk latency of one
     ctcpb_stream_chunk call advancing every stream (device time by HIP events,
-    host time from enqueue to completion).  With mask_theta, each chunk is
-    gated by a speech mask computed once on the GPU as blank log-prob <
-    log(mask_theta) (frames flagged 0 are skipped)."""
+    host time from enqueue to completion).  `capacity` is the frames (and
+    tokens) a stream can hold: the session's 1024, or the page's default 4096
+    (whose flat token lists no longer fit on chip).  With mask_theta, each
+    chunk is gated by a speech mask computed once on the GPU as blank log-prob
+    < log(mask_theta) (frames flagged 0 are skipped)."""
     import numpy as np
     import torch
 
@@ -105,10 +133,9 @@ def streaming_latency(reps=3, seed=0, mask_theta=None):
     import synth
     wl = synth.WORKLOADS["stream512"]
     x, _ = wl.make_device(seed, "cuda")
-    # capacity sized to the session (1024 frames), as the decoder's state is
-    # allocated for the longest stream it must hold
+    cap = wl.T if capacity is None else capacity
     pool = cpb.StreamPool(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest, max_out_len=wl.T,
-                                            capacity=wl.T), wl.V, wl.B)
+                                            capacity=cap), wl.V, wl.B)
     mask = None
     if mask_theta is not None:
         mask = (x[:, :, 0] < float(np.float32(np.log(mask_theta)))).to(torch.uint8)
@@ -137,13 +164,14 @@ def streaming_latency(reps=3, seed=0, mask_theta=None):
                 "p90_chunk_ms": round(float(np.percentile(d, 90)), 4),
                 "decoded_frames_per_s": round(float(wl.B * wl.chunk * frac / (d.mean() / 1e3)), 1),
                 "chunks_timed": int(d.size)}
-    return {"workload": "stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks, "
-                        "capacity 1024",
+    return {"workload": f"stream512: 256 streams, V=512, beam 10, 16-frame chunks, 64 chunks, "
+                        f"capacity {cap}",
             "p50_chunk_ms": round(float(np.percentile(d, 50)), 4),
             "p90_chunk_ms": round(float(np.percentile(d, 90)), 4),
             "p99_chunk_ms": round(float(np.percentile(d, 99)), 4),
             "p50_host_chunk_ms": round(float(np.percentile(h, 50)), 4),
             "frames_per_s": round(float(wl.B * wl.chunk / (d.mean() / 1e3)), 1),
+            "launches_per_chunk": 1,
             "chunks_timed": int(d.size)}
 
 
@@ -180,34 +208,41 @@ def wide_beams():
 
 
 def other_workloads():
-    """Every offline workload once more (flat storage, and vocab5000 paged),
-    for the comparison table; not part of the default run."""
+    """The other offline workloads (flat token lists, as configured) and
+    vocab5000 with flat storage beside the paged headline: one decode per
+    step, timed with HIP events, with each one's roofline fraction."""
     import numpy as np
     import torch
 
     import ctc_prefix_beam_amd as cpb
     import synth
     res = {}
-    for name, paged in (("bpe256", False), ("bpe1024", False), ("vocab5000", False),
-                        ("vocab5000", True)):
+    for name, paged, steps in (("tiny", False, 20), ("bpe256", False, 10), ("bpe1024", False, 10),
+                               ("vocab5000", False, 5)):
         wl = synth.WORKLOADS[name]
         x, lens = wl.make_device(0, "cuda")
         lens_d = torch.from_numpy(lens).cuda()
         dec = cpb.OfflineDecoder(cpb.DecoderConfig(beam=wl.beam, nbest=wl.nbest,
                                                    blank_threshold=wl.threshold,
                                                    max_out_len=wl.max_out_len, paged=paged))
-        out = None
         out = dec.decode(x, lens_d)
-        wall, kms = time_offline(dec, x, lens_d, out, 5, 1)
-        key = name + ("_paged" if paged else "_flat")
+        wall, kms = time_offline(dec, x, lens_d, out, steps, 2)
         st = dec.row_stats().cpu().numpy()
-        res[key] = {"frames_per_s": round(wl.B * wl.T * 5 / wall, 1),
-                    "valid_frames_per_s": round(float(np.sum(lens)) * 5 / wall, 1),
-                    "ms_per_decode": round(float(np.mean(kms)), 4),
-                    "fallback_steps": int(st[:, 4].sum()), "steps": int(st[:, 0].sum()),
-                    "workspace_bytes": int(dec.workspace.numel()),
-                    "pages_high_per_row": int(st[:, 3].max()) if paged else None}
+        sel = int(st[:, 1].sum())
+        ms = float(np.mean(kms))
+        alg = sel * algorithmic_bytes_per_frame(wl.V, wl.beam)
+        key = name + ("_paged" if paged else "_flat")
+        res[key] = {"shape": f"B={wl.B} T={wl.T} V={wl.V} beam={wl.beam}",
+                    "ms_per_decode": round(ms, 4),
+                    "frames_per_s": round(wl.B * wl.T / (ms / 1e3), 1),
+                    "valid_frames_per_s": round(float(np.sum(lens)) / (ms / 1e3), 1),
+                    "selected_frames": sel,
+                    "hbm_frac": round(alg / (ms / 1e3) / (PEAK_HBM_GBS * 1e9), 5),
+                    "us_per_step": round(ms * 1e3 / max(1, int(st[:, 0].max())), 3),
+                    "fallback_steps": int(st[:, 4].sum()),
+                    "workspace_bytes": int(dec.workspace.numel())}
         del x
+        torch.cuda.empty_cache()
     return res
 
 
@@ -218,11 +253,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="vocab5000")
     ap.add_argument("--storage", choices=["paged", "flat"], default="paged")
-    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the streaming latency run")
-    ap.add_argument("--compare", action="store_true",
-                    help="also time every offline workload (flat and paged) for comparison")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other workloads, streaming latency and wide beams")
     ap.add_argument("--with-copy", action="store_true",
                     help="after the timed decodes, run a plain streaming kernel of known size "
                          "twice (1 GiB read, 1 GiB written, 16-byte accesses per lane) to "
@@ -293,6 +327,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(bytes_per_launch),
                      "launch_ms": round(launch_ms, 4)},
         "decode": {"selected_frames": selected, "fallback_steps": int(stats[:, 4].sum()),
+                   "launches_per_decoded_frame": round(2 / max(selected, 1), 8),
                    "merge_verifications": int(stats[:, 5].sum()),
                    "workspace_bytes": ws_bytes, "paged_pages_high_per_row": pages_high,
                    "kernel_sha": kernel_sha()},
@@ -324,15 +359,16 @@ def main():
     del x
     torch.cuda.empty_cache()
     if not args.no_extras:
-        log("[bench] streaming latency, 256 streams")
+        log("[bench] other workloads (tiny, bpe256, bpe1024, vocab5000 flat)")
+        result["workloads"] = other_workloads()
+        log("[bench] streaming latency, 256 streams, capacity 1024")
         result["streaming"] = streaming_latency()
+        log("[bench] streaming latency, capacity 4096")
+        result["streaming"]["capacity_4096"] = streaming_latency(capacity=4096)
         log("[bench] streaming latency with a speech mask")
         result["streaming"]["speech_masked"] = streaming_latency(mask_theta=0.7)
         log("[bench] wide beams (64, 128)")
         result["wide_beams"] = wide_beams()
-    if args.compare:
-        log("[bench] other workloads")
-        result["other_workloads"] = other_workloads()
     print(json.dumps(result))
 
 
