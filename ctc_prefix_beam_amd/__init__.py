@@ -36,7 +36,7 @@ class CtcpbConfig(ctypes.Structure):
                 ("blank_id", ctypes.c_int32), ("blank_threshold", ctypes.c_float),
                 ("max_out_len", ctypes.c_int32), ("capacity", ctypes.c_int32),
                 ("storage", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("space_id", ctypes.c_int32)]
 
 
 @dataclass
@@ -51,11 +51,13 @@ class DecoderConfig:
     paged: bool = False
     page_size: int = 16
     num_pages: int = 0
+    space_id: int = -1     # label of the space slot (sec. 3.4.2), -1 none
 
     def c_struct(self, vocab: int, max_out_len: int) -> CtcpbConfig:
         return CtcpbConfig(self.beam, self.nbest or self.beam, vocab, self.blank_id,
                            float(self.blank_threshold), max_out_len, self.capacity,
-                           PAGED if self.paged else FLAT, self.page_size, self.num_pages)
+                           PAGED if self.paged else FLAT, self.page_size, self.num_pages,
+                           self.space_id)
 
 
 _lib = None

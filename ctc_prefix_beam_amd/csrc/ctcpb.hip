@@ -832,7 +832,7 @@ __device__ __forceinline__ int full_select(const Ctx& C, const float* row, int p
     float key;
     if (c == blank) {
       key = C.kb[k];
-    } else if (c == C.lastk[k]) {
+    } else if (c == C.lastk[k] && c != L.space) {
       key = C.kc[k];
     } else {
       const int nc = C.nchild[k];
@@ -867,6 +867,9 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // (reads and writes below run on every lane: `last` is always a label, and
   // lanes without an effect write to their own spare entry or OR in zero)
   const bool has_last = lv & (last != blank);
+  // a beam ending in the space label (sec. 3.4.2) extends by it like by any
+  // other label and has no repeated-label slot and no stay term
+  const bool rep_last = has_last & (last != L.space);
   const float lpc_raw = row[last];
   const float lpb = row[blank];
   const int rr_raw = (int)C.rank[last];
@@ -882,14 +885,14 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // the repeated-label slot) and the last label of each child (merged away).
   // The masks (two words per lane: ranks 0..63) were cleared at the end of
   // the previous step.
-  const bool same = (par >= 0) & (last == last_par);
-  const bool child_other = (par >= 0) & (last != last_par);
+  const bool same = (par >= 0) & (last == last_par) & rep_last;
+  const bool child_other = (par >= 0) & !same;
   const bool rr_in = has_last & (rr_raw >= 0);
   const int rw = sel(rr_in, rr_raw, 0);
   const uint32_t rbit = sel(rr_in, 1u << (rw & 31), 0u);
   C.exclast[sel(same, par, kWave - 1 - lane % (kWave - kMaxBeam))] = 1;
   atomicOr(&C.exm[sel(par >= 0, par, lane) * 2 + (rw >> 5)], sel(child_other, rbit, 0u));
-  atomicOr(&C.exm[lane * 2 + (rw >> 5)], rbit);
+  atomicOr(&C.exm[lane * 2 + (rw >> 5)], sel(rep_last, rbit, 0u));
   // The reads of the exclusion masks below follow this wave's writes above
   // (one wave's LDS operations are performed in issue order); the fence only
   // keeps the compiler from moving them up.  The reads are issued before the
@@ -915,7 +918,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float A = sel(lv, b.A, kNeg);
   const float pb1 = g ? A : b.pb, pnb1 = g ? kNeg : b.pnb;
   const float pb1_par = g ? A_par : pb_par;
-  const bool rep_ok = has_last & (excl_own == 0);
+  const bool rep_ok = rep_last & (excl_own == 0);
   const float keyc = sel(rep_ok, lpc + pb1, kNeg);
 
   const uint64_t fr = sel(lv, ~exw & in_pool, (uint64_t)0);
@@ -944,7 +947,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const float ptb = sel(lv, lpb + A, kNeg);
   // logsumexp(x, NEG) == x exactly, so beams without a parent pass through
   const float from_parent = sel(par < 0, kNeg, sel(same, lpc + pb1_par, lpc + A_par));
-  const float ptnb = lse(sel(lv & !g & (last != blank), lpc + pnb1, kNeg), from_parent);
+  const float ptnb = lse(sel(!g & rep_last, lpc + pnb1, kNeg), from_parent);
   const float keyb = sel(lv, lse(ptb, ptnb), kNeg);
   // per-beam values that only the rare selection fallbacks read from LDS
   auto share_beam_values = [&]() {
@@ -2309,7 +2312,7 @@ int ok() {
 }
 
 struct Resolved {
-  int W, N, V, blank, mol, paged, ps, npages_cfg, cap_stream;
+  int W, N, V, blank, space, mol, paged, ps, npages_cfg, cap_stream;
   float threshold;
 };
 
@@ -2333,10 +2336,14 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
     return fail(CTCPB_ERR_INVALID, "page_size must be a power of two in [4, 64]");
   if (cfg->num_pages < 0) return fail(CTCPB_ERR_INVALID, "num_pages must be >= 0");
   if (cfg->capacity < 0) return fail(CTCPB_ERR_INVALID, "capacity must be >= 0");
+  if (cfg->space_id >= cfg->vocab)
+    return fail(CTCPB_ERR_INVALID, "space_id must be < vocab (or -1 for no space slot)");
   R.W = cfg->beam;
   R.N = cfg->nbest;
   R.V = cfg->vocab;
   R.blank = cfg->blank_id;
+  // the space slot exists for a space label other than the blank (sec. 3.4.2)
+  R.space = (cfg->space_id >= 0 && cfg->space_id != cfg->blank_id) ? cfg->space_id : -1;
   R.mol = cfg->max_out_len;
   R.paged = cfg->storage == CTCPB_STORAGE_PAGED;
   R.ps = ps;
@@ -2411,7 +2418,9 @@ LdsPlan plan_lds(const Layout& L) {
 }
 
 Layout layout_for(const Resolved& R, int cap, int cap_sel) {
-  return make_layout(R.W, R.V, R.blank, cap, R.paged, R.ps, R.npages_cfg, cap_sel);
+  Layout L = make_layout(R.W, R.V, R.blank, cap, R.paged, R.ps, R.npages_cfg, cap_sel);
+  L.space = R.space;
+  return L;
 }
 
 int check_lds(const Layout& L, const LdsPlan& S) {

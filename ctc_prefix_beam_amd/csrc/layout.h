@@ -51,6 +51,7 @@ struct Layout {
   int W;          // beam
   int V;          // vocabulary
   int blank;
+  int space;      // label of the space slot, -1 none (not part of the sizes)
   int cap;        // token (and frame) capacity of a row
   int ldc;        // flat: row stride of clist (cap rounded up to 4)
   int paged;      // 0 flat, 1 paged
@@ -78,6 +79,7 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   L.W = W;
   L.V = V;
   L.blank = blank;
+  L.space = -1;
   L.cap = cap;
   L.ldc = (cap + 3) & ~3;
   L.paged = paged;

@@ -366,8 +366,11 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       const float pb1 = g ? A : pb, pnb1 = g ? kNeg : pnb;
       const int last = s_last[k];
       const bool has_last = lv && last != blank;
+      // a beam ending in the space label (sec. 3.4.2) extends by it like by
+      // any other label and has no repeated-label slot and no stay term
+      const bool rep_last = has_last && last != L.space;
       const float lpc = has_last ? row[last] : kNeg;
-      float stay = (has_last && !g) ? lpc + pnb1 : kNeg;
+      float stay = (rep_last && !g) ? lpc + pnb1 : kNeg;
       const int par = lv ? s_par[k] : -1;
       if (par >= 0) {
         // the parent's extension by this beam's last label joins this beam's
@@ -375,9 +378,10 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         const int lastp = s_last[par];
         const float Ap = lse(s_pb[par], s_pnb[par]);
         const float pb1p = g ? Ap : s_pb[par];
-        const float from = last == lastp ? lpc + pb1p : lpc + Ap;
+        const bool same = rep_last && last == lastp;
+        const float from = same ? lpc + pb1p : lpc + Ap;
         stay = lse(stay, from);
-        if (last == lastp) {
+        if (same) {
           s_exc[par] = 1;
         } else {
           const int r = rmap[last];
@@ -385,7 +389,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         }
       }
       // the beam's own last label is its repeated-label slot, not an ordinary one
-      if (has_last) {
+      if (rep_last) {
         const int r = rmap[last];
         if (r >= 0) atomicOr(&s_exm[k * kExw + (r >> 5)], 1u << (r & 31));
       }
@@ -395,7 +399,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_ptb[k] = ptb;
       s_stay[k] = stay;
       s_kb[k] = lv ? lse(ptb, stay) : kNeg;
-      s_kc[k] = has_last ? lpc + pb1 : kNeg;
+      s_kc[k] = rep_last ? lpc + pb1 : kNeg;
       s_lpc[k] = lpc;
     }
     __syncthreads();
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       if (c == blank) {
         npb = s_ptb[k];
         npnb = s_stay[k];
-      } else if (c == lastk) {
+      } else if (c == lastk && c != L.space) {
         npb = kNeg;
         npnb = s_lpc[k] + s_pb1[k];
       } else {

@@ -72,6 +72,15 @@ typedef struct {
                               its own pool) and the other rows are unaffected.  The
                               high-water mark (ctcpb_row_stats [3]) of a decode is
                               the pool that decodes that row exactly. */
+  int32_t space_id;        /* the space label of the optional space slot (sec. 3.4.1,
+                              3.4.2), or -1 for none (the page's default); the blank
+                              label also means none.  With a space label, every beam's
+                              space extension scores lp[space] + logsumexp(pb, pnb),
+                              also after a beam that ends in the space label, and a
+                              beam ending in the space label has no non-blank stay
+                              term: every space frame emits a new space token.
+                              Zero-initialised configs get space_id 0, which is a
+                              space slot unless blank_id is 0: set it to -1. */
 } ctcpb_config;
 
 /* Bytes of device workspace ctcpb_decode_offline needs for `batch` rows of up

@@ -62,8 +62,13 @@ def lib():
         L.oracle_decode.restype = i32
         L.oracle_decode.argtypes = [p, i64, i64, i32, i32, p, i32, i32, i32, i32, f32, i32,
                                     p, p, p]
+        L.oracle_decode_sp.restype = i32
+        L.oracle_decode_sp.argtypes = [p, i64, i64, i32, i32, p, i32, i32, i32, i32, f32, i32,
+                                       p, p, p, i32]
         L.oracle_stream_new.restype = p
         L.oracle_stream_new.argtypes = [i32, i32, i32, i32]
+        L.oracle_stream_new_sp.restype = p
+        L.oracle_stream_new_sp.argtypes = [i32, i32, i32, i32, i32]
         L.oracle_stream_free.restype = None
         L.oracle_stream_free.argtypes = [p]
         L.oracle_stream_reset.restype = None
@@ -134,9 +139,10 @@ def select_frames(lp_row: np.ndarray, length: int, blank: int, threshold: float)
 
 
 def decode(log_prob: np.ndarray, seq_lengths, beam: int, nbest: int | None = None,
-           blank: int = 0, threshold: float = 1.0, max_out_len: int | None = None):
-    """Offline decode.  Returns (tokens[B,N,max_out_len] -1 padded, lengths[B,N],
-    scores[B,N])."""
+           blank: int = 0, threshold: float = 1.0, max_out_len: int | None = None,
+           space: int = -1):
+    """Offline decode (`space`: the space label of the space slot, -1 none).
+    Returns (tokens[B,N,max_out_len] -1 padded, lengths[B,N], scores[B,N])."""
     log_prob = np.ascontiguousarray(log_prob, dtype=np.float32)
     B, T, V = log_prob.shape
     nbest = beam if nbest is None else nbest
@@ -146,9 +152,9 @@ def decode(log_prob: np.ndarray, seq_lengths, beam: int, nbest: int | None = Non
     toks = np.full((B, nbest, max(max_out_len, 0)), -1, np.int32)
     lengths = np.zeros((B, nbest), np.int32)
     scores = np.zeros((B, nbest), np.float32)
-    rc = lib().oracle_decode(_ptr(log_prob), T * V, V, B, T, _ptr(lens), beam, nbest, V, blank,
-                             float(threshold), max_out_len, _ptr(toks), _ptr(lengths),
-                             _ptr(scores))
+    rc = lib().oracle_decode_sp(_ptr(log_prob), T * V, V, B, T, _ptr(lens), beam, nbest, V,
+                                blank, float(threshold), max_out_len, _ptr(toks),
+                                _ptr(lengths), _ptr(scores), int(space))
     if rc != 0:
         raise ValueError("oracle_decode: invalid argument")
     return toks, lengths, scores
@@ -159,9 +165,10 @@ class Stream:
     speech mask (0 = skip the frame) and numbered from a caller-given frame
     index."""
 
-    def __init__(self, beam: int, vocab: int, blank: int = 0, capacity: int = 4096):
+    def __init__(self, beam: int, vocab: int, blank: int = 0, capacity: int = 4096,
+                 space: int = -1):
         self.beam, self.vocab = beam, vocab
-        self._h = lib().oracle_stream_new(beam, vocab, blank, capacity)
+        self._h = lib().oracle_stream_new_sp(beam, vocab, blank, capacity, space)
         if not self._h:
             raise ValueError("oracle_stream_new: invalid argument")
 
@@ -220,12 +227,12 @@ class Stream:
 
 
 def decode_parallel(log_prob, seq_lengths, beam, nbest=None, blank=0, threshold=1.0,
-                    max_out_len=None, processes: int = 1):
+                    max_out_len=None, processes: int = 1, space: int = -1):
     """Rows spread over `processes` threads of this process (rows are
     independent, each decode is single-threaded C and ctypes releases the
     GIL).  Same results as ``decode``."""
     if processes <= 1:
-        return decode(log_prob, seq_lengths, beam, nbest, blank, threshold, max_out_len)
+        return decode(log_prob, seq_lengths, beam, nbest, blank, threshold, max_out_len, space)
     from concurrent.futures import ThreadPoolExecutor
     B = log_prob.shape[0]
     nbest = beam if nbest is None else nbest
@@ -234,7 +241,7 @@ def decode_parallel(log_prob, seq_lengths, beam, nbest=None, blank=0, threshold=
 
     def one(b):
         return decode(log_prob[b:b + 1], lens[b:b + 1], beam, nbest, blank, threshold,
-                      max_out_len)
+                      max_out_len, space)
 
     with ThreadPoolExecutor(processes) as ex:
         parts = list(ex.map(one, range(B)))

@@ -44,6 +44,12 @@
  *     the gap rule above, exactly as after an offline skip.
  *   - Final hypotheses are reported in (score desc, slot asc) order; positions
  *     past a hypothesis' length and dead hypotheses' tokens are -1.
+ *   - Space slot (optional, sec. 3.4.1 / 3.4.2): the space label is skipped
+ *     by the ordinary extension loop and scored as lp[space] + logsumexp(pb,
+ *     pnb) for every beam, also one that already ends in it; a beam ending
+ *     in the space label therefore has no non-blank stay term (NEG).  The
+ *     result is prefix search under the collapse in which every space frame
+ *     emits a new space token.
  */
 #include <float.h>
 #include <math.h>
@@ -172,6 +178,7 @@ typedef struct {
 
 struct OracleStream {
     int beam, vocab, blank, capacity;
+    int space;   /* the space label, or -1 (no space slot) */
     int step;    /* number of frames decoded so far */
     int last_t;  /* frame index of the last decoded frame */
     int frames;  /* frames given so far, decoded or not: the next frame's index */
@@ -227,11 +234,13 @@ static void reset_empty(OracleStream *st)
     st->frames = 0;
 }
 
-OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
+OracleStream *oracle_stream_new_sp(int beam, int vocab, int blank, int capacity, int space)
 {
-    if (beam < 1 || vocab < 2 || blank < 0 || blank >= vocab || capacity < 0)
+    if (beam < 1 || vocab < 2 || blank < 0 || blank >= vocab || capacity < 0 || space >= vocab)
         return NULL;
     OracleStream *st = (OracleStream *)calloc(1, sizeof(OracleStream));
+    /* sec. 3.4.2: the space slot exists for space_id >= 0 other than the blank */
+    st->space = (space >= 0 && space != blank) ? space : -1;
     st->beam = beam;
     st->vocab = vocab;
     st->blank = blank;
@@ -247,6 +256,11 @@ OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
     st->order = (int64_t *)malloc(sizeof(int64_t) * (size_t)beam * (size_t)vocab);
     reset_empty(st);
     return st;
+}
+
+OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
+{
+    return oracle_stream_new_sp(beam, vocab, blank, capacity, -1);
 }
 
 void oracle_stream_free(OracleStream *st)
@@ -319,7 +333,7 @@ static void first_step(OracleStream *st, const float *lp, int t)
 /* One step s >= 1 (sec. 3.4.1 - 3.4.5) on the frame row lp. */
 static void next_step(OracleStream *st, const float *lp, int need_add_blank)
 {
-    const int W = st->beam, V = st->vocab, blank = st->blank;
+    const int W = st->beam, V = st->vocab, blank = st->blank, space = st->space;
     float *pt = st->ptable, *ptn = st->ptablen;
 
     /* sec. 3.4.1 / 3.4.2: extension tables.  Dead beams get NEG everywhere. */
@@ -340,9 +354,22 @@ static void next_step(OracleStream *st, const float *lp, int need_add_blank)
             prev_nb = s->pnb;
         }
         int last = slot_clast(s, blank);
+        /* The non-blank "stay" below reaches the blank slot only from the
+         * loop's c == last case.  The loop skips the space label (sec.
+         * 3.4.1), so a beam ending in the space label has no stay term: NEG
+         * (the page leaves whatever the slot held; this is the reading
+         * taken). */
+        rown[blank] = NEG;
         for (int c = 0; c < V; c++) {
             if (c == blank)
                 continue;
+            if (c == space) {
+                /* sec. 3.4.2 space slot: a new label from either part, also
+                 * after a beam that already ends in the space label */
+                rown[c] = lp[c] + oracle_lse(prev_b, prev_nb);
+                rowb[c] = NEG;
+                continue;
+            }
             if (c == last) {
                 rown[c] = lp[c] + prev_b;        /* same label: blank path only */
                 rown[blank] = lp[c] + prev_nb;   /* "stay" folds into the blank slot */
@@ -510,13 +537,13 @@ void oracle_stream_read(const OracleStream *st, int nbest, int max_out_len,
 
 /* Offline decode of a batch (sec. 3.7): select frames, decode every selected
  * frame in order, report the N best per row. */
-int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
-                  int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
-                  int blank, float threshold, int max_out_len, int *out_tokens,
-                  int *out_lengths, float *out_scores)
+int oracle_decode_sp(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                     int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
+                     int blank, float threshold, int max_out_len, int *out_tokens,
+                     int *out_lengths, float *out_scores, int space)
 {
     if (beam < 1 || nbest < 1 || nbest > beam || vocab < 2 || blank < 0 || blank >= vocab ||
-        max_out_len < 0 || batch < 0 || max_T < 0)
+        max_out_len < 0 || batch < 0 || max_T < 0 || space >= vocab)
         return 1;
     int *sel = (int *)malloc(sizeof(int) * (size_t)(max_T > 0 ? max_T : 1));
     for (int b = 0; b < batch; b++) {
@@ -525,7 +552,7 @@ int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int
         if (len > max_T) len = max_T;
         const float *row = log_prob + (int64_t)b * stride_b;
         int n = oracle_select_frames(row, stride_t, len, blank, threshold, sel);
-        OracleStream *st = oracle_stream_new(beam, vocab, blank, len);
+        OracleStream *st = oracle_stream_new_sp(beam, vocab, blank, len, space);
         for (int s = 0; s < n; s++)
             decode_frame(st, row + (int64_t)sel[s] * stride_t, sel[s]);
         oracle_stream_read(st, nbest, max_out_len,
@@ -535,4 +562,14 @@ int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int
     }
     free(sel);
     return 0;
+}
+
+int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                  int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
+                  int blank, float threshold, int max_out_len, int *out_tokens,
+                  int *out_lengths, float *out_scores)
+{
+    return oracle_decode_sp(log_prob, stride_b, stride_t, batch, max_T, seq_lengths, beam, nbest,
+                            vocab, blank, threshold, max_out_len, out_tokens, out_lengths,
+                            out_scores, -1);
 }

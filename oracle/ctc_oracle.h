@@ -33,10 +33,17 @@ int oracle_decode(const float *log_prob, int64_t stride_b, int64_t stride_t, int
                   int blank, float threshold, int max_out_len, int *out_tokens,
                   int *out_lengths, float *out_scores);
 
+/* The same with a space slot for label `space` (-1 or the blank: none). */
+int oracle_decode_sp(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                     int max_T, const int *seq_lengths, int beam, int nbest, int vocab,
+                     int blank, float threshold, int max_out_len, int *out_tokens,
+                     int *out_lengths, float *out_scores, int space);
+
 /* Streaming: one stream, frames fed in chunks (optionally gated by a speech
  * mask, and from a caller-given frame index). */
 typedef struct OracleStream OracleStream;
 OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity);
+OracleStream *oracle_stream_new_sp(int beam, int vocab, int blank, int capacity, int space);
 void oracle_stream_free(OracleStream *st);
 void oracle_stream_reset(OracleStream *st);
 int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, int n_frames);

@@ -28,7 +28,7 @@ def declared_functions():
 
 def cfg(**kw):
     base = dict(beam=8, nbest=8, vocab=256, blank_id=0, blank_threshold=0.999, max_out_len=200,
-                capacity=0, storage=0, page_size=16, num_pages=0)
+                capacity=0, storage=0, page_size=16, num_pages=0, space_id=-1)
     base.update(kw)
     return cpb.CtcpbConfig(**base)
 
@@ -74,6 +74,7 @@ def test_size_queries(L):
     (dict(storage=2), 1), (dict(storage=1, page_size=3), 1), (dict(storage=1, page_size=65), 1),
     (dict(storage=1, page_size=6), 1), (dict(storage=1, page_size=12), 1),
     (dict(num_pages=-1), 1), (dict(capacity=-5), 1), (dict(blank_threshold=float("nan")), 1),
+    (dict(space_id=256), 1),
 ])
 def test_config_validation(L, kw, code):
     rc, _ = ws(L, cfg(**kw), 2, 10)

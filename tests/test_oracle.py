@@ -480,3 +480,83 @@ def test_all_zero_mask_decodes_nothing(oracle_lib):
     for t in range(10, 20):
         ref.step_at(lp[0, t], t)
     assert all((x == y).all() for x, y in zip(st.read(3, 10), ref.read(3, 10)))
+
+
+# ------------------------------------------------------------ space slot --
+# The space slot (sec. 3.4.1 skips the space label; sec. 3.4.2 scores it as
+# lp[space] + logsumexp(pb, pnb) for every beam): a space frame always emits
+# a new space token, so a beam ending in the space label has no stay term.
+def collapse_space(path, blank, space):
+    out, prev = [], None
+    for c in path:
+        if c == blank:
+            pass
+        elif c == space or c != prev:
+            out.append(c)
+        prev = c
+    return tuple(out)
+
+
+def brute_force_space(lp, blank, space):
+    T, V = lp.shape
+    lp64 = lp.astype(np.float64)
+    acc = {}
+    for path in itertools.product(range(V), repeat=T):
+        s = float(sum(lp64[t, c] for t, c in enumerate(path)))
+        key = collapse_space(path, blank, space)
+        acc[key] = np.logaddexp(acc[key], s) if key in acc else s
+    return acc
+
+
+@pytest.mark.parametrize("T,V,space,seed", [(4, 3, 2, 0), (5, 4, 3, 1), (6, 3, 1, 2), (5, 4, 1, 3),
+                                            (6, 4, 2, 4)])
+def test_space_slot_unpruned_equals_brute_force(oracle_lib, T, V, space, seed):
+    # token bias on the space label too, so that runs of space frames occur
+    lp, lens = synth.peaky(1, T, V, seed=300 + seed, p_blank=0.4, blank_bias=1.0, token_bias=1.5,
+                           repeat_p=0.6)
+    exact = brute_force_space(lp[0], 0, space)
+    W = len(exact) + V
+    toks, L, S = oracle_lib.decode(lp, lens, W, W, 0, 1.0, T, space=space)
+    got = live_hyps(toks[0], L[0], S[0])
+    assert {h for h, _ in got} == set(exact)
+    for h, sc in got:
+        assert sc == pytest.approx(exact[h], abs=2e-5), h
+    assert np.logaddexp.reduce([sc for _, sc in got]) == pytest.approx(0.0, abs=2e-5)
+    # repeated spaces do occur among the hypotheses
+    assert any(space in h and any(a == b == space for a, b in zip(h, h[1:])) for h, _ in got)
+
+
+def test_space_slot_disabled_forms(oracle_lib):
+    # -1 and the blank label mean no space slot (sec. 3.4.2: space_id >= 0 and
+    # != blank_id)
+    lp, lens = synth.peaky(3, 40, 9, seed=310, p_blank=0.5)
+    base = oracle_lib.decode(lp, lens, 6, 6, 0, 1.0, 40)
+    for sp in (-1, 0):
+        other = oracle_lib.decode(lp, lens, 6, 6, 0, 1.0, 40, space=sp)
+        for a, b in zip(base, other):
+            assert (a == b).all()
+    # and a space label that never reaches a beam changes nothing: label 8
+    # made improbable in every frame
+    lp2 = lp.copy()
+    lp2[:, :, 8] = np.float32(-60.0)
+    plain = oracle_lib.decode(lp2, lens, 6, 6, 0, 1.0, 40)
+    sp = oracle_lib.decode(lp2, lens, 6, 6, 0, 1.0, 40, space=8)
+    for a, b in zip(plain, sp):
+        assert (a == b).all()
+
+
+def test_space_slot_golden(oracle_lib):
+    g = json.load(open(os.path.join(GOLDEN, "space_slot.json")))
+    lp = f32log(g["probs"])
+    T = lp.shape[0]
+    toks, L, S = oracle_lib.decode(lp[None], [T], g["beam"], g["nbest"], g["blank"],
+                                   g["threshold"], T, space=g["space"])
+    hyps = live_hyps(toks[0], L[0], S[0])
+    assert [list(h) for h, _ in hyps] == g["expected_tokens"]
+    for (_, s), p in zip(hyps, g["expected_scores_log"]):
+        assert s == pytest.approx(math.log(p), abs=1e-6)
+    # streaming gives the same (the space slot is part of every step)
+    st = oracle_lib.Stream(g["beam"], g["vocab"], g["blank"], space=g["space"])
+    st.feed(lp)
+    t2, l2, s2 = st.read(g["nbest"], T)
+    assert (t2 == toks[0]).all() and (l2 == L[0]).all() and (s2 == S[0]).all()
