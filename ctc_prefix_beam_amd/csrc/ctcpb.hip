@@ -2247,6 +2247,27 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
   Beam b;
   beam_fresh(b, L.blank);
   beam_store(C, b);
+  if (L.W > kMaxBeam) {
+    // the wide decoder's kept state: the empty hypothesis in slot 0, every
+    // other slot dead, no token rows written yet
+    float* wf = reinterpret_cast<float*>(base + L.o_wide);
+    int* wi = reinterpret_cast<int*>(base + L.o_wide);
+    for (int i = lane; i < kMaxBeamWide; i += kWave) {
+      wf[kWPb * kMaxBeamWide + i] = i == 0 ? 0.0f : kNeg;
+      wf[kWPnb * kMaxBeamWide + i] = kNeg;
+      wf[kWSc * kMaxBeamWide + i] = i == 0 ? 0.0f : kNeg;
+      wi[kWLast * kMaxBeamWide + i] = L.blank;
+      wi[kWLen * kMaxBeamWide + i] = 0;
+      wi[kWPar * kMaxBeamWide + i] = -1;
+      wi[kWH * kMaxBeamWide + i] = (int)kHashEmpty;
+      wi[kWHp * kMaxBeamWide + i] = (int)kHashEmpty;
+      wi[kWLive * kMaxBeamWide + i] = i == 0 ? 1 : 0;
+      wi[kWSrc0 * kMaxBeamWide + i] = -1;
+      wi[kWSrc1 * kMaxBeamWide + i] = -1;
+      wi[kWFlen0 * kMaxBeamWide + i] = -1;
+      wi[kWFlen1 * kMaxBeamWide + i] = -1;
+    }
+  }
   if (L.paged) {
     int* gt = reinterpret_cast<int*>(base + L.o_tab);
     int* gr = reinterpret_cast<int*>(base + L.o_ref);
@@ -2355,13 +2376,11 @@ int resolve(const ctcpb_config* cfg, Resolved& R) {
 
 int align16(int x) { return (x + 15) & ~15; }
 
-// Beams above 32 run on the wide offline kernel, which keeps flat token lists:
-// paged storage and streaming need the narrow decoder.
+// Beams above 32 run on the wide kernel, which keeps flat token lists: paged
+// storage needs the narrow decoder.
 int check_wide(const Resolved& R, bool streaming) {
+  (void)streaming;
   if (R.W <= kMaxBeam) return CTCPB_OK;
-  if (streaming)
-    return fail(CTCPB_ERR_UNSUPPORTED, "streaming supports beam <= 32 (this beam: " +
-                                           std::to_string(R.W) + ")");
   if (R.paged)
     return fail(CTCPB_ERR_UNSUPPORTED, "paged storage supports beam <= 32 (this beam: " +
                                            std::to_string(R.W) + "); use flat storage");
@@ -2583,7 +2602,7 @@ int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
   if (wide_path) {
-    if (int rc = launch(wide::decode_wide_kernel, batch, wide::kNT,
+    if (int rc = launch(wide::decode_wide_kernel<false>, batch, wide::kNT,
                         wide::lds_bytes(R.V, P.S.nslot), st, P, "decode_wide_kernel"))
       return rc;
     return ok();
@@ -2716,8 +2735,15 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
     return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");
   Params P{};
   P.L = L;
-  P.S = plan_lds(L);
-  if (int rc = check_lds(P.L, P.S)) return rc;
+  const bool wide_path = R.W > kMaxBeam;
+  if (!wide_path) {
+    P.S = plan_lds(L);
+    if (int rc = check_lds(P.L, P.S)) return rc;
+  } else {
+    P.S.nslot = wide::lds_bytes(R.V, 2) <= kLdsLimit ? 2 : 1;
+    if (wide::lds_bytes(R.V, P.S.nslot) > kLdsLimit)
+      return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
+  }
   P.N = R.N;
   P.max_out_len = R.mol;
   P.lp = log_prob_chunk;
@@ -2731,6 +2757,13 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
   P.state = static_cast<char*>(state);
   P.vec4 = aligned16(log_prob_chunk) && (R.V % 4 == 0) && (stride_row % 4 == 0) &&
            (stride_t % 4 == 0);
+  if (wide_path) {
+    if (int rc = launch(wide::decode_wide_kernel<true>, n_rows, wide::kNT,
+                        wide::lds_bytes(R.V, P.S.nslot), static_cast<hipStream_t>(stream), P,
+                        "decode_wide_kernel<stream>"))
+      return rc;
+    return ok();
+  }
   if (int rc = launch(decode_kernel_for<true>(R.W), n_rows, 64 * (3 + P.S.nprod), P.S.total,
                       static_cast<hipStream_t>(stream), P, "decode_kernel<stream>"))
     return rc;
@@ -2782,6 +2815,12 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
   P.out_tokens = out_tokens;
   P.out_lengths = out_lengths;
   P.out_scores = out_scores;
+  if (R.W > kMaxBeam) {
+    if (int rc = launch(wide::read_state_wide_kernel, n_rows, wide::kNT, 0,
+                        static_cast<hipStream_t>(stream), P, "read_state_wide_kernel"))
+      return rc;
+    return ok();
+  }
   // only the small per-row scratch is needed: rows/ranks, no frame buffers
   const int lds = lds::scal + kScalCount * 4;
   if (int rc = launch(read_state_kernel, n_rows, 64, lds, static_cast<hipStream_t>(stream), P,

@@ -8,6 +8,8 @@
 //   header      64 x int32   step, last frame, counters, parity bookkeeping
 //   beam arrays kMaxBeam x {pb, pnb, score, len, last token, parent slot,
 //               second-to-last token, live, prefix hash, parent-prefix hash}
+//   wide        beams above kMaxBeam: kWideArrays x kMaxBeamWide words of the
+//               wide decoder's beam state
 //   sel         cap_sel x int32     offline: selected frame indices
 //   flat:       clist[2][beam][ldc] int32 tokens, double-buffered by parity
 //               (ldc = cap rounded up to a multiple of 4)
@@ -22,6 +24,14 @@
 namespace ctcpb {
 
 constexpr int kMaxBeam = 32;     // widest beam of the fused decoder
+constexpr int kMaxBeamWide = 128;   // widest beam of the wide decoder
+
+// Beam state of the wide decoder (beams above kMaxBeam) kept between the
+// chunks of a stream: arrays of kMaxBeamWide entries, in this order.
+enum WideArray {
+  kWPb = 0, kWPnb, kWSc, kWLast, kWLen, kWPar, kWH, kWHp, kWLive, kWSrc0, kWSrc1, kWFlen0,
+  kWFlen1, kWideArrays
+};
 constexpr int kHdrInts = 64;
 constexpr int kInvalidPage = -1;
 
@@ -62,6 +72,7 @@ struct Layout {
   int cap_sel;    // entries of sel (offline: max_T; streaming: 0)
   int64_t row_bytes;
   int64_t o_beam, o_sel, o_clist, o_tab, o_ref, o_free, o_pages, o_tail, o_tlen;
+  int64_t o_wide;   // beams above kMaxBeam: the wide decoder's beam state (WideArray)
 };
 
 // Beam arrays inside a row region (offsets from o_beam).
@@ -92,6 +103,8 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   int64_t off = kHdrInts * 4;
   L.o_beam = off;
   off += BeamArrays::bytes;
+  L.o_wide = off;
+  if (W > kMaxBeam) off += align256((int64_t)kWideArrays * kMaxBeamWide * 4);
   L.o_sel = off;
   off += align256((int64_t)cap_sel * 4);
   if (!paged) {

@@ -178,13 +178,60 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
   }
 }
 
+// The N best of one row (sec. 3.6): live slots by (score desc, slot asc),
+// tokens from the flat lists of the last step's parity.  out_rank: LDS
+// scratch of at least kNT ints.  Ends with a block barrier.
+__device__ __forceinline__ void wide_nbest(const Params& P, int out_row, int W, int step, int ldc,
+                                           const int* clist, const int* s_live, const float* s_sc,
+                                           const int* s_len, int* out_rank) {
+  const int tid = threadIdx.x;
+  const int parity = step > 0 ? (step - 1) & 1 : 0;
+  const int N = P.N, mol = P.max_out_len;
+  out_rank[tid] = -1;
+  __syncthreads();
+  if (tid < W && s_live[tid]) {
+    const float sc = s_sc[tid];
+    int r = 0;
+    for (int j = 0; j < W; j++) {
+      if (!s_live[j]) continue;
+      const float sj = s_sc[j];
+      r += (sj > sc || (sj == sc && j < tid)) ? 1 : 0;
+    }
+    if (r < N) out_rank[r] = tid;
+  }
+  __syncthreads();
+  if (tid < N) {
+    const int s = out_rank[tid];
+    P.out_lengths[(int64_t)out_row * N + tid] = s < 0 ? 0 : s_len[s];
+    P.out_scores[(int64_t)out_row * N + tid] = s < 0 ? kNeg : s_sc[s];
+  }
+  int* ot = P.out_tokens + (int64_t)out_row * N * mol;
+  for (int i = tid; i < N * mol; i += kNT) {
+    const int n = i / mol, pos = i - n * mol;
+    const int s = out_rank[n];
+    int v = -1;
+    if (s >= 0 && pos < s_len[s]) v = step > 0 ? clist[(int64_t)(parity * W + s) * ldc + pos] : -1;
+    ot[i] = v;
+  }
+  __syncthreads();
+}
+
+// Offline rows (STREAM = false) or streaming chunk rows (STREAM = true: the
+// beam state is loaded from the stream's region at the start and stored back
+// at the end; frames come from the chunk, optionally gated by a speech mask).
+template <bool STREAM>
 __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   extern __shared__ __align__(16) char smem[];
   const Layout L = P.L;
   const int W = L.W, V = L.V, blank = L.blank;
   const int tid = threadIdx.x;
   const int row_i = blockIdx.x;
-  char* base = P.state + (int64_t)row_i * L.row_bytes;
+  int srow = row_i;
+  if (STREAM) {
+    srow = P.rows ? P.rows[row_i] : row_i;
+    if (srow < 0 || srow >= P.num_rows) return;
+  }
+  char* base = P.state + (int64_t)srow * L.row_bytes;
   int* hdr = reinterpret_cast<int*>(base);
   const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
   int* clist = reinterpret_cast<int*>(base + L.o_clist);
@@ -230,39 +277,93 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   int16_t* rmap = reinterpret_cast<int16_t*>(smem + off::end + nbuf * off::a16(V * 4));
   const int wave = tid >> 6;
 
-  const int nframes = hdr[kNSel];
   const int K = min(V - 1, 2 * W + 2);
   const int ldc = L.ldc;
+  // streaming: chunk frame c is frame number frame0 + c; with a speech mask
+  // only the frames it flags are decoded (sec. 9 is_speech_mask,
+  // start_frame_idx).  next_frame(c) is the first chunk frame >= c to decode
+  // (the scan is the same on every thread).
+  const int step_in = STREAM ? hdr[kStep] : 0;
+  const int frame0 = STREAM ? (P.start_frame ? P.start_frame[row_i] : hdr[kFrames]) : 0;
+  const uint8_t* speech = STREAM && P.speech ? P.speech + (int64_t)row_i * P.T : nullptr;
+  auto next_frame = [&](int c) {
+    if (speech)
+      while (c < P.T && speech[c] == 0) c++;
+    return c;
+  };
+  int nframes;
+  if (STREAM) {
+    int avail = P.T;
+    if (speech) {
+      if (tid == 0) sh[14] = 0;
+      __syncthreads();
+      int cnt = 0;
+      for (int c = tid; c < P.T; c += kNT) cnt += speech[c] != 0;
+      if (cnt) atomicAdd(&sh[14], cnt);
+      __syncthreads();
+      avail = sh[14];
+    }
+    nframes = L.cap - step_in;
+    nframes = nframes < 0 ? 0 : (nframes > avail ? avail : nframes);
+  } else {
+    nframes = hdr[kNSel];
+  }
+  // the row of frame f: offline, frame sel[f] of the row; streaming, chunk row
+  // cf (the f-th frame to decode)
+  int cf = STREAM ? next_frame(0) : 0;
+  auto frame_src = [&](int f, int c) {
+    return lp_row + (int64_t)(STREAM ? c : sel[f]) * P.stride_t;
+  };
 
-  // fresh row: the empty hypothesis in slot 0 (sec. 13), every other slot dead
   for (int c = tid; c < V; c += kNT) rmap[c] = -1;
+  float* wst = reinterpret_cast<float*>(base + L.o_wide);   // streaming: kept beam state
+  int* wsti = reinterpret_cast<int*>(base + L.o_wide);
   if (tid < kMaxW) {
-    s_live[tid] = tid == 0 ? 1 : 0;
-    s_pb[tid] = tid == 0 ? 0.0f : kNeg;
-    s_pnb[tid] = kNeg;
-    s_sc[tid] = tid == 0 ? 0.0f : kNeg;
-    s_last[tid] = blank;
-    s_len[tid] = 0;
-    s_par[tid] = -1;
-    s_h[tid] = kHashEmpty;
-    s_hp[tid] = kHashEmpty;
-    s_src[tid] = s_src[kMaxW + tid] = -1;
-    s_flen[tid] = s_flen[kMaxW + tid] = -1;
+    if (STREAM) {
+      s_pb[tid] = wst[kWPb * kMaxW + tid];
+      s_pnb[tid] = wst[kWPnb * kMaxW + tid];
+      s_sc[tid] = wst[kWSc * kMaxW + tid];
+      s_last[tid] = wsti[kWLast * kMaxW + tid];
+      s_len[tid] = wsti[kWLen * kMaxW + tid];
+      s_par[tid] = wsti[kWPar * kMaxW + tid];
+      s_h[tid] = (uint32_t)wsti[kWH * kMaxW + tid];
+      s_hp[tid] = (uint32_t)wsti[kWHp * kMaxW + tid];
+      s_live[tid] = wsti[kWLive * kMaxW + tid];
+      s_src[tid] = wsti[kWSrc0 * kMaxW + tid];
+      s_src[kMaxW + tid] = wsti[kWSrc1 * kMaxW + tid];
+      s_flen[tid] = wsti[kWFlen0 * kMaxW + tid];
+      s_flen[kMaxW + tid] = wsti[kWFlen1 * kMaxW + tid];
+    } else {
+      // fresh row: the empty hypothesis in slot 0 (sec. 13), every other slot dead
+      s_live[tid] = tid == 0 ? 1 : 0;
+      s_pb[tid] = tid == 0 ? 0.0f : kNeg;
+      s_pnb[tid] = kNeg;
+      s_sc[tid] = tid == 0 ? 0.0f : kNeg;
+      s_last[tid] = blank;
+      s_len[tid] = 0;
+      s_par[tid] = -1;
+      s_h[tid] = kHashEmpty;
+      s_hp[tid] = kHashEmpty;
+      s_src[tid] = s_src[kMaxW + tid] = -1;
+      s_flen[tid] = s_flen[kMaxW + tid] = -1;
+    }
   }
   // with two row buffers, wave 3 fetches frame f + 1 while frame f is decoded
-  if (nbuf == 2 && wave == 3 && nframes > 0)
-    row_fetch_async(lp_row + (int64_t)sel[0] * P.stride_t, rows, V, P.vec4);
-  int last_t = -1, step = 0, prevK = 0, nver = 0;
+  if (nbuf == 2 && wave == 3 && nframes > 0) row_fetch_async(frame_src(0, cf), rows, V, P.vec4);
+  int last_t = STREAM ? hdr[kLastT] : -1, step = step_in, prevK = 0, nver = 0;
   for (int i = tid; i < 2 * 256; i += kNT) khist[i] = 0;
   if (tid == 0) {
-    sh[6] = sh[7] = 0;   // common token prefix of the live rows of parity 0 / 1
+    // common token prefix of the live rows of parity 0 / 1
+    sh[6] = STREAM ? hdr[kCpl0] : 0;
+    sh[7] = STREAM ? hdr[kCpl1] : 0;
     sh[9] = 0;    // exact token comparisons
-    sh[10] = 0;   // status bits
+    sh[10] = STREAM ? hdr[kStatus] : 0;   // status bits
   }
   __syncthreads();
 
   for (int f = 0; f < nframes; f++) {
-    const int t = sel[f];
+    const int t = STREAM ? frame0 + cf : sel[f];
+    const int cnext = STREAM && f + 1 < nframes ? next_frame(cf + 1) : 0;
     const bool g = t > last_t + 1;    // frames skipped before t (step 0: t > 0)
     const int p = step & 1, q = p ^ 1;
     // ---- stage the row; clear the previous list's label map entries
@@ -270,7 +371,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     if (nbuf == 2) {
       if (wave == 3) row_fetch_wait();
     } else {
-      const float* gr = lp_row + (int64_t)t * P.stride_t;
+      const float* gr = frame_src(f, cf);
       if (P.vec4) {
         for (int i = tid; i < (V >> 2); i += kNT)
           reinterpret_cast<float4*>(row)[i] = reinterpret_cast<const float4*>(gr)[i];
@@ -282,8 +383,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     __syncthreads();
     // the other buffer was last read in the previous step: fetch the next frame
     if (nbuf == 2 && wave == 3 && f + 1 < nframes)
-      row_fetch_async(lp_row + (int64_t)sel[f + 1] * P.stride_t, rows + ((f + 1) & 1) * rstride,
-                      V, P.vec4);
+      row_fetch_async(frame_src(f + 1, cnext), rows + ((f + 1) & 1) * rstride, V, P.vec4);
 
     // ---- the frame's best K non-blank labels, (lp desc, label asc)
     auto lkey = [&](int c) -> uint64_t {
@@ -353,6 +453,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       __syncthreads();
       last_t = t;
       step++;
+      cf = cnext;
       continue;
     }
 
@@ -925,38 +1026,41 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     __syncthreads();
     last_t = t;
     step++;
+    cf = cnext;
   }
 
-  // ---- N best (sec. 3.6): live slots by (score desc, slot asc)
-  const int parity = step > 0 ? (step - 1) & 1 : 0;
-  const int N = P.N, mol = P.max_out_len;
-  int* out_rank = hist;   // rank -> slot
-  if (tid < 256) out_rank[tid] = -1;
-  __syncthreads();
-  if (tid < W && s_live[tid]) {
-    const float sc = s_sc[tid];
-    int r = 0;
-    for (int j = 0; j < W; j++) {
-      if (!s_live[j]) continue;
-      const float sj = s_sc[j];
-      r += (sj > sc || (sj == sc && j < tid)) ? 1 : 0;
+  if (STREAM) {
+    // keep the beam state for the stream's next chunk
+    if (nver) atomicAdd(&sh[9], nver);
+    if (tid < kMaxW) {
+      wst[kWPb * kMaxW + tid] = s_pb[tid];
+      wst[kWPnb * kMaxW + tid] = s_pnb[tid];
+      wst[kWSc * kMaxW + tid] = s_sc[tid];
+      wsti[kWLast * kMaxW + tid] = s_last[tid];
+      wsti[kWLen * kMaxW + tid] = s_len[tid];
+      wsti[kWPar * kMaxW + tid] = s_par[tid];
+      wsti[kWH * kMaxW + tid] = (int)s_h[tid];
+      wsti[kWHp * kMaxW + tid] = (int)s_hp[tid];
+      wsti[kWLive * kMaxW + tid] = s_live[tid];
+      wsti[kWSrc0 * kMaxW + tid] = s_src[tid];
+      wsti[kWSrc1 * kMaxW + tid] = s_src[kMaxW + tid];
+      wsti[kWFlen0 * kMaxW + tid] = s_flen[tid];
+      wsti[kWFlen1 * kMaxW + tid] = s_flen[kMaxW + tid];
     }
-    if (r < N) out_rank[r] = tid;
+    __syncthreads();
+    if (tid == 0) {
+      hdr[kStep] = step;
+      hdr[kLastT] = last_t;
+      hdr[kFrames] = frame0 + P.T;
+      hdr[kStatus] = sh[10];
+      hdr[kVerifies] += sh[9];
+      hdr[kCpl0] = sh[6];
+      hdr[kCpl1] = sh[7];
+    }
+    return;
   }
-  __syncthreads();
-  if (tid < N) {
-    const int s = out_rank[tid];
-    P.out_lengths[(int64_t)row_i * N + tid] = s < 0 ? 0 : s_len[s];
-    P.out_scores[(int64_t)row_i * N + tid] = s < 0 ? kNeg : s_sc[s];
-  }
-  int* ot = P.out_tokens + (int64_t)row_i * N * mol;
-  for (int i = tid; i < N * mol; i += kNT) {
-    const int n = i / mol, pos = i - n * mol;
-    const int s = out_rank[n];
-    int v = -1;
-    if (s >= 0 && pos < s_len[s]) v = step > 0 ? clist[(int64_t)(parity * W + s) * ldc + pos] : -1;
-    ot[i] = v;
-  }
+
+  wide_nbest(P, row_i, W, step, ldc, clist, s_live, s_sc, s_len, hist);
   if (nver) atomicAdd(&sh[9], nver);
   __syncthreads();
   if (tid == 0) {
@@ -969,6 +1073,32 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     hdr[kCpl0] = hdr[kCpl1] = hdr[kPcp0] = hdr[kPcp1] = 0;
     hdr[kFrames] = 0;
   }
+}
+
+// read_state for streams of beams above kMaxBeam: the N best of each listed
+// stream from its kept beam state, without changing it.
+__global__ __launch_bounds__(kNT) void read_state_wide_kernel(Params P) {
+  __shared__ int out_rank[kNT];
+  __shared__ int s_live[kMaxW];
+  __shared__ int s_len[kMaxW];
+  __shared__ float s_sc[kMaxW];
+  const Layout L = P.L;
+  const int tid = threadIdx.x;
+  const int srow = P.rows ? P.rows[blockIdx.x] : (int)blockIdx.x;
+  if (srow < 0 || srow >= P.num_rows) return;
+  const char* base = P.state + (int64_t)srow * L.row_bytes;
+  const int step = reinterpret_cast<const int*>(base)[kStep];
+  const float* wst = reinterpret_cast<const float*>(base + L.o_wide);
+  const int* wsti = reinterpret_cast<const int*>(base + L.o_wide);
+  if (tid < kMaxW) {
+    // a stream that has decoded nothing holds the empty hypothesis (sec. 13)
+    s_live[tid] = step > 0 ? wsti[kWLive * kMaxW + tid] : (tid == 0 ? 1 : 0);
+    s_len[tid] = step > 0 ? wsti[kWLen * kMaxW + tid] : 0;
+    s_sc[tid] = step > 0 ? wst[kWSc * kMaxW + tid] : (tid == 0 ? 0.0f : kNeg);
+  }
+  __syncthreads();
+  wide_nbest(P, (int)blockIdx.x, L.W, step, L.ldc, reinterpret_cast<const int*>(base + L.o_clist),
+             s_live, s_sc, s_len, out_rank);
 }
 
 }  // namespace wide

@@ -38,8 +38,8 @@ enum {
   CTCPB_OK = 0,
   CTCPB_ERR_INVALID = 1,     /* an argument is out of range or inconsistent */
   CTCPB_ERR_TOO_SMALL = 2,   /* workspace / state buffer smaller than required */
-  CTCPB_ERR_UNSUPPORTED = 3, /* valid but not supported by this library (beam > 32 with paged storage
-                                or streaming, LDS budget) */
+  CTCPB_ERR_UNSUPPORTED = 3, /* valid but not supported by this library (beam > 32 with paged storage,
+                                LDS budget) */
   CTCPB_ERR_DEVICE = 4       /* a HIP launch failed */
 };
 
@@ -48,7 +48,8 @@ enum { CTCPB_STORAGE_FLAT = 0, CTCPB_STORAGE_PAGED = 1 };
 /* Decoder configuration (sec. 10 GpuDecoderConfig, sec. 11 options). */
 typedef struct {
   int32_t beam;            /* beam width W, 1..128 (sec. 10); beams above 32 (the page's
-                              multi-kernel path) are decoded offline with flat storage only */
+                              multi-kernel path) run on a separate decoder, offline and
+                              streaming, with flat storage only */
   int32_t nbest;           /* hypotheses reported per row, 1..beam */
   int32_t vocab;           /* V >= 2, at most 16384 */
   int32_t blank_id;        /* 0 <= blank_id < vocab */

@@ -107,12 +107,14 @@ def test_decode_argument_errors_need_no_device(L):
                                   need, p, p, p, n) == 3
 
 
-def test_wide_beams_offline_flat_only(L):
-    # beams of 33..128 run on the wide offline decoder (flat token lists)
+def test_wide_beams_flat_only(L):
+    # beams of 33..128 run on the wide decoder (flat token lists), offline and
+    # streaming; its kept beam state makes a stream's region larger
     assert ws(L, cfg(beam=128, nbest=128), 2, 100)[0] == 0
     assert ws(L, cfg(beam=128, nbest=128, storage=1), 2, 100)[0] == 3
-    assert ss(L, cfg(beam=64, nbest=8), 4)[0] == 3
-    assert ss(L, cfg(beam=32, nbest=8), 4)[0] == 0
+    rc, wide = ss(L, cfg(beam=64, nbest=8), 4)
+    assert rc == 0 and wide > ss(L, cfg(beam=32, nbest=8), 4)[1]
+    assert ss(L, cfg(beam=64, nbest=8, storage=1), 4)[0] == 3
 
 
 def test_stream_argument_errors_need_no_device(L):

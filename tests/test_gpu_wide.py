@@ -78,3 +78,103 @@ def test_wide_beam_bpe1024_full_size_sampled():
     lp = x[rows].cpu().numpy()
     ref = oracle.decode(lp, lens[rows], W, W, 0, wl.threshold, wl.max_out_len)
     assert_parity(tuple(g[rows] for g in got), ref, what="wide bpe1024")
+
+
+# ------------------------------------------------- streaming, beams 33..128 --
+def oracle_streams(lp, W, capacity, cuts, nbest, mol, masks=None, starts=None):
+    outs = []
+    for s in range(lp.shape[0]):
+        st = oracle.Stream(W, lp.shape[2], 0, capacity)
+        for i, (a, b) in enumerate(zip(cuts[:-1], cuts[1:])):
+            m = None if masks is None else masks[s, a:b]
+            sf = None if (starts is None or i > 0) else int(starts[s])
+            st.feed(lp[s, a:b], m, sf)
+        outs.append(st.read(nbest, mol))
+    return tuple(np.stack([o[i] for o in outs]) for i in range(3))
+
+
+def pool_read(pool, rows=None):
+    import torch
+    t, l, s = pool.read(rows)
+    st = pool.row_stats().cpu().numpy()
+    torch.cuda.synchronize()
+    assert (st[:, 2] == 0).all()
+    return t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("W,cuts", [(40, [0, 16, 32, 48, 64, 80]), (64, [0, 1, 17, 40, 41, 80]),
+                                    (128, [0, 30, 80])])
+def test_wide_beams_streaming_equals_oracle_and_offline(W, cuts):
+    import torch
+    S, T, V = 4, 80, 200
+    lp, _ = synth.peaky(S, T, V, seed=90 + W, p_blank=0.55)
+    print(f"[case] wide stream W={W} S={S} T={T} V={V} cuts={cuts}", flush=True)
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T), V, S)
+    x = torch.from_numpy(lp).cuda()
+    fresh = pool_read(pool)
+    assert (fresh[1] == 0).all() and (fresh[2][:, 0] == 0).all()
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        pool.chunk(x[:, a:b])
+        if a == cuts[1]:
+            # read midway: non-mutating, and equal to the oracle there
+            mid = pool_read(pool)
+            assert_parity(mid, oracle_streams(lp, W, 4096, cuts[:3], W, T), what="wide mid")
+    got = pool_read(pool)
+    assert_parity(got, oracle_streams(lp, W, 4096, cuts, W, T), what=f"wide stream W{W}")
+    off = gpu_offline(lp, np.full(S, T, np.int32), W, W, 0, 1.0, T)
+    for g, o in zip(got, off):
+        assert np.array_equal(g, o)
+
+
+def test_wide_beams_streaming_mask_start_frames_capacity_and_reset():
+    import torch
+    S, T, V, W, CH, CAP = 4, 64, 120, 48, 16, 40
+    lp, _ = synth.peaky(S, T, V, seed=97, p_blank=0.5)
+    mask = (np.random.default_rng(98).random((S, T)) < 0.75).astype(np.uint8)
+    mask[1, :20] = 0                 # first decoded frame > 0: seeded under the gap rule
+    start = np.array([0, 3, 50, 9], np.int32)
+    print(f"[case] wide stream mask W={W} cap={CAP}", flush=True)
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, capacity=CAP), V, S)
+    x = torch.from_numpy(lp).cuda()
+    m = torch.from_numpy(mask).cuda()
+    rows = torch.tensor([2, 0, 3, 1], dtype=torch.int32, device="cuda")
+    perm = [2, 0, 3, 1]   # chunk row i continues stream perm[i]
+    for a in range(0, T, CH):
+        sf = torch.from_numpy(start[perm]).cuda() if a == 0 else None
+        pool.chunk(x[perm, a:a + CH], rows=rows, is_speech=m[perm, a:a + CH].contiguous(),
+                   start_frame=sf)
+    got = pool_read(pool)
+    ref = oracle_streams(lp, W, CAP, list(range(0, T + 1, CH)), W, T, masks=mask, starts=start)
+    assert_parity(got, ref, what="wide stream mask")
+    st = pool.row_stats().cpu().numpy()
+    assert list(st[:, 0]) == [min(CAP, int(mask[s].sum())) for s in range(S)]
+    assert list(st[:, 1]) == list(start + T)
+    # reset stream 1 and feed it stream 3's frames, unmasked
+    one = torch.tensor([1], dtype=torch.int32, device="cuda")
+    pool.reset(one)
+    for a in range(0, T, CH):
+        pool.chunk(x[[3], a:a + CH], rows=one)
+    t, l, s = pool.read(one)
+    ref = oracle_streams(lp[[3]], W, CAP, list(range(0, T + 1, CH)), W, T)
+    assert_parity((t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()), ref, what="wide reset")
+
+
+def test_wide_beams_per_frame_step():
+    import torch
+    S, T, V, W = 3, 30, 60, 36
+    lp, _ = synth.peaky(S, T, V, seed=99)
+    idx = (np.cumsum(np.random.default_rng(100).integers(1, 4, size=(S, T)), axis=1) - 1).astype(
+        np.int32)
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T), V, S)
+    x = torch.from_numpy(lp).cuda()
+    fi = torch.from_numpy(idx).cuda()
+    for t in range(T):
+        pool.step(x[:, t], frame_index=fi[:, t].contiguous())
+    got = pool_read(pool)
+    outs = []
+    for s in range(S):
+        st = oracle.Stream(W, V, 0)
+        for t in range(T):
+            st.step_at(lp[s, t], int(idx[s, t]))
+        outs.append(st.read(W, T))
+    assert_parity(got, tuple(np.stack([o[i] for o in outs]) for i in range(3)), what="wide step")
