@@ -809,12 +809,20 @@ __device__ __forceinline__ void store_seed(const Ctx& C, StoreState& ss, const W
 
 // ------------------------------------------------------------ steps >= 1 ---
 // The full beam x vocab selection (exact for any input): every candidate of
-// the step is regenerated from the per-beam values left in LDS and streamed
-// through stream_topk.  Used when the pruned candidate set cannot be proven
-// to contain the top W.
-__device__ __forceinline__ int full_select(const Ctx& C, const float* row, int par, int last) {
+// the step, from the per-beam values left in LDS and the frame's row in
+// global memory (its LDS slot has been handed back), into C.buf by a
+// streaming top-W.  Used when the pruned candidate set cannot be proven to
+// contain the top W.  The blank and repeated-label slots go first; then the
+// ordinary labels beam by beam, in slot order (slots are ranked, so the
+// beams' scores mostly decrease), each beam's labels read 256 at a time with
+// coalesced loads.  A beam is skipped when even the row's largest
+// log-probability plus its score, with the smallest id it could have, does
+// not beat the W-th candidate found so far: ordinary keys lp + A never exceed
+// max(lp) + A (rounded addition is monotone).
+__device__ __attribute__((noinline)) int full_select(const Ctx& C, const float* row, int par,
+                                                     int last) {
   const Layout& L = C.L;
-  const int W = L.W, V = L.V, blank = L.blank;
+  const int W = L.W, V = L.V, blank = L.blank, space = L.space;
   const int lane = lane_id();
   // labels merged away from each beam: the last label of each of its children
   if (lane < W) C.nchild[lane] = 0;
@@ -824,25 +832,77 @@ __device__ __forceinline__ int full_select(const Ctx& C, const float* row, int p
     C.childc[par * kMaxBeam + pos] = last;
   }
   lds_sync();
-  auto gen = [&](int64_t i) -> uint64_t {
-    const int k = (int)(i / V);
-    const int c = (int)(i - (int64_t)k * V);
-    const float A = C.A[k];
-    if (!(A > kNeg)) return 0ull;
-    float key;
-    if (c == blank) {
-      key = C.kb[k];
-    } else if (c == C.lastk[k] && c != L.space) {
-      key = C.kc[k];
-    } else {
-      const int nc = C.nchild[k];
-      for (int j = 0; j < nc; j++)
-        if (C.childc[k * kMaxBeam + j] == c) return 0ull;
-      key = row[c] + A;
+  // the row's largest non-blank log-probability
+  float rmax = -__builtin_inff();
+  for (int c0 = lane; c0 < V; c0 += 4 * kWave) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int c = c0 + u * kWave;
+      v[u] = c < V ? row[c] : -__builtin_inff();
     }
-    return key > kNeg ? compose(key, cand_id(k, c)) : 0ull;
+#pragma unroll
+    for (int u = 0; u < 4; u++) rmax = (c0 + u * kWave != blank) ? fmaxf(rmax, v[u]) : rmax;
+  }
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 64));
+
+  uint64_t* buf = C.buf;
+  uint64_t thr = comp_floor();   // the W-th key of the buffer once it holds W
+  int cnt = 0;
+  auto flush = [&]() {   // sort the buffer and keep its best W
+    lds_sync();
+    wave_sort_lds(buf, cnt);
+    lds_sync();
+    cnt = cnt < W ? cnt : W;
+    if (cnt == W) thr = buf[W - 1];
   };
-  return stream_topk(C, W, (int64_t)W * V, gen);
+  auto push = [&](uint64_t x) {   // keys of this lane (0 = none), 64 at a time
+    const bool pass = x > thr;
+    const uint64_t m = __ballot(pass);
+    if (pass) buf[cnt + lanes_below(m)] = x;
+    cnt += __popcll(m);
+    if (cnt > kBuf - kWave) flush();
+  };
+  // the blank and repeated-label slots of every beam
+  {
+    const bool in = lane < W;
+    const float A = in ? C.A[lane] : kNeg;
+    const float kb = in ? C.kb[lane] : kNeg, kc = in ? C.kc[lane] : kNeg;
+    const int lk = in ? C.lastk[lane] : blank;
+    const bool lv = A > kNeg;
+    push(lv && kb > kNeg ? compose(kb, cand_id(lane, blank)) : 0ull);
+    push(lv && lk != blank && lk != space && kc > kNeg ? compose(kc, cand_id(lane, lk)) : 0ull);
+  }
+  flush();
+  // ordinary labels, beam by beam
+  for (int k = 0; k < W; k++) {
+    const float Ak = C.A[k];
+    if (!(Ak > kNeg)) continue;
+    if (cnt == W && compose(rmax + Ak, cand_id(k, 0)) <= thr) continue;
+    const int lk = C.lastk[k];
+    const int lk_rep = lk != space ? lk : -1;   // the label of the repeated-label slot
+    const int nc = C.nchild[k];
+    const int chl = lane < nc ? C.childc[k * kMaxBeam + lane] : -1;
+    for (int c0 = lane; c0 - lane < V; c0 += 4 * kWave) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int c = c0 + u * kWave;
+        v[u] = c < V ? row[c] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int c = c0 + u * kWave;
+        bool ok = c < V && c != blank && c != lk_rep;
+        for (int j = 0; j < nc; j++) ok = ok && c != __builtin_amdgcn_readlane(chl, j);
+        const float key = v[u] + Ak;
+        push(ok && key > kNeg ? compose(key, cand_id(k, c)) : 0ull);
+      }
+    }
+    flush();
+  }
+  return cnt;
 }
 
 template <int NB>

@@ -202,3 +202,18 @@ def test_bounded_page_pool():
     assert np.array_equal(gpu_offline.last_stats[:, 3], high)
     for a, e in zip(got, full):
         assert np.array_equal(a, e)
+
+
+def test_exact_selection_every_step_at_vocab5000():
+    # frames uniform over every label (the blank included) at beam 32, V =
+    # 5000: candidates tie across the list boundary, so the ranked list cannot
+    # bound the unlisted labels and the full beam x vocabulary selection
+    # decides the steps; the oracle decides what is right
+    B, T, V, W = 2, 40, 5000, 32
+    lp, lens = synth.peaky(B, T, V, seed=61, p_blank=0.5)
+    lp[:, 1:] = np.float32(np.log(1.0 / V))   # frame 0 peaky (distinct per row), then uniform
+    print(f"[case] uniform every step B={B} T={T} V={V} W={W}", flush=True)
+    got = gpu_offline(lp, lens, W, W, 0, 1.0, T)
+    fb = gpu_offline.last_stats[:, cpb.STAT_FIELDS.index("fallbacks")]
+    assert_parity(got, oracle.decode(lp, lens, W, W, 0, 1.0, T), what="uniform every step")
+    assert (fb >= T // 4).all(), fb        # about a third of the steps
