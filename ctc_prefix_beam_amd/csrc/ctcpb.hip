@@ -819,17 +819,28 @@ __device__ __forceinline__ void store_seed(const Ctx& C, StoreState& ss, const W
 // log-probability plus its score, with the smallest id it could have, does
 // not beat the W-th candidate found so far: ordinary keys lp + A never exceed
 // max(lp) + A (rounded addition is monotone).
-__device__ __attribute__((noinline)) int full_select(const Ctx& C, const float* row, int par,
-                                                     int last) {
-  const Layout& L = C.L;
-  const int W = L.W, V = L.V, blank = L.blank, space = L.space;
+//
+// It takes plain values (the LDS structures it uses sit at fixed offsets), so
+// that the caller's context never has its address taken: a context passed by
+// reference to a function that is not inlined lives in scratch memory, and
+// the frame loop would reload its fields from there on every step.
+__device__ __attribute__((noinline)) int full_select(const float* row, int par, int last, int W,
+                                                     int V, int blank, int space) {
+  extern __shared__ __align__(16) char smem[];
+  uint64_t* const buf = reinterpret_cast<uint64_t*>(smem + lds::buf);
+  const float* const sA = reinterpret_cast<const float*>(smem + lds::A);
+  const float* const skb = reinterpret_cast<const float*>(smem + lds::kb);
+  const float* const skc = reinterpret_cast<const float*>(smem + lds::kc);
+  const int* const slastk = reinterpret_cast<const int*>(smem + lds::lastk);
+  int* const nchild = reinterpret_cast<int*>(smem + lds::nchild);
+  int* const childc = reinterpret_cast<int*>(smem + lds::childc);
   const int lane = lane_id();
   // labels merged away from each beam: the last label of each of its children
-  if (lane < W) C.nchild[lane] = 0;
+  if (lane < W) nchild[lane] = 0;
   lds_sync();
   if (par >= 0) {
-    const int pos = atomicAdd(&C.nchild[par], 1);
-    C.childc[par * kMaxBeam + pos] = last;
+    const int pos = atomicAdd(&nchild[par], 1);
+    childc[par * kMaxBeam + pos] = last;
   }
   lds_sync();
   // the row's largest non-blank log-probability
@@ -847,7 +858,6 @@ __device__ __attribute__((noinline)) int full_select(const Ctx& C, const float* 
 #pragma unroll
   for (int m = 32; m > 0; m >>= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, m, 64));
 
-  uint64_t* buf = C.buf;
   uint64_t thr = comp_floor();   // the W-th key of the buffer once it holds W
   int cnt = 0;
   auto flush = [&]() {   // sort the buffer and keep its best W
@@ -867,9 +877,9 @@ __device__ __attribute__((noinline)) int full_select(const Ctx& C, const float* 
   // the blank and repeated-label slots of every beam
   {
     const bool in = lane < W;
-    const float A = in ? C.A[lane] : kNeg;
-    const float kb = in ? C.kb[lane] : kNeg, kc = in ? C.kc[lane] : kNeg;
-    const int lk = in ? C.lastk[lane] : blank;
+    const float A = in ? sA[lane] : kNeg;
+    const float kb = in ? skb[lane] : kNeg, kc = in ? skc[lane] : kNeg;
+    const int lk = in ? slastk[lane] : blank;
     const bool lv = A > kNeg;
     push(lv && kb > kNeg ? compose(kb, cand_id(lane, blank)) : 0ull);
     push(lv && lk != blank && lk != space && kc > kNeg ? compose(kc, cand_id(lane, lk)) : 0ull);
@@ -877,13 +887,13 @@ __device__ __attribute__((noinline)) int full_select(const Ctx& C, const float* 
   flush();
   // ordinary labels, beam by beam
   for (int k = 0; k < W; k++) {
-    const float Ak = C.A[k];
+    const float Ak = sA[k];
     if (!(Ak > kNeg)) continue;
     if (cnt == W && compose(rmax + Ak, cand_id(k, 0)) <= thr) continue;
-    const int lk = C.lastk[k];
+    const int lk = slastk[k];
     const int lk_rep = lk != space ? lk : -1;   // the label of the repeated-label slot
-    const int nc = C.nchild[k];
-    const int chl = lane < nc ? C.childc[k * kMaxBeam + lane] : -1;
+    const int nc = nchild[k];
+    const int chl = lane < nc ? childc[k * kMaxBeam + lane] : -1;
     for (int c0 = lane; c0 - lane < V; c0 += 4 * kWave) {
       float v[4];
 #pragma unroll
@@ -1170,7 +1180,7 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   }
   if (__builtin_expect(need_full, 0)) {
     share_beam_values();
-    full_select(C, C.grow, par, last);
+    full_select(C.grow, par, last, W, V, blank, L.space);
     if (lane == 0) C.scal[kScalFallbacks] += 1;
     wc = lane < W ? C.buf[lane] : 0ull;
   }
@@ -2002,8 +2012,18 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     int cur = 0;            // streaming with a mask: next chunk frame to look at
     int blk_base = -64;     // the 64 flags read last, as a bit mask
     uint64_t blk = 0ull;
+#ifdef CTCPB_PHASE_PROF
+    uint64_t lw = 0, ll = 0, lt = clock64();
+#endif
     for (int f = 0, sl = 0; f < nframes; f++, sl = sl + 1 == nslot ? 0 : sl + 1) {
       if (!spin_wait(consumed, f - nslot, false, abortf)) break;
+#ifdef CTCPB_PHASE_PROF
+      {
+        const uint64_t now = clock64();
+        lw += now - lt;
+        lt = now;
+      }
+#endif
       int c = f;   // chunk frame decoded as step f
       if (STREAM && speech) {
         // the next flagged frame (nframes counts flagged frames only, so one
@@ -2033,7 +2053,22 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       if (lane == 0) frame_t[sl] = t;
       row_fetch_wait();
       flag_publish_lds(&loaded[sl], f);
+#ifdef CTCPB_PHASE_PROF
+      {
+        const uint64_t now = clock64();
+        ll += now - lt;
+        lt = now;
+      }
+#endif
     }
+#ifdef CTCPB_PHASE_PROF
+    // (offline: the row region's beam arrays are unused, they take the counters)
+    if (!STREAM && lane == 0) {
+      uint64_t* d = reinterpret_cast<uint64_t*>(base + L.o_beam);
+      d[0] = lw;
+      d[1] = ll;
+    }
+#endif
     return;
   }
 

@@ -69,6 +69,8 @@ def profile(name: str, paged: bool, seed: int = 0) -> dict:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     rb = dec.workspace.numel() // B
+    lay = dec.workspace[: B * rb].view(B, rb)[:, 256:256 + 16].contiguous().cpu().numpy()
+    ldr = lay.view(np.uint64).astype(np.float64)   # loader counters (beam arrays region)
     hdr = dec.workspace[: B * rb].view(B, rb)[:, :256].contiguous().cpu().numpy()
     h32 = hdr.view(np.int32)[:, :64]
     h64 = hdr.view(np.uint64)[:, :32].astype(np.float64)
@@ -84,6 +86,8 @@ def profile(name: str, paged: bool, seed: int = 0) -> dict:
                                          "wait": round(extra[:, 0].sum() / steps)},
            "rank_phases_per_frame": {v: round(rprof[:, i].sum() / steps)
                                      for i, v in enumerate(RANK_PHASES)},
+           "loader_cycles_per_frame": {"wait_for_slot": round(ldr[:, 0].sum() / steps),
+                                       "load": round(ldr[:, 1].sum() / steps)},
            "store_wave_cycles_per_step": {"work": round(extra[:, 3].sum() / steps),
                                           "wait": round(extra[:, 2].sum() / steps)},
            "shader_clock_ghz_est": round(beam["total"] / (ms * 1e6 / max(1, h32[:, 0].max())), 3)}

@@ -51,7 +51,16 @@ typedef struct {
                               multi-kernel path) run on a separate decoder, offline and
                               streaming, with flat storage only */
   int32_t nbest;           /* hypotheses reported per row, 1..beam */
-  int32_t vocab;           /* V >= 2, at most 16384 */
+  int32_t vocab;           /* V >= 2, at most 16384.  Beams of 1..32 keep a ring of
+                              frame rows (4V bytes each) and, paged, the page tables,
+                              refcounts and free stack in one CU's 160 KB of LDS;
+                              configurations that do not fit return
+                              CTCPB_ERR_UNSUPPORTED.  Flat storage fits up to
+                              V = 14640; paged storage at 1500 frames (offline max_T,
+                              streaming capacity) up to 13756 / 12896 / 11180 for
+                              beams 8 / 16 / 32, at 4096 frames and beam 32 up to
+                              5996 (a larger page_size shrinks the tables).  Beams
+                              above 32 fit every V. */
   int32_t blank_id;        /* 0 <= blank_id < vocab */
   float blank_threshold;   /* offline frame skip (sec. 3.5): frame t is decoded iff
                               log_prob[t, blank] < log(blank_threshold); >= 1 keeps
