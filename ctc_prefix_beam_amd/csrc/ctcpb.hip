@@ -820,11 +820,11 @@ __device__ __forceinline__ void store_seed(const Ctx& C, StoreState& ss, const W
 // not beat the W-th candidate found so far: ordinary keys lp + A never exceed
 // max(lp) + A (rounded addition is monotone).
 //
-// It takes plain values (the LDS structures it uses sit at fixed offsets), so
-// that the caller's context never has its address taken: a context passed by
-// reference to a function that is not inlined lives in scratch memory, and
-// the frame loop would reload its fields from there on every step.
-__device__ __attribute__((noinline)) int full_select(const float* row, int par, int last, int W,
+// It takes plain values (the LDS structures it uses sit at fixed offsets).
+// It is inlined although it is rare: a call would make the kernel reserve
+// scalar registers for the stack and the return address, and the beam
+// wave's frame loop, short of scalar registers, would spill more of its own.
+__device__ __forceinline__ int full_select(const float* row, int par, int last, int W,
                                                      int V, int blank, int space) {
   extern __shared__ __align__(16) char smem[];
   uint64_t* const buf = reinterpret_cast<uint64_t*>(smem + lds::buf);
@@ -1368,10 +1368,9 @@ __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int ste
 }
 
 // Grow the common prefix of the live beams of parity p (flat store), reading
-// the next 64 positions of every live row.  Not inlined: its 32 row
-// addresses would otherwise be computed (and held) on every store step.
-__device__ __attribute__((noinline)) int common_prefix_flat(const int* clist, int W, int ldc,
-                                                            int p, int cpl, bool nlive, int nlen) {
+// the next 64 positions of every live row (every 16th store step).
+__device__ __forceinline__ int common_prefix_flat(const int* clist, int W, int ldc, int p, int cpl,
+                                                  bool nlive, int nlen) {
   const int lane = lane_id();
   const uint64_t live = __ballot(lane < W && nlive);
   if (live == 0ull) return cpl;
@@ -2228,6 +2227,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
 
   bool aborted = false;
   int next_ready = -2;          // value of the next slot's flag, read one step early
+  int next_t = -1;              // and its frame's time index, read with it
   int wdone_seen = step - 1;    // store-wave progress last observed
   C.release = consumed;
   for (int f = 0, sl = 0, ek = 0; f < nframes; f++) {
@@ -2239,9 +2239,12 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       C.prof_t = clock64();
     }
 #endif
-    if (__builtin_expect(next_ready != f, 0) && !spin_wait(&ready[sl], f, true, abortf)) {
-      aborted = true;
-      break;
+    if (__builtin_expect(next_ready != f, 0)) {
+      if (!spin_wait(&ready[sl], f, true, abortf)) {
+        aborted = true;
+        break;
+      }
+      next_t = frame_t[sl];
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     PROF_MARK(0);
@@ -2249,7 +2252,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     C.Rc = rk_Rc(ek);
     C.Rl = rk_Rl(ek);
     C.rank = slot_rank(sl);
-    const int t = frame_t[sl];
+    const int t = uni(next_t);
     C.frame = f;
     // its row in global memory: offline, frame t of the row; streaming, chunk
     // row t - frame0 (not f: with a speech mask, step f of the chunk decodes
@@ -2283,6 +2286,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     // slot's data)
     next_ready = __hip_atomic_load(&ready[sl_next], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+    // (read after the flag: if the flag shows the frame, its time index,
+    // written before it, is seen too; otherwise it is read again after the wait)
+    next_t = __hip_atomic_load(&frame_t[sl_next], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     ring[(f % kRing) * kWave + lane] =
         make_int2(w.valid ? ((w.k << 16) | w.c) : -1, w.valid ? w.len_k : 0);
     PROF_MARK(7);
