@@ -2367,6 +2367,8 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
       wi[kWSrc1 * kMaxBeamWide + i] = -1;
       wi[kWFlen0 * kMaxBeamWide + i] = -1;
       wi[kWFlen1 * kMaxBeamWide + i] = -1;
+      wi[kWNp0 * kMaxBeamWide + i] = 0;
+      wi[kWNp1 * kMaxBeamWide + i] = 0;
     }
   }
   if (L.paged) {
@@ -2479,15 +2481,6 @@ int align16(int x) { return (x + 15) & ~15; }
 
 // Beams above 32 run on the wide kernel, which keeps flat token lists: paged
 // storage needs the narrow decoder.
-int check_wide(const Resolved& R, bool streaming) {
-  (void)streaming;
-  if (R.W <= kMaxBeam) return CTCPB_OK;
-  if (R.paged)
-    return fail(CTCPB_ERR_UNSUPPORTED, "paged storage supports beam <= 32 (this beam: " +
-                                           std::to_string(R.W) + "); use flat storage");
-  return CTCPB_OK;
-}
-
 LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
   LdsPlan S{};
   int off = lds::end;
@@ -2607,7 +2600,6 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
                          size_t* out_bytes) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, false)) return rc;
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
@@ -2618,7 +2610,6 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
 int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, true)) return rc;
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (num_streams < 0) return fail(CTCPB_ERR_INVALID, "num_streams must be >= 0");
   const Layout L = layout_for(R, R.cap_stream, 0);
@@ -2652,7 +2643,6 @@ int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t 
     return fail(CTCPB_ERR_INVALID, "stride_b must be >= 0 (0: every row reads the same frames)");
   if (!scratch_ws && !aligned16(workspace))
     return fail(CTCPB_ERR_INVALID, "workspace must be 16-byte aligned");
-  if (int rc = check_wide(R, false)) return rc;
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
   const size_t need = (size_t)batch * (size_t)L.row_bytes;
   if (workspace_bytes < need) {
@@ -2795,7 +2785,6 @@ int ctcpb_stream_reset(const ctcpb_config* cfg, void* state, size_t state_bytes,
                        int32_t num_streams, const int32_t* rows, int32_t n_rows, void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
   if (n_rows == 0) return ok();
@@ -2822,7 +2811,6 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
                           void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams || chunk_T < 0)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams and chunk_T >= 0");
   if (n_rows == 0 || chunk_T == 0) return ok();
@@ -2895,7 +2883,6 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
                      void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, true)) return rc;
   if (num_streams < 0 || n_rows < 0 || n_rows > num_streams)
     return fail(CTCPB_ERR_INVALID, "need 0 <= n_rows <= num_streams");
   if (n_rows == 0) return ok();
@@ -2934,7 +2921,6 @@ int ctcpb_row_stats(const ctcpb_config* cfg, const void* buf, size_t buf_bytes, 
                     int32_t max_T, int32_t* out, void* stream) {
   Resolved R;
   if (int rc = resolve(cfg, R)) return rc;
-  if (int rc = check_wide(R, max_T == 0)) return rc;
   if (num_rows < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "num_rows and max_T must be >= 0");
   if (num_rows == 0) return ok();
   if (!buf || !out) return fail(CTCPB_ERR_INVALID, "a required pointer is NULL");

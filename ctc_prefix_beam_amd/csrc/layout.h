@@ -30,7 +30,7 @@ constexpr int kMaxBeamWide = 128;   // widest beam of the wide decoder
 // chunks of a stream: arrays of kMaxBeamWide entries, in this order.
 enum WideArray {
   kWPb = 0, kWPnb, kWSc, kWLast, kWLen, kWPar, kWH, kWHp, kWLive, kWSrc0, kWSrc1, kWFlen0,
-  kWFlen1, kWideArrays
+  kWFlen1, kWNp0, kWNp1, kWideArrays
 };
 constexpr int kHdrInts = 64;
 constexpr int kInvalidPage = -1;

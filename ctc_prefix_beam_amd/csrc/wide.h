@@ -14,9 +14,11 @@
 //     be in the top W, which leaves about W^2/2 candidates;
 //   - those are held in registers, and a radix select over their 64-bit
 //     (score, id) keys gives the W-th; the winners are ranked by counting;
-//   - tokens are double-buffered flat lists in the workspace (sec. 3.1); merge
-//     parents are tracked structurally, with a hash lookup and an exact token
-//     comparison where a parent prefix may have been re-created.
+//   - tokens are double-buffered flat lists in the workspace (sec. 3.1), or
+//     pages with reference-counted sharing (sec. 3.4.5 paged variant, sec.
+//     4.2; see WidePager); merge parents are tracked structurally, with a
+//     hash lookup and an exact token comparison where a parent prefix may have
+//     been re-created.
 #pragma once
 
 namespace ctcpb {
@@ -66,7 +68,10 @@ constexpr int hist = cbuf + kCBuf * 8;                  // int [256]
 constexpr int sh = hist + 256 * 4;                      // int [16] block scalars
 constexpr int khist = sh + 16 * 4;                      // int [2][256]: kth_largest, kept zero
 constexpr int ksh = khist + 2 * 256 * 4;                // int [8]: kth_largest's scalars
-constexpr int end = ksh + 8 * 4;
+constexpr int pg = ksh + 8 * 4;                         // int [8]: pager scalars
+constexpr int pgP = pg + 8 * 4;                         // int [kMaxW]: page a slot appends into
+constexpr int np = pgP + kMaxW * 4;                     // int [2][kMaxW]: pages held per row
+constexpr int end = np + 2 * kMaxW * 4;
 }  // namespace off
 
 // Bytes of LDS for vocabulary V: nbuf rows of floats (2: the next frame is
@@ -178,11 +183,51 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
   }
 }
 
+// Paged token storage (sec. 3.4.5 paged variant, sec. 4.2) in the row region:
+// block tables [2][W][max_lp] of page ids (-1 none; the pages a row holds are
+// the leading entries of its table row), a reference count per page, a LIFO
+// stack of freed pages and a bump pointer over the row's pool of npages.
+// Each step forks every new row onto its source's pages, then appends the new
+// label in slot order: a label that starts a page takes a fresh one; one that
+// goes into a partial page shared with another row (its reference count,
+// less the slots before it that already copied it away, is above 1) copies
+// the page first; otherwise it writes in place.  A pop with nothing left
+// gives no page: the beam keeps its prefix without appending and the row's
+// status sets bit 0 (its outputs are then unspecified).
+struct WidePager {
+  int* tab;
+  int* ref;
+  int* fstk;
+  int* pages;
+  int W, ps, psh, mlp, npages;
+  __device__ int* row(int par, int s) const { return tab + (int64_t)(par * W + s) * mlp; }
+  // token pos of row (par, s), -1 where the row holds no page
+  __device__ int tok(int par, int s, int pos) const {
+    const int e = row(par, s)[pos >> psh];
+    return e >= 0 ? pages[(int64_t)e * ps + (pos & (ps - 1))] : -1;
+  }
+};
+
+__device__ __forceinline__ WidePager wide_pager(const Layout& L, char* base) {
+  WidePager G;
+  G.tab = reinterpret_cast<int*>(base + L.o_tab);
+  G.ref = reinterpret_cast<int*>(base + L.o_ref);
+  G.fstk = reinterpret_cast<int*>(base + L.o_free);
+  G.pages = reinterpret_cast<int*>(base + L.o_pages);
+  G.W = L.W;
+  G.ps = L.ps;
+  G.psh = L.ps_log2;
+  G.mlp = L.max_lp;
+  G.npages = L.npages;
+  return G;
+}
+
 // The N best of one row (sec. 3.6): live slots by (score desc, slot asc),
-// tokens from the flat lists of the last step's parity.  out_rank: LDS
-// scratch of at least kNT ints.  Ends with a block barrier.
+// tokens from the flat lists (or the pages) of the last step's parity.
+// out_rank: LDS scratch of at least kNT ints.  Ends with a block barrier.
 __device__ __forceinline__ void wide_nbest(const Params& P, int out_row, int W, int step, int ldc,
-                                           const int* clist, const int* s_live, const float* s_sc,
+                                           const int* clist, bool paged, const WidePager G,
+                                           const int* s_live, const float* s_sc,
                                            const int* s_len, int* out_rank) {
   const int tid = threadIdx.x;
   const int parity = step > 0 ? (step - 1) & 1 : 0;
@@ -210,7 +255,8 @@ __device__ __forceinline__ void wide_nbest(const Params& P, int out_row, int W, 
     const int n = i / mol, pos = i - n * mol;
     const int s = out_rank[n];
     int v = -1;
-    if (s >= 0 && pos < s_len[s]) v = step > 0 ? clist[(int64_t)(parity * W + s) * ldc + pos] : -1;
+    if (s >= 0 && pos < s_len[s] && step > 0)
+      v = paged ? G.tok(parity, s, pos) : clist[(int64_t)(parity * W + s) * ldc + pos];
     ot[i] = v;
   }
   __syncthreads();
@@ -236,6 +282,8 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
   int* clist = reinterpret_cast<int*>(base + L.o_clist);
   const float* lp_row = P.lp + (int64_t)row_i * P.stride_b;
+  const bool paged = L.paged != 0;
+  const WidePager G = wide_pager(L, base);
 
   int* Rc = reinterpret_cast<int*>(smem + off::Rc);
   float* Rl = reinterpret_cast<float*>(smem + off::Rl);
@@ -271,6 +319,9 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   int* sh = reinterpret_cast<int*>(smem + off::sh);
   int* khist = reinterpret_cast<int*>(smem + off::khist);
   int* ksh = reinterpret_cast<int*>(smem + off::ksh);
+  int* pgs = reinterpret_cast<int*>(smem + off::pg);      // free-stack depth, bump, high, counts
+  int* s_pgP = reinterpret_cast<int*>(smem + off::pgP);
+  int* s_np = reinterpret_cast<int*>(smem + off::np);
   const int nbuf = P.S.nslot;   // frame rows in LDS: 1 or 2
   float* rows = reinterpret_cast<float*>(smem + off::end);
   const int rstride = off::a16(V * 4) / 4;
@@ -333,6 +384,8 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_src[kMaxW + tid] = wsti[kWSrc1 * kMaxW + tid];
       s_flen[tid] = wsti[kWFlen0 * kMaxW + tid];
       s_flen[kMaxW + tid] = wsti[kWFlen1 * kMaxW + tid];
+      s_np[tid] = wsti[kWNp0 * kMaxW + tid];
+      s_np[kMaxW + tid] = wsti[kWNp1 * kMaxW + tid];
     } else {
       // fresh row: the empty hypothesis in slot 0 (sec. 13), every other slot dead
       s_live[tid] = tid == 0 ? 1 : 0;
@@ -346,7 +399,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_hp[tid] = kHashEmpty;
       s_src[tid] = s_src[kMaxW + tid] = -1;
       s_flen[tid] = s_flen[kMaxW + tid] = -1;
+      s_np[tid] = s_np[kMaxW + tid] = 0;
     }
+  }
+  if (!STREAM && paged) {
+    // a fresh row's pager: no page held, none in use
+    for (int i = tid; i < 2 * W * G.mlp; i += kNT) G.tab[i] = kInvalidPage;
+    for (int i = tid; i < G.npages; i += kNT) G.ref[i] = 0;
+    __threadfence();
   }
   // with two row buffers, wave 3 fetches frame f + 1 while frame f is decoded
   if (nbuf == 2 && wave == 3 && nframes > 0) row_fetch_async(frame_src(0, cf), rows, V, P.vec4);
@@ -358,6 +418,9 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     sh[7] = STREAM ? hdr[kCpl1] : 0;
     sh[9] = 0;    // exact token comparisons
     sh[10] = STREAM ? hdr[kStatus] : 0;   // status bits
+    pgs[0] = STREAM ? hdr[kFreeTop] : 0;
+    pgs[1] = STREAM ? hdr[kNextFree] : 0;
+    pgs[2] = STREAM ? hdr[kPagesHigh] : 0;
   }
   __syncthreads();
 
@@ -432,7 +495,22 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
           sc = key;
           h = hash_push(kHashEmpty, last);
           par = W > 1 ? W - 1 : -1;
-          clist[(int64_t)(0 * W + r) * ldc] = last;
+          if (!paged) {
+            clist[(int64_t)(0 * W + r) * ldc] = last;
+          } else {
+            // a page per seeded slot, taken in slot order from a fresh row's pool
+            const int top = pgs[0], nf = pgs[1];
+            const int pid = r < top ? G.fstk[top - 1 - r]
+                                    : (nf + r - top < G.npages ? nf + r - top : kInvalidPage);
+            if (pid >= 0) {
+              G.row(0, r)[0] = pid;
+              atomicExch(&G.ref[pid], 1);
+              G.pages[(int64_t)pid * G.ps] = last;
+              s_np[r] = 1;
+            } else {
+              atomicOr(&sh[10], kStatusOutOfPages);
+            }
+          }
         } else if (W > 1 && r == W - 1) {
           live = 1;
           pb = row[blank];
@@ -451,6 +529,13 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         s_flen[r] = len;
       }
       __syncthreads();
+      if (paged && tid == 0) {
+        const int m0 = min(W > 1 ? W - 1 : 1, K);
+        const int from = min(pgs[0], m0);
+        pgs[0] -= from;
+        pgs[1] = min(G.npages, pgs[1] + (m0 - from));
+        pgs[2] = max(pgs[2], pgs[1] - pgs[0]);
+      }
       last_t = t;
       step++;
       cf = cnext;
@@ -829,88 +914,181 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       nhp = c == blank ? s_hp[k] : s_h[k];
       if (c == blank) s_bslot[k] = tid;
     }
-    // ---- tokens: row tid of parity p <- row k of parity q (+ c).  If row k
-    // was itself copied from slot tid one step earlier, slot tid's row of
-    // parity p already holds its first s_flen[p][tid] tokens.
-    // Otherwise, if slot tid was live two steps ago, its row already holds the
-    // tokens that every live row then shared.
-    int start = 0;
-    const int klen = k >= 0 ? s_len[k] : 0;
-    if (k >= 0) {
-      const int oldlen = s_flen[p * kMaxW + tid];
-      if (oldlen >= 0) start = min(s_src[q * kMaxW + k] == tid ? oldlen : sh[6 + p], klen);
-    }
-    const int s4 = start >> 2;
-    const int e4 = (klen + 3) >> 2;
-    const int cnt = k >= 0 ? e4 - s4 : 0;
-    __syncthreads();   // s_bslot complete; every read of the old state done
-    // copy counts (int4 units) -> prefix sums; per destination its source
-    // slot and first int4
-    if (tid < kMaxW) hist[tid] = tid < W ? cnt : 0;
-    if (tid < W) {
-      hist[128 + tid] = k;
-      s_lim[tid] = s4;
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const int a = hist[2 * tid], b = hist[2 * tid + 1];
-      const int incl = wave_incl_scan(a + b);
-      s_offs[2 * tid] = incl - a - b;
-      s_offs[2 * tid + 1] = incl - b;
-      if (tid == 63) sh[5] = incl;
-    }
-    __syncthreads();
-    {
-      const int ntok4 = sh[5];
-      int4* c4 = reinterpret_cast<int4*>(clist);
-      const int64_t ld4 = ldc >> 2;
-      // destination of this thread's first item by binary search, later ones
-      // by walking forward
-      int a = 0;
-      if (tid < ntok4) {
-        int lo = 0, hi = W - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_offs[mid] <= tid) lo = mid;
-          else hi = mid - 1;
-        }
-        a = lo;
+    if (!paged) {
+      // ---- tokens: row tid of parity p <- row k of parity q (+ c).  If row k
+      // was itself copied from slot tid one step earlier, slot tid's row of
+      // parity p already holds its first s_flen[p][tid] tokens.
+      // Otherwise, if slot tid was live two steps ago, its row already holds the
+      // tokens that every live row then shared.
+      int start = 0;
+      const int klen = k >= 0 ? s_len[k] : 0;
+      if (k >= 0) {
+        const int oldlen = s_flen[p * kMaxW + tid];
+        if (oldlen >= 0) start = min(s_src[q * kMaxW + k] == tid ? oldlen : sh[6 + p], klen);
       }
-      auto where = [&](int i, int64_t& dst, int64_t& src) {
-        while (a + 1 < W && s_offs[a + 1] <= i) a++;
-        const int64_t pos4 = s_lim[a] + (i - s_offs[a]);
-        dst = (int64_t)(p * W + a) * ld4 + pos4;
-        src = (int64_t)(q * W + hist[128 + a]) * ld4 + pos4;
-      };
-      // four copies per round: the loads are issued before the stores
-      for (int i = tid; i < ntok4; i += 4 * kNT) {
-        int64_t d0, s0, d1 = 0, s1 = 0, d2 = 0, s2 = 0, d3 = 0, s3 = 0;
-        int4 v1, v2, v3;
-        where(i, d0, s0);
-        const int4 v0 = c4[s0];
-        const bool b1 = i + kNT < ntok4, b2 = i + 2 * kNT < ntok4, b3 = i + 3 * kNT < ntok4;
-        if (b1) {
-          where(i + kNT, d1, s1);
-          v1 = c4[s1];
+      const int s4 = start >> 2;
+      const int e4 = (klen + 3) >> 2;
+      const int cnt = k >= 0 ? e4 - s4 : 0;
+      __syncthreads();   // s_bslot complete; every read of the old state done
+      // copy counts (int4 units) -> prefix sums; per destination its source
+      // slot and first int4
+      if (tid < kMaxW) hist[tid] = tid < W ? cnt : 0;
+      if (tid < W) {
+        hist[128 + tid] = k;
+        s_lim[tid] = s4;
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const int a = hist[2 * tid], b = hist[2 * tid + 1];
+        const int incl = wave_incl_scan(a + b);
+        s_offs[2 * tid] = incl - a - b;
+        s_offs[2 * tid + 1] = incl - b;
+        if (tid == 63) sh[5] = incl;
+      }
+      __syncthreads();
+      {
+        const int ntok4 = sh[5];
+        int4* c4 = reinterpret_cast<int4*>(clist);
+        const int64_t ld4 = ldc >> 2;
+        // destination of this thread's first item by binary search, later ones
+        // by walking forward
+        int a = 0;
+        if (tid < ntok4) {
+          int lo = 0, hi = W - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_offs[mid] <= tid) lo = mid;
+            else hi = mid - 1;
+          }
+          a = lo;
         }
-        if (b2) {
-          where(i + 2 * kNT, d2, s2);
-          v2 = c4[s2];
+        auto where = [&](int i, int64_t& dst, int64_t& src) {
+          while (a + 1 < W && s_offs[a + 1] <= i) a++;
+          const int64_t pos4 = s_lim[a] + (i - s_offs[a]);
+          dst = (int64_t)(p * W + a) * ld4 + pos4;
+          src = (int64_t)(q * W + hist[128 + a]) * ld4 + pos4;
+        };
+        // four copies per round: the loads are issued before the stores
+        for (int i = tid; i < ntok4; i += 4 * kNT) {
+          int64_t d0, s0, d1 = 0, s1 = 0, d2 = 0, s2 = 0, d3 = 0, s3 = 0;
+          int4 v1, v2, v3;
+          where(i, d0, s0);
+          const int4 v0 = c4[s0];
+          const bool b1 = i + kNT < ntok4, b2 = i + 2 * kNT < ntok4, b3 = i + 3 * kNT < ntok4;
+          if (b1) {
+            where(i + kNT, d1, s1);
+            v1 = c4[s1];
+          }
+          if (b2) {
+            where(i + 2 * kNT, d2, s2);
+            v2 = c4[s2];
+          }
+          if (b3) {
+            where(i + 3 * kNT, d3, s3);
+            v3 = c4[s3];
+          }
+          c4[d0] = v0;
+          if (b1) c4[d1] = v1;
+          if (b2) c4[d2] = v2;
+          if (b3) c4[d3] = v3;
         }
-        if (b3) {
-          where(i + 3 * kNT, d3, s3);
-          v3 = c4[s3];
+      }
+      __syncthreads();
+      if (tid < W && k >= 0 && c != blank) clist[(int64_t)(p * W + tid) * ldc + klen] = c;
+      __threadfence_block();
+      __syncthreads();
+    } else {
+      // ---- tokens, paged (sec. 3.4.5 paged variant).  Pass 1: row tid of
+      // parity p takes the pages of row k of parity q and releases the ones it
+      // held; every reference is taken before any is released, so that a
+      // page held by both an old and a new row never drops to zero in between.
+      const int klen = k >= 0 ? s_len[k] : 0;
+      const int npo = tid < W ? s_np[p * kMaxW + tid] : 0;
+      const int nps = k >= 0 ? s_np[q * kMaxW + k] : 0;
+      int* drow = G.row(p, tid < W ? tid : 0);
+      const int* srow_k = G.row(q, k >= 0 ? k : 0);
+      __syncthreads();   // s_bslot complete; every read of the old state done
+      for (int j = 0; j < nps; j++) {
+        const int e = srow_k[j];
+        if ((j >= npo || drow[j] != e) && e >= 0) atomicAdd(&G.ref[e], 1);
+      }
+      __threadfence_block();
+      __syncthreads();
+      const int nmax = max(npo, nps);
+      for (int j = 0; j < nmax; j++) {
+        const int old = j < npo ? drow[j] : kInvalidPage;
+        const int e = j < nps ? srow_k[j] : kInvalidPage;
+        if (old == e) continue;
+        if (old >= 0 && atomicSub(&G.ref[old], 1) == 1) {
+          const int at = atomicAdd(&pgs[0], 1);
+          if (at < G.npages) G.fstk[at] = old;
         }
-        c4[d0] = v0;
-        if (b1) c4[d1] = v1;
-        if (b2) c4[d2] = v2;
-        if (b3) c4[d3] = v3;
+        drow[j] = e;
+      }
+      // Pass 2: the new label, in slot order.  It goes to offset klen mod
+      // page_size of page klen / page_size: a fresh page at offset 0, else the
+      // row's last page, copied first when another row still holds it.
+      const bool ext = tid < W && k >= 0 && c != blank;
+      const int po = klen & (G.ps - 1), pi = klen >> G.psh;
+      bool fresh = false;
+      int pshared = -1;
+      if (ext) {
+        if (po == 0) fresh = pi == nps && pi < G.mlp;
+        else if (pi == nps - 1) pshared = srow_k[pi];
+      }
+      if (tid < W) s_pgP[tid] = pshared;
+      __threadfence_block();
+      __syncthreads();
+      bool cow = false;
+      if (pshared >= 0) {
+        int before = 0;   // earlier slots appending into the same page copy it away first
+        for (int s2 = 0; s2 < tid; s2++) before += s_pgP[s2] == pshared ? 1 : 0;
+        const int rc = __hip_atomic_load(&G.ref[pshared], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        cow = rc - before > 1;
+      }
+      const bool need = fresh || cow;
+      const uint64_t bm = __ballot(need);
+      if ((tid & 63) == 0) pgs[4 + wave] = __popcll(bm);
+      __syncthreads();
+      const int ord = (wave > 0 ? pgs[4] : 0) + (wave > 1 ? pgs[5] : 0) +
+                      (wave > 2 ? pgs[6] : 0) + lanes_below(bm);
+      const int top = min(pgs[0], G.npages), nf = pgs[1];
+      const int nalloc = pgs[4] + pgs[5] + pgs[6] + pgs[7];
+      int npn = nps;
+      if (need) {
+        // pops in slot order: the free stack from its top, then the bump pointer
+        const int pid = ord < top ? G.fstk[top - 1 - ord]
+                                  : (nf + ord - top < G.npages ? nf + ord - top : kInvalidPage);
+        if (pid >= 0) {
+          __hip_atomic_store(&G.ref[pid], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          int* dst = G.pages + (int64_t)pid * G.ps;
+          if (cow) {
+            const int* src = G.pages + (int64_t)pshared * G.ps;
+            for (int j = 0; j < po; j++) dst[j] = src[j];
+            atomicSub(&G.ref[pshared], 1);   // stays >= 1: another row holds it
+          }
+          dst[po] = c;
+          drow[pi] = pid;
+          if (fresh) npn = nps + 1;
+        } else {
+          atomicOr(&sh[10], kStatusOutOfPages);   // keeps its prefix (sec. 4.2)
+        }
+      } else if (pshared >= 0) {
+        G.pages[(int64_t)pshared * G.ps + po] = c;   // the only holder left: in place
+      } else if (ext) {
+        atomicOr(&sh[10], kStatusOutOfPages);   // a row already short of pages
+      }
+      if (tid < W) s_np[p * kMaxW + tid] = npn;
+      __threadfence_block();
+      __syncthreads();
+      if (tid == 0) {
+        const int from = min(top, nalloc);
+        pgs[0] = top - from;
+        pgs[1] = min(G.npages, nf + (nalloc - from));
+        pgs[2] = max(pgs[2], pgs[1] - pgs[0]);
       }
     }
-    __syncthreads();
-    if (tid < W && k >= 0 && c != blank) clist[(int64_t)(p * W + tid) * ldc + klen] = c;
-    __threadfence_block();
-    __syncthreads();
 
     // ---- structural merge parents for the next step; a blank winner whose
     // source had no live parent may find its parent prefix re-created: hash
@@ -949,13 +1127,29 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         {
           const int i = hist[pos];
           if (s_tag[i] != want || i == tid) continue;
-          // the first nlen - 1 tokens of both rows, 16 per round (rows are
+          const int n = nlen - 1;
+          bool eq = true;
+          if (paged) {
+            // the first nlen - 1 tokens, page by page; a page both rows hold is equal
+            const int* ta = G.row(p, tid);
+            const int* tb = G.row(p, i);
+            for (int b0 = 0; b0 < n && eq; b0 += G.ps) {
+              const int ea = ta[b0 >> G.psh], eb = tb[b0 >> G.psh];
+              if (ea == eb && ea >= 0) continue;
+              if (ea < 0 || eb < 0) {
+                eq = false;
+                break;
+              }
+              const int m = min(G.ps, n - b0);
+              for (int j = 0; j < m && eq; j++)
+                eq = G.pages[(int64_t)ea * G.ps + j] == G.pages[(int64_t)eb * G.ps + j];
+            }
+          }
+          // flat: the first nlen - 1 tokens of both rows, 16 per round (rows are
           // 16-byte aligned: ldc is a multiple of 4)
           const int4* ra = reinterpret_cast<const int4*>(clist + (int64_t)(p * W + tid) * ldc);
           const int4* rb = reinterpret_cast<const int4*>(clist + (int64_t)(p * W + i) * ldc);
-          const int n = nlen - 1;
-          bool eq = true;
-          for (int x4 = 0; x4 * 4 < n && eq; x4 += 4) {
+          for (int x4 = 0; !paged && x4 * 4 < n && eq; x4 += 4) {
 #pragma unroll
             for (int u2 = 0; u2 < 4; u2++) {
               const int b = (x4 + u2) * 4;
@@ -981,7 +1175,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       s_src[p * kMaxW + tid] = k;
       s_flen[p * kMaxW + tid] = nlive ? nlen : -1;
     }
-    if ((step & 15) == 15) {
+    if (!paged && (step & 15) == 15) {
       // grow the common prefix of the live rows of parity p by up to 64
       // positions (it never shrinks: every row extends a row of the step before)
       if (tid < 64) {
@@ -1046,6 +1240,8 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       wsti[kWSrc1 * kMaxW + tid] = s_src[kMaxW + tid];
       wsti[kWFlen0 * kMaxW + tid] = s_flen[tid];
       wsti[kWFlen1 * kMaxW + tid] = s_flen[kMaxW + tid];
+      wsti[kWNp0 * kMaxW + tid] = s_np[tid];
+      wsti[kWNp1 * kMaxW + tid] = s_np[kMaxW + tid];
     }
     __syncthreads();
     if (tid == 0) {
@@ -1056,11 +1252,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       hdr[kVerifies] += sh[9];
       hdr[kCpl0] = sh[6];
       hdr[kCpl1] = sh[7];
+      hdr[kFreeTop] = pgs[0];
+      hdr[kNextFree] = pgs[1];
+      hdr[kPagesHigh] = pgs[2];
     }
     return;
   }
 
-  wide_nbest(P, row_i, W, step, ldc, clist, s_live, s_sc, s_len, hist);
+  wide_nbest(P, row_i, W, step, ldc, clist, paged, G, s_live, s_sc, s_len, hist);
   if (nver) atomicAdd(&sh[9], nver);
   __syncthreads();
   if (tid == 0) {
@@ -1068,7 +1267,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     hdr[kLastT] = last_t;
     hdr[kStatus] = sh[10];
     hdr[kVerifies] = sh[9];
-    hdr[kPagesHigh] = 0;
+    hdr[kPagesHigh] = paged ? pgs[2] : 0;
     hdr[kFallbacks] = 0;
     hdr[kCpl0] = hdr[kCpl1] = hdr[kPcp0] = hdr[kPcp1] = 0;
     hdr[kFrames] = 0;
@@ -1097,8 +1296,9 @@ __global__ __launch_bounds__(kNT) void read_state_wide_kernel(Params P) {
     s_sc[tid] = step > 0 ? wst[kWSc * kMaxW + tid] : (tid == 0 ? 0.0f : kNeg);
   }
   __syncthreads();
+  const WidePager G = wide_pager(L, const_cast<char*>(base));
   wide_nbest(P, (int)blockIdx.x, L.W, step, L.ldc, reinterpret_cast<const int*>(base + L.o_clist),
-             s_live, s_sc, s_len, out_rank);
+             L.paged != 0, G, s_live, s_sc, s_len, out_rank);
 }
 
 }  // namespace wide

@@ -38,8 +38,8 @@ enum {
   CTCPB_OK = 0,
   CTCPB_ERR_INVALID = 1,     /* an argument is out of range or inconsistent */
   CTCPB_ERR_TOO_SMALL = 2,   /* workspace / state buffer smaller than required */
-  CTCPB_ERR_UNSUPPORTED = 3, /* valid but not supported by this library (beam > 32 with paged storage,
-                                LDS budget) */
+  CTCPB_ERR_UNSUPPORTED = 3, /* valid but not supported by this library (LDS budget, vocab
+                                above 16384) */
   CTCPB_ERR_DEVICE = 4       /* a HIP launch failed */
 };
 
@@ -49,7 +49,12 @@ enum { CTCPB_STORAGE_FLAT = 0, CTCPB_STORAGE_PAGED = 1 };
 typedef struct {
   int32_t beam;            /* beam width W, 1..128 (sec. 10); beams above 32 (the page's
                               multi-kernel path) run on a separate decoder, offline and
-                              streaming, with flat storage only */
+                              streaming, flat or paged.  Its pager follows the page's
+                              copy-on-write rule literally (an append into a partial
+                              page another row still holds copies it first), so its
+                              high-water marks are not those of beams up to 32, whose
+                              pager appends in place to a partial page that only the
+                              source row also holds. */
   int32_t nbest;           /* hypotheses reported per row, 1..beam */
   int32_t vocab;           /* V >= 2, at most 16384.  Beams of 1..32 keep a ring of
                               frame rows (4V bytes each) and, paged, the page tables,
@@ -75,7 +80,8 @@ typedef struct {
                               reference-counted prefix sharing (sec. 3.4.5, 4.2) */
   int32_t page_size;       /* paged: tokens per page, a power of two in 4..64 (0 = 16) */
   int32_t num_pages;       /* paged: pages per row/stream (0 = beam * (ceil(cap /
-                              page_size) + 1), the bound of sec. 4.2), at most 32767.
+                              page_size) + 1), the bound of sec. 4.2), at most 32767
+                              for beams up to 32 (16-bit page ids on chip).
                               A smaller pool is allowed: a row that needs more pages
                               than it holds sets status bit 0 (ctcpb_row_stats [2]),
                               its outputs are then unspecified (all accesses stay in

@@ -68,7 +68,7 @@ def test_size_queries(L):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(beam=0), 1), (dict(beam=129), 1), (dict(beam=33, nbest=1, storage=1), 3),
+    (dict(beam=0), 1), (dict(beam=129), 1),
     (dict(nbest=0), 1), (dict(nbest=9), 1), (dict(vocab=1), 1), (dict(vocab=20000), 3),
     (dict(blank_id=-1), 1), (dict(blank_id=256), 1), (dict(max_out_len=-1), 1),
     (dict(storage=2), 1), (dict(storage=1, page_size=3), 1), (dict(storage=1, page_size=65), 1),
@@ -107,14 +107,15 @@ def test_decode_argument_errors_need_no_device(L):
                                   need, p, p, p, n) == 3
 
 
-def test_wide_beams_flat_only(L):
-    # beams of 33..128 run on the wide decoder (flat token lists), offline and
-    # streaming; its kept beam state makes a stream's region larger
+def test_wide_beams_flat_and_paged(L):
+    # beams of 33..128 run on the wide decoder (flat or paged tokens), offline
+    # and streaming; its kept beam state makes a stream's region larger
     assert ws(L, cfg(beam=128, nbest=128), 2, 100)[0] == 0
-    assert ws(L, cfg(beam=128, nbest=128, storage=1), 2, 100)[0] == 3
+    rc, paged = ws(L, cfg(beam=128, nbest=128, storage=1), 2, 100)
+    assert rc == 0 and paged > 0
     rc, wide = ss(L, cfg(beam=64, nbest=8), 4)
     assert rc == 0 and wide > ss(L, cfg(beam=32, nbest=8), 4)[1]
-    assert ss(L, cfg(beam=64, nbest=8, storage=1), 4)[0] == 3
+    assert ss(L, cfg(beam=64, nbest=8, storage=1), 4)[0] == 0
 
 
 def test_stream_argument_errors_need_no_device(L):
@@ -148,4 +149,4 @@ def test_python_wrapper_raises():
     with pytest.raises(ValueError):
         cpb.workspace_size(cpb.DecoderConfig(beam=0), 256, 2, 10)
     with pytest.raises(RuntimeError):
-        cpb.workspace_size(cpb.DecoderConfig(beam=40, paged=True), 256, 2, 10)
+        cpb.workspace_size(cpb.DecoderConfig(beam=8), 20000, 2, 10)

@@ -178,3 +178,77 @@ def test_wide_beams_per_frame_step():
             st.step_at(lp[s, t], int(idx[s, t]))
         outs.append(st.read(W, T))
     assert_parity(got, tuple(np.stack([o[i] for o in outs]) for i in range(3)), what="wide step")
+
+
+# ------------------------------------------------- paged storage, 33..128 --
+@pytest.mark.parametrize("W,ps", [(33, 4), (64, 16), (100, 8), (128, 64)])
+def test_wide_beams_paged_equals_oracle_and_flat(W, ps):
+    # pages of 4..64 tokens (page boundaries every few labels with 4), prefix
+    # sharing by reference counts and copy-on-write; ragged and empty rows
+    lp, _ = synth.peaky(4, 90, 250, seed=110 + W, p_blank=0.45)
+    lens = np.array([90, 0, 61, 1], np.int32)
+    print(f"[case] wide paged W={W} page_size={ps}", flush=True)
+    got = gpu_offline(lp, lens, W, W, 0, 1.0, 90, paged=True, page_size=ps)
+    high = gpu_offline.last_stats[:, 3]
+    assert_parity(got, oracle.decode(lp, lens, W, W, 0, 1.0, 90), what=f"wide paged W{W}")
+    flat = gpu_offline(lp, lens, W, W, 0, 1.0, 90)
+    assert all(np.array_equal(a, b) for a, b in zip(got, flat))
+    # pages in use at most: one per seeded slot after the first frame, and
+    # never more than the default pool, W (ceil(T / ps) + 1)
+    assert high[1] == 0 and 0 < high[0] <= W * ((90 + ps - 1) // ps + 1)
+
+
+def test_wide_beams_paged_skips_and_truncation():
+    lp, lens = synth.peaky(3, 80, 200, seed=120, p_blank=0.6)
+    print("[case] wide paged skips", flush=True)
+    got = gpu_offline(lp, lens, 72, 12, 0, 0.9, 7, paged=True, page_size=8)
+    assert_parity(got, oracle.decode(lp, lens, 72, 12, 0, 0.9, 7), what="wide paged skips")
+
+
+def test_wide_beams_paged_bounded_pool():
+    # a pool equal to a row's reported high-water mark decodes it exactly; one
+    # page less flags the row (status bit 0) and leaves the other rows as they were
+    lp, lens = synth.peaky(3, 70, 120, seed=121, p_blank=0.5)
+    W = 48
+    print("[case] wide paged bounded pool", flush=True)
+    full = gpu_offline(lp, lens, W, W, 0, 1.0, 70, paged=True, page_size=4)
+    high = gpu_offline.last_stats[:, 3].copy()
+    tight = int(high.max())
+    got = gpu_offline(lp, lens, W, W, 0, 1.0, 70, paged=True, page_size=4, num_pages=tight)
+    assert (gpu_offline.last_stats[:, 2] == 0).all()
+    assert all(np.array_equal(a, b) for a, b in zip(got, full))
+    short = gpu_offline(lp, lens, W, W, 0, 1.0, 70, paged=True, page_size=4,
+                        num_pages=tight - 1, check_status=False)
+    st = gpu_offline.last_stats
+    for r in range(3):
+        if high[r] > tight - 1:
+            assert st[r, 2] & 1, (r, high[r])
+        else:
+            assert st[r, 2] == 0
+            assert all(np.array_equal(a[r], b[r]) for a, b in zip(short, full))
+
+
+@pytest.mark.parametrize("W,cuts,ps", [(40, [0, 16, 32, 48, 64, 80], 4), (128, [0, 1, 30, 80], 16)])
+def test_wide_beams_paged_streaming(W, cuts, ps):
+    import torch
+    S, T, V = 4, 80, 200
+    lp, _ = synth.peaky(S, T, V, seed=130 + W, p_blank=0.55)
+    print(f"[case] wide paged stream W={W} ps={ps} cuts={cuts}", flush=True)
+    pool = cpb.StreamPool(cpb.DecoderConfig(beam=W, nbest=W, max_out_len=T, paged=True,
+                                            page_size=ps), V, S)
+    x = torch.from_numpy(lp).cuda()
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        pool.chunk(x[:, a:b])
+    got = pool_read(pool)
+    assert_parity(got, oracle_streams(lp, W, 4096, cuts, W, T), what=f"wide paged stream W{W}")
+    off = gpu_offline(lp, np.full(S, T, np.int32), W, W, 0, 1.0, T, paged=True, page_size=ps)
+    for g, o in zip(got, off):
+        assert np.array_equal(g, o)
+    # reset stream 2 and decode stream 0's frames in it again
+    two = torch.tensor([2], dtype=torch.int32, device="cuda")
+    pool.reset(two)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        pool.chunk(x[[0], a:b], rows=two)
+    t, l, s = pool.read(two)
+    assert np.array_equal(t.cpu().numpy()[0], got[0][0])
+    assert np.array_equal(s.cpu().numpy()[0], got[2][0])
