@@ -83,6 +83,15 @@ def lib():
         L.oracle_stream_step_count.argtypes = [p]
         L.oracle_stream_read.restype = None
         L.oracle_stream_read.argtypes = [p, i32, i32, p, p, p]
+        L.oracle_stream_new_paged.restype = p
+        L.oracle_stream_new_paged.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.oracle_stream_pages.restype = None
+        L.oracle_stream_pages.argtypes = [p, p]
+        L.oracle_decode_pages.restype = i32
+        L.oracle_decode_pages.argtypes = [p, i64, i64, i32, i32, p, i32, i32, i32, f32, i32,
+                                          i32, i32, p]
+        L.oracle_page_model_run.restype = i32
+        L.oracle_page_model_run.argtypes = [i32, i32, i32, i32, i32, i32, i32, p, p, p, p]
         _lib = L
     return _lib
 
@@ -160,17 +169,62 @@ def decode(log_prob: np.ndarray, seq_lengths, beam: int, nbest: int | None = Non
     return toks, lengths, scores
 
 
+def decode_pages(log_prob: np.ndarray, seq_lengths, beam: int, blank: int = 0,
+                 threshold: float = 1.0, space: int = -1, page_size: int = 16,
+                 num_pages: int = 0) -> np.ndarray:
+    """The paged variant's page accounting along offline decodes (the page's
+    allocator, sec. 3.4.5 / 4.2): int32 [B, 3] = most pages in use at once, 1
+    if a pop found nothing, the step of the first such pop (-1)."""
+    log_prob = np.ascontiguousarray(log_prob, dtype=np.float32)
+    B, T, V = log_prob.shape
+    lens = np.ascontiguousarray(seq_lengths, dtype=np.int32)
+    out = np.zeros((B, 3), np.int32)
+    rc = lib().oracle_decode_pages(_ptr(log_prob), T * V, V, B, T, _ptr(lens), beam, V, blank,
+                                   float(threshold), int(space), page_size, num_pages, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode_pages: invalid argument")
+    return out
+
+
+def page_model_run(beam: int, page_size: int, cap: int, nseed: int, src, lab, blank: int = 0,
+                   num_pages: int = 0):
+    """The page model alone on given winners: src / lab [nsteps][beam] for
+    steps 1..nsteps (source slot, -1 dead; label).  Returns (pages in use
+    after each step [nsteps + 1], (high, failed, first failing step))."""
+    src = np.ascontiguousarray(src, dtype=np.int32).reshape(-1, beam)
+    lab = np.ascontiguousarray(lab, dtype=np.int32).reshape(-1, beam)
+    n = src.shape[0]
+    used = np.zeros(n + 1, np.int32)
+    out = np.zeros(3, np.int32)
+    rc = lib().oracle_page_model_run(beam, page_size, num_pages, cap, blank, nseed, n,
+                                     _ptr(src), _ptr(lab), _ptr(used), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_page_model_run: invalid argument")
+    return used, tuple(int(v) for v in out)
+
+
 class Stream:
     """One streaming decode: frames fed in chunks, optionally gated by a
     speech mask (0 = skip the frame) and numbered from a caller-given frame
-    index."""
+    index.  With page_size, it also counts pages as the paged variant's
+    allocator would (pages())."""
 
     def __init__(self, beam: int, vocab: int, blank: int = 0, capacity: int = 4096,
-                 space: int = -1):
+                 space: int = -1, page_size: int | None = None, num_pages: int = 0):
         self.beam, self.vocab = beam, vocab
-        self._h = lib().oracle_stream_new_sp(beam, vocab, blank, capacity, space)
+        if page_size is None:
+            self._h = lib().oracle_stream_new_sp(beam, vocab, blank, capacity, space)
+        else:
+            self._h = lib().oracle_stream_new_paged(beam, vocab, blank, capacity, space,
+                                                    page_size, num_pages)
         if not self._h:
             raise ValueError("oracle_stream_new: invalid argument")
+
+    def pages(self):
+        """(most pages in use at once, 1 if a pop found nothing, first such step)."""
+        out = np.zeros(3, np.int32)
+        lib().oracle_stream_pages(self._h, _ptr(out))
+        return tuple(int(v) for v in out)
 
     def feed(self, frames: np.ndarray, is_speech=None, start_frame: int | None = None) -> int:
         """Chunk frame f is frame number start + f (start = start_frame, or the

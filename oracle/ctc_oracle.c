@@ -50,6 +50,21 @@
  *     in the space label therefore has no non-blank stay term (NEG).  The
  *     result is prefix search under the collapse in which every space frame
  *     emits a new space token.
+ *   - Paged variant, page accounting (sec. 3.4.5 paged variant, sec. 4.2):
+ *     an optional model that follows the page's allocator along the decode
+ *     and counts pages; tokens stay in the flat lists.  Per step, pass 1
+ *     forks every new row onto its source's pages and releases the pages it
+ *     held, a page being freed when no row refers to it any more (the page's
+ *     per-entry release and acquire, read as never freeing a page a new row
+ *     takes); pass 2 appends each new label in ascending slot order: a label
+ *     that starts a page pops a page, one that goes into a partial page whose
+ *     reference count is above 1 pops a page for the copy and drops one
+ *     reference from the shared page, otherwise it writes in place.  Pops
+ *     take the LIFO stack of freed pages first, then the bump pointer, and
+ *     give nothing past the row's pool: the beam then keeps its prefix
+ *     without appending (sec. 4.2), which the model records.  After the
+ *     first such pop the decode's tokens are no longer the page's (the
+ *     token lists here always append), so only counts up to it are compared.
  */
 #include <float.h>
 #include <math.h>
@@ -186,7 +201,173 @@ struct OracleStream {
     float *ptable, *ptablen; /* [beam][vocab] */
     int64_t *order;          /* candidate ids for the sort */
     const float *sort_keys;  /* keys the comparator reads */
+    struct PageModel *pages; /* optional page accounting (NULL: none) */
 };
+
+/* ---------------------------------------------------------------------- */
+/* Page accounting of the paged variant (sec. 3.4.5 paged variant, 4.2).    */
+/* ---------------------------------------------------------------------- */
+
+typedef struct PageModel {
+    int beam, ps, npages, max_lp;
+    int *tab[2];  /* [beam][max_lp] page ids of the two table parities, -1 none */
+    int *held[2]; /* [beam] pages a row holds: the leading entries of its row */
+    int *ref;     /* [npages] rows referring to each page */
+    int *stack;   /* [npages] freed pages, LIFO */
+    int top, next_free;
+    int high;        /* most pages in use at once (handed out, not freed) */
+    int failed;      /* a pop found nothing */
+    int failed_step; /* step of the first such pop, -1 */
+} PageModel;
+
+static void pm_reset(PageModel *m)
+{
+    for (int i = 0; i < 2 * m->beam * m->max_lp; i++) {
+        m->tab[0][i] = -1;
+    }
+    for (int k = 0; k < m->beam; k++) m->held[0][k] = m->held[1][k] = 0;
+    for (int i = 0; i < m->npages; i++) m->ref[i] = 0;
+    m->top = m->next_free = m->high = m->failed = 0;
+    m->failed_step = -1;
+}
+
+static PageModel *pm_new(int beam, int ps, int npages, int cap)
+{
+    PageModel *m = (PageModel *)calloc(1, sizeof(PageModel));
+    m->beam = beam;
+    m->ps = ps;
+    m->max_lp = (cap + ps - 1) / ps + 1;
+    /* sec. 4.2: the default pool is beam * (max_logical_pages + 1) per row */
+    m->npages = npages > 0 ? npages : beam * ((cap + ps - 1) / ps + 1);
+    m->tab[0] = (int *)malloc(sizeof(int) * (size_t)(2 * beam * m->max_lp));
+    m->tab[1] = m->tab[0] + beam * m->max_lp;
+    m->held[0] = (int *)malloc(sizeof(int) * (size_t)(2 * beam));
+    m->held[1] = m->held[0] + beam;
+    m->ref = (int *)malloc(sizeof(int) * (size_t)(m->npages > 0 ? m->npages : 1));
+    m->stack = (int *)malloc(sizeof(int) * (size_t)(m->npages > 0 ? m->npages : 1));
+    pm_reset(m);
+    return m;
+}
+
+static void pm_free(PageModel *m)
+{
+    if (!m) return;
+    free(m->tab[0]);
+    free(m->held[0]);
+    free(m->ref);
+    free(m->stack);
+    free(m);
+}
+
+/* alloc_page: the stack of freed pages first (LIFO), then the bump pointer;
+ * -1 past the row's pool */
+static int pm_pop(PageModel *m)
+{
+    if (m->top > 0) return m->stack[--m->top];
+    if (m->next_free < m->npages) return m->next_free++;
+    return -1;
+}
+
+static void pm_fail(PageModel *m, int step)
+{
+    if (!m->failed) m->failed_step = step;
+    m->failed = 1;
+}
+
+static void pm_note_use(PageModel *m)
+{
+    int used = m->next_free - m->top;
+    if (used > m->high) m->high = used;
+}
+
+/* Step 0 (sec. 3.3): each of the first nseed slots holds one label, on a page
+ * of its own, taken in slot order; the table of parity 0 is written. */
+static void pm_seed(PageModel *m, int nseed)
+{
+    for (int r = 0; r < nseed && r < m->beam; r++) {
+        int pg = pm_pop(m);
+        if (pg < 0) {
+            pm_fail(m, 0);
+            continue;
+        }
+        m->ref[pg] = 1;
+        m->tab[0][r * m->max_lp] = pg;
+        m->held[0][r] = 1;
+    }
+    pm_note_use(m);
+}
+
+/* Step s >= 1: new row r (table parity s & 1) continues row src[r] of the
+ * other parity (-1: a dead slot) whose hypothesis had srclen[r] labels, and
+ * appends lab[r] unless it is the blank. */
+static void pm_step(PageModel *m, int step, const int *src, const int *lab, const int *srclen,
+                    int blank)
+{
+    const int W = m->beam, L = m->max_lp, p = step & 1, q = p ^ 1;
+    int *newtab = (int *)malloc(sizeof(int) * (size_t)(W * L));
+    int *newheld = (int *)malloc(sizeof(int) * (size_t)W);
+    /* pass 1, fork: the new rows refer to their sources' pages ... */
+    for (int r = 0; r < W; r++) {
+        int k = src[r];
+        newheld[r] = k >= 0 ? m->held[q][k] : 0;
+        for (int j = 0; j < newheld[r]; j++) {
+            newtab[r * L + j] = m->tab[q][k * L + j];
+            m->ref[newtab[r * L + j]]++;
+        }
+    }
+    /* ... and the pages the replaced rows held are released; one that no row
+     * refers to any more goes on the stack */
+    for (int r = 0; r < W; r++) {
+        for (int j = 0; j < m->held[p][r]; j++) {
+            int e = m->tab[p][r * L + j];
+            if (--m->ref[e] == 0) m->stack[m->top++] = e;
+        }
+        for (int j = 0; j < L; j++) m->tab[p][r * L + j] = j < newheld[r] ? newtab[r * L + j] : -1;
+        m->held[p][r] = newheld[r];
+    }
+    /* pass 2, append / copy-on-write, in ascending slot order */
+    for (int r = 0; r < W; r++) {
+        if (src[r] < 0 || lab[r] == blank) continue;
+        int len = srclen[r], pi = len / m->ps, off = len % m->ps;
+        int *row = m->tab[p] + r * L;
+        if (off == 0) {
+            /* the label starts a page */
+            if (m->held[p][r] != pi) {
+                pm_fail(m, step); /* a row already short of pages */
+                continue;
+            }
+            int pg = pm_pop(m);
+            if (pg < 0) {
+                pm_fail(m, step);
+                continue;
+            }
+            m->ref[pg] = 1;
+            row[pi] = pg;
+            m->held[p][r] = pi + 1;
+        } else {
+            if (m->held[p][r] != pi + 1) {
+                pm_fail(m, step);
+                continue;
+            }
+            int shared = row[pi];
+            if (m->ref[shared] > 1) {
+                /* shared with another row: copy it to a page of its own */
+                int pg = pm_pop(m);
+                if (pg < 0) {
+                    pm_fail(m, step);
+                    continue;
+                }
+                m->ref[pg] = 1;
+                m->ref[shared]--; /* > 1 before: it never reaches 0 here */
+                row[pi] = pg;
+            }
+            /* otherwise the row holds the page alone and writes in place */
+        }
+    }
+    pm_note_use(m);
+    free(newtab);
+    free(newheld);
+}
 
 static int slot_clast(const Slot *s, int blank)
 {
@@ -232,6 +413,7 @@ static void reset_empty(OracleStream *st)
     st->step = 0;
     st->last_t = -1;
     st->frames = 0;
+    if (st->pages) pm_reset(st->pages);
 }
 
 OracleStream *oracle_stream_new_sp(int beam, int vocab, int blank, int capacity, int space)
@@ -263,6 +445,23 @@ OracleStream *oracle_stream_new(int beam, int vocab, int blank, int capacity)
     return oracle_stream_new_sp(beam, vocab, blank, capacity, -1);
 }
 
+OracleStream *oracle_stream_new_paged(int beam, int vocab, int blank, int capacity, int space,
+                                      int page_size, int num_pages)
+{
+    if (page_size < 1 || num_pages < 0) return NULL;
+    OracleStream *st = oracle_stream_new_sp(beam, vocab, blank, capacity, space);
+    if (st) st->pages = pm_new(beam, page_size, num_pages, capacity);
+    return st;
+}
+
+void oracle_stream_pages(const OracleStream *st, int *out)
+{
+    const PageModel *m = st->pages;
+    out[0] = m ? m->high : 0;
+    out[1] = m ? m->failed : 0;
+    out[2] = m ? m->failed_step : -1;
+}
+
 void oracle_stream_free(OracleStream *st)
 {
     if (!st) return;
@@ -275,6 +474,7 @@ void oracle_stream_free(OracleStream *st)
     free(st->ptable);
     free(st->ptablen);
     free(st->order);
+    pm_free(st->pages);
     free(st);
 }
 
@@ -327,6 +527,7 @@ static void first_step(OracleStream *st, const float *lp, int t)
         s->pnb = NEG;
         s->score = lp[blank];
     }
+    if (st->pages) pm_seed(st->pages, m);
     free(chars);
 }
 
@@ -416,8 +617,19 @@ static void next_step(OracleStream *st, const float *lp, int need_add_blank)
 
     /* sec. 3.4.5: state update from the snapshot of the source beams. */
     int nw = (n < W) ? (int)n : W;
+    int *psrc = NULL, *plab = NULL, *plen = NULL;   /* the page model's view */
+    if (st->pages) {
+        psrc = (int *)malloc(sizeof(int) * (size_t)(3 * W));
+        plab = psrc + W;
+        plen = plab + W;
+    }
     for (int r = 0; r < W; r++) {
         Slot *d = &st->nxt[r];
+        if (psrc) {
+            psrc[r] = -1;
+            plab[r] = blank;
+            plen[r] = 0;
+        }
         if (r >= nw) {
             d->live = 0;
             d->len = 0;
@@ -427,6 +639,11 @@ static void next_step(OracleStream *st, const float *lp, int need_add_blank)
         int64_t id = st->order[r];
         int k = (int)(id / V), c = (int)(id % V);
         const Slot *s = &st->cur[k];
+        if (psrc) {
+            psrc[r] = k;
+            plab[r] = c;
+            plen[r] = s->len;
+        }
         d->live = 1;
         memcpy(d->tok, s->tok, sizeof(int) * (size_t)s->len);
         d->len = s->len;
@@ -442,6 +659,10 @@ static void next_step(OracleStream *st, const float *lp, int need_add_blank)
         }
     }
     free(keys);
+    if (psrc) {
+        pm_step(st->pages, st->step, psrc, plab, plen, blank);
+        free(psrc);
+    }
     Slot *tmp = st->cur;
     st->cur = st->nxt;
     st->nxt = tmp;
@@ -561,6 +782,71 @@ int oracle_decode_sp(const float *log_prob, int64_t stride_b, int64_t stride_t, 
         oracle_stream_free(st);
     }
     free(sel);
+    return 0;
+}
+
+/* Page accounting along offline decodes (sec. 3.4.5 paged variant, 4.2):
+ * per row out[3b] the most pages in use at once, out[3b+1] 1 if a pop found
+ * nothing, out[3b+2] the step of the first such pop (-1).  The pool is
+ * num_pages, or beam * (ceil(max_T / page_size) + 1) for 0. */
+int oracle_decode_pages(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                        int max_T, const int *seq_lengths, int beam, int vocab, int blank,
+                        float threshold, int space, int page_size, int num_pages, int *out)
+{
+    if (beam < 1 || vocab < 2 || blank < 0 || blank >= vocab || batch < 0 || max_T < 0 ||
+        space >= vocab || page_size < 1 || num_pages < 0)
+        return 1;
+    int *sel = (int *)malloc(sizeof(int) * (size_t)(max_T > 0 ? max_T : 1));
+    const int pool = num_pages > 0 ? num_pages : beam * ((max_T + page_size - 1) / page_size + 1);
+    for (int b = 0; b < batch; b++) {
+        int len = seq_lengths[b];
+        if (len < 0) len = 0;
+        if (len > max_T) len = max_T;
+        const float *row = log_prob + (int64_t)b * stride_b;
+        int n = oracle_select_frames(row, stride_t, len, blank, threshold, sel);
+        OracleStream *st =
+            oracle_stream_new_paged(beam, vocab, blank, max_T, space, page_size, pool);
+        for (int s = 0; s < n; s++)
+            decode_frame(st, row + (int64_t)sel[s] * stride_t, sel[s]);
+        oracle_stream_pages(st, out + 3 * b);
+        oracle_stream_free(st);
+    }
+    free(sel);
+    return 0;
+}
+
+/* The page model alone, on given winners (hand-worked cases): nseed seeded
+ * slots at step 0, then for steps 1..nsteps the source slot (-1 dead) and the
+ * label of every slot, src/lab[(s - 1) * beam + r].  Writes the pages in use
+ * after every step to used[0..nsteps] and the summary to out[3] as above. */
+int oracle_page_model_run(int beam, int page_size, int num_pages, int cap, int blank, int nseed,
+                          int nsteps, const int *src, const int *lab, int *used, int *out)
+{
+    if (beam < 1 || page_size < 1 || num_pages < 0 || cap < 1 || nsteps < 0) return 1;
+    PageModel *m = pm_new(beam, page_size, num_pages, cap);
+    int *len = (int *)calloc((size_t)beam, sizeof(int));
+    int *nlen = (int *)calloc((size_t)beam, sizeof(int));
+    int *srclen = (int *)calloc((size_t)beam, sizeof(int));
+    for (int r = 0; r < nseed && r < beam; r++) len[r] = 1;
+    pm_seed(m, nseed);
+    used[0] = m->next_free - m->top;
+    for (int s = 1; s <= nsteps; s++) {
+        const int *sr = src + (size_t)(s - 1) * beam, *lb = lab + (size_t)(s - 1) * beam;
+        for (int r = 0; r < beam; r++) {
+            srclen[r] = sr[r] >= 0 ? len[sr[r]] : 0;
+            nlen[r] = sr[r] >= 0 ? srclen[r] + (lb[r] != blank) : 0;
+        }
+        pm_step(m, s, sr, lb, srclen, blank);
+        memcpy(len, nlen, sizeof(int) * (size_t)beam);
+        used[s] = m->next_free - m->top;
+    }
+    out[0] = m->high;
+    out[1] = m->failed;
+    out[2] = m->failed_step;
+    free(len);
+    free(nlen);
+    free(srclen);
+    pm_free(m);
     return 0;
 }
 

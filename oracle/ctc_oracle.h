@@ -50,6 +50,19 @@ int oracle_stream_feed(OracleStream *st, const float *frames, int64_t stride_t, 
 int oracle_stream_feed_ex(OracleStream *st, const float *frames, int64_t stride_t, int n_frames,
                           const unsigned char *is_speech, int start_frame);
 int oracle_stream_frame_count(const OracleStream *st);
+
+/* Page accounting of the paged variant (see ctc_oracle.c): a stream that
+ * counts pages as the page's allocator hands them out; out[0] most pages in
+ * use at once, out[1] 1 if a pop found nothing, out[2] the step of the first
+ * such pop (-1).  num_pages 0: the default pool. */
+OracleStream *oracle_stream_new_paged(int beam, int vocab, int blank, int capacity, int space,
+                                      int page_size, int num_pages);
+void oracle_stream_pages(const OracleStream *st, int *out);
+int oracle_decode_pages(const float *log_prob, int64_t stride_b, int64_t stride_t, int batch,
+                        int max_T, const int *seq_lengths, int beam, int vocab, int blank,
+                        float threshold, int space, int page_size, int num_pages, int *out);
+int oracle_page_model_run(int beam, int page_size, int num_pages, int cap, int blank, int nseed,
+                          int nsteps, const int *src, const int *lab, int *used, int *out);
 int oracle_stream_step_count(const OracleStream *st);
 void oracle_stream_read(const OracleStream *st, int nbest, int max_out_len, int *out_tokens,
                         int *out_lengths, float *out_scores);

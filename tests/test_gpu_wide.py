@@ -193,8 +193,10 @@ def test_wide_beams_paged_equals_oracle_and_flat(W, ps):
     assert_parity(got, oracle.decode(lp, lens, W, W, 0, 1.0, 90), what=f"wide paged W{W}")
     flat = gpu_offline(lp, lens, W, W, 0, 1.0, 90)
     assert all(np.array_equal(a, b) for a, b in zip(got, flat))
-    # pages in use at most: one per seeded slot after the first frame, and
-    # never more than the default pool, W (ceil(T / ps) + 1)
+    # pages in use at most: the page's allocator as the oracle models it
+    # (sec. 3.4.5 / 4.2), never more than the default pool W (ceil(T / ps) + 1)
+    model = oracle.decode_pages(lp, lens, W, page_size=ps)
+    assert list(high) == list(model[:, 0]) and (model[:, 1] == 0).all()
     assert high[1] == 0 and 0 < high[0] <= W * ((90 + ps - 1) // ps + 1)
 
 
@@ -220,6 +222,11 @@ def test_wide_beams_paged_bounded_pool():
     short = gpu_offline(lp, lens, W, W, 0, 1.0, 70, paged=True, page_size=4,
                         num_pages=tight - 1, check_status=False)
     st = gpu_offline.last_stats
+    # the oracle's model of the page's allocator: same high-water marks, and
+    # the same rows run dry in the smaller pool
+    assert list(high) == list(oracle.decode_pages(lp, lens, W, page_size=4)[:, 0])
+    dry = oracle.decode_pages(lp, lens, W, page_size=4, num_pages=tight - 1)[:, 1]
+    assert list(st[:, 2] & 1) == list(dry)
     for r in range(3):
         if high[r] > tight - 1:
             assert st[r, 2] & 1, (r, high[r])
@@ -241,6 +248,13 @@ def test_wide_beams_paged_streaming(W, cuts, ps):
         pool.chunk(x[:, a:b])
     got = pool_read(pool)
     assert_parity(got, oracle_streams(lp, W, 4096, cuts, W, T), what=f"wide paged stream W{W}")
+    # pages in use at most, against the oracle's model along the same chunks
+    high = pool.row_stats().cpu().numpy()[:, 3]
+    for s_ in range(S):
+        st = oracle.Stream(W, V, 0, 4096, page_size=ps)
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            st.feed(lp[s_, a:b])
+        assert st.pages()[0] == high[s_] and st.pages()[1] == 0
     off = gpu_offline(lp, np.full(S, T, np.int32), W, W, 0, 1.0, T, paged=True, page_size=ps)
     for g, o in zip(got, off):
         assert np.array_equal(g, o)

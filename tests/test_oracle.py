@@ -560,3 +560,48 @@ def test_space_slot_golden(oracle_lib):
     st.feed(lp)
     t2, l2, s2 = st.read(g["nbest"], T)
     assert (t2 == toks[0]).all() and (l2 == L[0]).all() and (s2 == S[0]).all()
+
+
+# ------------------------------------------------- paged page accounting --
+def test_page_model_hand_worked(oracle_lib):
+    # sec. 3.4.5 / 4.2 allocator on hand-chosen winners (tests/golden/page_model.json)
+    oracle = oracle_lib
+    g = json.load(open(os.path.join(GOLDEN, "page_model.json")))
+    used, summary = oracle.page_model_run(g["beam"], g["page_size"], g["cap"], g["nseed"],
+                                          g["src"], g["lab"], g["blank"])
+    assert list(used) == g["used"]
+    assert list(summary) == g["summary"]
+    for pool in (4, 3):
+        _, s = oracle.page_model_run(g["beam"], g["page_size"], g["cap"], g["nseed"], g["src"],
+                                     g["lab"], g["blank"], num_pages=pool)
+        assert list(s) == g[f"pool_{pool}"], pool
+
+
+@pytest.mark.parametrize("W,ps", [(4, 4), (10, 16), (33, 8)])
+def test_page_model_bounds_and_exact_pool(oracle_lib, W, ps):
+    # the page's sizing claim (sec. 4.2): a row never needs more than
+    # beam * (ceil(T / page_size) + 1) pages; pops take freed pages before the
+    # bump pointer, so a pool of exactly the high-water mark never runs dry
+    # and one page less does
+    oracle = oracle_lib
+    lp, lens = synth.peaky(4, 60, 30, seed=140 + W, p_blank=0.4)
+    st = oracle.decode_pages(lp, lens, W, page_size=ps)
+    bound = W * (-(-60 // ps) + 1)
+    assert (st[:, 0] <= bound).all() and (st[:, 1] == 0).all() and (st[:, 0] > 0).all()
+    for b in range(4):
+        h = int(st[b, 0])
+        ok = oracle.decode_pages(lp[b:b + 1], lens[b:b + 1], W, page_size=ps, num_pages=h)
+        short = oracle.decode_pages(lp[b:b + 1], lens[b:b + 1], W, page_size=ps, num_pages=h - 1)
+        assert ok[0, 1] == 0 and ok[0, 0] == h
+        assert short[0, 1] == 1 and short[0, 2] >= 0
+
+
+def test_page_model_stream_equals_offline(oracle_lib):
+    # the accounting along a stream fed in chunks is that of the offline decode
+    oracle = oracle_lib
+    lp, lens = synth.peaky(1, 50, 20, seed=150, p_blank=0.5)
+    st = oracle.Stream(12, 20, 0, capacity=50, page_size=4)
+    for a in range(0, 50, 7):
+        st.feed(lp[0, a:a + 7])
+    off = oracle.decode_pages(lp, lens, 12, page_size=4)
+    assert st.pages() == tuple(int(v) for v in off[0])
