@@ -1507,10 +1507,27 @@ __device__ __forceinline__ void store_paged(Ctx& C, StoreState& ss, int step, co
   lds_order();
   SP_MARK(1);
 
-  // pass 2: append.  With only the source's row of the previous step and this
-  // row referencing the partial page, the label is written in place: the
-  // source's row ends before it (and is not read again).
-  const bool inplace = phys >= 0 && C.ref[phys] <= 2;
+  // pass 2: append.  A label that goes into a partial page:
+  //  - with a pool the caller sized (num_pages > 0), exactly as the page's
+  //    allocator in ascending slot order (sec. 3.4.5), so that a pool runs
+  //    out where the page's would: in place only if no other row holds the
+  //    page (its reference count, less the earlier slots that copy it away
+  //    first, is 1), else the page is copied.  The source's row of the
+  //    previous step always holds its last page, so in practice every such
+  //    label copies;
+  //  - with the default pool, which cannot run out (sec. 4.2), in place also
+  //    when only the source's row and this row hold it: the source's row ends
+  //    before the label and is released at the next step, so no row can see
+  //    the difference, and the copies and their pages are saved.
+  const bool strict = L.paged == 2;
+  int before = 0;
+  if (strict) {
+    for (uint64_t m = __ballot(phys >= 0); m != 0ull; m &= m - 1ull) {
+      const int j = __ffsll((long long)m) - 1;
+      before += (j < lane && __builtin_amdgcn_readlane(phys, j) == phys) ? 1 : 0;
+    }
+  }
+  const bool inplace = phys >= 0 && C.ref[phys] - before <= (strict ? 1 : 2);
   const bool need = ext && !inplace;
   const uint64_t mk = __ballot(need);
   const int idx = lanes_below(mk);

@@ -64,7 +64,8 @@ struct Layout {
   int space;      // label of the space slot, -1 none (not part of the sizes)
   int cap;        // token (and frame) capacity of a row
   int ldc;        // flat: row stride of clist (cap rounded up to 4)
-  int paged;      // 0 flat, 1 paged
+  int paged;      // 0 flat; paged: 1 the default pool, 2 a pool the caller sized
+                  // (appends follow the page's copy-on-write rule exactly, see store_paged)
   int ps;         // page size (a power of two)
   int ps_log2;    // log2(page size)
   int max_lp;     // pages per block-table row
@@ -93,7 +94,7 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   L.space = -1;
   L.cap = cap;
   L.ldc = (cap + 3) & ~3;
-  L.paged = paged;
+  L.paged = paged ? (npages_cfg > 0 ? 2 : 1) : 0;
   L.ps = paged ? ps : 0;
   L.ps_log2 = 0;
   while (paged && (1 << L.ps_log2) < ps) L.ps_log2++;

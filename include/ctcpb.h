@@ -49,12 +49,8 @@ enum { CTCPB_STORAGE_FLAT = 0, CTCPB_STORAGE_PAGED = 1 };
 typedef struct {
   int32_t beam;            /* beam width W, 1..128 (sec. 10); beams above 32 (the page's
                               multi-kernel path) run on a separate decoder, offline and
-                              streaming, flat or paged.  Its pager follows the page's
-                              copy-on-write rule literally (an append into a partial
-                              page another row still holds copies it first), so its
-                              high-water marks are not those of beams up to 32, whose
-                              pager appends in place to a partial page that only the
-                              source row also holds. */
+                              streaming, flat or paged (whose pager always follows
+                              the page's copy-on-write rule, see num_pages). */
   int32_t nbest;           /* hypotheses reported per row, 1..beam */
   int32_t vocab;           /* V >= 2, at most 16384.  Beams of 1..32 keep a ring of
                               frame rows (4V bytes each) and, paged, the page tables,
@@ -82,12 +78,22 @@ typedef struct {
   int32_t num_pages;       /* paged: pages per row/stream (0 = beam * (ceil(cap /
                               page_size) + 1), the bound of sec. 4.2), at most 32767
                               for beams up to 32 (16-bit page ids on chip).
-                              A smaller pool is allowed: a row that needs more pages
-                              than it holds sets status bit 0 (ctcpb_row_stats [2]),
-                              its outputs are then unspecified (all accesses stay in
-                              its own pool) and the other rows are unaffected.  The
-                              high-water mark (ctcpb_row_stats [3]) of a decode is
-                              the pool that decodes that row exactly. */
+                              A pool given here (> 0) is handed out exactly as the
+                              page's allocator does (sec. 3.4.5 fork, then appends
+                              in ascending slot order with copy-on-write of a page
+                              another row holds; sec. 4.2 freed pages first, then
+                              the bump pointer), so it runs out where the page's
+                              would.  A row that runs out sets status bit 0
+                              (ctcpb_row_stats [2]); the beam keeps its prefix
+                              without the label, the row's outputs are then
+                              unspecified (all accesses stay in its own pool) and
+                              the other rows are unaffected.  With such a pool, the
+                              high-water mark (ctcpb_row_stats [3]) is the smallest
+                              pool that decodes the row.  The default pool (0)
+                              cannot run out; beams up to 32 then also append in
+                              place to a partial page that only the source row of
+                              the previous step holds (same outputs, fewer pages
+                              and copies), so its marks are lower. */
   int32_t space_id;        /* the space label of the optional space slot (sec. 3.4.1,
                               3.4.2), or -1 for none (the page's default); the blank
                               label also means none.  With a space label, every beam's

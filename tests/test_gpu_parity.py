@@ -180,10 +180,21 @@ def test_bounded_page_pool():
     lp, lens = synth.peaky(6, 240, 300, seed=98, p_blank=0.4)
     lens[:] = [240, 200, 160, 120, 80, 40]
     print("[case] bounded pool B=6 T=240 V=300 W=16 ps=8", flush=True)
-    full = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8)
+    # a pool the caller sizes (here the default's size, given explicitly)
+    # follows the page's allocator exactly; the default pool appends in place
+    # where only the source row also holds the page, which needs fewer pages
+    loose = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8)
+    loose_high = gpu_offline.last_stats[:, 3].copy()
+    full = gpu_offline(lp, lens, 16, 16, 0, 1.0, 240, paged=True, page_size=8,
+                       num_pages=16 * (240 // 8 + 1))
     high = gpu_offline.last_stats[:, 3].copy()
+    assert (loose_high <= high).all()
+    assert all(np.array_equal(a, b) for a, b in zip(loose, full))
     assert (gpu_offline.last_stats[:, 2] == 0).all()
     assert_parity(full, oracle.decode(lp, lens, 16, 16, 0, 1.0, 240), what="bounded pool")
+    # the marks are those of the page's allocator as the oracle models it
+    # (sec. 3.4.5 fork / copy-on-write, sec. 4.2 alloc_page)
+    assert list(high) == list(oracle.decode_pages(lp, lens, 16, page_size=8)[:, 0])
     assert high.min() < high.max()
     npages = int(np.median(high))
     fits = high <= npages
@@ -192,6 +203,8 @@ def test_bounded_page_pool():
                       check_status=False)
     st = gpu_offline.last_stats
     assert np.array_equal(st[:, 2] & 1, (~fits).astype(st.dtype))
+    dry = oracle.decode_pages(lp, lens, 16, page_size=8, num_pages=npages)[:, 1]
+    assert np.array_equal(st[:, 2] & 1, dry.astype(st.dtype))
     for b in np.nonzero(fits)[0]:
         for a, e in zip(got, full):
             assert np.array_equal(a[b], e[b])
@@ -202,6 +215,26 @@ def test_bounded_page_pool():
     assert np.array_equal(gpu_offline.last_stats[:, 3], high)
     for a, e in zip(got, full):
         assert np.array_equal(a, e)
+
+
+@pytest.mark.parametrize("W,ps,theta", [(4, 4, 1.0), (10, 16, 0.9), (32, 64, 1.0), (32, 4, 0.95)])
+def test_page_counts_equal_the_page_allocator(W, ps, theta):
+    # pages in use at most per row (paged storage, beams up to 32) against the
+    # oracle's model of the page's allocator, and the same rows running dry in
+    # a pool one page short of the largest mark
+    lp, lens = synth.peaky(4, 150, 200, seed=160 + W + ps, p_blank=0.5, lengths=(40, 150))
+    print(f"[case] page counts W={W} ps={ps} theta={theta}", flush=True)
+    got = gpu_offline(lp, lens, W, W, 0, theta, 150, paged=True, page_size=ps,
+                      num_pages=W * (-(-150 // ps) + 1))
+    high = gpu_offline.last_stats[:, 3].copy()
+    model = oracle.decode_pages(lp, lens, W, threshold=theta, page_size=ps)
+    assert list(high) == list(model[:, 0])
+    assert_parity(got, oracle.decode(lp, lens, W, W, 0, theta, 150), what="page counts")
+    n = int(high.max()) - 1
+    gpu_offline(lp, lens, W, W, 0, theta, 150, paged=True, page_size=ps, num_pages=n,
+                check_status=False)
+    dry = oracle.decode_pages(lp, lens, W, threshold=theta, page_size=ps, num_pages=n)[:, 1]
+    assert list(gpu_offline.last_stats[:, 2] & 1) == list(dry) and dry.any()
 
 
 def test_exact_selection_every_step_at_vocab5000():

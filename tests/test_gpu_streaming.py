@@ -297,10 +297,17 @@ def test_bounded_page_pool_streams():
         st = pool.row_stats().cpu().numpy()
         return pool, (t.cpu().numpy(), l.cpu().numpy(), s.cpu().numpy()), st
 
-    _, full, st = run(0)
+    # the pool sized explicitly (the default's size) follows the page's
+    # allocator, whose marks are the pools that decode each stream exactly
+    _, full, st = run(W * (-(-T // 8) + 1))
     assert (st[:, 2] == 0).all()
     assert_parity(full, oracle_streams(lp, W, T, CH, W, T), what="stream pool")
     high = st[:, 3].copy()
+    for s_ in range(S):
+        ost = oracle.Stream(W, V, 0, T, page_size=8)
+        for a in range(0, T, CH):
+            ost.feed(lp[s_, a:a + CH])
+        assert ost.pages()[0] == high[s_]
     npages = int(np.median(high))
     fits = high <= npages
     assert fits.any() and (~fits).any(), high
