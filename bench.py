@@ -349,14 +349,28 @@ def main():
     if paged:
         # token storage per row (f32-sized tokens): the two flat lists of every
         # slot at full capacity, the default page pool (the bound that cannot
-        # run out) and the pool this decode's busiest row actually needed
+        # run out), the pages this decode's busiest row held at most with the
+        # default pool (in-place appends where only the source row also holds
+        # the page), and the pool the page's allocator needs on the same decode
+        # (a pool given explicitly, of the default's size, follows it exactly;
+        # that mark is the smallest pool that decodes the row)
         ps = cfg.page_size or 16
         flat_b = 2 * wl.beam * wl.T * 4
-        pool_b = wl.beam * (-(-wl.T // ps) + 1) * ps * 4
+        npool = wl.beam * (-(-wl.T // ps) + 1)
+        pool_b = npool * ps * 4
         high_b = pages_high * ps * 4
+        exact = cpb.OfflineDecoder(cpb.DecoderConfig(
+            beam=wl.beam, nbest=wl.nbest, blank_threshold=wl.threshold,
+            max_out_len=wl.max_out_len, paged=True, num_pages=npool))
+        exact.decode(x, lens_d)
+        rule_high = int(exact.row_stats().cpu().numpy()[:, 3].max())
+        del exact
+        rule_b = rule_high * ps * 4
         result["decode"]["token_store_bytes_per_row"] = {
             "flat_lists": flat_b, "paged_default_pool": pool_b, "paged_high_water": high_b,
-            "flat_over_high_water": round(flat_b / max(high_b, 1), 2)}
+            "flat_over_high_water": round(flat_b / max(high_b, 1), 2),
+            "paged_high_water_page_allocator": rule_b,
+            "flat_over_page_allocator": round(flat_b / max(rule_b, 1), 2)}
     if args.with_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
         a.fill_(1.0)
