@@ -2532,7 +2532,10 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
 // up to three frame slots beyond one per producer so that the loader can run
 // ahead (a slot is held from its load until the beam wave has used it).
 LdsPlan plan_lds(const Layout& L) {
-  const int pref = L.V >= 3000 ? 4 : (L.V >= 1000 ? 3 : 2);
+  // four producer waves whenever they fit: ranking costs about the same per
+  // frame at any vocabulary (its threshold search and sort are fixed work),
+  // so small vocabularies need as many producers as large ones
+  const int pref = 4;
   // flat token lists in LDS if they fit next to at least one producer
   for (int lds_clist = 1; lds_clist >= 0; lds_clist--) {
     if (lds_clist && L.paged) continue;
