@@ -90,7 +90,7 @@ inline int lds_bytes(int V, int nbuf) {
 // (ksh holds one set of the chosen digit's scalars per histogram, and a set
 // is written again only two passes later, after everyone has read it).
 template <int R, typename Gen>
-__device__ uint64_t kth_largest(int n, int kth, Gen gen, int* khist, int* ksh) {
+__device__ __forceinline__ uint64_t kth_largest(int n, int kth, Gen gen, int* khist, int* ksh) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint64_t kr[R];
 #pragma unroll
@@ -730,21 +730,16 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
           else hi = mid - 1;
         }
         const int k = lo, j = i - s_offs[k];
-        float key;
-        int c;
-        bool ex = false;
-        if (j == 0) {
-          key = s_kb[k];
-          c = blank;
-        } else if (j == 1) {
-          key = s_kc[k];
-          c = s_last[k];
-        } else {
-          const int r = j - 2;
-          ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
-          key = s_A[k] + Rl[r];
-          c = Rc[r];
-        }
+        // every read is made and the values selected: selecting between the
+        // reads would turn into a load through a selected generic pointer,
+        // with `blank` spilled to scratch memory
+        const int r = j >= 2 ? j - 2 : 0;
+        const float kbv = s_kb[k], kcv = s_kc[k], lkey = s_A[k] + Rl[r];
+        const int lastv = s_last[k], rcv = Rc[r];
+        const uint32_t exw = s_exm[k * kExw + (r >> 5)];
+        const float key = j == 0 ? kbv : (j == 1 ? kcv : lkey);
+        const int c = j == 0 ? blank : (j == 1 ? lastv : rcv);
+        const bool ex = j >= 2 && ((exw >> (r & 31)) & 1u);
         const uint64_t x =
             (!ex && key > kNeg) ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
         cbuf[i] = x >= tau ? x : 0ull;
@@ -804,20 +799,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
           if (qi < ntot) {
             while (s_offs[k + 1] <= qi) k++;
             const int j = qi - s_offs[k];
-            float key;
-            int c;
-            if (j == 0) {
-              key = s_kb[k];
-              c = blank;
-            } else if (j == 1) {
-              key = s_kc[k];
-              c = s_last[k];
-            } else {
-              const int r = j - 2;
-              const bool ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
-              key = ex ? kNeg : s_A[k] + Rl[r];
-              c = Rc[r];
-            }
+            // (reads made, values selected: see the sampled gather above)
+            const int r = j >= 2 ? j - 2 : 0;
+            const float kbv = s_kb[k], kcv = s_kc[k], lkey = s_A[k] + Rl[r];
+            const int lastv = s_last[k], rcv = Rc[r];
+            const uint32_t exw = s_exm[k * kExw + (r >> 5)];
+            const bool ex = j >= 2 && ((exw >> (r & 31)) & 1u);
+            const float key = j == 0 ? kbv : (j == 1 ? kcv : (ex ? kNeg : lkey));
+            const int c = j == 0 ? blank : (j == 1 ? lastv : rcv);
             x = key > kNeg ? compose(key, (uint32_t)((k << kIdShift) | c)) : 0ull;
           }
           ck[u] = x;
