@@ -217,7 +217,8 @@ def test_bounded_page_pool():
         assert np.array_equal(a, e)
 
 
-@pytest.mark.parametrize("W,ps,theta", [(4, 4, 1.0), (10, 16, 0.9), (32, 64, 1.0), (32, 4, 0.95)])
+@pytest.mark.parametrize("W,ps,theta", [(1, 4, 1.0), (2, 8, 0.9), (4, 4, 1.0), (10, 16, 0.9),
+                                         (32, 64, 1.0), (32, 4, 0.95)])
 def test_page_counts_equal_the_page_allocator(W, ps, theta):
     # pages in use at most per row (paged storage, beams up to 32) against the
     # oracle's model of the page's allocator, and the same rows running dry in

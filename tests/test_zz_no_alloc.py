@@ -43,12 +43,15 @@ def no_alloc(cfg, x, lens_d, N, mol):
 
 
 CASES = [
-    # (B, T, V, beam, threshold, max_out_len, paged, seed): the first call fills
-    # much of the scratch, the second is smaller and reads over stale contents
-    (24, 400, 1024, 16, 0.999, 256, True, 1),
-    (5, 150, 1024, 16, 0.9, 150, True, 2),
-    (12, 300, 300, 32, 1.0, 300, False, 3),
-    (2, 60, 40, 4, 0.9, 60, False, 4),
+    # (B, T, V, beam, threshold, max_out_len, paged, seed, num_pages): the first
+    # call fills much of the scratch, the next ones are smaller and read over
+    # stale contents (a pool the caller sizes, and beams above 32, included)
+    (24, 400, 1024, 16, 0.999, 256, True, 1, 0),
+    (5, 150, 1024, 16, 0.9, 150, True, 2, 0),
+    (12, 300, 300, 32, 1.0, 300, False, 3, 0),
+    (6, 120, 200, 48, 1.0, 120, True, 5, 0),
+    (4, 100, 200, 8, 0.95, 100, True, 6, 8 * (100 // 16 + 2)),
+    (2, 60, 40, 4, 0.9, 60, False, 4, 0),
 ]
 
 
@@ -68,13 +71,14 @@ def test_no_alloc_equals_workspace_decode_at_full_size_then_smaller():
         assert np.array_equal(a, b)
     del x
     torch.cuda.empty_cache()
-    for B, T, V, W, thr, mol, paged, seed in CASES:
-        print(f"[case] no-alloc B={B} T={T} V={V} W={W} paged={paged}", flush=True)
+    for B, T, V, W, thr, mol, paged, seed, npages in CASES:
+        print(f"[case] no-alloc B={B} T={T} V={V} W={W} paged={paged} num_pages={npages}",
+              flush=True)
         lp, lens = synth.peaky(B, T, V, seed=seed, p_blank=0.6, lengths=(T // 2, T))
         x = torch.from_numpy(lp).cuda()
         lens_d = torch.from_numpy(lens).cuda()
         cfg = cpb.DecoderConfig(beam=W, nbest=W, blank_threshold=thr, max_out_len=mol,
-                                paged=paged)
+                                paged=paged, num_pages=npages)
         ref = with_workspace(cfg, x, lens_d)
         got = no_alloc(cfg, x, lens_d, W, mol)
         for a, b in zip(got, ref):
