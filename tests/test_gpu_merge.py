@@ -36,7 +36,7 @@ def recreated_parents(lp, W):
     return n
 
 
-@pytest.mark.parametrize("W,paged", [(4, False), (6, True), (3, False)])
+@pytest.mark.parametrize("W,paged", [(4, False), (6, True), (3, False), (40, False), (36, True)])
 def test_recreated_parent_prefixes_are_compared_exactly(W, paged):
     B, T, V = 40, 60, 3
     rows = [synth.peaky(1, T, V, seed=s, p_blank=0.3, blank_bias=1.0, token_bias=1.0,
