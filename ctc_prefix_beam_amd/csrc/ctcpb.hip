@@ -721,6 +721,8 @@ struct StoreState {
   int freetop, nextfree, high;   // paged: free-stack top, next never-used page, high water
   int len0, len1;          // this lane's slot (flat: row length, -1 unknown; paged: pages)
   int src0, src1;          // this lane's slot: source slot of its last fork (-1 none)
+  int lab0, lab1;          // flat: the label its last fork appended (-1 none)
+  int m0, m1;              // flat: which common-prefix matrix holds parity 0 / 1's
 };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -742,6 +744,16 @@ __device__ __forceinline__ StoreState store_state_load(const Ctx& C) {
   ss.len1 = L.paged ? (in ? C.tlen[kMaxBeam + lane] : 0) : -1;
   ss.src0 = -1;
   ss.src1 = -1;
+  ss.lab0 = -1;
+  ss.lab1 = -1;
+  // flat: both parities start on matrix 0, all zeros (a valid lower bound)
+  ss.m0 = 0;
+  ss.m1 = 0;
+  if (!L.paged) {
+    int4* z = reinterpret_cast<int4*>(C.tail);
+    const int n4 = (4 * L.W * L.W + 15) >> 4;   // within the 16-byte aligned region
+    for (int i = lane; i < n4; i += kWave) z[i] = make_int4(0, 0, 0, 0);
+  }
   return ss;
 }
 
@@ -773,6 +785,7 @@ __device__ __forceinline__ void store_seed(const Ctx& C, StoreState& ss, const W
   const int W = L.W;
   const bool want = w.valid && w.c != L.blank;
   ss.src0 = -1;
+  ss.lab0 = want ? w.c : -1;
   if (!L.paged) {
     ss.len0 = want ? 1 : 0;
     if (want) C.clist[(int64_t)lane * L.ldc] = w.c;
@@ -1305,10 +1318,16 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
 // ------------------------------------------------------------ token stores --
 // Flat (sec. 3.1, 7): slot r of parity p receives its source's tokens from
 // parity p^1 plus the new label.  Only positions that can differ from what
-// the row already holds are copied: if the source beam was itself copied
-// from slot r one step earlier, the row's old content is a prefix of the new
-// one; otherwise positions below the common prefix that every live beam of
-// two steps ago shared are already in place.  Copies move 4 tokens at once.
+// the row already holds are written: if the source beam was itself forked
+// from slot r one step earlier, the row's old content is the source's tokens
+// but the label that fork appended, which is written directly (no copy);
+// otherwise the row's old beam and the source's own source (both of two steps
+// ago) share a known prefix, which is in place, and the rest is copied, 4
+// tokens at once.  In a step where no slot changes lineage nothing is copied.
+// The shared prefixes are lower bounds kept per parity in a W x W matrix:
+// rows forked from one source share its tokens, rows from two sources share
+// at least what those shared; a step where every slot keeps its lineage keeps
+// the previous step's matrix.
 __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int step, const Winner& w) {
   const Layout& L = C.L;
   const int lane = lane_id();
@@ -1318,52 +1337,90 @@ __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int ste
   const int cplp = p ? ss.pre1 : ss.pre0;
   const int old_len = p ? ss.len1 : ss.len0;
   const int ksrc = __shfl(p ? ss.src0 : ss.src1, w.k, 64);   // source of w.k one step earlier
+  const int klab = __shfl(p ? ss.lab0 : ss.lab1, w.k, 64);   // and the label it got then
+  int16_t* mats = reinterpret_cast<int16_t*>(C.tail);
+  const int16_t* mp = mats + (p ? ss.m1 : ss.m0) * W * W;    // rows of parity p (two steps ago)
   int start = 0;
+  bool own = false;
   if (w.valid) {
-    if (ksrc == lane && old_len >= 0) start = old_len;
-    else if ((live2 >> lane) & 1u) start = cplp;
+    if (ksrc == lane && old_len >= 0) {
+      start = old_len;
+      own = true;
+    } else if ((live2 >> lane) & 1u) {
+      start = cplp;
+      if (ksrc >= 0 && ((live2 >> ksrc) & 1u)) start = max(start, (int)mp[lane * W + ksrc]);
+    }
     if (start > w.len_k) start = w.len_k;
   }
+  // the row holds the source's tokens but (at most) the label of its last fork
+  const bool direct = own && (w.len_k == old_len || (w.len_k == old_len + 1 && klab >= 0));
   const int s4 = start >> 2;
   const int e4 = w.valid ? (w.len_k + 3) >> 2 : 0;
-  const int cnt = w.valid ? e4 - s4 : 0;
-  const int incl = wave_incl_scan(lane < W ? cnt : 0);
-  const int total = __shfl(incl, 63, 64);
-  int* offs = C.offs;  // [0, 33): offsets; [40, 72): first int4; [80, 112): sources
-  if (lane < W) {
-    offs[lane] = incl - cnt;
-    offs[40 + lane] = s4;
-    offs[80 + lane] = w.k;
-  }
-  lds_sync();
-  int4* c4 = reinterpret_cast<int4*>(C.clist);
-  const int64_t ld4 = L.ldc >> 2;
-  for (int i = lane; i < total; i += kWave) {
-    int a = 0, z = W - 1;
-    while (a < z) {
-      const int mid = (a + z + 1) >> 1;
-      if (offs[mid] <= i) a = mid;
-      else z = mid - 1;
+  const int cnt = (w.valid && !direct) ? e4 - s4 : 0;
+  int* row = C.clist + (int64_t)(p * W + (lane < W ? lane : 0)) * L.ldc;
+  if (__ballot(lane < W && cnt > 0) != 0ull) {
+    const int incl = wave_incl_scan(lane < W ? cnt : 0);
+    const int total = __shfl(incl, 63, 64);
+    int* offs = C.offs;  // [0, 33): offsets; [40, 72): first int4; [80, 112): sources
+    if (lane < W) {
+      offs[lane] = incl - cnt;
+      offs[40 + lane] = s4;
+      offs[80 + lane] = w.k;
     }
-    const int64_t pos4 = offs[40 + a] + (i - offs[a]);
-    c4[(int64_t)(p * W + a) * ld4 + pos4] = c4[(int64_t)(q * W + offs[80 + a]) * ld4 + pos4];
+    lds_sync();
+    int4* c4 = reinterpret_cast<int4*>(C.clist);
+    const int64_t ld4 = L.ldc >> 2;
+    for (int i = lane; i < total; i += kWave) {
+      int a = 0, z = W - 1;
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (offs[mid] <= i) a = mid;
+        else z = mid - 1;
+      }
+      const int64_t pos4 = offs[40 + a] + (i - offs[a]);
+      c4[(int64_t)(p * W + a) * ld4 + pos4] = c4[(int64_t)(q * W + offs[80 + a]) * ld4 + pos4];
+    }
+    wave_sync();  // the copies land before the labels written below
   }
-  wave_sync();  // the copies land before the appended label
-  if (w.valid && w.c != blank) C.clist[((int64_t)(p * W + lane)) * L.ldc + w.len_k] = w.c;
+  if (direct && w.len_k == old_len + 1) row[old_len] = klab;
+  if (w.valid && w.c != blank) row[w.len_k] = w.c;
+  // this step's matrix (read above for parity p: the new one goes to the
+  // buffer that parity q's does not use)
+  const int mq = p ? ss.m0 : ss.m1;
+  int mnew = mq;
+  if (__ballot(lane < W && w.valid && w.k != lane) != 0ull) {
+    mnew = 1 - mq;
+    const int16_t* fq = mats + mq * W * W;
+    int16_t* fn = mats + mnew * W * W + (lane < W ? lane : 0) * W;
+    const int k1 = w.k < W ? w.k : 0;   // (slots without a beam: any row, never read)
+    const int16_t lk1 = (int16_t)min(w.len_k, 32767);
+    if (lane < W) {
+#pragma unroll 4
+      for (int r2 = 0; r2 < W; r2++) {
+        const int k2 = __builtin_amdgcn_readlane(k1, r2);
+        fn[r2] = k1 == k2 ? lk1 : fq[k1 * W + k2];
+      }
+    }
+  }
   const int nlen = w.valid ? w.len_k + (w.c != blank ? 1 : 0) : -1;
   const int nsrc = w.valid ? w.k : -1;
+  const int nlab = (w.valid && w.c != blank) ? w.c : -1;
   const uint32_t vm = (uint32_t)__ballot(w.valid);
   const int cplq = q ? ss.pre1 : ss.pre0;
   if (p) {
     ss.len1 = nlen;
     ss.src1 = nsrc;
+    ss.lab1 = nlab;
     ss.live1 = vm;
     ss.pre1 = cplq;
+    ss.m1 = mnew;
   } else {
     ss.len0 = nlen;
     ss.src0 = nsrc;
+    ss.lab0 = nlab;
     ss.live0 = vm;
     ss.pre0 = cplq;
+    ss.m0 = mnew;
   }
 }
 
@@ -2519,7 +2576,9 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
   S.tab = take(L.paged ? 2 * L.W * L.max_lp * 2 : 0);   // 16-bit page ids
   S.ref = take(L.paged ? L.npages * 4 : 0);             // 32-bit: updated atomically
   S.fstk = take(L.paged ? L.npages * 2 : 0);
-  S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 0);
+  // paged: the tail mirrors; flat: the store wave's two matrices of pairwise
+  // common-prefix lengths (int16, W x W each)
+  S.tail = take(L.paged ? 2 * L.W * L.ps * 4 : 2 * L.W * L.W * 2);
   S.tlen = take(L.paged ? 2 * kMaxBeam * 4 : 0);
   S.clist_lds = (!L.paged && clist_lds) ? 1 : 0;
   S.clist = take(S.clist_lds ? 2 * L.W * L.ldc * 4 : 0);
@@ -2608,6 +2667,17 @@ int launch(K kernel, int blocks, int threads, int lds, hipStream_t st, const Par
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the decoder can hold a row of this layout on one CU (the checks the
+// decode and stream calls make before launching).
+int check_fits(const Resolved& R, const Layout& L) {
+  if (R.W > kMaxBeam) {
+    if (wide::lds_bytes(R.V, 1) > kLdsLimit)
+      return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
+    return CTCPB_OK;
+  }
+  return check_lds(L, plan_lds(L));
+}
+
 }  // namespace
 
 extern "C" {
@@ -2623,6 +2693,7 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
+  if (int rc = check_fits(R, L)) return rc;
   *out_bytes = (size_t)batch * (size_t)L.row_bytes;
   return ok();
 }
@@ -2633,6 +2704,7 @@ int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_b
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (num_streams < 0) return fail(CTCPB_ERR_INVALID, "num_streams must be >= 0");
   const Layout L = layout_for(R, R.cap_stream, 0);
+  if (int rc = check_fits(R, L)) return rc;
   *out_bytes = (size_t)num_streams * (size_t)L.row_bytes;
   return ok();
 }

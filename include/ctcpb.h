@@ -57,7 +57,8 @@ typedef struct {
                               refcounts and free stack in one CU's 160 KB of LDS;
                               configurations that do not fit return
                               CTCPB_ERR_UNSUPPORTED.  Flat storage fits up to
-                              V = 14640; paged storage at 1500 frames (offline max_T,
+                              V = 14616 / 14540 / 14232 for beams 8 / 16 / 32;
+                              paged storage at 1500 frames (offline max_T,
                               streaming capacity) up to 13756 / 12896 / 11180 for
                               beams 8 / 16 / 32, at 4096 frames and beam 32 up to
                               5996 (a larger page_size shrinks the tables).  Beams
@@ -106,7 +107,9 @@ typedef struct {
 } ctcpb_config;
 
 /* Bytes of device workspace ctcpb_decode_offline needs for `batch` rows of up
- * to `max_T` frames (sec. 5 calculate_[paged_]workspace_size). */
+ * to `max_T` frames (sec. 5 calculate_[paged_]workspace_size).  Returns
+ * CTCPB_ERR_UNSUPPORTED, with nothing written, when a row of this
+ * configuration does not fit one CU's LDS (see ctcpb_config.vocab). */
 int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
                          size_t* out_bytes);
 
@@ -165,7 +168,9 @@ int ctcpb_decode_offline_noalloc(const ctcpb_config* cfg, const float* log_prob,
                                  int32_t* out_lengths, float* out_scores, void* stream);
 
 /* Bytes of a streaming state blob holding `num_streams` independent streams
- * (sec. 5 calculate_[paged_]state_buffer_size). */
+ * (sec. 5 calculate_[paged_]state_buffer_size).  Returns
+ * CTCPB_ERR_UNSUPPORTED, with nothing written, when a stream of this
+ * configuration does not fit one CU's LDS (see ctcpb_config.vocab). */
 int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_bytes);
 
 /* Put every stream of the blob in the fresh state (no frame decoded; reads

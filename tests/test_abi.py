@@ -101,10 +101,33 @@ def test_decode_argument_errors_need_no_device(L):
     # empty batch: nothing to do
     assert L.ctcpb_decode_offline(ctypes.byref(c), n, 0, 256, 0, 500, n, n, 0, n, n, n, n) == 0
     # LDS budget: a very wide vocabulary with paged metadata does not fit a CU
+    # (the size query says so too)
     big = cfg(vocab=16384, beam=32, nbest=32, storage=1, page_size=4, max_out_len=8)
-    need = ws(L, big, 1, 20000)[1]
+    assert ws(L, big, 1, 20000)[0] == 3
     assert L.ctcpb_decode_offline(ctypes.byref(big), p, 20000 * 16384, 16384, 1, 20000, p, p,
-                                  need, p, p, p, n) == 3
+                                  1 << 62, p, p, p, n) == 3
+
+
+# The vocabulary limits ctcpb_config.vocab documents: (beam, storage, frames,
+# largest V that fits one CU).  Checked through the size queries, which make
+# the decoder's own LDS check and launch nothing.
+DOCUMENTED_LIMITS = [(8, 0, 1500, 14616), (16, 0, 1500, 14540), (32, 0, 1500, 14232),
+                     (8, 1, 1500, 13756), (16, 1, 1500, 12896), (32, 1, 1500, 11180),
+                     (32, 1, 4096, 5996)]
+
+
+@pytest.mark.parametrize("beam,storage,T,vmax", DOCUMENTED_LIMITS)
+def test_documented_vocabulary_limits(L, beam, storage, T, vmax):
+    def c(V):
+        return cfg(beam=beam, nbest=min(beam, 8), vocab=V, storage=storage, max_out_len=512,
+                   capacity=T)
+    assert ws(L, c(vmax), 1, T)[0] == 0
+    assert ws(L, c(vmax + 1), 1, T)[0] == 3
+    # a stream's capacity plays the part of max_T
+    assert ss(L, c(vmax), 1)[0] == 0
+    assert ss(L, c(vmax + 1), 1)[0] == 3
+    # beams above 32 (the wide decoder) fit every vocabulary
+    assert ws(L, cfg(beam=64, nbest=8, vocab=16384, storage=storage), 1, T)[0] == 0
 
 
 def test_wide_beams_flat_and_paged(L):
