@@ -1370,15 +1370,40 @@ __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int ste
     lds_sync();
     int4* c4 = reinterpret_cast<int4*>(C.clist);
     const int64_t ld4 = L.ldc >> 2;
-    for (int i = lane; i < total; i += kWave) {
-      int a = 0, z = W - 1;
-      while (a < z) {
-        const int mid = (a + z + 1) >> 1;
-        if (offs[mid] <= i) a = mid;
-        else z = mid - 1;
+    // piece i goes to row a, the last with offs[a] <= i.  A lane's pieces
+    // only move forward: the row of its first is found by binary lifting, the
+    // later ones by stepping on (the next row's first piece kept at hand).
+    int a = 0;
+#pragma unroll
+    for (int st = 16; st > 0; st >>= 1)
+      if (a + st < W && offs[a + st] <= lane) a += st;
+    int oa = offs[a], sa = offs[40 + a], ka = offs[80 + a];
+    int nx = a + 1 < W ? offs[a + 1] : 0x7fffffff;
+    auto locate = [&](int i, int64_t& d, int64_t& sidx) {
+      while (i >= nx) {
+        a++;
+        oa = nx;
+        sa = offs[40 + a];
+        ka = offs[80 + a];
+        nx = a + 1 < W ? offs[a + 1] : 0x7fffffff;
       }
-      const int64_t pos4 = offs[40 + a] + (i - offs[a]);
-      c4[(int64_t)(p * W + a) * ld4 + pos4] = c4[(int64_t)(q * W + offs[80 + a]) * ld4 + pos4];
+      const int64_t pos4 = sa + (i - oa);
+      d = (int64_t)(p * W + a) * ld4 + pos4;
+      sidx = (int64_t)(q * W + ka) * ld4 + pos4;
+    };
+    // four pieces per lane in flight before any is stored (pieces past the
+    // end stand on the last one and are not stored)
+    for (int i0 = lane; i0 < total; i0 += 4 * kWave) {
+      int64_t d0, s0, d1, s1, d2, s2, d3, s3;
+      locate(i0, d0, s0);
+      locate(min(i0 + kWave, total - 1), d1, s1);
+      locate(min(i0 + 2 * kWave, total - 1), d2, s2);
+      locate(min(i0 + 3 * kWave, total - 1), d3, s3);
+      const int4 v0 = c4[s0], v1 = c4[s1], v2 = c4[s2], v3 = c4[s3];
+      c4[d0] = v0;
+      if (i0 + kWave < total) c4[d1] = v1;
+      if (i0 + 2 * kWave < total) c4[d2] = v2;
+      if (i0 + 3 * kWave < total) c4[d3] = v3;
     }
     wave_sync();  // the copies land before the labels written below
   }
