@@ -43,6 +43,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <climits>
 #include <mutex>
 #include <string>
 
@@ -2810,6 +2811,13 @@ int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int rc = launch(select_kernel, batch, 256, 0, st, P, "select_kernel")) return rc;
   if (wide_path) {
+    // the ranked labels of every selected frame first, in parallel over frames
+    const int groups = wide::rank_groups(P.T);
+    if ((int64_t)batch * groups > INT_MAX)
+      return fail(CTCPB_ERR_UNSUPPORTED, "too many rows for one wide-beam launch");
+    if (int rc = launch(wide::rank_wide_kernel, batch * groups, wide::kNT,
+                        wide::rank_lds_bytes(R.V), st, P, "rank_wide_kernel"))
+      return rc;
     if (int rc = launch(wide::decode_wide_kernel<false>, batch, wide::kNT,
                         wide::lds_bytes(R.V, P.S.nslot), st, P, "decode_wide_kernel"))
       return rc;

@@ -125,6 +125,12 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
     L.o_tlen = off;
     off += align256((int64_t)2 * kMaxBeam * 4);
   }
+  // offline beams above kMaxBeam: the ranked labels of every selected frame,
+  // [cap_sel][K] with K = min(V - 1, 2W + 2), at the end of the region
+  if (W > kMaxBeam && cap_sel > 0) {
+    const int K = V - 1 < 2 * W + 2 ? V - 1 : 2 * W + 2;
+    off += align256((int64_t)cap_sel * K * 4);
+  }
   L.row_bytes = align256(off);
   return L;
 }

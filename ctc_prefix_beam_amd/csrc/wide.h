@@ -183,6 +183,84 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
   }
 }
 
+// The best K non-blank labels of a frame row by (lp desc, label asc) (sec.
+// 3.4.6): out(rank, label) once per rank r < K (K <= V - 1: at least K labels
+// have a nonzero key).  kb64: the gathered keys (kMaxK + 8); tmp: rank_keys'
+// chunks; khist / ksh as kth_largest; cnt: one int.  Ends without a barrier
+// (out's writes come last).
+template <typename Out>
+__device__ __forceinline__ void rank_frame_wide(const float* row, int V, int blank, int K,
+                                                uint64_t* kb64, uint64_t* tmp, int* khist,
+                                                int* ksh, int* cnt, Out out) {
+  const int tid = threadIdx.x;
+  auto lkey = [&](int c) -> uint64_t {
+    return c == blank ? 0ull : compose(row[c], (uint32_t)c);
+  };
+  const uint64_t xk = kth_largest<8>(V, K, lkey, khist, ksh);
+  if (tid == 0) *cnt = 0;
+  __syncthreads();
+  for (int c = tid; c < V; c += kNT) {
+    const uint64_t x = lkey(c);
+    if (x != 0ull && x >= xk) kb64[atomicAdd(cnt, 1)] = x;
+  }
+  __syncthreads();
+  rank_keys(kb64, K, tmp, [&](int r, uint64_t x) { out(r, (int)comp_id(x)); });
+}
+
+// Offline: the ranked labels of every selected frame are independent of the
+// beams, so a pre-pass ranks all of them in parallel (the page hoists its
+// vocabulary ranking out of the fused step the same way, sec. 3.4.6) into
+// the row's list region, [max_T][K] labels in rank order; the decode reads
+// one list per step.  Block i ranks frames g, g + G, ... of row i / G (g =
+// i % G, G = rank_groups(max_T)) with the decode's own ranking.
+constexpr int kRankGroups = 256;
+__host__ __device__ inline int rank_groups(int max_T) {
+  return max_T < 1 ? 1 : (max_T < kRankGroups ? max_T : kRankGroups);
+}
+inline int rank_lds_bytes(int V) {
+  return off::a16(V * 4) + off::a16((kMaxK + 8) * 8) + 64 * kRankChunks * 8 + 2 * 256 * 4 + 16 * 4;
+}
+__device__ __forceinline__ int* rank_lists(const Layout& L, char* base, int K) {
+  const int64_t bytes = ((int64_t)L.cap_sel * K * 4 + 255) & ~(int64_t)255;   // align256
+  return reinterpret_cast<int*>(base + L.row_bytes - bytes);
+}
+
+__global__ __launch_bounds__(kNT) void rank_wide_kernel(Params P) {
+  extern __shared__ __align__(16) char smem[];
+  const Layout L = P.L;
+  const int G = rank_groups(P.T);
+  const int V = L.V, blank = L.blank, W = L.W;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  char* base = P.state + (int64_t)b * L.row_bytes;
+  const int* hdr = reinterpret_cast<const int*>(base);
+  const int* sel = reinterpret_cast<const int*>(base + L.o_sel);
+  const int nsel = hdr[kNSel];
+  const int K = min(V - 1, 2 * W + 2);
+  int* lists = rank_lists(L, base, K);
+  float* row = reinterpret_cast<float*>(smem);
+  uint64_t* kb64 = reinterpret_cast<uint64_t*>(smem + off::a16(V * 4));
+  uint64_t* tmp = kb64 + (kMaxK + 8);
+  int* khist = reinterpret_cast<int*>(tmp + 64 * kRankChunks);
+  int* ksh = khist + 2 * 256;
+  int* cnt = ksh + 8;
+  for (int i = threadIdx.x; i < 2 * 256; i += kNT) khist[i] = 0;
+  const float* lp_row = P.lp + (int64_t)b * P.stride_b;
+  for (int f = g; f < nsel; f += G) {
+    const float* gr = lp_row + (int64_t)sel[f] * P.stride_t;
+    if (P.vec4) {
+      for (int i = threadIdx.x; i < (V >> 2); i += kNT)
+        reinterpret_cast<float4*>(row)[i] = reinterpret_cast<const float4*>(gr)[i];
+    } else {
+      for (int i = threadIdx.x; i < V; i += kNT) row[i] = gr[i];
+    }
+    __syncthreads();
+    int* out = lists + (int64_t)f * K;
+    rank_frame_wide(row, V, blank, K, kb64, tmp, khist, ksh, cnt,
+                    [&](int r, int c) { out[r] = c; });
+    __syncthreads();   // the row and the scratch are reused by the next frame
+  }
+}
+
 // Paged token storage (sec. 3.4.5 paged variant, sec. 4.2) in the row region:
 // block tables [2][W][max_lp] of page ids (-1 none; the pages a row holds are
 // the leading entries of its table row), a reference count per page, a LIFO
@@ -412,6 +490,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   if (nbuf == 2 && wave == 3 && nframes > 0) row_fetch_async(frame_src(0, cf), rows, V, P.vec4);
   int last_t = STREAM ? hdr[kLastT] : -1, step = step_in, prevK = 0, nver = 0;
   for (int i = tid; i < 2 * 256; i += kNT) khist[i] = 0;
+  // offline: the pre-pass's lists (rank_wide_kernel); this thread's entries
+  // r = tid and tid + kNT of the next frame's list are loaded one step ahead
+  const int* lists = STREAM ? nullptr : rank_lists(L, base, K);
+  int lst0 = 0, lst1 = 0;
+  if (!STREAM && nframes > 0) {
+    lst0 = tid < K ? lists[tid] : 0;
+    lst1 = tid + kNT < K ? lists[tid + kNT] : 0;
+  }
   if (tid == 0) {
     // common token prefix of the live rows of parity 0 / 1
     sh[6] = STREAM ? hdr[kCpl0] : 0;
@@ -449,23 +535,30 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       row_fetch_async(frame_src(f + 1, cnext), rows + ((f + 1) & 1) * rstride, V, P.vec4);
 
     // ---- the frame's best K non-blank labels, (lp desc, label asc)
-    auto lkey = [&](int c) -> uint64_t {
-      return c == blank ? 0ull : compose(row[c], (uint32_t)c);
-    };
-    const uint64_t xk = kth_largest<8>(V, K, lkey, khist, ksh);
-    if (tid == 0) sh[2] = 0;
-    __syncthreads();
-    for (int c = tid; c < V; c += kNT) {
-      const uint64_t x = lkey(c);
-      if (x != 0ull && x >= xk) kb64[atomicAdd(&sh[2], 1)] = x;
+    if (STREAM) {
+      rank_frame_wide(row, V, blank, K, kb64, cbuf, khist, ksh, &sh[2], [&](int r, int c) {
+        Rc[r] = c;
+        Rl[r] = row[c];
+        rmap[c] = (int16_t)r;
+      });
+    } else {
+      // ranked by the pre-pass
+      if (tid < K) {
+        Rc[tid] = lst0;
+        Rl[tid] = row[lst0];
+        rmap[lst0] = (int16_t)tid;
+      }
+      if (tid + kNT < K) {
+        Rc[tid + kNT] = lst1;
+        Rl[tid + kNT] = row[lst1];
+        rmap[lst1] = (int16_t)(tid + kNT);
+      }
+      if (f + 1 < nframes) {
+        const int* nl = lists + (int64_t)(f + 1) * K;
+        lst0 = tid < K ? nl[tid] : 0;
+        lst1 = tid + kNT < K ? nl[tid + kNT] : 0;
+      }
     }
-    __syncthreads();
-    rank_keys(kb64, K, cbuf, [&](int r, uint64_t x) {
-      const int c = (int)comp_id(x);
-      Rc[r] = c;
-      Rl[r] = row[c];
-      rmap[c] = (int16_t)r;
-    });
     prevK = K;
     if (tid < kMaxW) {
       for (int w = 0; w < kExw; w++) s_exm[tid * kExw + w] = 0u;
