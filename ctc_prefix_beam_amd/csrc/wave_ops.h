@@ -225,6 +225,26 @@ __device__ __forceinline__ T wave_sort64_desc(T v) {
   return v;
 }
 
+// The 64 largest of two sorted runs of 64 keys, a descending and b
+// ascending (a lane each), in descending lane order: the half-cleaner of a
+// bitonic merge keeps the larger of each pair a[l], b[l] (a bitonic sequence
+// holding the 64 largest), and the last six stages order it.
+__device__ __forceinline__ uint64_t wave_top64_merge(uint64_t a, uint64_t b) {
+  uint64_t v = a > b ? a : b;
+  v = bitonic_stage<64, 32>(v);
+  v = bitonic_stage<64, 16>(v);
+  v = bitonic_stage<64, 8>(v);
+  v = bitonic_stage<64, 4>(v);
+  v = bitonic_stage<64, 2>(v);
+  v = bitonic_stage<64, 1>(v);
+  return v;
+}
+
+// One key per lane sorted ascending (the complements sorted descending).
+__device__ __forceinline__ uint64_t wave_sort64_asc(uint64_t v) {
+  return ~wave_sort64_desc<uint64_t>(~v);
+}
+
 // Maximum over the wave, returned to every lane.
 __device__ __forceinline__ float wave_max(float v) {
   int x = __float_as_int(v);

@@ -183,6 +183,37 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
   }
 }
 
+// The 64 largest of the keys keys[0, n) (n <= 256; missing ones count as 0)
+// in descending order, returned in wave 0's lanes (other waves: unspecified).
+// Each of the first ceil(n / 64) waves sorts a chunk of 64 (odd chunks
+// ascending) into tmp[0, 256); with more than two chunks waves 0 and 1 merge
+// the pairs into tmp[256, 384) (wave 1's run stored ascending); wave 0 merges
+// the last pair.  Block-wide: every thread calls it; tmp must not overlap
+// keys.  Ends with wave 0 holding the result (no barrier after the merge).
+__device__ __forceinline__ uint64_t block_top64(const uint64_t* keys, int n, uint64_t* tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = (n + 63) >> 6;
+  if (wave < nch) {
+    const uint64_t x = tid < n ? keys[tid] : 0ull;
+    tmp[tid] = (wave & 1) ? wave_sort64_asc(x) : wave_sort64_desc<uint64_t>(x);
+  } else if (wave < (nch > 2 ? 4 : 2)) {
+    tmp[tid] = 0ull;   // empty chunks up to the end of the last pair
+  }
+  __syncthreads();
+  const uint64_t* pair = tmp;
+  if (nch > 2) {
+    if (wave < 2) {
+      const uint64_t m = wave_top64_merge(tmp[128 * wave + lane], tmp[128 * wave + 64 + lane]);
+      tmp[256 + 64 * wave + (wave ? 63 - lane : lane)] = m;
+    }
+    __syncthreads();
+    pair = tmp + 256;
+  }
+  uint64_t top = 0ull;
+  if (wave == 0) top = wave_top64_merge(pair[lane], pair[64 + lane]);
+  return top;
+}
+
 // The best K non-blank labels of a frame row by (lp desc, label asc) (sec.
 // 3.4.6): out(rank, label) once per rank r < K (K <= V - 1: at least K labels
 // have a nonzero key).  kb64: the gathered keys (kMaxK + 8); tmp: rank_keys'
@@ -722,7 +753,19 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       cbuf[4 * k + 3] = o1;
     }
     __syncthreads();
-    uint64_t tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
+    // tau: the W-th largest of the 4W sample keys (0 when fewer are nonzero)
+    uint64_t tau;
+    if (W <= 64) {
+      const uint64_t top = block_top64(cbuf, 4 * W, cbuf + kCBuf - 384);
+      if (wave == 0) {
+        const uint64_t tw = readlane_u64(top, W - 1);
+        if (tid == 0) reinterpret_cast<unsigned long long*>(sh + 12)[0] = tw;
+      }
+      __syncthreads();
+      tau = reinterpret_cast<unsigned long long*>(sh + 12)[0];
+    } else {
+      tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
+    }
     if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
     const float tau_key = comp_key(tau);
     // each live beam's place h - 1 among the beams' bests (in s_lim until the
@@ -839,7 +882,19 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       }
       if (tid == 0) sh[4] = 0;
       __syncthreads();
-      if (nsurv <= 64 * kRankChunks) {
+      if (W <= 64 && nsurv <= 256) {
+        // at most 256 survivors (the usual case for beams up to 64): their 64
+        // largest in order (zeros, the candidates below the bound, come last)
+        const uint64_t top = block_top64(cbuf, nsurv, cbuf + kCBuf - 384);
+        if (wave == 0) {
+          if (tid < W) win[tid] = top;
+          const int cnt = __popcll(__ballot(tid < W && top != 0ull));
+          if (tid == 0) sh[4] = cnt;
+        }
+        __syncthreads();
+        nw = sh[4];
+        ranked = true;
+      } else if (nsurv <= 64 * kRankChunks) {
         // few survivors (the usual case): rank them all, in place, and keep
         // the first W (zeros, the candidates below the bound, rank last and
         // are skipped)
