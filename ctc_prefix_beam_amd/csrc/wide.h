@@ -1145,22 +1145,43 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       int* drow = G.row(p, tid < W ? tid : 0);
       const int* srow_k = G.row(q, k >= 0 ? k : 0);
       __syncthreads();   // s_bslot complete; every read of the old state done
-      for (int j = 0; j < nps; j++) {
-        const int e = srow_k[j];
-        if ((j >= npo || drow[j] != e) && e >= 0) atomicAdd(&G.ref[e], 1);
+      // (table entries are read eight at a time, all loads issued before any
+      // is used: the tables live in global memory)
+      constexpr int kB = 8;
+      for (int j0 = 0; j0 < nps; j0 += kB) {
+        int e[kB], o[kB];
+#pragma unroll
+        for (int u = 0; u < kB; u++) {
+          e[u] = j0 + u < nps ? srow_k[j0 + u] : kInvalidPage;
+          o[u] = j0 + u < npo ? drow[j0 + u] : kInvalidPage;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; u++)
+          if (e[u] >= 0 && (j0 + u >= npo || o[u] != e[u])) atomicAdd(&G.ref[e[u]], 1);
       }
       __threadfence_block();
       __syncthreads();
       const int nmax = max(npo, nps);
-      for (int j = 0; j < nmax; j++) {
-        const int old = j < npo ? drow[j] : kInvalidPage;
-        const int e = j < nps ? srow_k[j] : kInvalidPage;
-        if (old == e) continue;
-        if (old >= 0 && atomicSub(&G.ref[old], 1) == 1) {
-          const int at = atomicAdd(&pgs[0], 1);
-          if (at < G.npages) G.fstk[at] = old;
+      for (int j0 = 0; j0 < nmax; j0 += kB) {
+        int e[kB], o[kB], left[kB];
+#pragma unroll
+        for (int u = 0; u < kB; u++) {
+          o[u] = j0 + u < npo ? drow[j0 + u] : kInvalidPage;
+          e[u] = j0 + u < nps ? srow_k[j0 + u] : kInvalidPage;
         }
-        drow[j] = e;
+        // the releases are issued together, then their old counts checked
+#pragma unroll
+        for (int u = 0; u < kB; u++)
+          left[u] = (o[u] >= 0 && o[u] != e[u]) ? atomicSub(&G.ref[o[u]], 1) : 0;
+#pragma unroll
+        for (int u = 0; u < kB; u++) {
+          if (j0 + u >= nmax || o[u] == e[u]) continue;
+          if (left[u] == 1) {
+            const int at = atomicAdd(&pgs[0], 1);
+            if (at < G.npages) G.fstk[at] = o[u];
+          }
+          drow[j0 + u] = e[u];
+        }
       }
       // Pass 2: the new label, in slot order.  It goes to offset klen mod
       // page_size of page klen / page_size: a fresh page at offset 0, else the
