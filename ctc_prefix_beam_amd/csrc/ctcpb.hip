@@ -728,10 +728,68 @@ struct StoreState {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ __forceinline__ StoreState store_state_load(const Ctx& C) {
+// dst[i] = src[i] for i < n by one wave, four loads per lane in flight before
+// their stores.
+template <typename D, typename S>
+__device__ __forceinline__ void wave_copy(D* dst, const S* src, int n) {
+  const int lane = lane_id();
+  for (int i = lane; i < n; i += 4 * kWave) {
+    const int j1 = i + kWave, j2 = i + 2 * kWave, j3 = i + 3 * kWave;
+    const S v0 = src[i], v1 = src[min(j1, n - 1)], v2 = src[min(j2, n - 1)],
+            v3 = src[min(j3, n - 1)];
+    dst[i] = (D)v0;
+    if (j1 < n) dst[j1] = (D)v1;
+    if (j2 < n) dst[j2] = (D)v2;
+    if (j3 < n) dst[j3] = (D)v3;
+  }
+}
+
+// The store wave's per-slot lineage and, for flat lists, the two matrices of
+// common-prefix bounds at the start of a launch.  A stream's flat lists go on
+// from what its previous chunk kept (the lineage and bounds describe the rows
+// in its state); otherwise every row's lineage is unknown and both parities
+// start on matrix 0, all zeros (a valid lower bound).  None of this is LDS
+// state that the beam wave sets up, so it runs before the first hand-off and
+// its loads overlap that wait.
+__device__ __forceinline__ void store_state_init(const Ctx& C, StoreState& ss, bool kept) {
   const Layout& L = C.L;
   const int lane = lane_id();
-  StoreState ss;
+  ss.len0 = ss.len1 = -1;
+  ss.src0 = ss.src1 = -1;
+  ss.lab0 = ss.lab1 = -1;
+  ss.m0 = ss.m1 = 0;
+  if (L.paged) return;
+  int16_t* mats = reinterpret_cast<int16_t*>(C.tail);
+  const int n = L.W * L.W;
+  if (kept) {
+    const char* a = C.base + L.o_sst;
+    const int* len = reinterpret_cast<const int*>(a + StoreArrays::len);
+    const int* src = reinterpret_cast<const int*>(a + StoreArrays::src);
+    const int* lab = reinterpret_cast<const int*>(a + StoreArrays::lab);
+    if (lane < kMaxBeam) {
+      ss.len0 = len[lane];
+      ss.len1 = len[kMaxBeam + lane];
+      ss.src0 = src[lane];
+      ss.src1 = src[kMaxBeam + lane];
+      ss.lab0 = lab[lane];
+      ss.lab1 = lab[kMaxBeam + lane];
+    }
+    const int16_t* gm = reinterpret_cast<const int16_t*>(a + StoreArrays::mat);
+    wave_copy(mats, gm, n);   // parity 0's matrix into buffer 0, parity 1's into buffer 1
+    wave_copy(mats + n, gm + kMaxBeam * kMaxBeam, n);
+    ss.m1 = 1;
+  } else {
+    int4* z = reinterpret_cast<int4*>(C.tail);
+    const int n4 = (4 * n + 15) >> 4;   // within the 16-byte aligned region
+    for (int i = lane; i < n4; i += kWave) z[i] = make_int4(0, 0, 0, 0);
+  }
+}
+
+// The wave-uniform part, from the LDS scalars (and the paged row lengths)
+// that the beam wave sets up: read once its first step is published.
+__device__ __forceinline__ void store_state_load(const Ctx& C, StoreState& ss) {
+  const Layout& L = C.L;
+  const int lane = lane_id();
   ss.live0 = (uint32_t)uni(C.scal[kScalLive0]);
   ss.live1 = (uint32_t)uni(C.scal[kScalLive1]);
   const int pk = L.paged ? kScalPcp0 : kScalCpl0;
@@ -740,25 +798,17 @@ __device__ __forceinline__ StoreState store_state_load(const Ctx& C) {
   ss.freetop = uni(C.scal[kScalFreeTop]);
   ss.nextfree = uni(C.scal[kScalNextFree]);
   ss.high = uni(C.scal[kScalHigh]);
-  const bool in = lane < kMaxBeam;
-  ss.len0 = L.paged ? (in ? C.tlen[lane] : 0) : -1;
-  ss.len1 = L.paged ? (in ? C.tlen[kMaxBeam + lane] : 0) : -1;
-  ss.src0 = -1;
-  ss.src1 = -1;
-  ss.lab0 = -1;
-  ss.lab1 = -1;
-  // flat: both parities start on matrix 0, all zeros (a valid lower bound)
-  ss.m0 = 0;
-  ss.m1 = 0;
-  if (!L.paged) {
-    int4* z = reinterpret_cast<int4*>(C.tail);
-    const int n4 = (4 * L.W * L.W + 15) >> 4;   // within the 16-byte aligned region
-    for (int i = lane; i < n4; i += kWave) z[i] = make_int4(0, 0, 0, 0);
+  if (L.paged) {
+    const bool in = lane < kMaxBeam;
+    ss.len0 = in ? C.tlen[lane] : 0;
+    ss.len1 = in ? C.tlen[kMaxBeam + lane] : 0;
   }
-  return ss;
 }
 
-__device__ __forceinline__ void store_state_save(const Ctx& C, const StoreState& ss) {
+// After the launch's last step: the scalars back to LDS (the beam wave moves
+// them to the header), paged row lengths to LDS, and a stream's flat lineage
+// and bounds to its state (`keep`).
+__device__ __forceinline__ void store_state_save(const Ctx& C, const StoreState& ss, bool keep) {
   const Layout& L = C.L;
   const int lane = lane_id();
   lds_order();
@@ -775,6 +825,25 @@ __device__ __forceinline__ void store_state_save(const Ctx& C, const StoreState&
   if (L.paged && lane < kMaxBeam) {
     C.tlen[lane] = ss.len0;
     C.tlen[kMaxBeam + lane] = ss.len1;
+  }
+  if (keep && !L.paged) {
+    char* a = C.base + L.o_sst;
+    int* len = reinterpret_cast<int*>(a + StoreArrays::len);
+    int* src = reinterpret_cast<int*>(a + StoreArrays::src);
+    int* lab = reinterpret_cast<int*>(a + StoreArrays::lab);
+    if (lane < kMaxBeam) {
+      len[lane] = ss.len0;
+      len[kMaxBeam + lane] = ss.len1;
+      src[lane] = ss.src0;
+      src[kMaxBeam + lane] = ss.src1;
+      lab[lane] = ss.lab0;
+      lab[kMaxBeam + lane] = ss.lab1;
+    }
+    const int n = L.W * L.W;
+    const int16_t* mats = reinterpret_cast<const int16_t*>(C.tail);
+    int16_t* gm = reinterpret_cast<int16_t*>(a + StoreArrays::mat);
+    wave_copy(gm, mats + ss.m0 * n, n);
+    wave_copy(gm + kMaxBeam * kMaxBeam, mats + ss.m1 * n, n);
   }
   lds_order();
 }
@@ -1324,7 +1393,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
 // but the label that fork appended, which is written directly (no copy);
 // otherwise the row's old beam and the source's own source (both of two steps
 // ago) share a known prefix, which is in place, and the rest is copied, 4
-// tokens at once.  In a step where no slot changes lineage nothing is copied.
+// tokens at once, eight such pieces per lane in flight.  In a step where no
+// slot changes lineage nothing is copied.
 // The shared prefixes are lower bounds kept per parity in a W x W matrix:
 // rows forked from one source share its tokens, rows from two sources share
 // at least what those shared; a step where every slot keeps its lineage keeps
@@ -1380,7 +1450,10 @@ __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int ste
       if (a + st < W && offs[a + st] <= lane) a += st;
     int oa = offs[a], sa = offs[40 + a], ka = offs[80 + a];
     int nx = a + 1 < W ? offs[a + 1] : 0x7fffffff;
-    auto locate = [&](int i, int64_t& d, int64_t& sidx) {
+    struct Piece {
+      int64_t d, s;   // destination and source, in 16-byte units of the lists
+    };
+    auto locate = [&](int i) -> Piece {
       while (i >= nx) {
         a++;
         oa = nx;
@@ -1389,22 +1462,25 @@ __device__ __forceinline__ void store_flat(const Ctx& C, StoreState& ss, int ste
         nx = a + 1 < W ? offs[a + 1] : 0x7fffffff;
       }
       const int64_t pos4 = sa + (i - oa);
-      d = (int64_t)(p * W + a) * ld4 + pos4;
-      sidx = (int64_t)(q * W + ka) * ld4 + pos4;
+      return Piece{(int64_t)(p * W + a) * ld4 + pos4, (int64_t)(q * W + ka) * ld4 + pos4};
     };
-    // four pieces per lane in flight before any is stored (pieces past the
-    // end stand on the last one and are not stored)
-    for (int i0 = lane; i0 < total; i0 += 4 * kWave) {
-      int64_t d0, s0, d1, s1, d2, s2, d3, s3;
-      locate(i0, d0, s0);
-      locate(min(i0 + kWave, total - 1), d1, s1);
-      locate(min(i0 + 2 * kWave, total - 1), d2, s2);
-      locate(min(i0 + 3 * kWave, total - 1), d3, s3);
-      const int4 v0 = c4[s0], v1 = c4[s1], v2 = c4[s2], v3 = c4[s3];
-      c4[d0] = v0;
-      if (i0 + kWave < total) c4[d1] = v1;
-      if (i0 + 2 * kWave < total) c4[d2] = v2;
-      if (i0 + 3 * kWave < total) c4[d3] = v3;
+    // eight pieces per lane in flight before any is stored (pieces past the
+    // end stand on the last one and are not stored; with the lists in global
+    // memory each round is one memory round trip)
+    for (int i0 = lane; i0 < total; i0 += 8 * kWave) {
+      auto at = [&](int u) { return locate(min(i0 + u * kWave, total - 1)); };
+      const Piece p0 = at(0), p1 = at(1), p2 = at(2), p3 = at(3), p4 = at(4), p5 = at(5),
+                  p6 = at(6), p7 = at(7);
+      const int4 v0 = c4[p0.s], v1 = c4[p1.s], v2 = c4[p2.s], v3 = c4[p3.s], v4 = c4[p4.s],
+                 v5 = c4[p5.s], v6 = c4[p6.s], v7 = c4[p7.s];
+      c4[p0.d] = v0;
+      if (i0 + kWave < total) c4[p1.d] = v1;
+      if (i0 + 2 * kWave < total) c4[p2.d] = v2;
+      if (i0 + 3 * kWave < total) c4[p3.d] = v3;
+      if (i0 + 4 * kWave < total) c4[p4.d] = v4;
+      if (i0 + 5 * kWave < total) c4[p5.d] = v5;
+      if (i0 + 6 * kWave < total) c4[p6.d] = v6;
+      if (i0 + 7 * kWave < total) c4[p7.d] = v7;
     }
     wave_sync();  // the copies land before the labels written below
   }
@@ -1740,9 +1816,10 @@ __device__ __forceinline__ void write_outputs(const Ctx& C, const Beam& b, int p
 }
 
 // ---------------------------------------------------------- state helpers --
-__device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
+// The beam arrays at `a` into registers (lanes past the fused decoder's beams
+// hold the dead state); A is left for the caller.
+__device__ __forceinline__ void beam_read(const char* a, int blank, Beam& b) {
   const int lane = lane_id();
-  const char* a = C.base + C.L.o_beam;
   if (lane < kMaxBeam) {
     b.pb = reinterpret_cast<const float*>(a + BeamArrays::pb)[lane];
     b.pnb = reinterpret_cast<const float*>(a + BeamArrays::pnb)[lane];
@@ -1754,17 +1831,21 @@ __device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
     b.live = reinterpret_cast<const int*>(a + BeamArrays::live)[lane];
     b.h = reinterpret_cast<const uint32_t*>(a + BeamArrays::hash)[lane];
     b.hp = reinterpret_cast<const uint32_t*>(a + BeamArrays::phash)[lane];
-    b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
   } else {
     b.live = 0;
     b.pb = b.pnb = b.score = kNeg;
     b.len = 0;
-    b.last = C.L.blank;
+    b.last = blank;
     b.parent = b.last2 = -1;
     b.h = kHashEmpty;
     b.hp = 0;
-    b.A = kNeg;
   }
+  b.A = kNeg;
+}
+
+__device__ __forceinline__ void beam_load(const Ctx& C, Beam& b) {
+  beam_read(C.base + C.L.o_beam, C.L.blank, b);
+  b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
 }
 
 __device__ __forceinline__ void beam_store(const Ctx& C, const Beam& b) {
@@ -1843,22 +1924,6 @@ __device__ __forceinline__ Ctx make_ctx(const Layout& L, const LdsPlan& S, int N
   return C;
 }
 
-// dst[i] = src[i] for i < n by one wave, four loads per lane in flight before
-// their stores.
-template <typename D, typename S>
-__device__ __forceinline__ void wave_copy(D* dst, const S* src, int n) {
-  const int lane = lane_id();
-  for (int i = lane; i < n; i += 4 * kWave) {
-    const int j1 = i + kWave, j2 = i + 2 * kWave, j3 = i + 3 * kWave;
-    const S v0 = src[i], v1 = src[min(j1, n - 1)], v2 = src[min(j2, n - 1)],
-            v3 = src[min(j3, n - 1)];
-    dst[i] = (D)v0;
-    if (j1 < n) dst[j1] = (D)v1;
-    if (j2 < n) dst[j2] = (D)v2;
-    if (j3 < n) dst[j3] = (D)v3;
-  }
-}
-
 // Paged metadata: global row region <-> LDS.
 __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
   const Layout& L = C.L;
@@ -1881,42 +1946,6 @@ __device__ __forceinline__ void paged_meta_io(const Ctx& C, bool to_lds) {
     wave_copy(gl, C.tail, nl);
     wave_copy(gn, C.tlen, 2 * kMaxBeam);
   }
-}
-
-__device__ __forceinline__ void clist_io(const Ctx& C, const Beam& b, int parity, bool to_lds) {
-  // The live rows' tokens as one flat list of 16-byte pieces (rows start
-  // 16-byte aligned: ldc is a multiple of 4), eight pieces per lane in flight
-  // before any is stored.
-  const Layout& L = C.L;
-  const int lane = lane_id();
-  int4* g4 = reinterpret_cast<int4*>(C.base + L.o_clist);
-  int4* s4 = reinterpret_cast<int4*>(C.clist);
-  const int64_t ld4 = L.ldc >> 2;
-  const bool lv = lane < L.W && b.live;
-  const int n4 = lv ? (b.len + 3) >> 2 : 0;
-  const int incl = wave_incl_scan(n4);
-  const int total = __shfl(incl, 63, 64);
-  int* offs = C.offs;   // first piece of each row
-  offs[lane] = incl - n4;
-  lds_sync();
-  int r = 0;   // row of this lane's current piece (pieces only move forward)
-  auto where = [&](int i) -> int64_t {
-    i = min(i, total - 1);
-    while (r + 1 < L.W && offs[r + 1] <= i) r++;
-    return (int64_t)(parity * L.W + r) * ld4 + (i - offs[r]);
-  };
-  for (int i0 = lane; i0 < total; i0 += 4 * kWave) {
-    const int64_t a0 = where(i0), a1 = where(i0 + kWave), a2 = where(i0 + 2 * kWave),
-                  a3 = where(i0 + 3 * kWave);
-    const int4* src = to_lds ? g4 : s4;
-    int4* dst = to_lds ? s4 : g4;
-    const int4 v0 = src[a0], v1 = src[a1], v2 = src[a2], v3 = src[a3];
-    dst[a0] = v0;
-    if (i0 + kWave < total) dst[a1] = v1;
-    if (i0 + 2 * kWave < total) dst[a2] = v2;
-    if (i0 + 3 * kWave < total) dst[a3] = v3;
-  }
-  lds_sync();
 }
 
 // Header fields <-> LDS scalars.
@@ -2050,6 +2079,27 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   auto slot_rank = [&](int sl) { return reinterpret_cast<int8_t*>(smem + lds::end + sl * S.slot_stride + S.slot_rank); };
 
   const int step_in = STREAM ? hdr[kStep] : 0;
+  // wave roles: 0 beam; with 5 or more waves the light loader shares SIMD 0
+  // with the beam wave (waves are spread over the 4 SIMDs in order)
+  const int nwaves = 3 + nprod;
+  const int store_wave = nwaves >= 5 ? 3 : 2;
+  const int loader_wave = nwaves >= 5 ? 4 : 3;
+  const int pid = wave == 1 ? 0 : (wave == 2 && nwaves >= 5 ? 1 : wave - 3);
+  const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
+  const int64_t stride_t = P.stride_t;
+  const int vec4 = P.vec4;
+  // streaming: the beam wave reads the stream's header words and beam state,
+  // and the loader fetches the chunk's first frame into slot 0 (without a
+  // speech mask step 0 decodes chunk frame 0), while the set-up below runs:
+  // these loads overlap the header read instead of following it
+  int hv = 0;   // lane i < 16: header word i
+  Beam bin;
+  if (STREAM && wave == 0) {
+    hv = lane < 16 ? hdr[lane] : 0;
+    beam_read(base + L.o_beam, L.blank, bin);
+  }
+  const bool early_row = STREAM && P.speech == nullptr && wave == loader_wave;
+  if (early_row) row_fetch_async(lp_row, slot_row(0), V, vec4);
   // set-up shared by all waves: empty label ranks, flags
   for (int sl = 0; sl < nslot; sl++)
     for (int c = (int)threadIdx.x; c < V; c += (int)blockDim.x) slot_rank(sl)[c] = -1;
@@ -2085,9 +2135,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   } else {
     nframes = hdr[kNSel];
   }
-  const float* lp_row = P.lp + (int64_t)(STREAM ? row_i : srow) * P.stride_b;
-  const int64_t stride_t = P.stride_t;
-  const int vec4 = P.vec4;
   // ranked labels per frame: 2W + 3, at most 40, so that the labels gathered
   // to rank them mostly fit one per lane.  Any step where a label outside the
   // list could still compete is detected and decoded by the full beam x vocab
@@ -2095,13 +2142,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   const int K = min(V - 1, min(2 * W + 3, kMaxRanked));
   const int complete = K == V - 1;
   __syncthreads();
-
-  // wave roles: 0 beam; with 5 or more waves the light loader shares SIMD 0
-  // with the beam wave (waves are spread over the 4 SIMDs in order)
-  const int nwaves = 3 + nprod;
-  const int store_wave = nwaves >= 5 ? 3 : 2;
-  const int loader_wave = nwaves >= 5 ? 4 : 3;
-  const int pid = wave == 1 ? 0 : (wave == 2 && nwaves >= 5 ? 1 : wave - 3);
 
   if (wave == loader_wave) {
     // ------------------------------------------------------------ loader
@@ -2148,7 +2188,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
         cur = c + 1;
       }
       const int t = STREAM ? frame0 + c : sel[f];
-      row_fetch_async(lp_row + (int64_t)(STREAM ? c : t) * stride_t, slot_row(sl), V, vec4);
+      if (!(early_row && f == 0))   // (frame 0 of an unmasked chunk is on its way)
+        row_fetch_async(lp_row + (int64_t)(STREAM ? c : t) * stride_t, slot_row(sl), V, vec4);
       if (lane == 0) frame_t[sl] = t;
       row_fetch_wait();
       flag_publish_lds(&loaded[sl], f);
@@ -2160,6 +2201,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       }
 #endif
     }
+    if (early_row) row_fetch_wait();   // the early fetch has landed, even if unused
 #ifdef CTCPB_PHASE_PROF
     // (offline: the row region's beam arrays are unused, they take the counters)
     if (!STREAM && lane == 0) {
@@ -2222,6 +2264,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
     // ---------------------------------------------------------- store wave
     C.offs = reinterpret_cast<int*>(smem + lds::soffs);
     StoreState ss{};
+    store_state_init(C, ss, STREAM);
 #ifdef CTCPB_PHASE_PROF
     for (int i = 0; i < 4; i++) C.sprof[i] = 0;
 #endif
@@ -2257,16 +2300,18 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
       const int nlen = w.valid ? w.len_k + (w.c != L.blank ? 1 : 0) : 0;
       // (the beam wave's set-up of the LDS state is visible once its first
       // step is published)
-      if (f == 0) ss = store_state_load(C);
+      if (f == 0) store_state_load(C, ss);
       if (step == 0) {
         store_seed(C, ss, w);
       } else if (L.paged) {
         store_paged(C, ss, step, w, nlive, nlen);
       } else {
         store_flat(C, ss, step, w);
-        if ((step & 15) == 15) advance_cpl_flat(C, ss, step & 1, nlive, nlen);
+        // (every 16 steps, mid-way through a 16-frame stream chunk: its reads
+        // of the lists in global memory would otherwise delay the chunk's end)
+        if ((step & 15) == 7) advance_cpl_flat(C, ss, step & 1, nlive, nlen);
       }
-      if (f == nframes - 1) store_state_save(C, ss);
+      if (f == nframes - 1) store_state_save(C, ss, STREAM);
       // the ring entry is free again (its LDS state is written); the token
       // writes may still be in flight
       flag_publish_lds(wdone, step);
@@ -2299,15 +2344,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   int step, last_t;
   if (STREAM) {
     step = step_in;
-    last_t = hdr[kLastT];
+    last_t = __builtin_amdgcn_readlane(hv, kLastT);
     scal_from_header(C);
-    beam_load(C, b);
+    b = bin;
+    b.A = b.live ? lse(b.pb, b.pnb) : kNeg;
     if (L.paged) paged_meta_io(C, true);
-    if (S.clist_lds && step > 0) {
-      clist_io(C, b, (step - 1) & 1, true);
-      // the other parity was not kept: its rows must be rewritten in full
-      if (lane == 0) C.scal[kScalLive0 + (step & 1)] = 0;
-    }
   } else {
     step = 0;
     last_t = -1;
@@ -2419,10 +2460,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel(Params P) {
   if (STREAM) {
     beam_store(C, b);
     if (L.paged) paged_meta_io(C, false);
-    if (S.clist_lds && step > 0) {
-      wave_sync();
-      clist_io(C, b, (step - 1) & 1, false);
-    }
     scal_to_header(C, step, last_t, STREAM ? frame0 + P.T : -1);
   } else {
     wave_sync();
@@ -2448,6 +2485,12 @@ __global__ __launch_bounds__(64) void stream_fresh_kernel(Params P) {
   Beam b;
   beam_fresh(b, L.blank);
   beam_store(C, b);
+  if (!L.paged && L.W <= kMaxBeam) {
+    // the token store's kept state: no lineage, all-zero common-prefix bounds
+    int* a = reinterpret_cast<int*>(base + L.o_sst);
+    for (int i = lane; i < (int)(StoreArrays::bytes / 4); i += kWave)
+      a[i] = i < (int)(StoreArrays::mat / 4) ? -1 : 0;
+  }
   if (L.W > kMaxBeam) {
     // the wide decoder's kept state: the empty hypothesis in slot 0, every
     // other slot dead, no token rows written yet
@@ -2616,14 +2659,17 @@ LdsPlan plan_lds_with(const Layout& L, int nprod, int spare, bool clist_lds) {
 // V while the beam recursion does not), as many as the LDS budget allows, and
 // up to three frame slots beyond one per producer so that the loader can run
 // ahead (a slot is held from its load until the beam wave has used it).
-LdsPlan plan_lds(const Layout& L) {
+// Flat token lists go to LDS only for offline decodes (`lists_in_lds`): a
+// stream's lists persist in its state, and copying the live rows in and out
+// around every chunk costs more than the faster copies inside it save.
+LdsPlan plan_lds(const Layout& L, bool lists_in_lds) {
   // four producer waves whenever they fit: ranking costs about the same per
   // frame at any vocabulary (its threshold search and sort are fixed work),
   // so small vocabularies need as many producers as large ones
   const int pref = 4;
   // flat token lists in LDS if they fit next to at least one producer
   for (int lds_clist = 1; lds_clist >= 0; lds_clist--) {
-    if (lds_clist && L.paged) continue;
+    if (lds_clist && (L.paged || !lists_in_lds)) continue;
     for (int nprod = pref; nprod >= 1; nprod--) {
       for (int spare = 3; spare >= 1; spare--) {
         if (nprod + spare > kMaxSlots) continue;
@@ -2695,13 +2741,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Whether the decoder can hold a row of this layout on one CU (the checks the
 // decode and stream calls make before launching).
-int check_fits(const Resolved& R, const Layout& L) {
+int check_fits(const Resolved& R, const Layout& L, bool stream) {
   if (R.W > kMaxBeam) {
     if (wide::lds_bytes(R.V, 1) > kLdsLimit)
       return fail(CTCPB_ERR_UNSUPPORTED, "vocabulary too wide for the wide-beam decoder");
     return CTCPB_OK;
   }
-  return check_lds(L, plan_lds(L));
+  return check_lds(L, plan_lds(L, !stream));
 }
 
 }  // namespace
@@ -2719,7 +2765,7 @@ int ctcpb_workspace_size(const ctcpb_config* cfg, int32_t batch, int32_t max_T,
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (batch < 0 || max_T < 0) return fail(CTCPB_ERR_INVALID, "batch and max_T must be >= 0");
   const Layout L = layout_for(R, max_T > 0 ? max_T : 1, max_T);
-  if (int rc = check_fits(R, L)) return rc;
+  if (int rc = check_fits(R, L, false)) return rc;
   *out_bytes = (size_t)batch * (size_t)L.row_bytes;
   return ok();
 }
@@ -2730,7 +2776,7 @@ int ctcpb_state_size(const ctcpb_config* cfg, int32_t num_streams, size_t* out_b
   if (!out_bytes) return fail(CTCPB_ERR_INVALID, "out_bytes is NULL");
   if (num_streams < 0) return fail(CTCPB_ERR_INVALID, "num_streams must be >= 0");
   const Layout L = layout_for(R, R.cap_stream, 0);
-  if (int rc = check_fits(R, L)) return rc;
+  if (int rc = check_fits(R, L, true)) return rc;
   *out_bytes = (size_t)num_streams * (size_t)L.row_bytes;
   return ok();
 }
@@ -2775,7 +2821,7 @@ int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t 
   Params P{};
   P.L = L;
   if (!wide_path) {
-    P.S = plan_lds(L);
+    P.S = plan_lds(L, true);
     if (int rc = check_lds(P.L, P.S)) return rc;
   } else {
     // two frame rows in LDS when they fit (the next frame is fetched ahead)
@@ -2951,7 +2997,7 @@ int ctcpb_stream_chunk_ex(const ctcpb_config* cfg, void* state, size_t state_byt
   P.L = L;
   const bool wide_path = R.W > kMaxBeam;
   if (!wide_path) {
-    P.S = plan_lds(L);
+    P.S = plan_lds(L, false);
     if (int rc = check_lds(P.L, P.S)) return rc;
   } else {
     P.S.nslot = wide::lds_bytes(R.V, 2) <= kLdsLimit ? 2 : 1;
@@ -3019,7 +3065,7 @@ int ctcpb_read_state(const ctcpb_config* cfg, const void* state, size_t state_by
     return fail(CTCPB_ERR_TOO_SMALL, "state smaller than ctcpb_state_size");
   Params P{};
   P.L = L;
-  P.S = plan_lds(L);
+  P.S = plan_lds(L, false);
   P.N = R.N;
   P.max_out_len = R.mol;
   P.num_rows = num_streams;

@@ -12,7 +12,8 @@
 //               wide decoder's beam state
 //   sel         cap_sel x int32     offline: selected frame indices
 //   flat:       clist[2][beam][ldc] int32 tokens, double-buffered by parity
-//               (ldc = cap rounded up to a multiple of 4)
+//               (ldc = cap rounded up to a multiple of 4); beams up to 32: the
+//               token store's lineage and common-prefix bounds (StoreArrays)
 //   paged:      table[2][beam][max_lp] int32 page ids (-1 none),
 //               refcount[num_pages], free stack[num_pages],
 //               pages[num_pages][page_size] int32 tokens,
@@ -74,6 +75,7 @@ struct Layout {
   int64_t row_bytes;
   int64_t o_beam, o_sel, o_clist, o_tab, o_ref, o_free, o_pages, o_tail, o_tlen;
   int64_t o_wide;   // beams above kMaxBeam: the wide decoder's beam state (WideArray)
+  int64_t o_sst;    // flat lists, beams up to kMaxBeam: the store wave's kept state (StoreArrays)
 };
 
 // Beam arrays inside a row region (offsets from o_beam).
@@ -81,6 +83,18 @@ struct BeamArrays {
   static constexpr int64_t pb = 0, pnb = 128, score = 256, len = 384, last = 512,
                            parent = 640, last2 = 768, live = 896, hash = 1024, phash = 1152,
                            bytes = 1280;
+};
+
+// The token store's state kept between the chunks of a stream (flat lists,
+// beams up to kMaxBeam), offsets from o_sst: per parity and slot the row's
+// length (-1 unknown), the source slot of its last fork and the label that
+// fork appended (-1 none), as int arrays [2][kMaxBeam]; then per parity the
+// W x W matrix of lower bounds on the common prefix of two rows (int16, row
+// stride W, kMaxBeam^2 entries reserved each).
+struct StoreArrays {
+  static constexpr int64_t len = 0, src = 2 * kMaxBeam * 4, lab = 4 * kMaxBeam * 4,
+                           mat = 6 * kMaxBeam * 4, mat_bytes = kMaxBeam * kMaxBeam * 2,
+                           bytes = mat + 2 * mat_bytes;
 };
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -111,6 +125,8 @@ inline Layout make_layout(int W, int V, int blank, int cap, int paged, int ps, i
   if (!paged) {
     L.o_clist = off;
     off += align256((int64_t)2 * W * L.ldc * 4);
+    L.o_sst = off;
+    if (W <= kMaxBeam) off += align256(StoreArrays::bytes);
   } else {
     L.o_tab = off;
     off += align256((int64_t)2 * W * L.max_lp * 4);
