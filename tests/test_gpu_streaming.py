@@ -360,3 +360,49 @@ def test_masked_chunks_take_the_exact_selection_from_the_flagged_frame(paged):
     assert st[:, cpb.STAT_FIELDS.index("fallbacks")].sum() > 0, "no step took the full selection"
     ref, _ = oracle_masked(lp, mask, W, 4096, CH, W, T)
     assert_parity(got, ref, what="stream masked uniform")
+
+
+def test_long_streams_with_reordering_beams_and_uneven_chunks():
+    # ambiguous frames make the beams change lineage often, so the flat store
+    # copies rows on many steps; uneven chunks move the chunk boundaries (where
+    # the store's lineage and common-prefix bounds are saved and reloaded)
+    # across every phase of its 16-step prefix advance; one stream is reset
+    # halfway and restarted on another stream's frames
+    S, T, V, W = 6, 320, 64, 10
+    lp, _ = synth.peaky(S, T, V, seed=41, p_blank=0.5, token_bias=(0.5, 3.0), p_low=0.3)
+    sched = [5, 11, 3, 16, 7, 1, 9, 13, 2, 17]
+    cuts, a = [], 0
+    while a < T:
+        b = min(T, a + sched[len(cuts) % len(sched)])
+        cuts.append((a, b))
+        a = b
+    print(f"[case] long streams S={S} T={T} V={V} W={W} chunks={len(cuts)}", flush=True)
+    cfg = cpb.DecoderConfig(beam=W, nbest=W, capacity=4096, max_out_len=T)
+    pool = cpb.StreamPool(cfg, V, S)
+    x = torch.from_numpy(lp).cuda()
+    half = len(cuts) // 2
+    for i, (a, b) in enumerate(cuts):
+        if i == half:
+            pool.reset(torch.tensor([2], dtype=torch.int32, device="cuda"))
+        pool.chunk(x[:, a:b])
+    got = read(pool)
+    # stream 2 decoded frames [cuts[half][0], T) only
+    t0 = cuts[half][0]
+    refs = []
+    for s in range(S):
+        st = oracle.Stream(W, V, 0, 4096)
+        for i, (a, b) in enumerate(cuts):
+            if s == 2 and i < half:
+                continue
+            st.feed(lp[s, a:b])
+        refs.append(st.read(W, T))
+    ref = tuple(np.stack([r[i] for r in refs]) for i in range(3))
+    assert_parity(got, ref, what="long streams")
+    keep = [s for s in range(S) if s != 2]
+    off = gpu_offline(lp[keep], np.full(len(keep), T, np.int32), W, W, 0, 1.0, T)
+    for g, o in zip(got, off):
+        assert np.array_equal(g[keep], o)
+    off2 = gpu_offline(np.ascontiguousarray(lp[2:3, t0:]), np.array([T - t0], np.int32), W, W, 0,
+                       1.0, T)
+    for g, o in zip(got, off2):
+        assert np.array_equal(g[2:3], o)
