@@ -1126,8 +1126,8 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   const uint64_t t1 = shi > o1 ? shi : o1;
   const uint64_t mid = shi > o1 ? o1 : shi, lo2 = slo > o2 ? slo : o2;
   const uint64_t t2 = mid > lo2 ? mid : lo2;
-  // the beam's third candidate (its lists are sorted, so all later ones are
-  // below it); ranked labels past the list are bounded separately below
+  // the beam's third candidate (its lists are sorted, so no later one scores
+  // above it); ranked labels past the list are bounded separately below
   const uint64_t n3 = slo > o1 ? o1 : (shi > o2 ? lo2 : (shi > o3 ? shi : o3));
   PROF_MARK(9);
   // beam j's best goes to lane j, its second best to lane j + NB / 2 (one
@@ -1136,27 +1136,33 @@ __device__ __forceinline__ Winner beam_step(Ctx& C, Beam& b, const float* row, i
   // branch: a lane that is switched off supplies no value to the exchange)
   //
   // Usually the sort is not needed: when each beam's best candidate ranks in
-  // beam order (beam j's above beam j + 1's) and no beam's second candidate
-  // beats the last beam's best, the top W are exactly the beams' best
+  // beam order (beam j's above beam j + 1's) and every beam's second candidate
+  // scores below the last beam's best, the top W are exactly the beams' best
   // candidates, already in rank order (nonzero keys are distinct, and beams
   // without a candidate hold 0, so t1[j] >= t1[j + 1] means "in order").
+  //
+  // Both checks on the candidates left out compare scores (the keys' upper 32
+  // bits), not whole keys: a later label whose score rounds to the same value
+  // as an earlier one's outranks it when its id is smaller, so only a strictly
+  // lower score bounds the labels that follow a beam's first ones.
+  constexpr uint64_t kScoreBits = 0xffffffff00000000ull;
   const uint64_t t1_next = wave_shl1_u64(t1);   // lane j: t1 of lane j + 1 (0 past the end)
   const uint64_t c1W = readlane_u64(t1, W - 1);
   const bool in_order = __ballot(t1 < t1_next) == 0ull;
-  const bool no_second = __ballot((t2 != 0ull) & (t2 > c1W)) == 0ull;
+  const bool no_second = __ballot((t2 != 0ull) & (t2 >= (c1W & kScoreBits))) == 0ull;
   uint64_t top, cW;
   bool exact;
   if (__builtin_expect(in_order & no_second, 1)) {
     top = t1;
     cW = c1W;
-    exact = true;   // every third candidate is below its beam's second
+    exact = true;   // every later candidate scores below its beam's second
   } else {
     constexpr int H = NB / 2;
     const uint64_t t2x = xor_lane_u64<H>(t2);
     top = wave_sort_blocks_desc<NB>(
         __builtin_amdgcn_inverse_ballot_w64(lanes_below_n(H)) ? t1 : t2x);
     cW = readlane_u64(top, W - 1);
-    exact = __ballot(n3 > cW) == 0ull;
+    exact = __ballot((n3 != 0ull) & (n3 >= (cW & kScoreBits))) == 0ull;
   }
   PROF_MARK(3);
   uint64_t wc;  // winner of slot `lane` (composite key, 0 = none)

@@ -183,6 +183,30 @@ __device__ __forceinline__ void rank_keys(const uint64_t* keys, int n, uint64_t*
   }
 }
 
+// The run of ranks whose score A + Rl[r] rounds to that of rank r (the
+// scores do not increase with the rank): its first rank, and one past its last
+// (at most `end`), by binary search.
+__device__ __forceinline__ int tie_run_start(float A, const float* Rl, int r) {
+  const float key = A + Rl[r];
+  int lo = 0, hi = r;   // first rank in [0, r] whose score is not above key
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (A + Rl[mid] > key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int tie_run_end(float A, const float* Rl, int r, int end) {
+  const float key = A + Rl[r];
+  int lo = r + 1, hi = end;   // first rank in (r, end) whose score is below key
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (A + Rl[mid] < key) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
 // The 64 largest of the keys keys[0, n) (n <= 256; missing ones count as 0)
 // in descending order, returned in wave 0's lanes (other waves: unspecified).
 // Each of the first ceil(n / 64) waves sorts a chunk of 64 (odd chunks
@@ -715,26 +739,49 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     __syncthreads();
     // each beam's best candidate, its first two open ranks, and the sample
     // (both slots and those two ranks of every beam) whose W-th largest key
-    // bounds the W-th largest candidate from below
+    // bounds the W-th largest candidate from below; n3: the score of the
+    // beam's third open rank (no later label of the beam scores above it)
+    float n3 = kNeg;
     if (tid < W) {
       const int k = tid;
       const bool lv = s_live[k] != 0;
       if (s_exc[k]) s_kc[k] = kNeg;
       const float kb = s_kb[k], kc = s_exc[k] ? kNeg : s_kc[k];
-      uint64_t cb = 0ull, cc = 0ull, o0 = 0ull, o1 = 0ull;
+      uint64_t cb = 0ull, cc = 0ull, o0 = 0ull, o1 = 0ull, ob = 0ull;
       if (lv) {
         cb = kb > kNeg ? compose(kb, (uint32_t)((k << kIdShift) | blank)) : 0ull;
         cc = kc > kNeg ? compose(kc, (uint32_t)((k << kIdShift) | s_last[k])) : 0ull;
-        int r0 = -1, r1 = -1;
-        for (int w = 0; w < kExw && r1 < 0; w++) {
+        int r0 = -1, r1 = -1, r2 = -1;
+        for (int w = 0; w < kExw && r2 < 0; w++) {
           uint32_t open = ~s_exm[k * kExw + w];
-          while (open && r1 < 0) {
+          while (open && r2 < 0) {
             const int r = w * 32 + __ffs((int)open) - 1;
             open &= open - 1u;
             if (r >= K) break;
             if (r0 < 0) r0 = r;
-            else r1 = r;
+            else if (r1 < 0) r1 = r;
+            else r2 = r;
           }
+        }
+        if (r2 >= 0) n3 = s_A[k] + Rl[r2];
+        // the beam's best ordinary candidate (for its place among the beams'
+        // bests): the first open rank, unless a later open rank whose score
+        // rounds to the same value has a smaller label and outranks it (only
+        // where the run of that score holds different log-probabilities: in a
+        // run of equal ones the labels already ascend)
+        int rb = r0;
+        if (r0 >= 0) {
+          const float A = s_A[k], kr0 = A + Rl[r0];
+          if (r0 + 1 < K && A + Rl[r0 + 1] == kr0) {
+            const int re = tie_run_end(A, Rl, r0, K);
+            if (Rl[re - 1] != Rl[r0]) {
+              for (int r = r0 + 1; r < re; r++) {
+                const bool ex = (s_exm[k * kExw + (r >> 5)] >> (r & 31)) & 1u;
+                if (!ex && Rc[r] < Rc[rb]) rb = r;
+              }
+            }
+          }
+          ob = kr0 > kNeg ? compose(kr0, (uint32_t)((k << kIdShift) | Rc[rb])) : 0ull;
         }
         if (r0 >= 0) {
           const float key = s_A[k] + Rl[r0];
@@ -746,32 +793,73 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         }
       }
       const uint64_t b1 = cb > cc ? cb : cc;
-      s_head[k] = b1 > o0 ? b1 : o0;
+      s_head[k] = b1 > ob ? b1 : ob;
       cbuf[4 * k + 0] = cb;
       cbuf[4 * k + 1] = cc;
       cbuf[4 * k + 2] = o0;
       cbuf[4 * k + 3] = o1;
     }
+    if (tid == 0) {
+      sh[4] = 0;
+      sh[15] = 0;
+    }
     __syncthreads();
     // tau: the W-th largest of the 4W sample keys (0 when fewer are nonzero)
     uint64_t tau;
+    bool fast = false;   // set when the sample's best W are the winners
     if (W <= 64) {
       const uint64_t top = block_top64(cbuf, 4 * W, cbuf + kCBuf - 384);
       if (wave == 0) {
+        // (beams up to 64: all in this wave) when every beam's third open rank
+        // scores strictly below the W-th sample key, so does every candidate
+        // outside the sample (a later label whose score rounds to the same
+        // value may outrank it by id, hence the strict score bound), and the
+        // sample's best W, sorted, are the winners
         const uint64_t tw = readlane_u64(top, W - 1);
-        if (tid == 0) reinterpret_cast<unsigned long long*>(sh + 12)[0] = tw;
+        const float twk = tw != 0ull ? comp_key(tw) : -__builtin_inff();
+        const bool exact = __ballot(tid < W && n3 > kNeg && !(n3 < twk)) == 0ull;
+        if (exact) {
+          if (tid < W) win[tid] = top;
+          const int cnt = __popcll(__ballot(tid < W && top != 0ull));
+          if (tid == 0) sh[4] = cnt;
+        }
+        if (tid == 0) {
+          reinterpret_cast<unsigned long long*>(sh + 12)[0] = tw;
+          sh[15] = exact ? 0 : 1;
+        }
       }
       __syncthreads();
       tau = reinterpret_cast<unsigned long long*>(sh + 12)[0];
+      fast = sh[15] == 0;
     } else {
       tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
+      // the same test with the beams in two waves; when it holds, the sample
+      // keys at or above the W-th are the winners (ranked below)
+      const float twk = tau != 0ull ? comp_key(tau) : -__builtin_inff();
+      if (tid < W && n3 > kNeg && !(n3 < twk)) sh[15] = 1;
+      __syncthreads();
+      fast = sh[15] == 0;
+      if (fast) {
+        const uint64_t lo = tau != 0ull ? tau : 1ull;
+        for (int i = tid; i < 4 * W; i += kNT) {
+          const uint64_t x = cbuf[i];
+          if (x >= lo) kb64[atomicAdd(&sh[4], 1)] = x;
+        }
+        __syncthreads();
+      }
     }
-    if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
-    const float tau_key = comp_key(tau);
+    int nw;
+    bool ranked = false;   // win[0, nw) already holds the winners in rank order
+    if (fast) {
+      nw = sh[4];
+      ranked = W <= 64;
+    } else {
     // each live beam's place h - 1 among the beams' bests (in s_lim until the
     // beam overwrites it below)
     rank_keys(s_head, W, kb64, [&](int r, uint64_t x) { s_lim[comp_id(x) >> kIdShift] = r; });
     __syncthreads();
+    if (tau == 0ull) tau = 1ull;   // fewer than W in the sample: no bound
+    const float tau_key = comp_key(tau);
     // per beam: open ranks considered (at most W - h + 1 open ones when its
     // best is the h-th best of the beams), and the leading ones whose key
     // reaches the bound
@@ -818,9 +906,27 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
           }
           lim = fbase + pos + 1;
         }
+        const float A = s_A[k];
+        // a label past the last one considered whose score rounds to the same
+        // value outranks the considered labels of that score with larger ids:
+        // the limit moves past the last such label (in a run of equal
+        // log-probabilities the ids already ascend, and nothing moves)
+        if (lim < K) {
+          const float kl = A + Rl[lim - 1];
+          if (kl > kNeg && A + Rl[lim] == kl) {
+            const int rs = tie_run_start(A, Rl, lim - 1), re = tie_run_end(A, Rl, lim - 1, K);
+            if (Rl[rs] != Rl[re - 1]) {
+              int lmax = Rc[lim - 1];
+              for (int i = rs; i < lim - 1; i++) lmax = max(lmax, Rc[i]);
+              int nl = lim;
+              for (int i = lim; i < re; i++)
+                if (Rc[i] < lmax) nl = i + 1;
+              lim = nl;
+            }
+          }
+        }
         // keys A + Rl[r] do not increase with r: binary search of the first
         // rank below the bound
-        const float A = s_A[k];
         int lo = 0, hi = lim;
         if (tau > 1ull) {
           while (lo < hi) {
@@ -852,8 +958,6 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     }
     __syncthreads();
     const int nsurv = sh[3];
-    int nw;
-    bool ranked = false;   // win[0, nw) already holds the winners in rank order
     if (nsurv <= kCBuf) {
       // ---- top W (sec. 3.4.4 / 3.4.5) among the candidates at or above the
       // bound, each beam writing its own
@@ -1014,6 +1118,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       __syncthreads();
       nw = sh[4];
     }
+    }   // (not fast)
     if (!ranked) rank_keys(kb64, nw, cbuf, [&](int r, uint64_t x) { win[r] = x; });
     if (tid < kMaxW) s_bslot[tid] = -1;
     __syncthreads();

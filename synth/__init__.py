@@ -118,6 +118,29 @@ def peaky_device(B: int, T: int, V: int, seed: int, device, p_blank: float = 0.6
     return out, lens
 
 
+def rounding_ties(V: int = 8, n_tied: int = 4, dtype=np.float32):
+    """Two frames (log_prob[1, 2, V]) built so that the second frame's best
+    extensions of the first frame's best prefix all round to one score.
+
+    Frame 0 makes the empty prefix score -1000 and the prefix [1] score
+    -1000.5.  In frame 1, labels 4, 5, 6, ... get -1.0 and the next floats
+    below it, and label 2 the float below those (n_tied labels in all): added
+    to -1000 (spacing 2^-14 there) they all give -1001.0.  So the label that
+    ranks last by log-probability has the smallest id among the tied
+    extensions.  Every other entry is far below.
+    """
+    lp = np.full((1, 2, V), -3000.0, dtype)
+    lp[0, 0, 0] = -1000.0
+    lp[0, 0, 1] = -1000.5
+    lp[0, 1, :] = -100.0 - np.arange(V, dtype=dtype)
+    x = np.float32(-1.0)
+    for c in list(range(4, 4 + n_tied - 1)) + [2]:
+        lp[0, 1, c] = x
+        x = np.nextafter(x, np.float32(-np.inf))
+    lp[0, 1, 0] = -60.0
+    return lp
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str

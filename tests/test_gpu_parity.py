@@ -251,3 +251,15 @@ def test_exact_selection_every_step_at_vocab5000():
     fb = gpu_offline.last_stats[:, cpb.STAT_FIELDS.index("fallbacks")]
     assert_parity(got, oracle.decode(lp, lens, W, W, 0, 1.0, T), what="uniform every step")
     assert (fb >= T // 4).all(), fb        # about a third of the steps
+
+
+@pytest.mark.parametrize("beam,V,n_tied,paged", [(2, 8, 4, False), (2, 8, 4, True), (3, 10, 5, False),
+                                                 (4, 12, 6, False), (8, 24, 12, False)])
+def test_rounding_ties_across_the_checked_candidates(beam, V, n_tied, paged):
+    # extensions whose sums round to one score rank by id, not by log-prob:
+    # the tie runs past the candidates each beam sends to the sort, so only a
+    # score-level bound on the ones left out keeps the selection exact
+    lp = synth.rounding_ties(V=V, n_tied=n_tied)
+    got, ref = run_both(lp, np.array([2], np.int32), beam, beam, paged=paged, what="rounding ties")
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)

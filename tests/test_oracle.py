@@ -605,3 +605,16 @@ def test_page_model_stream_equals_offline(oracle_lib):
         st.feed(lp[0, a:a + 7])
     off = oracle.decode_pages(lp, lens, 12, page_size=4)
     assert st.pages() == tuple(int(v) for v in off[0])
+
+
+def test_rounding_ties_rank_by_id(oracle_lib):
+    # frame 1 extends the empty prefix (score -1000) by labels 4, 5, 6 (log-prob
+    # -1.0 and the next floats below it) and 2 (the float below those): every
+    # sum rounds to -1001.0, so the candidates tie and rank by id, label 2
+    # first, although it ranks last by log-probability.  The best two are [2]
+    # and [4]; the prefix [1] (-1000.5) extends to -1001.5 at best.
+    lp = synth.rounding_ties()
+    assert {float(np.float32(-1000.0) + lp[0, 1, c]) for c in (2, 4, 5, 6)} == {-1001.0}
+    t, l, s = oracle_lib.decode(lp, np.array([2], np.int32), 2, 2, 0, 1.0, 2)
+    assert t[0, :, 0].tolist() == [2, 4] and l[0].tolist() == [1, 1]
+    assert s[0].tolist() == [-1001.0, -1001.0]
