@@ -238,6 +238,65 @@ __device__ __forceinline__ uint64_t block_top64(const uint64_t* keys, int n, uin
   return top;
 }
 
+// The 128 largest of keys[0, n) (n <= 512; missing ones count as 0) in
+// descending order, in wave 0's lanes: hi holds ranks 0-63, lo ranks 64-127
+// (other waves: unspecified).  Each wave orders a chunk of 128 (two keys per
+// lane: a run of 64 each way, which together are bitonic, then the merge's
+// cross stage and the last six stages on each half); waves 1 and 3 hand
+// their runs to waves 0 and 2 through tmp, which keep the 128 largest of the
+// two (the merge's first half-cleaner against the partner's run reversed,
+// then the same ordering); wave 2 hands its result to wave 0 for the last
+// merge.  Block-wide: every thread calls it; tmp (384 keys) must not overlap
+// keys.  Ends with wave 0 holding the result (no barrier after the merge).
+__device__ __forceinline__ uint64_t wave_bitonic64_desc(uint64_t v) {
+  v = bitonic_stage<64, 32>(v);
+  v = bitonic_stage<64, 16>(v);
+  v = bitonic_stage<64, 8>(v);
+  v = bitonic_stage<64, 4>(v);
+  v = bitonic_stage<64, 2>(v);
+  return bitonic_stage<64, 1>(v);
+}
+__device__ __forceinline__ void order128(uint64_t& h, uint64_t& l) {   // bitonic (h, l) -> desc
+  const uint64_t a = h > l ? h : l, b = h > l ? l : h;
+  h = wave_bitonic64_desc(a);
+  l = wave_bitonic64_desc(b);
+}
+__device__ __forceinline__ void block_top128(const uint64_t* keys, int n, uint64_t* tmp,
+                                             uint64_t& hi, uint64_t& lo) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int base = 128 * wave;
+  uint64_t h = base + lane < n ? keys[base + lane] : 0ull;
+  uint64_t l = base + 64 + lane < n ? keys[base + 64 + lane] : 0ull;
+  h = wave_sort64_desc<uint64_t>(h);
+  l = wave_sort64_asc(l);
+  order128(h, l);
+  // the 128 largest of (h, l) and a descending run y of 128 held in tmp:
+  // element i against y[127 - i]
+  auto keep128 = [&](const uint64_t* y) {
+    const uint64_t yh = y[127 - lane], yl = y[63 - lane];
+    uint64_t mh = h > yh ? h : yh, ml = l > yl ? l : yl;
+    order128(mh, ml);
+    h = mh;
+    l = ml;
+  };
+  if (wave & 1) {
+    tmp[(wave >> 1) * 128 + lane] = h;
+    tmp[(wave >> 1) * 128 + 64 + lane] = l;
+  }
+  __syncthreads();
+  if (!(wave & 1)) keep128(tmp + (wave >> 1) * 128);
+  if (wave == 2) {
+    tmp[256 + lane] = h;
+    tmp[256 + 64 + lane] = l;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    keep128(tmp + 256);
+    hi = h;
+    lo = l;
+  }
+}
+
 // The best K non-blank labels of a frame row by (lp desc, label asc) (sec.
 // 3.4.6): out(rank, label) once per rank r < K (K <= V - 1: at least K labels
 // have a nonzero key).  kb64: the gathered keys (kMaxK + 8); tmp: rank_keys'
@@ -832,27 +891,33 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       tau = reinterpret_cast<unsigned long long*>(sh + 12)[0];
       fast = sh[15] == 0;
     } else {
-      tau = kth_largest<2>(4 * W, W, [&](int i) { return cbuf[i]; }, khist, ksh);
-      // the same test with the beams in two waves; when it holds, the sample
-      // keys at or above the W-th are the winners (ranked below)
+      // beams of 65-128: the sample's best 128 in order, handed to the winners
+      // in advance (the slow path below overwrites them); the same test with
+      // the beams in two waves
+      uint64_t th = 0ull, tl = 0ull;
+      block_top128(cbuf, 4 * W, cbuf + kCBuf - 384, th, tl);
+      if (wave == 0) {
+        const uint64_t tw = readlane_u64(tl, W - 65);
+        win[tid] = th;   // (wave 0: tid is the lane)
+        if (64 + tid < W) win[64 + tid] = tl;
+        const int cnt = __popcll(__ballot(th != 0ull)) + __popcll(__ballot(64 + tid < W && tl != 0ull));
+        if (tid == 0) {
+          reinterpret_cast<unsigned long long*>(sh + 12)[0] = tw;
+          sh[4] = cnt;
+        }
+      }
+      __syncthreads();
+      tau = reinterpret_cast<unsigned long long*>(sh + 12)[0];
       const float twk = tau != 0ull ? comp_key(tau) : -__builtin_inff();
       if (tid < W && n3 > kNeg && !(n3 < twk)) sh[15] = 1;
       __syncthreads();
       fast = sh[15] == 0;
-      if (fast) {
-        const uint64_t lo = tau != 0ull ? tau : 1ull;
-        for (int i = tid; i < 4 * W; i += kNT) {
-          const uint64_t x = cbuf[i];
-          if (x >= lo) kb64[atomicAdd(&sh[4], 1)] = x;
-        }
-        __syncthreads();
-      }
     }
     int nw;
     bool ranked = false;   // win[0, nw) already holds the winners in rank order
     if (fast) {
       nw = sh[4];
-      ranked = W <= 64;
+      ranked = true;
     } else {
     // each live beam's place h - 1 among the beams' bests (in s_lim until the
     // beam overwrites it below)
