@@ -1223,19 +1223,25 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     }
     if (!paged) {
       // ---- tokens: row tid of parity p <- row k of parity q (+ c).  If row k
-      // was itself copied from slot tid one step earlier, slot tid's row of
-      // parity p already holds its first s_flen[p][tid] tokens.
-      // Otherwise, if slot tid was live two steps ago, its row already holds the
-      // tokens that every live row then shared.
-      int start = 0;
+      // was itself forked from slot tid one step earlier, slot tid's row of
+      // parity p already holds row k's tokens but (at most) the label that
+      // fork appended, the last one of row k: it is written directly, nothing
+      // is copied.  Otherwise, if slot tid was live two steps ago, its row
+      // already holds the tokens that every live row then shared.
+      int start = 0, dlab = -1;
+      bool direct = false;
       const int klen = k >= 0 ? s_len[k] : 0;
       if (k >= 0) {
         const int oldlen = s_flen[p * kMaxW + tid];
-        if (oldlen >= 0) start = min(s_src[q * kMaxW + k] == tid ? oldlen : sh[6 + p], klen);
+        if (oldlen >= 0) {
+          direct = s_src[q * kMaxW + k] == tid;   // then klen is oldlen or oldlen + 1
+          start = min(direct ? oldlen : sh[6 + p], klen);
+          if (direct && klen > oldlen) dlab = s_last[k];
+        }
       }
       const int s4 = start >> 2;
       const int e4 = (klen + 3) >> 2;
-      const int cnt = k >= 0 ? e4 - s4 : 0;
+      const int cnt = (k >= 0 && !direct) ? e4 - s4 : 0;
       __syncthreads();   // s_bslot complete; every read of the old state done
       // copy counts (int4 units) -> prefix sums; per destination its source
       // slot and first int4
@@ -1301,6 +1307,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
         }
       }
       __syncthreads();
+      if (dlab >= 0) clist[(int64_t)(p * W + tid) * ldc + klen - 1] = dlab;
       if (tid < W && k >= 0 && c != blank) clist[(int64_t)(p * W + tid) * ldc + klen] = c;
       __threadfence_block();
       __syncthreads();
