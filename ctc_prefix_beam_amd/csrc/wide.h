@@ -238,6 +238,22 @@ __device__ __forceinline__ uint64_t block_top64(const uint64_t* keys, int n, uin
   return top;
 }
 
+// A bitonic sequence of 64 keys (one per lane) into descending order.
+__device__ __forceinline__ uint64_t wave_bitonic64_desc(uint64_t v) {
+  v = bitonic_stage<64, 32>(v);
+  v = bitonic_stage<64, 16>(v);
+  v = bitonic_stage<64, 8>(v);
+  v = bitonic_stage<64, 4>(v);
+  v = bitonic_stage<64, 2>(v);
+  return bitonic_stage<64, 1>(v);
+}
+// A bitonic sequence of 128 keys (h: the first 64, l: the rest) into
+// descending order.
+__device__ __forceinline__ void order128(uint64_t& h, uint64_t& l) {
+  const uint64_t a = h > l ? h : l, b = h > l ? l : h;
+  h = wave_bitonic64_desc(a);
+  l = wave_bitonic64_desc(b);
+}
 // The 128 largest of keys[0, n) (n <= 512; missing ones count as 0) in
 // descending order, in wave 0's lanes: hi holds ranks 0-63, lo ranks 64-127
 // (other waves: unspecified).  Each wave orders a chunk of 128 (two keys per
@@ -248,19 +264,6 @@ __device__ __forceinline__ uint64_t block_top64(const uint64_t* keys, int n, uin
 // then the same ordering); wave 2 hands its result to wave 0 for the last
 // merge.  Block-wide: every thread calls it; tmp (384 keys) must not overlap
 // keys.  Ends with wave 0 holding the result (no barrier after the merge).
-__device__ __forceinline__ uint64_t wave_bitonic64_desc(uint64_t v) {
-  v = bitonic_stage<64, 32>(v);
-  v = bitonic_stage<64, 16>(v);
-  v = bitonic_stage<64, 8>(v);
-  v = bitonic_stage<64, 4>(v);
-  v = bitonic_stage<64, 2>(v);
-  return bitonic_stage<64, 1>(v);
-}
-__device__ __forceinline__ void order128(uint64_t& h, uint64_t& l) {   // bitonic (h, l) -> desc
-  const uint64_t a = h > l ? h : l, b = h > l ? l : h;
-  h = wave_bitonic64_desc(a);
-  l = wave_bitonic64_desc(b);
-}
 __device__ __forceinline__ void block_top128(const uint64_t* keys, int n, uint64_t* tmp,
                                              uint64_t& hi, uint64_t& lo) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
