@@ -2870,8 +2870,17 @@ int decode_offline_impl(const ctcpb_config* cfg, const float* log_prob, int64_t 
     if (int rc = launch(wide::rank_wide_kernel, batch * groups, wide::kNT,
                         wide::rank_lds_bytes(R.V), st, P, "rank_wide_kernel"))
       return rc;
-    if (int rc = launch(wide::decode_wide_kernel<false>, batch, wide::kNT,
-                        wide::lds_bytes(R.V, P.S.nslot), st, P, "decode_wide_kernel"))
+    // paged: the page tables, refcounts and free stack in LDS when they fit
+    // (S.tab / S.ref / S.fstk: their LDS offsets; 0: in the workspace)
+    int wlds = wide::lds_bytes(R.V, P.S.nslot);
+    if (L.paged && wlds + wide::pager_lds_bytes(L) <= kLdsLimit) {
+      P.S.tab = wlds;
+      P.S.ref = P.S.tab + align16(2 * L.W * L.max_lp * 4);
+      P.S.fstk = P.S.ref + align16(L.npages * 4);
+      wlds += wide::pager_lds_bytes(L);
+    }
+    if (int rc = launch(wide::decode_wide_kernel<false>, batch, wide::kNT, wlds, st, P,
+                        "decode_wide_kernel"))
       return rc;
     return ok();
   }

@@ -80,6 +80,12 @@ inline int lds_bytes(int V, int nbuf) {
   return off::end + nbuf * off::a16(V * 4) + off::a16(V * 2);
 }
 
+// Bytes of LDS for an offline row's page tables, refcounts and free stack
+// (int32, laid out after the lds_bytes part when they fit).
+inline int pager_lds_bytes(const Layout& L) {
+  return off::a16(2 * L.W * L.max_lp * 4) + 2 * off::a16(L.npages * 4);
+}
+
 // Block-wide: the kth largest (1-based) nonzero 64-bit key of the items, by
 // radix select over 8-bit digits; 0 when fewer than kth keys are nonzero.
 // gen(i) gives item i's key for i in [0, n): the keys of items tid + j kNT,
@@ -478,7 +484,14 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
   int* clist = reinterpret_cast<int*>(base + L.o_clist);
   const float* lp_row = P.lp + (int64_t)row_i * P.stride_b;
   const bool paged = L.paged != 0;
-  const WidePager G = wide_pager(L, base);
+  WidePager G = wide_pager(L, base);
+  if (!STREAM && paged && P.S.tab > 0) {
+    // offline, when they fit: the row's page tables, refcounts and free stack
+    // in LDS (they do not outlive the launch; the pages stay in the workspace)
+    G.tab = reinterpret_cast<int*>(smem + P.S.tab);
+    G.ref = reinterpret_cast<int*>(smem + P.S.ref);
+    G.fstk = reinterpret_cast<int*>(smem + P.S.fstk);
+  }
 
   int* Rc = reinterpret_cast<int*>(smem + off::Rc);
   float* Rl = reinterpret_cast<float*>(smem + off::Rl);
