@@ -817,6 +817,7 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
     // bounds the W-th largest candidate from below; n3: the score of the
     // beam's third open rank (no later label of the beam scores above it)
     float n3 = kNeg;
+    uint64_t t1k = 0ull, t2k = 0ull;   // the beam's best and second best sample key
     if (tid < W) {
       const int k = tid;
       const bool lv = s_live[k] != 0;
@@ -873,16 +874,44 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       cbuf[4 * k + 1] = cc;
       cbuf[4 * k + 2] = o0;
       cbuf[4 * k + 3] = o1;
+      if (W <= 64) {
+        const uint64_t m1 = cb > cc ? cb : cc, m2 = cb > cc ? cc : cb;
+        const uint64_t q1 = o0 > o1 ? o0 : o1, q2 = o0 > o1 ? o1 : o0;
+        t1k = m1 > q1 ? m1 : q1;
+        const uint64_t r1 = m1 > q1 ? q1 : m1, r2 = m2 > q2 ? m2 : q2;
+        t2k = r1 > r2 ? r1 : r2;
+      }
     }
     if (tid == 0) {
       sh[4] = 0;
       sh[15] = 0;
     }
+    if (W <= 64 && wave == 0) {
+      // (beams up to 64, one per lane of this wave) as in the fused decoder:
+      // when every beam's best ranks in beam order and every beam's second
+      // scores strictly below the last beam's best, the beams' bests are the
+      // winners, in rank order (every later candidate scores no higher than
+      // its beam's second), and no sort is needed
+      constexpr uint64_t kScoreBits = 0xffffffff00000000ull;
+      const uint64_t nxt = wave_shl1_u64(t1k);
+      const uint64_t c1W = readlane_u64(t1k, W - 1);
+      const bool in_order = __ballot(t1k < nxt) == 0ull;
+      const bool no_second = __ballot((t2k != 0ull) & (t2k >= (c1W & kScoreBits))) == 0ull;
+      const bool ok = in_order && no_second;
+      if (ok) {
+        if (tid < W) win[tid] = t1k;
+        const int cnt = __popcll(__ballot(tid < W && t1k != 0ull));
+        if (tid == 0) sh[4] = cnt;
+      }
+      if (tid == 0) sh[1] = ok ? 1 : 0;
+    }
     __syncthreads();
+    const bool in_order_fast = W <= 64 && sh[1] != 0;
     // tau: the W-th largest of the 4W sample keys (0 when fewer are nonzero)
-    uint64_t tau;
-    bool fast = false;   // set when the sample's best W are the winners
-    if (W <= 64) {
+    uint64_t tau = 1ull;
+    bool fast = in_order_fast;   // set when the winners are known without the survivors
+    if (in_order_fast) {
+    } else if (W <= 64) {
       const uint64_t top = block_top64(cbuf, 4 * W, cbuf + kCBuf - 384);
       if (wave == 0) {
         // (beams up to 64: all in this wave) when every beam's third open rank
