@@ -874,17 +874,21 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       cbuf[4 * k + 1] = cc;
       cbuf[4 * k + 2] = o0;
       cbuf[4 * k + 3] = o1;
-      if (W <= 64) {
-        const uint64_t m1 = cb > cc ? cb : cc, m2 = cb > cc ? cc : cb;
-        const uint64_t q1 = o0 > o1 ? o0 : o1, q2 = o0 > o1 ? o1 : o0;
-        t1k = m1 > q1 ? m1 : q1;
-        const uint64_t r1 = m1 > q1 ? q1 : m1, r2 = m2 > q2 ? m2 : q2;
-        t2k = r1 > r2 ? r1 : r2;
-      }
+      const uint64_t m1 = cb > cc ? cb : cc, m2 = cb > cc ? cc : cb;
+      const uint64_t q1 = o0 > o1 ? o0 : o1, q2 = o0 > o1 ? o1 : o0;
+      t1k = m1 > q1 ? m1 : q1;
+      const uint64_t r1 = m1 > q1 ? q1 : m1, r2 = m2 > q2 ? m2 : q2;
+      t2k = r1 > r2 ? r1 : r2;
     }
+    constexpr uint64_t kScoreBits = 0xffffffff00000000ull;
     if (tid == 0) {
       sh[4] = 0;
       sh[15] = 0;
+      if (W > 64) sh[1] = 1;
+    }
+    if (W > 64) {   // for the test below across two waves
+      if (tid == 64) kb64[0] = t1k;
+      if (tid == W - 1) kb64[1] = t1k;
     }
     if (W <= 64 && wave == 0) {
       // (beams up to 64, one per lane of this wave) as in the fused decoder:
@@ -892,7 +896,6 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       // scores strictly below the last beam's best, the beams' bests are the
       // winners, in rank order (every later candidate scores no higher than
       // its beam's second), and no sort is needed
-      constexpr uint64_t kScoreBits = 0xffffffff00000000ull;
       const uint64_t nxt = wave_shl1_u64(t1k);
       const uint64_t c1W = readlane_u64(t1k, W - 1);
       const bool in_order = __ballot(t1k < nxt) == 0ull;
@@ -906,7 +909,24 @@ __global__ __launch_bounds__(kNT, 1) void decode_wide_kernel(Params P) {
       if (tid == 0) sh[1] = ok ? 1 : 0;
     }
     __syncthreads();
-    const bool in_order_fast = W <= 64 && sh[1] != 0;
+    if (W > 64) {
+      // the same test with the beams in two waves (the beam after a wave's
+      // last and the last beam's best from LDS); the winners are written in
+      // advance, and the paths below overwrite them
+      if (wave < 2) {
+        uint64_t nxt = wave_shl1_u64(t1k);
+        if (tid == 63) nxt = kb64[0];
+        const uint64_t c1W = kb64[1];
+        const bool bad = __ballot(t1k < nxt) != 0ull ||
+                         __ballot((t2k != 0ull) & (t2k >= (c1W & kScoreBits))) != 0ull;
+        if (bad && (tid & 63) == 0) sh[1] = 0;
+        if (tid < W) win[tid] = t1k;
+        const int cnt = __popcll(__ballot(tid < W && t1k != 0ull));
+        if ((tid & 63) == 0 && cnt) atomicAdd(&sh[4], cnt);
+      }
+      __syncthreads();
+    }
+    const bool in_order_fast = sh[1] != 0;
     // tau: the W-th largest of the 4W sample keys (0 when fewer are nonzero)
     uint64_t tau = 1ull;
     bool fast = in_order_fast;   // set when the winners are known without the survivors
